@@ -1,0 +1,386 @@
+"""fp64 CPU oracle of the routed MoE expert-FFN path.
+
+TEST INFRASTRUCTURE. Only tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg may import this module. The product path (the HIP library and
+its Python binding) never imports, calls or links it, and shares no code with
+it: number formats, routing, permutation, quantisation, dequantisation,
+epilogue and combine are written out here a second time, plainly, in float64.
+
+What each step computes, and the passage it follows (the pages are cited by
+title and section):
+
+  route      -- sigmoid-gate top-k with log-sigmoid renormalisation and
+                shared-sink columns: "Enable and fuse the Inkling MoE gate
+                epilogue on Intel XPU" (sglang PR #36385), "2. Correctness"
+                (w = exp(lp - logsumexp(lp)), lp = logsigmoid(x)) and
+                "3. Performance" plus the epilogue commit message (iterative
+                masked-max top-k, raw logit carried, trailing SHARED_SINK
+                columns join the normaliser, global_scale).
+  permute    -- expert-parallel rebase: routing ids are global, per-expert
+                tables are rank-local, rebase by local_expert_offset and
+                bounds-check: "FlashInfer 0.6.18 SM100a+SM103a MoE-LoRA AOT"
+                release notes, "Changes since 1b699bf"; tokens grouped per
+                expert ("per-expert sorted-token dispatch"): "Fused INT4
+                grouped + SiLU Triton kernel" (batchgen PR #239), commit text.
+  quant_act  -- per-token, per-128-column fp8 e4m3 activation quantisation
+                that goes with blockwise 128x128 FP8 weights ("DeepSeekFp8"):
+                sglang PR #39920, "Modifications"; rounding read as
+                round-to-nearest-even with saturation at +-448.
+  dequant    -- FP8 q * block scale; INT4 (nibble - 8) * scale[n, k/32],
+                low nibble = even k: batchgen PR #239, commit text.
+  swiglu     -- g' = min(g, L), u' = clamp(u, -L, L),
+                h = g' * sigmoid(alpha g') * (u' + beta); defaults alpha = 1,
+                beta = 0, no clamp: sglang PR #39920 "Modifications" and
+                "fix(sm90): support parameterized SwiGLU in FP8 MegaMoE"
+                (DeepGEMM PR #445), "Summary" and "Compatibility".
+  lora       -- delta added to gate and up in true units, i.e. after each
+                half's own global scale: MoE-LoRA AOT release notes,
+                "Changes since 1b699bf".
+  combine    -- out[t] = sum over t's local slots of w[t, j] * y[t, j], fp32
+                accumulation on the device ("slot-specific routing-weight
+                reduction"): batchgen PR #239, commit text.
+
+Readings taken where the pages leave a step open are listed in the design
+notes; the code states each one where it is used.
+
+Parity of the whole layer against a printed page output is unpinned (the pages
+print no layer outputs); each step is pinned separately by the tests.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+E4M3_MAX = 448.0
+
+
+# ----------------------------------------------------------------------------
+# number formats (OCP e4m3fn, bfloat16), written from their definitions
+# ----------------------------------------------------------------------------
+
+def e4m3_decode(codes) -> np.ndarray:
+    """OCP e4m3fn code -> value: sign * 2^(e-7) * (1 + m/8) for e >= 1,
+    sign * 2^-6 * m/8 for e == 0; 0x7F / 0xFF are NaN (no infinities)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    val = np.where(e == 0, np.ldexp(m / 8.0, -6),
+                   np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int32)))
+    val = np.where((e == 15) & ((c & 7) == 7), np.nan, val)
+    return sign * val
+
+
+def e4m3_round(v) -> np.ndarray:
+    """Nearest e4m3fn code to the exact value v (float64), ties to the even
+    code, magnitudes >= 448 saturated to +-448. Returns uint8 codes."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    sign = np.where(np.signbit(v), 0x80, 0).astype(np.int64)
+    # subnormal range: multiples of 2^-9 below 2^-6 (m = 8 is the first normal)
+    sub = a < 2.0 ** -6
+    code_sub = np.rint(np.where(sub, a, 0.0) * 512.0).astype(np.int64)
+    # normal range: 4 significant bits
+    an = np.where(sub | ~np.isfinite(a), 1.0, a)
+    _, ex = np.frexp(an)
+    e = (ex - 1).astype(np.int64)                # an = 1.f * 2^e
+    mant = np.rint(np.ldexp(an, (3 - e).astype(np.int32))).astype(np.int64)
+    e = np.where(mant >= 16, e + 1, e)           # rounding carried into e
+    mant = np.where(mant >= 16, 8, mant)
+    code_norm = ((e + 7) << 3) | (mant - 8)
+    code = np.where(sub, code_sub, code_norm)
+    code = np.where(a >= E4M3_MAX, 0x7E, code)
+    code = np.where(np.isnan(v), 0x7F, code | sign)
+    return code.astype(np.uint8)
+
+
+def bf16_decode(bits) -> np.ndarray:
+    """bfloat16 bits (uint16) -> float64: the top half of an IEEE binary32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def bf16_round(v) -> np.ndarray:
+    """Nearest bfloat16 value (8 significant bits, ties to even) of float64 v,
+    returned as float64. Normal range only (|v| >= 2^-126), which covers every
+    value rounded here; smaller magnitudes round on the 2^-133 grid."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, ex = np.frexp(np.where(a == 0, 1.0, a))
+    e = np.maximum(ex - 1, -126)
+    q = np.ldexp(np.rint(np.ldexp(a, (7 - e).astype(np.int32))),
+                 (e - 7).astype(np.int32))
+    return np.where(np.signbit(v), -q, q)
+
+
+# ----------------------------------------------------------------------------
+# router epilogue (sglang PR #36385)
+# ----------------------------------------------------------------------------
+
+def logsigmoid(x) -> np.ndarray:
+    """log(sigmoid(x)) = min(x, 0) - log1p(exp(-|x|)), the overflow-free form."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.minimum(x, 0.0) - np.log1p(np.exp(-np.abs(x)))
+
+
+def topk_masked_max(keys, k):
+    """k passes of argmax over the keys not yet taken; equal keys resolve to
+    the lower column index. Slot j holds the j-th pick."""
+    keys = np.asarray(keys, dtype=np.float64)
+    T, N = keys.shape
+    ids = np.zeros((T, k), dtype=np.int64)
+    remaining = np.ones((T, N), dtype=bool)
+    for j in range(k):
+        masked = np.where(remaining, keys, np.nan)
+        pick = np.nanargmax(masked, axis=1)       # first index of the max
+        ids[:, j] = pick
+        remaining[np.arange(T), pick] = False
+    return ids
+
+
+def route(logits, n_routed, n_sink, top_k, route_scale=1.0, global_scale=1.0):
+    """Top-k over the n_routed columns of each fp32 logit row (ranked on the
+    raw logit: with no selection bias sigmoid is strictly increasing, so this
+    is the order of sigmoid(x)), then weights over the k winners and the
+    n_sink trailing sink columns:
+        lp = logsigmoid(x),  w = exp(lp - logsumexp(lp)) * route_scale * global_scale.
+    Returns ids [T, k] (global column ids), w [T, k], sink_w [T, n_sink]."""
+    lg = np.asarray(logits, dtype=np.float32)
+    T = lg.shape[0]
+    keys = lg[:, :n_routed].astype(np.float64)
+    ids = topk_masked_max(keys, top_k)
+    chosen = np.take_along_axis(keys, ids, axis=1)          # raw logits
+    sinks = lg[:, n_routed:n_routed + n_sink].astype(np.float64)
+    lp = logsigmoid(np.concatenate([chosen, sinks], axis=1))
+    if T == 0:
+        return ids, np.zeros((0, top_k)), np.zeros((0, n_sink))
+    m = lp.max(axis=1, keepdims=True)
+    lse = m + np.log(np.exp(lp - m).sum(axis=1, keepdims=True))
+    scale = float(np.float32(route_scale)) * float(np.float32(global_scale))
+    w = np.exp(lp - lse) * scale
+    return ids, w[:, :top_k], w[:, top_k:]
+
+
+# ----------------------------------------------------------------------------
+# permutation by expert with expert-parallel rebase
+# ----------------------------------------------------------------------------
+
+ERR_GLOBAL_ID_OOB = 0x1
+
+
+def permute(ids, num_experts_global, local_offset, num_local, shared):
+    """Group the (token, slot) pairs by local expert.
+
+    Pair id p = t*k + j for routed slots; the always-on shared expert (if any)
+    is group num_local with pair ids T*k + t. A global id is rebased to
+    e = id - local_offset and kept iff 0 <= e < num_local; ids outside
+    [0, num_experts_global) set ERR_GLOBAL_ID_OOB and are skipped.
+    Within a group pairs are ordered by p. Returns (offsets [G+1],
+    sorted_pair [P], pair_row [T*k (+T)], err)."""
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    G = num_local + (1 if shared else 0)
+    groups = [[] for _ in range(G)]
+    err = 0
+    for t in range(T):
+        for j in range(k):
+            gid = int(ids[t, j])
+            if gid < 0 or gid >= num_experts_global:
+                err |= ERR_GLOBAL_ID_OOB
+                continue
+            e = gid - local_offset
+            if 0 <= e < num_local:
+                groups[e].append(t * k + j)
+    if shared:
+        groups[num_local] = [T * k + t for t in range(T)]
+    offsets = [0]
+    sorted_pair = []
+    for g in range(G):
+        sorted_pair.extend(groups[g])
+        offsets.append(len(sorted_pair))
+    n_pairs = T * k + (T if shared else 0)
+    pair_row = -np.ones(n_pairs, dtype=np.int64)
+    pair_row[np.asarray(sorted_pair, dtype=np.int64)] = np.arange(len(sorted_pair))
+    return (np.asarray(offsets, dtype=np.int64),
+            np.asarray(sorted_pair, dtype=np.int64), pair_row, err)
+
+
+# ----------------------------------------------------------------------------
+# fp8 activation quantisation (per token, per 128 columns)
+# ----------------------------------------------------------------------------
+
+def quant_act_fp8(x_f32, group=128):
+    """amax over each 128-column group in fp32, s = fp32(amax / 448) (s = 1
+    when amax = 0), q = e4m3 RNE of the fp32 quotient fp32(x / s), saturated.
+    Returns (codes uint8 [T, H], s float32 [T, H/128])."""
+    x = np.asarray(x_f32, dtype=np.float32)
+    T, H = x.shape
+    xg = x.reshape(T, H // group, group)
+    amax = np.abs(xg).max(axis=2) if T else np.zeros((0, H // group), np.float32)
+    s = np.where(amax > 0, amax / np.float32(E4M3_MAX),
+                 np.float32(1.0)).astype(np.float32)
+    quot = (xg / s[:, :, None]).astype(np.float32)          # fp32 division
+    q = e4m3_round(quot.astype(np.float64)).reshape(T, H)
+    return q, s
+
+
+def requant_fp8(h, group=128):
+    """The FP8 path's intermediate rounding of h [P, I] (float64): per row and
+    128-column group, amax taken to fp32, s = fp32(amax / 448) (1 if zero),
+    q = e4m3 RNE of h / s, saturated. Returns the value q * s (float64)."""
+    h = np.asarray(h, dtype=np.float64)
+    P, I = h.shape
+    hg = h.reshape(P, I // group, group)
+    amax = np.abs(hg).max(axis=2).astype(np.float32) if P else \
+        np.zeros((0, I // group), np.float32)
+    s = np.where(amax > 0, amax / np.float32(E4M3_MAX),
+                 np.float32(1.0)).astype(np.float32).astype(np.float64)
+    q = e4m3_round(hg / s[:, :, None])
+    return (e4m3_decode(q) * s[:, :, None]).reshape(P, I)
+
+
+# ----------------------------------------------------------------------------
+# weight dequantisation, one expert at a time, exact in float64
+# ----------------------------------------------------------------------------
+
+def dequant_fp8_block(q, bs):
+    """w[n, k] = e4m3(q[n, k]) * bs[n // 128, k // 128]."""
+    w = e4m3_decode(q)
+    return w * np.repeat(np.repeat(np.asarray(bs, np.float64), 128, axis=0),
+                         128, axis=1)
+
+
+def dequant_int4_g32(packed, scale_bits):
+    """Byte j of row n holds k = 2j in its low nibble and k = 2j + 1 in its
+    high nibble; w[n, k] = (nibble - 8) * scale[n, k // 32] (bf16 scale)."""
+    b = np.asarray(packed, dtype=np.uint8).astype(np.int64)
+    N, Kh = b.shape
+    nib = np.empty((N, 2 * Kh), dtype=np.float64)
+    nib[:, 0::2] = (b & 0xF) - 8
+    nib[:, 1::2] = (b >> 4) - 8
+    return nib * np.repeat(bf16_decode(scale_bits), 32, axis=1)
+
+
+def dequant(fmt, q, s):
+    if fmt == "bf16":
+        return bf16_decode(q)
+    if fmt == "fp8":
+        return dequant_fp8_block(q, s)
+    if fmt == "int4":
+        return dequant_int4_g32(q, s)
+    raise ValueError(fmt)
+
+
+# ----------------------------------------------------------------------------
+# parameterized SwiGLU epilogue
+# ----------------------------------------------------------------------------
+
+def sigmoid(z):
+    z = np.asarray(z, dtype=np.float64)
+    ez = np.exp(-np.abs(z))
+    return np.where(z >= 0, 1.0 / (1.0 + ez), ez / (1.0 + ez))
+
+
+def swiglu(g, u, alpha=1.0, beta=0.0, limit=math.inf):
+    """Clamp first (gate from above only, up on both sides), alpha scales the
+    clamped gate inside the sigmoid, beta is added to the clamped up."""
+    gp = np.minimum(g, limit)
+    up = np.clip(u, -limit, limit)
+    return gp * sigmoid(alpha * gp) * (up + beta)
+
+
+# ----------------------------------------------------------------------------
+# one expert over its pairs, and the whole layer
+# ----------------------------------------------------------------------------
+
+def w13_dequant(spec, arr, e):
+    """Dequantised fused [gate | up] weight of group e: rows 0..I-1 gate,
+    I..2I-1 up, each half times its own global scale when present."""
+    w = dequant(spec.fmt, arr["w13_q"][e],
+                None if arr["w13_s"] is None else arr["w13_s"][e])
+    if arr.get("gs") is not None:
+        I = spec.I
+        gs = np.asarray(arr["gs"][e], dtype=np.float32).astype(np.float64)
+        w[:I] *= gs[0]
+        w[I:] *= gs[1]
+    return w
+
+
+def lora_delta(spec, arr, e, x_bf16_rows):
+    """Rank-r delta on [gate | up] in true units: z = x A_e^T (kept in full
+    precision), delta = lora_scale * z B_e^T, shape [m, 2I]."""
+    A = bf16_decode(arr["lora_A"][e])              # [r, H]
+    B = bf16_decode(arr["lora_B"][e])              # [2I, r]
+    z = x_bf16_rows @ A.T
+    return float(np.float32(spec.lora_scale)) * (z @ B.T)
+
+
+def expert_ffn(spec, arr, e, xhat_rows, x_bf16_rows):
+    """y = round_h(swiglu(g, u)) W2_e^T for the rows of one group.
+    xhat_rows are the GEMM1 input values (fp8-dequantised for FP8 layers,
+    the bf16 values otherwise); x_bf16_rows feed the LoRA input."""
+    I = spec.I
+    w13 = w13_dequant(spec, arr, e)
+    gu = xhat_rows @ w13.T                         # [m, 2I]
+    g, u = gu[:, :I].copy(), gu[:, I:].copy()
+    if spec.lora_rank and e < spec.n_local:
+        d = lora_delta(spec, arr, e, x_bf16_rows)
+        g += d[:, :I]
+        u += d[:, I:]
+    f32 = lambda v: float(np.float32(v))
+    h = swiglu(g, u, f32(spec.alpha), f32(spec.beta), f32(spec.limit))
+    hhat = requant_fp8(h) if spec.fmt == "fp8" else bf16_round(h)
+    w2 = dequant(spec.fmt, arr["w2_q"][e],
+                 None if arr["w2_s"] is None else arr["w2_s"][e])
+    return hhat @ w2.T                             # [m, H]
+
+
+def gemm1_input(spec, x_bits):
+    """Values that enter GEMM1: the bf16 x, or for FP8 layers the dequantised
+    per-token per-128-column e4m3 codes."""
+    x = bf16_decode(x_bits)
+    if spec.fmt == "fp8":
+        q, s = quant_act_fp8(x.astype(np.float32))
+        return e4m3_decode(q) * np.repeat(s.astype(np.float64), 128, axis=1), x
+    return x, x
+
+
+def moe_layer(spec, arr, x_bits, logits, tokens=None, routing=None):
+    """Output rows out[t, :] (float64) for the tokens asked for (all by
+    default): route, rebase, per-expert FFN, then for each token
+    sum_j w[t, j] y[t, j] over its local slots in ascending j, plus
+    shared_w * y_shared last. `arr` maps array names to per-group indexable
+    arrays (a dict of full arrays, or lazy accessors)."""
+    T = x_bits.shape[0]
+    if routing is None:
+        routing = route(logits, spec.n_routed, spec.n_sink, spec.top_k,
+                        spec.route_scale, spec.global_scale)
+    ids, w, _ = routing
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens)
+    pairs = {}            # group -> list of (row in output, slot or -1)
+    for i, t in enumerate(tokens):
+        for j in range(spec.top_k):
+            e = int(ids[t, j]) - spec.offset
+            if 0 <= int(ids[t, j]) < spec.n_routed and 0 <= e < spec.n_local:
+                pairs.setdefault(e, []).append((i, j))
+        if spec.shared:
+            pairs.setdefault(spec.n_local, []).append((i, -1))
+    xhat, xb = gemm1_input(spec, x_bits[tokens])
+    contrib = {}
+    for e in sorted(pairs):
+        rows = [i for i, _ in pairs[e]]
+        y = expert_ffn(spec, arr, e, xhat[rows], xb[rows])
+        for (i, j), yrow in zip(pairs[e], y):
+            contrib[(i, j)] = yrow
+    out = np.zeros((len(tokens), spec.H))
+    sw = float(np.float32(spec.shared_w))
+    for i, t in enumerate(tokens):
+        acc = np.zeros(spec.H)
+        for j in range(spec.top_k):
+            if (i, j) in contrib:
+                acc = acc + w[t, j] * contrib[(i, j)]
+        if (i, -1) in contrib:
+            acc = acc + sw * contrib[(i, -1)]
+        out[i] = acc
+    return out

@@ -1,0 +1,192 @@
+"""Pins of the oracle's expert FFN and combine (no GPU): the SwiGLU epilogue
+against library activations, LoRA invariants from the MoE-LoRA release
+notes, and the whole layer against the independent brute-force formulation,
+with planted mistakes that must be caught."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import brute
+from oracle import moe_oracle as O
+from synth import make_batch, make_layer, to_numpy_batch, to_numpy_layer
+from tests.tinyspecs import TINY
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gu(n=20000, scale=8.0, seed=11):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(n, generator=g, dtype=torch.float64) * scale,
+            torch.randn(n, generator=g, dtype=torch.float64) * scale)
+
+
+def test_swiglu_defaults_reduce_to_silu_times_up():
+    g, u = _gu()
+    ours = O.swiglu(g.numpy(), u.numpy())
+    np.testing.assert_allclose(ours, (F.silu(g) * u).numpy(), rtol=1e-13, atol=1e-300)
+
+
+def test_swiglu_clamped_matches_page_formula():
+    p = json.load(open(os.path.join(GOLD, "epilogue_params.json")))["clamped_swiglu"]
+    g, u = _gu()
+    L = p["limit"]
+    ref = F.silu(torch.clamp(g, max=L)) * torch.clamp(u, -L, L)
+    np.testing.assert_allclose(O.swiglu(g.numpy(), u.numpy(), 1.0, 0.0, L),
+                               ref.numpy(), rtol=1e-13, atol=1e-300)
+
+
+def test_swiglu_oai_matches_page_formula_and_bounds():
+    p = json.load(open(os.path.join(GOLD, "epilogue_params.json")))["oai_swiglu"]
+    a, b, L = p["alpha"], p["beta"], p["limit"]
+    g, u = _gu()
+    gc = torch.clamp(g, max=L)
+    ref = gc * torch.sigmoid(a * gc) * (torch.clamp(u, min=-L, max=L) + b)
+    h = O.swiglu(g.numpy(), u.numpy(), a, b, L)
+    np.testing.assert_allclose(h, ref.numpy(), rtol=1e-13, atol=1e-300)
+    # |h| <= max(L sigma(aL), max_x |x sigma(a x)| over x < 0) * (L + |b|)
+    neg_peak = 0.27846454276107 / a
+    bound = max(L / (1 + math.exp(-a * L)), neg_peak) * (L + abs(b))
+    assert np.all(np.abs(h) <= bound * (1 + 1e-12))
+    # above the limit the output no longer depends on g
+    h1 = O.swiglu(np.array([L + 0.5, L + 50.0]), np.array([1.0, 1.0]), a, b, L)
+    assert h1[0] == h1[1]
+
+
+def _oracle_and_brute(spec, T, mutate=None, monkeypatch=None):
+    layer = make_layer(spec)
+    batch = make_batch(spec, layer, T)
+    arr = to_numpy_layer(layer)
+    nb = to_numpy_batch(batch)
+    ref = np.array(brute.layer(spec, arr, nb["x_bits"], nb["logits"]))
+    if mutate is not None:
+        mutate(monkeypatch)
+    ours = O.moe_layer(spec, arr, nb["x_bits"], nb["logits"])
+    if monkeypatch is not None:
+        monkeypatch.undo()
+    return ours, ref
+
+
+@pytest.mark.parametrize("name", list(TINY))
+def test_oracle_layer_matches_brute_force(name):
+    spec = TINY[name]
+    ours, ref = _oracle_and_brute(spec, 5)
+    scale = np.abs(ref).max()
+    assert scale > 0
+    assert np.max(np.abs(ours - ref)) <= 1e-9 * scale
+
+
+def test_oracle_k1_single_expert_and_linearity():
+    spec = TINY["bf16"].scaled(top_k=1, name="tiny_k1")
+    ours, ref = _oracle_and_brute(spec, 5)
+    assert np.max(np.abs(ours - ref)) <= 1e-9 * np.abs(ref).max()
+    layer = make_layer(spec)
+    batch = make_batch(spec, layer, 5)
+    arr, nb = to_numpy_layer(layer), to_numpy_batch(batch)
+    o1 = O.moe_layer(spec, arr, nb["x_bits"], nb["logits"])
+    o2 = O.moe_layer(spec.scaled(route_scale=2.0), arr, nb["x_bits"], nb["logits"])
+    assert np.array_equal(o2, 2.0 * o1)
+
+
+def _mut_swap_gate_up(mp):
+    real = O.w13_dequant
+
+    def swapped(spec, arr, e):
+        w = real(spec, arr, e)
+        return np.concatenate([w[spec.I:], w[:spec.I]])
+    mp.setattr(O, "w13_dequant", swapped)
+
+
+def _mut_drop_clamp(mp):
+    real = O.swiglu
+    mp.setattr(O, "swiglu", lambda g, u, a=1.0, b=0.0, L=math.inf: real(g, u, a, b))
+
+
+def _mut_no_requant(mp):
+    mp.setattr(O, "requant_fp8", lambda h, group=128: h)
+
+
+@pytest.mark.parametrize("mut,name", [
+    (_mut_swap_gate_up, "fp8_clamp_shared"), (_mut_drop_clamp, "fp8_clamp_shared"),
+    (_mut_drop_clamp, "fp8_oai"), (_mut_no_requant, "fp8_oai")])
+def test_planted_mistakes_are_caught_by_brute_force(mut, name, monkeypatch):
+    spec = TINY[name]
+    ours, ref = _oracle_and_brute(spec, 5, mut, monkeypatch)
+    assert np.max(np.abs(ours - ref)) > 1e-6 * np.abs(ref).max()
+
+
+def test_planted_missing_rebase_is_caught(monkeypatch):
+    spec = TINY["ep_lora"]
+    layer = make_layer(spec)
+    batch = make_batch(spec, layer, 5)
+    arr, nb = to_numpy_layer(layer), to_numpy_batch(batch)
+    ref = np.array(brute.layer(spec, arr, nb["x_bits"], nb["logits"]))
+    bad = O.moe_layer(spec.scaled(offset=0), arr, nb["x_bits"], nb["logits"])
+    assert np.max(np.abs(bad - ref)) > 1e-6 * np.abs(ref).max()
+
+
+# ---------------------------------------------------------------- LoRA pins
+
+def _lora_setup(T=6):
+    spec = TINY["ep_lora"]
+    layer = make_layer(spec)
+    batch = make_batch(spec, layer, T)
+    return spec, layer, to_numpy_layer(layer), to_numpy_batch(batch)
+
+
+def test_lora_zero_B_equals_base_and_no_adapter_equals_base():
+    spec, layer, arr, nb = _lora_setup()
+    base = O.moe_layer(spec.scaled(lora_rank=0), arr, nb["x_bits"], nb["logits"])
+    arr0 = dict(arr, lora_B=np.zeros_like(arr["lora_B"]))
+    zero_b = O.moe_layer(spec, arr0, nb["x_bits"], nb["logits"])
+    assert np.array_equal(base, zero_b)
+    with_lora = O.moe_layer(spec, arr, nb["x_bits"], nb["logits"])
+    assert np.max(np.abs(with_lora - base)) > 1e-3 * np.abs(base).max()
+
+
+def _resplit(spec, arr, factor):
+    """Move a factor between the up half's global scale and its block scales:
+    the dequantised weights stay the same."""
+    a = dict(arr)
+    gs = arr["gs"].copy()
+    gs[:, 1] = (gs[:, 1] / np.float32(factor)).astype(np.float32)
+    s = arr["w13_s"].copy()
+    nb_half = spec.I // 128
+    s[:, nb_half:, :] = (s[:, nb_half:, :] * np.float32(factor)).astype(np.float32)
+    a["gs"], a["w13_s"] = gs, s
+    return a
+
+
+def test_lora_true_units_invariant_to_up_gate_split():
+    spec, layer, arr, nb = _lora_setup()
+    ref = O.moe_layer(spec, arr, nb["x_bits"], nb["logits"])
+    # power-of-two re-split: bit-identical
+    out = O.moe_layer(spec, _resplit(spec, arr, 4.0), nb["x_bits"], nb["logits"])
+    assert np.array_equal(out, ref)
+    # arbitrary re-split: equal up to fp32 rounding of the moved scales
+    out = O.moe_layer(spec, _resplit(spec, arr, 1.37), nb["x_bits"], nb["logits"])
+    assert np.max(np.abs(out - ref)) <= 1e-5 * np.abs(ref).max()
+
+
+def test_lora_old_units_bug_is_caught(monkeypatch):
+    """The pre-fix behaviour (delta added before the up half is rescaled,
+    i.e. the up delta multiplied by gs_up / gs_gate) breaks the invariance."""
+    spec, layer, arr, nb = _lora_setup()
+    real = O.lora_delta
+
+    def buggy(spec_, arr_, e, xrows):
+        d = real(spec_, arr_, e, xrows)
+        gs = arr_["gs"][e].astype(np.float64)
+        d[:, spec_.I:] *= gs[1] / gs[0]
+        return d
+    monkeypatch.setattr(O, "lora_delta", buggy)
+    a = O.moe_layer(spec, arr, nb["x_bits"], nb["logits"])
+    b = O.moe_layer(spec, _resplit(spec, arr, 1.8), nb["x_bits"], nb["logits"])
+    monkeypatch.undo()
+    ref = O.moe_layer(spec, arr, nb["x_bits"], nb["logits"])
+    assert np.max(np.abs(a - b)) > 1e-3 * np.abs(ref).max()
+    assert np.max(np.abs(a - ref)) > 1e-3 * np.abs(ref).max()

@@ -1,0 +1,21 @@
+"""Tiny layer shapes for the brute-force pins and quick parity cases."""
+import math
+
+from synth import CONFIGS, LayerSpec
+
+TINY = {
+    "bf16": LayerSpec(name="tiny_bf16_t", cfg_id=101, fmt="bf16", H=64, I=32,
+                      n_routed=4, top_k=2, w13_std=0.1, w2_std=0.1),
+    "fp8_clamp_shared": LayerSpec(name="tiny_fp8_t", cfg_id=102, fmt="fp8",
+                                  H=128, I=128, n_routed=4, top_k=2, shared=1,
+                                  limit=10.0),
+    "fp8_oai": LayerSpec(name="tiny_fp8_oai_t", cfg_id=103, fmt="fp8", H=128,
+                         I=128, n_routed=4, top_k=2, alpha=1.702, beta=1.0,
+                         limit=7.0, logits="skewed"),
+    "int4": LayerSpec(name="tiny_int4_t", cfg_id=104, fmt="int4", H=64, I=32,
+                      n_routed=4, top_k=2),
+    "ep_lora": LayerSpec(name="tiny_ep_lora_t", cfg_id=105, fmt="fp8", H=128,
+                         I=128, n_routed=8, n_sink=2, top_k=3, E_loc=3,
+                         offset=2, lora_rank=4, gscale=True, logits="mix258",
+                         route_scale=1.5),
+}
