@@ -1,0 +1,241 @@
+/*
+ * moe_mi355x.h -- C ABI of the routed mixture-of-experts expert-FFN hot path
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited by title and section:
+ *   [GATE-PR]  "Enable and fuse the Inkling MoE gate epilogue on Intel XPU"
+ *              (sglang PR #36385)
+ *   [CLAMP-PR] "[Moe] Fix flashinfer_trtllm silently dropping swiglu_limit
+ *              clamped SwiGLU activation" (sglang PR #39920)
+ *   [OAI-PR]   "fix(sm90): support parameterized SwiGLU in FP8 MegaMoE"
+ *              (DeepGEMM PR #445)
+ *   [INT4-PR]  "sm100: Fused INT4 grouped + SiLU Triton kernel"
+ *              (batchgen PR #239)
+ *   [LORA-AOT] "FlashInfer 0.6.18 SM100a+SM103a MoE-LoRA AOT -- SwiGLU LoRA
+ *              up-delta units, EP scale lookups" (release notes)
+ *
+ * Conventions for every entry point:
+ *   - Every array argument is DEVICE memory owned by the caller (plain
+ *     pointers; the descriptors moe_weights / moe_lora / moe_layer /
+ *     moe_act_params themselves are HOST structs read during the call).
+ *     The library keeps no pointer after a call returns, allocates no device
+ *     or host memory, and never synchronises except in
+ *     moe_read_device_error. `stream` is a hipStream_t (NULL = default).
+ *   - Work is enqueued asynchronously on `stream`; outputs are valid once the
+ *     stream reaches that point.
+ *   - Host-detectable problems return a negative moe_status and enqueue
+ *     nothing. Launch failures return MOE_ERR_HIP (moe_last_error() has the
+ *     HIP message). Data-dependent problems found on the device (a routing
+ *     id outside [0, num_experts_global)) OR a MOE_DEVERR_* bit into a
+ *     caller-owned int32 `err_word` (the caller zeroes it), skip the bad
+ *     pair and leave every valid pair unaffected.
+ *   - Row-major layouts; a "[G][N][K]" weight is G matrices of N output rows
+ *     by K input columns.
+ *   - Calls that share a workspace must not run concurrently.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,        /* a required pointer is NULL */
+  MOE_ERR_SHAPE = -2,       /* a size is out of range or not a multiple */
+  MOE_ERR_FORMAT = -3,      /* unknown weight format or format mismatch */
+  MOE_ERR_LOCAL_RANGE = -4, /* missing/invalid local expert range */
+  MOE_ERR_PARAM = -5,       /* non-finite or out-of-range scalar parameter */
+  MOE_ERR_WORKSPACE = -6,   /* workspace NULL or too small */
+  MOE_ERR_HIP = -8          /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum {
+  MOE_W_BF16 = 0,      /* bf16 [G][N][K]; scale NULL */
+  MOE_W_FP8_B128 = 1,  /* OCP e4m3fn [G][N][K]; scale fp32 [G][N/128][K/128]
+                          (w = q * scale, 128x128 blocks) [CLAMP-PR
+                          "Modifications": blockwise 128x128 FP8] */
+  MOE_W_INT4_G32 = 2   /* u8 [G][N][K/2] (byte j of a row: low nibble k=2j,
+                          high nibble k=2j+1); scale bf16 [G][N][K/32];
+                          w = (nibble - 8) * scale [INT4-PR commit text] */
+} moe_wfmt;
+
+/* err_word bits */
+#define MOE_DEVERR_GLOBAL_ID_OOB 0x1 /* a routing id < 0 or >= num_experts_global */
+
+/* Parameterized SwiGLU [CLAMP-PR "Modifications"; OAI-PR "Summary",
+ * "Compatibility"]:
+ *   g' = min(g, limit), u' = clamp(u, -limit, limit),
+ *   h  = g' * sigmoid(alpha * g') * (u' + beta).
+ * Defaults alpha = 1, beta = 0, limit = +INFINITY (no clamp) give
+ * silu(g) * u. alpha and beta must be finite, limit > 0 (may be +inf). */
+typedef struct {
+  float alpha, beta, limit;
+} moe_act_params;
+
+/* One stacked expert weight (W13 = fused [gate | up], or W2 = down). */
+typedef struct {
+  int fmt;              /* moe_wfmt */
+  int n_groups;         /* G: stacked matrices (local experts [+ shared]) */
+  int N, K;             /* each matrix is [N][K]: W13 N = 2I, K = H;
+                           W2 N = H, K = I */
+  const void *q;        /* codes, layout per moe_wfmt */
+  const void *scale;    /* scales, layout per moe_wfmt (NULL for BF16) */
+  const float *gscale;  /* W13 only, nullable: fp32 [G][2] = (gate, up)
+                           per-expert global scales multiplying the dequantised
+                           gate rows 0..I-1 and up rows I..2I-1; the "true
+                           units" of [LORA-AOT "Changes since 1b699bf"] */
+} moe_weights;
+
+/* Rank-r LoRA on the fused gate/up projection of the local experts
+ * [LORA-AOT "Changes since 1b699bf"]:  z = x A_e^T (fp32),
+ * delta = scale * z B_e^T, added to g and u after each half's own global
+ * scale, before the clamp.  A: bf16 [n_groups][rank][H], B: bf16
+ * [n_groups][2I][rank]. The shared expert (group E_loc) carries no LoRA. */
+typedef struct {
+  int rank;             /* 1..32 */
+  int n_groups;         /* adapters for groups 0..n_groups-1 (the local
+                           routed experts); later groups have none */
+  float scale;
+  const void *A;
+  const void *B;
+} moe_lora;
+
+/* ---------------------------------------------------------------- route -- */
+/* Sigmoid-gate top-k with log-sigmoid renormalisation and shared-sink
+ * columns [GATE-PR "2. Correctness", "3. Performance", router-epilogue
+ * commit message]. Per token row t of `logits` (fp32, row stride `ld`
+ * elements, ld >= n_routed + n_sink):
+ *   - top_k passes of masked argmax over the n_routed leading columns,
+ *     ranked on the raw logit (no selection bias: sigmoid is monotone),
+ *     equal logits resolved to the lower column index;
+ *   - lp = logsigmoid of the k winners' raw logits and of the n_sink
+ *     trailing sink columns; w = exp(lp - logsumexp(lp)) * route_scale *
+ *     global_scale (finite when every logit is far below -104).
+ * Outputs: topk_ids int32 [T][top_k] (global column ids, selection order),
+ * topk_w fp32 [T][top_k], sink_w fp32 [T][n_sink] (NULL iff n_sink == 0).
+ * Limits: 1 <= top_k <= n_routed, top_k + n_sink <= 64,
+ * n_routed + n_sink <= 1024, T >= 0. Logits are assumed finite. */
+int moe_route(const float *logits, long T, long ld, int n_routed, int n_sink,
+              int top_k, float route_scale, float global_scale,
+              int *topk_ids, float *topk_w, float *sink_w, void *stream);
+
+/* -------------------------------------------------------------- permute -- */
+/* Expert-parallel rebase and grouping of (token, slot) pairs by local expert
+ * [LORA-AOT "Changes since 1b699bf": ids are global, per-expert tables are
+ * rank-local, rebase by local_expert_offset and bounds-check against the
+ * local count; INT4-PR: per-expert sorted-token dispatch].
+ *   pair id p = t*top_k + j; e = topk_ids[p] - local_expert_offset; the pair
+ *   is local iff 0 <= e < num_local_experts. With shared_expert = 1 an
+ *   always-on group G-1 = num_local_experts holds pairs p = T*top_k + t.
+ *   Groups are laid out in order, pairs inside a group by ascending p.
+ * Outputs: offsets int32 [G+1] (group g owns sorted rows
+ * offsets[g]..offsets[g+1]-1), sorted_pair int32 [P_cap] (pair id of each
+ * sorted row), pair_row int32 [T*top_k + shared*T] (sorted row of each pair
+ * or -1), with P_cap = T*top_k + shared*T and G = num_local_experts +
+ * shared_expert. Ids outside [0, num_experts_global) set
+ * MOE_DEVERR_GLOBAL_ID_OOB in *err_word and are skipped.
+ * Errors: MOE_ERR_LOCAL_RANGE unless num_local_experts >= 1,
+ * local_expert_offset >= 0 and offset + num_local_experts <=
+ * num_experts_global; MOE_ERR_SHAPE if G > 1024 or T*top_k >= 2^30.
+ * Workspace: moe_permute_workspace_size(T, top_k, G) bytes. */
+int moe_permute(const int *topk_ids, long T, int top_k, int num_experts_global,
+                int local_expert_offset, int num_local_experts,
+                int shared_expert, int *offsets, int *sorted_pair,
+                int *pair_row, int *err_word, void *ws, size_t ws_bytes,
+                void *stream);
+size_t moe_permute_workspace_size(long T, int top_k, int n_groups);
+
+/* -------------------------------------------------- activation quantise -- */
+/* Per token and per 128-column group: amax in fp32, s = amax / 448 (s = 1
+ * when amax == 0), q = e4m3fn(round-to-nearest-even(x / s)) saturated to
+ * +-448 [CLAMP-PR "Modifications": the activation side of blockwise FP8].
+ * x bf16 [T][H] -> xq e4m3fn [T][H], xs fp32 [T][H/128]. H % 128 == 0. */
+int moe_quantize_act_fp8(const void *x_bf16, long T, int H, void *xq,
+                         float *xs, void *stream);
+
+/* ------------------------------------------------ grouped GEMM1 + SwiGLU -- */
+/* For each group g and each of its sorted rows r (token t of pair
+ * sorted_pair[r]):  [g | u] = x_t W13_g^T  (fp32 accumulation;
+ * FP8: per 128-K block partial sums times xs[t][kb] * scale[g][nb][kb]),
+ * times gscale[g] (gate, up) when given, plus the LoRA delta when given,
+ * then the parameterized SwiGLU `act` -> h[r][0..I-1].
+ *   FP8 weights: x = xq e4m3fn [T][H] with xs fp32 [T][H/128]; h is
+ *     re-quantised like moe_quantize_act_fp8 per row and 128 columns:
+ *     h e4m3fn [P_cap][I], hs fp32 [P_cap][I/128].
+ *   BF16 / INT4 weights: x bf16 [T][H] (xs NULL); h bf16 [P_cap][I]
+ *     (round-to-nearest-even), hs NULL.
+ * x_bf16 bf16 [T][H] is the LoRA input (NULL without LoRA).
+ * offsets / sorted_pair come from moe_permute for the same (T, top_k);
+ * w13->n_groups = G, w13->N = 2I, w13->K = H. p_cap = rows allocated in h.
+ * Limits: H % 128 == 0 and I % 128 == 0. Workspace:
+ * moe_gemm1_workspace_size(p_cap, lora). */
+int moe_grouped_gemm1_act(const moe_weights *w13, const void *x,
+                          const float *xs, const void *x_bf16, long T, int H,
+                          int I, int top_k, long p_cap, const int *offsets,
+                          const int *sorted_pair, const moe_act_params *act,
+                          const moe_lora *lora, void *h, float *hs, void *ws,
+                          size_t ws_bytes, void *stream);
+size_t moe_gemm1_workspace_size(long p_cap, const moe_lora *lora);
+
+/* ---------------------------------------- grouped GEMM2 + weighted combine -- */
+/* y[r] = h[r] W2_g^T (fp32; FP8 per 128-K block partial sums times
+ * hs[r][kb] * scale[g][nb][kb]) for every sorted row, then
+ *   out[t][:] = sum_{j < top_k, pair_row[t*top_k+j] >= 0} topk_w[t][j] *
+ *               y[pair_row[t*top_k+j]]   (ascending j, fp32)
+ *             + shared_w * y[pair_row[T*top_k + t]]   (if shared_expert)
+ * [INT4-PR: slot-specific routing-weight reduction, fp32 accumulation].
+ * Every out element is written (0 for a token with no local pair).
+ * w2->N = H, w2->K = I. out fp32 [T][H]. Workspace:
+ * moe_gemm2_workspace_size(p_cap, H) (the fp32 y rows). */
+int moe_grouped_gemm2_combine(const moe_weights *w2, const void *h,
+                              const float *hs, long T, int H, int I,
+                              int top_k, int shared_expert, long p_cap,
+                              const int *offsets, const int *pair_row,
+                              const float *topk_w, float shared_w, float *out,
+                              void *ws, size_t ws_bytes, void *stream);
+size_t moe_gemm2_workspace_size(long p_cap, int H);
+
+/* ---------------------------------------------------------- whole layer -- */
+typedef struct {
+  int H, I;
+  int num_experts_global;   /* routed experts E (logit columns 0..E-1) */
+  int num_local_experts;    /* experts held here, global ids
+                               [offset, offset + num_local_experts) */
+  int local_expert_offset;
+  int shared_expert;        /* 0 | 1: always-on group num_local_experts */
+  int top_k, n_sink;        /* n_sink trailing sink logit columns */
+  float route_scale, global_scale, shared_w;
+  moe_weights w13, w2;      /* n_groups = num_local_experts + shared_expert */
+  moe_act_params act;
+  const moe_lora *lora;     /* nullable */
+} moe_layer;
+
+/* One call of the whole path on `stream`: moe_route -> moe_permute ->
+ * (FP8) moe_quantize_act_fp8 -> moe_grouped_gemm1_act ->
+ * moe_grouped_gemm2_combine. x_bf16 bf16 [T][H]; logits fp32 [T][ld_logits]
+ * with ld_logits >= num_experts_global + n_sink. Outputs out fp32 [T][H],
+ * topk_ids/topk_w [T][top_k], sink_w [T][n_sink] (NULL iff n_sink == 0),
+ * err_word as in moe_permute. Workspace: moe_workspace_size(layer, T_max)
+ * bytes, T <= T_max. Errors: those of the steps, checked before any launch. */
+int moe_forward(const moe_layer *layer, const void *x_bf16,
+                const float *logits, long T, long ld_logits, float *out,
+                int *topk_ids, float *topk_w, float *sink_w, int *err_word,
+                void *ws, size_t ws_bytes, void *stream);
+size_t moe_workspace_size(const moe_layer *layer, long T_max);
+
+/* --------------------------------------------------------------- misc -- */
+/* Synchronises `stream`, then copies *err_word (device) to *host_bits. */
+int moe_read_device_error(const int *err_word, int *host_bits, void *stream);
+const char *moe_status_string(int status);
+/* Last HIP error message of the calling thread ("" if none). */
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,412 @@
+// Host side of the C ABI (include/moe_mi355x.h): argument validation,
+// workspace carving and kernel launches. No allocation, no synchronisation
+// (except moe_read_device_error), no state kept between calls apart from the
+// calling thread's last HIP error message.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "common.h"
+#include "launch.h"
+#include "moe_mi355x.h"
+
+static_assert(MOE_DEVERR_GLOBAL_ID_OOB == MOE_DEVERR_BIT_OOB, "err bit");
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int hip_fail(hipError_t e, const char* where) {
+  snprintf(g_last_error, sizeof g_last_error, "%s: %s", where,
+           hipGetErrorString(e));
+  return MOE_ERR_HIP;
+}
+
+inline size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
+inline bool finite(float v) { return isfinite(v); }
+
+int check_weights(const moe_weights* w, int N, int K) {
+  if (!w || !w->q) return MOE_ERR_NULL;
+  if (w->fmt != MOE_W_BF16 && w->fmt != MOE_W_FP8_B128 && w->fmt != MOE_W_INT4_G32)
+    return MOE_ERR_FORMAT;
+  if (w->fmt != MOE_W_BF16 && !w->scale) return MOE_ERR_NULL;
+  if (w->N != N || w->K != K) return MOE_ERR_SHAPE;
+  if (w->n_groups < 1 || w->n_groups > 1024) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+int check_act(const moe_act_params* a) {
+  if (!a) return MOE_ERR_NULL;
+  if (!finite(a->alpha) || !finite(a->beta) || !(a->limit > 0.0f))
+    return MOE_ERR_PARAM;
+  return MOE_OK;
+}
+
+int check_lora(const moe_lora* l, int G) {
+  if (!l) return MOE_OK;
+  if (!l->A || !l->B) return MOE_ERR_NULL;
+  if (l->rank < 1 || l->rank > 32) return MOE_ERR_SHAPE;
+  if (l->n_groups < 0 || l->n_groups > G) return MOE_ERR_SHAPE;
+  if (!finite(l->scale)) return MOE_ERR_PARAM;
+  return MOE_OK;
+}
+
+long pcap_of(long T, int k, int shared) { return T * (long)k + (shared ? T : 0); }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "required pointer is NULL";
+    case MOE_ERR_SHAPE: return "size out of range or not a required multiple";
+    case MOE_ERR_FORMAT: return "unknown or mismatched weight format";
+    case MOE_ERR_LOCAL_RANGE: return "missing or invalid local expert range";
+    case MOE_ERR_PARAM: return "non-finite or out-of-range parameter";
+    case MOE_ERR_WORKSPACE: return "workspace NULL or too small";
+    case MOE_ERR_HIP: return "HIP launch or runtime failure";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error; }
+
+int moe_route(const float* logits, long T, long ld, int n_routed, int n_sink,
+              int top_k, float route_scale, float global_scale, int* topk_ids,
+              float* topk_w, float* sink_w, void* stream) {
+  if (T < 0 || n_routed < 1 || n_sink < 0 || top_k < 1 || top_k > n_routed ||
+      top_k + n_sink > 64 || n_routed + n_sink > 1024 || ld < n_routed + n_sink)
+    return MOE_ERR_SHAPE;
+  if (!finite(route_scale) || !finite(global_scale)) return MOE_ERR_PARAM;
+  if (T > 0 && (!logits || !topk_ids || !topk_w || (n_sink > 0 && !sink_w)))
+    return MOE_ERR_NULL;
+  hipError_t e = moe::launch_route(logits, T, ld, n_routed, n_sink, top_k,
+                                   route_scale * global_scale, topk_ids,
+                                   topk_w, sink_w, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_route");
+}
+
+size_t moe_permute_workspace_size(long T, int top_k, int n_groups) {
+  if (T < 0 || top_k < 1 || n_groups < 1) return 0;
+  return moe::permute_ws_bytes(T, top_k, n_groups);
+}
+
+static int permute_checks(long T, int top_k, int E, int off, int E_loc,
+                          int shared) {
+  if (T < 0 || top_k < 1) return MOE_ERR_SHAPE;
+  if (E_loc < 1 || off < 0 || (long)off + E_loc > E) return MOE_ERR_LOCAL_RANGE;
+  if (shared != 0 && shared != 1) return MOE_ERR_PARAM;
+  if (E_loc + shared > 1024) return MOE_ERR_SHAPE;
+  if (T * (long)top_k >= (1L << 30)) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+int moe_permute(const int* topk_ids, long T, int top_k, int num_experts_global,
+                int local_expert_offset, int num_local_experts,
+                int shared_expert, int* offsets, int* sorted_pair,
+                int* pair_row, int* err_word, void* ws, size_t ws_bytes,
+                void* stream) {
+  int st = permute_checks(T, top_k, num_experts_global, local_expert_offset,
+                          num_local_experts, shared_expert);
+  if (st) return st;
+  long np = pcap_of(T, top_k, shared_expert);
+  if (!offsets || !err_word || (T > 0 && !topk_ids) ||
+      (np > 0 && (!sorted_pair || !pair_row)))
+    return MOE_ERR_NULL;
+  int G = num_local_experts + shared_expert;
+  if (!ws || ws_bytes < moe::permute_ws_bytes(T, top_k, G))
+    return MOE_ERR_WORKSPACE;
+  hipError_t e = moe::launch_permute(
+      topk_ids, T, top_k, num_experts_global, local_expert_offset,
+      num_local_experts, shared_expert, offsets, sorted_pair, pair_row,
+      err_word, ws, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_permute");
+}
+
+int moe_quantize_act_fp8(const void* x_bf16, long T, int H, void* xq,
+                         float* xs, void* stream) {
+  if (T < 0 || H < 128 || H % 128) return MOE_ERR_SHAPE;
+  if (T > 0 && (!x_bf16 || !xq || !xs)) return MOE_ERR_NULL;
+  hipError_t e = moe::launch_quant_act(x_bf16, T, H, xq, xs, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_quantize_act_fp8");
+}
+
+size_t moe_gemm1_workspace_size(long p_cap, const moe_lora* lora) {
+  if (p_cap < 0) return 0;
+  return lora ? al((size_t)p_cap * lora->rank * 4) : 0;
+}
+
+static int gemm1_checks(const moe_weights* w13, const void* x, const float* xs,
+                        const void* x_bf16, long T, int H, int I, int top_k,
+                        long p_cap, const int* offsets, const int* sorted_pair,
+                        const moe_act_params* act, const moe_lora* lora,
+                        const void* h, const float* hs) {
+  if (T < 0 || p_cap < 0 || top_k < 1) return MOE_ERR_SHAPE;
+  if (H < 128 || I < 128 || H % 128 || I % 128) return MOE_ERR_SHAPE;
+  int st = check_weights(w13, 2 * I, H);
+  if (st) return st;
+  if ((st = check_act(act))) return st;
+  if ((st = check_lora(lora, w13->n_groups))) return st;
+  if (!offsets || (p_cap > 0 && (!x || !sorted_pair || !h))) return MOE_ERR_NULL;
+  if (w13->fmt == MOE_W_FP8_B128 && p_cap > 0 && (!xs || !hs)) return MOE_ERR_NULL;
+  if (lora && p_cap > 0 && !x_bf16) return MOE_ERR_NULL;
+  return MOE_OK;
+}
+
+static moe::Gemm1Args gemm1_args(const moe_weights* w13, const void* x,
+                                 const float* xs, long T, int H, int I,
+                                 int top_k, long p_cap, const int* offsets,
+                                 const int* sorted_pair,
+                                 const moe_act_params* act,
+                                 const moe_lora* lora, const float* z, void* h,
+                                 float* hs) {
+  moe::Gemm1Args a{};
+  a.fmt = w13->fmt;
+  a.wq = w13->q;
+  a.ws = w13->scale;
+  a.gscale = w13->gscale;
+  a.x = x;
+  a.xs = xs;
+  a.T = T;
+  a.H = H;
+  a.I = I;
+  a.top_k = top_k;
+  a.G = w13->n_groups;
+  a.p_cap = p_cap;
+  a.offsets = offsets;
+  a.sorted_pair = sorted_pair;
+  a.alpha = act->alpha;
+  a.beta = act->beta;
+  a.limit = act->limit;
+  a.z = lora ? z : nullptr;
+  a.lora_B = lora ? lora->B : nullptr;
+  a.lora_rank = lora ? lora->rank : 0;
+  a.lora_groups = lora ? lora->n_groups : 0;
+  a.lora_scale = lora ? lora->scale : 0.0f;
+  a.h = h;
+  a.hs = hs;
+  return a;
+}
+
+int moe_grouped_gemm1_act(const moe_weights* w13, const void* x,
+                          const float* xs, const void* x_bf16, long T, int H,
+                          int I, int top_k, long p_cap, const int* offsets,
+                          const int* sorted_pair, const moe_act_params* act,
+                          const moe_lora* lora, void* h, float* hs, void* ws,
+                          size_t ws_bytes, void* stream) {
+  int st = gemm1_checks(w13, x, xs, x_bf16, T, H, I, top_k, p_cap, offsets,
+                        sorted_pair, act, lora, h, hs);
+  if (st) return st;
+  size_t need = moe_gemm1_workspace_size(p_cap, lora);
+  if (need && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  float* z = (float*)ws;
+  hipError_t e = hipSuccess;
+  if (lora)
+    e = moe::launch_lora_z(x_bf16, lora->A, lora->rank, T, H, top_k,
+                           lora->n_groups, p_cap, offsets, sorted_pair, z, s);
+  if (e == hipSuccess)
+    e = moe::launch_gemm1(gemm1_args(w13, x, xs, T, H, I, top_k, p_cap, offsets,
+                                     sorted_pair, act, lora, z, h, hs), s);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_grouped_gemm1_act");
+}
+
+size_t moe_gemm2_workspace_size(long p_cap, int H) {
+  if (p_cap < 0 || H < 0) return 0;
+  return al((size_t)p_cap * H * 4);
+}
+
+static int gemm2_checks(const moe_weights* w2, const void* h, const float* hs,
+                        long T, int H, int I, int top_k, int shared,
+                        long p_cap, const int* offsets, const int* pair_row,
+                        const float* topk_w, float shared_w, const float* out) {
+  if (T < 0 || p_cap < 0 || top_k < 1) return MOE_ERR_SHAPE;
+  if (H < 128 || I < 128 || H % 128 || I % 128) return MOE_ERR_SHAPE;
+  if (shared != 0 && shared != 1) return MOE_ERR_PARAM;
+  if (!finite(shared_w)) return MOE_ERR_PARAM;
+  int st = check_weights(w2, H, I);
+  if (st) return st;
+  if (!offsets) return MOE_ERR_NULL;
+  if (p_cap > 0 && (!h || (w2->fmt == MOE_W_FP8_B128 && !hs))) return MOE_ERR_NULL;
+  if (T > 0 && (!out || !pair_row || !topk_w)) return MOE_ERR_NULL;
+  if (p_cap < pcap_of(T, top_k, shared) && T > 0) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+int moe_grouped_gemm2_combine(const moe_weights* w2, const void* h,
+                              const float* hs, long T, int H, int I, int top_k,
+                              int shared_expert, long p_cap, const int* offsets,
+                              const int* pair_row, const float* topk_w,
+                              float shared_w, float* out, void* ws,
+                              size_t ws_bytes, void* stream) {
+  int st = gemm2_checks(w2, h, hs, T, H, I, top_k, shared_expert, p_cap,
+                        offsets, pair_row, topk_w, shared_w, out);
+  if (st) return st;
+  size_t need = moe_gemm2_workspace_size(p_cap, H);
+  if (need && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  float* y = (float*)ws;
+  moe::Gemm2Args a{};
+  a.fmt = w2->fmt;
+  a.wq = w2->q;
+  a.ws = w2->scale;
+  a.h = h;
+  a.hs = hs;
+  a.H = H;
+  a.I = I;
+  a.G = w2->n_groups;
+  a.p_cap = p_cap;
+  a.offsets = offsets;
+  a.y = y;
+  hipError_t e = moe::launch_gemm2(a, s);
+  if (e == hipSuccess)
+    e = moe::launch_combine(y, T, H, top_k, shared_expert, pair_row, topk_w,
+                            shared_w, out, s);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_grouped_gemm2_combine");
+}
+
+// ---------------------------------------------------------------- forward --
+
+namespace {
+struct FwdLayout {
+  size_t offsets, sorted_pair, pair_row, perm_ws, xq, xs, z, h, hs, y, total;
+  size_t perm_bytes;
+};
+
+FwdLayout layout(const moe_layer* L, long T) {
+  FwdLayout o{};
+  int G = L->num_local_experts + L->shared_expert;
+  long pc = pcap_of(T, L->top_k, L->shared_expert);
+  bool fp8 = L->w13.fmt == MOE_W_FP8_B128;
+  size_t cur = 0;
+  auto take = [&](size_t bytes) { size_t at = cur; cur += al(bytes); return at; };
+  o.offsets = take((size_t)(G + 1) * 4);
+  o.sorted_pair = take((size_t)pc * 4);
+  o.pair_row = take((size_t)pc * 4);
+  o.perm_bytes = moe::permute_ws_bytes(T, L->top_k, G);
+  o.perm_ws = take(o.perm_bytes);
+  o.xq = take(fp8 ? (size_t)T * L->H : 0);
+  o.xs = take(fp8 ? (size_t)T * (L->H / 128) * 4 : 0);
+  o.z = take(L->lora ? (size_t)pc * L->lora->rank * 4 : 0);
+  o.h = take((size_t)pc * L->I * (fp8 ? 1 : 2));
+  o.hs = take(fp8 ? (size_t)pc * (L->I / 128) * 4 : 0);
+  o.y = take((size_t)pc * L->H * 4);
+  o.total = cur;
+  return o;
+}
+
+int layer_checks(const moe_layer* L) {
+  if (!L) return MOE_ERR_NULL;
+  if (L->H < 128 || L->I < 128 || L->H % 128 || L->I % 128) return MOE_ERR_SHAPE;
+  int st = permute_checks(0, L->top_k, L->num_experts_global,
+                          L->local_expert_offset, L->num_local_experts,
+                          L->shared_expert);
+  if (st) return st;
+  int G = L->num_local_experts + L->shared_expert;
+  if ((st = check_weights(&L->w13, 2 * L->I, L->H))) return st;
+  if ((st = check_weights(&L->w2, L->H, L->I))) return st;
+  if (L->w13.n_groups != G || L->w2.n_groups != G) return MOE_ERR_SHAPE;
+  if (L->w13.fmt != L->w2.fmt) return MOE_ERR_FORMAT;
+  if ((st = check_act(&L->act))) return st;
+  if ((st = check_lora(L->lora, G))) return st;
+  if (L->lora && L->lora->n_groups > L->num_local_experts) return MOE_ERR_SHAPE;
+  if (L->n_sink < 0 || L->top_k > L->num_experts_global ||
+      L->top_k + L->n_sink > 64 || L->num_experts_global + L->n_sink > 1024)
+    return MOE_ERR_SHAPE;
+  if (!finite(L->route_scale) || !finite(L->global_scale) || !finite(L->shared_w))
+    return MOE_ERR_PARAM;
+  return MOE_OK;
+}
+}  // namespace
+
+size_t moe_workspace_size(const moe_layer* layer, long T_max) {
+  if (!layer || T_max < 0 || layer_checks(layer) != MOE_OK) return 0;
+  return layout(layer, T_max).total;
+}
+
+int moe_forward(const moe_layer* L, const void* x_bf16, const float* logits,
+                long T, long ld_logits, float* out, int* topk_ids,
+                float* topk_w, float* sink_w, int* err_word, void* ws,
+                size_t ws_bytes, void* stream) {
+  int st = layer_checks(L);
+  if (st) return st;
+  if (T < 0) return MOE_ERR_SHAPE;
+  if (ld_logits < L->num_experts_global + L->n_sink) return MOE_ERR_SHAPE;
+  if (!err_word) return MOE_ERR_NULL;
+  if (T > 0 && (!x_bf16 || !logits || !out || !topk_ids || !topk_w ||
+                (L->n_sink > 0 && !sink_w)))
+    return MOE_ERR_NULL;
+  if (T * (long)L->top_k >= (1L << 30)) return MOE_ERR_SHAPE;
+  FwdLayout o = layout(L, T);
+  if (!ws || ws_bytes < o.total) return MOE_ERR_WORKSPACE;
+  char* base = (char*)ws;
+  hipStream_t s = (hipStream_t)stream;
+  const int G = L->num_local_experts + L->shared_expert;
+  const long pc = pcap_of(T, L->top_k, L->shared_expert);
+  int* offsets = (int*)(base + o.offsets);
+  int* sorted_pair = (int*)(base + o.sorted_pair);
+  int* pair_row = (int*)(base + o.pair_row);
+  const bool fp8 = L->w13.fmt == MOE_W_FP8_B128;
+  void* xq = base + o.xq;
+  float* xs = (float*)(base + o.xs);
+  float* z = (float*)(base + o.z);
+  void* h = base + o.h;
+  float* hs = (float*)(base + o.hs);
+  float* y = (float*)(base + o.y);
+
+  hipError_t e = moe::launch_route(logits, T, ld_logits, L->num_experts_global,
+                                   L->n_sink, L->top_k,
+                                   L->route_scale * L->global_scale, topk_ids,
+                                   topk_w, sink_w, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_forward/route");
+  e = moe::launch_permute(topk_ids, T, L->top_k, L->num_experts_global,
+                          L->local_expert_offset, L->num_local_experts,
+                          L->shared_expert, offsets, sorted_pair, pair_row,
+                          err_word, base + o.perm_ws, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_forward/permute");
+  if (fp8) {
+    e = moe::launch_quant_act(x_bf16, T, L->H, xq, xs, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_forward/quant");
+  }
+  if (L->lora) {
+    e = moe::launch_lora_z(x_bf16, L->lora->A, L->lora->rank, T, L->H,
+                           L->top_k, L->lora->n_groups, pc, offsets,
+                           sorted_pair, z, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_forward/lora_z");
+  }
+  e = moe::launch_gemm1(gemm1_args(&L->w13, fp8 ? xq : x_bf16, fp8 ? xs : nullptr,
+                                   T, L->H, L->I, L->top_k, pc, offsets,
+                                   sorted_pair, &L->act, L->lora, z, h,
+                                   fp8 ? hs : nullptr), s);
+  if (e != hipSuccess) return hip_fail(e, "moe_forward/gemm1");
+  moe::Gemm2Args a{};
+  a.fmt = L->w2.fmt;
+  a.wq = L->w2.q;
+  a.ws = L->w2.scale;
+  a.h = h;
+  a.hs = fp8 ? hs : nullptr;
+  a.H = L->H;
+  a.I = L->I;
+  a.G = G;
+  a.p_cap = pc;
+  a.offsets = offsets;
+  a.y = y;
+  e = moe::launch_gemm2(a, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_forward/gemm2");
+  e = moe::launch_combine(y, T, L->H, L->top_k, L->shared_expert, pair_row,
+                          topk_w, L->shared_w, out, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_forward/combine");
+  return MOE_OK;
+}
+
+int moe_read_device_error(const int* err_word, int* host_bits, void* stream) {
+  if (!err_word || !host_bits) return MOE_ERR_NULL;
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e == hipSuccess)
+    e = hipMemcpy(host_bits, err_word, sizeof(int), hipMemcpyDeviceToHost);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_read_device_error");
+}
+
+}  // extern "C"

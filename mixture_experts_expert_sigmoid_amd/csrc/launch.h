@@ -1,0 +1,71 @@
+// Internal kernel launchers (host side), one per step of the path. The
+// public C ABI in api.hip validates arguments and calls these.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_route(const float* logits, long T, long ld, int n_routed,
+                        int n_sink, int k, float scale, int* ids, float* w,
+                        float* sw, hipStream_t s);
+
+// permute: rank/count, scan, scatter (three launches)
+constexpr int kPermBlock = 1024;
+size_t permute_ws_bytes(long T, int k, int G);
+hipError_t launch_permute(const int* ids, long T, int k, int E_global, int off,
+                          int E_loc, int shared, int* offsets,
+                          int* sorted_pair, int* pair_row, int* err_word,
+                          void* ws, hipStream_t s);
+
+hipError_t launch_quant_act(const void* x, long T, int H, void* xq, float* xs,
+                            hipStream_t s);
+
+// z[r][q] = sum_h x[t(r)][h] * A[g(r)][q][h] for every sorted row of a
+// local group (fp32)
+hipError_t launch_lora_z(const void* x_bf16, const void* A, int rank, long T,
+                         int H, int top_k, int n_lora_groups, long p_cap,
+                         const int* offsets, const int* sorted_pair, float* z,
+                         hipStream_t s);
+
+struct Gemm1Args {
+  int fmt;
+  const void* wq;
+  const void* ws;
+  const float* gscale;
+  const void* x;
+  const float* xs;
+  long T;
+  int H, I, top_k, G;
+  long p_cap;
+  const int* offsets;
+  const int* sorted_pair;
+  float alpha, beta, limit;
+  const float* z;        // LoRA z rows [p_cap][rank] or NULL
+  const void* lora_B;    // bf16 [E_loc][2I][rank]
+  int lora_rank, lora_groups;
+  float lora_scale;
+  void* h;
+  float* hs;
+};
+hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t s);
+
+struct Gemm2Args {
+  int fmt;
+  const void* wq;
+  const void* ws;
+  const void* h;
+  const float* hs;
+  int H, I, G;
+  long p_cap;
+  const int* offsets;
+  float* y;              // [p_cap][H] fp32
+};
+hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t s);
+
+hipError_t launch_combine(const float* y, long T, int H, int top_k, int shared,
+                          const int* pair_row, const float* topk_w,
+                          float shared_w, float* out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,100 @@
+// Router epilogue: sigmoid-gate top-k with log-sigmoid renormalisation and
+// trailing shared-sink columns.
+//
+// "Enable and fuse the Inkling MoE gate epilogue on Intel XPU" (sglang PR
+// #36385): "3. Performance" ranks with iterative masked-max passes instead
+// of a sort; "2. Correctness" normalises as exp(lp - logsumexp(lp)) with
+// lp = logsigmoid(x) so rows whose logits are all below the fp32 sigmoid
+// flush point stay finite; the router-epilogue commit message carries the
+// winner's raw logit out of the top-k loop and lets the sink columns join
+// the normaliser only.
+//
+// One wave64 owns one token row. Lane l holds columns l, l + 64, ... of the
+// routed part in registers; each pass reduces (value, column) across the wave
+// with a butterfly, the owner lane marks the winner taken. Equal values
+// resolve to the lower column. After k passes lane j < k holds slot j's raw
+// logit and lanes k .. k+S-1 the sink logits; the renormalisation is a wave
+// max and a wave sum.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+template <int NV>
+__global__ __launch_bounds__(256) void route_kernel(
+    const float* __restrict__ logits, long T, long ld, int n_routed,
+    int n_sink, int k, float scale, int* __restrict__ ids,
+    float* __restrict__ w, float* __restrict__ sw) {
+  const int lane = lane_id();
+  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= T) return;
+  const float* x = logits + row * ld;
+
+  float v[NV];
+  uint32_t taken = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    int c = lane + 64 * i;
+    v[i] = (c < n_routed) ? x[c] : 0.0f;
+    if (c >= n_routed) taken |= 1u << i;   // not a candidate
+  }
+
+  float my_x = -INFINITY;   // raw logit of the slot / sink this lane reports
+  int my_c = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bc = 0x7FFFFFFF;       // no candidate yet
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      int c = lane + 64 * i;
+      bool cand = !((taken >> i) & 1u);
+      if (cand && (v[i] > bv || (v[i] == bv && c < bc))) { bv = v[i]; bc = c; }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      float ov = __shfl_xor(bv, o, kWave);
+      int oc = __shfl_xor(bc, o, kWave);
+      if (ov > bv || (ov == bv && oc < bc)) { bv = ov; bc = oc; }
+    }
+    if ((bc & 63) == lane) taken |= 1u << (bc >> 6);
+    if (lane == j) { my_x = bv; my_c = bc; }
+  }
+  const bool active = lane < k + n_sink;
+  if (lane >= k && active) my_x = x[n_routed + (lane - k)];
+
+  // lp = logsigmoid(x) = min(x, 0) - log1p(exp(-|x|));
+  // exp(lp - logsumexp(lp)) evaluated as e / sum(e) with e = exp(lp - max lp):
+  // lp - max is exact for nearby lp, so rows far below zero (lp ~ -200) keep
+  // full fp32 relative accuracy instead of inheriting the rounding of a
+  // logsumexp formed at magnitude ~200.
+  float lp = active ? fminf(my_x, 0.0f) - log1pf(expf(-fabsf(my_x))) : -INFINITY;
+  float m = wave_max(lp);
+  float e = active ? expf(lp - m) : 0.0f;
+  float wt = e / wave_sum(e) * scale;
+  if (lane < k) {
+    ids[row * k + lane] = my_c;
+    w[row * k + lane] = wt;
+  } else if (active) {
+    sw[row * n_sink + (lane - k)] = wt;
+  }
+}
+
+hipError_t launch_route(const float* logits, long T, long ld, int n_routed,
+                        int n_sink, int k, float scale, int* ids, float* w,
+                        float* sw, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  dim3 grid((unsigned)((T + 3) / 4)), block(256);
+  int nv = (n_routed + 63) / 64;
+#define RT(NV)                                                                \
+  hipLaunchKernelGGL(route_kernel<NV>, grid, block, 0, s, logits, T, ld,      \
+                     n_routed, n_sink, k, scale, ids, w, sw)
+  if (nv <= 1) RT(1);
+  else if (nv <= 2) RT(2);
+  else if (nv <= 4) RT(4);
+  else if (nv <= 8) RT(8);
+  else RT(16);
+#undef RT
+  return hipGetLastError();
+}
+
+}  // namespace moe

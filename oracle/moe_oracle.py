@@ -316,24 +316,108 @@ def lora_delta(spec, arr, e, x_bf16_rows):
     return float(np.float32(spec.lora_scale)) * (z @ B.T)
 
 
-def expert_ffn(spec, arr, e, xhat_rows, x_bf16_rows):
+# ----------------------------------------------------------------------------
+# rounding decisions of h taken from an fp32 kernel
+# ----------------------------------------------------------------------------
+# The quantised code of h (FP8 layers) or its bf16 rounding is an integer
+# decided by floating point. A kernel that forms g and u with fp32 sums of
+# exact products reaches h only to within a small error, so where the exact h
+# lies within that error of a rounding boundary both neighbouring codes are
+# correct results. These constants bound the kernel-side error used to find
+# such boundary elements (they widen the set of admissible results; they do
+# not change the oracle's own value):
+ACC_REL = 2e-6     # |fp32 sum - exact| <= ACC_REL * sum |terms| (g, u, delta)
+EVAL_REL = 2e-6    # relative error of the fp32 SwiGLU evaluation and of s
+
+
+def swiglu_slopes(g, u, alpha=1.0, beta=0.0, limit=math.inf):
+    """|dh/dg|, |dh/du| (one-sided bounds at the clamps)."""
+    gp = np.minimum(g, limit)
+    up = np.clip(u, -limit, limit)
+    sg = sigmoid(alpha * gp)
+    dg = np.abs(sg * (1.0 + alpha * gp * (1.0 - sg)) * (up + beta))
+    du = np.abs(gp * sg)
+    return dg, du
+
+
+def _e4m3_neighbours(codes):
+    """Magnitudes of the next smaller / larger e4m3 values (0 at the ends)."""
+    c = np.asarray(codes, np.int64) & 0x7F
+    lo = np.where(c > 0, np.abs(e4m3_decode(np.maximum(c - 1, 0))), 0.0)
+    hi = np.where(c < 0x7E, np.abs(e4m3_decode(np.minimum(c + 1, 0x7E))), 0.0)
+    return lo, hi
+
+
+def rounding_alternatives(h, err_h, fmt, group=128):
+    """For every h element whose exact value lies within err_h of a rounding
+    boundary, a bound on |admissible rounded value - oracle's rounded value|
+    (every rounding of a value in [h - err_h, h + err_h] is admissible:
+    one step plus twice the error); 0 for every other element."""
+    h = np.asarray(h, np.float64)
+    if fmt == "fp8":
+        P, I = h.shape
+        hg = h.reshape(P, I // group, group)
+        amax = np.abs(hg).max(axis=2).astype(np.float32) if P else \
+            np.zeros((0, I // group), np.float32)
+        s = np.where(amax > 0, amax / np.float32(E4M3_MAX),
+                     np.float32(1.0)).astype(np.float32).astype(np.float64)
+        v = np.abs(hg / s[:, :, None])
+        ev = np.asarray(err_h, np.float64).reshape(P, I // group, group) / s[:, :, None] \
+            + v * EVAL_REL
+        q = e4m3_round(v)
+        qv = np.abs(e4m3_decode(q))
+        lo, hi = _e4m3_neighbours(q)
+        near_lo = (q & 0x7F) > 0
+        near_lo &= (v - (qv + lo) / 2) <= ev
+        near_hi = ((q & 0x7F) < 0x7E) & (((qv + hi) / 2 - v) <= ev)
+        step = np.maximum(np.where(near_lo, qv - lo, 0.0), np.where(near_hi, hi - qv, 0.0))
+        alt = np.where(near_lo | near_hi, step + 2.0 * ev, 0.0)
+        return (alt * s[:, :, None]).reshape(P, I)
+    # bf16 grid: spacing 2^(e-7) for |h| in [2^e, 2^(e+1))
+    a = np.abs(h)
+    _, ex = np.frexp(np.where(a == 0, 1.0, a))
+    ulp = np.ldexp(1.0, (ex - 8).astype(np.int32))
+    r = bf16_round(a)
+    dist = ulp / 2 - np.abs(a - r)
+    e = np.asarray(err_h) + a * EVAL_REL
+    return np.where(dist <= e, ulp + 2.0 * e, 0.0)
+
+
+def expert_ffn(spec, arr, e, xhat_rows, x_bf16_rows, detail=False):
     """y = round_h(swiglu(g, u)) W2_e^T for the rows of one group.
     xhat_rows are the GEMM1 input values (fp8-dequantised for FP8 layers,
-    the bf16 values otherwise); x_bf16_rows feed the LoRA input."""
+    the bf16 values otherwise); x_bf16_rows feed the LoRA input.
+    detail=True also returns the bound on y from boundary rounding decisions
+    of h (see rounding_alternatives) and the intermediates."""
     I = spec.I
     w13 = w13_dequant(spec, arr, e)
     gu = xhat_rows @ w13.T                         # [m, 2I]
     g, u = gu[:, :I].copy(), gu[:, I:].copy()
-    if spec.lora_rank and e < spec.n_local:
+    lora = spec.lora_rank and e < spec.n_local
+    if lora:
         d = lora_delta(spec, arr, e, x_bf16_rows)
         g += d[:, :I]
         u += d[:, I:]
     f32 = lambda v: float(np.float32(v))
-    h = swiglu(g, u, f32(spec.alpha), f32(spec.beta), f32(spec.limit))
+    al, be, L = f32(spec.alpha), f32(spec.beta), f32(spec.limit)
+    h = swiglu(g, u, al, be, L)
     hhat = requant_fp8(h) if spec.fmt == "fp8" else bf16_round(h)
     w2 = dequant(spec.fmt, arr["w2_q"][e],
                  None if arr["w2_s"] is None else arr["w2_s"][e])
-    return hhat @ w2.T                             # [m, H]
+    y = hhat @ w2.T                                # [m, H]
+    if not detail:
+        return y
+    mag = np.abs(xhat_rows) @ np.abs(w13).T
+    if lora:
+        A = np.abs(bf16_decode(arr["lora_A"][e]))
+        B = np.abs(bf16_decode(arr["lora_B"][e]))
+        mag = mag + abs(spec.lora_scale) * ((np.abs(x_bf16_rows) @ A.T) @ B.T)
+    dg, du = swiglu_slopes(g, u, al, be, L)
+    err_h = ACC_REL * (dg * mag[:, :I] + du * mag[:, I:]) + EVAL_REL * np.abs(h)
+    alt = rounding_alternatives(h, err_h, spec.fmt)
+    y_allow = alt @ np.abs(w2).T
+    return y, dict(h=h, hhat=hhat, alt=alt, y_allow=y_allow,
+                   n_boundary=int(np.count_nonzero(alt)))
 
 
 def gemm1_input(spec, x_bits):
@@ -346,12 +430,16 @@ def gemm1_input(spec, x_bits):
     return x, x
 
 
-def moe_layer(spec, arr, x_bits, logits, tokens=None, routing=None):
+def moe_layer(spec, arr, x_bits, logits, tokens=None, routing=None,
+              with_allowance=False):
     """Output rows out[t, :] (float64) for the tokens asked for (all by
     default): route, rebase, per-expert FFN, then for each token
     sum_j w[t, j] y[t, j] over its local slots in ascending j, plus
     shared_w * y_shared last. `arr` maps array names to per-group indexable
-    arrays (a dict of full arrays, or lazy accessors)."""
+    arrays (a dict of full arrays, or lazy accessors).
+    with_allowance=True also returns, per output element, the largest change
+    that boundary rounding decisions of h (either neighbour admissible) can
+    make: sum_j |w[t, j]| * |alt_h| |W2|^T, and the count of such elements."""
     T = x_bits.shape[0]
     if routing is None:
         routing = route(logits, spec.n_routed, spec.n_sink, spec.top_k,
@@ -367,20 +455,34 @@ def moe_layer(spec, arr, x_bits, logits, tokens=None, routing=None):
         if spec.shared:
             pairs.setdefault(spec.n_local, []).append((i, -1))
     xhat, xb = gemm1_input(spec, x_bits[tokens])
-    contrib = {}
+    contrib, allow = {}, {}
+    n_boundary = 0
     for e in sorted(pairs):
         rows = [i for i, _ in pairs[e]]
-        y = expert_ffn(spec, arr, e, xhat[rows], xb[rows])
+        if with_allowance:
+            y, det = expert_ffn(spec, arr, e, xhat[rows], xb[rows], detail=True)
+            n_boundary += det["n_boundary"]
+            for (i, j), arow in zip(pairs[e], det["y_allow"]):
+                allow[(i, j)] = arow
+        else:
+            y = expert_ffn(spec, arr, e, xhat[rows], xb[rows])
         for (i, j), yrow in zip(pairs[e], y):
             contrib[(i, j)] = yrow
     out = np.zeros((len(tokens), spec.H))
+    out_allow = np.zeros((len(tokens), spec.H))
     sw = float(np.float32(spec.shared_w))
     for i, t in enumerate(tokens):
         acc = np.zeros(spec.H)
         for j in range(spec.top_k):
             if (i, j) in contrib:
                 acc = acc + w[t, j] * contrib[(i, j)]
+                if with_allowance:
+                    out_allow[i] += abs(w[t, j]) * allow[(i, j)]
         if (i, -1) in contrib:
             acc = acc + sw * contrib[(i, -1)]
+            if with_allowance:
+                out_allow[i] += abs(sw) * allow[(i, -1)]
         out[i] = acc
+    if with_allowance:
+        return out, out_allow, n_boundary
     return out

@@ -1,0 +1,121 @@
+"""The C-ABI library loads, exports every symbol the header declares, and its
+host-side validation rejects bad arguments before touching the device
+(no GPU needed: every call here returns before any HIP call)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import mixture_experts_expert_sigmoid_amd as M
+
+pytestmark = pytest.mark.skipif(not os.path.exists(M.LIB_PATH),
+                                reason="library not built")
+
+
+def _declared():
+    src = open(M.HEADER_PATH).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert "moe_forward" in names and "moe_route" in names
+    L = ctypes.CDLL(M.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    # the spec entry points are all there
+    for n in ("moe_route", "moe_permute", "moe_grouped_gemm1_act",
+              "moe_grouped_gemm2_combine", "moe_forward"):
+        assert n in names
+
+
+def test_binding_covers_every_declared_symbol():
+    for n in _declared():
+        assert n in M._SIGS, n
+
+
+def _w(fmt=M.MOE_W_FP8_B128, G=4, N=256, K=256, q=1, s=1):
+    return M.MoeWeights(fmt, G, N, K, q, s, None)
+
+
+def test_route_validation():
+    L = M.lib()
+    f = lambda *a: L.moe_route(*a)
+    # top_k > n_routed, top_k + n_sink > 64, ld too small, T < 0
+    assert f(1, 4, 8, 8, 0, 9, 1.0, 1.0, 1, 1, None, None) == -2
+    assert f(1, 4, 100, 60, 8, 60, 1.0, 1.0, 1, 1, 1, None) == -2
+    assert f(1, 4, 7, 8, 0, 2, 1.0, 1.0, 1, 1, None, None) == -2
+    assert f(1, -1, 8, 8, 0, 2, 1.0, 1.0, 1, 1, None, None) == -2
+    assert f(1, 4, 8, 8, 0, 2, math.nan, 1.0, 1, 1, None, None) == -5
+    assert f(None, 4, 8, 8, 0, 2, 1.0, 1.0, 1, 1, None, None) == -1
+    assert f(1, 4, 10, 8, 2, 2, 1.0, 1.0, 1, 1, None, None) == -1   # sinks need sink_w
+
+
+def test_permute_validation_local_range():
+    L = M.lib()
+    ws = ctypes.c_void_p(1)
+    # missing / invalid local range is an error, not a silent out-of-bounds read
+    assert L.moe_permute(1, 4, 8, 256, 96, 0, 0, 1, 1, 1, 1, ws, 1 << 20, None) == -4
+    assert L.moe_permute(1, 4, 8, 256, -1, 32, 0, 1, 1, 1, 1, ws, 1 << 20, None) == -4
+    assert L.moe_permute(1, 4, 8, 256, 240, 32, 0, 1, 1, 1, 1, ws, 1 << 20, None) == -4
+    assert L.moe_permute(1, 4, 8, 256, 96, 32, 0, 1, 1, 1, 1, None, 0, None) == -6
+    assert L.moe_permute(1, 4, 8, 256, 96, 32, 0, 1, 1, 1, 1, ws, 16, None) == -6
+    assert L.moe_permute(1, 4, 8, 2048, 0, 1100, 0, 1, 1, 1, 1, ws, 1 << 20, None) == -2
+    assert L.moe_permute_workspace_size(4096, 8, 289) > 4096 * 8 * 4
+
+
+def test_gemm_validation():
+    L = M.lib()
+    act = M.act_params(1.0, 0.0, math.inf)
+    w = _w(N=2 * 128, K=256)
+    g1 = lambda w_, act_, H=256, I=128, lora=None: L.moe_grouped_gemm1_act(
+        ctypes.byref(w_), 1, 1, None, 4, H, I, 2, 8, 1, 1, ctypes.byref(act_),
+        lora, 1, 1, ctypes.c_void_p(1), 1 << 20, None)
+    assert g1(_w(N=256, K=250), act, H=250) == -2        # H % 128
+    assert g1(_w(N=256, K=256), act, H=256, I=100) == -2   # I % 128
+    assert g1(_w(N=512, K=256), act) == -2               # N != 2I
+    assert g1(M.MoeWeights(7, 4, 256, 256, 1, 1, None), act) == -3
+    assert g1(M.MoeWeights(1, 4, 256, 256, 1, None, None), act) == -1   # fp8 needs scales
+    assert g1(w, M.act_params(1.0, 0.0, 0.0)) == -5       # limit must be > 0
+    assert g1(w, M.act_params(1.0, 0.0, math.nan)) == -5
+    assert g1(w, M.act_params(math.inf, 0.0, 7.0)) == -5
+    assert g1(w, M.act_params(1.0, math.nan, 7.0)) == -5
+    lo = M.MoeLora(64, 4, 1.0, 1, 1)
+    assert g1(w, act, lora=ctypes.pointer(lo)) == -2      # rank > 32
+    w2 = _w(N=256, K=128)
+    out = L.moe_grouped_gemm2_combine(ctypes.byref(w2), 1, 1, 4, 256, 128, 2, 0, 8,
+                                      1, 1, 1, 1.0, 1, None, 0, None)
+    assert out == -6                                     # workspace
+    assert L.moe_gemm2_workspace_size(100, 256) >= 100 * 256 * 4
+
+
+def _layer(**kw):
+    w13 = _w(N=256, K=256, G=kw.pop("G", 4))
+    w2 = _w(N=256, K=128, G=w13.n_groups)
+    d = dict(H=256, I=128, E=8, E_loc=4, off=4, shared=0, k=2, S=0)
+    d.update(kw)
+    return M.layer_desc(d["H"], d["I"], d["E"], d["E_loc"], d["off"], d["shared"],
+                        d["k"], d["S"], 1.0, 1.0, 1.0, w13, w2, M.act_params())
+
+
+def test_forward_validation_and_workspace():
+    L = M.lib()
+    good = _layer()
+    assert L.moe_workspace_size(ctypes.byref(good), 64) > 0
+    bad_range = _layer(off=6)                 # 6 + 4 > 8
+    assert L.moe_workspace_size(ctypes.byref(bad_range), 64) == 0
+    r = L.moe_forward(ctypes.byref(bad_range), 1, 1, 4, 8, 1, 1, 1, None, 1,
+                      ctypes.c_void_p(1), 1 << 30, None)
+    assert r == -4
+    r = L.moe_forward(ctypes.byref(good), 1, 1, 4, 8, 1, 1, 1, None, 1,
+                      ctypes.c_void_p(1), 16, None)
+    assert r == -6
+    r = L.moe_forward(ctypes.byref(good), 1, 1, 4, 8, 1, 1, 1, None, None,
+                      ctypes.c_void_p(1), 1 << 30, None)
+    assert r == -1                            # err_word is required
+    groups_mismatch = _layer(G=5)
+    assert L.moe_workspace_size(ctypes.byref(groups_mismatch), 64) == 0
+    assert L.moe_status_string(-4) == b"missing or invalid local expert range"

@@ -190,3 +190,46 @@ def test_lora_old_units_bug_is_caught(monkeypatch):
     ref = O.moe_layer(spec, arr, nb["x_bits"], nb["logits"])
     assert np.max(np.abs(a - b)) > 1e-3 * np.abs(ref).max()
     assert np.max(np.abs(a - ref)) > 1e-3 * np.abs(ref).max()
+
+
+# ------------------------------------------------ boundary rounding decisions
+
+def test_rounding_alternatives_fp8_marks_only_boundary_elements():
+    # group amax 448 -> s = 1; values at and away from e4m3 midpoints
+    h = np.zeros((1, 128))
+    h[0, 0] = 448.0
+    h[0, 1] = 1.0625          # midpoint of 1.0 and 1.125
+    h[0, 2] = 1.03            # well inside (1.0 is nearest)
+    h[0, 3] = 3 * 2.0 ** -10  # midpoint of subnormals 2^-9 and 2^-8
+    h[0, 4] = 248.0           # midpoint of 240 and 256
+    alt = O.rounding_alternatives(h, np.full_like(h, 1e-9), "fp8")
+    np.testing.assert_allclose([alt[0, 1], alt[0, 3], alt[0, 4]],
+                               [0.125, 2.0 ** -9, 16.0], rtol=1e-4)
+    assert alt[0, 0] == 0 and alt[0, 2] == 0
+    # a wider error band catches 1.03 too (distance to 1.0625 is 0.0325)
+    alt = O.rounding_alternatives(h, np.full_like(h, 0.04), "fp8")
+    assert alt[0, 2] >= 0.125
+
+
+def test_rounding_alternatives_bf16():
+    h = np.array([[1.0 + 2.0 ** -8, 1.0 + 2.0 ** -9, 3.0]])   # midpoint, inside, exact
+    alt = O.rounding_alternatives(h, np.full_like(h, 1e-12), "bf16")
+    np.testing.assert_allclose(alt[0, 0], 2.0 ** -7, rtol=1e-3)
+    assert alt[0, 1] == 0 and alt[0, 2] == 0
+    # an error band wider than the grid: every rounding inside it is allowed
+    alt = O.rounding_alternatives(np.array([[5.6e-7]]), np.array([[1e-6]]), "bf16")
+    assert alt[0, 0] >= 2e-6
+
+
+def test_allowance_is_zero_or_small_and_value_unchanged():
+    spec = TINY["fp8_clamp_shared"]
+    layer = make_layer(spec)
+    batch = make_batch(spec, layer, 5)
+    arr, nb = to_numpy_layer(layer), to_numpy_batch(batch)
+    out = O.moe_layer(spec, arr, nb["x_bits"], nb["logits"])
+    out2, allow, nbnd = O.moe_layer(spec, arr, nb["x_bits"], nb["logits"],
+                                    with_allowance=True)
+    assert np.array_equal(out, out2)
+    assert np.all(allow >= 0)
+    # boundary decisions are rare for an fp32-accurate kernel
+    assert nbnd <= 0.01 * 5 * 3 * spec.I
