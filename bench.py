@@ -1,0 +1,243 @@
+"""Throughput of the routed MoE expert-FFN hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+
+Workload: the FP8 blockwise layer with clamped SwiGLU (H = 6144, I = 2048,
+288 routed experts top-8 plus one shared expert, L = 10), at T = 4096 tokens
+per step; T = 1 and T = 64 are reported in "sweep". Inputs are seeded,
+synthetic and resident in HBM before timing. A step is one moe_forward: route
+-> permute -> activation quant -> grouped GEMM1 + SwiGLU -> grouped GEMM2 +
+combine. Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOAD = "fp8_clamp_288"
+T_MAIN = 4096
+T_SWEEP = (1, 64, 4096)
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5033.0
+BF16_PEAK_TFLOPS = 2517.0
+METRIC = ("MoE layer tokens/s + TFLOP/s (% MFMA peak) and weight GB/s (% HBM) "
+          "at T=1..4096")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    return ap.parse_args()
+
+
+def algorithmic(spec, ids_np, T):
+    """Pairs, touched experts, GEMM flops and bytes from the run's routing."""
+    k, H, I = spec.top_k, spec.H, spec.I
+    e_loc = ids_np.reshape(-1) - spec.offset
+    local = (e_loc >= 0) & (e_loc < spec.n_local)
+    touched = len(set(e_loc[local].tolist())) + (spec.shared if T > 0 else 0)
+    P = int(local.sum()) + (T if spec.shared else 0)
+    w13_b = 2 * I * H + 4 * (2 * I // 128) * (H // 128)
+    w2_b = H * I + 4 * (H // 128) * (I // 128)
+    return dict(
+        P=P, touched=touched,
+        flops=6.0 * P * H * I,
+        gemm1_flops=4.0 * P * H * I,
+        weight_bytes=touched * (w13_b + w2_b),
+        # GEMM1 algorithmic bytes: touched W13 + scales, x codes + scales read
+        # once, h codes + scales written
+        gemm1_bytes=touched * w13_b + T * (H + 4 * H // 128) + P * (I + 4 * I // 128),
+    )
+
+
+def time_calls(fn, steps, stream):
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / steps
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import mixture_experts_expert_sigmoid_amd as M
+    from synth import CONFIGS, make_batch, make_layer
+    from tests.gpu_helpers import module_for
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    spec = CONFIGS[WORKLOAD]
+    t0 = time.time()
+    layer = make_layer(spec, device="cuda")
+    torch.cuda.synchronize()
+    print(f"# layer generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    mod = module_for(spec, layer)
+    stream = torch.cuda.current_stream()
+
+    results = {}
+    for T in (T_SWEEP if not args.no_sweep else (T_MAIN,)):
+        batch = make_batch(spec, None, T, device="cuda")
+        x, lg = batch.x, batch.logits
+        outs = mod.alloc_outputs(T)
+        mod.workspace(T)
+        for _ in range(args.warmup):
+            mod.forward(x, lg, outs)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(args.steps):
+            mod.forward(x, lg, outs)
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / args.steps
+        ids = outs["topk_ids"].cpu().numpy()
+        alg = algorithmic(spec, ids, T)
+        results[T] = dict(ms=ms, alg=alg, batch=batch, outs=outs)
+        print(f"# T={T}: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    # ---- per-call timing of the path's steps at the main size ---------------
+    T = T_MAIN
+    r = results[T]
+    x, lg = r["batch"].x, r["batch"].logits
+    k, N, H, I, G = spec.top_k, spec.n_routed, spec.H, spec.I, spec.n_groups
+    pc = T * k + T
+    d32 = dict(device="cuda", dtype=torch.int32)
+    ids = torch.empty(T, k, **d32)
+    w = torch.empty(T, k, device="cuda")
+    offsets = torch.empty(G + 1, **d32)
+    sp = torch.empty(pc, **d32)
+    pr = torch.empty(pc, **d32)
+    err = torch.zeros(1, **d32)
+    wsp = torch.empty(M.moe_permute_workspace_size(T, k, G), dtype=torch.uint8, device="cuda")
+    xq = torch.empty(T, H, dtype=torch.uint8, device="cuda")
+    xs = torch.empty(T, H // 128, device="cuda")
+    h = torch.empty(pc, I, dtype=torch.uint8, device="cuda")
+    hs = torch.empty(pc, I // 128, device="cuda")
+    out = torch.empty(T, H, device="cuda")
+    ws2 = torch.empty(M.moe_gemm2_workspace_size(pc, H), dtype=torch.uint8, device="cuda")
+    calls = {
+        "route": lambda: M.moe_route(lg, N, 0, k, 1.0, 1.0, ids, w, None),
+        "permute": lambda: M.moe_permute(ids, k, N, 0, N, 1, offsets, sp, pr, err, wsp),
+        "quant": lambda: M.moe_quantize_act_fp8(x, xq, xs),
+        "gemm1": lambda: M.moe_grouped_gemm1_act(mod.w13, xq, xs, None, T, H, I, k, pc,
+                                                  offsets, sp, mod.act, None, h, hs, None),
+        "gemm2_combine": lambda: M.moe_grouped_gemm2_combine(
+            mod.w2, h, hs, T, H, I, k, 1, pc, offsets, pr, w, 1.0, out, ws2),
+    }
+    for f in calls.values():      # warm and fill the intermediates in order
+        f()
+    torch.cuda.synchronize()
+    per_call = {}
+    for name, f in calls.items():
+        for _ in range(2):
+            f()
+        per_call[name] = time_calls(f, args.steps, stream)
+    assert torch.equal(out, r["outs"]["out"]), "step-wise path differs from moe_forward"
+
+    alg = r["alg"]
+    g1_ms = per_call["gemm1"]
+    g1_gbs = alg["gemm1_bytes"] / (g1_ms * 1e-3) / 1e9
+    roofline = {"kernel": "grouped_gemm_kernel<FP8,BM=128,GEMM1> (moe_grouped_gemm1_act)",
+                "bound": "hbm", "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(g1_gbs / HBM_PEAK_GBS, 4),
+                "traffic": None,
+                "gemm1_ms": round(g1_ms, 4),
+                "gemm1_tflops": round(alg["gemm1_flops"] / (g1_ms * 1e-3) / 1e12, 1)}
+
+    sweep = []
+    for T_, rr in results.items():
+        a = rr["alg"]
+        s = rr["ms"] * 1e-3
+        sweep.append({"T": T_, "ms_per_step": round(rr["ms"], 4),
+                      "tokens_per_s": round(T_ / s, 1),
+                      "tflops": round(a["flops"] / s / 1e12, 2),
+                      "pct_fp8_mfma_peak": round(100 * a["flops"] / s / 1e12 / FP8_PEAK_TFLOPS, 2),
+                      "weight_gbs": round(a["weight_bytes"] / s / 1e9, 1),
+                      "pct_hbm_peak": round(100 * a["weight_bytes"] / s / 1e9 / HBM_PEAK_GBS, 2),
+                      "pairs": a["P"], "experts_touched": a["touched"]})
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(spec, layer, r["batch"], T_MAIN)
+
+    main_ms = results[T_MAIN]["ms"]
+    line = {
+        "metric": METRIC, "value": round(T_MAIN / (main_ms * 1e-3), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(main_ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8", "data": "synthetic",
+        "config": {"workload": f"{WORKLOAD}: FP8 blockwise 128x128, H=6144, I=2048, "
+                               "288 routed top-8 + 1 shared, clamped SwiGLU L=10",
+                   "T": T_MAIN, "H": spec.H, "I": spec.I, "experts": spec.n_routed,
+                   "shared_experts": spec.shared, "top_k": spec.top_k},
+        "roofline": roofline, "cpu_baseline": cpu,
+        "per_call_ms": {k_: round(v, 4) for k_, v in per_call.items()},
+        "sweep": sweep,
+    }
+    print(json.dumps(line))
+
+
+def cpu_baseline(spec, layer, batch, T, n_experts=4):
+    """The fp64 oracle as it stands on the host cores, on a bounded sample:
+    routing, permutation and activation quantisation of all T tokens plus
+    the expert FFNs of the first `n_experts` routed experts (all their
+    pairs); the layer time is extrapolated by pair count."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    from synth import to_numpy_batch
+    from tests.gpu_helpers import LazyExperts
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    nb = to_numpy_batch(batch)
+    arr = LazyExperts(layer)
+    t0 = time.time()
+    ids, w, _ = O.route(nb["logits"], spec.n_routed, spec.n_sink, spec.top_k)
+    offsets, sp, _, _ = O.permute(ids, spec.n_routed, spec.offset, spec.n_local, spec.shared)
+    xhat, xb = O.gemm1_input(spec, nb["x_bits"])
+    t_fixed = time.time() - t0
+    k = spec.top_k
+    done = 0
+    t1 = time.time()
+    for e in range(n_experts):
+        rows = np.arange(offsets[e], offsets[e + 1])
+        toks = sp[rows] // k
+        O.expert_ffn(spec, arr, e, xhat[toks], xb[toks])
+        done += len(rows)
+    t_ffn = time.time() - t1
+    P = int(offsets[-1])
+    t_layer = t_fixed + t_ffn * P / max(done, 1)
+    return {"value": round(T / t_layer, 2), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"fp64 oracle: route+permute+quant of all {T} tokens "
+                      f"({t_fixed:.1f}s) + expert FFN of {n_experts} of {spec.n_groups} "
+                      f"groups ({done} of {P} pairs, {t_ffn:.1f}s), layer time "
+                      f"extrapolated by pair count to {t_layer:.0f}s"}
+
+
+if __name__ == "__main__":
+    main()
