@@ -1,0 +1,282 @@
+// Shared pieces of the grouped expert GEMM kernels: parameters, exact
+// format expansions, the device-side tile schedule and the BF16 / INT4
+// epilogue (the FP8 kernel has its own).
+//
+// Epilogue semantics: g' = min(g, L), u' = clamp(u, -L, L),
+// h = g' sigmoid(alpha g') (u' + beta) ("[Moe] Fix flashinfer_trtllm silently
+// dropping swiglu_limit clamped SwiGLU activation", sglang PR #39920,
+// "Modifications"; "fix(sm90): support parameterized SwiGLU in FP8
+// MegaMoE", DeepGEMM PR #445, "Summary"), after each half's own global scale
+// and the LoRA delta in true units ("FlashInfer 0.6.18 SM100a+SM103a
+// MoE-LoRA AOT" release notes, "Changes since 1b699bf"). BF16 and INT4
+// layers round h to bf16.
+#pragma once
+#include <algorithm>
+#include <type_traits>
+
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+enum { FMT_BF16 = 0, FMT_FP8 = 1, FMT_INT4 = 2 };
+
+constexpr int kThreads = 512;
+constexpr int kMaxGroups = 1024;
+constexpr int KS = 64;               // K elements per pipeline stage
+
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+
+// 8 bf16 -> 8 fp16 (exact for |v| in [2^-14, 65504])
+__device__ __forceinline__ i32x4 bf16x8_to_f16x8(i32x4 v) {
+  i32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t w = (uint32_t)v[i];
+    _Float16 lo = (_Float16)bf16_bits_to_f32(w & 0xFFFFu);
+    _Float16 hi = (_Float16)bf16_bits_to_f32(w >> 16);
+    o[i] = (int)((uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16));
+  }
+  return o;
+}
+
+// 8 packed nibbles (k = 0..7, low nibble first) -> 8 fp16 (nibble - 8) * s
+__device__ __forceinline__ i32x4 int4x8_to_f16x8(uint32_t w, f16x2 sc2) {
+  uint32_t lo = w & 0x0F0F0F0Fu;          // even-k nibbles, byte i = pair i
+  uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // odd-k nibbles
+  i32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t pr = ((lo >> (8 * i)) & 0xFFu) | (((hi >> (8 * i)) & 0xFFu) << 16);
+    pr |= 0x64006400u;                    // (1024 + n_even, 1024 + n_odd)
+    f16x2 v = __builtin_bit_cast(f16x2, pr);
+    v = (v - (f16x2){(_Float16)1032.0f, (_Float16)1032.0f}) * sc2;
+    o[i] = (int)__builtin_bit_cast(uint32_t, v);
+  }
+  return o;
+}
+
+struct GemmParams {
+  // A side
+  const uint8_t* a;          // x (GEMM1: gathered by token) or h (GEMM2)
+  const float* as;           // FP8 per-row scales [rows][K/128]
+  long a_ld;                 // bytes per A row
+  const int* sorted_pair;    // GEMM1: sorted row -> pair id
+  long T;
+  int top_k;
+  // B side
+  const uint8_t* w;          // [G][N][K] codes (bytes; INT4 packed)
+  const void* wsc;           // FP8 fp32 [G][N/128][K/128]; INT4 bf16 [G][N][K/32]
+  int N, K, G;
+  const int* offsets;
+  int I;
+  // GEMM1 epilogue
+  const float* gscale;
+  float alpha, beta, limit;
+  const float* z;
+  const uint16_t* lora_B;
+  int lora_rank, lora_groups;
+  float lora_scale;
+  uint8_t* h;                // GEMM1 out: e4m3 [p_cap][I] or bf16 [p_cap][I]
+  float* hs;
+  // GEMM2 out
+  float* y;                  // [p_cap][N]
+};
+
+
+// ---------------------------------------------------------------------------
+// device-side tile schedule: M-tiles of BM rows per group, NT column tiles
+// ---------------------------------------------------------------------------
+
+// Fills s_cum[0..G] with the exclusive prefix of ceil(rows_g / BM) (needs
+// all 512 threads; G <= 1024).
+template <int BM>
+__device__ __forceinline__ void tile_prefix(const int* offsets, int G, int* s_cum,
+                                            int* s_wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int c0 = 0, c1 = 0;
+  const int g0 = 2 * tid, g1 = 2 * tid + 1;
+  if (g0 < G) c0 = (offsets[g0 + 1] - offsets[g0] + BM - 1) / BM;
+  if (g1 < G) c1 = (offsets[g1 + 1] - offsets[g1] + BM - 1) / BM;
+  int v = c0 + c1, incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int i = 0; i < wave; ++i) base += s_wsum[i];
+  int excl = base + incl - v;
+  if (g0 < G) s_cum[g0] = excl;
+  if (g1 < G) s_cum[g1] = excl + c0;
+  if (tid == 0) {
+    int tot = 0;
+    for (int i = 0; i < 8; ++i) tot += s_wsum[i];
+    s_cum[G] = tot;
+  }
+  __syncthreads();
+}
+
+struct Tile {
+  int g, row0, m, nt, n_lo, n_hi;
+};
+
+// Logical tile lt -> group, first sorted row, valid rows, column halves.
+// GEMM1: lo = gate rows nt*128.., hi = up rows I + nt*128..;
+// GEMM2: lo/hi = output columns nt*256.. and nt*256+128.. (hi = lo if ragged).
+template <int BM, bool G1>
+__device__ __forceinline__ Tile decode_tile(const GemmParams& P, int lt, int NT,
+                                            const int* s_cum) {
+  Tile t;
+  const int mt = lt / NT;
+  t.nt = lt - mt * NT;
+  int glo = 0, ghi = P.G - 1;                 // last g with s_cum[g] <= mt
+  while (glo < ghi) {
+    int mid = (glo + ghi + 1) >> 1;
+    if (s_cum[mid] <= mt) glo = mid; else ghi = mid - 1;
+  }
+  t.g = glo;
+  t.row0 = P.offsets[t.g] + (mt - s_cum[t.g]) * BM;
+  t.m = min(BM, P.offsets[t.g + 1] - t.row0);
+  if (G1) {
+    t.n_lo = t.nt * 128;
+    t.n_hi = P.I + t.nt * 128;
+  } else {
+    t.n_lo = t.nt * 256;
+    t.n_hi = (t.n_lo + 128 < P.N) ? t.n_lo + 128 : t.n_lo;
+  }
+  return t;
+}
+
+// Row index of the A operand for sorted row r: the token (GEMM1 gathers x)
+// or r itself (GEMM2 reads h in sorted order).
+template <bool G1>
+__device__ __forceinline__ long a_source_row(const GemmParams& P, int r) {
+  if (!G1) return r;
+  int p = P.sorted_pair[r];
+  long npr = P.T * (long)P.top_k;
+  return (p < npr) ? (long)(p / P.top_k) : (long)(p - npr);
+}
+
+// ---------------------------------------------------------------------------
+// epilogues. acc[ms][ns] holds rows rbase + 16 ms + 4 (lane/16) + r and
+// column (ns < 2 ? lo : hi) + wn*32 + (ns & 1)*16 + lane%16.
+// smem: at least max(BM*128*2, R*BM*4, BM*128 + 16*BM) bytes, free to reuse.
+// ---------------------------------------------------------------------------
+template <int FMT, int BM, bool G1>
+__device__ __forceinline__ void tile_epilogue(const GemmParams& P, const Tile& t,
+                                              f32x4 (&acc)[BM / 32][4], uint8_t* smem) {
+  constexpr int MS = BM / 32;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int rbase = wm * (BM / 2);
+  const int g = t.g, row0 = t.row0, m = t.m, nt = t.nt;
+  if constexpr (!G1) {
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+      for (int ns = 0; ns < 4; ++ns) {
+        int col = (ns < 2 ? t.n_lo : t.n_hi) + wn * 32 + (ns & 1) * 16 + lr;
+        bool colok = (ns < 2) || (t.n_hi != t.n_lo);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          int tr = rbase + ms * 16 + 4 * lg + r;
+          if (tr < m && colok) P.y[(long)(row0 + tr) * P.N + col] = acc[ms][ns][r];
+        }
+      }
+    return;
+  } else {
+    // gate = ns 0,1 ; up = ns 2,3 (same h columns)
+    float gsg = 1.0f, gsu = 1.0f;
+    if (P.gscale) { gsg = P.gscale[2 * g]; gsu = P.gscale[2 * g + 1]; }
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          acc[ms][j][r] *= gsg;
+          acc[ms][j + 2][r] *= gsu;
+        }
+    if (P.z && g < P.lora_groups) {
+      // delta[row][n] = s * sum_q z[row][q] * B[g][n][q]; z staged as [q][BM]
+      float* sz = (float*)smem;
+      const int R = P.lora_rank;
+      for (int i = tid; i < R * BM; i += kThreads) {
+        int q = i / BM, tr = i - q * BM;
+        int rr = row0 + (tr < m ? tr : 0);
+        sz[q * BM + tr] = P.z[(long)rr * R + q];
+      }
+      __syncthreads();
+      const uint16_t* Bg = P.lora_B + (long)g * 2 * P.I * R;
+      for (int q = 0; q < R; ++q) {
+        float bgv[2], buv[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          int c = wn * 32 + j * 16 + lr;
+          bgv[j] = P.lora_scale * bf16_bits_to_f32(Bg[(long)(t.n_lo + c) * R + q]);
+          buv[j] = P.lora_scale * bf16_bits_to_f32(Bg[(long)(t.n_hi + c) * R + q]);
+        }
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) {
+          f32x4 zq = *(const f32x4*)(sz + q * BM + rbase + ms * 16 + 4 * lg);
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              acc[ms][j][r] = fmaf(zq[r], bgv[j], acc[ms][j][r]);
+              acc[ms][j + 2][r] = fmaf(zq[r], buv[j], acc[ms][j + 2][r]);
+            }
+        }
+      }
+      __syncthreads();
+    }
+    float hv[MS][2][4];
+    const float L = P.limit, al = P.alpha, be = P.beta;
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float gg = fminf(acc[ms][j][r], L);
+          float uu = fminf(fmaxf(acc[ms][j + 2][r], -L), L);
+          float sg = 1.0f / (1.0f + expf(-al * gg));
+          hv[ms][j][r] = gg * sg * (uu + be);
+        }
+    {
+      uint16_t* sh16 = (uint16_t*)smem;               // [BM][128] bf16
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          int tr = rbase + ms * 16 + 4 * lg + r;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            int c = wn * 32 + j * 16 + lr;
+            sh16[tr * 128 + c] = (uint16_t)f32_to_bf16_bits(hv[ms][j][r]);
+          }
+        }
+      __syncthreads();
+      uint16_t* hout = (uint16_t*)P.h;
+      for (int c = tid; c < BM * 16; c += kThreads) {
+        int tr = c >> 4, ch = c & 15;
+        if (tr < m)
+          *(i32x4*)(hout + (long)(row0 + tr) * P.I + nt * 128 + ch * 8) =
+              *(const i32x4*)(sh16 + tr * 128 + ch * 8);
+      }
+    }
+  }
+}
+
+int num_cus();
+
+// Blockwise-FP8 grouped GEMM (gemm_fp8.hip).
+hipError_t launch_gemm_fp8(const GemmParams& P, bool g1, long p_cap, int NT, long rows_hint,
+                           hipStream_t s);
+
+}  // namespace moe

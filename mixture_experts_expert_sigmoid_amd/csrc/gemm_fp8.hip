@@ -1,0 +1,414 @@
+// Grouped GEMM for blockwise-FP8 experts: GEMM1 over [gate | up] with the
+// SwiGLU epilogue and e4m3 re-quantisation of h, and GEMM2 (down) writing
+// fp32 rows for the weighted combine.
+//
+// Scales: "DeepSeekFp8" blockwise 128x128 weight scales and per-token
+// per-128-column activation scales ("[Moe] Fix flashinfer_trtllm silently
+// dropping swiglu_limit clamped SwiGLU activation", sglang PR #39920,
+// "Modifications"). Each 128-deep slice of K is its own dot product, whose
+// sum is multiplied by xs[row][kb] * ws[nb][kb]. A K step of this kernel is
+// exactly one such block: for every 16x16 output subtile four 32-deep MFMAs
+// sum the block into a short-lived partial that is scaled into the fp32
+// accumulator, so no per-block accumulators live across steps.
+//
+// Arithmetic: the e4m3 codes are expanded exactly to bf16 (hardware
+// v_cvt_scalef32_pk_bf16_fp8 with scale 1; every e4m3 value has at most 4
+// significant bits) and multiplied on v_mfma_f32_16x16x32_bf16, whose
+// accumulation of such products is exact. The FP8 MFMA is not used: on
+// gfx950 it accumulates at reduced internal precision (measured about 2e-5
+// of sum |products|), enough to flip the e4m3 re-quantisation of h.
+//
+// Work split: a workgroup of 8 waves owns BM sorted rows of one expert and
+// 256 weight rows in two halves ("lo", "hi"). GEMM1: lo = gate rows
+// nt*128.., hi = the matching up rows I + nt*128.., so one tile yields 128
+// complete h columns, the FP8 re-quantisation group; GEMM2: lo/hi = output
+// columns nt*256.. and nt*256 + 128... Wave w computes all BM rows of
+// columns 16w..16w+15 of both halves: gate and up of one h element meet in
+// one lane, and every weight byte is used by exactly one wave, so weights
+// stream from HBM straight into registers (two K blocks in flight), are
+// expanded there once per block and never pass through LDS. The activation
+// block is expanded to bf16 once per workgroup while it is staged in LDS
+// (double buffered, one barrier per K block) together with the per-row
+// combined scales xs * ws_lo and xs * ws_hi, and read by all 8 waves.
+//
+// K order inside a block: lane (r = l % 16, q = l / 16) feeds the MFMA with
+// elements 32q + 8j .. 32q + 8j + 7 of its row at step j, on both operands
+// -- any permutation of K shared by A and B leaves the dot product
+// unchanged and this one gives every lane 32 contiguous weight bytes per
+// row.
+#include "gemm_common.h"
+
+namespace moe {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+template <int BM>
+struct F8Geo {
+  static constexpr int MS = BM / 16;                       // 16-row subtiles
+  static constexpr int A_BYTES = BM * 256;                 // one K block, bf16
+  static constexpr int A_CH = BM * 8;                      // 16-byte code chunks
+  static constexpr int A_PT = (A_CH + kThreads - 1) / kThreads;
+  static constexpr int C_BYTES = 2 * BM * 4;               // combined scales lo, hi
+  static constexpr int STAGE = A_BYTES + C_BYTES;
+  static constexpr int LDS = 2 * STAGE;
+};
+
+// bf16 A rows are 256 bytes = 16 chunks of 16; chunk c of row r is stored
+// at c ^ (r & 0b1011). gfx950 serves a ds_read_b128 / ds_write_b128 in four
+// passes of 16 lanes -- the lanes that share lane bit 5 and the parity of
+// lane bits 2..4 -- over 64 four-byte banks (fitted to bank-conflict counter
+// readings of eight address patterns); under that rule this XOR makes both
+// the 16-row fragment reads and the row-wise chunk stores conflict-free,
+// where the plain c ^ (r & 15) costs two passes per read.
+__device__ __forceinline__ int swz16(int row, int c) { return c ^ (row & 11); }
+
+// 8 e4m3fn codes (two dwords, byte order) -> 8 bf16, exact
+__device__ __forceinline__ bf16x8 e4m3x8_bf16(uint32_t w0, uint32_t w1) {
+  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  return (bf16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+template <int BM, bool G1>
+__device__ __forceinline__ void fp8_epilogue(const GemmParams& P, const Tile& t,
+                                             f32x4 (&acc)[BM / 16][2], uint8_t* smem) {
+  constexpr int MS = BM / 16;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int c = 16 * wave + lr;                 // column inside each half
+  const int g = t.g, row0 = t.row0, m = t.m;
+  if constexpr (!G1) {
+    const bool hi_ok = t.n_hi != t.n_lo;
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tr = 16 * ms + 4 * lg + r;
+        if (tr < m) {
+          float* yr = P.y + (long)(row0 + tr) * P.N;
+          yr[t.n_lo + c] = acc[ms][0][r];
+          if (hi_ok) yr[t.n_hi + c] = acc[ms][1][r];
+        }
+      }
+  } else {
+    float gsg = 1.0f, gsu = 1.0f;
+    if (P.gscale) { gsg = P.gscale[2 * g]; gsu = P.gscale[2 * g + 1]; }
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        acc[ms][0][r] *= gsg;
+        acc[ms][1][r] *= gsu;
+      }
+    if (P.z && g < P.lora_groups) {
+      // delta[row][n] = s * sum_q z[row][q] * B[g][n][q], z staged as [q][BM]
+      float* sz = (float*)smem;
+      const int R = P.lora_rank;
+      for (int i = tid; i < R * BM; i += kThreads) {
+        const int q = i / BM, tr = i - q * BM;
+        sz[q * BM + tr] = P.z[(long)(row0 + (tr < m ? tr : 0)) * R + q];
+      }
+      __syncthreads();
+      const uint16_t* Bg = P.lora_B + (long)g * 2 * P.I * R;
+      for (int q = 0; q < R; ++q) {
+        const float bgv = P.lora_scale * bf16_bits_to_f32(Bg[(long)(t.n_lo + c) * R + q]);
+        const float buv = P.lora_scale * bf16_bits_to_f32(Bg[(long)(t.n_hi + c) * R + q]);
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) {
+          const f32x4 zq = *(const f32x4*)(sz + q * BM + 16 * ms + 4 * lg);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            acc[ms][0][r] = fmaf(zq[r], bgv, acc[ms][0][r]);
+            acc[ms][1][r] = fmaf(zq[r], buv, acc[ms][1][r]);
+          }
+        }
+      }
+      __syncthreads();
+    }
+    float hv[MS][4];
+    const float L = P.limit, al = P.alpha, be = P.beta;
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float gg = fminf(acc[ms][0][r], L);
+        const float uu = fminf(fmaxf(acc[ms][1][r], -L), L);
+        const float sg = __builtin_amdgcn_rcpf(1.0f + expf(-al * gg));
+        hv[ms][r] = gg * sg * (uu + be);
+      }
+    // e4m3 re-quantisation per row and 128 columns: s = amax / 448, codes
+    // round-to-nearest-even of h * (1 / s). Row amax: 16 lanes per wave by
+    // shuffles, then the 8 waves' partial maxima through LDS.
+    constexpr int kStg = 144;                         // staging row stride
+    uint8_t* sh = smem;                               // [BM][kStg] codes
+    float* s_amax = (float*)(smem + BM * kStg);       // [BM][8]
+    float* s_inv = s_amax + 8 * BM;                   // [BM]
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float a = max16(fabsf(hv[ms][r]));
+        if (lr == 0) s_amax[(16 * ms + 4 * lg + r) * 8 + wave] = a;
+      }
+    __syncthreads();
+    if (tid < BM) {
+      const f32x4 a0 = *(const f32x4*)(s_amax + tid * 8);
+      const f32x4 a1 = *(const f32x4*)(s_amax + tid * 8 + 4);
+      const float a = fmaxf(fmaxf(fmaxf(a0[0], a0[1]), fmaxf(a0[2], a0[3])),
+                            fmaxf(fmaxf(a1[0], a1[1]), fmaxf(a1[2], a1[3])));
+      const float sc = a > 0.0f ? a / 448.0f : 1.0f;
+      s_inv[tid] = 1.0f / sc;
+      if (tid < m) P.hs[(long)(row0 + tid) * (P.I >> 7) + t.nt] = sc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+      const f32x4 inv = *(const f32x4*)(s_inv + 16 * ms + 4 * lg);
+      float q[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)   // |q| <= 448 up to rounding; clamp, then RNE
+        q[r] = __builtin_amdgcn_fmed3f(hv[ms][r] * inv[r], -448.0f, 448.0f);
+      const uint32_t c01 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+      const uint32_t c23 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], 0, false);
+      uint8_t* dst = sh + (16 * ms + 4 * lg) * kStg + c;
+      dst[0] = (uint8_t)c01;
+      dst[kStg] = (uint8_t)(c01 >> 8);
+      dst[2 * kStg] = (uint8_t)c23;
+      dst[3 * kStg] = (uint8_t)(c23 >> 8);
+    }
+    __syncthreads();
+    for (int i = tid; i < BM * 8; i += kThreads) {
+      const int tr = i >> 3, ch = i & 7;
+      if (tr < m)
+        *(i32x4*)(P.h + (long)(row0 + tr) * P.I + t.nt * 128 + ch * 16) =
+            *(const i32x4*)(sh + tr * kStg + ch * 16);
+    }
+  }
+}
+
+template <int BM, bool G1>
+__global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
+  using Gm = F8Geo<BM>;
+  constexpr int MS = Gm::MS;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // 2 stages
+  __shared__ int s_cum[kMaxGroups + 1];
+  __shared__ int s_wsum[8];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int G = P.G, K = P.K;
+  const int NT = G1 ? (P.I >> 7) : ((P.N + 255) >> 8);
+  const int NS = K >> 7;                      // K blocks of 128
+
+  tile_prefix<BM>(P.offsets, G, s_cum, s_wsum);
+  const int total = s_cum[G] * NT;
+  // XCD x (= blockIdx % 8) owns logical tiles [x*chunk, (x+1)*chunk)
+  const int xcd = blockIdx.x & 7, nper = gridDim.x >> 3, slot = blockIdx.x >> 3;
+  const int chunk = (total + 7) >> 3;
+  const int t_end = min(total, (xcd + 1) * chunk);
+
+  for (int lt = xcd * chunk + slot; lt < t_end; lt += nper) {
+    Tile tl = decode_tile<BM, G1>(P, lt, NT, s_cum);
+    tl.g = __builtin_amdgcn_readfirstlane(tl.g);
+    tl.row0 = __builtin_amdgcn_readfirstlane(tl.row0);
+    tl.m = __builtin_amdgcn_readfirstlane(tl.m);
+    tl.nt = __builtin_amdgcn_readfirstlane(tl.nt);
+    tl.n_lo = __builtin_amdgcn_readfirstlane(tl.n_lo);
+    tl.n_hi = __builtin_amdgcn_readfirstlane(tl.n_hi);
+    const int g = tl.g, row0 = tl.row0, m = tl.m;
+
+    // ---- this thread's sources at K block 0 (+128 bytes per block) --------
+    const uint8_t* ap[Gm::A_PT];
+    int a_st[Gm::A_PT];                    // LDS offsets of the 2 bf16 chunks
+#pragma unroll
+    for (int i = 0; i < Gm::A_PT; ++i) {
+      const int cc = min(tid + i * kThreads, Gm::A_CH - 1);
+      const int row = cc >> 3, ch = cc & 7;
+      ap[i] = P.a + a_source_row<G1>(P, row0 + (row < m ? row : 0)) * P.a_ld + ch * 16;
+      a_st[i] = row * 256;
+    }
+    const float* xsp = P.as;               // row (tid mod BM)'s activation scales
+    {
+      const int r = tid & (BM - 1);
+      xsp = P.as + a_source_row<G1>(P, row0 + (r < m ? r : 0)) * NS;
+    }
+    const uint8_t* wg = P.w + (long)g * P.N * K;
+    const uint8_t* bp0 = wg + (long)(tl.n_lo + 16 * wave + lr) * K + 32 * lg;
+    const uint8_t* bp1 = wg + (long)(tl.n_hi + 16 * wave + lr) * K + 32 * lg;
+    const float* wsl = (const float*)P.wsc + ((long)g * (P.N >> 7) + (tl.n_lo >> 7)) * NS;
+    const float* wsh = (const float*)P.wsc + ((long)g * (P.N >> 7) + (tl.n_hi >> 7)) * NS;
+
+    i32x4 ra[Gm::A_PT];
+    float rxs = 0.0f, rws = 0.0f;
+    auto gload_a = [&](int s) {           // past the last block: re-read it
+      const int sc = min(s, NS - 1);
+      const long adv = (long)sc * 128;
+#pragma unroll
+      for (int i = 0; i < Gm::A_PT; ++i) ra[i] = *(const i32x4*)(ap[i] + adv);
+      if (tid < 2 * BM) {
+        rxs = xsp[sc];
+        rws = tid < BM ? wsl[sc] : wsh[sc];
+      }
+    };
+    // expand the codes to bf16 into LDS buffer buf, with the row's combined
+    // scales xs * ws_lo and xs * ws_hi
+    auto store_a = [&](int buf) {
+      uint8_t* st = smem + buf * Gm::STAGE;
+#pragma unroll
+      for (int i = 0; i < Gm::A_PT; ++i) {
+        if (Gm::A_CH % kThreads == 0 || tid + i * kThreads < Gm::A_CH) {
+          const int cc = tid + i * kThreads, row = cc >> 3, ch = cc & 7;
+          const i32x4 v = ra[i];
+          *(bf16x8*)(st + a_st[i] + 16 * swz16(row, 2 * ch)) =
+              e4m3x8_bf16((uint32_t)v[0], (uint32_t)v[1]);
+          *(bf16x8*)(st + a_st[i] + 16 * swz16(row, 2 * ch + 1)) =
+              e4m3x8_bf16((uint32_t)v[2], (uint32_t)v[3]);
+        }
+      }
+      if (tid < 2 * BM) ((float*)(st + Gm::A_BYTES))[tid] = rxs * rws;
+    };
+    auto gload_b = [&](i32x4 (&rb)[4], int s) {
+      const long adv = (long)min(s, NS - 1) * 128;
+      rb[0] = *(const i32x4*)(bp0 + adv);
+      rb[1] = *(const i32x4*)(bp0 + adv + 16);
+      rb[2] = *(const i32x4*)(bp1 + adv);
+      rb[3] = *(const i32x4*)(bp1 + adv + 16);
+    };
+
+    f32x4 acc[MS][2];
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+      acc[i][0] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      acc[i][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+
+    // One K block: expand this block's weights, prefetch (A one block ahead,
+    // B two blocks ahead into the registers just freed), then MFMA + scale.
+    auto block = [&](int s, int buf, i32x4 (&rb)[4]) {
+      // pin this block's weight registers here so their expansion is not
+      // hoisted into the previous block (it would double the live registers)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(rb[i]));
+      bf16x8 bw[2][4];
+#pragma unroll
+      for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const i32x4 v = rb[2 * ns + h];
+          bw[ns][2 * h] = e4m3x8_bf16((uint32_t)v[0], (uint32_t)v[1]);
+          bw[ns][2 * h + 1] = e4m3x8_bf16((uint32_t)v[2], (uint32_t)v[3]);
+        }
+      gload_a(s + 1);
+      gload_b(rb, s + 2);
+      const uint8_t* sa = smem + buf * Gm::STAGE;
+      const float* sc = (const float*)(sa + Gm::A_BYTES);
+      auto lds_a = [&](int ms, bf16x8 (&af)[4]) {
+        const int row = 16 * ms + lr;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          af[j] = *(const bf16x8*)(sa + row * 256 + 16 * swz16(row, 4 * lg + j));
+      };
+      // software pipeline over the 16-row subtiles: the LDS reads of subtile
+      // ms + 1 and the scaling of subtile ms - 1 surround the MFMAs of ms;
+      // the scheduling fences keep the live registers to one subtile's worth
+      auto scale_into = [&](int ms, const f32x4& p0, const f32x4& p1) {
+        const f32x4 cl = *(const f32x4*)(sc + 16 * ms + 4 * lg);
+        const f32x4 ch = *(const f32x4*)(sc + BM + 16 * ms + 4 * lg);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          acc[ms][0][r] = fmaf(p0[r], cl[r], acc[ms][0][r]);
+          acc[ms][1][r] = fmaf(p1[r], ch[r], acc[ms][1][r]);
+        }
+        asm volatile("" : "+v"(acc[ms][0]), "+v"(acc[ms][1]));   // keep in place
+      };
+      // two named fragment / partial sets alternate between even and odd
+      // subtiles, so the pipeline needs no register copies
+      auto sub = [&](int ms, const bf16x8 (&af)[4], f32x4& p0, f32x4& p1) {
+        p0 = (f32x4){0.f, 0.f, 0.f, 0.f};
+        p1 = p0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], bw[0][j], p0, 0, 0, 0);
+          p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], bw[1][j], p1, 0, 0, 0);
+        }
+      };
+      bf16x8 fa[4], fb[4];
+      f32x4 pa0, pa1, pb0, pb1;
+      lds_a(0, fa);
+#pragma unroll
+      for (int ms = 0; ms < MS; ms += 2) {
+        lds_a(ms + 1, fb);
+        sub(ms, fa, pa0, pa1);
+        if (ms > 0) scale_into(ms - 1, pb0, pb1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ms + 2 < MS) lds_a(ms + 2, fa);
+        sub(ms + 1, fb, pb0, pb1);
+        scale_into(ms, pa0, pa1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      scale_into(MS - 1, pb0, pb1);
+      store_a(buf ^ 1);
+    };
+
+    i32x4 rb0[4], rb1[4];
+    gload_b(rb0, 0);
+    gload_b(rb1, 1);
+    gload_a(0);
+    store_a(0);
+    __syncthreads();
+    int s = 0;
+    for (; s + 2 <= NS; s += 2) {
+      block(s, 0, rb0);
+      __syncthreads();
+      block(s + 1, 1, rb1);
+      __syncthreads();
+    }
+    if (s < NS) {            // odd block count
+      block(s, 0, rb0);
+      __syncthreads();
+    }
+    fp8_epilogue<BM, G1>(P, tl, acc, smem);
+    __syncthreads();         // LDS is reused by the next tile
+  }
+}
+
+template <int BM, bool G1>
+static hipError_t run_fp8(const GemmParams& P, long p_cap, int NT, hipStream_t s) {
+  constexpr int shm = F8Geo<BM>::LDS;
+  static int per_cu = 0;   // resident workgroups per CU, per instantiation
+  if (per_cu == 0) {
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&moe_gemm_fp8_kernel<BM, G1>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, shm);
+    if (e != hipSuccess) return e;
+    int nb = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &nb, reinterpret_cast<const void*>(&moe_gemm_fp8_kernel<BM, G1>), kThreads, shm);
+    if (e != hipSuccess) return e;
+    per_cu = nb > 0 ? nb : 1;
+  }
+  long max_tiles = ((p_cap + BM - 1) / BM + P.G) * (long)NT;
+  long nwg = std::min<long>(max_tiles, (long)num_cus() * per_cu);
+  nwg = (nwg + 7) & ~7L;
+  if (nwg == 0) return hipSuccess;
+  moe_gemm_fp8_kernel<BM, G1><<<dim3((unsigned)nwg), dim3(kThreads), shm, s>>>(P);
+  return hipGetLastError();
+}
+
+template <bool G1>
+static hipError_t run_fp8_bm(const GemmParams& P, long p_cap, int NT, long rows_hint,
+                             hipStream_t s) {
+  if (rows_hint <= 32) return run_fp8<32, G1>(P, p_cap, NT, s);
+  if (rows_hint <= 64) return run_fp8<64, G1>(P, p_cap, NT, s);
+  return run_fp8<128, G1>(P, p_cap, NT, s);
+}
+
+hipError_t launch_gemm_fp8(const GemmParams& P, bool g1, long p_cap, int NT, long rows_hint,
+                           hipStream_t s) {
+  return g1 ? run_fp8_bm<true>(P, p_cap, NT, rows_hint, s)
+            : run_fp8_bm<false>(P, p_cap, NT, rows_hint, s);
+}
+
+}  // namespace moe
