@@ -1,6 +1,7 @@
 """Throughput of the routed MoE expert-FFN hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+    python bench.py --profile      # workload + copy calibration, for rocprofv3
 
 Workload: the FP8 blockwise layer with clamped SwiGLU (H = 6144, I = 2048,
 288 routed experts top-8 plus one shared expert, L = 10), at T = 4096 tokens
@@ -8,13 +9,24 @@ per step; T = 1 and T = 64 are reported in "sweep". Inputs are seeded,
 synthetic and resident in HBM before timing. A step is one moe_forward: route
 -> permute -> activation quant -> grouped GEMM1 + SwiGLU -> grouped GEMM2 +
 combine. Prints one JSON line.
+
+roofline: the dominant kernel is the FP8 GEMM1 (moe_gemm_fp8_kernel<128,
+true>). "achieved" is its algorithmic bytes (touched W13 codes + scales, the
+x codes + scales once, the h codes + scales written) over its average launch
+time measured here with HIP events on the launching stream. "traffic" is the
+HBM bytes per launch measured by rocprofv3 FETCH_SIZE + WRITE_SIZE (scaled by
+the same counters on a plain copy of known size), read from the committed
+summary profiles/gemm1_fp8_T4096_traffic.md -- and null when the kernel
+sources no longer hash to the ones the counters were taken on.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -29,6 +41,10 @@ FP8_PEAK_TFLOPS = 5033.0
 BF16_PEAK_TFLOPS = 2517.0
 METRIC = ("MoE layer tokens/s + TFLOP/s (% MFMA peak) and weight GB/s (% HBM) "
           "at T=1..4096")
+GEMM1_KERNEL = "moe_gemm_fp8_kernel<128, true> (moe_grouped_gemm1_act)"
+CSRC = os.path.join(ROOT, "mixture_experts_expert_sigmoid_amd", "csrc")
+KERNEL_SOURCES = ("gemm_fp8.hip", "gemm_common.h", "common.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm1_fp8_T4096_traffic.md")
 
 
 def parse():
@@ -38,7 +54,32 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="run only the forward at --profile-tokens (warmup + steps) and "
+                         "a copy of known size, for rocprofv3 counter passes")
+    ap.add_argument("--profile-tokens", type=int, default=T_MAIN)
     return ap.parse_args()
+
+
+def kernel_sources_sha256():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per GEMM1 launch from the committed counter summary, or
+    None when it is missing or was taken on other kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    sha = re.search(r"sources_sha256:\s*([0-9a-f]{64})", text)
+    val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not sha or not val or sha.group(1) != kernel_sources_sha256():
+        return None
+    return float(val.group(1))
 
 
 def algorithmic(spec, ids_np, T):
@@ -76,7 +117,8 @@ def time_calls(fn, steps, stream):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "bench.py measures one GPU's share of the layer; "
+                                   "--gpus must be 1 (no multi-GPU runs)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import numpy as np
@@ -94,6 +136,22 @@ def main():
     print(f"# layer generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     mod = module_for(spec, layer)
     stream = torch.cuda.current_stream()
+
+    if args.profile:
+        # copy calibration: 1 GiB read + 1 GiB written by a plain copy kernel
+        src = torch.ones(1 << 28, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        Tp = args.profile_tokens
+        batch = make_batch(spec, None, Tp, device="cuda")
+        outs = mod.alloc_outputs(Tp)
+        for _ in range(args.warmup + args.steps):
+            mod.forward(batch.x, batch.logits, outs)
+        torch.cuda.synchronize()
+        print(f"# profile run done: copy 3 x 1 GiB, forward T={Tp} x "
+              f"{args.warmup + args.steps}", flush=True)
+        return
 
     results = {}
     for T in (T_SWEEP if not args.no_sweep else (T_MAIN,)):
@@ -159,10 +217,11 @@ def main():
     alg = r["alg"]
     g1_ms = per_call["gemm1"]
     g1_gbs = alg["gemm1_bytes"] / (g1_ms * 1e-3) / 1e9
-    roofline = {"kernel": "grouped_gemm_kernel<FP8,BM=128,GEMM1> (moe_grouped_gemm1_act)",
+    roofline = {"kernel": GEMM1_KERNEL,
                 "bound": "hbm", "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(g1_gbs / HBM_PEAK_GBS, 4),
-                "traffic": None,
+                "traffic": measured_traffic(),
+                "algorithmic_bytes": alg["gemm1_bytes"],
                 "gemm1_ms": round(g1_ms, 4),
                 "gemm1_tflops": round(alg["gemm1_flops"] / (g1_ms * 1e-3) / 1e12, 1)}
 

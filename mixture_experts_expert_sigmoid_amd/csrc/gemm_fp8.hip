@@ -310,12 +310,16 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
         for (int j = 0; j < 4; ++j)
           af[j] = *(const bf16x8*)(sa + row * 256 + 16 * swz16(row, 4 * lg + j));
       };
-      // software pipeline over the 16-row subtiles: the LDS reads of subtile
-      // ms + 1 and the scaling of subtile ms - 1 surround the MFMAs of ms;
-      // the scheduling fences keep the live registers to one subtile's worth
-      auto scale_into = [&](int ms, const f32x4& p0, const f32x4& p1) {
-        const f32x4 cl = *(const f32x4*)(sc + 16 * ms + 4 * lg);
-        const f32x4 ch = *(const f32x4*)(sc + BM + 16 * ms + 4 * lg);
+      // software pipeline over the 16-row subtiles: while the MFMAs of
+      // subtile ms run, the A fragments of ms + 1 and the scales of ms - 1
+      // are in flight and ms - 1 is scaled into the accumulator. The
+      // scheduling fences keep the live registers to that working set.
+      auto load_c = [&](int ms, f32x4& cl, f32x4& ch) {
+        cl = *(const f32x4*)(sc + 16 * ms + 4 * lg);
+        ch = *(const f32x4*)(sc + BM + 16 * ms + 4 * lg);
+      };
+      auto scale_into = [&](int ms, const f32x4& p0, const f32x4& p1, const f32x4& cl,
+                            const f32x4& ch) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           acc[ms][0][r] = fmaf(p0[r], cl[r], acc[ms][0][r]);
@@ -325,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
       };
       // two named fragment / partial sets alternate between even and odd
       // subtiles, so the pipeline needs no register copies
-      auto sub = [&](int ms, const bf16x8 (&af)[4], f32x4& p0, f32x4& p1) {
+      auto sub = [&](const bf16x8 (&af)[4], f32x4& p0, f32x4& p1) {
         p0 = (f32x4){0.f, 0.f, 0.f, 0.f};
         p1 = p0;
 #pragma unroll
@@ -335,20 +339,23 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
         }
       };
       bf16x8 fa[4], fb[4];
-      f32x4 pa0, pa1, pb0, pb1;
+      f32x4 pa0, pa1, pb0, pb1, cl, ch;
       lds_a(0, fa);
 #pragma unroll
       for (int ms = 0; ms < MS; ms += 2) {
         lds_a(ms + 1, fb);
-        sub(ms, fa, pa0, pa1);
-        if (ms > 0) scale_into(ms - 1, pb0, pb1);
+        if (ms > 0) load_c(ms - 1, cl, ch);
+        sub(fa, pa0, pa1);
+        if (ms > 0) scale_into(ms - 1, pb0, pb1, cl, ch);
         __builtin_amdgcn_sched_barrier(0);
         if (ms + 2 < MS) lds_a(ms + 2, fa);
-        sub(ms + 1, fb, pb0, pb1);
-        scale_into(ms, pa0, pa1);
+        load_c(ms, cl, ch);
+        sub(fb, pb0, pb1);
+        scale_into(ms, pa0, pa1, cl, ch);
         __builtin_amdgcn_sched_barrier(0);
       }
-      scale_into(MS - 1, pb0, pb1);
+      load_c(MS - 1, cl, ch);
+      scale_into(MS - 1, pb0, pb1, cl, ch);
       store_a(buf ^ 1);
     };
 
