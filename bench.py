@@ -258,7 +258,7 @@ def main():
     print(json.dumps(line))
 
 
-def cpu_baseline(spec, layer, batch, T, n_experts=4):
+def cpu_baseline(spec, layer, batch, T, n_experts=20):
     """The fp64 oracle as it stands on the host cores, on a bounded sample:
     routing, permutation and activation quantisation of all T tokens plus
     the expert FFNs of the first `n_experts` routed experts (all their
