@@ -28,8 +28,12 @@
 // stream from HBM straight into registers (two K blocks in flight), are
 // expanded there once per block and never pass through LDS. The activation
 // block is expanded to bf16 once per workgroup while it is staged in LDS
-// (double buffered, one barrier per K block) together with the per-row
-// combined scales xs * ws_lo and xs * ws_hi, and read by all 8 waves.
+// (double buffered, one barrier per K block) together with its rows'
+// activation scales, and read by all 8 waves. The weights are the MFMA's
+// first operand, so a lane's partials belong to one activation row and
+// four consecutive weight columns: the block scale of a partial is one
+// product xs[row] * ws[half] per lane and subtile, and the epilogue writes
+// whole dwords of codes (GEMM1) or 16-byte fp32 runs (GEMM2).
 //
 // K order inside a block: lane (r = l % 16, q = l / 16) feeds the MFMA with
 // elements 32q + 8j .. 32q + 8j + 7 of its row at step j, on both operands
@@ -48,8 +52,8 @@ struct F8Geo {
   static constexpr int A_BYTES = BM * 256;                 // one K block, bf16
   static constexpr int A_CH = BM * 8;                      // 16-byte code chunks
   static constexpr int A_PT = (A_CH + kThreads - 1) / kThreads;
-  static constexpr int C_BYTES = 2 * BM * 4;               // combined scales lo, hi
-  static constexpr int STAGE = A_BYTES + C_BYTES;
+  static constexpr int X_BYTES = BM * 4;                   // row scales, [16][MS]
+  static constexpr int STAGE = A_BYTES + X_BYTES;
   static constexpr int LDS = 2 * STAGE;
 };
 
@@ -71,27 +75,28 @@ __device__ __forceinline__ bf16x8 e4m3x8_bf16(uint32_t w0, uint32_t w1) {
   return (bf16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// Accumulator layout (weights are the MFMA's first operand): acc[ms][ns][r]
+// is activation row 16 ms + (lane % 16) and weight column
+// (ns ? hi : lo) + 16 wave + 4 (lane / 16) + r.
 template <int BM, bool G1>
 __device__ __forceinline__ void fp8_epilogue(const GemmParams& P, const Tile& t,
                                              f32x4 (&acc)[BM / 16][2], uint8_t* smem) {
   constexpr int MS = BM / 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int c = 16 * wave + lr;                 // column inside each half
+  const int c0 = 16 * wave + 4 * lg;            // first of the lane's 4 columns
   const int g = t.g, row0 = t.row0, m = t.m;
   if constexpr (!G1) {
     const bool hi_ok = t.n_hi != t.n_lo;
 #pragma unroll
-    for (int ms = 0; ms < MS; ++ms)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tr = 16 * ms + 4 * lg + r;
-        if (tr < m) {
-          float* yr = P.y + (long)(row0 + tr) * P.N;
-          yr[t.n_lo + c] = acc[ms][0][r];
-          if (hi_ok) yr[t.n_hi + c] = acc[ms][1][r];
-        }
+    for (int ms = 0; ms < MS; ++ms) {
+      const int tr = 16 * ms + lr;
+      if (tr < m) {
+        float* yr = P.y + (long)(row0 + tr) * P.N;
+        *(f32x4*)(yr + t.n_lo + c0) = acc[ms][0];
+        if (hi_ok) *(f32x4*)(yr + t.n_hi + c0) = acc[ms][1];
       }
+    }
   } else {
     float gsg = 1.0f, gsu = 1.0f;
     if (P.gscale) { gsg = P.gscale[2 * g]; gsu = P.gscale[2 * g + 1]; }
@@ -113,15 +118,19 @@ __device__ __forceinline__ void fp8_epilogue(const GemmParams& P, const Tile& t,
       __syncthreads();
       const uint16_t* Bg = P.lora_B + (long)g * 2 * P.I * R;
       for (int q = 0; q < R; ++q) {
-        const float bgv = P.lora_scale * bf16_bits_to_f32(Bg[(long)(t.n_lo + c) * R + q]);
-        const float buv = P.lora_scale * bf16_bits_to_f32(Bg[(long)(t.n_hi + c) * R + q]);
+        float bgv[4], buv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          bgv[r] = P.lora_scale * bf16_bits_to_f32(Bg[(long)(t.n_lo + c0 + r) * R + q]);
+          buv[r] = P.lora_scale * bf16_bits_to_f32(Bg[(long)(t.n_hi + c0 + r) * R + q]);
+        }
 #pragma unroll
         for (int ms = 0; ms < MS; ++ms) {
-          const f32x4 zq = *(const f32x4*)(sz + q * BM + 16 * ms + 4 * lg);
+          const float zq = sz[q * BM + 16 * ms + lr];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            acc[ms][0][r] = fmaf(zq[r], bgv, acc[ms][0][r]);
-            acc[ms][1][r] = fmaf(zq[r], buv, acc[ms][1][r]);
+            acc[ms][0][r] = fmaf(zq, bgv[r], acc[ms][0][r]);
+            acc[ms][1][r] = fmaf(zq, buv[r], acc[ms][1][r]);
           }
         }
       }
@@ -139,19 +148,20 @@ __device__ __forceinline__ void fp8_epilogue(const GemmParams& P, const Tile& t,
         hv[ms][r] = gg * sg * (uu + be);
       }
     // e4m3 re-quantisation per row and 128 columns: s = amax / 448, codes
-    // round-to-nearest-even of h * (1 / s). Row amax: 16 lanes per wave by
-    // shuffles, then the 8 waves' partial maxima through LDS.
+    // round-to-nearest-even of h * (1 / s). Row amax: the lane's 4 columns,
+    // the 4 lanes of the row (lane / 16), then the 8 waves through LDS.
     constexpr int kStg = 144;                         // staging row stride
     uint8_t* sh = smem;                               // [BM][kStg] codes
     float* s_amax = (float*)(smem + BM * kStg);       // [BM][8]
     float* s_inv = s_amax + 8 * BM;                   // [BM]
 #pragma unroll
-    for (int ms = 0; ms < MS; ++ms)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float a = max16(fabsf(hv[ms][r]));
-        if (lr == 0) s_amax[(16 * ms + 4 * lg + r) * 8 + wave] = a;
-      }
+    for (int ms = 0; ms < MS; ++ms) {
+      float a = fmaxf(fmaxf(fabsf(hv[ms][0]), fabsf(hv[ms][1])),
+                      fmaxf(fabsf(hv[ms][2]), fabsf(hv[ms][3])));
+      a = fmaxf(a, __shfl_xor(a, 16, kWave));
+      a = fmaxf(a, __shfl_xor(a, 32, kWave));
+      if (lg == 0) s_amax[(16 * ms + lr) * 8 + wave] = a;
+    }
     __syncthreads();
     if (tid < BM) {
       const f32x4 a0 = *(const f32x4*)(s_amax + tid * 8);
@@ -165,18 +175,15 @@ __device__ __forceinline__ void fp8_epilogue(const GemmParams& P, const Tile& t,
     __syncthreads();
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) {
-      const f32x4 inv = *(const f32x4*)(s_inv + 16 * ms + 4 * lg);
+      const int tr = 16 * ms + lr;
+      const float inv = s_inv[tr];
       float q[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r)   // |q| <= 448 up to rounding; clamp, then RNE
-        q[r] = __builtin_amdgcn_fmed3f(hv[ms][r] * inv[r], -448.0f, 448.0f);
-      const uint32_t c01 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
-      const uint32_t c23 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], 0, false);
-      uint8_t* dst = sh + (16 * ms + 4 * lg) * kStg + c;
-      dst[0] = (uint8_t)c01;
-      dst[kStg] = (uint8_t)(c01 >> 8);
-      dst[2 * kStg] = (uint8_t)c23;
-      dst[3 * kStg] = (uint8_t)(c23 >> 8);
+        q[r] = __builtin_amdgcn_fmed3f(hv[ms][r] * inv, -448.0f, 448.0f);
+      int v = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+      v = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], v, true);
+      *(int*)(sh + tr * kStg + c0) = v;               // 4 consecutive columns
     }
     __syncthreads();
     for (int i = tid; i < BM * 8; i += kThreads) {
@@ -221,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
 
     // ---- this thread's sources at K block 0 (+128 bytes per block) --------
     const uint8_t* ap[Gm::A_PT];
-    int a_st[Gm::A_PT];                    // LDS offsets of the 2 bf16 chunks
+    int a_st[Gm::A_PT];
 #pragma unroll
     for (int i = 0; i < Gm::A_PT; ++i) {
       const int cc = min(tid + i * kThreads, Gm::A_CH - 1);
@@ -229,11 +236,8 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
       ap[i] = P.a + a_source_row<G1>(P, row0 + (row < m ? row : 0)) * P.a_ld + ch * 16;
       a_st[i] = row * 256;
     }
-    const float* xsp = P.as;               // row (tid mod BM)'s activation scales
-    {
-      const int r = tid & (BM - 1);
-      xsp = P.as + a_source_row<G1>(P, row0 + (r < m ? r : 0)) * NS;
-    }
+    const float* xsp = P.as;               // row tid's activation scales
+    if (tid < BM) xsp = P.as + a_source_row<G1>(P, row0 + (tid < m ? tid : 0)) * NS;
     const uint8_t* wg = P.w + (long)g * P.N * K;
     const uint8_t* bp0 = wg + (long)(tl.n_lo + 16 * wave + lr) * K + 32 * lg;
     const uint8_t* bp1 = wg + (long)(tl.n_hi + 16 * wave + lr) * K + 32 * lg;
@@ -241,19 +245,15 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
     const float* wsh = (const float*)P.wsc + ((long)g * (P.N >> 7) + (tl.n_hi >> 7)) * NS;
 
     i32x4 ra[Gm::A_PT];
-    float rxs = 0.0f, rws = 0.0f;
+    float rxs = 0.0f;
     auto gload_a = [&](int s) {           // past the last block: re-read it
-      const int sc = min(s, NS - 1);
-      const long adv = (long)sc * 128;
+      const long adv = (long)min(s, NS - 1) * 128;
 #pragma unroll
       for (int i = 0; i < Gm::A_PT; ++i) ra[i] = *(const i32x4*)(ap[i] + adv);
-      if (tid < 2 * BM) {
-        rxs = xsp[sc];
-        rws = tid < BM ? wsl[sc] : wsh[sc];
-      }
+      if (tid < BM) rxs = xsp[min(s, NS - 1)];
     };
-    // expand the codes to bf16 into LDS buffer buf, with the row's combined
-    // scales xs * ws_lo and xs * ws_hi
+    // expand the codes to bf16 into LDS buffer buf; row scales as [16][MS]
+    // so that each lane reads its rows' scales (rows lr, lr + 16, ...) at once
     auto store_a = [&](int buf) {
       uint8_t* st = smem + buf * Gm::STAGE;
 #pragma unroll
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
               e4m3x8_bf16((uint32_t)v[2], (uint32_t)v[3]);
         }
       }
-      if (tid < 2 * BM) ((float*)(st + Gm::A_BYTES))[tid] = rxs * rws;
+      if (tid < BM) ((float*)(st + Gm::A_BYTES))[(tid & 15) * MS + (tid >> 4)] = rxs;
     };
     auto gload_b = [&](i32x4 (&rb)[4], int s) {
       const long adv = (long)min(s, NS - 1) * 128;
@@ -300,10 +300,25 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
           bw[ns][2 * h] = e4m3x8_bf16((uint32_t)v[0], (uint32_t)v[1]);
           bw[ns][2 * h + 1] = e4m3x8_bf16((uint32_t)v[2], (uint32_t)v[3]);
         }
+      const float wl = wsl[s], wh = wsh[s];
       gload_a(s + 1);
       gload_b(rb, s + 2);
       const uint8_t* sa = smem + buf * Gm::STAGE;
-      const float* sc = (const float*)(sa + Gm::A_BYTES);
+      // this lane's activation scales for rows lr + 16 ms
+      float xs[MS];
+      {
+        const float* sx = (const float*)(sa + Gm::A_BYTES) + lr * MS;
+        if constexpr (MS >= 4) {
+#pragma unroll
+          for (int i = 0; i < MS; i += 4) {
+            const f32x4 v = *(const f32x4*)(sx + i);
+            xs[i] = v[0]; xs[i + 1] = v[1]; xs[i + 2] = v[2]; xs[i + 3] = v[3];
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < MS; ++i) xs[i] = sx[i];
+        }
+      }
       auto lds_a = [&](int ms, bf16x8 (&af)[4]) {
         const int row = 16 * ms + lr;
 #pragma unroll
@@ -311,51 +326,46 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
           af[j] = *(const bf16x8*)(sa + row * 256 + 16 * swz16(row, 4 * lg + j));
       };
       // software pipeline over the 16-row subtiles: while the MFMAs of
-      // subtile ms run, the A fragments of ms + 1 and the scales of ms - 1
-      // are in flight and ms - 1 is scaled into the accumulator. The
-      // scheduling fences keep the live registers to that working set.
-      auto load_c = [&](int ms, f32x4& cl, f32x4& ch) {
-        cl = *(const f32x4*)(sc + 16 * ms + 4 * lg);
-        ch = *(const f32x4*)(sc + BM + 16 * ms + 4 * lg);
-      };
-      auto scale_into = [&](int ms, const f32x4& p0, const f32x4& p1, const f32x4& cl,
-                            const f32x4& ch) {
+      // subtile ms run, the A fragments of ms + 1 are in flight and ms - 1
+      // is scaled into the accumulator. The scheduling fences keep the live
+      // registers to that working set.
+      auto scale_into = [&](int ms, const f32x4& p0, const f32x4& p1) {
+        const float cl = xs[ms] * wl, ch = xs[ms] * wh;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          acc[ms][0][r] = fmaf(p0[r], cl[r], acc[ms][0][r]);
-          acc[ms][1][r] = fmaf(p1[r], ch[r], acc[ms][1][r]);
+          acc[ms][0][r] = fmaf(p0[r], cl, acc[ms][0][r]);
+          acc[ms][1][r] = fmaf(p1[r], ch, acc[ms][1][r]);
         }
         asm volatile("" : "+v"(acc[ms][0]), "+v"(acc[ms][1]));   // keep in place
       };
-      // two named fragment / partial sets alternate between even and odd
-      // subtiles, so the pipeline needs no register copies
+      // weights as the first MFMA operand: p[r] = weight column 4 lg + r of
+      // the wave's 16, activation row lr
       auto sub = [&](const bf16x8 (&af)[4], f32x4& p0, f32x4& p1) {
         p0 = (f32x4){0.f, 0.f, 0.f, 0.f};
         p1 = p0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], bw[0][j], p0, 0, 0, 0);
-          p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], bw[1][j], p1, 0, 0, 0);
+          p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw[0][j], af[j], p0, 0, 0, 0);
+          p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw[1][j], af[j], p1, 0, 0, 0);
         }
       };
+      // two named fragment / partial sets alternate between even and odd
+      // subtiles, so the pipeline needs no register copies
       bf16x8 fa[4], fb[4];
-      f32x4 pa0, pa1, pb0, pb1, cl, ch;
+      f32x4 pa0, pa1, pb0, pb1;
       lds_a(0, fa);
 #pragma unroll
       for (int ms = 0; ms < MS; ms += 2) {
         lds_a(ms + 1, fb);
-        if (ms > 0) load_c(ms - 1, cl, ch);
         sub(fa, pa0, pa1);
-        if (ms > 0) scale_into(ms - 1, pb0, pb1, cl, ch);
+        if (ms > 0) scale_into(ms - 1, pb0, pb1);
         __builtin_amdgcn_sched_barrier(0);
         if (ms + 2 < MS) lds_a(ms + 2, fa);
-        load_c(ms, cl, ch);
         sub(fb, pb0, pb1);
-        scale_into(ms, pa0, pa1, cl, ch);
+        scale_into(ms, pa0, pa1);
         __builtin_amdgcn_sched_barrier(0);
       }
-      load_c(MS - 1, cl, ch);
-      scale_into(MS - 1, pb0, pb1, cl, ch);
+      scale_into(MS - 1, pb0, pb1);
       store_a(buf ^ 1);
     };
 
