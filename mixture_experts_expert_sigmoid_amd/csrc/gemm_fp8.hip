@@ -354,15 +354,27 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
       bf16x8 fa[4], fb[4];
       f32x4 pa0, pa1, pb0, pb1;
       lds_a(0, fa);
+      // order inside a region: the prefetch reads first, then the MFMAs
+      // with the scaling arithmetic spread between them
+      auto pattern = [&](bool reads) {
+        if (reads) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // DS read
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
+          if (i < 5) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0); // VALU
+        }
+      };
 #pragma unroll
       for (int ms = 0; ms < MS; ms += 2) {
         lds_a(ms + 1, fb);
         sub(fa, pa0, pa1);
         if (ms > 0) scale_into(ms - 1, pb0, pb1);
+        pattern(true);
         __builtin_amdgcn_sched_barrier(0);
         if (ms + 2 < MS) lds_a(ms + 2, fa);
         sub(fb, pb0, pb1);
         scale_into(ms, pa0, pa1);
+        pattern(ms + 2 < MS);
         __builtin_amdgcn_sched_barrier(0);
       }
       scale_into(MS - 1, pb0, pb1);
