@@ -246,11 +246,15 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
 
     i32x4 ra[Gm::A_PT];
     float rxs = 0.0f;
+    float wl_n = 0.0f, wh_n = 0.0f;       // weight block scales, one block ahead
     auto gload_a = [&](int s) {           // past the last block: re-read it
-      const long adv = (long)min(s, NS - 1) * 128;
+      const int sc = min(s, NS - 1);
+      const long adv = (long)sc * 128;
 #pragma unroll
       for (int i = 0; i < Gm::A_PT; ++i) ra[i] = *(const i32x4*)(ap[i] + adv);
-      if (tid < BM) rxs = xsp[min(s, NS - 1)];
+      if (tid < BM) rxs = xsp[sc];
+      wl_n = wsl[sc];
+      wh_n = wsh[sc];
     };
     // expand the codes to bf16 into LDS buffer buf; row scales as [16][MS]
     // so that each lane reads its rows' scales (rows lr, lr + 16, ...) at once
@@ -300,7 +304,9 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
           bw[ns][2 * h] = e4m3x8_bf16((uint32_t)v[0], (uint32_t)v[1]);
           bw[ns][2 * h + 1] = e4m3x8_bf16((uint32_t)v[2], (uint32_t)v[3]);
         }
-      const float wl = wsl[s], wh = wsh[s];
+      // block s's weight scales arrived with its activations; reading them
+      // here would expose a global-load latency per block on small tiles
+      const float wl = wl_n, wh = wh_n;
       gload_a(s + 1);
       gload_b(rb, s + 2);
       const uint8_t* sa = smem + buf * Gm::STAGE;
