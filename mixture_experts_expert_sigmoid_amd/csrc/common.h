@@ -48,23 +48,60 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
   return sign | ((r >> 20) - (120u << 3));          // rebias 127 -> 7
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+// Cross-lane reductions in registers. Within a row of 16 lanes: DPP
+// quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror (each lane
+// meets every other lane of its row once). Across rows: gfx950's
+// v_permlane16_swap / v_permlane32_swap exchange rows so that lane l meets
+// l ^ 16 and l ^ 32. Every lane ends with the same result; the combination
+// order is fixed, so sums are deterministic. (A __shfl_xor butterfly goes
+// through LDS, one round trip per step.)
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+
+template <typename T, typename Op>
+__device__ __forceinline__ T row16_reduce(T v, Op op) {
+  v = op(v, __builtin_bit_cast(T, dpp_u32<0xB1>(__builtin_bit_cast(uint32_t, v))));
+  v = op(v, __builtin_bit_cast(T, dpp_u32<0x4E>(__builtin_bit_cast(uint32_t, v))));
+  v = op(v, __builtin_bit_cast(T, dpp_u32<0x141>(__builtin_bit_cast(uint32_t, v))));
+  v = op(v, __builtin_bit_cast(T, dpp_u32<0x140>(__builtin_bit_cast(uint32_t, v))));
   return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+// op(v[l], v[l ^ 16]) and op(v[l], v[l ^ 32]), lower row first
+template <typename T, typename Op>
+__device__ __forceinline__ T xor16_reduce(T v, Op op) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return op(__builtin_bit_cast(T, (uint32_t)p[0]), __builtin_bit_cast(T, (uint32_t)p[1]));
+}
+template <typename T, typename Op>
+__device__ __forceinline__ T xor32_reduce(T v, Op op) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return op(__builtin_bit_cast(T, (uint32_t)p[0]), __builtin_bit_cast(T, (uint32_t)p[1]));
 }
 
-// max over the 16 lanes that share lane / 16 (xor over lane bits 0..3)
-__device__ __forceinline__ float max16(float v) {
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  return xor32_reduce(xor16_reduce(row16_reduce(v, op), op), op);
+}
+
+struct OpMax { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+struct OpSum { __device__ float operator()(float a, float b) const { return a + b; } };
+struct OpMinI { __device__ int operator()(int a, int b) const { return a < b ? a : b; } };
+
+__device__ __forceinline__ float wave_max(float v) { return wave_reduce(v, OpMax{}); }
+__device__ __forceinline__ float wave_sum(float v) { return wave_reduce(v, OpSum{}); }
+__device__ __forceinline__ int wave_min_i32(int v) { return wave_reduce(v, OpMinI{}); }
+
+// max over the 16 lanes that share lane / 16
+__device__ __forceinline__ float max16(float v) { return row16_reduce(v, OpMax{}); }
+
+// max over the 4 lanes that share lane % 16
+__device__ __forceinline__ float max_across_rows(float v) {
+  return xor32_reduce(xor16_reduce(v, OpMax{}), OpMax{});
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }

@@ -158,8 +158,7 @@ __device__ __forceinline__ void fp8_epilogue(const GemmParams& P, const Tile& t,
     for (int ms = 0; ms < MS; ++ms) {
       float a = fmaxf(fmaxf(fabsf(hv[ms][0]), fabsf(hv[ms][1])),
                       fmaxf(fabsf(hv[ms][2]), fabsf(hv[ms][3])));
-      a = fmaxf(a, __shfl_xor(a, 16, kWave));
-      a = fmaxf(a, __shfl_xor(a, 32, kWave));
+      a = max_across_rows(a);
       if (lg == 0) s_amax[(16 * ms + lr) * 8 + wave] = a;
     }
     __syncthreads();

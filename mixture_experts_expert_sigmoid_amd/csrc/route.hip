@@ -10,9 +10,10 @@
 // the normaliser only.
 //
 // One wave64 owns one token row. Lane l holds columns l, l + 64, ... of the
-// routed part in registers; each pass reduces (value, column) across the wave
-// with a butterfly, the owner lane marks the winner taken. Equal values
-// resolve to the lower column. After k passes lane j < k holds slot j's raw
+// routed part in registers; each pass takes the wave maximum of the lanes'
+// best values, then the lowest column holding it (register-level DPP /
+// row-swap reductions), and the owner lane marks the winner taken. Equal
+// values resolve to the lower column. After k passes lane j < k holds slot j's raw
 // logit and lanes k .. k+S-1 the sink logits; the renormalisation is a wave
 // max and a wave sum.
 #include "common.h"
@@ -50,14 +51,11 @@ __global__ __launch_bounds__(256) void route_kernel(
       bool cand = !((taken >> i) & 1u);
       if (cand && (v[i] > bv || (v[i] == bv && c < bc))) { bv = v[i]; bc = c; }
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      float ov = __shfl_xor(bv, o, kWave);
-      int oc = __shfl_xor(bc, o, kWave);
-      if (ov > bv || (ov == bv && oc < bc)) { bv = ov; bc = oc; }
-    }
+    // winner: the largest value, then the lowest column holding it
+    const float wv = wave_max(bv);
+    bc = wave_min_i32(bv == wv ? bc : 0x7FFFFFFF);
     if ((bc & 63) == lane) taken |= 1u << (bc >> 6);
-    if (lane == j) { my_x = bv; my_c = bc; }
+    if (lane == j) { my_x = wv; my_c = bc; }
   }
   const bool active = lane < k + n_sink;
   if (lane >= k && active) my_x = x[n_routed + (lane - k)];
