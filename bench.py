@@ -58,6 +58,10 @@ def parse():
                     help="run only the forward at --profile-tokens (warmup + steps) and "
                          "a copy of known size, for rocprofv3 counter passes")
     ap.add_argument("--profile-tokens", type=int, default=T_MAIN)
+    ap.add_argument("--configs", action="store_true",
+                    help="also time moe_forward on every seeded configuration at its "
+                         "token counts and print a table to stderr (not part of the "
+                         "JSON line)")
     return ap.parse_args()
 
 
@@ -241,6 +245,9 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(spec, layer, r["batch"], T_MAIN)
 
+    if args.configs:
+        config_table(args, stream)
+
     main_ms = results[T_MAIN]["ms"]
     line = {
         "metric": METRIC, "value": round(T_MAIN / (main_ms * 1e-3), 1),
@@ -256,6 +263,49 @@ def main():
         "sweep": sweep,
     }
     print(json.dumps(line))
+
+
+def config_table(args, stream):
+    """moe_forward time per seeded configuration and token count, with the
+    touched-weight GB/s and useful TFLOP/s (stderr)."""
+    import torch
+    from synth import CONFIGS, make_batch, make_layer
+    from tests.gpu_helpers import module_for
+    print("# config              T       ms/step    tokens/s    TFLOP/s   weight GB/s",
+          file=sys.stderr)
+    for name, spec in CONFIGS.items():
+        layer = make_layer(spec, device="cuda")
+        mod = module_for(spec, layer)
+        for T in spec.Ts:
+            batch = make_batch(spec, layer, T, device="cuda")
+            outs = mod.alloc_outputs(T)
+            mod.workspace(T)
+            for _ in range(args.warmup):
+                mod.forward(batch.x, batch.logits, outs)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record(stream)
+            for _ in range(args.steps):
+                mod.forward(batch.x, batch.logits, outs)
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / args.steps
+            ids = outs["topk_ids"].cpu().numpy()
+            e_loc = ids.reshape(-1) - spec.offset
+            local = (e_loc >= 0) & (e_loc < spec.n_local)
+            touched = len(set(e_loc[local].tolist())) + (spec.shared if T > 0 else 0)
+            P = int(local.sum()) + (T if spec.shared else 0)
+            bytes_w = layer.w13_q[0].numel() * layer.w13_q.element_size() + \
+                layer.w2_q[0].numel() * layer.w2_q.element_size()
+            if layer.w13_s is not None:
+                bytes_w += layer.w13_s[0].numel() * layer.w13_s.element_size() + \
+                    layer.w2_s[0].numel() * layer.w2_s.element_size()
+            fl = 6.0 * P * spec.H * spec.I
+            print(f"# {name:18s} {T:5d} {ms:12.4f} {T / ms * 1e3:11.1f} "
+                  f"{fl / ms / 1e9:10.2f} {touched * bytes_w / ms / 1e6:12.1f}",
+                  file=sys.stderr, flush=True)
+        del layer, mod
+        torch.cuda.empty_cache()
 
 
 def cpu_baseline(spec, layer, batch, T, n_experts=20):

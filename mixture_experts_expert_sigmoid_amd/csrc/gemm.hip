@@ -328,7 +328,7 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t s) {
   P.h = (uint8_t*)a.h;
   P.hs = a.hs;
   long hint = a.G > 0 ? a.p_cap / a.G : a.p_cap;
-  if (a.fmt == FMT_FP8) return launch_gemm_fp8(P, true, a.p_cap, a.I / 128, hint, s);
+  if (a.fmt == FMT_FP8) return launch_gemm_fp8(P, true, a.p_cap, a.I / 128, s);
   return dispatch<true>(a.fmt, P, a.p_cap, a.I / 128, hint, s);
 }
 
@@ -346,7 +346,7 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t s) {
   P.I = a.I;
   P.y = a.y;
   long hint = a.G > 0 ? a.p_cap / a.G : a.p_cap;
-  if (a.fmt == FMT_FP8) return launch_gemm_fp8(P, false, a.p_cap, (a.H + 255) / 256, hint, s);
+  if (a.fmt == FMT_FP8) return launch_gemm_fp8(P, false, a.p_cap, (a.H + 255) / 256, s);
   return dispatch<false>(a.fmt, P, a.p_cap, (a.H + 255) / 256, hint, s);
 }
 

@@ -276,7 +276,6 @@ __device__ __forceinline__ void tile_epilogue(const GemmParams& P, const Tile& t
 int num_cus();
 
 // Blockwise-FP8 grouped GEMM (gemm_fp8.hip).
-hipError_t launch_gemm_fp8(const GemmParams& P, bool g1, long p_cap, int NT, long rows_hint,
-                           hipStream_t s);
+hipError_t launch_gemm_fp8(const GemmParams& P, bool g1, long p_cap, int NT, hipStream_t s);
 
 }  // namespace moe

@@ -194,21 +194,214 @@ __device__ __forceinline__ void fp8_epilogue(const GemmParams& P, const Tile& t,
   }
 }
 
+// One tile of BM rows (BM = 32, 64 or 128; the rows at and after tl.m are
+// padding): staging, K loop and epilogue. Called by the whole workgroup.
 template <int BM, bool G1>
-__global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
+__device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, uint8_t* smem) {
   using Gm = F8Geo<BM>;
   constexpr int MS = Gm::MS;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int K = P.K;
+  const int NS = K >> 7;                      // K blocks of 128
+  const int g = tl.g, row0 = tl.row0, m = tl.m;
+
+  // ---- this thread's sources at K block 0 (+128 bytes per block) --------
+  const uint8_t* ap[Gm::A_PT];
+  int a_st[Gm::A_PT];
+#pragma unroll
+  for (int i = 0; i < Gm::A_PT; ++i) {
+    const int cc = min(tid + i * kThreads, Gm::A_CH - 1);
+    const int row = cc >> 3, ch = cc & 7;
+    ap[i] = P.a + a_source_row<G1>(P, row0 + (row < m ? row : 0)) * P.a_ld + ch * 16;
+    a_st[i] = row * 256;
+  }
+  const float* xsp = P.as;               // row tid's activation scales
+  if (tid < BM) xsp = P.as + a_source_row<G1>(P, row0 + (tid < m ? tid : 0)) * NS;
+  const uint8_t* wg = P.w + (long)g * P.N * K;
+  const uint8_t* bp0 = wg + (long)(tl.n_lo + 16 * wave + lr) * K + 32 * lg;
+  const uint8_t* bp1 = wg + (long)(tl.n_hi + 16 * wave + lr) * K + 32 * lg;
+  const float* wsl = (const float*)P.wsc + ((long)g * (P.N >> 7) + (tl.n_lo >> 7)) * NS;
+  const float* wsh = (const float*)P.wsc + ((long)g * (P.N >> 7) + (tl.n_hi >> 7)) * NS;
+
+  i32x4 ra[Gm::A_PT];
+  float rxs = 0.0f;
+  float wl_n = 0.0f, wh_n = 0.0f;       // weight block scales, one block ahead
+  auto gload_a = [&](int s) {           // past the last block: re-read it
+    const int sc = min(s, NS - 1);
+    const long adv = (long)sc * 128;
+#pragma unroll
+    for (int i = 0; i < Gm::A_PT; ++i) ra[i] = *(const i32x4*)(ap[i] + adv);
+    if (tid < BM) rxs = xsp[sc];
+    wl_n = wsl[sc];
+    wh_n = wsh[sc];
+  };
+  // expand the codes to bf16 into LDS buffer buf; row scales as [16][MS]
+  // so that each lane reads its rows' scales (rows lr, lr + 16, ...) at once
+  auto store_a = [&](int buf) {
+    uint8_t* st = smem + buf * Gm::STAGE;
+#pragma unroll
+    for (int i = 0; i < Gm::A_PT; ++i) {
+      if (Gm::A_CH % kThreads == 0 || tid + i * kThreads < Gm::A_CH) {
+        const int cc = tid + i * kThreads, row = cc >> 3, ch = cc & 7;
+        const i32x4 v = ra[i];
+        *(bf16x8*)(st + a_st[i] + 16 * swz16(row, 2 * ch)) =
+            e4m3x8_bf16((uint32_t)v[0], (uint32_t)v[1]);
+        *(bf16x8*)(st + a_st[i] + 16 * swz16(row, 2 * ch + 1)) =
+            e4m3x8_bf16((uint32_t)v[2], (uint32_t)v[3]);
+      }
+    }
+    if (tid < BM) ((float*)(st + Gm::A_BYTES))[(tid & 15) * MS + (tid >> 4)] = rxs;
+  };
+  auto gload_b = [&](i32x4 (&rb)[4], int s) {
+    const long adv = (long)min(s, NS - 1) * 128;
+    rb[0] = *(const i32x4*)(bp0 + adv);
+    rb[1] = *(const i32x4*)(bp0 + adv + 16);
+    rb[2] = *(const i32x4*)(bp1 + adv);
+    rb[3] = *(const i32x4*)(bp1 + adv + 16);
+  };
+
+  f32x4 acc[MS][2];
+#pragma unroll
+  for (int i = 0; i < MS; ++i) {
+    acc[i][0] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    acc[i][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+
+  // One K block: expand this block's weights, prefetch (A one block ahead,
+  // B two blocks ahead into the registers just freed), then MFMA + scale.
+  auto block = [&](int s, int buf, i32x4 (&rb)[4]) {
+    // pin this block's weight registers here so their expansion is not
+    // hoisted into the previous block (it would double the live registers)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(rb[i]));
+    bf16x8 bw[2][4];
+#pragma unroll
+    for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const i32x4 v = rb[2 * ns + h];
+        bw[ns][2 * h] = e4m3x8_bf16((uint32_t)v[0], (uint32_t)v[1]);
+        bw[ns][2 * h + 1] = e4m3x8_bf16((uint32_t)v[2], (uint32_t)v[3]);
+      }
+    // block s's weight scales arrived with its activations; reading them
+    // here would expose a global-load latency per block on small tiles
+    const float wl = wl_n, wh = wh_n;
+    gload_a(s + 1);
+    gload_b(rb, s + 2);
+    const uint8_t* sa = smem + buf * Gm::STAGE;
+    // this lane's activation scales for rows lr + 16 ms
+    float xs[MS];
+    {
+      const float* sx = (const float*)(sa + Gm::A_BYTES) + lr * MS;
+      if constexpr (MS >= 4) {
+#pragma unroll
+        for (int i = 0; i < MS; i += 4) {
+          const f32x4 v = *(const f32x4*)(sx + i);
+          xs[i] = v[0]; xs[i + 1] = v[1]; xs[i + 2] = v[2]; xs[i + 3] = v[3];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < MS; ++i) xs[i] = sx[i];
+      }
+    }
+    auto lds_a = [&](int ms, bf16x8 (&af)[4]) {
+      const int row = 16 * ms + lr;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        af[j] = *(const bf16x8*)(sa + row * 256 + 16 * swz16(row, 4 * lg + j));
+    };
+    // software pipeline over the 16-row subtiles: while the MFMAs of
+    // subtile ms run, the A fragments of ms + 1 are in flight and ms - 1
+    // is scaled into the accumulator. The scheduling fences keep the live
+    // registers to that working set.
+    auto scale_into = [&](int ms, const f32x4& p0, const f32x4& p1) {
+      const float cl = xs[ms] * wl, ch = xs[ms] * wh;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        acc[ms][0][r] = fmaf(p0[r], cl, acc[ms][0][r]);
+        acc[ms][1][r] = fmaf(p1[r], ch, acc[ms][1][r]);
+      }
+      asm volatile("" : "+v"(acc[ms][0]), "+v"(acc[ms][1]));   // keep in place
+    };
+    // weights as the first MFMA operand: p[r] = weight column 4 lg + r of
+    // the wave's 16, activation row lr
+    auto sub = [&](const bf16x8 (&af)[4], f32x4& p0, f32x4& p1) {
+      p0 = (f32x4){0.f, 0.f, 0.f, 0.f};
+      p1 = p0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw[0][j], af[j], p0, 0, 0, 0);
+        p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw[1][j], af[j], p1, 0, 0, 0);
+      }
+    };
+    // two named fragment / partial sets alternate between even and odd
+    // subtiles, so the pipeline needs no register copies
+    bf16x8 fa[4], fb[4];
+    f32x4 pa0, pa1, pb0, pb1;
+    lds_a(0, fa);
+    // order inside a region: the prefetch reads first, then the MFMAs
+    // with the scaling arithmetic spread between them
+    auto pattern = [&](bool reads) {
+      if (reads) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // DS read
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
+        if (i < 5) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0); // VALU
+      }
+    };
+#pragma unroll
+    for (int ms = 0; ms < MS; ms += 2) {
+      lds_a(ms + 1, fb);
+      sub(fa, pa0, pa1);
+      if (ms > 0) scale_into(ms - 1, pb0, pb1);
+      pattern(true);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ms + 2 < MS) lds_a(ms + 2, fa);
+      sub(fb, pb0, pb1);
+      scale_into(ms, pa0, pa1);
+      pattern(ms + 2 < MS);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    scale_into(MS - 1, pb0, pb1);
+    store_a(buf ^ 1);
+  };
+
+  i32x4 rb0[4], rb1[4];
+  gload_b(rb0, 0);
+  gload_b(rb1, 1);
+  gload_a(0);
+  store_a(0);
+  __syncthreads();
+  int s = 0;
+  for (; s + 2 <= NS; s += 2) {
+    block(s, 0, rb0);
+    __syncthreads();
+    block(s + 1, 1, rb1);
+    __syncthreads();
+  }
+  if (s < NS) {            // odd block count
+    block(s, 0, rb0);
+    __syncthreads();
+  }
+  fp8_epilogue<BM, G1>(P, tl, acc, smem);
+  __syncthreads();         // LDS is reused by the next tile
+}
+
+// Tiles are scheduled with up to TBM rows of one expert; each runs the code
+// of the smallest row class (32 / 64 / 128, at most TBM) that holds its
+// valid rows, so a lightly loaded expert does not pay for TBM rows of MFMA
+// work.
+template <int TBM, bool G1>
+__global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // 2 stages
   __shared__ int s_cum[kMaxGroups + 1];
   __shared__ int s_wsum[8];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, lg = lane >> 4;
-  const int G = P.G, K = P.K;
+  const int G = P.G;
   const int NT = G1 ? (P.I >> 7) : ((P.N + 255) >> 8);
-  const int NS = K >> 7;                      // K blocks of 128
 
-  tile_prefix<BM>(P.offsets, G, s_cum, s_wsum);
+  tile_prefix<TBM>(P.offsets, G, s_cum, s_wsum);
   const int total = s_cum[G] * NT;
   // XCD x (= blockIdx % 8) owns logical tiles [x*chunk, (x+1)*chunk)
   const int xcd = blockIdx.x & 7, nper = gridDim.x >> 3, slot = blockIdx.x >> 3;
@@ -216,233 +409,57 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
   const int t_end = min(total, (xcd + 1) * chunk);
 
   for (int lt = xcd * chunk + slot; lt < t_end; lt += nper) {
-    Tile tl = decode_tile<BM, G1>(P, lt, NT, s_cum);
+    Tile tl = decode_tile<TBM, G1>(P, lt, NT, s_cum);
     tl.g = __builtin_amdgcn_readfirstlane(tl.g);
     tl.row0 = __builtin_amdgcn_readfirstlane(tl.row0);
     tl.m = __builtin_amdgcn_readfirstlane(tl.m);
     tl.nt = __builtin_amdgcn_readfirstlane(tl.nt);
     tl.n_lo = __builtin_amdgcn_readfirstlane(tl.n_lo);
     tl.n_hi = __builtin_amdgcn_readfirstlane(tl.n_hi);
-    const int g = tl.g, row0 = tl.row0, m = tl.m;
-
-    // ---- this thread's sources at K block 0 (+128 bytes per block) --------
-    const uint8_t* ap[Gm::A_PT];
-    int a_st[Gm::A_PT];
-#pragma unroll
-    for (int i = 0; i < Gm::A_PT; ++i) {
-      const int cc = min(tid + i * kThreads, Gm::A_CH - 1);
-      const int row = cc >> 3, ch = cc & 7;
-      ap[i] = P.a + a_source_row<G1>(P, row0 + (row < m ? row : 0)) * P.a_ld + ch * 16;
-      a_st[i] = row * 256;
+    if constexpr (TBM >= 128) {
+      if (tl.m > 64) { fp8_tile<128, G1>(P, tl, smem); continue; }
     }
-    const float* xsp = P.as;               // row tid's activation scales
-    if (tid < BM) xsp = P.as + a_source_row<G1>(P, row0 + (tid < m ? tid : 0)) * NS;
-    const uint8_t* wg = P.w + (long)g * P.N * K;
-    const uint8_t* bp0 = wg + (long)(tl.n_lo + 16 * wave + lr) * K + 32 * lg;
-    const uint8_t* bp1 = wg + (long)(tl.n_hi + 16 * wave + lr) * K + 32 * lg;
-    const float* wsl = (const float*)P.wsc + ((long)g * (P.N >> 7) + (tl.n_lo >> 7)) * NS;
-    const float* wsh = (const float*)P.wsc + ((long)g * (P.N >> 7) + (tl.n_hi >> 7)) * NS;
-
-    i32x4 ra[Gm::A_PT];
-    float rxs = 0.0f;
-    float wl_n = 0.0f, wh_n = 0.0f;       // weight block scales, one block ahead
-    auto gload_a = [&](int s) {           // past the last block: re-read it
-      const int sc = min(s, NS - 1);
-      const long adv = (long)sc * 128;
-#pragma unroll
-      for (int i = 0; i < Gm::A_PT; ++i) ra[i] = *(const i32x4*)(ap[i] + adv);
-      if (tid < BM) rxs = xsp[sc];
-      wl_n = wsl[sc];
-      wh_n = wsh[sc];
-    };
-    // expand the codes to bf16 into LDS buffer buf; row scales as [16][MS]
-    // so that each lane reads its rows' scales (rows lr, lr + 16, ...) at once
-    auto store_a = [&](int buf) {
-      uint8_t* st = smem + buf * Gm::STAGE;
-#pragma unroll
-      for (int i = 0; i < Gm::A_PT; ++i) {
-        if (Gm::A_CH % kThreads == 0 || tid + i * kThreads < Gm::A_CH) {
-          const int cc = tid + i * kThreads, row = cc >> 3, ch = cc & 7;
-          const i32x4 v = ra[i];
-          *(bf16x8*)(st + a_st[i] + 16 * swz16(row, 2 * ch)) =
-              e4m3x8_bf16((uint32_t)v[0], (uint32_t)v[1]);
-          *(bf16x8*)(st + a_st[i] + 16 * swz16(row, 2 * ch + 1)) =
-              e4m3x8_bf16((uint32_t)v[2], (uint32_t)v[3]);
-        }
-      }
-      if (tid < BM) ((float*)(st + Gm::A_BYTES))[(tid & 15) * MS + (tid >> 4)] = rxs;
-    };
-    auto gload_b = [&](i32x4 (&rb)[4], int s) {
-      const long adv = (long)min(s, NS - 1) * 128;
-      rb[0] = *(const i32x4*)(bp0 + adv);
-      rb[1] = *(const i32x4*)(bp0 + adv + 16);
-      rb[2] = *(const i32x4*)(bp1 + adv);
-      rb[3] = *(const i32x4*)(bp1 + adv + 16);
-    };
-
-    f32x4 acc[MS][2];
-#pragma unroll
-    for (int i = 0; i < MS; ++i) {
-      acc[i][0] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      acc[i][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    if constexpr (TBM >= 64) {
+      if (tl.m > 32) { fp8_tile<64, G1>(P, tl, smem); continue; }
     }
-
-    // One K block: expand this block's weights, prefetch (A one block ahead,
-    // B two blocks ahead into the registers just freed), then MFMA + scale.
-    auto block = [&](int s, int buf, i32x4 (&rb)[4]) {
-      // pin this block's weight registers here so their expansion is not
-      // hoisted into the previous block (it would double the live registers)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(rb[i]));
-      bf16x8 bw[2][4];
-#pragma unroll
-      for (int ns = 0; ns < 2; ++ns)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const i32x4 v = rb[2 * ns + h];
-          bw[ns][2 * h] = e4m3x8_bf16((uint32_t)v[0], (uint32_t)v[1]);
-          bw[ns][2 * h + 1] = e4m3x8_bf16((uint32_t)v[2], (uint32_t)v[3]);
-        }
-      // block s's weight scales arrived with its activations; reading them
-      // here would expose a global-load latency per block on small tiles
-      const float wl = wl_n, wh = wh_n;
-      gload_a(s + 1);
-      gload_b(rb, s + 2);
-      const uint8_t* sa = smem + buf * Gm::STAGE;
-      // this lane's activation scales for rows lr + 16 ms
-      float xs[MS];
-      {
-        const float* sx = (const float*)(sa + Gm::A_BYTES) + lr * MS;
-        if constexpr (MS >= 4) {
-#pragma unroll
-          for (int i = 0; i < MS; i += 4) {
-            const f32x4 v = *(const f32x4*)(sx + i);
-            xs[i] = v[0]; xs[i + 1] = v[1]; xs[i + 2] = v[2]; xs[i + 3] = v[3];
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < MS; ++i) xs[i] = sx[i];
-        }
-      }
-      auto lds_a = [&](int ms, bf16x8 (&af)[4]) {
-        const int row = 16 * ms + lr;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          af[j] = *(const bf16x8*)(sa + row * 256 + 16 * swz16(row, 4 * lg + j));
-      };
-      // software pipeline over the 16-row subtiles: while the MFMAs of
-      // subtile ms run, the A fragments of ms + 1 are in flight and ms - 1
-      // is scaled into the accumulator. The scheduling fences keep the live
-      // registers to that working set.
-      auto scale_into = [&](int ms, const f32x4& p0, const f32x4& p1) {
-        const float cl = xs[ms] * wl, ch = xs[ms] * wh;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          acc[ms][0][r] = fmaf(p0[r], cl, acc[ms][0][r]);
-          acc[ms][1][r] = fmaf(p1[r], ch, acc[ms][1][r]);
-        }
-        asm volatile("" : "+v"(acc[ms][0]), "+v"(acc[ms][1]));   // keep in place
-      };
-      // weights as the first MFMA operand: p[r] = weight column 4 lg + r of
-      // the wave's 16, activation row lr
-      auto sub = [&](const bf16x8 (&af)[4], f32x4& p0, f32x4& p1) {
-        p0 = (f32x4){0.f, 0.f, 0.f, 0.f};
-        p1 = p0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw[0][j], af[j], p0, 0, 0, 0);
-          p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw[1][j], af[j], p1, 0, 0, 0);
-        }
-      };
-      // two named fragment / partial sets alternate between even and odd
-      // subtiles, so the pipeline needs no register copies
-      bf16x8 fa[4], fb[4];
-      f32x4 pa0, pa1, pb0, pb1;
-      lds_a(0, fa);
-      // order inside a region: the prefetch reads first, then the MFMAs
-      // with the scaling arithmetic spread between them
-      auto pattern = [&](bool reads) {
-        if (reads) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // DS read
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
-          if (i < 5) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0); // VALU
-        }
-      };
-#pragma unroll
-      for (int ms = 0; ms < MS; ms += 2) {
-        lds_a(ms + 1, fb);
-        sub(fa, pa0, pa1);
-        if (ms > 0) scale_into(ms - 1, pb0, pb1);
-        pattern(true);
-        __builtin_amdgcn_sched_barrier(0);
-        if (ms + 2 < MS) lds_a(ms + 2, fa);
-        sub(fb, pb0, pb1);
-        scale_into(ms, pa0, pa1);
-        pattern(ms + 2 < MS);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      scale_into(MS - 1, pb0, pb1);
-      store_a(buf ^ 1);
-    };
-
-    i32x4 rb0[4], rb1[4];
-    gload_b(rb0, 0);
-    gload_b(rb1, 1);
-    gload_a(0);
-    store_a(0);
-    __syncthreads();
-    int s = 0;
-    for (; s + 2 <= NS; s += 2) {
-      block(s, 0, rb0);
-      __syncthreads();
-      block(s + 1, 1, rb1);
-      __syncthreads();
-    }
-    if (s < NS) {            // odd block count
-      block(s, 0, rb0);
-      __syncthreads();
-    }
-    fp8_epilogue<BM, G1>(P, tl, acc, smem);
-    __syncthreads();         // LDS is reused by the next tile
+    fp8_tile<32, G1>(P, tl, smem);
   }
 }
 
-template <int BM, bool G1>
+template <int TBM, bool G1>
 static hipError_t run_fp8(const GemmParams& P, long p_cap, int NT, hipStream_t s) {
-  constexpr int shm = F8Geo<BM>::LDS;
+  constexpr int shm = F8Geo<TBM>::LDS;
   static int per_cu = 0;   // resident workgroups per CU, per instantiation
   if (per_cu == 0) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&moe_gemm_fp8_kernel<BM, G1>),
+        reinterpret_cast<const void*>(&moe_gemm_fp8_kernel<TBM, G1>),
         hipFuncAttributeMaxDynamicSharedMemorySize, shm);
     if (e != hipSuccess) return e;
     int nb = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &nb, reinterpret_cast<const void*>(&moe_gemm_fp8_kernel<BM, G1>), kThreads, shm);
+        &nb, reinterpret_cast<const void*>(&moe_gemm_fp8_kernel<TBM, G1>), kThreads, shm);
     if (e != hipSuccess) return e;
     per_cu = nb > 0 ? nb : 1;
   }
-  long max_tiles = ((p_cap + BM - 1) / BM + P.G) * (long)NT;
+  long max_tiles = ((p_cap + TBM - 1) / TBM + P.G) * (long)NT;
   long nwg = std::min<long>(max_tiles, (long)num_cus() * per_cu);
   nwg = (nwg + 7) & ~7L;
   if (nwg == 0) return hipSuccess;
-  moe_gemm_fp8_kernel<BM, G1><<<dim3((unsigned)nwg), dim3(kThreads), shm, s>>>(P);
+  moe_gemm_fp8_kernel<TBM, G1><<<dim3((unsigned)nwg), dim3(kThreads), shm, s>>>(P);
   return hipGetLastError();
 }
 
 template <bool G1>
-static hipError_t run_fp8_bm(const GemmParams& P, long p_cap, int NT, long rows_hint,
-                             hipStream_t s) {
-  if (rows_hint <= 32) return run_fp8<32, G1>(P, p_cap, NT, s);
-  if (rows_hint <= 64) return run_fp8<64, G1>(P, p_cap, NT, s);
+static hipError_t run_fp8_tbm(const GemmParams& P, long p_cap, int NT, hipStream_t s) {
+  // the largest row class worth scheduling: rows per group on average
+  const long hint = P.G > 0 ? p_cap / P.G : p_cap;
+  if (hint <= 32) return run_fp8<32, G1>(P, p_cap, NT, s);
+  if (hint <= 64) return run_fp8<64, G1>(P, p_cap, NT, s);
   return run_fp8<128, G1>(P, p_cap, NT, s);
 }
 
-hipError_t launch_gemm_fp8(const GemmParams& P, bool g1, long p_cap, int NT, long rows_hint,
-                           hipStream_t s) {
-  return g1 ? run_fp8_bm<true>(P, p_cap, NT, rows_hint, s)
-            : run_fp8_bm<false>(P, p_cap, NT, rows_hint, s);
+hipError_t launch_gemm_fp8(const GemmParams& P, bool g1, long p_cap, int NT, hipStream_t s) {
+  return g1 ? run_fp8_tbm<true>(P, p_cap, NT, s) : run_fp8_tbm<false>(P, p_cap, NT, s);
 }
 
 }  // namespace moe
