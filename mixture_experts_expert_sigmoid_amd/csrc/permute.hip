@@ -87,10 +87,18 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(
   // per-group totals and exclusive per-block prefixes
   int total = 0;
   if (tid < E_loc) {
-    for (long b = 0; b < nblk; ++b) {
-      int c = blockcnt[b * G + tid];
-      blockcnt[b * G + tid] = total;
-      total += c;
+    // 16 block counts in flight at a time (a dependent walk would pay one
+    // memory latency per block)
+    for (long b0 = 0; b0 < nblk; b0 += 16) {
+      int c[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c[i] = b0 + i < nblk ? blockcnt[(b0 + i) * G + tid] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (b0 + i < nblk) {
+          blockcnt[(b0 + i) * G + tid] = total;
+          total += c[i];
+        }
     }
   } else if (tid < G) {
     total = (int)T;                       // the shared group

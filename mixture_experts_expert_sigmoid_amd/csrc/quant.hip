@@ -68,56 +68,82 @@ hipError_t launch_quant_act(const void* x, long T, int H, void* xq, float* xs,
   return hipGetLastError();
 }
 
-// One wave per sorted row of a LoRA-carrying group.
-template <int R>
+// One workgroup (4 waves) per 16 consecutive sorted rows:
+// z[16 rows][16 ranks] = X A^T on v_mfma_f32_16x16x32_bf16 (bf16 products,
+// fp32 accumulation), the expert's A read once per tile instead of once
+// per row. Wave w covers the w-th quarter of H; the four partials are added
+// in wave order through LDS. Rows of a tile normally share one expert; a
+// tile that straddles expert boundaries is done once per expert it
+// touches, each pass keeping its own rows.
+template <int NQ>    // 16-column blocks covering the rank
 __global__ __launch_bounds__(256) void lora_z_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ A, int rank,
     long T, int H, int top_k, int n_lora_groups, long p_cap,
     const int* __restrict__ offsets, const int* __restrict__ sorted_pair,
     float* __restrict__ z) {
-  const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = lane_id();
-  if (r >= p_cap || r >= offsets[n_lora_groups]) return;
-  // group of row r: largest g with offsets[g] <= r
-  int lo = 0, hi = n_lora_groups - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (offsets[mid] <= r) lo = mid; else hi = mid - 1;
-  }
-  const int g = lo;
-  const int p = sorted_pair[r];
-  const long t = p / top_k;
-  const uint16_t* xr = x + t * H;
-  const uint16_t* Ag = A + (long)g * rank * H;
-  float acc[R];
+  __shared__ f32x4 red[4][NQ][64];
+  const long r0 = (long)blockIdx.x * 16;
+  const long rend = min(p_cap, (long)offsets[n_lora_groups]);
+  if (r0 >= rend) return;                        // uniform over the workgroup
+  const int wave = threadIdx.x >> 6, lane = lane_id(), lr = lane & 15, lg = lane >> 4;
+  auto group_of = [&](long row) {        // largest g with offsets[g] <= row
+    int lo = 0, hi = n_lora_groups - 1;
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (offsets[mid] <= row) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+  const int hq = H >> 2;                         // this wave's quarter of H
+  const long rl = min(r0 + lr, rend - 1);        // this lane's operand row
+  const uint16_t* xr = x + (long)(sorted_pair[rl] / top_k) * H + wave * hq + 8 * lg;
+  const int g0 = group_of(r0), g1 = group_of(min(r0 + 15, rend - 1));
+  for (int g = g0; g <= g1; ++g) {
+    const uint16_t* Ag = A + (long)g * rank * H + wave * hq + 8 * lg;
+    f32x4 acc[NQ];
 #pragma unroll
-  for (int q = 0; q < R; ++q) acc[q] = 0.0f;
-  for (int h0 = lane * 8; h0 < H; h0 += 512) {
-    i32x4 xv = *(const i32x4*)(xr + h0);
-    float xf[8];
+    for (int n = 0; n < NQ; ++n) acc[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    // 8 K steps per round: all their loads are issued before the MFMAs
+    for (int h0 = 0; h0 < hq; h0 += 256) {
+      i32x4 xv[8], av[NQ][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      xf[2 * i] = bf16_bits_to_f32((uint32_t)xv[i] & 0xFFFFu);
-      xf[2 * i + 1] = bf16_bits_to_f32((uint32_t)xv[i] >> 16);
+      for (int j = 0; j < 8; ++j) {
+        const int h = min(h0 + 32 * j, hq - 32);   // hq % 32 == 0
+        xv[j] = *(const i32x4*)(xr + h);
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) {
+          const int q = 16 * n + lr;
+          av[n][j] = (i32x4){0, 0, 0, 0};
+          if (q < rank) av[n][j] = *(const i32x4*)(Ag + (long)q * H + h);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (h0 + 32 * j >= hq) break;
+#pragma unroll
+        for (int n = 0; n < NQ; ++n)
+          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[j]),
+                                                          __builtin_bit_cast(bf16x8, av[n][j]),
+                                                          acc[n], 0, 0, 0);
+      }
     }
 #pragma unroll
-    for (int q = 0; q < R; ++q) {
-      if (q < rank) {
-        i32x4 av = *(const i32x4*)(Ag + (long)q * H + h0);
+    for (int n = 0; n < NQ; ++n) red[wave][n][lane] = acc[n];
+    __syncthreads();
+    if (wave == 0) {
+      const long glo = offsets[g], ghi = min((long)offsets[g + 1], rend);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[q] += xf[2 * i] * bf16_bits_to_f32((uint32_t)av[i] & 0xFFFFu);
-          acc[q] += xf[2 * i + 1] * bf16_bits_to_f32((uint32_t)av[i] >> 16);
+      for (int n = 0; n < NQ; ++n) {
+        const f32x4 v = ((red[0][n][lane] + red[1][n][lane]) + red[2][n][lane]) + red[3][n][lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const long row = r0 + 4 * lg + r;
+          const int q = 16 * n + lr;
+          if (row >= glo && row < ghi && q < rank) z[row * rank + q] = v[r];
         }
       }
     }
-  }
-#pragma unroll
-  for (int q = 0; q < R; ++q) {
-    if (q < rank) {
-      float v = wave_sum(acc[q]);
-      if (lane == 0) z[r * rank + q] = v;
-    }
+    __syncthreads();
   }
 }
 
@@ -126,14 +152,14 @@ hipError_t launch_lora_z(const void* x_bf16, const void* A, int rank, long T,
                          const int* offsets, const int* sorted_pair, float* z,
                          hipStream_t s) {
   if (p_cap == 0 || n_lora_groups == 0) return hipSuccess;
-  dim3 grid((unsigned)((p_cap + 3) / 4)), block(256);
-#define LZ(R)                                                                 \
-  hipLaunchKernelGGL(lora_z_kernel<R>, grid, block, 0, s,                     \
+  const long tiles = (p_cap + 15) / 16;
+  dim3 grid((unsigned)tiles), block(256);
+#define LZ(NQ)                                                                \
+  hipLaunchKernelGGL(lora_z_kernel<NQ>, grid, block, 0, s,                    \
                      (const uint16_t*)x_bf16, (const uint16_t*)A, rank, T, H, \
                      top_k, n_lora_groups, p_cap, offsets, sorted_pair, z)
-  if (rank <= 8) LZ(8);
-  else if (rank <= 16) LZ(16);
-  else LZ(32);
+  if (rank <= 16) LZ(1);
+  else LZ(2);
 #undef LZ
   return hipGetLastError();
 }
