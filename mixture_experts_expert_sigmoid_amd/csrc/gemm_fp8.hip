@@ -7,16 +7,22 @@
 // dropping swiglu_limit clamped SwiGLU activation", sglang PR #39920,
 // "Modifications"). Each 128-deep slice of K is its own dot product, whose
 // sum is multiplied by xs[row][kb] * ws[nb][kb]. A K step of this kernel is
-// exactly one such block: for every 16x16 output subtile four 32-deep MFMAs
-// sum the block into a short-lived partial that is scaled into the fp32
-// accumulator, so no per-block accumulators live across steps.
+// exactly one such block: for every 16x16 output subtile four 32-deep bf16
+// MFMAs (GEMM1) or one 128-deep FP8 MFMA (GEMM2) sum the block into a
+// short-lived partial that is scaled into the fp32 accumulator, so no
+// per-block accumulators live across steps.
 //
-// Arithmetic: the e4m3 codes are expanded exactly to bf16 (hardware
+// Arithmetic, GEMM1: the e4m3 codes are expanded exactly to bf16 (hardware
 // v_cvt_scalef32_pk_bf16_fp8 with scale 1; every e4m3 value has at most 4
 // significant bits) and multiplied on v_mfma_f32_16x16x32_bf16, whose
-// accumulation of such products is exact. The FP8 MFMA is not used: on
-// gfx950 it accumulates at reduced internal precision (measured about 2e-5
-// of sum |products|), enough to flip the e4m3 re-quantisation of h.
+// accumulation of such products is exact. The FP8 MFMA is not used there:
+// on gfx950 it accumulates at reduced internal precision (measured about
+// 2e-5 of sum |products|), enough to flip many e4m3 re-quantisation
+// decisions of h. GEMM2's fp32 output only feeds the weighted combine, so
+// it runs on v_mfma_f32_16x16x128_f8f6f4 straight from the codes: one
+// instruction per 16x16 subtile and scale block, no conversions, half the
+// LDS bytes (measured output error 2e-4..5e-4 of RMS(out), against about
+// 1e-6 for the exact path).
 //
 // Work split: a workgroup of 8 waves owns BM sorted rows of one expert and
 // 256 weight rows in two halves ("lo", "hi"). GEMM1: lo = gate rows
@@ -25,31 +31,34 @@
 // columns nt*256.. and nt*256 + 128... Wave w computes all BM rows of
 // columns 16w..16w+15 of both halves: gate and up of one h element meet in
 // one lane, and every weight byte is used by exactly one wave, so weights
-// stream from HBM straight into registers (two K blocks in flight), are
-// expanded there once per block and never pass through LDS. The activation
-// block is expanded to bf16 once per workgroup while it is staged in LDS
-// (double buffered, one barrier per K block) together with its rows'
-// activation scales, and read by all 8 waves. The weights are the MFMA's
-// first operand, so a lane's partials belong to one activation row and
-// four consecutive weight columns: the block scale of a partial is one
-// product xs[row] * ws[half] per lane and subtile, and the epilogue writes
-// whole dwords of codes (GEMM1) or 16-byte fp32 runs (GEMM2).
+// stream from HBM straight into registers (two K blocks in flight) and
+// never pass through LDS (GEMM1 expands them there once per block). The
+// activation block is staged in LDS (double buffered, one barrier per K
+// block) together with its rows' activation scales -- expanded to bf16 once
+// per workgroup for GEMM1, as raw codes for GEMM2 -- and read by all 8
+// waves. The weights are the MFMA's first operand, so a lane's partials
+// belong to one activation row and four consecutive weight columns: the
+// block scale of a partial is one product xs[row] * ws[half] per lane and
+// subtile, and the epilogue writes whole dwords of codes (GEMM1) or 16-byte
+// fp32 runs (GEMM2).
 //
 // K order inside a block: lane (r = l % 16, q = l / 16) feeds the MFMA with
-// elements 32q + 8j .. 32q + 8j + 7 of its row at step j, on both operands
-// -- any permutation of K shared by A and B leaves the dot product
-// unchanged and this one gives every lane 32 contiguous weight bytes per
-// row.
+// elements 32q .. 32q + 31 of its row (bf16: 8 of them per 32-deep MFMA,
+// step j taking 32q + 8j ..), on both operands -- any permutation of K
+// shared by A and B leaves the dot product unchanged and this one gives
+// every lane 32 contiguous weight bytes per row.
 #include "gemm_common.h"
 
 namespace moe {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-template <int BM>
+// F8: the activation block stays e4m3 (128-byte rows) for the FP8 MFMA;
+// otherwise it is expanded to bf16 (256-byte rows)
+template <int BM, bool F8>
 struct F8Geo {
   static constexpr int MS = BM / 16;                       // 16-row subtiles
-  static constexpr int A_BYTES = BM * 256;                 // one K block, bf16
+  static constexpr int A_BYTES = BM * (F8 ? 128 : 256);    // one K block
   static constexpr int A_CH = BM * 8;                      // 16-byte code chunks
   static constexpr int A_PT = (A_CH + kThreads - 1) / kThreads;
   static constexpr int X_BYTES = BM * 4;                   // row scales, [16][MS]
@@ -65,6 +74,12 @@ struct F8Geo {
 // the 16-row fragment reads and the row-wise chunk stores conflict-free,
 // where the plain c ^ (r & 15) costs two passes per read.
 __device__ __forceinline__ int swz16(int row, int c) { return c ^ (row & 11); }
+
+// e4m3 A rows are 128 bytes = 8 chunks of 16; chunk c of row r is stored at
+// c ^ swz8(r). A fragment read (lanes r = 0..15 of a pass reading chunks 2q,
+// 2q + 1 of rows 16 ms + r) and the row-wise chunk stores are both
+// conflict-free under the four-pass rule above.
+__device__ __forceinline__ int swz8(int row) { return ((row >> 1) & 1) | ((row >> 1) & 4); }
 
 // 8 e4m3fn codes (two dwords, byte order) -> 8 bf16, exact
 __device__ __forceinline__ bf16x8 e4m3x8_bf16(uint32_t w0, uint32_t w1) {
@@ -198,7 +213,12 @@ __device__ __forceinline__ void fp8_epilogue(const GemmParams& P, const Tile& t,
 // padding): staging, K loop and epilogue. Called by the whole workgroup.
 template <int BM, bool G1>
 __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, uint8_t* smem) {
-  using Gm = F8Geo<BM>;
+  // GEMM2 runs on the FP8 MFMA: its fp32 output feeds only the weighted
+  // combine, where the FP8 MFMA's reduced-precision accumulation stays far
+  // inside the output tolerance; GEMM1 keeps the exact bf16 path because its
+  // output is re-quantised to e4m3.
+  constexpr bool F8 = !G1;
+  using Gm = F8Geo<BM, F8>;
   constexpr int MS = Gm::MS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -214,7 +234,7 @@ __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, ui
     const int cc = min(tid + i * kThreads, Gm::A_CH - 1);
     const int row = cc >> 3, ch = cc & 7;
     ap[i] = P.a + a_source_row<G1>(P, row0 + (row < m ? row : 0)) * P.a_ld + ch * 16;
-    a_st[i] = row * 256;
+    a_st[i] = F8 ? row * 128 + 16 * (ch ^ swz8(row)) : row * 256;
   }
   const float* xsp = P.as;               // row tid's activation scales
   if (tid < BM) xsp = P.as + a_source_row<G1>(P, row0 + (tid < m ? tid : 0)) * NS;
@@ -245,10 +265,14 @@ __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, ui
       if (Gm::A_CH % kThreads == 0 || tid + i * kThreads < Gm::A_CH) {
         const int cc = tid + i * kThreads, row = cc >> 3, ch = cc & 7;
         const i32x4 v = ra[i];
-        *(bf16x8*)(st + a_st[i] + 16 * swz16(row, 2 * ch)) =
-            e4m3x8_bf16((uint32_t)v[0], (uint32_t)v[1]);
-        *(bf16x8*)(st + a_st[i] + 16 * swz16(row, 2 * ch + 1)) =
-            e4m3x8_bf16((uint32_t)v[2], (uint32_t)v[3]);
+        if constexpr (F8) {
+          *(i32x4*)(st + a_st[i]) = v;
+        } else {
+          *(bf16x8*)(st + a_st[i] + 16 * swz16(row, 2 * ch)) =
+              e4m3x8_bf16((uint32_t)v[0], (uint32_t)v[1]);
+          *(bf16x8*)(st + a_st[i] + 16 * swz16(row, 2 * ch + 1)) =
+              e4m3x8_bf16((uint32_t)v[2], (uint32_t)v[3]);
+        }
       }
     }
     if (tid < BM) ((float*)(st + Gm::A_BYTES))[(tid & 15) * MS + (tid >> 4)] = rxs;
@@ -275,15 +299,24 @@ __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, ui
     // hoisted into the previous block (it would double the live registers)
 #pragma unroll
     for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(rb[i]));
-    bf16x8 bw[2][4];
+    bf16x8 bw[2][4];     // bf16 path: the 32 codes of each row, expanded
+    i32x8 bw8[2];        // FP8 path: the same codes as one MFMA operand
+    if constexpr (F8) {
 #pragma unroll
-    for (int ns = 0; ns < 2; ++ns)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const i32x4 v = rb[2 * ns + h];
-        bw[ns][2 * h] = e4m3x8_bf16((uint32_t)v[0], (uint32_t)v[1]);
-        bw[ns][2 * h + 1] = e4m3x8_bf16((uint32_t)v[2], (uint32_t)v[3]);
+      for (int ns = 0; ns < 2; ++ns) {
+        const i32x4 u = rb[2 * ns], v = rb[2 * ns + 1];
+        bw8[ns] = (i32x8){u[0], u[1], u[2], u[3], v[0], v[1], v[2], v[3]};
       }
+    } else {
+#pragma unroll
+      for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const i32x4 v = rb[2 * ns + h];
+          bw[ns][2 * h] = e4m3x8_bf16((uint32_t)v[0], (uint32_t)v[1]);
+          bw[ns][2 * h + 1] = e4m3x8_bf16((uint32_t)v[2], (uint32_t)v[3]);
+        }
+    }
     // block s's weight scales arrived with its activations; reading them
     // here would expose a global-load latency per block on small tiles
     const float wl = wl_n, wh = wh_n;
@@ -305,11 +338,23 @@ __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, ui
         for (int i = 0; i < MS; ++i) xs[i] = sx[i];
       }
     }
-    auto lds_a = [&](int ms, bf16x8 (&af)[4]) {
+    // A fragment of subtile ms: bf16 path 4 x 8 elements (K 32 lg + 8 j ..),
+    // FP8 path the 32 codes K 32 lg .. 32 lg + 31 (as the weights)
+    struct Frag {
+      bf16x8 h[4];
+      i32x8 q;
+    };
+    auto lds_a = [&](int ms, Frag& af) {
       const int row = 16 * ms + lr;
+      if constexpr (F8) {
+        const i32x4 u = *(const i32x4*)(sa + row * 128 + 16 * ((2 * lg) ^ swz8(row)));
+        const i32x4 v = *(const i32x4*)(sa + row * 128 + 16 * ((2 * lg + 1) ^ swz8(row)));
+        af.q = (i32x8){u[0], u[1], u[2], u[3], v[0], v[1], v[2], v[3]};
+      } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        af[j] = *(const bf16x8*)(sa + row * 256 + 16 * swz16(row, 4 * lg + j));
+        for (int j = 0; j < 4; ++j)
+          af.h[j] = *(const bf16x8*)(sa + row * 256 + 16 * swz16(row, 4 * lg + j));
+      }
     };
     // software pipeline over the 16-row subtiles: while the MFMAs of
     // subtile ms run, the A fragments of ms + 1 are in flight and ms - 1
@@ -326,28 +371,41 @@ __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, ui
     };
     // weights as the first MFMA operand: p[r] = weight column 4 lg + r of
     // the wave's 16, activation row lr
-    auto sub = [&](const bf16x8 (&af)[4], f32x4& p0, f32x4& p1) {
+    auto sub = [&](const Frag& af, f32x4& p0, f32x4& p1) {
       p0 = (f32x4){0.f, 0.f, 0.f, 0.f};
       p1 = p0;
+      if constexpr (F8) {   // e4m3 x e4m3, unscaled (scale operands 0)
+        p0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bw8[0], af.q, p0, 0, 0, 0, 0, 0, 0);
+        p1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bw8[1], af.q, p1, 0, 0, 0, 0, 0, 0);
+      } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw[0][j], af[j], p0, 0, 0, 0);
-        p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw[1][j], af[j], p1, 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+          p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw[0][j], af.h[j], p0, 0, 0, 0);
+          p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw[1][j], af.h[j], p1, 0, 0, 0);
+        }
       }
     };
     // two named fragment / partial sets alternate between even and odd
     // subtiles, so the pipeline needs no register copies
-    bf16x8 fa[4], fb[4];
+    Frag fa, fb;
     f32x4 pa0, pa1, pb0, pb1;
     lds_a(0, fa);
     // order inside a region: the prefetch reads first, then the MFMAs
     // with the scaling arithmetic spread between them
     auto pattern = [&](bool reads) {
-      if (reads) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // DS read
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      if constexpr (F8) {
+        if (reads) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); // DS read
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
-        if (i < 5) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0); // VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);            // VALU
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      } else {
+        if (reads) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0); // DS read
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
+          if (i < 5) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0); // VALU
+        }
       }
     };
 #pragma unroll
@@ -428,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
 
 template <int TBM, bool G1>
 static hipError_t run_fp8(const GemmParams& P, long p_cap, int NT, hipStream_t s) {
-  constexpr int shm = F8Geo<TBM>::LDS;
+  constexpr int shm = F8Geo<TBM, !G1>::LDS;
   static int per_cu = 0;   // resident workgroups per CU, per instantiation
   if (per_cu == 0) {
     hipError_t e = hipFuncSetAttribute(
