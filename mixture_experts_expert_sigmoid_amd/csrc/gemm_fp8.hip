@@ -211,7 +211,11 @@ __device__ __forceinline__ void fp8_epilogue(const GemmParams& P, const Tile& t,
 
 // One tile of BM rows (BM = 32, 64 or 128; the rows at and after tl.m are
 // padding): staging, K loop and epilogue. Called by the whole workgroup.
-template <int BM, bool G1>
+// DEEP: the A fragments are read from LDS two subtiles ahead (three
+// register sets), the first two before the weight expansion; it pays where
+// registers allow (kernels whose largest row class is 64 or less) and
+// spills in the 128-row class.
+template <int BM, bool G1, bool DEEP>
 __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, uint8_t* smem) {
   // GEMM2 runs on the FP8 MFMA: its fp32 output feeds only the weighted
   // combine, where the FP8 MFMA's reduced-precision accumulation stays far
@@ -295,6 +299,31 @@ __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, ui
   // One K block: expand this block's weights, prefetch (A one block ahead,
   // B two blocks ahead into the registers just freed), then MFMA + scale.
   auto block = [&](int s, int buf, i32x4 (&rb)[4]) {
+    const uint8_t* sa = smem + buf * Gm::STAGE;
+    // A fragment of subtile ms: bf16 path 4 x 8 elements (K 32 lg + 8 j ..),
+    // FP8 path the 32 codes K 32 lg .. 32 lg + 31 (as the weights)
+    struct Frag {
+      bf16x8 h[4];
+      i32x8 q;
+    };
+    auto lds_a = [&](int ms, Frag& af) {
+      const int row = 16 * ms + lr;
+      if constexpr (F8) {
+        const i32x4 u = *(const i32x4*)(sa + row * 128 + 16 * ((2 * lg) ^ swz8(row)));
+        const i32x4 v = *(const i32x4*)(sa + row * 128 + 16 * ((2 * lg + 1) ^ swz8(row)));
+        af.q = (i32x8){u[0], u[1], u[2], u[3], v[0], v[1], v[2], v[3]};
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          af.h[j] = *(const bf16x8*)(sa + row * 256 + 16 * swz16(row, 4 * lg + j));
+      }
+    };
+    constexpr int D = DEEP ? 2 : 1;     // LDS prefetch distance, subtiles
+    Frag fr[D + 1];
+    if constexpr (DEEP) {
+      lds_a(0, fr[0]);
+      if (MS > 1) lds_a(1, fr[1]);
+    }
     // pin this block's weight registers here so their expansion is not
     // hoisted into the previous block (it would double the live registers)
 #pragma unroll
@@ -322,7 +351,6 @@ __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, ui
     const float wl = wl_n, wh = wh_n;
     gload_a(s + 1);
     gload_b(rb, s + 2);
-    const uint8_t* sa = smem + buf * Gm::STAGE;
     // this lane's activation scales for rows lr + 16 ms
     float xs[MS];
     {
@@ -338,24 +366,6 @@ __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, ui
         for (int i = 0; i < MS; ++i) xs[i] = sx[i];
       }
     }
-    // A fragment of subtile ms: bf16 path 4 x 8 elements (K 32 lg + 8 j ..),
-    // FP8 path the 32 codes K 32 lg .. 32 lg + 31 (as the weights)
-    struct Frag {
-      bf16x8 h[4];
-      i32x8 q;
-    };
-    auto lds_a = [&](int ms, Frag& af) {
-      const int row = 16 * ms + lr;
-      if constexpr (F8) {
-        const i32x4 u = *(const i32x4*)(sa + row * 128 + 16 * ((2 * lg) ^ swz8(row)));
-        const i32x4 v = *(const i32x4*)(sa + row * 128 + 16 * ((2 * lg + 1) ^ swz8(row)));
-        af.q = (i32x8){u[0], u[1], u[2], u[3], v[0], v[1], v[2], v[3]};
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          af.h[j] = *(const bf16x8*)(sa + row * 256 + 16 * swz16(row, 4 * lg + j));
-      }
-    };
     // software pipeline over the 16-row subtiles: while the MFMAs of
     // subtile ms run, the A fragments of ms + 1 are in flight and ms - 1
     // is scaled into the accumulator. The scheduling fences keep the live
@@ -385,11 +395,10 @@ __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, ui
         }
       }
     };
-    // two named fragment / partial sets alternate between even and odd
+    // D + 1 fragment sets and two partial sets rotate over the (unrolled)
     // subtiles, so the pipeline needs no register copies
-    Frag fa, fb;
-    f32x4 pa0, pa1, pb0, pb1;
-    lds_a(0, fa);
+    f32x4 pp[2][2];
+    if constexpr (!DEEP) lds_a(0, fr[0]);
     // order inside a region: the prefetch reads first, then the MFMAs
     // with the scaling arithmetic spread between them
     auto pattern = [&](bool reads) {
@@ -409,19 +418,14 @@ __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, ui
       }
     };
 #pragma unroll
-    for (int ms = 0; ms < MS; ms += 2) {
-      lds_a(ms + 1, fb);
-      sub(fa, pa0, pa1);
-      if (ms > 0) scale_into(ms - 1, pb0, pb1);
-      pattern(true);
-      __builtin_amdgcn_sched_barrier(0);
-      if (ms + 2 < MS) lds_a(ms + 2, fa);
-      sub(fb, pb0, pb1);
-      scale_into(ms, pa0, pa1);
-      pattern(ms + 2 < MS);
+    for (int ms = 0; ms < MS; ++ms) {
+      if (ms + D < MS) lds_a(ms + D, fr[(ms + D) % (D + 1)]);
+      sub(fr[ms % (D + 1)], pp[ms & 1][0], pp[ms & 1][1]);
+      if (ms > 0) scale_into(ms - 1, pp[(ms - 1) & 1][0], pp[(ms - 1) & 1][1]);
+      pattern(ms + D < MS);
       __builtin_amdgcn_sched_barrier(0);
     }
-    scale_into(MS - 1, pb0, pb1);
+    scale_into(MS - 1, pp[(MS - 1) & 1][0], pp[(MS - 1) & 1][1]);
     store_a(buf ^ 1);
   };
 
@@ -475,12 +479,12 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
     tl.n_lo = __builtin_amdgcn_readfirstlane(tl.n_lo);
     tl.n_hi = __builtin_amdgcn_readfirstlane(tl.n_hi);
     if constexpr (TBM >= 128) {
-      if (tl.m > 64) { fp8_tile<128, G1>(P, tl, smem); continue; }
+      if (tl.m > 64) { fp8_tile<128, G1, false>(P, tl, smem); continue; }
     }
     if constexpr (TBM >= 64) {
-      if (tl.m > 32) { fp8_tile<64, G1>(P, tl, smem); continue; }
+      if (tl.m > 32) { fp8_tile<64, G1, G1 && TBM <= 64>(P, tl, smem); continue; }
     }
-    fp8_tile<32, G1>(P, tl, smem);
+    fp8_tile<32, G1, G1 && TBM <= 64>(P, tl, smem);
   }
 }
 
