@@ -198,7 +198,7 @@ def main():
     h = torch.empty(pc, I, dtype=torch.uint8, device="cuda")
     hs = torch.empty(pc, I // 128, device="cuda")
     out = torch.empty(T, H, device="cuda")
-    ws2 = torch.empty(M.moe_gemm2_workspace_size(pc, H), dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty(M.moe_gemm2_workspace_size(mod.w2, pc), dtype=torch.uint8, device="cuda")
     calls = {
         "route": lambda: M.moe_route(lg, N, 0, k, 1.0, 1.0, ids, w, None),
         "permute": lambda: M.moe_permute(ids, k, N, 0, N, 1, offsets, sp, pr, err, wsp),

@@ -172,14 +172,19 @@ int moe_quantize_act_fp8(const void *x_bf16, long T, int H, void *xq,
  * offsets / sorted_pair come from moe_permute for the same (T, top_k);
  * w13->n_groups = G, w13->N = 2I, w13->K = H. p_cap = rows allocated in h.
  * Limits: H % 128 == 0 and I % 128 == 0. Workspace:
- * moe_gemm1_workspace_size(p_cap, lora). */
+ * moe_gemm1_workspace_size(w13, p_cap, lora) bytes: the LoRA z rows and,
+ * for FP8 weights at decode sizes (at most 1024 tiles of 32 rows x 128 h
+ * columns can exist), the fp32 partial sums of the split-K schedule, which
+ * spreads the K blocks of the few tiles over all CUs and reduces them in a
+ * fixed order. Returns 0 for a NULL w13 or N not a multiple of 256. */
 int moe_grouped_gemm1_act(const moe_weights *w13, const void *x,
                           const float *xs, const void *x_bf16, long T, int H,
                           int I, int top_k, long p_cap, const int *offsets,
                           const int *sorted_pair, const moe_act_params *act,
                           const moe_lora *lora, void *h, float *hs, void *ws,
                           size_t ws_bytes, void *stream);
-size_t moe_gemm1_workspace_size(long p_cap, const moe_lora *lora);
+size_t moe_gemm1_workspace_size(const moe_weights *w13, long p_cap,
+                                const moe_lora *lora);
 
 /* ---------------------------------------- grouped GEMM2 + weighted combine -- */
 /* y[r] = h[r] W2_g^T (fp32; FP8 per 128-K block partial sums times
@@ -190,14 +195,16 @@ size_t moe_gemm1_workspace_size(long p_cap, const moe_lora *lora);
  * [INT4-PR: slot-specific routing-weight reduction, fp32 accumulation].
  * Every out element is written (0 for a token with no local pair).
  * w2->N = H, w2->K = I. out fp32 [T][H]. Workspace:
- * moe_gemm2_workspace_size(p_cap, H) (the fp32 y rows). */
+ * moe_gemm2_workspace_size(w2, p_cap) bytes: the fp32 y rows, or for FP8
+ * weights at decode sizes their split-K partial sums (reduced by the
+ * combine in a fixed order). Returns 0 for a NULL w2. */
 int moe_grouped_gemm2_combine(const moe_weights *w2, const void *h,
                               const float *hs, long T, int H, int I,
                               int top_k, int shared_expert, long p_cap,
                               const int *offsets, const int *pair_row,
                               const float *topk_w, float shared_w, float *out,
                               void *ws, size_t ws_bytes, void *stream);
-size_t moe_gemm2_workspace_size(long p_cap, int H);
+size_t moe_gemm2_workspace_size(const moe_weights *w2, long p_cap);
 
 /* ---------------------------------------------------------- whole layer -- */
 typedef struct {

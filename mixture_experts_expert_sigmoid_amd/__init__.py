@@ -75,13 +75,13 @@ _SIGS = {
                                       POINTER(MoeActParams), POINTER(MoeLora),
                                       c_void_p, c_void_p, c_void_p, c_size_t,
                                       c_void_p]),
-    "moe_gemm1_workspace_size": (c_size_t, [c_long, POINTER(MoeLora)]),
+    "moe_gemm1_workspace_size": (c_size_t, [POINTER(MoeWeights), c_long, POINTER(MoeLora)]),
     "moe_grouped_gemm2_combine": (c_int, [POINTER(MoeWeights), c_void_p, c_void_p,
                                           c_long, c_int, c_int, c_int, c_int,
                                           c_long, c_void_p, c_void_p, c_void_p,
                                           c_float, c_void_p, c_void_p, c_size_t,
                                           c_void_p]),
-    "moe_gemm2_workspace_size": (c_size_t, [c_long, c_int]),
+    "moe_gemm2_workspace_size": (c_size_t, [POINTER(MoeWeights), c_long]),
     "moe_forward": (c_int, [POINTER(MoeLayer), c_void_p, c_void_p, c_long, c_long,
                             c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                             c_void_p, c_size_t, c_void_p]),
@@ -195,9 +195,9 @@ def moe_quantize_act_fp8(x_bf16, xq, xs, stream=None):
                                       _stream(stream)), "moe_quantize_act_fp8")
 
 
-def moe_gemm1_workspace_size(p_cap, lora: Optional[MoeLora] = None) -> int:
+def moe_gemm1_workspace_size(w13: MoeWeights, p_cap, lora: Optional[MoeLora] = None) -> int:
     return lib().moe_gemm1_workspace_size(
-        p_cap, ctypes.pointer(lora) if lora is not None else None)
+        ctypes.byref(w13), p_cap, ctypes.pointer(lora) if lora is not None else None)
 
 
 def moe_grouped_gemm1_act(w13: MoeWeights, x, xs, x_bf16, T, H, I, top_k, p_cap,
@@ -211,8 +211,8 @@ def moe_grouped_gemm1_act(w13: MoeWeights, x, xs, x_bf16, T, H, I, top_k, p_cap,
         _stream(stream)), "moe_grouped_gemm1_act")
 
 
-def moe_gemm2_workspace_size(p_cap, H) -> int:
-    return lib().moe_gemm2_workspace_size(p_cap, H)
+def moe_gemm2_workspace_size(w2: MoeWeights, p_cap) -> int:
+    return lib().moe_gemm2_workspace_size(ctypes.byref(w2), p_cap)
 
 
 def moe_grouped_gemm2_combine(w2: MoeWeights, h, hs, T, H, I, top_k,

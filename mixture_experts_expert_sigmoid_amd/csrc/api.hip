@@ -3,6 +3,8 @@
 // (except moe_read_device_error), no state kept between calls apart from the
 // calling thread's last HIP error message.
 #include <math.h>
+
+#include <algorithm>
 #include <stdio.h>
 #include <string.h>
 
@@ -133,9 +135,33 @@ int moe_quantize_act_fp8(const void* x_bf16, long T, int H, void* xq,
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_quantize_act_fp8");
 }
 
-size_t moe_gemm1_workspace_size(long p_cap, const moe_lora* lora) {
-  if (p_cap < 0) return 0;
+}  // extern "C"
+
+namespace {
+// GEMM1 workspace: LoRA z rows, then (stream-K) the fp32 partial sums
+size_t g1_z_bytes(long p_cap, const moe_lora* lora) {
   return lora ? al((size_t)p_cap * lora->rank * 4) : 0;
+}
+size_t g1_part_bytes(const moe_weights* w13, long p_cap) {
+  if (!moe::fp8_streamk(w13->fmt, p_cap, w13->n_groups, w13->N / 256, w13->K / 128))
+    return 0;
+  return al((size_t)moe::kSkSlots * p_cap * w13->N * 4);
+}
+// GEMM2 workspace: fp32 y rows, or (stream-K) their partial sums
+size_t g2_bytes(const moe_weights* w2, long p_cap) {
+  const int NT = (w2->N + 255) / 256;
+  const size_t rows = moe::fp8_streamk(w2->fmt, p_cap, w2->n_groups, NT, w2->K / 128)
+                          ? (size_t)moe::kSkSlots * p_cap : (size_t)p_cap;
+  return al(rows * w2->N * 4);
+}
+}  // namespace
+
+extern "C" {
+
+size_t moe_gemm1_workspace_size(const moe_weights* w13, long p_cap,
+                                const moe_lora* lora) {
+  if (!w13 || p_cap < 0 || w13->N < 256 || w13->N % 256) return 0;
+  return g1_z_bytes(p_cap, lora) + g1_part_bytes(w13, p_cap);
 }
 
 static int gemm1_checks(const moe_weights* w13, const void* x, const float* xs,
@@ -161,7 +187,7 @@ static moe::Gemm1Args gemm1_args(const moe_weights* w13, const void* x,
                                  const int* sorted_pair,
                                  const moe_act_params* act,
                                  const moe_lora* lora, const float* z, void* h,
-                                 float* hs) {
+                                 float* hs, float* part) {
   moe::Gemm1Args a{};
   a.fmt = w13->fmt;
   a.wq = w13->q;
@@ -187,6 +213,7 @@ static moe::Gemm1Args gemm1_args(const moe_weights* w13, const void* x,
   a.lora_scale = lora ? lora->scale : 0.0f;
   a.h = h;
   a.hs = hs;
+  a.part = part;
   return a;
 }
 
@@ -199,23 +226,25 @@ int moe_grouped_gemm1_act(const moe_weights* w13, const void* x,
   int st = gemm1_checks(w13, x, xs, x_bf16, T, H, I, top_k, p_cap, offsets,
                         sorted_pair, act, lora, h, hs);
   if (st) return st;
-  size_t need = moe_gemm1_workspace_size(p_cap, lora);
+  size_t need = moe_gemm1_workspace_size(w13, p_cap, lora);
   if (need && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   float* z = (float*)ws;
+  float* part = g1_part_bytes(w13, p_cap)
+                    ? (float*)((char*)ws + g1_z_bytes(p_cap, lora)) : nullptr;
   hipError_t e = hipSuccess;
   if (lora)
     e = moe::launch_lora_z(x_bf16, lora->A, lora->rank, T, H, top_k,
                            lora->n_groups, p_cap, offsets, sorted_pair, z, s);
   if (e == hipSuccess)
     e = moe::launch_gemm1(gemm1_args(w13, x, xs, T, H, I, top_k, p_cap, offsets,
-                                     sorted_pair, act, lora, z, h, hs), s);
+                                     sorted_pair, act, lora, z, h, hs, part), s);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_grouped_gemm1_act");
 }
 
-size_t moe_gemm2_workspace_size(long p_cap, int H) {
-  if (p_cap < 0 || H < 0) return 0;
-  return al((size_t)p_cap * H * 4);
+size_t moe_gemm2_workspace_size(const moe_weights* w2, long p_cap) {
+  if (!w2 || p_cap < 0 || w2->N < 0) return 0;
+  return g2_bytes(w2, p_cap);
 }
 
 static int gemm2_checks(const moe_weights* w2, const void* h, const float* hs,
@@ -244,7 +273,7 @@ int moe_grouped_gemm2_combine(const moe_weights* w2, const void* h,
   int st = gemm2_checks(w2, h, hs, T, H, I, top_k, shared_expert, p_cap,
                         offsets, pair_row, topk_w, shared_w, out);
   if (st) return st;
-  size_t need = moe_gemm2_workspace_size(p_cap, H);
+  size_t need = moe_gemm2_workspace_size(w2, p_cap);
   if (need && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   float* y = (float*)ws;
@@ -260,10 +289,12 @@ int moe_grouped_gemm2_combine(const moe_weights* w2, const void* h,
   a.p_cap = p_cap;
   a.offsets = offsets;
   a.y = y;
+  int sk_grid = 0;
+  a.sk_grid = &sk_grid;
   hipError_t e = moe::launch_gemm2(a, s);
   if (e == hipSuccess)
     e = moe::launch_combine(y, T, H, top_k, shared_expert, pair_row, topk_w,
-                            shared_w, out, s);
+                            shared_w, out, s, sk_grid, p_cap, I, a.G, offsets);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_grouped_gemm2_combine");
 }
 
@@ -292,7 +323,9 @@ FwdLayout layout(const moe_layer* L, long T) {
   o.z = take(L->lora ? (size_t)pc * L->lora->rank * 4 : 0);
   o.h = take((size_t)pc * L->I * (fp8 ? 1 : 2));
   o.hs = take(fp8 ? (size_t)pc * (L->I / 128) * 4 : 0);
-  o.y = take((size_t)pc * L->H * 4);
+  // y rows (or their stream-K partials); GEMM1's partials, consumed before
+  // GEMM2 starts, share the region
+  o.y = take(std::max(g2_bytes(&L->w2, pc), g1_part_bytes(&L->w13, pc)));
   o.total = cur;
   return o;
 }
@@ -376,10 +409,11 @@ int moe_forward(const moe_layer* L, const void* x_bf16, const float* logits,
                            sorted_pair, z, s);
     if (e != hipSuccess) return hip_fail(e, "moe_forward/lora_z");
   }
+  float* g1_part = g1_part_bytes(&L->w13, pc) ? y : nullptr;
   e = moe::launch_gemm1(gemm1_args(&L->w13, fp8 ? xq : x_bf16, fp8 ? xs : nullptr,
                                    T, L->H, L->I, L->top_k, pc, offsets,
                                    sorted_pair, &L->act, L->lora, z, h,
-                                   fp8 ? hs : nullptr), s);
+                                   fp8 ? hs : nullptr, g1_part), s);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/gemm1");
   moe::Gemm2Args a{};
   a.fmt = L->w2.fmt;
@@ -393,10 +427,12 @@ int moe_forward(const moe_layer* L, const void* x_bf16, const float* logits,
   a.p_cap = pc;
   a.offsets = offsets;
   a.y = y;
+  int sk_grid = 0;
+  a.sk_grid = &sk_grid;
   e = moe::launch_gemm2(a, s);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/gemm2");
   e = moe::launch_combine(y, T, L->H, L->top_k, L->shared_expert, pair_row,
-                          topk_w, L->shared_w, out, s);
+                          topk_w, L->shared_w, out, s, sk_grid, pc, L->I, G, offsets);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/combine");
   return MOE_OK;
 }

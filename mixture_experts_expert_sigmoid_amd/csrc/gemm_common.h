@@ -82,6 +82,9 @@ struct GemmParams {
   float* hs;
   // GEMM2 out
   float* y;                  // [p_cap][N]
+  // stream-K (decode sizes): fp32 partial sums [kSkSlots][p_rows][N]
+  float* part;
+  long p_rows;
 };
 
 
@@ -123,6 +126,44 @@ __device__ __forceinline__ void tile_prefix(const int* offsets, int G, int* s_cu
 struct Tile {
   int g, row0, m, nt, n_lo, n_hi;
 };
+
+// ---------------------------------------------------------------------------
+// stream-K schedule for decode sizes, where the tiles of a grouped GEMM are
+// fewer than the CUs: the U = tiles * NS (tile, K block) units are cut into
+// W equal contiguous ranges, one per workgroup; workgroup w owns units
+// [w U / W, (w + 1) U / W). W is capped so that every range holds at least
+// ceil(NS / (kSkSlots - 1)) units, which bounds the workgroups meeting one
+// tile -- its partial-sum slots -- to kSkSlots. When the tiles already fill
+// 80..100 % of the grid, W = tiles: one whole tile per workgroup, one slot.
+// Partials are reduced in slot order by the consumer, so results do not
+// depend on timing. Producer and consumers evaluate this from the same
+// (tiles, NS, grid).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int sk_workgroups(long tiles, int NS, int grid) {
+  if (tiles <= grid && tiles * 5 >= 4L * grid) return (int)tiles;
+  const int lmin = (NS + kSkSlots - 2) / (kSkSlots - 1);
+  const long w = tiles * NS / lmin;
+  return (int)(w < 1 ? 1 : (w < grid ? w : grid));
+}
+// the workgroup whose range holds unit u
+__device__ __forceinline__ int sk_owner(long u, long U, int W) {
+  return (int)(((u + 1) * W - 1) / U);
+}
+// number of partial slots (consecutive workgroups) of the tile whose units
+// start at uf
+__device__ __forceinline__ int sk_nslots(long uf, int NS, long U, int W) {
+  return sk_owner(uf + NS - 1, U, W) - sk_owner(uf, U, W) + 1;
+}
+// the group owning sorted row r: last g with s_off[g] <= r (LDS copy of
+// the offsets; empty groups share their successor's offset)
+__device__ __forceinline__ int group_of_row(const int* s_off, int G, int r) {
+  int lo = 0, hi = G - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_off[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
 
 // Logical tile lt -> group, first sorted row, valid rows, column halves.
 // GEMM1: lo = gate rows nt*128.., hi = up rows I + nt*128..;
@@ -275,7 +316,11 @@ __device__ __forceinline__ void tile_epilogue(const GemmParams& P, const Tile& t
 
 int num_cus();
 
-// Blockwise-FP8 grouped GEMM (gemm_fp8.hip).
-hipError_t launch_gemm_fp8(const GemmParams& P, bool g1, long p_cap, int NT, hipStream_t s);
+// Blockwise-FP8 grouped GEMM (gemm_fp8.hip). With P.part set it runs the
+// stream-K schedule and leaves partial sums for sk_grid workgroups; the
+// consumer (launch_gemm1_sk_epilogue, or the combine) reduces them.
+hipError_t launch_gemm_fp8(const GemmParams& P, bool g1, long p_cap, int NT, hipStream_t s,
+                           int* sk_grid = nullptr);
+hipError_t launch_gemm1_sk_epilogue(const GemmParams& P, int sk_grid, hipStream_t s);
 
 }  // namespace moe

@@ -210,13 +210,15 @@ __device__ __forceinline__ void fp8_epilogue(const GemmParams& P, const Tile& t,
 }
 
 // One tile of BM rows (BM = 32, 64 or 128; the rows at and after tl.m are
-// padding): staging, K loop and epilogue. Called by the whole workgroup.
-// DEEP: the A fragments are read from LDS two subtiles ahead (three
-// register sets), the first two before the weight expansion; it pays where
-// registers allow (kernels whose largest row class is 64 or less) and
-// spills in the 128-row class.
-template <int BM, bool G1, bool DEEP>
-__device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, uint8_t* smem) {
+// padding) over K blocks [k0, k1): staging, K loop and epilogue. Called by
+// the whole workgroup. DEEP: the A fragments are read from LDS two subtiles
+// ahead (three register sets), the first two before the weight expansion;
+// it pays where registers allow (kernels whose largest row class is 64 or
+// less) and spills in the 128-row class. PART: the block-scaled fp32 sums
+// go to partial slot `slot` instead of the epilogue (stream-K).
+template <int BM, bool G1, bool DEEP, bool PART = false>
+__device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, uint8_t* smem,
+                                         int k0, int k1, int slot = 0) {
   // GEMM2 runs on the FP8 MFMA: its fp32 output feeds only the weighted
   // combine, where the FP8 MFMA's reduced-precision accumulation stays far
   // inside the output tolerance; GEMM1 keeps the exact bf16 path because its
@@ -227,7 +229,7 @@ __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, ui
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int K = P.K;
-  const int NS = K >> 7;                      // K blocks of 128
+  const int NS = K >> 7;                      // K blocks of 128 (scale stride)
   const int g = tl.g, row0 = tl.row0, m = tl.m;
 
   // ---- this thread's sources at K block 0 (+128 bytes per block) --------
@@ -252,7 +254,7 @@ __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, ui
   float rxs = 0.0f;
   float wl_n = 0.0f, wh_n = 0.0f;       // weight block scales, one block ahead
   auto gload_a = [&](int s) {           // past the last block: re-read it
-    const int sc = min(s, NS - 1);
+    const int sc = min(s, k1 - 1);
     const long adv = (long)sc * 128;
 #pragma unroll
     for (int i = 0; i < Gm::A_PT; ++i) ra[i] = *(const i32x4*)(ap[i] + adv);
@@ -282,7 +284,7 @@ __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, ui
     if (tid < BM) ((float*)(st + Gm::A_BYTES))[(tid & 15) * MS + (tid >> 4)] = rxs;
   };
   auto gload_b = [&](i32x4 (&rb)[4], int s) {
-    const long adv = (long)min(s, NS - 1) * 128;
+    const long adv = (long)min(s, k1 - 1) * 128;
     rb[0] = *(const i32x4*)(bp0 + adv);
     rb[1] = *(const i32x4*)(bp0 + adv + 16);
     rb[2] = *(const i32x4*)(bp1 + adv);
@@ -430,24 +432,39 @@ __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, ui
   };
 
   i32x4 rb0[4], rb1[4];
-  gload_b(rb0, 0);
-  gload_b(rb1, 1);
-  gload_a(0);
+  gload_b(rb0, k0);
+  gload_b(rb1, k0 + 1);
+  gload_a(k0);
   store_a(0);
   __syncthreads();
-  int s = 0;
-  for (; s + 2 <= NS; s += 2) {
+  int s = k0;
+  for (; s + 2 <= k1; s += 2) {
     block(s, 0, rb0);
     __syncthreads();
     block(s + 1, 1, rb1);
     __syncthreads();
   }
-  if (s < NS) {            // odd block count
+  if (s < k1) {            // odd block count
     block(s, 0, rb0);
     __syncthreads();
   }
-  fp8_epilogue<BM, G1>(P, tl, acc, smem);
-  __syncthreads();         // LDS is reused by the next tile
+  if constexpr (PART) {
+    // acc[ms][ns][r]: row 16 ms + lr, column (ns ? hi : lo) + 16 wave + 4 lg + r
+    const int c0 = 16 * wave + 4 * lg;
+    const bool hi_ok = G1 || tl.n_hi != tl.n_lo;
+    float* base = P.part + ((long)slot * P.p_rows + row0) * P.N;
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+      const int tr = 16 * ms + lr;
+      if (tr < m) {
+        *(f32x4*)(base + (long)tr * P.N + tl.n_lo + c0) = acc[ms][0];
+        if (hi_ok) *(f32x4*)(base + (long)tr * P.N + tl.n_hi + c0) = acc[ms][1];
+      }
+    }
+  } else {
+    fp8_epilogue<BM, G1>(P, tl, acc, smem);
+    __syncthreads();       // LDS is reused by the next tile
+  }
 }
 
 // Tiles are scheduled with up to TBM rows of one expert; each runs the code
@@ -478,13 +495,117 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
     tl.nt = __builtin_amdgcn_readfirstlane(tl.nt);
     tl.n_lo = __builtin_amdgcn_readfirstlane(tl.n_lo);
     tl.n_hi = __builtin_amdgcn_readfirstlane(tl.n_hi);
+    const int NS = P.K >> 7;
     if constexpr (TBM >= 128) {
-      if (tl.m > 64) { fp8_tile<128, G1, false>(P, tl, smem); continue; }
+      if (tl.m > 64) { fp8_tile<128, G1, false>(P, tl, smem, 0, NS); continue; }
     }
     if constexpr (TBM >= 64) {
-      if (tl.m > 32) { fp8_tile<64, G1, G1 && TBM <= 64>(P, tl, smem); continue; }
+      if (tl.m > 32) { fp8_tile<64, G1, G1 && TBM <= 64>(P, tl, smem, 0, NS); continue; }
     }
-    fp8_tile<32, G1, G1 && TBM <= 64>(P, tl, smem);
+    fp8_tile<32, G1, G1 && TBM <= 64>(P, tl, smem, 0, NS);
+  }
+}
+
+// Stream-K schedule over 32-row tiles (see gemm_common.h): workgroup b runs
+// the K-block segments of its unit range and leaves fp32 partial sums in
+// slot b - (first workgroup of the tile).
+template <bool G1>
+__global__ __launch_bounds__(kThreads) void moe_gemm_fp8_sk_kernel(GemmParams P) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int s_cum[kMaxGroups + 1];
+  __shared__ int s_wsum[8];
+  const int G = P.G;
+  const int NT = G1 ? (P.I >> 7) : ((P.N + 255) >> 8);
+  const int NS = P.K >> 7;
+  tile_prefix<kSkBM>(P.offsets, G, s_cum, s_wsum);
+  const long U = (long)s_cum[G] * NT * NS;
+  const int W = sk_workgroups((long)s_cum[G] * NT, NS, gridDim.x);
+  const int b = blockIdx.x;
+  if (b >= W) return;
+  const long u1 = (long)(b + 1) * U / W;
+  for (long u = (long)b * U / W; u < u1;) {
+    const int t = (int)(u / NS);
+    const int k0 = (int)(u - (long)t * NS);
+    const int k1 = (int)std::min<long>(NS, k0 + (u1 - u));
+    Tile tl = decode_tile<kSkBM, G1>(P, t, NT, s_cum);
+    tl.g = __builtin_amdgcn_readfirstlane(tl.g);
+    tl.row0 = __builtin_amdgcn_readfirstlane(tl.row0);
+    tl.m = __builtin_amdgcn_readfirstlane(tl.m);
+    tl.nt = __builtin_amdgcn_readfirstlane(tl.nt);
+    tl.n_lo = __builtin_amdgcn_readfirstlane(tl.n_lo);
+    tl.n_hi = __builtin_amdgcn_readfirstlane(tl.n_hi);
+    const int slot = b - sk_owner((long)t * NS, U, W);
+    fp8_tile<kSkBM, G1, G1, true>(P, tl, smem, k0, k1, slot);
+    u += k1 - k0;
+  }
+}
+
+// GEMM1 after stream-K: one wave per (sorted row r, 128 h columns nt) sums
+// the partial slots of r's tile in slot order, then applies the epilogue of
+// fp8_epilogue with the same arithmetic (global scales, LoRA delta in true
+// units, parameterized SwiGLU, e4m3 re-quantisation per 128 columns); lane
+// l owns h columns nt*128 + 2l, 2l + 1.
+__global__ __launch_bounds__(kThreads) void gemm1_sk_epilogue_kernel(GemmParams P, int grid) {
+  __shared__ int s_cum[kMaxGroups + 1];
+  __shared__ int s_off[kMaxGroups + 1];
+  __shared__ int s_wsum[8];
+  const int G = P.G, I = P.I;
+  const int NT = I >> 7, NS = P.K >> 7;
+  tile_prefix<kSkBM>(P.offsets, G, s_cum, s_wsum);
+  for (int i = threadIdx.x; i <= G; i += kThreads) s_off[i] = P.offsets[i];
+  __syncthreads();
+  const long U = (long)s_cum[G] * NT * NS;
+  const int W = sk_workgroups((long)s_cum[G] * NT, NS, grid);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long items = (long)s_off[G] * NT;
+  for (long it = (long)blockIdx.x * 8 + wave; it < items; it += (long)gridDim.x * 8) {
+    const int r = (int)(it / NT), nt = (int)(it - (long)r * NT);
+    const int g = group_of_row(s_off, G, r);
+    const int mt = s_cum[g] + (r - s_off[g]) / kSkBM;
+    const int nsl = sk_nslots(((long)mt * NT + nt) * NS, NS, U, W);
+    const int c = nt * 128 + 2 * lane;
+    float a[2][2] = {{0.f, 0.f}, {0.f, 0.f}};       // [gate | up][column]
+    for (int sl = 0; sl < nsl; ++sl) {
+      const float* pr = P.part + ((long)sl * P.p_rows + r) * P.N;
+      const f32x2 vg = *(const f32x2*)(pr + c), vu = *(const f32x2*)(pr + I + c);
+      a[0][0] += vg[0]; a[0][1] += vg[1];
+      a[1][0] += vu[0]; a[1][1] += vu[1];
+    }
+    if (P.gscale) {
+      const float gsg = P.gscale[2 * g], gsu = P.gscale[2 * g + 1];
+      a[0][0] *= gsg; a[0][1] *= gsg;
+      a[1][0] *= gsu; a[1][1] *= gsu;
+    }
+    if (P.z && g < P.lora_groups) {
+      const int R = P.lora_rank;
+      const uint16_t* Bg = P.lora_B + (long)g * 2 * I * R;
+      const float* zr = P.z + (long)r * R;
+      for (int q = 0; q < R; ++q) {
+        const float zq = zr[q];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          a[0][j] = fmaf(zq, P.lora_scale * bf16_bits_to_f32(Bg[(long)(c + j) * R + q]), a[0][j]);
+          a[1][j] = fmaf(zq, P.lora_scale * bf16_bits_to_f32(Bg[(long)(I + c + j) * R + q]), a[1][j]);
+        }
+      }
+    }
+    const float L = P.limit, al = P.alpha, be = P.beta;
+    float hv[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float gg = fminf(a[0][j], L);
+      const float uu = fminf(fmaxf(a[1][j], -L), L);
+      const float sg = __builtin_amdgcn_rcpf(1.0f + expf(-al * gg));
+      hv[j] = gg * sg * (uu + be);
+    }
+    const float am = wave_max(fmaxf(fabsf(hv[0]), fabsf(hv[1])));
+    const float sc = am > 0.0f ? am / 448.0f : 1.0f;
+    const float inv = 1.0f / sc;
+    const float q0 = __builtin_amdgcn_fmed3f(hv[0] * inv, -448.0f, 448.0f);
+    const float q1 = __builtin_amdgcn_fmed3f(hv[1] * inv, -448.0f, 448.0f);
+    const int v = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+    *(uint16_t*)(P.h + (long)r * I + c) = (uint16_t)v;
+    if (lane == 0) P.hs[(long)r * NT + nt] = sc;
   }
 }
 
@@ -512,6 +633,37 @@ static hipError_t run_fp8(const GemmParams& P, long p_cap, int NT, hipStream_t s
 }
 
 template <bool G1>
+static hipError_t run_fp8_sk(const GemmParams& P, long p_cap, int NT, hipStream_t s,
+                             int* sk_grid) {
+  constexpr int shm = F8Geo<kSkBM, !G1>::LDS;
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&moe_gemm_fp8_sk_kernel<G1>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, shm);
+    if (e != hipSuccess) return e;
+    int nb = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &nb, reinterpret_cast<const void*>(&moe_gemm_fp8_sk_kernel<G1>), kThreads, shm);
+    if (e != hipSuccess) return e;
+    per_cu = nb > 0 ? nb : 1;
+  }
+  const int grid = num_cus() * per_cu;
+  *sk_grid = grid;
+  if (p_cap == 0) return hipSuccess;
+  moe_gemm_fp8_sk_kernel<G1><<<dim3((unsigned)grid), dim3(kThreads), shm, s>>>(P);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm1_sk_epilogue(const GemmParams& P, int sk_grid, hipStream_t s) {
+  const long items = P.p_rows * (P.I >> 7);     // upper bound: rows used <= p_rows
+  if (items == 0) return hipSuccess;
+  const long nwg = std::min<long>((items + 7) / 8, (long)num_cus() * 4);
+  gemm1_sk_epilogue_kernel<<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(P, sk_grid);
+  return hipGetLastError();
+}
+
+template <bool G1>
 static hipError_t run_fp8_tbm(const GemmParams& P, long p_cap, int NT, hipStream_t s) {
   // the largest row class worth scheduling: rows per group on average
   const long hint = P.G > 0 ? p_cap / P.G : p_cap;
@@ -520,7 +672,11 @@ static hipError_t run_fp8_tbm(const GemmParams& P, long p_cap, int NT, hipStream
   return run_fp8<128, G1>(P, p_cap, NT, s);
 }
 
-hipError_t launch_gemm_fp8(const GemmParams& P, bool g1, long p_cap, int NT, hipStream_t s) {
+hipError_t launch_gemm_fp8(const GemmParams& P, bool g1, long p_cap, int NT, hipStream_t s,
+                           int* sk_grid) {
+  if (P.part)
+    return g1 ? run_fp8_sk<true>(P, p_cap, NT, s, sk_grid)
+              : run_fp8_sk<false>(P, p_cap, NT, s, sk_grid);
   return g1 ? run_fp8_tbm<true>(P, p_cap, NT, s) : run_fp8_tbm<false>(P, p_cap, NT, s);
 }
 

@@ -89,7 +89,19 @@ def test_gemm_validation():
     out = L.moe_grouped_gemm2_combine(ctypes.byref(w2), 1, 1, 4, 256, 128, 2, 0, 8,
                                       1, 1, 1, 1.0, 1, None, 0, None)
     assert out == -6                                     # workspace
-    assert L.moe_gemm2_workspace_size(100, 256) >= 100 * 256 * 4
+    assert L.moe_gemm2_workspace_size(ctypes.byref(w2), 100) >= 100 * 256 * 4
+    assert L.moe_gemm2_workspace_size(None, 100) == 0
+    # FP8 at decode sizes (few tiles for the CUs): room for the split-K
+    # partial sums; at large p_cap plain rows only
+    w13f = _w(fmt=M.MOE_W_FP8_B128, G=289, N=4096, K=6144)      # 9 x 16 tiles
+    assert L.moe_gemm1_workspace_size(ctypes.byref(w13f), 9, None) >= 4 * 9 * 4096 * 4
+    assert L.moe_gemm1_workspace_size(ctypes.byref(w13f), 36864, None) == 0
+    w2f = _w(fmt=M.MOE_W_FP8_B128, G=128, N=3072, K=1536)       # 4 x 12 tiles
+    assert L.moe_gemm2_workspace_size(ctypes.byref(w2f), 4) >= 4 * 4 * 3072 * 4
+    assert L.moe_gemm2_workspace_size(ctypes.byref(w2f), 16384) == 16384 * 3072 * 4
+    w13b = _w(fmt=M.MOE_W_BF16, G=289, N=4096, K=6144)
+    assert L.moe_gemm1_workspace_size(ctypes.byref(w13b), 9, None) == 0   # BF16: none
+    assert L.moe_gemm1_workspace_size(None, 9, None) == 0
 
 
 def _layer(**kw):

@@ -142,6 +142,13 @@ SMALL = {
         name="ep_lora_small", H=256, I=256, cfg_id=25), 300),
     "ep_lora_mid": (CONFIGS["ep_lora_258"].scaled(
         name="ep_lora_mid", H=256, I=256, cfg_id=25), 37),
+    # decode shapes with long K: both FP8 GEMMs take the split-K (stream-K)
+    # schedule with several partial slots per tile; the second also runs the
+    # LoRA delta and both global scales in the split-K epilogue
+    "fp8_oai_sk": (CONFIGS["fp8_oai_128_skew"].scaled(
+        name="fp8_oai_sk", H=2048, I=2048, n_routed=16, cfg_id=26), 2),
+    "ep_lora_sk": (CONFIGS["ep_lora_258"].scaled(
+        name="ep_lora_sk", H=2048, I=2048, n_routed=64, offset=16, cfg_id=27), 1),
 }
 
 _cache = {}
@@ -222,12 +229,12 @@ def _stepwise(spec, mod, batch, T):
         xin, xs = x, None
         h = torch.empty(pc, I, dtype=torch.bfloat16, device="cuda")
         hs = None
-    ws1 = torch.empty(max(M.moe_gemm1_workspace_size(pc, mod.lora), 1),
+    ws1 = torch.empty(max(M.moe_gemm1_workspace_size(mod.w13, pc, mod.lora), 1),
                       dtype=torch.uint8, device="cuda")
     M.moe_grouped_gemm1_act(mod.w13, xin, xs, x, T, H, I, k, pc, offsets, sp, mod.act,
                             mod.lora, h, hs, ws1)
     out = torch.empty(T, H, device="cuda")
-    ws2 = torch.empty(M.moe_gemm2_workspace_size(pc, H), dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty(M.moe_gemm2_workspace_size(mod.w2, pc), dtype=torch.uint8, device="cuda")
     M.moe_grouped_gemm2_combine(mod.w2, h, hs, T, H, I, k, spec.shared, pc, offsets, pr,
                                 w, spec.shared_w, out, ws2)
     torch.cuda.synchronize()
@@ -242,7 +249,8 @@ def _stepwise(spec, mod, batch, T):
 
 
 @pytest.mark.parametrize("name", ["tiny_bf16", "fp8_clamp_small", "fp8_oai_small",
-                                  "int4_small", "ep_lora_small"])
+                                  "int4_small", "ep_lora_small", "fp8_oai_sk",
+                                  "ep_lora_sk"])
 def test_gemm1_h_codes(name):
     """GEMM1 output h (codes and scales) against the oracle: equal wherever
     the exact h is not within the kernel's error of a rounding boundary;
@@ -273,10 +281,14 @@ def test_gemm1_h_codes(name):
         n_tot += diff.size
     _log(f"  h elements={n_tot} boundary={n_bnd} outside-admissible={n_bad}")
     assert n_bad == 0
-def test_stepwise_entry_points_match_forward_and_oracle():
+
+
+@pytest.mark.parametrize("name", ["ep_lora_small", "fp8_oai_sk", "ep_lora_sk"])
+def test_stepwise_entry_points_match_forward_and_oracle(name):
     """route -> permute -> quant -> gemm1 -> gemm2+combine through the
-    individual C-ABI calls gives moe_forward's output bit for bit."""
-    spec, T, layer, batch, arr, nb = _setup("ep_lora_small")
+    individual C-ABI calls gives moe_forward's output bit for bit (also on
+    the split-K schedule, whose partial sums live in different workspaces)."""
+    spec, T, layer, batch, arr, nb = _setup(name)
     _log("stepwise", spec.name, T)
     mod = module_for(spec, layer)
     ref_out = mod.forward(batch.x.cuda(), batch.logits.cuda())["out"].clone()
