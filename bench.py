@@ -280,8 +280,15 @@ def config_table(args, stream):
             batch = make_batch(spec, layer, T, device="cuda")
             outs = mod.alloc_outputs(T)
             mod.workspace(T)
-            for _ in range(args.warmup):
+            # warm up for >= 50 ms of wall time: a GPU left idle while the
+            # host builds a layer needs that long to return to full clocks
+            t_end = time.perf_counter() + 0.05
+            n = 0
+            while n < args.warmup or time.perf_counter() < t_end:
                 mod.forward(batch.x, batch.logits, outs)
+                n += 1
+                if n % 16 == 0:
+                    torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             a.record(stream)

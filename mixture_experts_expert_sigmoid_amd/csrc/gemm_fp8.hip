@@ -577,15 +577,32 @@ __global__ __launch_bounds__(kThreads) void gemm1_sk_epilogue_kernel(GemmParams 
       a[1][0] *= gsu; a[1][1] *= gsu;
     }
     if (P.z && g < P.lora_groups) {
+      // ranks in steps of 8 whose loads are all issued before the FMAs
+      // (ascending q, as in the fused epilogue)
       const int R = P.lora_rank;
       const uint16_t* Bg = P.lora_B + (long)g * 2 * I * R;
       const float* zr = P.z + (long)r * R;
-      for (int q = 0; q < R; ++q) {
-        const float zq = zr[q];
+      for (int q0 = 0; q0 < R; q0 += 8) {
+        float zq[8], bv[2][2][8];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          a[0][j] = fmaf(zq, P.lora_scale * bf16_bits_to_f32(Bg[(long)(c + j) * R + q]), a[0][j]);
-          a[1][j] = fmaf(zq, P.lora_scale * bf16_bits_to_f32(Bg[(long)(I + c + j) * R + q]), a[1][j]);
+        for (int i = 0; i < 8; ++i) {
+          const int q = min(q0 + i, R - 1);
+          zq[i] = zr[q];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            bv[0][j][i] = bf16_bits_to_f32(Bg[(long)(c + j) * R + q]);
+            bv[1][j][i] = bf16_bits_to_f32(Bg[(long)(I + c + j) * R + q]);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (q0 + i < R) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              a[0][j] = fmaf(zq[i], P.lora_scale * bv[0][j][i], a[0][j]);
+              a[1][j] = fmaf(zq[i], P.lora_scale * bv[1][j][i], a[1][j]);
+            }
+          }
         }
       }
     }

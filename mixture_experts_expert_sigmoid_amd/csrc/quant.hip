@@ -10,6 +10,8 @@
 // LoRA: the delta on gate/up must be in true units ("FlashInfer 0.6.18
 // SM100a+SM103a MoE-LoRA AOT" release notes, "Changes since 1b699bf");
 // z is kept in fp32 and consumed by the GEMM1 epilogue.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -68,82 +70,109 @@ hipError_t launch_quant_act(const void* x, long T, int H, void* xq, float* xs,
   return hipGetLastError();
 }
 
-// One workgroup (4 waves) per 16 consecutive sorted rows:
-// z[16 rows][16 ranks] = X A^T on v_mfma_f32_16x16x32_bf16 (bf16 products,
-// fp32 accumulation), the expert's A read once per tile instead of once
-// per row. Wave w covers the w-th quarter of H; the four partials are added
-// in wave order through LDS. Rows of a tile normally share one expert; a
-// tile that straddles expert boundaries is done once per expert it
-// touches, each pass keeping its own rows.
+// Exclusive prefix over the first G groups of ceil(rows_g / 16) into
+// s_cum[0..G] (256 threads, G <= 1024: four groups per thread).
+__device__ __forceinline__ void lora_tile_prefix(const int* offsets, int G, int* s_cum,
+                                                 int* s_wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int c[4], v = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = 4 * tid + i;
+    c[i] = g < G ? (offsets[g + 1] - offsets[g] + 15) >> 4 : 0;
+    v += c[i];
+  }
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  int run = incl - v;
+  for (int w = 0; w < wave; ++w) run += s_wsum[w];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = 4 * tid + i;
+    if (g < G) s_cum[g] = run;
+    run += c[i];
+  }
+  if (tid == 0) s_cum[G] = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+  __syncthreads();
+}
+
+// One workgroup (4 waves) per 16-row tile of one expert's sorted rows (tile
+// t of expert g covers rows offsets[g] + 16 (t - s_cum[g]) ..):
+// z[16 rows][16 ranks] = X A_g^T on v_mfma_f32_16x16x32_bf16 (bf16
+// products, fp32 accumulation), A_g read once per tile instead of once per
+// row. Wave w covers the w-th quarter of H; the four partials are added in
+// wave order through LDS.
 template <int NQ>    // 16-column blocks covering the rank
 __global__ __launch_bounds__(256) void lora_z_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ A, int rank,
-    long T, int H, int top_k, int n_lora_groups, long p_cap,
+    long T, int H, int top_k, int n_lora_groups,
     const int* __restrict__ offsets, const int* __restrict__ sorted_pair,
     float* __restrict__ z) {
   __shared__ f32x4 red[4][NQ][64];
-  const long r0 = (long)blockIdx.x * 16;
-  const long rend = min(p_cap, (long)offsets[n_lora_groups]);
-  if (r0 >= rend) return;                        // uniform over the workgroup
+  __shared__ int s_cum[1025];
+  __shared__ int s_wsum[4];
+  lora_tile_prefix(offsets, n_lora_groups, s_cum, s_wsum);
+  const int tile = blockIdx.x;
+  if (tile >= s_cum[n_lora_groups]) return;      // uniform over the workgroup
+  int g = 0, hi = n_lora_groups - 1;             // last g with s_cum[g] <= tile
+  while (g < hi) {
+    const int mid = (g + hi + 1) >> 1;
+    if (s_cum[mid] <= tile) g = mid; else hi = mid - 1;
+  }
+  const long r0 = offsets[g] + 16L * (tile - s_cum[g]);
+  const int m = (int)min(16L, (long)offsets[g + 1] - r0);
   const int wave = threadIdx.x >> 6, lane = lane_id(), lr = lane & 15, lg = lane >> 4;
-  auto group_of = [&](long row) {        // largest g with offsets[g] <= row
-    int lo = 0, hi = n_lora_groups - 1;
-    while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
-      if (offsets[mid] <= row) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-  };
   const int hq = H >> 2;                         // this wave's quarter of H
-  const long rl = min(r0 + lr, rend - 1);        // this lane's operand row
+  const long rl = r0 + min(lr, m - 1);           // this lane's operand row
   const uint16_t* xr = x + (long)(sorted_pair[rl] / top_k) * H + wave * hq + 8 * lg;
-  const int g0 = group_of(r0), g1 = group_of(min(r0 + 15, rend - 1));
-  for (int g = g0; g <= g1; ++g) {
-    const uint16_t* Ag = A + (long)g * rank * H + wave * hq + 8 * lg;
-    f32x4 acc[NQ];
+  const uint16_t* Ag = A + (long)g * rank * H + wave * hq + 8 * lg;
+  f32x4 acc[NQ];
 #pragma unroll
-    for (int n = 0; n < NQ; ++n) acc[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    // 8 K steps per round: all their loads are issued before the MFMAs
-    for (int h0 = 0; h0 < hq; h0 += 256) {
-      i32x4 xv[8], av[NQ][8];
+  for (int n = 0; n < NQ; ++n) acc[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // 8 K steps per round: all their loads are issued before the MFMAs
+  for (int h0 = 0; h0 < hq; h0 += 256) {
+    i32x4 xv[8], av[NQ][8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int h = min(h0 + 32 * j, hq - 32);   // hq % 32 == 0
-        xv[j] = *(const i32x4*)(xr + h);
-#pragma unroll
-        for (int n = 0; n < NQ; ++n) {
-          const int q = 16 * n + lr;
-          av[n][j] = (i32x4){0, 0, 0, 0};
-          if (q < rank) av[n][j] = *(const i32x4*)(Ag + (long)q * H + h);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (h0 + 32 * j >= hq) break;
-#pragma unroll
-        for (int n = 0; n < NQ; ++n)
-          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[j]),
-                                                          __builtin_bit_cast(bf16x8, av[n][j]),
-                                                          acc[n], 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int n = 0; n < NQ; ++n) red[wave][n][lane] = acc[n];
-    __syncthreads();
-    if (wave == 0) {
-      const long glo = offsets[g], ghi = min((long)offsets[g + 1], rend);
+    for (int j = 0; j < 8; ++j) {
+      const int h = min(h0 + 32 * j, hq - 32);   // hq % 32 == 0
+      xv[j] = *(const i32x4*)(xr + h);
 #pragma unroll
       for (int n = 0; n < NQ; ++n) {
-        const f32x4 v = ((red[0][n][lane] + red[1][n][lane]) + red[2][n][lane]) + red[3][n][lane];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const long row = r0 + 4 * lg + r;
-          const int q = 16 * n + lr;
-          if (row >= glo && row < ghi && q < rank) z[row * rank + q] = v[r];
-        }
+        const int q = 16 * n + lr;
+        av[n][j] = (i32x4){0, 0, 0, 0};
+        if (q < rank) av[n][j] = *(const i32x4*)(Ag + (long)q * H + h);
       }
     }
-    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (h0 + 32 * j >= hq) break;
+#pragma unroll
+      for (int n = 0; n < NQ; ++n)
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[j]),
+                                                        __builtin_bit_cast(bf16x8, av[n][j]),
+                                                        acc[n], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < NQ; ++n) red[wave][n][lane] = acc[n];
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+      const f32x4 v = ((red[0][n][lane] + red[1][n][lane]) + red[2][n][lane]) + red[3][n][lane];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tr = 4 * lg + r;
+        const int q = 16 * n + lr;
+        if (tr < m && q < rank) z[(r0 + tr) * rank + q] = v[r];
+      }
+    }
   }
 }
 
@@ -152,12 +181,13 @@ hipError_t launch_lora_z(const void* x_bf16, const void* A, int rank, long T,
                          const int* offsets, const int* sorted_pair, float* z,
                          hipStream_t s) {
   if (p_cap == 0 || n_lora_groups == 0) return hipSuccess;
-  const long tiles = (p_cap + 15) / 16;
+  // tiles <= one per non-empty expert plus one per 16 rows
+  const long tiles = std::min<long>(p_cap, n_lora_groups + p_cap / 16);
   dim3 grid((unsigned)tiles), block(256);
 #define LZ(NQ)                                                                \
   hipLaunchKernelGGL(lora_z_kernel<NQ>, grid, block, 0, s,                    \
                      (const uint16_t*)x_bf16, (const uint16_t*)A, rank, T, H, \
-                     top_k, n_lora_groups, p_cap, offsets, sorted_pair, z)
+                     top_k, n_lora_groups, offsets, sorted_pair, z)
   if (rank <= 16) LZ(1);
   else LZ(2);
 #undef LZ
