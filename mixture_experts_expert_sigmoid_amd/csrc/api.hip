@@ -143,16 +143,13 @@ size_t g1_z_bytes(long p_cap, const moe_lora* lora) {
   return lora ? al((size_t)p_cap * lora->rank * 4) : 0;
 }
 size_t g1_part_bytes(const moe_weights* w13, long p_cap) {
-  if (!moe::fp8_streamk(w13->fmt, p_cap, w13->n_groups, w13->N / 256, w13->K / 128))
-    return 0;
-  return al((size_t)moe::kSkSlots * p_cap * w13->N * 4);
+  if (!moe::fp8_splitk_possible(w13->fmt, p_cap, w13->N)) return 0;
+  return moe::splitk_bytes(p_cap, w13->N);
 }
 // GEMM2 workspace: fp32 y rows, or (stream-K) their partial sums
 size_t g2_bytes(const moe_weights* w2, long p_cap) {
-  const int NT = (w2->N + 255) / 256;
-  const size_t rows = moe::fp8_streamk(w2->fmt, p_cap, w2->n_groups, NT, w2->K / 128)
-                          ? (size_t)moe::kSkSlots * p_cap : (size_t)p_cap;
-  return al(rows * w2->N * 4);
+  if (moe::fp8_splitk_possible(w2->fmt, p_cap, w2->N)) return moe::splitk_bytes(p_cap, w2->N);
+  return al((size_t)p_cap * w2->N * 4);
 }
 }  // namespace
 

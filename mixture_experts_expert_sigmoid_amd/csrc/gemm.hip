@@ -332,6 +332,8 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t s) {
     if (!a.part) return launch_gemm_fp8(P, true, a.p_cap, a.I / 128, s);
     P.part = a.part;
     P.p_rows = a.p_cap;
+    P.sk_cus = num_cus();
+    P.sk_flag = (int*)((char*)a.part + splitk_slot_bytes(a.p_cap, 2 * a.I));
     int grid = 0;
     hipError_t e = launch_gemm_fp8(P, true, a.p_cap, a.I / 128, s, &grid);
     return e == hipSuccess ? launch_gemm1_sk_epilogue(P, grid, s) : e;
@@ -356,23 +358,19 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t s) {
   *a.sk_grid = 0;
   const int NT = (a.H + 255) / 256;
   if (a.fmt == FMT_FP8) {
-    if (!fp8_streamk(a.fmt, a.p_cap, a.G, NT, a.I / 128))
+    if (!fp8_splitk_possible(a.fmt, a.p_cap, a.H))
       return launch_gemm_fp8(P, false, a.p_cap, NT, s);
-    P.part = a.y;
+    P.part = a.y;                  // split: partial slots; plain: slot 0 = y
     P.p_rows = a.p_cap;
+    P.sk_cus = num_cus();
+    P.sk_flag = (int*)((char*)a.y + splitk_slot_bytes(a.p_cap, a.H));
     return launch_gemm_fp8(P, false, a.p_cap, NT, s, a.sk_grid);
   }
   return dispatch<false>(a.fmt, P, a.p_cap, NT, hint, s);
 }
 
-bool fp8_streamk(int fmt, long p_cap, int G, int NT, int NS) {
-  if (fmt != FMT_FP8 || p_cap <= 0) return false;
-  const long tiles = std::min<long>(p_cap, G + p_cap / kSkBM) * NT;
-  if (tiles > kSkMaxTiles) return false;
-  // one tile per workgroup in waves of kSkCUs: split K when the slots that
-  // schedule leaves idle add up to at least 8 K blocks per CU
-  const long waves = (tiles + kSkCUs - 1) / kSkCUs;
-  return (waves * kSkCUs - tiles) * NS >= 8 * kSkCUs;
+bool fp8_splitk_possible(int fmt, long p_cap, int N) {
+  return fmt == FMT_FP8 && p_cap > 0 && p_cap * (long)N <= kSkMaxPartial;
 }
 
 }  // namespace moe

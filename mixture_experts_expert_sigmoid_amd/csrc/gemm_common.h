@@ -82,9 +82,11 @@ struct GemmParams {
   float* hs;
   // GEMM2 out
   float* y;                  // [p_cap][N]
-  // stream-K (decode sizes): fp32 partial sums [kSkSlots][p_rows][N]
+  // split-K (decode sizes): fp32 partial sums [kSkSlots][p_rows][N]
   float* part;
   long p_rows;
+  int sk_cus;                // CUs of the device, for the split decision
+  int* sk_flag;              // written by the kernel: 1 = split, 0 = plain
 };
 
 
@@ -128,6 +130,16 @@ struct Tile {
 };
 
 // ---------------------------------------------------------------------------
+// Split or not (decided on the device from the real tile count, so the
+// producer and every consumer reach the same answer): split K when one tile
+// per workgroup, in waves over the CUs, would leave idle slots worth at
+// least 8 K blocks per CU.
+__device__ __forceinline__ bool sk_split(long tiles, int NS, int cus) {
+  if (tiles <= 0 || tiles > kSkMaxTiles) return false;
+  const long waves = (tiles + cus - 1) / cus;
+  return (waves * cus - tiles) * NS >= 8L * cus;
+}
+
 // stream-K schedule for decode sizes, where the tiles of a grouped GEMM are
 // fewer than the CUs: the U = tiles * NS (tile, K block) units are cut into
 // W equal contiguous ranges, one per workgroup; workgroup w owns units

@@ -471,22 +471,18 @@ __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, ui
 // of the smallest row class (32 / 64 / 128, at most TBM) that holds its
 // valid rows, so a lightly loaded expert does not pay for TBM rows of MFMA
 // work.
+// The tiles (TBM-row scheduling, s_cum its prefix) walked by persistent
+// workgroups: XCD x (= blockIdx % 8) owns logical tiles [x*chunk,
+// (x+1)*chunk), so the N-tiles of one expert share an L2.
 template <int TBM, bool G1>
-__global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // 2 stages
-  __shared__ int s_cum[kMaxGroups + 1];
-  __shared__ int s_wsum[8];
-
-  const int G = P.G;
+__device__ __forceinline__ void plain_tiles(const GemmParams& P, uint8_t* smem,
+                                            const int* s_cum) {
   const int NT = G1 ? (P.I >> 7) : ((P.N + 255) >> 8);
-
-  tile_prefix<TBM>(P.offsets, G, s_cum, s_wsum);
-  const int total = s_cum[G] * NT;
-  // XCD x (= blockIdx % 8) owns logical tiles [x*chunk, (x+1)*chunk)
+  const int NS = P.K >> 7;
+  const int total = s_cum[P.G] * NT;
   const int xcd = blockIdx.x & 7, nper = gridDim.x >> 3, slot = blockIdx.x >> 3;
   const int chunk = (total + 7) >> 3;
   const int t_end = min(total, (xcd + 1) * chunk);
-
   for (int lt = xcd * chunk + slot; lt < t_end; lt += nper) {
     Tile tl = decode_tile<TBM, G1>(P, lt, NT, s_cum);
     tl.g = __builtin_amdgcn_readfirstlane(tl.g);
@@ -495,7 +491,6 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
     tl.nt = __builtin_amdgcn_readfirstlane(tl.nt);
     tl.n_lo = __builtin_amdgcn_readfirstlane(tl.n_lo);
     tl.n_hi = __builtin_amdgcn_readfirstlane(tl.n_hi);
-    const int NS = P.K >> 7;
     if constexpr (TBM >= 128) {
       if (tl.m > 64) { fp8_tile<128, G1, false>(P, tl, smem, 0, NS); continue; }
     }
@@ -506,9 +501,20 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
   }
 }
 
-// Stream-K schedule over 32-row tiles (see gemm_common.h): workgroup b runs
-// the K-block segments of its unit range and leaves fp32 partial sums in
-// slot b - (first workgroup of the tile).
+template <int TBM, bool G1>
+__global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // 2 stages
+  __shared__ int s_cum[kMaxGroups + 1];
+  __shared__ int s_wsum[8];
+  tile_prefix<TBM>(P.offsets, P.G, s_cum, s_wsum);
+  plain_tiles<TBM, G1>(P, smem, s_cum);
+}
+
+// Split-K capable kernel over 32-row tiles (see gemm_common.h). When
+// sk_split holds for the real tile count, workgroup b runs the K-block
+// segments of its unit range and leaves fp32 partial sums in slot b -
+// (first workgroup of the tile); otherwise it runs the plain schedule with
+// the fused epilogue (GEMM2: y rows into slot 0).
 template <bool G1>
 __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_sk_kernel(GemmParams P) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -518,6 +524,12 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_sk_kernel(GemmParams P)
   const int NT = G1 ? (P.I >> 7) : ((P.N + 255) >> 8);
   const int NS = P.K >> 7;
   tile_prefix<kSkBM>(P.offsets, G, s_cum, s_wsum);
+  const bool split = sk_split((long)s_cum[G] * NT, NS, P.sk_cus);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *P.sk_flag = split ? 1 : 0;
+  if (!split) {
+    plain_tiles<kSkBM, G1>(P, smem, s_cum);
+    return;
+  }
   const long U = (long)s_cum[G] * NT * NS;
   const int W = sk_workgroups((long)s_cum[G] * NT, NS, gridDim.x);
   const int b = blockIdx.x;
@@ -546,6 +558,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_sk_kernel(GemmParams P)
 // units, parameterized SwiGLU, e4m3 re-quantisation per 128 columns); lane
 // l owns h columns nt*128 + 2l, 2l + 1.
 __global__ __launch_bounds__(kThreads) void gemm1_sk_epilogue_kernel(GemmParams P, int grid) {
+  if (*P.sk_flag == 0) return;                 // not split: the epilogue was fused
   __shared__ int s_cum[kMaxGroups + 1];
   __shared__ int s_off[kMaxGroups + 1];
   __shared__ int s_wsum[8];
