@@ -138,17 +138,21 @@ int moe_quantize_act_fp8(const void* x_bf16, long T, int H, void* xq,
 }  // extern "C"
 
 namespace {
-// GEMM1 workspace: LoRA z rows, then (stream-K) the fp32 partial sums
+// GEMM1 workspace: LoRA z rows, then (split-K) the fp32 partial sums, then
+// (INT4) the f16 activations, T <= p_cap rows of K
 size_t g1_z_bytes(long p_cap, const moe_lora* lora) {
   return lora ? al((size_t)p_cap * lora->rank * 4) : 0;
 }
 size_t g1_part_bytes(const moe_weights* w13, long p_cap) {
-  if (!moe::fp8_splitk_possible(w13->fmt, p_cap, w13->N)) return 0;
+  if (!moe::splitk_possible(w13->fmt, p_cap, w13->N)) return 0;
   return moe::splitk_bytes(p_cap, w13->N);
 }
-// GEMM2 workspace: fp32 y rows, or (stream-K) their partial sums
+size_t g1_x16_bytes(const moe_weights* w13, long rows) {
+  return w13->fmt == MOE_W_INT4_G32 ? al((size_t)rows * w13->K * 2) : 0;
+}
+// GEMM2 workspace: fp32 y rows, or (split-K) their partial sums
 size_t g2_bytes(const moe_weights* w2, long p_cap) {
-  if (moe::fp8_splitk_possible(w2->fmt, p_cap, w2->N)) return moe::splitk_bytes(p_cap, w2->N);
+  if (moe::splitk_possible(w2->fmt, p_cap, w2->N)) return moe::splitk_bytes(p_cap, w2->N);
   return al((size_t)p_cap * w2->N * 4);
 }
 }  // namespace
@@ -158,7 +162,7 @@ extern "C" {
 size_t moe_gemm1_workspace_size(const moe_weights* w13, long p_cap,
                                 const moe_lora* lora) {
   if (!w13 || p_cap < 0 || w13->N < 256 || w13->N % 256) return 0;
-  return g1_z_bytes(p_cap, lora) + g1_part_bytes(w13, p_cap);
+  return g1_z_bytes(p_cap, lora) + g1_part_bytes(w13, p_cap) + g1_x16_bytes(w13, p_cap);
 }
 
 static int gemm1_checks(const moe_weights* w13, const void* x, const float* xs,
@@ -184,7 +188,7 @@ static moe::Gemm1Args gemm1_args(const moe_weights* w13, const void* x,
                                  const int* sorted_pair,
                                  const moe_act_params* act,
                                  const moe_lora* lora, const float* z, void* h,
-                                 float* hs, float* part) {
+                                 float* hs, float* part, void* x16) {
   moe::Gemm1Args a{};
   a.fmt = w13->fmt;
   a.wq = w13->q;
@@ -211,6 +215,7 @@ static moe::Gemm1Args gemm1_args(const moe_weights* w13, const void* x,
   a.h = h;
   a.hs = hs;
   a.part = part;
+  a.x16 = x16;
   return a;
 }
 
@@ -226,16 +231,18 @@ int moe_grouped_gemm1_act(const moe_weights* w13, const void* x,
   size_t need = moe_gemm1_workspace_size(w13, p_cap, lora);
   if (need && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
+  if (w13->fmt == MOE_W_INT4_G32 && T > p_cap) return MOE_ERR_SHAPE;
   float* z = (float*)ws;
   float* part = g1_part_bytes(w13, p_cap)
                     ? (float*)((char*)ws + g1_z_bytes(p_cap, lora)) : nullptr;
+  void* x16 = (char*)ws + g1_z_bytes(p_cap, lora) + g1_part_bytes(w13, p_cap);
   hipError_t e = hipSuccess;
   if (lora)
     e = moe::launch_lora_z(x_bf16, lora->A, lora->rank, T, H, top_k,
                            lora->n_groups, p_cap, offsets, sorted_pair, z, s);
   if (e == hipSuccess)
     e = moe::launch_gemm1(gemm1_args(w13, x, xs, T, H, I, top_k, p_cap, offsets,
-                                     sorted_pair, act, lora, z, h, hs, part), s);
+                                     sorted_pair, act, lora, z, h, hs, part, x16), s);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_grouped_gemm1_act");
 }
 
@@ -315,7 +322,8 @@ FwdLayout layout(const moe_layer* L, long T) {
   o.pair_row = take((size_t)pc * 4);
   o.perm_bytes = moe::permute_ws_bytes(T, L->top_k, G);
   o.perm_ws = take(o.perm_bytes);
-  o.xq = take(fp8 ? (size_t)T * L->H : 0);
+  // FP8 activation codes, or (INT4) the f16 activations
+  o.xq = take(fp8 ? (size_t)T * L->H : g1_x16_bytes(&L->w13, T));
   o.xs = take(fp8 ? (size_t)T * (L->H / 128) * 4 : 0);
   o.z = take(L->lora ? (size_t)pc * L->lora->rank * 4 : 0);
   o.h = take((size_t)pc * L->I * (fp8 ? 1 : 2));
@@ -410,7 +418,7 @@ int moe_forward(const moe_layer* L, const void* x_bf16, const float* logits,
   e = moe::launch_gemm1(gemm1_args(&L->w13, fp8 ? xq : x_bf16, fp8 ? xs : nullptr,
                                    T, L->H, L->I, L->top_k, pc, offsets,
                                    sorted_pair, &L->act, L->lora, z, h,
-                                   fp8 ? hs : nullptr, g1_part), s);
+                                   fp8 ? hs : nullptr, g1_part, xq), s);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/gemm1");
   moe::Gemm2Args a{};
   a.fmt = L->w2.fmt;

@@ -328,15 +328,26 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t s) {
   P.h = (uint8_t*)a.h;
   P.hs = a.hs;
   long hint = a.G > 0 ? a.p_cap / a.G : a.p_cap;
-  if (a.fmt == FMT_FP8) {
-    if (!a.part) return launch_gemm_fp8(P, true, a.p_cap, a.I / 128, s);
+  if (a.fmt == FMT_FP8 || a.fmt == FMT_INT4) {
+    const bool fp8 = a.fmt == FMT_FP8;
+    hipError_t e = hipSuccess;
+    if (!fp8) {                    // f16 activations in the INT4 kernel's K order
+      e = launch_act_f16p(a.x, a.T, a.H, a.x16, s);
+      if (e != hipSuccess) return e;
+      P.a = (const uint8_t*)a.x16;
+    }
+    auto run = [&](int* grid) {
+      return fp8 ? launch_gemm_fp8(P, true, a.p_cap, a.I / 128, s, grid)
+                 : launch_gemm_int4(P, true, a.p_cap, a.I / 128, s, grid);
+    };
+    if (!a.part) return run(nullptr);
     P.part = a.part;
     P.p_rows = a.p_cap;
     P.sk_cus = num_cus();
     P.sk_flag = (int*)((char*)a.part + splitk_slot_bytes(a.p_cap, 2 * a.I));
     int grid = 0;
-    hipError_t e = launch_gemm_fp8(P, true, a.p_cap, a.I / 128, s, &grid);
-    return e == hipSuccess ? launch_gemm1_sk_epilogue(P, grid, s) : e;
+    e = run(&grid);
+    return e == hipSuccess ? launch_gemm1_sk_epilogue(P, grid, fp8, s) : e;
   }
   return dispatch<true>(a.fmt, P, a.p_cap, a.I / 128, hint, s);
 }
@@ -357,20 +368,24 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t s) {
   long hint = a.G > 0 ? a.p_cap / a.G : a.p_cap;
   *a.sk_grid = 0;
   const int NT = (a.H + 255) / 256;
-  if (a.fmt == FMT_FP8) {
-    if (!fp8_splitk_possible(a.fmt, a.p_cap, a.H))
-      return launch_gemm_fp8(P, false, a.p_cap, NT, s);
-    P.part = a.y;                  // split: partial slots; plain: slot 0 = y
-    P.p_rows = a.p_cap;
-    P.sk_cus = num_cus();
-    P.sk_flag = (int*)((char*)a.y + splitk_slot_bytes(a.p_cap, a.H));
-    return launch_gemm_fp8(P, false, a.p_cap, NT, s, a.sk_grid);
+  if (a.fmt == FMT_FP8 || a.fmt == FMT_INT4) {
+    const bool fp8 = a.fmt == FMT_FP8;
+    int* grid = nullptr;
+    if (splitk_possible(a.fmt, a.p_cap, a.H)) {
+      P.part = a.y;                // split: partial slots; plain: slot 0 = y
+      P.p_rows = a.p_cap;
+      P.sk_cus = num_cus();
+      P.sk_flag = (int*)((char*)a.y + splitk_slot_bytes(a.p_cap, a.H));
+      grid = a.sk_grid;
+    }
+    return fp8 ? launch_gemm_fp8(P, false, a.p_cap, NT, s, grid)
+               : launch_gemm_int4(P, false, a.p_cap, NT, s, grid);
   }
   return dispatch<false>(a.fmt, P, a.p_cap, NT, hint, s);
 }
 
-bool fp8_splitk_possible(int fmt, long p_cap, int N) {
-  return fmt == FMT_FP8 && p_cap > 0 && p_cap * (long)N <= kSkMaxPartial;
+bool splitk_possible(int fmt, long p_cap, int N) {
+  return (fmt == FMT_FP8 || fmt == FMT_INT4) && p_cap > 0 && p_cap * (long)N <= kSkMaxPartial;
 }
 
 }  // namespace moe

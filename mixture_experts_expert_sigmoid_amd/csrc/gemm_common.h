@@ -333,6 +333,13 @@ int num_cus();
 // consumer (launch_gemm1_sk_epilogue, or the combine) reduces them.
 hipError_t launch_gemm_fp8(const GemmParams& P, bool g1, long p_cap, int NT, hipStream_t s,
                            int* sk_grid = nullptr);
-hipError_t launch_gemm1_sk_epilogue(const GemmParams& P, int sk_grid, hipStream_t s);
+// fp8h: e4m3 h + scales (FP8 layers), else bf16 h (INT4 layers)
+hipError_t launch_gemm1_sk_epilogue(const GemmParams& P, int sk_grid, bool fp8h, hipStream_t s);
+
+// Group-32 INT4 grouped GEMM (gemm_int4.hip), same conventions; GEMM1
+// reads f16 activations prepared by launch_act_f16p.
+hipError_t launch_gemm_int4(const GemmParams& P, bool g1, long p_cap, int NT, hipStream_t s,
+                            int* sk_grid = nullptr);
+hipError_t launch_act_f16p(const void* x, long T, int H, void* out, hipStream_t s);
 
 }  // namespace moe

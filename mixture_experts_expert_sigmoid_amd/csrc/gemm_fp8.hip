@@ -553,10 +553,11 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_sk_kernel(GemmParams P)
 }
 
 // GEMM1 after stream-K: one wave per (sorted row r, 128 h columns nt) sums
-// the partial slots of r's tile in slot order, then applies the epilogue of
-// fp8_epilogue with the same arithmetic (global scales, LoRA delta in true
-// units, parameterized SwiGLU, e4m3 re-quantisation per 128 columns); lane
-// l owns h columns nt*128 + 2l, 2l + 1.
+// the partial slots of r's tile in slot order, then applies the fused
+// epilogue's arithmetic (global scales, LoRA delta in true units,
+// parameterized SwiGLU, then FP8H: e4m3 re-quantisation per 128 columns,
+// else bf16 round-to-nearest-even); lane l owns h columns nt*128 + 2l, 2l + 1.
+template <bool FP8H>
 __global__ __launch_bounds__(kThreads) void gemm1_sk_epilogue_kernel(GemmParams P, int grid) {
   if (*P.sk_flag == 0) return;                 // not split: the epilogue was fused
   __shared__ int s_cum[kMaxGroups + 1];
@@ -628,14 +629,19 @@ __global__ __launch_bounds__(kThreads) void gemm1_sk_epilogue_kernel(GemmParams 
       const float sg = __builtin_amdgcn_rcpf(1.0f + expf(-al * gg));
       hv[j] = gg * sg * (uu + be);
     }
-    const float am = wave_max(fmaxf(fabsf(hv[0]), fabsf(hv[1])));
-    const float sc = am > 0.0f ? am / 448.0f : 1.0f;
-    const float inv = 1.0f / sc;
-    const float q0 = __builtin_amdgcn_fmed3f(hv[0] * inv, -448.0f, 448.0f);
-    const float q1 = __builtin_amdgcn_fmed3f(hv[1] * inv, -448.0f, 448.0f);
-    const int v = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
-    *(uint16_t*)(P.h + (long)r * I + c) = (uint16_t)v;
-    if (lane == 0) P.hs[(long)r * NT + nt] = sc;
+    if constexpr (FP8H) {
+      const float am = wave_max(fmaxf(fabsf(hv[0]), fabsf(hv[1])));
+      const float sc = am > 0.0f ? am / 448.0f : 1.0f;
+      const float inv = 1.0f / sc;
+      const float q0 = __builtin_amdgcn_fmed3f(hv[0] * inv, -448.0f, 448.0f);
+      const float q1 = __builtin_amdgcn_fmed3f(hv[1] * inv, -448.0f, 448.0f);
+      const int v = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+      *(uint16_t*)(P.h + (long)r * I + c) = (uint16_t)v;
+      if (lane == 0) P.hs[(long)r * NT + nt] = sc;
+    } else {
+      *(uint32_t*)((uint16_t*)P.h + (long)r * I + c) =
+          f32_to_bf16_bits(hv[0]) | (f32_to_bf16_bits(hv[1]) << 16);
+    }
   }
 }
 
@@ -685,11 +691,14 @@ static hipError_t run_fp8_sk(const GemmParams& P, long p_cap, int NT, hipStream_
   return hipGetLastError();
 }
 
-hipError_t launch_gemm1_sk_epilogue(const GemmParams& P, int sk_grid, hipStream_t s) {
+hipError_t launch_gemm1_sk_epilogue(const GemmParams& P, int sk_grid, bool fp8h, hipStream_t s) {
   const long items = P.p_rows * (P.I >> 7);     // upper bound: rows used <= p_rows
   if (items == 0) return hipSuccess;
   const long nwg = std::min<long>((items + 7) / 8, (long)num_cus() * 4);
-  gemm1_sk_epilogue_kernel<<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(P, sk_grid);
+  if (fp8h)
+    gemm1_sk_epilogue_kernel<true><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(P, sk_grid);
+  else
+    gemm1_sk_epilogue_kernel<false><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(P, sk_grid);
   return hipGetLastError();
 }
 

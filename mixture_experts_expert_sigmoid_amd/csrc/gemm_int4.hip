@@ -1,0 +1,458 @@
+// Grouped GEMM for group-32 INT4 experts: GEMM1 over [gate | up] with the
+// parameterized SwiGLU epilogue writing bf16 h, and GEMM2 (down) writing
+// fp32 rows for the weighted combine.
+//
+// Format ("sm100: Fused INT4 grouped + SiLU Triton kernel", batchgen PR
+// #239, commit text): w[n][k] = (nibble - 8) * scale[n][k / 32], byte j of a
+// row holding k = 2j in its low nibble and k = 2j + 1 in its high nibble;
+// bf16 activations, fp32 accumulation.
+//
+// Arithmetic: each nibble is expanded in registers to the exact f16 value
+// (nibble - 8) * scale: an AND-OR with 0x6400 places a nibble n in the
+// mantissa of 1024 + n (or 1024 + 16 n for the second nibble of a byte),
+// one f16 subtraction leaves n - 8 (or 16 (n - 8)) exactly, and one f16
+// multiplication by the scale (or scale / 16) is exact because n - 8 has at
+// most 3 significant bits and a bf16 scale 8: the product fits f16's 11 for
+// scales in [2^-10, 2^15]. The products with f16 activations are formed on
+// v_mfma_f32_16x16x32_f16 and accumulated in fp32 across the whole K; no
+// per-block scaling step is needed (the scale is inside the operand).
+//
+// K order: the expansion of one dword (k0..k7 of a 32-K group) yields the
+// f16 values in the order k0, k4, k1, k5, k2, k6, k3, k7; the activations
+// are laid out with the same permutation of each 8 (by the f16 conversion
+// pass for GEMM1, while staging for GEMM2), so the dot products are
+// unchanged.
+//
+// Work split as in the FP8 kernel: 8 waves own BM rows of one expert and
+// 256 weight rows in two halves (GEMM1: 128 gate + the matching 128 up
+// rows; GEMM2: 256 output columns); wave w computes all BM rows of columns
+// 16w..16w+15 of both halves, weights go HBM -> registers (two 128-K blocks
+// in flight, 16 bytes per row and lane per block) and are expanded there;
+// the f16 activation block is staged in LDS (double buffered).
+#include "gemm_common.h"
+
+namespace moe {
+
+template <int BM>
+struct I4Geo {
+  static constexpr int MS = BM / 16;              // 16-row subtiles
+  static constexpr int A_BYTES = BM * 256;        // one K block, f16
+  static constexpr int A_CH = BM * 16;            // 16-byte chunks
+  static constexpr int A_PT = (A_CH + kThreads - 1) / kThreads;
+  static constexpr int STAGE = A_BYTES;
+  static constexpr int LDS = 2 * STAGE;
+};
+
+// f16 A rows are 256 bytes; chunk c of row r is stored at c ^ (r & 0b1011),
+// conflict-free for the fragment reads and the row-wise stores (the FP8
+// kernel's bf16 layout)
+__device__ __forceinline__ int i4_swz(int row, int c) { return c ^ (row & 11); }
+
+__device__ __forceinline__ f16x2 h2_bits(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
+
+// one dword of nibbles (k0..k7, low nibble first) -> the 8 exact f16 values
+// (n - 8) * s in the order k0, k4, k1, k5, k2, k6, k3, k7; s2 = (s, s),
+// s16 = (s / 16, s / 16)
+__device__ __forceinline__ f16x8 int4x8_f16(uint32_t w, f16x2 s2, f16x2 s16) {
+  const uint32_t w8 = w >> 8;
+  const f16x2 b1032 = h2_bits(0x64086408u), b1152 = h2_bits(0x64806480u);   // 1032, 1152
+  const f16x2 a = (h2_bits((w & 0x000F000Fu) | 0x64006400u) - b1032) * s2;
+  const f16x2 b = (h2_bits((w & 0x00F000F0u) | 0x64006400u) - b1152) * s16;
+  const f16x2 c = (h2_bits((w8 & 0x000F000Fu) | 0x64006400u) - b1032) * s2;
+  const f16x2 d = (h2_bits((w8 & 0x00F000F0u) | 0x64006400u) - b1152) * s16;
+  return (f16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// 8 bf16 (k0..k7) -> 8 f16 in the order k0, k4, k1, k5, k2, k6, k3, k7
+__device__ __forceinline__ f16x8 bf16x8_f16p(i32x4 v) {
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t u = (uint32_t)v[i];
+    f[2 * i] = __uint_as_float(u << 16);
+    f[2 * i + 1] = __uint_as_float(u & 0xFFFF0000u);
+  }
+  return (f16x8){(_Float16)f[0], (_Float16)f[4], (_Float16)f[1], (_Float16)f[5],
+                 (_Float16)f[2], (_Float16)f[6], (_Float16)f[3], (_Float16)f[7]};
+}
+
+// Accumulator layout: acc[ms][ns][r] is activation row 16 ms + (lane % 16)
+// and weight column (ns ? hi : lo) + 16 wave + 4 (lane / 16) + r.
+template <int BM, bool G1>
+__device__ __forceinline__ void int4_epilogue(const GemmParams& P, const Tile& t,
+                                              f32x4 (&acc)[BM / 16][2], uint8_t* smem) {
+  constexpr int MS = BM / 16;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int c0 = 16 * wave + 4 * lg;
+  const int g = t.g, row0 = t.row0, m = t.m;
+  if constexpr (!G1) {
+    const bool hi_ok = t.n_hi != t.n_lo;
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+      const int tr = 16 * ms + lr;
+      if (tr < m) {
+        float* yr = P.y + (long)(row0 + tr) * P.N;
+        *(f32x4*)(yr + t.n_lo + c0) = acc[ms][0];
+        if (hi_ok) *(f32x4*)(yr + t.n_hi + c0) = acc[ms][1];
+      }
+    }
+  } else {
+    if (P.gscale) {
+      const float gsg = P.gscale[2 * g], gsu = P.gscale[2 * g + 1];
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          acc[ms][0][r] *= gsg;
+          acc[ms][1][r] *= gsu;
+        }
+    }
+    if (P.z && g < P.lora_groups) {
+      // delta[row][n] = s * sum_q z[row][q] * B[g][n][q], z staged as [q][BM]
+      float* sz = (float*)smem;
+      const int R = P.lora_rank;
+      for (int i = tid; i < R * BM; i += kThreads) {
+        const int q = i / BM, tr = i - q * BM;
+        sz[q * BM + tr] = P.z[(long)(row0 + (tr < m ? tr : 0)) * R + q];
+      }
+      __syncthreads();
+      const uint16_t* Bg = P.lora_B + (long)g * 2 * P.I * R;
+      for (int q = 0; q < R; ++q) {
+        float bgv[4], buv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          bgv[r] = P.lora_scale * bf16_bits_to_f32(Bg[(long)(t.n_lo + c0 + r) * R + q]);
+          buv[r] = P.lora_scale * bf16_bits_to_f32(Bg[(long)(t.n_hi + c0 + r) * R + q]);
+        }
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) {
+          const float zq = sz[q * BM + 16 * ms + lr];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            acc[ms][0][r] = fmaf(zq, bgv[r], acc[ms][0][r]);
+            acc[ms][1][r] = fmaf(zq, buv[r], acc[ms][1][r]);
+          }
+        }
+      }
+      __syncthreads();
+    }
+    const float L = P.limit, al = P.alpha, be = P.beta;
+    uint16_t* h = (uint16_t*)P.h;
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+      const int tr = 16 * ms + lr;
+      uint32_t hb[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float gg = fminf(acc[ms][0][r], L);
+        const float uu = fminf(fmaxf(acc[ms][1][r], -L), L);
+        const float sg = __builtin_amdgcn_rcpf(1.0f + expf(-al * gg));
+        hb[r] = f32_to_bf16_bits(gg * sg * (uu + be));
+      }
+      if (tr < m)         // 4 consecutive h columns
+        *(uint2*)(h + (long)(row0 + tr) * P.I + t.nt * 128 + c0) =
+            (uint2){hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+    }
+  }
+}
+
+// One tile of BM rows over K blocks [k0, k1) (see the FP8 kernel for the
+// pipeline); PART: fp32 sums to partial slot `slot` (split-K).
+template <int BM, bool G1, bool PART = false>
+__device__ __forceinline__ void int4_tile(const GemmParams& P, const Tile& tl, uint8_t* smem,
+                                          int k0, int k1, int slot = 0) {
+  using Gm = I4Geo<BM>;
+  constexpr int MS = Gm::MS;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int K = P.K;
+  const int g = tl.g, row0 = tl.row0, m = tl.m;
+
+  // ---- sources at K block 0 ----------------------------------------------
+  // A: 256 bytes (128 f16 or bf16) per row and block, 16 chunks of 16
+  const uint8_t* ap[Gm::A_PT];
+  int a_st[Gm::A_PT];
+#pragma unroll
+  for (int i = 0; i < Gm::A_PT; ++i) {
+    const int cc = min(tid + i * kThreads, Gm::A_CH - 1);
+    const int row = cc >> 4, ch = cc & 15;
+    ap[i] = P.a + a_source_row<G1>(P, row0 + (row < m ? row : 0)) * P.a_ld + ch * 16;
+    a_st[i] = row * 256 + 16 * i4_swz(row, ch);
+  }
+  // weights: K / 2 bytes per row, 64 per block; this lane's 16 bytes hold
+  // K 32 lg .. 32 lg + 31 of the block, whose scale is group 4 s + lg
+  const long wrow = K >> 1;
+  const uint8_t* wg = P.w + (long)g * P.N * wrow;
+  const long nl = tl.n_lo + 16 * wave + lr, nh = tl.n_hi + 16 * wave + lr;
+  const uint8_t* bp0 = wg + nl * wrow + 16 * lg;
+  const uint8_t* bp1 = wg + nh * wrow + 16 * lg;
+  const uint16_t* sc = (const uint16_t*)P.wsc + (long)g * P.N * (K >> 5);
+  const uint16_t* sp0 = sc + nl * (K >> 5) + lg;
+  const uint16_t* sp1 = sc + nh * (K >> 5) + lg;
+
+  i32x4 ra[Gm::A_PT];
+  auto gload_a = [&](int s) {            // past the last block: re-read it
+    const long adv = (long)min(s, k1 - 1) * 256;
+#pragma unroll
+    for (int i = 0; i < Gm::A_PT; ++i) ra[i] = *(const i32x4*)(ap[i] + adv);
+  };
+  auto store_a = [&](int buf) {
+    uint8_t* st = smem + buf * Gm::STAGE;
+#pragma unroll
+    for (int i = 0; i < Gm::A_PT; ++i) {
+      if (Gm::A_CH % kThreads == 0 || tid + i * kThreads < Gm::A_CH) {
+        if constexpr (G1)                // already f16 in the K order above
+          *(i32x4*)(st + a_st[i]) = ra[i];
+        else                             // h: bf16 -> f16, reordered
+          *(f16x8*)(st + a_st[i]) = bf16x8_f16p(ra[i]);
+      }
+    }
+  };
+  struct WB {
+    i32x4 q[2];                          // lo, hi rows
+    uint32_t s[2];                       // their bf16 group scales
+  };
+  auto gload_b = [&](WB& b, int s) {
+    const int sb = min(s, k1 - 1);
+    b.q[0] = *(const i32x4*)(bp0 + (long)sb * 64);
+    b.q[1] = *(const i32x4*)(bp1 + (long)sb * 64);
+    b.s[0] = sp0[4 * sb];
+    b.s[1] = sp1[4 * sb];
+  };
+
+  f32x4 acc[MS][2];
+#pragma unroll
+  for (int i = 0; i < MS; ++i) {
+    acc[i][0] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    acc[i][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+
+  auto block = [&](int s, int buf, WB& rb) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) asm volatile("" : "+v"(rb.q[i]));
+    f16x8 bw[2][4];
+#pragma unroll
+    for (int ns = 0; ns < 2; ++ns) {
+      const _Float16 sh = (_Float16)bf16_bits_to_f32(rb.s[ns]);
+      const f16x2 s2 = (f16x2){sh, sh};
+      const f16x2 s16 = s2 * (f16x2){(_Float16)0.0625f, (_Float16)0.0625f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bw[ns][j] = int4x8_f16((uint32_t)rb.q[ns][j], s2, s16);
+    }
+    gload_a(s + 1);
+    gload_b(rb, s + 2);
+    const uint8_t* sa = smem + buf * Gm::STAGE;
+    auto lds_a = [&](int ms, f16x8 (&af)[4]) {
+      const int row = 16 * ms + lr;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        af[j] = *(const f16x8*)(sa + row * 256 + 16 * i4_swz(row, 4 * lg + j));
+    };
+    auto sub = [&](int ms, const f16x8 (&af)[4]) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[ms][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bw[0][j], af[j], acc[ms][0], 0, 0, 0);
+        acc[ms][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bw[1][j], af[j], acc[ms][1], 0, 0, 0);
+      }
+    };
+    f16x8 fr[2][4];
+    lds_a(0, fr[0]);
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+      if (ms + 1 < MS) lds_a(ms + 1, fr[(ms + 1) & 1]);
+      sub(ms, fr[ms & 1]);
+      if (ms + 1 < MS) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                    // MFMA
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    store_a(buf ^ 1);
+  };
+
+  WB rb0, rb1;
+  gload_b(rb0, k0);
+  gload_b(rb1, k0 + 1);
+  gload_a(k0);
+  store_a(0);
+  __syncthreads();
+  int s = k0;
+  for (; s + 2 <= k1; s += 2) {
+    block(s, 0, rb0);
+    __syncthreads();
+    block(s + 1, 1, rb1);
+    __syncthreads();
+  }
+  if (s < k1) {
+    block(s, 0, rb0);
+    __syncthreads();
+  }
+  if constexpr (PART) {
+    const int c0 = 16 * wave + 4 * lg;
+    const bool hi_ok = G1 || tl.n_hi != tl.n_lo;
+    float* base = P.part + ((long)slot * P.p_rows + row0) * P.N;
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+      const int tr = 16 * ms + lr;
+      if (tr < m) {
+        *(f32x4*)(base + (long)tr * P.N + tl.n_lo + c0) = acc[ms][0];
+        if (hi_ok) *(f32x4*)(base + (long)tr * P.N + tl.n_hi + c0) = acc[ms][1];
+      }
+    }
+  } else {
+    int4_epilogue<BM, G1>(P, tl, acc, smem);
+    __syncthreads();       // LDS is reused by the next tile
+  }
+}
+
+template <int TBM, bool G1>
+__device__ __forceinline__ void int4_plain_tiles(const GemmParams& P, uint8_t* smem,
+                                                 const int* s_cum) {
+  const int NT = G1 ? (P.I >> 7) : ((P.N + 255) >> 8);
+  const int NS = P.K >> 7;
+  const int total = s_cum[P.G] * NT;
+  const int xcd = blockIdx.x & 7, nper = gridDim.x >> 3, slot = blockIdx.x >> 3;
+  const int chunk = (total + 7) >> 3;
+  const int t_end = min(total, (xcd + 1) * chunk);
+  for (int lt = xcd * chunk + slot; lt < t_end; lt += nper) {
+    Tile tl = decode_tile<TBM, G1>(P, lt, NT, s_cum);
+    tl.g = __builtin_amdgcn_readfirstlane(tl.g);
+    tl.row0 = __builtin_amdgcn_readfirstlane(tl.row0);
+    tl.m = __builtin_amdgcn_readfirstlane(tl.m);
+    tl.nt = __builtin_amdgcn_readfirstlane(tl.nt);
+    tl.n_lo = __builtin_amdgcn_readfirstlane(tl.n_lo);
+    tl.n_hi = __builtin_amdgcn_readfirstlane(tl.n_hi);
+    if constexpr (TBM >= 128) {
+      if (tl.m > 64) { int4_tile<128, G1>(P, tl, smem, 0, NS); continue; }
+    }
+    if constexpr (TBM >= 64) {
+      if (tl.m > 32) { int4_tile<64, G1>(P, tl, smem, 0, NS); continue; }
+    }
+    int4_tile<32, G1>(P, tl, smem, 0, NS);
+  }
+}
+
+template <int TBM, bool G1>
+__global__ __launch_bounds__(kThreads) void moe_gemm_int4_kernel(GemmParams P) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int s_cum[kMaxGroups + 1];
+  __shared__ int s_wsum[8];
+  tile_prefix<TBM>(P.offsets, P.G, s_cum, s_wsum);
+  int4_plain_tiles<TBM, G1>(P, smem, s_cum);
+}
+
+// Split-K capable variant (schedule and decision as in the FP8 kernel)
+template <bool G1>
+__global__ __launch_bounds__(kThreads) void moe_gemm_int4_sk_kernel(GemmParams P) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int s_cum[kMaxGroups + 1];
+  __shared__ int s_wsum[8];
+  const int G = P.G;
+  const int NT = G1 ? (P.I >> 7) : ((P.N + 255) >> 8);
+  const int NS = P.K >> 7;
+  tile_prefix<kSkBM>(P.offsets, G, s_cum, s_wsum);
+  const bool split = sk_split((long)s_cum[G] * NT, NS, P.sk_cus);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *P.sk_flag = split ? 1 : 0;
+  if (!split) {
+    int4_plain_tiles<kSkBM, G1>(P, smem, s_cum);
+    return;
+  }
+  const long U = (long)s_cum[G] * NT * NS;
+  const int W = sk_workgroups((long)s_cum[G] * NT, NS, gridDim.x);
+  const int b = blockIdx.x;
+  if (b >= W) return;
+  const long u1 = (long)(b + 1) * U / W;
+  for (long u = (long)b * U / W; u < u1;) {
+    const int t = (int)(u / NS);
+    const int k0 = (int)(u - (long)t * NS);
+    const int k1 = (int)std::min<long>(NS, k0 + (u1 - u));
+    Tile tl = decode_tile<kSkBM, G1>(P, t, NT, s_cum);
+    tl.g = __builtin_amdgcn_readfirstlane(tl.g);
+    tl.row0 = __builtin_amdgcn_readfirstlane(tl.row0);
+    tl.m = __builtin_amdgcn_readfirstlane(tl.m);
+    tl.nt = __builtin_amdgcn_readfirstlane(tl.nt);
+    tl.n_lo = __builtin_amdgcn_readfirstlane(tl.n_lo);
+    tl.n_hi = __builtin_amdgcn_readfirstlane(tl.n_hi);
+    const int slot = b - sk_owner((long)t * NS, U, W);
+    int4_tile<kSkBM, G1, true>(P, tl, smem, k0, k1, slot);
+    u += k1 - k0;
+  }
+}
+
+// x bf16 [T][H] -> f16 [T][H] with each 8 columns in the order k0, k4, k1,
+// k5, k2, k6, k3, k7 (the GEMM1 activation operand); one thread per 8
+__global__ __launch_bounds__(256) void act_f16p_kernel(const uint16_t* __restrict__ x, long n8,
+                                                       uint16_t* __restrict__ out) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  *(f16x8*)(out + 8 * i) = bf16x8_f16p(*(const i32x4*)(x + 8 * i));
+}
+
+hipError_t launch_act_f16p(const void* x, long T, int H, void* out, hipStream_t s) {
+  const long n8 = T * (long)H / 8;
+  if (n8 == 0) return hipSuccess;
+  act_f16p_kernel<<<dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s>>>(
+      (const uint16_t*)x, n8, (uint16_t*)out);
+  return hipGetLastError();
+}
+
+template <int TBM, bool G1>
+static hipError_t run_int4(const GemmParams& P, long p_cap, int NT, hipStream_t s) {
+  constexpr int shm = I4Geo<TBM>::LDS;
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&moe_gemm_int4_kernel<TBM, G1>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, shm);
+    if (e != hipSuccess) return e;
+    int nb = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &nb, reinterpret_cast<const void*>(&moe_gemm_int4_kernel<TBM, G1>), kThreads, shm);
+    if (e != hipSuccess) return e;
+    per_cu = nb > 0 ? nb : 1;
+  }
+  long max_tiles = ((p_cap + TBM - 1) / TBM + P.G) * (long)NT;
+  long nwg = std::min<long>(max_tiles, (long)num_cus() * per_cu);
+  nwg = (nwg + 7) & ~7L;
+  if (nwg == 0) return hipSuccess;
+  moe_gemm_int4_kernel<TBM, G1><<<dim3((unsigned)nwg), dim3(kThreads), shm, s>>>(P);
+  return hipGetLastError();
+}
+
+template <bool G1>
+static hipError_t run_int4_sk(const GemmParams& P, long p_cap, hipStream_t s, int* sk_grid) {
+  constexpr int shm = I4Geo<kSkBM>::LDS;
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&moe_gemm_int4_sk_kernel<G1>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, shm);
+    if (e != hipSuccess) return e;
+    int nb = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &nb, reinterpret_cast<const void*>(&moe_gemm_int4_sk_kernel<G1>), kThreads, shm);
+    if (e != hipSuccess) return e;
+    per_cu = nb > 0 ? nb : 1;
+  }
+  const int grid = num_cus() * per_cu;
+  *sk_grid = grid;
+  if (p_cap == 0) return hipSuccess;
+  moe_gemm_int4_sk_kernel<G1><<<dim3((unsigned)grid), dim3(kThreads), shm, s>>>(P);
+  return hipGetLastError();
+}
+
+template <bool G1>
+static hipError_t run_int4_tbm(const GemmParams& P, long p_cap, int NT, hipStream_t s) {
+  const long hint = P.G > 0 ? p_cap / P.G : p_cap;
+  if (hint <= 32) return run_int4<32, G1>(P, p_cap, NT, s);
+  if (hint <= 64) return run_int4<64, G1>(P, p_cap, NT, s);
+  return run_int4<128, G1>(P, p_cap, NT, s);
+}
+
+hipError_t launch_gemm_int4(const GemmParams& P, bool g1, long p_cap, int NT, hipStream_t s,
+                            int* sk_grid) {
+  if (P.part)
+    return g1 ? run_int4_sk<true>(P, p_cap, s, sk_grid) : run_int4_sk<false>(P, p_cap, s, sk_grid);
+  return g1 ? run_int4_tbm<true>(P, p_cap, NT, s) : run_int4_tbm<false>(P, p_cap, NT, s);
+}
+
+}  // namespace moe

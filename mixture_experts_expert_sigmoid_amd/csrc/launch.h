@@ -29,8 +29,9 @@ hipError_t launch_lora_z(const void* x_bf16, const void* A, int rank, long T,
                          const int* offsets, const int* sorted_pair, float* z,
                          hipStream_t s);
 
-// Split-K (stream-K) for the FP8 grouped GEMMs at decode sizes. The host
-// only decides whether it is possible -- FP8 weights and fp32 partial sums
+// Split-K (stream-K) for the FP8 and INT4 grouped GEMMs at decode sizes. The
+// host only decides whether it is possible -- FP8 / INT4 weights and fp32
+// partial sums
 // of at most kSkMaxPartial elements per slot (p_cap * N), a shape-only rule
 // so workspace sizes need no device -- and then provides kSkSlots * p_cap *
 // N fp32 of workspace; the kernels decide from the real tile count whether
@@ -39,7 +40,7 @@ constexpr long kSkMaxTiles = 1024;
 constexpr long kSkMaxPartial = 4L << 20;
 constexpr int kSkSlots = 4;          // partial-sum slots per tile
 constexpr int kSkBM = 32;            // tile rows under the split-K kernels
-bool fp8_splitk_possible(int fmt, long p_cap, int N);
+bool splitk_possible(int fmt, long p_cap, int N);
 // bytes of a split-K workspace: the slots, then the kernel's decision word
 inline size_t splitk_slot_bytes(long p_cap, int N) {
   return ((size_t)kSkSlots * p_cap * N * 4 + 255) & ~(size_t)255;
@@ -65,7 +66,8 @@ struct Gemm1Args {
   float lora_scale;
   void* h;
   float* hs;
-  float* part;           // split-K partials (when fp8_splitk_possible) or NULL
+  float* part;           // split-K partials (when splitk_possible) or NULL
+  void* x16;             // INT4: f16 activations (T * H * 2 bytes) or NULL
 };
 hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t s);
 

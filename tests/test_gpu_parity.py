@@ -149,6 +149,9 @@ SMALL = {
         name="fp8_oai_sk", H=2048, I=2048, n_routed=16, cfg_id=26), 2),
     "ep_lora_sk": (CONFIGS["ep_lora_258"].scaled(
         name="ep_lora_sk", H=2048, I=2048, n_routed=64, offset=16, cfg_id=27), 1),
+    # INT4 at the C4 shape with 16 experts, T = 2: 16 pairs, split-K on GEMM1
+    "int4_sk": (CONFIGS["int4_g32_64"].scaled(
+        name="int4_sk", n_routed=16, cfg_id=28), 2),
 }
 
 _cache = {}
@@ -250,7 +253,7 @@ def _stepwise(spec, mod, batch, T):
 
 @pytest.mark.parametrize("name", ["tiny_bf16", "fp8_clamp_small", "fp8_oai_small",
                                   "int4_small", "ep_lora_small", "fp8_oai_sk",
-                                  "ep_lora_sk"])
+                                  "ep_lora_sk", "int4_sk"])
 def test_gemm1_h_codes(name):
     """GEMM1 output h (codes and scales) against the oracle: equal wherever
     the exact h is not within the kernel's error of a rounding boundary;
@@ -283,7 +286,7 @@ def test_gemm1_h_codes(name):
     assert n_bad == 0
 
 
-@pytest.mark.parametrize("name", ["ep_lora_small", "fp8_oai_sk", "ep_lora_sk"])
+@pytest.mark.parametrize("name", ["ep_lora_small", "fp8_oai_sk", "ep_lora_sk", "int4_sk"])
 def test_stepwise_entry_points_match_forward_and_oracle(name):
     """route -> permute -> quant -> gemm1 -> gemm2+combine through the
     individual C-ABI calls gives moe_forward's output bit for bit (also on
