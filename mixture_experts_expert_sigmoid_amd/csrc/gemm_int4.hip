@@ -50,16 +50,23 @@ __device__ __forceinline__ int i4_swz(int row, int c) { return c ^ (row & 11); }
 
 __device__ __forceinline__ f16x2 h2_bits(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 
+// (a & m) | c in one v_and_or_b32 (m uniform: one scalar operand per VOP3)
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
+  return r;
+}
+
 // one dword of nibbles (k0..k7, low nibble first) -> the 8 exact f16 values
 // (n - 8) * s in the order k0, k4, k1, k5, k2, k6, k3, k7; s2 = (s, s),
 // s16 = (s / 16, s / 16)
 __device__ __forceinline__ f16x8 int4x8_f16(uint32_t w, f16x2 s2, f16x2 s16) {
   const uint32_t w8 = w >> 8;
   const f16x2 b1032 = h2_bits(0x64086408u), b1152 = h2_bits(0x64806480u);   // 1032, 1152
-  const f16x2 a = (h2_bits((w & 0x000F000Fu) | 0x64006400u) - b1032) * s2;
-  const f16x2 b = (h2_bits((w & 0x00F000F0u) | 0x64006400u) - b1152) * s16;
-  const f16x2 c = (h2_bits((w8 & 0x000F000Fu) | 0x64006400u) - b1032) * s2;
-  const f16x2 d = (h2_bits((w8 & 0x00F000F0u) | 0x64006400u) - b1152) * s16;
+  const f16x2 a = (h2_bits(and_or(w, 0x000F000Fu, 0x64006400u)) - b1032) * s2;
+  const f16x2 b = (h2_bits(and_or(w, 0x00F000F0u, 0x64006400u)) - b1152) * s16;
+  const f16x2 c = (h2_bits(and_or(w8, 0x000F000Fu, 0x64006400u)) - b1032) * s2;
+  const f16x2 d = (h2_bits(and_or(w8, 0x00F000F0u, 0x64006400u)) - b1152) * s16;
   return (f16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
@@ -213,7 +220,7 @@ __device__ __forceinline__ void int4_tile(const GemmParams& P, const Tile& tl, u
     i32x4 q[2];                          // lo, hi rows
     uint32_t s[2];                       // their bf16 group scales
   };
-  auto gload_b = [&](WB& b, int s) {
+  auto gload_b = [&](WB& b, int s) {   // past the last block: re-read it
     const int sb = min(s, k1 - 1);
     b.q[0] = *(const i32x4*)(bp0 + (long)sb * 64);
     b.q[1] = *(const i32x4*)(bp1 + (long)sb * 64);
@@ -228,42 +235,71 @@ __device__ __forceinline__ void int4_tile(const GemmParams& P, const Tile& tl, u
     acc[i][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
 
-  auto block = [&](int s, int buf, WB& rb) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) asm volatile("" : "+v"(rb.q[i]));
-    f16x8 bw[2][4];
+  // The weight expansion is pipelined: each block is done in two K halves
+  // (32-deep steps j = 0, 1, then j = 2, 3); the MFMAs of the first half run
+  // while the second half's weights are expanded, and those of the second
+  // half while the next block's first half is expanded, the conversions
+  // spread over the subtiles between the MFMAs.
+  f16x8 bwA[2][2], bwB[2][2];            // [ns][j] of the first / second half
+  auto scale_regs = [&](const WB& b, f16x2 (&s2)[2], f16x2 (&s16)[2]) {
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns) {
-      const _Float16 sh = (_Float16)bf16_bits_to_f32(rb.s[ns]);
-      const f16x2 s2 = (f16x2){sh, sh};
-      const f16x2 s16 = s2 * (f16x2){(_Float16)0.0625f, (_Float16)0.0625f};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bw[ns][j] = int4x8_f16((uint32_t)rb.q[ns][j], s2, s16);
+      const _Float16 sh = (_Float16)bf16_bits_to_f32(b.s[ns]);
+      s2[ns] = (f16x2){sh, sh};
+      s16[ns] = s2[ns] * (f16x2){(_Float16)0.0625f, (_Float16)0.0625f};
     }
+  };
+  auto block = [&](int s, int buf, WB& rc, WB& rn) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) asm volatile("" : "+v"(rc.q[i]), "+v"(rn.q[i]));
+    f16x2 s2[2], s16[2], s2n[2], s16n[2];
+    scale_regs(rc, s2, s16);
+    scale_regs(rn, s2n, s16n);
     gload_a(s + 1);
-    gload_b(rb, s + 2);
     const uint8_t* sa = smem + buf * Gm::STAGE;
-    auto lds_a = [&](int ms, f16x8 (&af)[4]) {
-      const int row = 16 * ms + lr;
+    // A fragment of step t = (half h, subtile ms): chunks 4 lg + 2 h, + 1
+    auto lds_h = [&](int t, f16x8 (&af)[2]) {
+      const int h = t / MS, row = 16 * (t % MS) + lr;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        af[j] = *(const f16x8*)(sa + row * 256 + 16 * i4_swz(row, 4 * lg + j));
+      for (int jj = 0; jj < 2; ++jj)
+        af[jj] = *(const f16x8*)(sa + row * 256 + 16 * i4_swz(row, 4 * lg + 2 * h + jj));
     };
-    auto sub = [&](int ms, const f16x8 (&af)[4]) {
+    f16x8 fr[2][2];
+    lds_h(0, fr[0]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[ms][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bw[0][j], af[j], acc[ms][0], 0, 0, 0);
-        acc[ms][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bw[1][j], af[j], acc[ms][1], 0, 0, 0);
+    for (int t = 0; t < 2 * MS; ++t) {
+      const int h = t / MS, ms = t % MS;
+      if (t + 1 < 2 * MS) lds_h(t + 1, fr[(t + 1) & 1]);
+      if (t == MS) gload_b(rc, s + 2);   // this block's raw weights are expanded
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        acc[ms][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(h ? bwB[0][jj] : bwA[0][jj],
+                                                           fr[t & 1][jj], acc[ms][0], 0, 0, 0);
+        acc[ms][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(h ? bwB[1][jj] : bwA[1][jj],
+                                                           fr[t & 1][jj], acc[ms][1], 0, 0, 0);
       }
-    };
-    f16x8 fr[2][4];
-    lds_a(0, fr[0]);
+      // expansion items (ns, jj) of this step: item i goes to subtile i*MS/4
+      int nitem = 0;
 #pragma unroll
-    for (int ms = 0; ms < MS; ++ms) {
-      if (ms + 1 < MS) lds_a(ms + 1, fr[(ms + 1) & 1]);
-      sub(ms, fr[ms & 1]);
-      if (ms + 1 < MS) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                    // MFMA
+      for (int i = 0; i < 4; ++i) {
+        if (i * MS / 4 == ms) {
+          const int ns = i >> 1, jj = i & 1;
+          if (h == 0)
+            bwB[ns][jj] = int4x8_f16((uint32_t)rc.q[ns][2 + jj], s2[ns], s16[ns]);
+          else
+            bwA[ns][jj] = int4x8_f16((uint32_t)rn.q[ns][jj], s2n[ns], s16n[ns]);
+          ++nitem;
+        }
+      }
+      if (t + 1 < 2 * MS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // MFMA
+        if (q < 3) {                                                          // VALU
+          if (nitem == 1) __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+          if (nitem == 2) __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     store_a(buf ^ 1);
@@ -274,16 +310,25 @@ __device__ __forceinline__ void int4_tile(const GemmParams& P, const Tile& tl, u
   gload_b(rb1, k0 + 1);
   gload_a(k0);
   store_a(0);
+  {                                      // first half of block k0
+    f16x2 s2[2], s16[2];
+    scale_regs(rb0, s2, s16);
+#pragma unroll
+    for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        bwA[ns][jj] = int4x8_f16((uint32_t)rb0.q[ns][jj], s2[ns], s16[ns]);
+  }
   __syncthreads();
   int s = k0;
   for (; s + 2 <= k1; s += 2) {
-    block(s, 0, rb0);
+    block(s, 0, rb0, rb1);
     __syncthreads();
-    block(s + 1, 1, rb1);
+    block(s + 1, 1, rb1, rb0);
     __syncthreads();
   }
   if (s < k1) {
-    block(s, 0, rb0);
+    block(s, 0, rb0, rb1);
     __syncthreads();
   }
   if constexpr (PART) {
