@@ -62,6 +62,8 @@ def parse():
                     help="run only the forward at --profile-tokens (warmup + steps) and "
                          "a copy of known size, for rocprofv3 counter passes")
     ap.add_argument("--profile-tokens", type=int, default=T_MAIN)
+    ap.add_argument("--profile-config", default=WORKLOAD,
+                    help="seeded configuration the --profile run uses")
     ap.add_argument("--configs", action="store_true",
                     help="also time moe_forward on every seeded configuration at its "
                          "token counts and print a table to stderr (not part of the "
@@ -168,7 +170,7 @@ def main():
     from tests.gpu_helpers import module_for
 
     assert torch.cuda.is_available(), "bench needs a GPU"
-    spec = CONFIGS[WORKLOAD]
+    spec = CONFIGS[args.profile_config if args.profile else WORKLOAD]
     t0 = time.time()
     layer = make_layer(spec, device="cuda")
     torch.cuda.synchronize()
@@ -188,7 +190,7 @@ def main():
         for _ in range(args.warmup + args.steps):
             mod.forward(batch.x, batch.logits, outs)
         torch.cuda.synchronize()
-        print(f"# profile run done: copy 3 x 1 GiB, forward T={Tp} x "
+        print(f"# profile run done: copy 3 x 1 GiB, {spec.name} forward T={Tp} x "
               f"{args.warmup + args.steps}", flush=True)
         return
 

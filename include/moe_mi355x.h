@@ -172,12 +172,13 @@ int moe_quantize_act_fp8(const void *x_bf16, long T, int H, void *xq,
  * offsets / sorted_pair come from moe_permute for the same (T, top_k);
  * w13->n_groups = G, w13->N = 2I, w13->K = H. p_cap = rows allocated in h.
  * Limits: H % 128 == 0 and I % 128 == 0. Workspace:
- * moe_gemm1_workspace_size(w13, p_cap, lora) bytes: the LoRA z rows and,
- * for FP8 weights with p_cap * 2I <= 4 Mi, room for the fp32 partial sums
- * of a split-K schedule (4 * p_cap * 2I floats + 256 bytes): the kernel
- * splits the K blocks of its tiles over all CUs when the real tiles are too
- * few for the CUs, and reduces them in a fixed order. Returns 0 for a NULL
- * w13 or N not a multiple of 256. */
+ * moe_gemm1_workspace_size(w13, p_cap, lora) bytes: the LoRA z rows; for
+ * FP8 / INT4 weights at decode sizes (few enough tiles of 32 rows x 128 h
+ * columns that one tile per workgroup would leave CUs idle) the fp32
+ * partial sums of a split-K schedule (4 * p_cap * 2I floats), which spreads
+ * the K blocks of those tiles over all CUs and reduces them in a fixed
+ * order; for INT4 weights the f16 copy of the activations (p_cap * H * 2
+ * bytes, T <= p_cap). Returns 0 for a NULL w13 or N not a multiple of 256. */
 int moe_grouped_gemm1_act(const moe_weights *w13, const void *x,
                           const float *xs, const void *x_bf16, long T, int H,
                           int I, int top_k, long p_cap, const int *offsets,
@@ -196,10 +197,10 @@ size_t moe_gemm1_workspace_size(const moe_weights *w13, long p_cap,
  * [INT4-PR: slot-specific routing-weight reduction, fp32 accumulation].
  * Every out element is written (0 for a token with no local pair).
  * w2->N = H, w2->K = I. out fp32 [T][H]. Workspace:
- * moe_gemm2_workspace_size(w2, p_cap) bytes: the fp32 y rows, or for FP8
- * weights with p_cap * H <= 4 Mi room for their split-K partial sums
- * (4 * p_cap * H floats + 256 bytes, reduced by the combine in a fixed
- * order). Returns 0 for a NULL w2. */
+ * moe_gemm2_workspace_size(w2, p_cap) bytes: the fp32 y rows, or for FP8 /
+ * INT4 weights at decode sizes their split-K partial sums (4 * p_cap * H
+ * floats, reduced by the combine in a fixed order). Returns 0 for a NULL
+ * w2. */
 int moe_grouped_gemm2_combine(const moe_weights *w2, const void *h,
                               const float *hs, long T, int H, int I,
                               int top_k, int shared_expert, long p_cap,

@@ -144,7 +144,7 @@ size_t g1_z_bytes(long p_cap, const moe_lora* lora) {
   return lora ? al((size_t)p_cap * lora->rank * 4) : 0;
 }
 size_t g1_part_bytes(const moe_weights* w13, long p_cap) {
-  if (!moe::splitk_possible(w13->fmt, p_cap, w13->N)) return 0;
+  if (!moe::splitk_use(w13->fmt, p_cap, w13->n_groups, w13->N / 256, w13->K / 128)) return 0;
   return moe::splitk_bytes(p_cap, w13->N);
 }
 size_t g1_x16_bytes(const moe_weights* w13, long rows) {
@@ -152,7 +152,8 @@ size_t g1_x16_bytes(const moe_weights* w13, long rows) {
 }
 // GEMM2 workspace: fp32 y rows, or (split-K) their partial sums
 size_t g2_bytes(const moe_weights* w2, long p_cap) {
-  if (moe::splitk_possible(w2->fmt, p_cap, w2->N)) return moe::splitk_bytes(p_cap, w2->N);
+  if (moe::splitk_use(w2->fmt, p_cap, w2->n_groups, (w2->N + 255) / 256, w2->K / 128))
+    return moe::splitk_bytes(p_cap, w2->N);
   return al((size_t)p_cap * w2->N * 4);
 }
 }  // namespace

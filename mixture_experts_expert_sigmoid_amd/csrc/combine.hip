@@ -39,33 +39,27 @@ __global__ __launch_bounds__(256) void combine_kernel(
   *(f32x4*)(out + t * H + 4 * c4) = acc;
 }
 
-// The same combine over the output of the FP8 GEMM2's split-K kernel
-// (slots [kSkSlots][p_rows][H]): when that kernel split K, each y element is
-// first summed over the slots of its tile in slot order; otherwise y is
-// slot 0. The tile schedule is rebuilt exactly as
+// The same combine over the partial sums of the FP8 / INT4 GEMM2's split-K
+// kernel (slots [kSkSlots][p_rows][H]): each y element is first summed over
+// the slots of its tile in slot order. The tile schedule is rebuilt exactly as
 // the GEMM built it (32-row tiles, 256-column tiles, I / 128 K blocks). One
 // workgroup per (token, 2048 columns); its token's pairs are looked up once.
 constexpr int kCsCols = 2048;
 __global__ __launch_bounds__(512) void combine_sk_kernel(
     const float* __restrict__ part, long T, int H, int top_k, int shared,
     const int* __restrict__ pair_row, const float* __restrict__ topk_w,
-    float shared_w, float* __restrict__ out, int grid, const int* __restrict__ sk_flag,
-    long p_rows, int I, int G, const int* __restrict__ offsets) {
+    float shared_w, float* __restrict__ out, int grid, long p_rows, int I, int G,
+    const int* __restrict__ offsets) {
   __shared__ int s_cum[kMaxGroups + 1];
   __shared__ int s_off[kMaxGroups + 1];
   __shared__ int s_wsum[8];
   __shared__ int s_row[65], s_mt[65];
   __shared__ float s_w[65];
-  const bool split = *sk_flag != 0;            // the GEMM's own decision
   const int NT = (H + 255) >> 8, NS = I >> 7;
-  long U = 0;
-  int W = 1;
-  if (split) {                                 // uniform over the workgroup
-    tile_prefix<kSkBM>(offsets, G, s_cum, s_wsum);
-    for (int i = threadIdx.x; i <= G; i += 512) s_off[i] = offsets[i];
-    U = (long)s_cum[G] * NT * NS;
-    W = sk_workgroups((long)s_cum[G] * NT, NS, grid);
-  }
+  tile_prefix<kSkBM>(offsets, G, s_cum, s_wsum);
+  for (int i = threadIdx.x; i <= G; i += 512) s_off[i] = offsets[i];
+  const long U = (long)s_cum[G] * NT * NS;
+  const int W = sk_workgroups((long)s_cum[G] * NT, NS, grid);
   const int chunks = (H + kCsCols - 1) / kCsCols;
   const long t = blockIdx.x / chunks;
   const int col0 = (int)(blockIdx.x - t * chunks) * kCsCols;
@@ -77,7 +71,7 @@ __global__ __launch_bounds__(512) void combine_sk_kernel(
     s_row[j] = r;
     s_w[j] = j < top_k ? topk_w[t * top_k + j] : shared_w;
     int mt = 0;
-    if (split && r >= 0) {
+    if (r >= 0) {
       const int g = group_of_row(s_off, G, r);
       mt = s_cum[g] + (r - s_off[g]) / kSkBM;
     }
@@ -91,7 +85,7 @@ __global__ __launch_bounds__(512) void combine_sk_kernel(
   for (int j = 0; j < np; ++j) {               // ascending slot, shared last
     const int r = s_row[j];
     if (r < 0) continue;
-    const int nsl = split ? sk_nslots(((long)s_mt[j] * NT + nt) * NS, NS, U, W) : 1;
+    const int nsl = sk_nslots(((long)s_mt[j] * NT + nt) * NS, NS, U, W);
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
     for (int sl = 0; sl < nsl; ++sl) {
       const f32x4 p = *(const f32x4*)(part + ((long)sl * p_rows + r) * H + col);
@@ -114,8 +108,7 @@ hipError_t launch_combine(const float* y, long T, int H, int top_k, int shared,
   if (sk_grid > 0) {
     const long nwg = T * ((H + kCsCols - 1) / kCsCols);
     hipLaunchKernelGGL(combine_sk_kernel, dim3((unsigned)nwg), dim3(512), 0, s, y, T, H,
-                       top_k, shared, pair_row, topk_w, shared_w, out, sk_grid,
-                       (const int*)((const char*)y + splitk_slot_bytes(p_cap, H)), p_cap,
+                       top_k, shared, pair_row, topk_w, shared_w, out, sk_grid, p_cap,
                        I, G, offsets);
     return hipGetLastError();
   }

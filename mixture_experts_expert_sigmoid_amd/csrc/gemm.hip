@@ -343,8 +343,6 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t s) {
     if (!a.part) return run(nullptr);
     P.part = a.part;
     P.p_rows = a.p_cap;
-    P.sk_cus = num_cus();
-    P.sk_flag = (int*)((char*)a.part + splitk_slot_bytes(a.p_cap, 2 * a.I));
     int grid = 0;
     e = run(&grid);
     return e == hipSuccess ? launch_gemm1_sk_epilogue(P, grid, fp8, s) : e;
@@ -371,11 +369,9 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t s) {
   if (a.fmt == FMT_FP8 || a.fmt == FMT_INT4) {
     const bool fp8 = a.fmt == FMT_FP8;
     int* grid = nullptr;
-    if (splitk_possible(a.fmt, a.p_cap, a.H)) {
-      P.part = a.y;                // split: partial slots; plain: slot 0 = y
+    if (splitk_use(a.fmt, a.p_cap, a.G, NT, a.I / 128)) {
+      P.part = a.y;                // the partial-sum slots
       P.p_rows = a.p_cap;
-      P.sk_cus = num_cus();
-      P.sk_flag = (int*)((char*)a.y + splitk_slot_bytes(a.p_cap, a.H));
       grid = a.sk_grid;
     }
     return fp8 ? launch_gemm_fp8(P, false, a.p_cap, NT, s, grid)
@@ -384,8 +380,12 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t s) {
   return dispatch<false>(a.fmt, P, a.p_cap, NT, hint, s);
 }
 
-bool splitk_possible(int fmt, long p_cap, int N) {
-  return (fmt == FMT_FP8 || fmt == FMT_INT4) && p_cap > 0 && p_cap * (long)N <= kSkMaxPartial;
+bool splitk_use(int fmt, long p_cap, int G, int NT, int NS) {
+  if ((fmt != FMT_FP8 && fmt != FMT_INT4) || p_cap <= 0) return false;
+  const long tiles = std::min<long>(p_cap, G + p_cap / kSkBM) * NT;
+  if (tiles > kSkMaxTiles) return false;
+  const long waves = (tiles + kSkCUs - 1) / kSkCUs;
+  return (waves * kSkCUs - tiles) * NS >= 8 * kSkCUs;
 }
 
 }  // namespace moe

@@ -85,8 +85,6 @@ struct GemmParams {
   // split-K (decode sizes): fp32 partial sums [kSkSlots][p_rows][N]
   float* part;
   long p_rows;
-  int sk_cus;                // CUs of the device, for the split decision
-  int* sk_flag;              // written by the kernel: 1 = split, 0 = plain
 };
 
 
@@ -130,16 +128,6 @@ struct Tile {
 };
 
 // ---------------------------------------------------------------------------
-// Split or not (decided on the device from the real tile count, so the
-// producer and every consumer reach the same answer): split K when one tile
-// per workgroup, in waves over the CUs, would leave idle slots worth at
-// least 8 K blocks per CU.
-__device__ __forceinline__ bool sk_split(long tiles, int NS, int cus) {
-  if (tiles <= 0 || tiles > kSkMaxTiles) return false;
-  const long waves = (tiles + cus - 1) / cus;
-  return (waves * cus - tiles) * NS >= 8L * cus;
-}
-
 // stream-K schedule for decode sizes, where the tiles of a grouped GEMM are
 // fewer than the CUs: the U = tiles * NS (tile, K block) units are cut into
 // W equal contiguous ranges, one per workgroup; workgroup w owns units
@@ -147,9 +135,11 @@ __device__ __forceinline__ bool sk_split(long tiles, int NS, int cus) {
 // ceil(NS / (kSkSlots - 1)) units, which bounds the workgroups meeting one
 // tile -- its partial-sum slots -- to kSkSlots. When the tiles already fill
 // 80..100 % of the grid, W = tiles: one whole tile per workgroup, one slot.
-// Partials are reduced in slot order by the consumer, so results do not
-// depend on timing. Producer and consumers evaluate this from the same
-// (tiles, NS, grid).
+// With more tiles than workgroups each range spans several whole tiles and
+// at most two split ones, so the work is balanced to one K block. Partials
+// are reduced in slot order by the consumer, so results do not depend on
+// timing. Producer and consumers evaluate this from the same (tiles, NS,
+// grid).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int sk_workgroups(long tiles, int NS, int grid) {
   if (tiles <= grid && tiles * 5 >= 4L * grid) return (int)tiles;

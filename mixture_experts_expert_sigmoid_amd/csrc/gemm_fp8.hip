@@ -510,11 +510,9 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
   plain_tiles<TBM, G1>(P, smem, s_cum);
 }
 
-// Split-K capable kernel over 32-row tiles (see gemm_common.h). When
-// sk_split holds for the real tile count, workgroup b runs the K-block
-// segments of its unit range and leaves fp32 partial sums in slot b -
-// (first workgroup of the tile); otherwise it runs the plain schedule with
-// the fused epilogue (GEMM2: y rows into slot 0).
+// Split-K (stream-K) kernel over 32-row tiles (see gemm_common.h):
+// workgroup b runs the K-block segments of its unit range and leaves fp32
+// partial sums in slot b - (first workgroup of the tile).
 template <bool G1>
 __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_sk_kernel(GemmParams P) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -524,12 +522,6 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_sk_kernel(GemmParams P)
   const int NT = G1 ? (P.I >> 7) : ((P.N + 255) >> 8);
   const int NS = P.K >> 7;
   tile_prefix<kSkBM>(P.offsets, G, s_cum, s_wsum);
-  const bool split = sk_split((long)s_cum[G] * NT, NS, P.sk_cus);
-  if (blockIdx.x == 0 && threadIdx.x == 0) *P.sk_flag = split ? 1 : 0;
-  if (!split) {
-    plain_tiles<kSkBM, G1>(P, smem, s_cum);
-    return;
-  }
   const long U = (long)s_cum[G] * NT * NS;
   const int W = sk_workgroups((long)s_cum[G] * NT, NS, gridDim.x);
   const int b = blockIdx.x;
@@ -559,7 +551,6 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_sk_kernel(GemmParams P)
 // else bf16 round-to-nearest-even); lane l owns h columns nt*128 + 2l, 2l + 1.
 template <bool FP8H>
 __global__ __launch_bounds__(kThreads) void gemm1_sk_epilogue_kernel(GemmParams P, int grid) {
-  if (*P.sk_flag == 0) return;                 // not split: the epilogue was fused
   __shared__ int s_cum[kMaxGroups + 1];
   __shared__ int s_off[kMaxGroups + 1];
   __shared__ int s_wsum[8];

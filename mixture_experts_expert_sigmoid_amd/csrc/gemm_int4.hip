@@ -385,7 +385,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_int4_kernel(GemmParams P) {
   int4_plain_tiles<TBM, G1>(P, smem, s_cum);
 }
 
-// Split-K capable variant (schedule and decision as in the FP8 kernel)
+// Split-K (stream-K) variant, schedule as in the FP8 kernel
 template <bool G1>
 __global__ __launch_bounds__(kThreads) void moe_gemm_int4_sk_kernel(GemmParams P) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -395,12 +395,6 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_int4_sk_kernel(GemmParams P
   const int NT = G1 ? (P.I >> 7) : ((P.N + 255) >> 8);
   const int NS = P.K >> 7;
   tile_prefix<kSkBM>(P.offsets, G, s_cum, s_wsum);
-  const bool split = sk_split((long)s_cum[G] * NT, NS, P.sk_cus);
-  if (blockIdx.x == 0 && threadIdx.x == 0) *P.sk_flag = split ? 1 : 0;
-  if (!split) {
-    int4_plain_tiles<kSkBM, G1>(P, smem, s_cum);
-    return;
-  }
   const long U = (long)s_cum[G] * NT * NS;
   const int W = sk_workgroups((long)s_cum[G] * NT, NS, gridDim.x);
   const int b = blockIdx.x;

@@ -29,23 +29,21 @@ hipError_t launch_lora_z(const void* x_bf16, const void* A, int rank, long T,
                          const int* offsets, const int* sorted_pair, float* z,
                          hipStream_t s);
 
-// Split-K (stream-K) for the FP8 and INT4 grouped GEMMs at decode sizes. The
-// host only decides whether it is possible -- FP8 / INT4 weights and fp32
-// partial sums
-// of at most kSkMaxPartial elements per slot (p_cap * N), a shape-only rule
-// so workspace sizes need no device -- and then provides kSkSlots * p_cap *
-// N fp32 of workspace; the kernels decide from the real tile count whether
-// to split (sk_split) and the consumers re-derive that decision.
+// Split-K (stream-K) for the FP8 and INT4 grouped GEMMs at decode sizes:
+// used when at most kSkMaxTiles tiles of 32 rows can exist (tiles <=
+// min(p_cap, G + p_cap / 32) * NT, NS K blocks each) and one tile per
+// workgroup, in waves over an MI355X's kSkCUs CUs, would leave idle slots
+// worth at least 8 K blocks per CU. A shape-only rule, so workspace sizes
+// need no device; the partial sums need kSkSlots * p_cap * N fp32.
 constexpr long kSkMaxTiles = 1024;
-constexpr long kSkMaxPartial = 4L << 20;
+constexpr long kSkCUs = 256;
 constexpr int kSkSlots = 4;          // partial-sum slots per tile
 constexpr int kSkBM = 32;            // tile rows under the split-K kernels
-bool splitk_possible(int fmt, long p_cap, int N);
-// bytes of a split-K workspace: the slots, then the kernel's decision word
-inline size_t splitk_slot_bytes(long p_cap, int N) {
+bool splitk_use(int fmt, long p_cap, int G, int NT, int NS);
+// bytes of a split-K workspace (the partial-sum slots)
+inline size_t splitk_bytes(long p_cap, int N) {
   return ((size_t)kSkSlots * p_cap * N * 4 + 255) & ~(size_t)255;
 }
-inline size_t splitk_bytes(long p_cap, int N) { return splitk_slot_bytes(p_cap, N) + 256; }
 
 struct Gemm1Args {
   int fmt;
@@ -66,7 +64,7 @@ struct Gemm1Args {
   float lora_scale;
   void* h;
   float* hs;
-  float* part;           // split-K partials (when splitk_possible) or NULL
+  float* part;           // split-K partials (when splitk_use) or NULL
   void* x16;             // INT4: f16 activations (T * H * 2 bytes) or NULL
 };
 hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t s);
@@ -85,9 +83,8 @@ struct Gemm2Args {
 };
 hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t s);
 
-// sk_grid > 0: y holds the output of the FP8 GEMM2's split-K kernel over G
-// groups -- partial sums reduced here per element in slot order, or plain
-// rows in slot 0 when that kernel chose not to split
+// sk_grid > 0: y holds the partial sums of the FP8 / INT4 GEMM2's split-K
+// kernel over G groups, reduced here per element in slot order
 hipError_t launch_combine(const float* y, long T, int H, int top_k, int shared,
                           const int* pair_row, const float* topk_w,
                           float shared_w, float* out, hipStream_t s,
