@@ -1,14 +1,10 @@
-// Grouped expert GEMMs on CDNA4 MFMA for the BF16 and INT4 formats: GEMM1
-// over the fused [gate | up] weight with the parameterized-SwiGLU epilogue
-// (plus optional per-half global scales and LoRA delta), and GEMM2 (down)
-// writing fp32 rows for the weighted combine. Blockwise-FP8 layers use the
-// kernel of gemm_fp8.hip.
+// Grouped expert GEMMs on CDNA4 MFMA for BF16 layers: GEMM1 over the fused
+// [gate | up] weight with the parameterized-SwiGLU epilogue (plus optional
+// per-half global scales and LoRA delta), and GEMM2 (down) writing fp32 rows
+// for the weighted combine. Blockwise-FP8 layers use the kernels of
+// gemm_fp8.hip, group-32 INT4 layers those of gemm_int4.hip; this file also
+// holds the host dispatch for all three formats.
 //
-// Formats:
-//   INT4 group-32 weights, byte = (odd k nibble << 4) | even k nibble,
-//        w = (nibble - 8) * scale[n][k/32] ("sm100: Fused INT4 grouped +
-//        SiLU Triton kernel", batchgen PR #239, commit text).
-//   BF16 weights and activations.
 // Epilogue: g' = min(g, L), u' = clamp(u, -L, L), h = g' sigmoid(alpha g')
 // (u' + beta) ("[Moe] Fix flashinfer_trtllm silently dropping swiglu_limit
 // clamped SwiGLU activation", sglang PR #39920, "Modifications"; "fix(sm90):
@@ -16,14 +12,7 @@
 // "Summary"). The LoRA delta and the per-half global scales follow the
 // true-units rule of "FlashInfer 0.6.18 SM100a+SM103a MoE-LoRA AOT"
 // ("Changes since 1b699bf"): each half is scaled by its own global scale
-// first, then the delta is added.
-//
-// Arithmetic: INT4 weights are expanded EXACTLY to fp16 while the tile is
-// written into LDS ((nibble - 8) * bf16 scale has at most 11 significant
-// bits; 0x6400 | nibble is the fp16 1024 + nibble, minus 1032 gives
-// nibble - 8) and the bf16 activations are converted to fp16 for that path;
-// BF16 tiles are stored as they are. Products run on
-// v_mfma_f32_16x16x32_{f16,bf16}.
+// first, then the delta is added. Products run on v_mfma_f32_16x16x32_bf16.
 //
 // Tiling: a workgroup of 8 waves owns BM sorted rows of one expert and 256
 // weight rows in two halves of 128 ("lo", "hi"): for GEMM1 lo = gate rows
@@ -31,10 +20,10 @@
 // 128 complete h columns; for GEMM2 lo/hi are output columns n0..n0+255.
 // Wave (wm, wn) computes rows wm*BM/2.. of columns wn*32..wn*32+31 of both
 // halves, so gate and up values of one h element sit in the same lane. K
-// advances 64 per stage: global -> registers (two stages in flight) ->
-// expansion -> LDS (double buffered, one barrier per stage). LDS rows are
-// 128 bytes; their 16-byte chunks are XOR-swizzled with (row / 2) mod 8 so
-// the 16 rows read by one ds_read_b128 are free of bank conflicts.
+// advances 64 per stage: global -> registers (two stages in flight) -> LDS
+// (double buffered, one barrier per stage). LDS rows are 128 bytes; their
+// 16-byte chunks are XOR-swizzled with (row / 2) mod 8 so the 16 rows read
+// by one ds_read_b128 are free of bank conflicts.
 // Workgroups are persistent: each computes the tile count from the expert
 // offsets on the device and walks its XCD's contiguous share of the tiles,
 // so the N-tiles of one expert (which share the gathered activation rows)
@@ -43,13 +32,13 @@
 
 namespace moe {
 
-template <int FMT, int BM>
+template <int BM>
 struct Geo {
   // per 64-K stage, in 16-byte global chunks
   static constexpr int A_SRC = 128;                               // bytes per A row
   static constexpr int A_CH = BM * A_SRC / 16;
   static constexpr int A_PT = (A_CH + kThreads - 1) / kThreads;   // loads per thread
-  static constexpr int B_SRC = (FMT == FMT_INT4) ? 32 : 128;
+  static constexpr int B_SRC = 128;
   static constexpr int B_CH = 256 * B_SRC / 16;
   static constexpr int B_PT = B_CH / kThreads;
   static constexpr int A_LDS = BM * 128;                          // 16-bit tile bytes
@@ -58,16 +47,15 @@ struct Geo {
   static constexpr int TOTAL = 2 * STAGE;
 };
 
-template <int FMT, int BM>
+template <int BM>
 struct Regs {
-  i32x4 a[Geo<FMT, BM>::A_PT];
-  i32x4 b[Geo<FMT, BM>::B_PT];
-  uint32_t sc;    // INT4: this thread's bf16 group scale
+  i32x4 a[Geo<BM>::A_PT];
+  i32x4 b[Geo<BM>::B_PT];
 };
 
-template <int FMT, int BM, bool G1>
+template <int BM, bool G1>
 __global__ __launch_bounds__(kThreads) void moe_gemm_kernel(GemmParams P) {
-  using Gm = Geo<FMT, BM>;
+  using Gm = Geo<BM>;
   constexpr int MS = BM / 32;            // 16-row subtiles per wave
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_cum[kMaxGroups + 1];
@@ -90,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_kernel(GemmParams P) {
   for (int lt = xcd * chunk + slot; lt < t_end; lt += nper) {
     const Tile tl = decode_tile<BM, G1>(P, lt, NT, s_cum);
     const int g = tl.g, row0 = tl.row0, m = tl.m, n_lo = tl.n_lo, n_hi = tl.n_hi;
-    const long wrow = (FMT == FMT_INT4) ? K / 2 : (long)K * 2;
+    const long wrow = (long)K * 2;
     const uint8_t* wg = P.w + (long)g * P.N * wrow;
 
     // ---- per-thread global sources for this tile -------------------------
@@ -117,16 +105,10 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_kernel(GemmParams P) {
       int n = (row < 128) ? n_lo + row : n_hi + (row - 128);
       bp[i] = wg + (long)n * wrow + ch * 16;
     }
-    const uint16_t* scp = nullptr;   // INT4: bf16 scale row of this thread's B chunk
-    if (FMT == FMT_INT4) {
-      int row = b_row[0];
-      int n = (row < 128) ? n_lo + row : n_hi + (row - 128);
-      scp = (const uint16_t*)P.wsc + ((long)g * P.N + n) * (K / 32) + b_ch[0];
-    }
 
     // Loads are unconditional (past the last stage they re-read it) so the
     // compiler's wait counts stay static and two stages remain in flight.
-    auto gload = [&](Regs<FMT, BM>& R, int s) {
+    auto gload = [&](Regs<BM>& R, int s) {
       s = min(s, NS - 1);
       const long adv = (long)s * Gm::A_SRC;
 #pragma unroll
@@ -134,9 +116,8 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_kernel(GemmParams P) {
       const long bdv = (long)s * Gm::B_SRC;
 #pragma unroll
       for (int i = 0; i < Gm::B_PT; ++i) R.b[i] = *(const i32x4*)(bp[i] + bdv);
-      if (FMT == FMT_INT4) R.sc = scp[2 * s];
     };
-    auto sstore = [&](const Regs<FMT, BM>& R, int s, auto par, auto guard) {
+    auto sstore = [&](const Regs<BM>& R, int s, auto par, auto guard) {
       constexpr int PAR = decltype(par)::value;
       if (decltype(guard)::value && s >= NS) return;
       uint8_t* sa = smem + PAR * Gm::STAGE;
@@ -146,25 +127,12 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_kernel(GemmParams P) {
         // surplus threads (a_on false) store the same bytes as the thread
         // they duplicated: harmless, and it keeps the stage branch-free
         const int row = a_row[i];
-        if constexpr (FMT == FMT_INT4) {
-          *(i32x4*)(sa + row * 128 + swz(row, a_ch[i]) * 16) = bf16x8_to_f16x8(R.a[i]);
-        } else {
-          *(i32x4*)(sa + row * 128 + swz(row, a_ch[i]) * 16) = R.a[i];
-        }
+        *(i32x4*)(sa + row * 128 + swz(row, a_ch[i]) * 16) = R.a[i];
       }
 #pragma unroll
       for (int i = 0; i < Gm::B_PT; ++i) {
         const int row = b_row[i];
-        if constexpr (FMT == FMT_INT4) {   // 32 nibbles -> chunks 4ch..4ch+3
-          _Float16 sh = (_Float16)bf16_bits_to_f32(R.sc);
-          f16x2 s2 = (f16x2){sh, sh};
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            *(i32x4*)(sb + row * 128 + swz(row, 4 * b_ch[i] + q) * 16) =
-                int4x8_to_f16x8((uint32_t)R.b[i][q], s2);
-        } else {
-          *(i32x4*)(sb + row * 128 + swz(row, b_ch[i]) * 16) = R.b[i];
-        }
+        *(i32x4*)(sb + row * 128 + swz(row, b_ch[i]) * 16) = R.b[i];
       }
     };
 
@@ -199,12 +167,8 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_kernel(GemmParams P) {
           for (int ms = 0; ms < MS; ++ms) {
             f32x4& d = acc[ms][ns];
             const f32x4 c = d;
-            if constexpr (FMT == FMT_INT4)
-              d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, af[ms]),
-                                                         __builtin_bit_cast(f16x8, bv), c, 0, 0, 0);
-            else
-              d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[ms]),
-                                                          __builtin_bit_cast(bf16x8, bv), c, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[ms]),
+                                                        __builtin_bit_cast(bf16x8, bv), c, 0, 0, 0);
           }
         }
       }
@@ -217,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_kernel(GemmParams P) {
     using P1 = std::integral_constant<int, 1>;
     using GY = std::true_type;    // guarded: skips stages past the end
     using GN = std::false_type;
-    Regs<FMT, BM> r0, r1, r2;
+    Regs<BM> r0, r1, r2;
     gload(r0, 0);
     gload(r1, 1);
     sstore(r0, 0, P0{}, GY{});
@@ -246,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_kernel(GemmParams P) {
       gload(r0, s + 6); compute(s + 4, P0{}, GY{}); sstore(r2, s + 5, P1{}, GY{}); __syncthreads();
     }
 
-    tile_epilogue<FMT, BM, G1>(P, tl, acc, smem);
+    tile_epilogue<BM, G1>(P, tl, acc, smem);
     __syncthreads();     // LDS is reused by the next tile
   }
 }
@@ -265,18 +229,18 @@ int num_cus() {
   return n;
 }
 
-template <int FMT, int BM, bool G1>
+template <int BM, bool G1>
 static hipError_t run(const GemmParams& P, long p_cap, int NT, hipStream_t s) {
-  constexpr int shm = Geo<FMT, BM>::TOTAL;
+  constexpr int shm = Geo<BM>::TOTAL;
   static int per_cu = 0;   // resident workgroups per CU, per instantiation
   if (per_cu == 0) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&moe_gemm_kernel<FMT, BM, G1>),
+        reinterpret_cast<const void*>(&moe_gemm_kernel<BM, G1>),
         hipFuncAttributeMaxDynamicSharedMemorySize, shm);
     if (e != hipSuccess) return e;
     int nb = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &nb, reinterpret_cast<const void*>(&moe_gemm_kernel<FMT, BM, G1>), kThreads, shm);
+        &nb, reinterpret_cast<const void*>(&moe_gemm_kernel<BM, G1>), kThreads, shm);
     if (e != hipSuccess) return e;
     per_cu = nb > 0 ? nb : 1;
   }
@@ -284,23 +248,17 @@ static hipError_t run(const GemmParams& P, long p_cap, int NT, hipStream_t s) {
   long nwg = std::min<long>(max_tiles, (long)num_cus() * per_cu);
   nwg = (nwg + 7) & ~7L;
   if (nwg == 0) return hipSuccess;
-  moe_gemm_kernel<FMT, BM, G1><<<dim3((unsigned)nwg), dim3(kThreads), shm, s>>>(P);
+  moe_gemm_kernel<BM, G1><<<dim3((unsigned)nwg), dim3(kThreads), shm, s>>>(P);
   return hipGetLastError();
 }
 
-template <int BM, bool G1>
-static hipError_t run_fmt(int fmt, const GemmParams& P, long p_cap, int NT, hipStream_t s) {
-  if (fmt == FMT_INT4) return run<FMT_INT4, BM, G1>(P, p_cap, NT, s);
-  return run<FMT_BF16, BM, G1>(P, p_cap, NT, s);
-}
-
+// BF16 layers: rows per expert on average decide the M tile
 template <bool G1>
-static hipError_t dispatch(int fmt, const GemmParams& P, long p_cap, int NT, long rows_hint,
+static hipError_t dispatch(const GemmParams& P, long p_cap, int NT, long rows_hint,
                            hipStream_t s) {
-  // rows per expert on average decides the M tile
-  if (rows_hint <= 32) return run_fmt<32, G1>(fmt, P, p_cap, NT, s);
-  if (rows_hint <= 64) return run_fmt<64, G1>(fmt, P, p_cap, NT, s);
-  return run_fmt<128, G1>(fmt, P, p_cap, NT, s);
+  if (rows_hint <= 32) return run<32, G1>(P, p_cap, NT, s);
+  if (rows_hint <= 64) return run<64, G1>(P, p_cap, NT, s);
+  return run<128, G1>(P, p_cap, NT, s);
 }
 
 hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t s) {
@@ -347,7 +305,7 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t s) {
     e = run(&grid);
     return e == hipSuccess ? launch_gemm1_sk_epilogue(P, grid, fp8, s) : e;
   }
-  return dispatch<true>(a.fmt, P, a.p_cap, a.I / 128, hint, s);
+  return dispatch<true>(P, a.p_cap, a.I / 128, hint, s);
 }
 
 hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t s) {
@@ -377,7 +335,7 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t s) {
     return fp8 ? launch_gemm_fp8(P, false, a.p_cap, NT, s, grid)
                : launch_gemm_int4(P, false, a.p_cap, NT, s, grid);
   }
-  return dispatch<false>(a.fmt, P, a.p_cap, NT, hint, s);
+  return dispatch<false>(P, a.p_cap, NT, hint, s);
 }
 
 bool splitk_use(int fmt, long p_cap, int G, int NT, int NS) {

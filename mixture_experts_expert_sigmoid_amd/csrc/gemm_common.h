@@ -1,6 +1,6 @@
-// Shared pieces of the grouped expert GEMM kernels: parameters, exact
-// format expansions, the device-side tile schedule and the BF16 / INT4
-// epilogue (the FP8 kernel has its own).
+// Shared pieces of the grouped expert GEMM kernels: parameters, the
+// device-side tile and split-K schedules, and the BF16 epilogue (the FP8 and
+// INT4 kernels have their own).
 //
 // Epilogue semantics: g' = min(g, L), u' = clamp(u, -L, L),
 // h = g' sigmoid(alpha g') (u' + beta) ("[Moe] Fix flashinfer_trtllm silently
@@ -26,36 +26,6 @@ constexpr int kMaxGroups = 1024;
 constexpr int KS = 64;               // K elements per pipeline stage
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
-
-// 8 bf16 -> 8 fp16 (exact for |v| in [2^-14, 65504])
-__device__ __forceinline__ i32x4 bf16x8_to_f16x8(i32x4 v) {
-  i32x4 o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t w = (uint32_t)v[i];
-    _Float16 lo = (_Float16)bf16_bits_to_f32(w & 0xFFFFu);
-    _Float16 hi = (_Float16)bf16_bits_to_f32(w >> 16);
-    o[i] = (int)((uint32_t)__builtin_bit_cast(uint16_t, lo) |
-                 ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16));
-  }
-  return o;
-}
-
-// 8 packed nibbles (k = 0..7, low nibble first) -> 8 fp16 (nibble - 8) * s
-__device__ __forceinline__ i32x4 int4x8_to_f16x8(uint32_t w, f16x2 sc2) {
-  uint32_t lo = w & 0x0F0F0F0Fu;          // even-k nibbles, byte i = pair i
-  uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // odd-k nibbles
-  i32x4 o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t pr = ((lo >> (8 * i)) & 0xFFu) | (((hi >> (8 * i)) & 0xFFu) << 16);
-    pr |= 0x64006400u;                    // (1024 + n_even, 1024 + n_odd)
-    f16x2 v = __builtin_bit_cast(f16x2, pr);
-    v = (v - (f16x2){(_Float16)1032.0f, (_Float16)1032.0f}) * sc2;
-    o[i] = (int)__builtin_bit_cast(uint32_t, v);
-  }
-  return o;
-}
 
 struct GemmParams {
   // A side
@@ -209,7 +179,7 @@ __device__ __forceinline__ long a_source_row(const GemmParams& P, int r) {
 // column (ns < 2 ? lo : hi) + wn*32 + (ns & 1)*16 + lane%16.
 // smem: at least max(BM*128*2, R*BM*4, BM*128 + 16*BM) bytes, free to reuse.
 // ---------------------------------------------------------------------------
-template <int FMT, int BM, bool G1>
+template <int BM, bool G1>
 __device__ __forceinline__ void tile_epilogue(const GemmParams& P, const Tile& t,
                                               f32x4 (&acc)[BM / 32][4], uint8_t* smem) {
   constexpr int MS = BM / 32;
