@@ -16,6 +16,12 @@ title and section):
                 "3. Performance" plus the epilogue commit message (iterative
                 masked-max top-k, raw logit carried, trailing SHARED_SINK
                 columns join the normaliser, global_scale).
+  gate       -- the router GEMM in front of that epilogue (the "258-column
+                gate GEMM" of the same PR, its fp32 [T, 258] gate row), an
+                optional selection bias [N] that shifts the ranking key to
+                sigmoid(x) + bias while the winner still carries its raw
+                logit, and the packed (id << 16 | bf16 weight) output: the
+                same PR, router-epilogue commit message.
   permute    -- expert-parallel rebase: routing ids are global, per-expert
                 tables are rank-local, rebase by local_expert_offset and
                 bounds-check: "FlashInfer 0.6.18 SM100a+SM103a MoE-LoRA AOT"
@@ -139,18 +145,41 @@ def topk_masked_max(keys, k):
     return ids
 
 
-def route(logits, n_routed, n_sink, top_k, route_scale=1.0, global_scale=1.0):
-    """Top-k over the n_routed columns of each fp32 logit row (ranked on the
-    raw logit: with no selection bias sigmoid is strictly increasing, so this
-    is the order of sigmoid(x)), then weights over the k winners and the
-    n_sink trailing sink columns:
-        lp = logsigmoid(x),  w = exp(lp - logsumexp(lp)) * route_scale * global_scale.
+def selection_keys(logits_routed, sel_bias):
+    """Ranking key under a selection bias, in the page's precision (fp32):
+    sigmoid of the fp32 logit rounded to fp32, plus the fp32 bias, the sum
+    rounded to fp32 (round to nearest even). Bias [N] covers the routed
+    columns only; sink columns never enter the ranking."""
+    x = np.asarray(logits_routed, dtype=np.float32).astype(np.float64)
+    s32 = sigmoid(x).astype(np.float32)
+    b32 = np.asarray(sel_bias, dtype=np.float32)
+    return (s32 + b32[None, :]).astype(np.float32)
+
+
+def _carry(raw, keys):
+    """The value a winner carries out of the top-k loop: its raw logit, not
+    its ranking key."""
+    return raw
+
+
+def route(logits, n_routed, n_sink, top_k, route_scale=1.0, global_scale=1.0,
+          sel_bias=None):
+    """Top-k over the n_routed columns of each fp32 logit row, then weights
+    over the k winners and the n_sink trailing sink columns:
+        lp = logsigmoid(x),  w = exp(lp - logsumexp(lp)) * route_scale * global_scale,
+    x the winners' RAW logits. Ranking key: with no selection bias the raw
+    logit (sigmoid is strictly increasing, so this is the order of
+    sigmoid(x)); with a bias [n_routed], selection_keys(). Equal keys go to
+    the lower column.
     Returns ids [T, k] (global column ids), w [T, k], sink_w [T, n_sink]."""
     lg = np.asarray(logits, dtype=np.float32)
     T = lg.shape[0]
-    keys = lg[:, :n_routed].astype(np.float64)
+    raw = lg[:, :n_routed].astype(np.float64)
+    keys = raw if sel_bias is None else \
+        selection_keys(lg[:, :n_routed], sel_bias).astype(np.float64)
     ids = topk_masked_max(keys, top_k)
-    chosen = np.take_along_axis(keys, ids, axis=1)          # raw logits
+    chosen = _carry(np.take_along_axis(raw, ids, axis=1),
+                    np.take_along_axis(keys, ids, axis=1))
     sinks = lg[:, n_routed:n_routed + n_sink].astype(np.float64)
     lp = logsigmoid(np.concatenate([chosen, sinks], axis=1))
     if T == 0:
@@ -160,6 +189,42 @@ def route(logits, n_routed, n_sink, top_k, route_scale=1.0, global_scale=1.0):
     scale = float(np.float32(route_scale)) * float(np.float32(global_scale))
     w = np.exp(lp - lse) * scale
     return ids, w[:, :top_k], w[:, top_k:]
+
+
+def gate_logits(x_bits, wg_bits):
+    """Router GEMM: logits[t, c] = sum_h x[t, h] * Wg[c, h] over bf16 x
+    [T, H] and bf16 Wg [N + S, H] (bit patterns). Each product of two bf16
+    values is exact in float64 and the float64 sum keeps ~1e-16 relative
+    error, so this is the exact dot product for all practical purposes."""
+    x = bf16_decode(x_bits)
+    w = bf16_decode(wg_bits)
+    return x @ w.T
+
+
+def gate_route(x_bits, wg_bits, n_routed, n_sink, top_k, route_scale=1.0,
+               global_scale=1.0, sel_bias=None):
+    """The gate row is the fp32 [T, N + S] matrix of logits (each the exact
+    dot product rounded once to fp32); the epilogue is route() on it.
+    Returns (logits fp32, ids, w, sink_w)."""
+    lg = gate_logits(x_bits, wg_bits).astype(np.float32)
+    ids, w, sw = route(lg, n_routed, n_sink, top_k, route_scale, global_scale,
+                       sel_bias)
+    return lg, ids, w, sw
+
+
+def bf16_bits(v) -> np.ndarray:
+    """Bit pattern (uint16) of the nearest bfloat16 (ties to even) of v."""
+    q = bf16_round(v).astype(np.float32)
+    return (q.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def pack_topk(ids, w) -> np.ndarray:
+    """Packed routing output: (id << 16) | bf16 bits of the routed weight,
+    one int32 per slot; a consumer recovers the id as p >> 16 and the weight
+    from p & 0xFFFF."""
+    ids = np.asarray(ids, dtype=np.int64)
+    p = (ids << 16) | bf16_bits(w).astype(np.int64)
+    return p.astype(np.uint32).view(np.int32)
 
 
 # ----------------------------------------------------------------------------

@@ -247,6 +247,28 @@ def make_batch(spec: LayerSpec, layer: Optional[Layer], T: int,
     return Batch(T, x.contiguous(), lg.float().contiguous())
 
 
+@dataclasses.dataclass
+class Gate:
+    wg: torch.Tensor      # [n_routed + n_sink, H] bf16 router weight
+    bias: torch.Tensor    # [n_routed] f32 selection bias
+
+
+def make_gate(spec: LayerSpec, device="cpu", logit_std: float = 1.0,
+              bias_amp: float = 0.02) -> Gate:
+    """Router weight and selection bias for the gate GEMM. The pages fix the
+    shape ([T, N + S] gate rows from an [N + S, H] weight) but no values:
+    Wg ~ N(0, (logit_std / sqrt(H))^2) in bf16 gives N(0, logit_std^2)
+    logits for N(0, 1) activations; the bias is U(-bias_amp, bias_amp), the
+    size of the gaps between the top sigmoid values at logit_std 1, so it
+    changes some selections and not others."""
+    g = _gen(device, spec.cfg_id, 7005)
+    N, S, H = spec.n_routed, spec.n_sink, spec.H
+    wg = (torch.randn(N + S, H, generator=g, device=device)
+          * (logit_std / math.sqrt(H))).to(torch.bfloat16)
+    bias = (torch.rand(N, generator=g, device=device) * 2.0 - 1.0) * bias_amp
+    return Gate(wg.contiguous(), bias.float().contiguous())
+
+
 def to_numpy_layer(layer: Layer, experts=None) -> dict:
     """Host copies of the stored arrays, as raw codes: bf16 -> uint16 bits,
     e4m3fn -> uint8 codes. `experts` limits the copy to some groups."""
