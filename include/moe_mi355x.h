@@ -110,18 +110,52 @@ typedef struct {
  * commit message]. Per token row t of `logits` (fp32, row stride `ld`
  * elements, ld >= n_routed + n_sink):
  *   - top_k passes of masked argmax over the n_routed leading columns,
- *     ranked on the raw logit (no selection bias: sigmoid is monotone),
- *     equal logits resolved to the lower column index;
- *   - lp = logsigmoid of the k winners' raw logits and of the n_sink
- *     trailing sink columns; w = exp(lp - logsumexp(lp)) * route_scale *
- *     global_scale (finite when every logit is far below -104).
+ *     ranked on the raw logit when sel_bias is NULL (sigmoid is monotone),
+ *     else on the fp32 key sigmoid(x) + sel_bias[c] (sel_bias fp32
+ *     [n_routed]; the sink columns take no bias and never rank); equal keys
+ *     resolve to the lower column index;
+ *   - the winners carry their RAW logits: lp = logsigmoid of the k winners'
+ *     raw logits and of the n_sink trailing sink columns; w = exp(lp -
+ *     logsumexp(lp)) * route_scale * global_scale (finite when every logit
+ *     is far below -104).
  * Outputs: topk_ids int32 [T][top_k] (global column ids, selection order),
- * topk_w fp32 [T][top_k], sink_w fp32 [T][n_sink] (NULL iff n_sink == 0).
+ * topk_w fp32 [T][top_k], sink_w fp32 [T][n_sink] (NULL iff n_sink == 0),
+ * packed int32 [T][top_k] or NULL: (id << 16) | bf16 bits of topk_w
+ * (round to nearest even); a consumer takes the id as p >> 16 and the
+ * weight from p & 0xFFFF.
  * Limits: 1 <= top_k <= n_routed, top_k + n_sink <= 64,
  * n_routed + n_sink <= 1024, T >= 0. Logits are assumed finite. */
 int moe_route(const float *logits, long T, long ld, int n_routed, int n_sink,
-              int top_k, float route_scale, float global_scale,
-              int *topk_ids, float *topk_w, float *sink_w, void *stream);
+              int top_k, const float *sel_bias, float route_scale,
+              float global_scale, int *topk_ids, float *topk_w, float *sink_w,
+              int *packed, void *stream);
+
+/* ----------------------------------------------------------- gate route -- */
+/* The router GEMM fused with the epilogue of moe_route [GATE-PR: the
+ * "258-column gate GEMM" whose fp32 [T, N + S] rows feed the epilogue;
+ * router-epilogue commit message]. logits[t][c] = sum_h x[t][h] * wg[c][h]
+ * for c < n_routed + n_sink, bf16 operands, fp32 accumulation (in an order
+ * of the kernel's choosing), then exactly the moe_route epilogue on those
+ * rows (selection bias, raw-logit carry, sinks, scales, packed output).
+ *   x_bf16   bf16 [T][H], row-major, 16-byte aligned;
+ *   wg_bf16  bf16 [n_routed + n_sink][H] (routed rows first, then the sink
+ *            rows), 16-byte aligned;
+ *   logits   fp32 [T][n_routed + n_sink] or NULL (the gate rows, if the
+ *            caller wants them);
+ *   topk_ids, topk_w, sink_w, packed, sel_bias as for moe_route;
+ *   ws       device workspace of moe_gate_route_workspace_size(T, H,
+ *            n_routed, n_sink) bytes (0 when T is large enough for the
+ *            single fused launch; NULL allowed then).
+ * Limits: H a multiple of 32, 1 <= top_k <= n_routed, top_k + n_sink <= 16,
+ * n_routed + n_sink <= 512, T >= 0 (T = 0 is a no-op). Errors: SHAPE for
+ * the limits, NULL for a missing required pointer, PARAM for non-finite
+ * scales or misaligned x / wg, WORKSPACE for a missing or short ws. */
+size_t moe_gate_route_workspace_size(long T, int H, int n_routed, int n_sink);
+int moe_gate_route(const void *x_bf16, const void *wg_bf16, long T, int H,
+                   int n_routed, int n_sink, int top_k, const float *sel_bias,
+                   float route_scale, float global_scale, float *logits,
+                   int *topk_ids, float *topk_w, float *sink_w, int *packed,
+                   void *ws, size_t ws_bytes, void *stream);
 
 /* -------------------------------------------------------------- permute -- */
 /* Expert-parallel rebase and grouping of (token, slot) pairs by local expert

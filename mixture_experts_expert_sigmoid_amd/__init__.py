@@ -61,8 +61,14 @@ class MoeLayer(ctypes.Structure):
 _lib = None
 
 _SIGS = {
-    "moe_route": (c_int, [c_void_p, c_long, c_long, c_int, c_int, c_int, c_float,
-                          c_float, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "moe_route": (c_int, [c_void_p, c_long, c_long, c_int, c_int, c_int, c_void_p,
+                          c_float, c_float, c_void_p, c_void_p, c_void_p, c_void_p,
+                          c_void_p]),
+    "moe_gate_route_workspace_size": (c_size_t, [c_long, c_int, c_int, c_int]),
+    "moe_gate_route": (c_int, [c_void_p, c_void_p, c_long, c_int, c_int, c_int, c_int,
+                               c_void_p, c_float, c_float, c_void_p, c_void_p,
+                               c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                               c_void_p]),
     "moe_permute": (c_int, [c_void_p, c_long, c_int, c_int, c_int, c_int, c_int,
                             c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                             c_size_t, c_void_p]),
@@ -166,11 +172,29 @@ def layer_desc(H, I, num_experts_global, num_local_experts, local_expert_offset,
 # ------------------------------------------------------------ entry points
 
 def moe_route(logits, n_routed, n_sink, top_k, route_scale, global_scale,
-              topk_ids, topk_w, sink_w=None, stream=None):
+              topk_ids, topk_w, sink_w=None, stream=None, sel_bias=None,
+              packed=None):
     T, ld = logits.shape
     _check(lib().moe_route(_p(logits), T, logits.stride(0), n_routed, n_sink,
-                           top_k, route_scale, global_scale, _p(topk_ids),
-                           _p(topk_w), _p(sink_w), _stream(stream)), "moe_route")
+                           top_k, _p(sel_bias), route_scale, global_scale,
+                           _p(topk_ids), _p(topk_w), _p(sink_w), _p(packed),
+                           _stream(stream)), "moe_route")
+
+
+def moe_gate_route_workspace_size(T, H, n_routed, n_sink) -> int:
+    return lib().moe_gate_route_workspace_size(T, H, n_routed, n_sink)
+
+
+def moe_gate_route(x_bf16, wg_bf16, n_routed, n_sink, top_k, route_scale,
+                   global_scale, topk_ids, topk_w, sink_w=None, sel_bias=None,
+                   logits=None, packed=None, ws=None, stream=None):
+    T, H = x_bf16.shape
+    _check(lib().moe_gate_route(_p(x_bf16), _p(wg_bf16), T, H, n_routed, n_sink,
+                                top_k, _p(sel_bias), route_scale, global_scale,
+                                _p(logits), _p(topk_ids), _p(topk_w), _p(sink_w),
+                                _p(packed), _p(ws),
+                                0 if ws is None else ws.numel() * ws.element_size(),
+                                _stream(stream)), "moe_gate_route")
 
 
 def moe_permute_workspace_size(T, top_k, n_groups) -> int:

@@ -5,6 +5,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <stdint.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -76,8 +77,9 @@ const char* moe_status_string(int s) {
 const char* moe_last_error(void) { return g_last_error; }
 
 int moe_route(const float* logits, long T, long ld, int n_routed, int n_sink,
-              int top_k, float route_scale, float global_scale, int* topk_ids,
-              float* topk_w, float* sink_w, void* stream) {
+              int top_k, const float* sel_bias, float route_scale,
+              float global_scale, int* topk_ids, float* topk_w, float* sink_w,
+              int* packed, void* stream) {
   if (T < 0 || n_routed < 1 || n_sink < 0 || top_k < 1 || top_k > n_routed ||
       top_k + n_sink > 64 || n_routed + n_sink > 1024 || ld < n_routed + n_sink)
     return MOE_ERR_SHAPE;
@@ -85,9 +87,57 @@ int moe_route(const float* logits, long T, long ld, int n_routed, int n_sink,
   if (T > 0 && (!logits || !topk_ids || !topk_w || (n_sink > 0 && !sink_w)))
     return MOE_ERR_NULL;
   hipError_t e = moe::launch_route(logits, T, ld, n_routed, n_sink, top_k,
-                                   route_scale * global_scale, topk_ids,
-                                   topk_w, sink_w, (hipStream_t)stream);
+                                   sel_bias, route_scale * global_scale,
+                                   topk_ids, topk_w, sink_w, packed,
+                                   (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_route");
+}
+
+static int gate_checks(long T, int H, int n_routed, int n_sink, int top_k) {
+  if (T < 0 || H < 32 || H % 32 != 0 || n_routed < 1 || n_sink < 0 ||
+      top_k < 1 || top_k > n_routed || top_k + n_sink > 16 ||
+      n_routed + n_sink > 512)
+    return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+size_t moe_gate_route_workspace_size(long T, int H, int n_routed, int n_sink) {
+  if (gate_checks(T, H, n_routed, n_sink, 1) != MOE_OK) return 0;
+  return moe::gate_ws_bytes(T, H, n_routed + n_sink);
+}
+
+int moe_gate_route(const void* x_bf16, const void* wg_bf16, long T, int H,
+                   int n_routed, int n_sink, int top_k, const float* sel_bias,
+                   float route_scale, float global_scale, float* logits,
+                   int* topk_ids, float* topk_w, float* sink_w, int* packed,
+                   void* ws, size_t ws_bytes, void* stream) {
+  int st = gate_checks(T, H, n_routed, n_sink, top_k);
+  if (st) return st;
+  if (!finite(route_scale) || !finite(global_scale)) return MOE_ERR_PARAM;
+  if (T > 0 && (!x_bf16 || !wg_bf16 || !topk_ids || !topk_w ||
+                (n_sink > 0 && !sink_w)))
+    return MOE_ERR_NULL;
+  if ((((uintptr_t)x_bf16) | ((uintptr_t)wg_bf16)) & 15) return MOE_ERR_PARAM;
+  const size_t need = moe::gate_ws_bytes(T, H, n_routed + n_sink);
+  if (need > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  moe::GateArgs a{};
+  a.x = x_bf16;
+  a.wg = wg_bf16;
+  a.T = T;
+  a.H = H;
+  a.n_routed = n_routed;
+  a.n_sink = n_sink;
+  a.k = top_k;
+  a.bias = sel_bias;
+  a.scale = route_scale * global_scale;
+  a.logits = logits;
+  a.ids = topk_ids;
+  a.w = topk_w;
+  a.sw = sink_w;
+  a.packed = packed;
+  a.ws = ws;
+  hipError_t e = moe::launch_gate(a, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_gate_route");
 }
 
 size_t moe_permute_workspace_size(long T, int top_k, int n_groups) {
@@ -396,9 +446,9 @@ int moe_forward(const moe_layer* L, const void* x_bf16, const float* logits,
   float* y = (float*)(base + o.y);
 
   hipError_t e = moe::launch_route(logits, T, ld_logits, L->num_experts_global,
-                                   L->n_sink, L->top_k,
+                                   L->n_sink, L->top_k, nullptr,
                                    L->route_scale * L->global_scale, topk_ids,
-                                   topk_w, sink_w, s);
+                                   topk_w, sink_w, nullptr, s);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/route");
   e = moe::launch_permute(topk_ids, T, L->top_k, L->num_experts_global,
                           L->local_expert_offset, L->num_local_experts,

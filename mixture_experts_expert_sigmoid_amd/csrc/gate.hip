@@ -1,0 +1,356 @@
+// Router GEMM fused with the sigmoid-gate epilogue, with an optional
+// selection bias and the packed (id << 16 | bf16 weight) output.
+//
+// "Enable and fuse the Inkling MoE gate epilogue on Intel XPU" (sglang PR
+// #36385): the 258-column gate GEMM that feeds the epilogue, ranking by
+// iterative masked-max passes ("3. Performance"), weights as
+// exp(lp - logsumexp(lp)) with lp = logsigmoid(x) ("2. Correctness"); the
+// router-epilogue commit message: the ranking key is sigmoid(logits) + bias
+// with the bias covering the routed columns only, the winner carries its
+// RAW logit out of the top-k loop, sink columns join only the normaliser,
+// the global scale multiplies the weights, and the packed form is read back
+// with & 0xFFFF.
+//
+// GEMM: logits[t][c] = sum_h x[t][h] Wg[c][h] with bf16 operands on
+// v_mfma_f32_16x16x32_bf16 and fp32 accumulation. A workgroup of 4 waves
+// owns 32 tokens (two 16-token subtiles) and every logit column; wave w owns
+// the 16-column subtiles w, w + 4, w + 8, ... of both token subtiles, so each
+// router-weight element is read by exactly one wave, straight from memory
+// into registers as the MFMA's first operand (a lane's four accumulators are
+// then four consecutive columns of one token), while the 32 token rows are
+// shared by the four waves through the L1 cache. Two K steps of 32 are in
+// flight. With enough tokens for the whole GPU (one launch) the workgroup
+// puts its 32 x C logits in LDS and runs the epilogue itself; with few
+// tokens the K range is split over workgroups that write fp32 partial sums,
+// and a second kernel adds them in split order and runs the same epilogue.
+//
+// Epilogue: one 16-lane group per token row (one DPP row: max, min and sum
+// over the group take four steps). Lane l of a group holds columns l,
+// l + 16, ...; each of the k passes takes the group maximum of the lanes'
+// best untaken keys, then the lowest column holding it, so equal keys go to
+// the lower column; the owner lane marks it taken and publishes the raw
+// logit. Then lane j < k holds slot j, lanes k .. k + S - 1 the sinks, and
+// the renormalisation is a group max and a group sum.
+#include <algorithm>
+
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+namespace {
+
+constexpr int kGBM = 32;          // tokens per GEMM workgroup
+constexpr int kGRows = 16;        // rows per epilogue workgroup (16-lane groups)
+constexpr int kGThreads = 256;    // 4 waves
+
+struct GateP {
+  const uint8_t* x;     // bf16 [T][H]
+  const uint8_t* wg;    // bf16 [NC][H]
+  long T;
+  int H, NC, n_routed, n_sink, k;
+  int NS;               // 16-column subtiles, ceil(NC / 16)
+  int steps;            // K steps of 32 per split
+  int S;                // splits
+  const float* bias;    // [n_routed] or NULL
+  float scale;
+  float* part;          // [S][T][16 NS] partial logits (S > 1)
+  float* logits;        // [T][NC] or NULL
+  int* ids;
+  float* w;
+  float* sw;
+  int* packed;          // [T][k] or NULL
+};
+
+struct OpOrU { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a | b; } };
+
+// ---------------------------------------------------------------- GEMM --
+// acc[j][ts] holds columns 16 (4 j + wave) + 4 (lane / 16) + r, r = 0..3, of
+// token t0 + 16 ts + lane % 16 over the split's K range.
+template <int NQ>
+__device__ __forceinline__ void gate_gemm(const GateP& P, f32x4 (&acc)[NQ][2],
+                                          long t0, int split) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const long rowb = (long)P.H * 2;
+  const int st0 = split * P.steps;
+  const int nst = min(P.steps, P.H / 32 - st0);
+  const long kb = ((long)st0 * 32 + 8 * lg) * 2;
+  const uint8_t* xa[2];
+#pragma unroll
+  for (int ts = 0; ts < 2; ++ts) {
+    const long row = min(t0 + 16 * ts + lr, P.T - 1);   // rows past T: discarded
+    xa[ts] = P.x + row * rowb + kb;
+  }
+  const uint8_t* wa[NQ];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const int col = min(16 * (4 * j + wave) + lr, P.NC - 1);   // padding: discarded
+    wa[j] = P.wg + (long)col * rowb + kb;
+  }
+#pragma unroll
+  for (int j = 0; j < NQ; ++j)
+#pragma unroll
+    for (int ts = 0; ts < 2; ++ts) acc[j][ts] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  struct Fr { i32x4 a[NQ]; i32x4 b[2]; };
+  // loads are unconditional (past the end they re-read the last step) so the
+  // wait counts stay static with two steps in flight
+  auto load = [&](Fr& f, int st) {
+    const long off = (long)min(st, nst - 1) * 64;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) f.a[j] = *(const i32x4*)(wa[j] + off);
+#pragma unroll
+    for (int ts = 0; ts < 2; ++ts) f.b[ts] = *(const i32x4*)(xa[ts] + off);
+  };
+  auto mma = [&](const Fr& f, int st) {
+    if (st >= nst) return;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      if (4 * j + wave >= P.NS) continue;           // wave-uniform
+#pragma unroll
+      for (int ts = 0; ts < 2; ++ts)
+        acc[j][ts] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, f.a[j]), __builtin_bit_cast(bf16x8, f.b[ts]),
+            acc[j][ts], 0, 0, 0);
+    }
+  };
+  Fr f0, f1, f2;
+  load(f0, 0);
+  load(f1, 1);
+  for (int st = 0; st < nst; st += 3) {
+    load(f2, st + 2); mma(f0, st);
+    load(f0, st + 3); mma(f1, st + 1);
+    load(f1, st + 4); mma(f2, st + 2);
+  }
+}
+
+// ------------------------------------------------------------ epilogue --
+__device__ __forceinline__ float sigmoid_f32(float x) {
+  return 1.0f / (1.0f + expf(-x));
+}
+
+// One token row per 16-lane group. L points at the row's fp32 logits in LDS
+// (columns 0 .. NC - 1 valid). NV >= ceil(n_routed / 16).
+template <int NV>
+__device__ __forceinline__ void route_row16(const GateP& P, const float* L, long row,
+                                            bool row_ok) {
+  const int lr = threadIdx.x & 15;
+  const int nvr = (P.n_routed + 15) >> 4;
+  float raw[NV], key[NV];
+  uint32_t taken = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lr + 16 * i;
+    raw[i] = (i < nvr) ? L[min(c, P.NC - 1)] : 0.0f;
+    if (c >= P.n_routed) taken |= 1u << i;          // not a candidate
+    key[i] = P.bias ? sigmoid_f32(raw[i]) + P.bias[min(c, P.n_routed - 1)] : raw[i];
+  }
+  float my_x = 0.0f;
+  int my_c = 0;
+  for (int j = 0; j < P.k; ++j) {
+    float bv = -INFINITY, braw = 0.0f;
+    int bi = NV;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const bool cand = !((taken >> i) & 1u);
+      if (cand && (bi == NV || key[i] > bv)) { bv = key[i]; braw = raw[i]; bi = i; }
+    }
+    const float m = row16_reduce(bv, OpMax{});
+    const int bc = (bi < NV && bv == m) ? lr + 16 * bi : 0x7FFFFFFF;
+    const int wc = row16_reduce(bc, OpMinI{});
+    const bool own = (wc & 15) == lr && bi < NV && lr + 16 * bi == wc;
+    if (own) taken |= 1u << bi;
+    const uint32_t xr = row16_reduce(own ? __float_as_uint(braw) : 0u, OpOrU{});
+    if (lr == j) { my_x = __uint_as_float(xr); my_c = wc; }
+  }
+  const bool active = lr < P.k + P.n_sink;
+  if (lr >= P.k && active) my_x = L[P.n_routed + (lr - P.k)];
+  float lp = active ? fminf(my_x, 0.0f) - log1pf(expf(-fabsf(my_x))) : -INFINITY;
+  const float m = row16_reduce(lp, OpMax{});
+  const float e = active ? expf(lp - m) : 0.0f;
+  const float wt = e / row16_reduce(e, OpSum{}) * P.scale;
+  if (!row_ok) return;
+  if (lr < P.k) {
+    P.ids[row * P.k + lr] = my_c;
+    P.w[row * P.k + lr] = wt;
+    if (P.packed) P.packed[row * P.k + lr] = (int)(((uint32_t)my_c << 16) | f32_to_bf16_bits(wt));
+  } else if (active) {
+    P.sw[row * P.n_sink + (lr - P.k)] = wt;
+  }
+}
+
+// ------------------------------------------------------------- kernels --
+// S == 1: GEMM over the whole K, logits to LDS, epilogue for the 32 rows.
+template <int NQ>
+__global__ __launch_bounds__(kGThreads) void gate_fused_kernel(GateP P) {
+  extern __shared__ __attribute__((aligned(16))) float sl[];
+  const int LP = 16 * P.NS + 4;                    // row pitch (floats)
+  const long t0 = (long)blockIdx.x * kGBM;
+  f32x4 acc[NQ][2];
+  gate_gemm<NQ>(P, acc, t0, 0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    if (4 * j + wave >= P.NS) continue;
+#pragma unroll
+    for (int ts = 0; ts < 2; ++ts)
+      *(f32x4*)(sl + (16 * ts + lr) * LP + 16 * (4 * j + wave) + 4 * lg) = acc[j][ts];
+  }
+  __syncthreads();
+  if (P.logits) {
+    const int rows = (int)min((long)kGBM, P.T - t0);
+    for (int i = threadIdx.x; i < rows * P.NC; i += kGThreads) {
+      const int r = i / P.NC, c = i - r * P.NC;
+      P.logits[(t0 + r) * P.NC + c] = sl[r * LP + c];
+    }
+  }
+  const int grp = threadIdx.x >> 4;                // 0..15
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int r = 16 * half + grp;
+    route_row16<4 * NQ>(P, sl + r * LP, t0 + r, t0 + r < P.T);
+  }
+}
+
+// S > 1: partial sums of one K range.
+template <int NQ>
+__global__ __launch_bounds__(kGThreads) void gate_part_kernel(GateP P) {
+  const long t0 = (long)blockIdx.x * kGBM;
+  const int split = blockIdx.y;
+  f32x4 acc[NQ][2];
+  gate_gemm<NQ>(P, acc, t0, split);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int NCP = 16 * P.NS;
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    if (4 * j + wave >= P.NS) continue;
+#pragma unroll
+    for (int ts = 0; ts < 2; ++ts) {
+      const long row = t0 + 16 * ts + lr;
+      if (row < P.T)
+        *(f32x4*)(P.part + ((long)split * P.T + row) * NCP + 16 * (4 * j + wave) + 4 * lg) =
+            acc[j][ts];
+    }
+  }
+}
+
+// S > 1: add the partial sums in split order for 16 rows, then the epilogue.
+template <int NQ>
+__global__ __launch_bounds__(kGThreads) void gate_reduce_route_kernel(GateP P) {
+  extern __shared__ __attribute__((aligned(16))) float sl[];
+  const int NCP = 16 * P.NS, LP = NCP + 4, n4 = NCP / 4;
+  const long t0 = (long)blockIdx.x * kGRows;
+  const int rows = (int)min((long)kGRows, P.T - t0);
+  const long slot = P.T * (long)NCP;
+  for (int i = threadIdx.x; i < rows * n4; i += kGThreads) {
+    const int r = i / n4, c = 4 * (i - r * n4);
+    const float* src = P.part + (t0 + r) * NCP + c;
+    f32x4 v = *(const f32x4*)src;
+    int s = 1;
+    for (; s + 4 <= P.S; s += 4) {                 // four loads in flight
+      const f32x4 a = *(const f32x4*)(src + s * slot);
+      const f32x4 b = *(const f32x4*)(src + (s + 1) * slot);
+      const f32x4 d = *(const f32x4*)(src + (s + 2) * slot);
+      const f32x4 e = *(const f32x4*)(src + (s + 3) * slot);
+      v += a; v += b; v += d; v += e;
+    }
+    for (; s < P.S; ++s) v += *(const f32x4*)(src + s * slot);
+    *(f32x4*)(sl + r * LP + c) = v;
+    if (P.logits) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (c + q < P.NC) P.logits[(t0 + r) * P.NC + c + q] = v[q];
+    }
+  }
+  __syncthreads();
+  const int grp = threadIdx.x >> 4;
+  route_row16<4 * NQ>(P, sl + grp * LP, t0 + grp, grp < rows);
+}
+
+int splits_for(long T, int H) {
+  const long tiles = (T + kGBM - 1) / kGBM;
+  const int steps = H / 32;
+  if (tiles >= kGateFusedTiles) return 1;
+  long S = (kGateSplitTarget + tiles - 1) / tiles;
+  S = std::max<long>(2, std::min<long>(S, std::min(32, steps)));
+  const long ps = (steps + S - 1) / S;
+  return (int)((steps + ps - 1) / ps);
+}
+
+template <int NQ>
+hipError_t run_gate(GateP& P, hipStream_t s) {
+  const unsigned tiles = (unsigned)((P.T + kGBM - 1) / kGBM);
+  const int LP = 16 * P.NS + 4;
+  if (P.S == 1) {
+    const size_t shm = (size_t)kGBM * LP * 4;   // <= 32 * 516 * 4 bytes
+    static bool attr = false;
+    if (!attr) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gate_fused_kernel<NQ>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         kGBM * (16 * 4 * NQ + 4) * 4);
+      if (e != hipSuccess) return e;
+      attr = true;
+    }
+    hipLaunchKernelGGL(gate_fused_kernel<NQ>, dim3(tiles), dim3(kGThreads), shm, s, P);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(gate_part_kernel<NQ>, dim3(tiles, (unsigned)P.S), dim3(kGThreads), 0,
+                     s, P);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned rb = (unsigned)((P.T + kGRows - 1) / kGRows);
+  const size_t shm = (size_t)kGRows * LP * 4;
+  hipLaunchKernelGGL(gate_reduce_route_kernel<NQ>, dim3(rb), dim3(kGThreads), shm, s, P);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int gate_splits(long T, int H) { return T > 0 ? splits_for(T, H) : 1; }
+
+size_t gate_ws_bytes(long T, int H, int n_cols) {
+  if (T <= 0) return 0;
+  const int S = splits_for(T, H);
+  if (S == 1) return 0;
+  const long NCP = 16L * ((n_cols + 15) / 16);
+  return ((size_t)S * T * NCP * 4 + 255) & ~(size_t)255;
+}
+
+hipError_t launch_gate(const GateArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  GateP P{};
+  P.x = (const uint8_t*)a.x;
+  P.wg = (const uint8_t*)a.wg;
+  P.T = a.T;
+  P.H = a.H;
+  P.n_routed = a.n_routed;
+  P.n_sink = a.n_sink;
+  P.NC = a.n_routed + a.n_sink;
+  P.k = a.k;
+  P.NS = (P.NC + 15) / 16;
+  P.S = splits_for(a.T, a.H);
+  P.steps = (a.H / 32 + P.S - 1) / P.S;
+  P.bias = a.bias;
+  P.scale = a.scale;
+  P.part = (float*)a.ws;
+  P.logits = a.logits;
+  P.ids = a.ids;
+  P.w = a.w;
+  P.sw = a.sw;
+  P.packed = a.packed;
+  switch ((P.NS + 3) / 4) {
+    case 1: return run_gate<1>(P, s);
+    case 2: return run_gate<2>(P, s);
+    case 3: return run_gate<3>(P, s);
+    case 4: return run_gate<4>(P, s);
+    case 5: return run_gate<5>(P, s);
+    case 6: return run_gate<6>(P, s);
+    case 7: return run_gate<7>(P, s);
+    case 8: return run_gate<8>(P, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace moe

@@ -7,9 +7,37 @@
 
 namespace moe {
 
+// bias: NULL (rank on the raw logit) or [n_routed] (rank on fp32
+// sigmoid(x) + bias); packed: NULL or [T][k] (id << 16 | bf16 weight)
 hipError_t launch_route(const float* logits, long T, long ld, int n_routed,
-                        int n_sink, int k, float scale, int* ids, float* w,
-                        float* sw, hipStream_t s);
+                        int n_sink, int k, const float* bias, float scale,
+                        int* ids, float* w, float* sw, int* packed,
+                        hipStream_t s);
+
+// Router GEMM fused with the gate epilogue. With at least kGateFusedTiles
+// tiles of 32 tokens the GEMM and the epilogue run in one launch; below,
+// the K range is split over about kGateSplitTarget / tiles workgroups per
+// tile and the partial sums (workspace, gate_ws_bytes) are added by the
+// epilogue kernel in split order.
+constexpr long kGateFusedTiles = 96;
+constexpr long kGateSplitTarget = 128;
+struct GateArgs {
+  const void* x;         // bf16 [T][H]
+  const void* wg;        // bf16 [n_routed + n_sink][H]
+  long T;
+  int H, n_routed, n_sink, k;
+  const float* bias;     // [n_routed] or NULL
+  float scale;           // route_scale * global_scale
+  float* logits;         // [T][n_routed + n_sink] or NULL
+  int* ids;
+  float* w;
+  float* sw;
+  int* packed;           // [T][k] or NULL
+  void* ws;              // gate_ws_bytes(T, H, n_routed + n_sink) bytes
+};
+int gate_splits(long T, int H);
+size_t gate_ws_bytes(long T, int H, int n_cols);
+hipError_t launch_gate(const GateArgs& a, hipStream_t s);
 
 // permute: rank/count, scan, scatter (three launches)
 constexpr int kPermBlock = 1024;

@@ -228,6 +228,12 @@ def _logits_mix258(spec: LayerSpec, T: int, g, device) -> torch.Tensor:
     return out.float().contiguous()
 
 
+def make_tokens(spec: LayerSpec, T: int, device="cpu", seed_extra: int = 0) -> torch.Tensor:
+    """The activations x [T, H] bf16 of make_batch alone (same draw)."""
+    g = _gen(device, spec.cfg_id, T, 11 + seed_extra)
+    return torch.randn(T, spec.H, generator=g, device=device).to(torch.bfloat16).contiguous()
+
+
 def make_batch(spec: LayerSpec, layer: Optional[Layer], T: int,
                device="cpu", seed_extra: int = 0) -> Batch:
     g = _gen(device, spec.cfg_id, T, 11 + seed_extra)

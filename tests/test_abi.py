@@ -43,15 +43,44 @@ def _w(fmt=M.MOE_W_FP8_B128, G=4, N=256, K=256, q=1, s=1):
 
 def test_route_validation():
     L = M.lib()
-    f = lambda *a: L.moe_route(*a)
+    # (logits, T, ld, n_routed, n_sink, top_k, sel_bias, scales, ids, w, sw, packed)
+    f = lambda lg, T, ld, N, S, k, rs=1.0, sw=None: L.moe_route(
+        lg, T, ld, N, S, k, None, rs, 1.0, 1, 1, sw, None, None)
     # top_k > n_routed, top_k + n_sink > 64, ld too small, T < 0
-    assert f(1, 4, 8, 8, 0, 9, 1.0, 1.0, 1, 1, None, None) == -2
-    assert f(1, 4, 100, 60, 8, 60, 1.0, 1.0, 1, 1, 1, None) == -2
-    assert f(1, 4, 7, 8, 0, 2, 1.0, 1.0, 1, 1, None, None) == -2
-    assert f(1, -1, 8, 8, 0, 2, 1.0, 1.0, 1, 1, None, None) == -2
-    assert f(1, 4, 8, 8, 0, 2, math.nan, 1.0, 1, 1, None, None) == -5
-    assert f(None, 4, 8, 8, 0, 2, 1.0, 1.0, 1, 1, None, None) == -1
-    assert f(1, 4, 10, 8, 2, 2, 1.0, 1.0, 1, 1, None, None) == -1   # sinks need sink_w
+    assert f(1, 4, 8, 8, 0, 9) == -2
+    assert f(1, 4, 100, 60, 8, 60, sw=1) == -2
+    assert f(1, 4, 7, 8, 0, 2) == -2
+    assert f(1, -1, 8, 8, 0, 2) == -2
+    assert f(1, 4, 8, 8, 0, 2, rs=math.nan) == -5
+    assert f(None, 4, 8, 8, 0, 2) == -1
+    assert f(1, 4, 10, 8, 2, 2) == -1   # sinks need sink_w
+
+
+def test_gate_route_validation():
+    L = M.lib()
+    ws = ctypes.c_void_p(256)
+
+    def f(x=256, wg=256, T=4, H=2048, N=256, S=2, k=8, rs=1.0, sw=1, ws_=ws,
+          nb=1 << 30):
+        return L.moe_gate_route(x, wg, T, H, N, S, k, None, rs, 1.0, None, 1, 1,
+                                sw, None, ws_, nb, None)
+    assert f(H=2040) == -2                  # H % 32
+    assert f(H=0) == -2
+    assert f(k=9, S=8) == -2                # top_k + n_sink > 16
+    assert f(N=500, S=13) == -2             # more than 512 columns
+    assert f(k=300) == -2                   # top_k > n_routed
+    assert f(T=-1) == -2
+    assert f(rs=math.inf) == -5
+    assert f(x=None) == -1
+    assert f(sw=None) == -1                 # sinks need sink_w
+    assert f(x=264) == -5                   # not 16-byte aligned
+    assert f(ws_=None) == -6                # split path needs the workspace
+    assert f(nb=16) == -6
+    # T = 0 is a no-op; large T needs no workspace (one fused launch)
+    assert f(T=0, x=None, wg=None, ws_=None, nb=0) == 0
+    assert L.moe_gate_route_workspace_size(1, 2048, 256, 2) >= 272 * 4
+    assert L.moe_gate_route_workspace_size(8192, 2048, 256, 2) == 0
+    assert L.moe_gate_route_workspace_size(4, 2040, 256, 2) == 0   # invalid H
 
 
 def test_permute_validation_local_range():
