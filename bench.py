@@ -5,7 +5,9 @@
 
 Workload: the FP8 blockwise layer with clamped SwiGLU (H = 6144, I = 2048,
 288 routed experts top-8 plus one shared expert, L = 10), at T = 4096 tokens
-per step; T = 1 and T = 64 are reported in "sweep". Inputs are seeded,
+per step; T = 1 and T = 64 are reported in "sweep", and the router GEMM
+fused with the gate epilogue (moe_gate_route, the 258-column gate of the
+ep_lora_258 layer) at T = 1 .. 8192 in "gate_route". Inputs are seeded,
 synthetic and resident in HBM before timing. A step is one moe_forward: route
 -> permute -> activation quant -> grouped GEMM1 + SwiGLU -> grouped GEMM2 +
 combine. Prints one JSON line. "value" is the back-to-back time of K steps
@@ -304,8 +306,56 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu,
         "per_call_ms": {k_: round(v, 4) for k_, v in per_call.items()},
         "sweep": sweep,
+        "gate_route": gate_route_table(args.steps, stream) if not args.no_sweep else None,
     }
     print(json.dumps(line))
+
+
+GATE_CFG = "ep_lora_258"
+GATE_T = (1, 37, 512, 8192)
+
+
+def gate_route_table(steps, stream):
+    """moe_gate_route (router GEMM fused with the gate epilogue: selection
+    bias, raw-logit carry, two sinks, packed output) on the 258-column gate
+    of the ep_lora_258 layer (H = 2048). Per-call time (HIP events on the
+    launching stream), algorithmic bytes (x once, the router weight once,
+    ids / weights / packed / sink weights written) as GB/s and % of 8 TB/s,
+    and 2 T C H flop as % of the bf16 MFMA peak."""
+    import torch
+    import mixture_experts_expert_sigmoid_amd as M
+    from synth import CONFIGS, make_gate, make_tokens
+    spec = CONFIGS[GATE_CFG]
+    N, S, k, H = spec.n_routed, spec.n_sink, spec.top_k, spec.H
+    gate = make_gate(spec)
+    wg, bias = gate.wg.cuda(), gate.bias.cuda()
+    out = []
+    for T in GATE_T:
+        x = make_tokens(spec, T, device="cuda")
+        ids = torch.empty(T, k, dtype=torch.int32, device="cuda")
+        w = torch.empty(T, k, device="cuda")
+        sw = torch.empty(T, S, device="cuda")
+        packed = torch.empty(T, k, dtype=torch.int32, device="cuda")
+        nb = M.moe_gate_route_workspace_size(T, H, N, S)
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+        f = lambda: M.moe_gate_route(x, wg, N, S, k, 1.0, 1.0, ids, w, sw,
+                                     sel_bias=bias, packed=packed, ws=ws)
+        for _ in range(5):
+            f()
+        ms = time_calls(f, steps, stream)
+        byts = T * H * 2 + (N + S) * H * 2 + T * (k * 12 + S * 4)
+        flops = 2.0 * T * (N + S) * H
+        gbs = byts / (ms * 1e-3) / 1e9
+        tfl = flops / (ms * 1e-3) / 1e12
+        out.append({"T": T, "us_per_call": round(ms * 1e3, 2),
+                    "tokens_per_s": round(T / (ms * 1e-3), 1),
+                    "path": "fused" if nb == 0 else "split-K + epilogue kernel",
+                    "algorithmic_bytes": byts, "gbs": round(gbs, 1),
+                    "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                    "tflops": round(tfl, 2),
+                    "pct_bf16_mfma_peak": round(100 * tfl / BF16_PEAK_TFLOPS, 2)})
+        print(f"# gate_route T={T}: {ms * 1e3:.2f} us/call", file=sys.stderr, flush=True)
+    return out
 
 
 def config_table(args, stream, flush):

@@ -107,4 +107,16 @@ __device__ __forceinline__ float max_across_rows(float v) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// fp32 sigmoid 1 / (1 + e^-x) for ranking keys, within a few ulp: e^-x =
+// 2^(hi + lo) with hi = fp32(-x log2 e) and lo its rounding error (one fma)
+// plus the tail of log2 e, 2^hi on v_exp_f32, 2^lo as 1 + lo ln 2, then
+// v_rcp_f32. Saturates to exactly 1 and 0 at the ends.
+__device__ __forceinline__ float sigmoid_key(float x) {
+  const float kL = 1.44269502e+00f, kLlo = 1.92596303e-08f;   // log2(e) = kL + kLlo
+  const float hi = -x * kL;
+  const float lo = fmaf(-x, kL, -hi) - x * kLlo;
+  const float e = __builtin_amdgcn_exp2f(hi) * fmaf(lo, 0.693147182f, 1.0f);
+  return __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 }  // namespace moe

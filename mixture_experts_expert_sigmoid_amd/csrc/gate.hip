@@ -40,8 +40,10 @@ namespace moe {
 namespace {
 
 constexpr int kGBM = 32;          // tokens per GEMM workgroup
-constexpr int kGRows = 16;        // rows per epilogue workgroup (16-lane groups)
+constexpr int kGRows = 4;         // rows per reduce + epilogue workgroup
+constexpr int kGMaxSplits = 32;   // K splits at most
 constexpr int kGThreads = 256;    // 4 waves
+constexpr int kGDepth = 4;        // K steps of the GEMM ring (3 in flight)
 
 struct GateP {
   const uint8_t* x;     // bf16 [T][H]
@@ -61,15 +63,14 @@ struct GateP {
   int* packed;          // [T][k] or NULL
 };
 
-struct OpOrU { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a | b; } };
-
 // ---------------------------------------------------------------- GEMM --
 // acc[j][ts] holds columns 16 (4 j + wave) + 4 (lane / 16) + r, r = 0..3, of
 // token t0 + 16 ts + lane % 16 over the split's K range.
 template <int NQ>
 __device__ __forceinline__ void gate_gemm(const GateP& P, f32x4 (&acc)[NQ][2],
                                           long t0, int split) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 15, lg = lane >> 4;
   const long rowb = (long)P.H * 2;
   const int st0 = split * P.steps;
@@ -91,10 +92,13 @@ __device__ __forceinline__ void gate_gemm(const GateP& P, f32x4 (&acc)[NQ][2],
   for (int j = 0; j < NQ; ++j)
 #pragma unroll
     for (int ts = 0; ts < 2; ++ts) acc[j][ts] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // this wave's column subtiles: 4 j + wave < NS for j < nq (wave-uniform)
+  const int nq = (P.NS - wave + 3) >> 2;
 
   struct Fr { i32x4 a[NQ]; i32x4 b[2]; };
   // loads are unconditional (past the end they re-read the last step) so the
-  // wait counts stay static with two steps in flight
+  // wait counts stay static: kGDepth steps in flight, a step's registers
+  // reloaded as soon as its MFMAs have issued
   auto load = [&](Fr& f, int st) {
     const long off = (long)min(st, nst - 1) * 64;
 #pragma unroll
@@ -106,7 +110,7 @@ __device__ __forceinline__ void gate_gemm(const GateP& P, f32x4 (&acc)[NQ][2],
     if (st >= nst) return;
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
-      if (4 * j + wave >= P.NS) continue;           // wave-uniform
+      if (j >= nq) break;
 #pragma unroll
       for (int ts = 0; ts < 2; ++ts)
         acc[j][ts] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -114,54 +118,58 @@ __device__ __forceinline__ void gate_gemm(const GateP& P, f32x4 (&acc)[NQ][2],
             acc[j][ts], 0, 0, 0);
     }
   };
-  Fr f0, f1, f2;
-  load(f0, 0);
-  load(f1, 1);
-  for (int st = 0; st < nst; st += 3) {
-    load(f2, st + 2); mma(f0, st);
-    load(f0, st + 3); mma(f1, st + 1);
-    load(f1, st + 4); mma(f2, st + 2);
+  constexpr int D = kGDepth;
+  Fr f[D];
+  // the scheduling barriers keep the loads in step order: loads complete in
+  // issue order, so a step is ready once the later steps' loads are the only
+  // ones outstanding
+#pragma unroll
+  for (int u = 0; u < D; ++u) {
+    load(f[u], u);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int st = 0; st < nst; st += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      mma(f[u], st + u);
+      __builtin_amdgcn_sched_barrier(0);
+      load(f[u], st + u + D);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
 // ------------------------------------------------------------ epilogue --
-__device__ __forceinline__ float sigmoid_f32(float x) {
-  return 1.0f / (1.0f + expf(-x));
-}
-
 // One token row per 16-lane group. L points at the row's fp32 logits in LDS
-// (columns 0 .. NC - 1 valid). NV >= ceil(n_routed / 16).
+// (columns 0 .. NC - 1 valid). NV >= ceil(n_routed / 16). Taken and
+// non-candidate columns hold key -inf; the winner's raw logit is read back
+// from L.
 template <int NV>
 __device__ __forceinline__ void route_row16(const GateP& P, const float* L, long row,
                                             bool row_ok) {
   const int lr = threadIdx.x & 15;
-  const int nvr = (P.n_routed + 15) >> 4;
-  float raw[NV], key[NV];
-  uint32_t taken = 0;
+  float key[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int c = lr + 16 * i;
-    raw[i] = (i < nvr) ? L[min(c, P.NC - 1)] : 0.0f;
-    if (c >= P.n_routed) taken |= 1u << i;          // not a candidate
-    key[i] = P.bias ? sigmoid_f32(raw[i]) + P.bias[min(c, P.n_routed - 1)] : raw[i];
+    const bool cand = c < P.n_routed;
+    const float raw = cand ? L[c] : 0.0f;
+    key[i] = !cand ? -INFINITY : P.bias ? sigmoid_key(raw) + P.bias[c] : raw;
   }
   float my_x = 0.0f;
   int my_c = 0;
   for (int j = 0; j < P.k; ++j) {
-    float bv = -INFINITY, braw = 0.0f;
-    int bi = NV;
+    float bv = key[0];
+    int bi = 0;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const bool cand = !((taken >> i) & 1u);
-      if (cand && (bi == NV || key[i] > bv)) { bv = key[i]; braw = raw[i]; bi = i; }
-    }
+    for (int i = 1; i < NV; ++i)
+      if (key[i] > bv) { bv = key[i]; bi = i; }      // first maximum: lowest column
     const float m = row16_reduce(bv, OpMax{});
-    const int bc = (bi < NV && bv == m) ? lr + 16 * bi : 0x7FFFFFFF;
-    const int wc = row16_reduce(bc, OpMinI{});
-    const bool own = (wc & 15) == lr && bi < NV && lr + 16 * bi == wc;
-    if (own) taken |= 1u << bi;
-    const uint32_t xr = row16_reduce(own ? __float_as_uint(braw) : 0u, OpOrU{});
-    if (lr == j) { my_x = __uint_as_float(xr); my_c = wc; }
+    const int wc = row16_reduce(bv == m ? lr + 16 * bi : 0x7FFFFFFF, OpMinI{});
+    const int bo = (wc & 15) == lr ? wc >> 4 : -1;     // owner lane: take it
+#pragma unroll
+    for (int i = 0; i < NV; ++i) key[i] = i == bo ? -INFINITY : key[i];
+    if (lr == j) { my_c = wc; my_x = L[wc]; }          // carry the raw logit
   }
   const bool active = lr < P.k + P.n_sink;
   if (lr >= P.k && active) my_x = L[P.n_routed + (lr - P.k)];
@@ -236,7 +244,9 @@ __global__ __launch_bounds__(kGThreads) void gate_part_kernel(GateP P) {
   }
 }
 
-// S > 1: add the partial sums in split order for 16 rows, then the epilogue.
+// S > 1: add the partial sums in split order for kGRows rows, then the
+// epilogue. Each thread owns one 4-column chunk of one row at a time and
+// issues the loads of all its splits before adding them in split order.
 template <int NQ>
 __global__ __launch_bounds__(kGThreads) void gate_reduce_route_kernel(GateP P) {
   extern __shared__ __attribute__((aligned(16))) float sl[];
@@ -247,26 +257,25 @@ __global__ __launch_bounds__(kGThreads) void gate_reduce_route_kernel(GateP P) {
   for (int i = threadIdx.x; i < rows * n4; i += kGThreads) {
     const int r = i / n4, c = 4 * (i - r * n4);
     const float* src = P.part + (t0 + r) * NCP + c;
-    f32x4 v = *(const f32x4*)src;
-    int s = 1;
-    for (; s + 4 <= P.S; s += 4) {                 // four loads in flight
-      const f32x4 a = *(const f32x4*)(src + s * slot);
-      const f32x4 b = *(const f32x4*)(src + (s + 1) * slot);
-      const f32x4 d = *(const f32x4*)(src + (s + 2) * slot);
-      const f32x4 e = *(const f32x4*)(src + (s + 3) * slot);
-      v += a; v += b; v += d; v += e;
-    }
-    for (; s < P.S; ++s) v += *(const f32x4*)(src + s * slot);
-    *(f32x4*)(sl + r * LP + c) = v;
+    f32x4 v[kGMaxSplits];
+#pragma unroll
+    for (int q = 0; q < kGMaxSplits; ++q)
+      if (q < P.S) v[q] = *(const f32x4*)(src + q * slot);
+    f32x4 sum = v[0];
+#pragma unroll
+    for (int q = 1; q < kGMaxSplits; ++q)
+      if (q < P.S) sum += v[q];
+    *(f32x4*)(sl + r * LP + c) = sum;
     if (P.logits) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        if (c + q < P.NC) P.logits[(t0 + r) * P.NC + c + q] = v[q];
+        if (c + q < P.NC) P.logits[(t0 + r) * P.NC + c + q] = sum[q];
     }
   }
   __syncthreads();
   const int grp = threadIdx.x >> 4;
-  route_row16<4 * NQ>(P, sl + grp * LP, t0 + grp, grp < rows);
+  if (grp < kGRows)                                 // whole 16-lane groups
+    route_row16<4 * NQ>(P, sl + grp * LP, t0 + grp, grp < rows);
 }
 
 int splits_for(long T, int H) {
@@ -274,7 +283,7 @@ int splits_for(long T, int H) {
   const int steps = H / 32;
   if (tiles >= kGateFusedTiles) return 1;
   long S = (kGateSplitTarget + tiles - 1) / tiles;
-  S = std::max<long>(2, std::min<long>(S, std::min(32, steps)));
+  S = std::max<long>(2, std::min<long>(S, std::min(kGMaxSplits, steps)));
   const long ps = (steps + S - 1) / S;
   return (int)((steps + ps - 1) / ps);
 }

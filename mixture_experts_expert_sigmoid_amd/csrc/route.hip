@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void route_kernel(
     v[i] = (c < n_routed) ? x[c] : 0.0f;
     if (c >= n_routed) taken |= 1u << i;   // not a candidate
     // with a selection bias the key is fp32 sigmoid(x) + bias
-    key[i] = bias ? 1.0f / (1.0f + expf(-v[i])) + bias[c < n_routed ? c : 0] : v[i];
+    key[i] = bias ? sigmoid_key(v[i]) + bias[c < n_routed ? c : 0] : v[i];
   }
 
   float my_x = -INFINITY;   // raw logit of the slot / sink this lane reports
