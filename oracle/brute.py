@@ -143,6 +143,17 @@ def layer(spec, arr, x_bits, logits):
                 g = min(gu[n], L)
                 u = max(min(gu[I + n], L), -L)
                 h.append(g * _sig(alpha * g) * (u + beta))
+            dn = None
+            if spec.lora_rank and spec.lora_down and e < spec.n_local:
+                # down LoRA on the true-units SwiGLU output, bf16-rounded
+                A2 = arr["lora_A2"][e]
+                B2 = arr["lora_B2"][e]
+                hl = [bf16_nearest(v) for v in h]
+                z2 = [sum(hl[n] * bf16_bits_value(int(A2[q][n])) for n in range(I))
+                      for q in range(spec.lora_rank)]
+                dn = [f32(spec.lora_scale) * sum(z2[q] * bf16_bits_value(int(B2[m][q]))
+                                                 for q in range(spec.lora_rank))
+                      for m in range(H)]
             if spec.fmt == "fp8":
                 hq = []
                 for c0 in range(0, I, 128):
@@ -154,6 +165,8 @@ def layer(spec, arr, x_bits, logits):
             else:
                 h = [bf16_nearest(v) for v in h]
             ys[(e, t)] = [sum(h[n] * W2[m][n] for n in range(I)) for m in range(H)]
+            if dn is not None:
+                ys[(e, t)] = [a + b for a, b in zip(ys[(e, t)], dn)]
     out = []
     for t in range(T):
         ids, w, _ = route_row([float(v) for v in logits[t]], spec.n_routed,

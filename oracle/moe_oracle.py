@@ -41,7 +41,10 @@ title and section):
                 (DeepGEMM PR #445), "Summary" and "Compatibility".
   lora       -- delta added to gate and up in true units, i.e. after each
                 half's own global scale: MoE-LoRA AOT release notes,
-                "Changes since 1b699bf".
+                "Changes since 1b699bf"; the down-projection LoRA consumes
+                activation_lora_input, the SwiGLU output in those true
+                units (same section: the pre-fix kernels left it off by
+                gate/up), its delta added to the expert's output.
   combine    -- out[t] = sum over t's local slots of w[t, j] * y[t, j], fp32
                 accumulation on the device ("slot-specific routing-weight
                 reduction"): batchgen PR #239, commit text.
@@ -381,6 +384,23 @@ def lora_delta(spec, arr, e, x_bf16_rows):
     return float(np.float32(spec.lora_scale)) * (z @ B.T)
 
 
+def down_lora_input(h):
+    """activation_lora_input: the SwiGLU output in true units (formed from
+    the gate and up halves after their own global scales and the up-delta),
+    rounded to bf16, before any re-quantisation for the down GEMM."""
+    return bf16_round(h)
+
+
+def down_lora_delta(spec, arr, e, h_lora_rows):
+    """Rank-r delta on the down projection: z2 = h_lora A2_e^T (full
+    precision), delta = lora_scale * z2 B2_e^T, shape [m, H]; added to the
+    expert's output row before the routing-weighted combine."""
+    A2 = bf16_decode(arr["lora_A2"][e])            # [r, I]
+    B2 = bf16_decode(arr["lora_B2"][e])            # [H, r]
+    z2 = h_lora_rows @ A2.T
+    return float(np.float32(spec.lora_scale)) * (z2 @ B2.T)
+
+
 # ----------------------------------------------------------------------------
 # rounding decisions of h taken from an fp32 kernel
 # ----------------------------------------------------------------------------
@@ -470,6 +490,9 @@ def expert_ffn(spec, arr, e, xhat_rows, x_bf16_rows, detail=False):
     w2 = dequant(spec.fmt, arr["w2_q"][e],
                  None if arr["w2_s"] is None else arr["w2_s"][e])
     y = hhat @ w2.T                                # [m, H]
+    down = lora and spec.lora_down
+    if down:
+        y = y + down_lora_delta(spec, arr, e, down_lora_input(h))
     if not detail:
         return y
     mag = np.abs(xhat_rows) @ np.abs(w13).T
@@ -481,6 +504,11 @@ def expert_ffn(spec, arr, e, xhat_rows, x_bf16_rows, detail=False):
     err_h = ACC_REL * (dg * mag[:, :I] + du * mag[:, I:]) + EVAL_REL * np.abs(h)
     alt = rounding_alternatives(h, err_h, spec.fmt)
     y_allow = alt @ np.abs(w2).T
+    if down:   # boundary decisions of the bf16 down-LoRA input
+        alt_l = rounding_alternatives(h, err_h, "bf16")
+        A2 = np.abs(bf16_decode(arr["lora_A2"][e]))
+        B2 = np.abs(bf16_decode(arr["lora_B2"][e]))
+        y_allow = y_allow + abs(spec.lora_scale) * ((alt_l @ A2.T) @ B2.T)
     return y, dict(h=h, hhat=hhat, alt=alt, y_allow=y_allow,
                    n_boundary=int(np.count_nonzero(alt)))
 

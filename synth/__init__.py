@@ -58,6 +58,7 @@ class LayerSpec:
     shared_w: float = 1.0
     lora_rank: int = 0
     lora_scale: float = 1.0
+    lora_down: bool = False  # the same adapter also carries a down-projection LoRA
     gscale: bool = False     # per-expert (gate, up) global scales
     logits: str = "normal"   # normal | skewed | router | mix258
     w13_std: Optional[float] = None
@@ -96,6 +97,7 @@ CONFIGS = {
     "ep_lora_258": LayerSpec(
         name="ep_lora_258", cfg_id=5, fmt=FMT_FP8, H=2048, I=1024,
         n_routed=256, n_sink=2, top_k=8, E_loc=32, offset=96, lora_rank=16,
+        lora_down=True,
         gscale=True, logits="mix258", Ts=(1, 37, 512, 8192)),
 }
 
@@ -134,6 +136,8 @@ class Layer:
     lora_A: Optional[torch.Tensor]  # [G, r, H] bf16
     lora_B: Optional[torch.Tensor]  # [G, 2I, r] bf16
     w_router: Optional[torch.Tensor]  # [H, E] f64 (router GEMM input recipe)
+    lora_A2: Optional[torch.Tensor] = None  # [G, r, I] bf16 (down LoRA)
+    lora_B2: Optional[torch.Tensor] = None  # [G, H, r] bf16
 
 
 @dataclasses.dataclass
@@ -197,8 +201,18 @@ def make_layer(spec: LayerSpec, device="cpu") -> Layer:
         g = _gen("cpu", spec.cfg_id, 7003)
         w_router = torch.randn(H, spec.n_routed, generator=g,
                                dtype=torch.float64) * 0.02
+    lora_A2 = lora_B2 = None
+    if spec.lora_rank and spec.lora_down:
+        r = spec.lora_rank
+        g = _gen(device, spec.cfg_id, 7006)
+        # RMS(h A2^T) ~ RMS(h) ~ RMS(y); B2 std 0.5 / sqrt(r) gives a delta
+        # of about half the base down-projection output
+        lora_A2 = (torch.randn(G, r, I, generator=g, device=device)
+                   / math.sqrt(I)).to(torch.bfloat16)
+        lora_B2 = (torch.randn(G, H, r, generator=g, device=device)
+                   * (0.5 / math.sqrt(r))).to(torch.bfloat16)
     return Layer(spec, st(q13), st(s13), st(q2), st(s2), gs, lora_A, lora_B,
-                 w_router)
+                 w_router, lora_A2, lora_B2)
 
 
 def _logits_mix258(spec: LayerSpec, T: int, g, device) -> torch.Tensor:
@@ -290,7 +304,8 @@ def to_numpy_layer(layer: Layer, experts=None) -> dict:
             return t.view(torch.uint8).numpy()
         return t.numpy()
     return {k: cp(getattr(layer, k)) for k in
-            ("w13_q", "w13_s", "w2_q", "w2_s", "gs", "lora_A", "lora_B")}
+            ("w13_q", "w13_s", "w2_q", "w2_s", "gs", "lora_A", "lora_B",
+             "lora_A2", "lora_B2")}
 
 
 def to_numpy_batch(batch: Batch) -> dict:

@@ -141,11 +141,55 @@ def _lora_setup(T=6):
 def test_lora_zero_B_equals_base_and_no_adapter_equals_base():
     spec, layer, arr, nb = _lora_setup()
     base = O.moe_layer(spec.scaled(lora_rank=0), arr, nb["x_bits"], nb["logits"])
-    arr0 = dict(arr, lora_B=np.zeros_like(arr["lora_B"]))
+    arr0 = dict(arr, lora_B=np.zeros_like(arr["lora_B"]),
+                lora_B2=np.zeros_like(arr["lora_B2"]))
     zero_b = O.moe_layer(spec, arr0, nb["x_bits"], nb["logits"])
     assert np.array_equal(base, zero_b)
     with_lora = O.moe_layer(spec, arr, nb["x_bits"], nb["logits"])
     assert np.max(np.abs(with_lora - base)) > 1e-3 * np.abs(base).max()
+    # zero down B: the up LoRA alone
+    up_only = O.moe_layer(spec.scaled(lora_down=False), arr, nb["x_bits"], nb["logits"])
+    arr2 = dict(arr, lora_B2=np.zeros_like(arr["lora_B2"]))
+    assert np.array_equal(O.moe_layer(spec, arr2, nb["x_bits"], nb["logits"]), up_only)
+    assert np.max(np.abs(with_lora - up_only)) > 1e-3 * np.abs(base).max()
+
+
+def test_down_lora_is_linear_in_its_B():
+    """Doubling B2 doubles the down delta: out(2 B2) - out(B2) = out(B2) -
+    out(0) (exact up to float64 rounding)."""
+    spec, layer, arr, nb = _lora_setup()
+    f = lambda b2: O.moe_layer(spec, dict(arr, lora_B2=b2), nb["x_bits"], nb["logits"])
+    b2 = arr["lora_B2"]
+    twice = (torch.from_numpy(b2.view(np.int16)).view(torch.bfloat16).float() * 2
+             ).bfloat16().view(torch.int16).numpy().view(np.uint16)
+    o0, o1, o2 = f(np.zeros_like(b2)), f(b2), f(twice)
+    np.testing.assert_allclose(o2 - o1, o1 - o0, rtol=0, atol=1e-9 * np.abs(o1).max())
+
+
+def _mut_down_input_after_requant(mp):
+    """Feed the down LoRA the re-quantised h (what the down GEMM reads)
+    instead of the true-units SwiGLU output."""
+    mp.setattr(O, "down_lora_input", lambda h: O.requant_fp8(h))
+
+
+def _mut_down_input_gate_units(mp):
+    """The pre-fix units: the up half (and so h and the down-LoRA input)
+    left off by gate/up."""
+    real = O.down_lora_delta
+    mp.setattr(O, "down_lora_delta", lambda spec, arr, e, hl: real(
+        spec, arr, e, hl * (float(arr["gs"][e][0]) / float(arr["gs"][e][1]))))
+
+
+def _mut_down_dropped(mp):
+    mp.setattr(O, "down_lora_delta", lambda spec, arr, e, hl: 0.0)
+
+
+@pytest.mark.parametrize("mut", [_mut_down_input_after_requant, _mut_down_input_gate_units,
+                                 _mut_down_dropped])
+def test_planted_down_lora_mistakes_are_caught(mut, monkeypatch):
+    spec = TINY["ep_lora"]
+    ours, ref = _oracle_and_brute(spec, 5, mut, monkeypatch)
+    assert np.max(np.abs(ours - ref)) > 1e-6 * np.abs(ref).max()
 
 
 def _resplit(spec, arr, factor):

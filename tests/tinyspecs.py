@@ -17,5 +17,5 @@ TINY = {
     "ep_lora": LayerSpec(name="tiny_ep_lora_t", cfg_id=105, fmt="fp8", H=128,
                          I=128, n_routed=8, n_sink=2, top_k=3, E_loc=3,
                          offset=2, lora_rank=4, gscale=True, logits="mix258",
-                         route_scale=1.5),
+                         route_scale=1.5, lora_down=True),
 }
