@@ -90,11 +90,17 @@ typedef struct {
                            units" of [LORA-AOT "Changes since 1b699bf"] */
 } moe_weights;
 
-/* Rank-r LoRA on the fused gate/up projection of the local experts
- * [LORA-AOT "Changes since 1b699bf"]:  z = x A_e^T (fp32),
+/* Rank-r LoRA of the local experts [LORA-AOT "Changes since 1b699bf"].
+ * On the fused gate/up projection ("lora"): z = x A_e^T (fp32),
  * delta = scale * z B_e^T, added to g and u after each half's own global
  * scale, before the clamp.  A: bf16 [n_groups][rank][H], B: bf16
- * [n_groups][2I][rank]. The shared expert (group E_loc) carries no LoRA. */
+ * [n_groups][2I][rank].
+ * On the down projection ("lora_down"): its input is activation_lora_input,
+ * the SwiGLU output h in those true units rounded to bf16 (before any FP8
+ * re-quantisation); z2 = h A2_e^T (fp32), y += scale * z2 B2_e^T, added to
+ * the expert's output row before the routing-weighted combine.  A2: bf16
+ * [n_groups][rank][I], B2: bf16 [n_groups][H][rank].
+ * The shared expert (group E_loc) carries no LoRA. */
 typedef struct {
   int rank;             /* 1..32 */
   int n_groups;         /* adapters for groups 0..n_groups-1 (the local
@@ -203,6 +209,10 @@ int moe_quantize_act_fp8(const void *x_bf16, long T, int H, void *xq,
  *   BF16 / INT4 weights: x bf16 [T][H] (xs NULL); h bf16 [P_cap][I]
  *     (round-to-nearest-even), hs NULL.
  * x_bf16 bf16 [T][H] is the LoRA input (NULL without LoRA).
+ * h_lora (FP8 weights only, else it must be NULL: MOE_ERR_PARAM), nullable:
+ * bf16 [P_cap][I], the SwiGLU output before the re-quantisation (round to
+ * nearest even), i.e. the down-LoRA input; BF16 / INT4 layers pass h itself
+ * to moe_grouped_gemm2_combine instead.
  * offsets / sorted_pair come from moe_permute for the same (T, top_k);
  * w13->n_groups = G, w13->N = 2I, w13->K = H. p_cap = rows allocated in h.
  * Limits: H % 128 == 0 and I % 128 == 0. Workspace:
@@ -217,31 +227,39 @@ int moe_grouped_gemm1_act(const moe_weights *w13, const void *x,
                           const float *xs, const void *x_bf16, long T, int H,
                           int I, int top_k, long p_cap, const int *offsets,
                           const int *sorted_pair, const moe_act_params *act,
-                          const moe_lora *lora, void *h, float *hs, void *ws,
-                          size_t ws_bytes, void *stream);
+                          const moe_lora *lora, void *h, float *hs,
+                          void *h_lora, void *ws, size_t ws_bytes,
+                          void *stream);
 size_t moe_gemm1_workspace_size(const moe_weights *w13, long p_cap,
                                 const moe_lora *lora);
 
 /* ---------------------------------------- grouped GEMM2 + weighted combine -- */
 /* y[r] = h[r] W2_g^T (fp32; FP8 per 128-K block partial sums times
- * hs[r][kb] * scale[g][nb][kb]) for every sorted row, then
+ * hs[r][kb] * scale[g][nb][kb]) for every sorted row, plus with lora_down
+ * the down-LoRA delta scale * (h_lora[r] A2_g^T) B2_g^T for groups
+ * g < lora_down->n_groups (h_lora bf16 [P_cap][I]: GEMM1's h_lora output
+ * for FP8 weights, h itself for BF16 / INT4), then
  *   out[t][:] = sum_{j < top_k, pair_row[t*top_k+j] >= 0} topk_w[t][j] *
  *               y[pair_row[t*top_k+j]]   (ascending j, fp32)
  *             + shared_w * y[pair_row[T*top_k + t]]   (if shared_expert)
  * [INT4-PR: slot-specific routing-weight reduction, fp32 accumulation].
  * Every out element is written (0 for a token with no local pair).
  * w2->N = H, w2->K = I. out fp32 [T][H]. Workspace:
- * moe_gemm2_workspace_size(w2, p_cap) bytes: the fp32 y rows, or for FP8 /
- * INT4 weights at decode sizes their split-K partial sums (4 * p_cap * H
- * floats, reduced by the combine in a fixed order). Returns 0 for a NULL
- * w2. */
+ * moe_gemm2_workspace_size(w2, p_cap, lora_down) bytes: the fp32 y rows, or
+ * for FP8 / INT4 weights at decode sizes their split-K partial sums
+ * (4 * p_cap * H floats, reduced by the combine in a fixed order; the
+ * down-LoRA delta enters the first partial of each tile), then the
+ * down-LoRA z2 rows (p_cap * rank floats). Errors: NULL for a lora_down
+ * without h_lora. Returns 0 for a NULL w2. */
 int moe_grouped_gemm2_combine(const moe_weights *w2, const void *h,
-                              const float *hs, long T, int H, int I,
+                              const float *hs, const void *h_lora,
+                              const moe_lora *lora_down, long T, int H, int I,
                               int top_k, int shared_expert, long p_cap,
                               const int *offsets, const int *pair_row,
                               const float *topk_w, float shared_w, float *out,
                               void *ws, size_t ws_bytes, void *stream);
-size_t moe_gemm2_workspace_size(const moe_weights *w2, long p_cap);
+size_t moe_gemm2_workspace_size(const moe_weights *w2, long p_cap,
+                                const moe_lora *lora_down);
 
 /* ---------------------------------------------------------- whole layer -- */
 typedef struct {
@@ -255,7 +273,9 @@ typedef struct {
   float route_scale, global_scale, shared_w;
   moe_weights w13, w2;      /* n_groups = num_local_experts + shared_expert */
   moe_act_params act;
-  const moe_lora *lora;     /* nullable */
+  const moe_lora *lora;     /* nullable: LoRA on [gate | up] */
+  const moe_lora *lora_down;/* nullable: LoRA on the down projection, input
+                               the true-units SwiGLU output (see moe_lora) */
 } moe_layer;
 
 /* One call of the whole path on `stream`: moe_route -> moe_permute ->

@@ -55,7 +55,8 @@ class MoeLayer(ctypes.Structure):
                 ("shared_expert", c_int), ("top_k", c_int), ("n_sink", c_int),
                 ("route_scale", c_float), ("global_scale", c_float),
                 ("shared_w", c_float), ("w13", MoeWeights), ("w2", MoeWeights),
-                ("act", MoeActParams), ("lora", POINTER(MoeLora))]
+                ("act", MoeActParams), ("lora", POINTER(MoeLora)),
+                ("lora_down", POINTER(MoeLora))]
 
 
 _lib = None
@@ -79,15 +80,17 @@ _SIGS = {
                                       c_void_p, c_long, c_int, c_int, c_int,
                                       c_long, c_void_p, c_void_p,
                                       POINTER(MoeActParams), POINTER(MoeLora),
-                                      c_void_p, c_void_p, c_void_p, c_size_t,
-                                      c_void_p]),
+                                      c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_size_t, c_void_p]),
     "moe_gemm1_workspace_size": (c_size_t, [POINTER(MoeWeights), c_long, POINTER(MoeLora)]),
     "moe_grouped_gemm2_combine": (c_int, [POINTER(MoeWeights), c_void_p, c_void_p,
+                                          c_void_p, POINTER(MoeLora),
                                           c_long, c_int, c_int, c_int, c_int,
                                           c_long, c_void_p, c_void_p, c_void_p,
                                           c_float, c_void_p, c_void_p, c_size_t,
                                           c_void_p]),
-    "moe_gemm2_workspace_size": (c_size_t, [POINTER(MoeWeights), c_long]),
+    "moe_gemm2_workspace_size": (c_size_t, [POINTER(MoeWeights), c_long,
+                                            POINTER(MoeLora)]),
     "moe_forward": (c_int, [POINTER(MoeLayer), c_void_p, c_void_p, c_long, c_long,
                             c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                             c_void_p, c_size_t, c_void_p]),
@@ -160,12 +163,12 @@ def lora_desc(A: torch.Tensor, B: torch.Tensor, scale=1.0) -> MoeLora:
 def layer_desc(H, I, num_experts_global, num_local_experts, local_expert_offset,
                shared_expert, top_k, n_sink, route_scale, global_scale, shared_w,
                w13: MoeWeights, w2: MoeWeights, act: MoeActParams,
-               lora: Optional[MoeLora] = None) -> MoeLayer:
+               lora: Optional[MoeLora] = None,
+               lora_down: Optional[MoeLora] = None) -> MoeLayer:
     L = MoeLayer(H, I, num_experts_global, num_local_experts, local_expert_offset,
                  shared_expert, top_k, n_sink, route_scale, global_scale,
-                 shared_w, w13, w2, act,
-                 ctypes.pointer(lora) if lora is not None else None)
-    L._keep = (w13, w2, lora)
+                 shared_w, w13, w2, act, _lp(lora), _lp(lora_down))
+    L._keep = (w13, w2, lora, lora_down)
     return L
 
 
@@ -224,29 +227,35 @@ def moe_gemm1_workspace_size(w13: MoeWeights, p_cap, lora: Optional[MoeLora] = N
         ctypes.byref(w13), p_cap, ctypes.pointer(lora) if lora is not None else None)
 
 
+def _lp(lora):
+    return ctypes.pointer(lora) if lora is not None else None
+
+
 def moe_grouped_gemm1_act(w13: MoeWeights, x, xs, x_bf16, T, H, I, top_k, p_cap,
                           offsets, sorted_pair, act: MoeActParams,
-                          lora: Optional[MoeLora], h, hs, ws, stream=None):
+                          lora: Optional[MoeLora], h, hs, ws, stream=None,
+                          h_lora=None):
     _check(lib().moe_grouped_gemm1_act(
         ctypes.byref(w13), _p(x), _p(xs), _p(x_bf16), T, H, I, top_k, p_cap,
-        _p(offsets), _p(sorted_pair), ctypes.byref(act),
-        ctypes.pointer(lora) if lora is not None else None, _p(h), _p(hs),
-        _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+        _p(offsets), _p(sorted_pair), ctypes.byref(act), _lp(lora), _p(h), _p(hs),
+        _p(h_lora), _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream)), "moe_grouped_gemm1_act")
 
 
-def moe_gemm2_workspace_size(w2: MoeWeights, p_cap) -> int:
-    return lib().moe_gemm2_workspace_size(ctypes.byref(w2), p_cap)
+def moe_gemm2_workspace_size(w2: MoeWeights, p_cap,
+                             lora_down: Optional[MoeLora] = None) -> int:
+    return lib().moe_gemm2_workspace_size(ctypes.byref(w2), p_cap, _lp(lora_down))
 
 
 def moe_grouped_gemm2_combine(w2: MoeWeights, h, hs, T, H, I, top_k,
                               shared_expert, p_cap, offsets, pair_row, topk_w,
-                              shared_w, out, ws, stream=None):
+                              shared_w, out, ws, stream=None, h_lora=None,
+                              lora_down: Optional[MoeLora] = None):
     _check(lib().moe_grouped_gemm2_combine(
-        ctypes.byref(w2), _p(h), _p(hs), T, H, I, top_k, shared_expert, p_cap,
-        _p(offsets), _p(pair_row), _p(topk_w), shared_w, _p(out), _p(ws),
-        ws.numel() * ws.element_size(), _stream(stream)),
-        "moe_grouped_gemm2_combine")
+        ctypes.byref(w2), _p(h), _p(hs), _p(h_lora), _lp(lora_down), T, H, I,
+        top_k, shared_expert, p_cap, _p(offsets), _p(pair_row), _p(topk_w),
+        shared_w, _p(out), _p(ws), ws.numel() * ws.element_size(),
+        _stream(stream)), "moe_grouped_gemm2_combine")
 
 
 def moe_workspace_size(layer: MoeLayer, T_max) -> int:
@@ -284,7 +293,7 @@ class MoeModule:
                  local_expert_offset=0, shared_expert=0, n_sink=0,
                  route_scale=1.0, global_scale=1.0, shared_w=1.0, alpha=1.0,
                  beta=0.0, limit=math.inf, lora_A=None, lora_B=None,
-                 lora_scale=1.0):
+                 lora_scale=1.0, lora_A2=None, lora_B2=None):
         self.fmt, self.H, self.I, self.top_k, self.n_sink = fmt, H, I, top_k, n_sink
         self.shared_expert = shared_expert
         E_loc = num_experts_global if num_local_experts is None else num_local_experts
@@ -292,10 +301,12 @@ class MoeModule:
         self.w2 = weights(fmt, w2_q, w2_s)
         self.act = act_params(alpha, beta, limit)
         self.lora = lora_desc(lora_A, lora_B, lora_scale) if lora_A is not None else None
+        self.lora_down = (lora_desc(lora_A2, lora_B2, lora_scale)
+                          if lora_A2 is not None else None)
         self.desc = layer_desc(H, I, num_experts_global, E_loc, local_expert_offset,
                                shared_expert, top_k, n_sink, route_scale,
                                global_scale, shared_w, self.w13, self.w2, self.act,
-                               self.lora)
+                               self.lora, self.lora_down)
         self._ws = None
 
     def workspace(self, T):

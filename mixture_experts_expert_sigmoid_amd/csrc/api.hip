@@ -239,7 +239,7 @@ static moe::Gemm1Args gemm1_args(const moe_weights* w13, const void* x,
                                  const int* sorted_pair,
                                  const moe_act_params* act,
                                  const moe_lora* lora, const float* z, void* h,
-                                 float* hs, float* part, void* x16) {
+                                 float* hs, float* part, void* x16, void* h_lora) {
   moe::Gemm1Args a{};
   a.fmt = w13->fmt;
   a.wq = w13->q;
@@ -267,6 +267,7 @@ static moe::Gemm1Args gemm1_args(const moe_weights* w13, const void* x,
   a.hs = hs;
   a.part = part;
   a.x16 = x16;
+  a.h_lora = h_lora;
   return a;
 }
 
@@ -274,11 +275,13 @@ int moe_grouped_gemm1_act(const moe_weights* w13, const void* x,
                           const float* xs, const void* x_bf16, long T, int H,
                           int I, int top_k, long p_cap, const int* offsets,
                           const int* sorted_pair, const moe_act_params* act,
-                          const moe_lora* lora, void* h, float* hs, void* ws,
-                          size_t ws_bytes, void* stream) {
+                          const moe_lora* lora, void* h, float* hs, void* h_lora,
+                          void* ws, size_t ws_bytes, void* stream) {
   int st = gemm1_checks(w13, x, xs, x_bf16, T, H, I, top_k, p_cap, offsets,
                         sorted_pair, act, lora, h, hs);
   if (st) return st;
+  // BF16 / INT4 layers write h in bf16 already: it is the down-LoRA input
+  if (h_lora && w13->fmt != MOE_W_FP8_B128) return MOE_ERR_PARAM;
   size_t need = moe_gemm1_workspace_size(w13, p_cap, lora);
   if (need && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
@@ -293,13 +296,15 @@ int moe_grouped_gemm1_act(const moe_weights* w13, const void* x,
                            lora->n_groups, p_cap, offsets, sorted_pair, z, s);
   if (e == hipSuccess)
     e = moe::launch_gemm1(gemm1_args(w13, x, xs, T, H, I, top_k, p_cap, offsets,
-                                     sorted_pair, act, lora, z, h, hs, part, x16), s);
+                                     sorted_pair, act, lora, z, h, hs, part, x16,
+                                     h_lora), s);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_grouped_gemm1_act");
 }
 
-size_t moe_gemm2_workspace_size(const moe_weights* w2, long p_cap) {
+size_t moe_gemm2_workspace_size(const moe_weights* w2, long p_cap,
+                                const moe_lora* lora_down) {
   if (!w2 || p_cap < 0 || w2->N < 0) return 0;
-  return g2_bytes(w2, p_cap);
+  return g2_bytes(w2, p_cap) + g1_z_bytes(p_cap, lora_down);
 }
 
 static int gemm2_checks(const moe_weights* w2, const void* h, const float* hs,
@@ -320,18 +325,27 @@ static int gemm2_checks(const moe_weights* w2, const void* h, const float* hs,
 }
 
 int moe_grouped_gemm2_combine(const moe_weights* w2, const void* h,
-                              const float* hs, long T, int H, int I, int top_k,
-                              int shared_expert, long p_cap, const int* offsets,
-                              const int* pair_row, const float* topk_w,
-                              float shared_w, float* out, void* ws,
-                              size_t ws_bytes, void* stream) {
+                              const float* hs, const void* h_lora,
+                              const moe_lora* lora_down, long T, int H, int I,
+                              int top_k, int shared_expert, long p_cap,
+                              const int* offsets, const int* pair_row,
+                              const float* topk_w, float shared_w, float* out,
+                              void* ws, size_t ws_bytes, void* stream) {
   int st = gemm2_checks(w2, h, hs, T, H, I, top_k, shared_expert, p_cap,
                         offsets, pair_row, topk_w, shared_w, out);
   if (st) return st;
-  size_t need = moe_gemm2_workspace_size(w2, p_cap);
+  if ((st = check_lora(lora_down, w2->n_groups))) return st;
+  if (lora_down && p_cap > 0 && !h_lora) return MOE_ERR_NULL;
+  size_t need = moe_gemm2_workspace_size(w2, p_cap, lora_down);
   if (need && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   float* y = (float*)ws;
+  float* z2 = (float*)((char*)ws + g2_bytes(w2, p_cap));
+  hipError_t e = hipSuccess;
+  if (lora_down)
+    e = moe::launch_lora_z(h_lora, lora_down->A, lora_down->rank, T, I, top_k,
+                           lora_down->n_groups, p_cap, offsets, nullptr, z2, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_grouped_gemm2_combine/lora_z");
   moe::Gemm2Args a{};
   a.fmt = w2->fmt;
   a.wq = w2->q;
@@ -346,7 +360,14 @@ int moe_grouped_gemm2_combine(const moe_weights* w2, const void* h,
   a.y = y;
   int sk_grid = 0;
   a.sk_grid = &sk_grid;
-  hipError_t e = moe::launch_gemm2(a, s);
+  if (lora_down) {
+    a.z = z2;
+    a.lora_B = lora_down->B;
+    a.lora_rank = lora_down->rank;
+    a.lora_groups = lora_down->n_groups;
+    a.lora_scale = lora_down->scale;
+  }
+  e = moe::launch_gemm2(a, s);
   if (e == hipSuccess)
     e = moe::launch_combine(y, T, H, top_k, shared_expert, pair_row, topk_w,
                             shared_w, out, s, sk_grid, p_cap, I, a.G, offsets);
@@ -357,7 +378,7 @@ int moe_grouped_gemm2_combine(const moe_weights* w2, const void* h,
 
 namespace {
 struct FwdLayout {
-  size_t offsets, sorted_pair, pair_row, perm_ws, xq, xs, z, h, hs, y, total;
+  size_t offsets, sorted_pair, pair_row, perm_ws, xq, xs, z, h, hs, h_lora, z2, y, total;
   size_t perm_bytes;
 };
 
@@ -379,6 +400,9 @@ FwdLayout layout(const moe_layer* L, long T) {
   o.z = take(L->lora ? (size_t)pc * L->lora->rank * 4 : 0);
   o.h = take((size_t)pc * L->I * (fp8 ? 1 : 2));
   o.hs = take(fp8 ? (size_t)pc * (L->I / 128) * 4 : 0);
+  // down LoRA: its bf16 input (FP8 layers; BF16 / INT4 read h) and z rows
+  o.h_lora = take(fp8 && L->lora_down ? (size_t)pc * L->I * 2 : 0);
+  o.z2 = take(L->lora_down ? (size_t)pc * L->lora_down->rank * 4 : 0);
   // y rows (or their stream-K partials); GEMM1's partials, consumed before
   // GEMM2 starts, share the region
   o.y = take(std::max(g2_bytes(&L->w2, pc), g1_part_bytes(&L->w13, pc)));
@@ -401,6 +425,8 @@ int layer_checks(const moe_layer* L) {
   if ((st = check_act(&L->act))) return st;
   if ((st = check_lora(L->lora, G))) return st;
   if (L->lora && L->lora->n_groups > L->num_local_experts) return MOE_ERR_SHAPE;
+  if ((st = check_lora(L->lora_down, G))) return st;
+  if (L->lora_down && L->lora_down->n_groups > L->num_local_experts) return MOE_ERR_SHAPE;
   if (L->n_sink < 0 || L->top_k > L->num_experts_global ||
       L->top_k + L->n_sink > 64 || L->num_experts_global + L->n_sink > 1024)
     return MOE_ERR_SHAPE;
@@ -444,6 +470,8 @@ int moe_forward(const moe_layer* L, const void* x_bf16, const float* logits,
   void* h = base + o.h;
   float* hs = (float*)(base + o.hs);
   float* y = (float*)(base + o.y);
+  void* h_lora = fp8 ? (void*)(base + o.h_lora) : h;
+  float* z2 = (float*)(base + o.z2);
 
   hipError_t e = moe::launch_route(logits, T, ld_logits, L->num_experts_global,
                                    L->n_sink, L->top_k, nullptr,
@@ -469,8 +497,15 @@ int moe_forward(const moe_layer* L, const void* x_bf16, const float* logits,
   e = moe::launch_gemm1(gemm1_args(&L->w13, fp8 ? xq : x_bf16, fp8 ? xs : nullptr,
                                    T, L->H, L->I, L->top_k, pc, offsets,
                                    sorted_pair, &L->act, L->lora, z, h,
-                                   fp8 ? hs : nullptr, g1_part, xq), s);
+                                   fp8 ? hs : nullptr, g1_part, xq,
+                                   fp8 && L->lora_down ? h_lora : nullptr), s);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/gemm1");
+  if (L->lora_down) {
+    e = moe::launch_lora_z(h_lora, L->lora_down->A, L->lora_down->rank, T, L->I,
+                           L->top_k, L->lora_down->n_groups, pc, offsets, nullptr,
+                           z2, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_forward/lora_z_down");
+  }
   moe::Gemm2Args a{};
   a.fmt = L->w2.fmt;
   a.wq = L->w2.q;
@@ -485,6 +520,13 @@ int moe_forward(const moe_layer* L, const void* x_bf16, const float* logits,
   a.y = y;
   int sk_grid = 0;
   a.sk_grid = &sk_grid;
+  if (L->lora_down) {
+    a.z = z2;
+    a.lora_B = L->lora_down->B;
+    a.lora_rank = L->lora_down->rank;
+    a.lora_groups = L->lora_down->n_groups;
+    a.lora_scale = L->lora_down->scale;
+  }
   e = moe::launch_gemm2(a, s);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/gemm2");
   e = moe::launch_combine(y, T, L->H, L->top_k, L->shared_expert, pair_row,

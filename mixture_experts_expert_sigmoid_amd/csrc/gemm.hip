@@ -285,6 +285,7 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t s) {
   P.lora_scale = a.lora_scale;
   P.h = (uint8_t*)a.h;
   P.hs = a.hs;
+  P.h_lora = (uint16_t*)a.h_lora;
   long hint = a.G > 0 ? a.p_cap / a.G : a.p_cap;
   if (a.fmt == FMT_FP8 || a.fmt == FMT_INT4) {
     const bool fp8 = a.fmt == FMT_FP8;
@@ -321,6 +322,11 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t s) {
   P.offsets = a.offsets;
   P.I = a.I;
   P.y = a.y;
+  P.z = a.z;
+  P.lora_B = (const uint16_t*)a.lora_B;
+  P.lora_rank = a.lora_rank;
+  P.lora_groups = a.z ? a.lora_groups : 0;
+  P.lora_scale = a.lora_scale;
   long hint = a.G > 0 ? a.p_cap / a.G : a.p_cap;
   *a.sk_grid = 0;
   const int NT = (a.H + 255) / 256;

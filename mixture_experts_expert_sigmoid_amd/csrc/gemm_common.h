@@ -44,12 +44,17 @@ struct GemmParams {
   // GEMM1 epilogue
   const float* gscale;
   float alpha, beta, limit;
+  // LoRA delta of this GEMM (GEMM1: on [gate | up]; GEMM2: on the down
+  // projection): acc += lora_scale * z[row] . B[g][column], z fp32
+  // [rows][rank], B bf16 [G][N][rank], groups g < lora_groups
   const float* z;
   const uint16_t* lora_B;
   int lora_rank, lora_groups;
   float lora_scale;
   uint8_t* h;                // GEMM1 out: e4m3 [p_cap][I] or bf16 [p_cap][I]
   float* hs;
+  uint16_t* h_lora;          // GEMM1 out (FP8 layers), nullable: bf16 [p_cap][I]
+                             // SwiGLU output before the re-quantisation
   // GEMM2 out
   float* y;                  // [p_cap][N]
   // split-K (decode sizes): fp32 partial sums [kSkSlots][p_rows][N]
@@ -174,6 +179,51 @@ __device__ __forceinline__ long a_source_row(const GemmParams& P, int r) {
   return (p < npr) ? (long)(p / P.top_k) : (long)(p - npr);
 }
 
+// LoRA delta on a tile of the FP8 / INT4 kernels, whose weights are the
+// MFMA's first operand: acc[ms][ns][r] is row 16 ms + lane % 16 of the tile
+// and column (ns ? n_hi : n_lo) + 16 wave + 4 (lane / 16) + r.
+//   acc += lora_scale * sum_q z[row][q] * B[g][column][q]  (q ascending)
+// z is staged through LDS as [q][BM]. The hi half is read only when hi_ok
+// (otherwise the lo columns are read again and the hi values never stored).
+// Every thread of the workgroup calls it (two barriers).
+template <int BM>
+__device__ __forceinline__ void lora_delta_tile(const GemmParams& P, const Tile& t,
+                                                f32x4 (&acc)[BM / 16][2], uint8_t* smem,
+                                                bool hi_ok) {
+  constexpr int MS = BM / 16;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int c0 = 16 * wave + 4 * lg;
+  const int g = t.g, row0 = t.row0, m = t.m;
+  float* sz = (float*)smem;
+  const int R = P.lora_rank;
+  for (int i = tid; i < R * BM; i += kThreads) {
+    const int q = i / BM, tr = i - q * BM;
+    sz[q * BM + tr] = P.z[(long)(row0 + (tr < m ? tr : 0)) * R + q];
+  }
+  __syncthreads();
+  const uint16_t* Bg = P.lora_B + (long)g * P.N * R;
+  const int nhi = hi_ok ? t.n_hi : t.n_lo;
+  for (int q = 0; q < R; ++q) {
+    float bl[4], bh[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      bl[r] = P.lora_scale * bf16_bits_to_f32(Bg[(long)(t.n_lo + c0 + r) * R + q]);
+      bh[r] = P.lora_scale * bf16_bits_to_f32(Bg[(long)(nhi + c0 + r) * R + q]);
+    }
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+      const float zq = sz[q * BM + 16 * ms + lr];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        acc[ms][0][r] = fmaf(zq, bl[r], acc[ms][0][r]);
+        acc[ms][1][r] = fmaf(zq, bh[r], acc[ms][1][r]);
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
 // epilogues. acc[ms][ns] holds rows rbase + 16 ms + 4 (lane/16) + r and
 // column (ns < 2 ? lo : hi) + wn*32 + (ns & 1)*16 + lane%16.
@@ -188,22 +238,9 @@ __device__ __forceinline__ void tile_epilogue(const GemmParams& P, const Tile& t
   const int lr = lane & 15, lg = lane >> 4;
   const int rbase = wm * (BM / 2);
   const int g = t.g, row0 = t.row0, m = t.m, nt = t.nt;
-  if constexpr (!G1) {
-#pragma unroll
-    for (int ms = 0; ms < MS; ++ms)
-#pragma unroll
-      for (int ns = 0; ns < 4; ++ns) {
-        int col = (ns < 2 ? t.n_lo : t.n_hi) + wn * 32 + (ns & 1) * 16 + lr;
-        bool colok = (ns < 2) || (t.n_hi != t.n_lo);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int tr = rbase + ms * 16 + 4 * lg + r;
-          if (tr < m && colok) P.y[(long)(row0 + tr) * P.N + col] = acc[ms][ns][r];
-        }
-      }
-    return;
-  } else {
-    // gate = ns 0,1 ; up = ns 2,3 (same h columns)
+  const bool hi_ok = G1 || t.n_hi != t.n_lo;
+  if constexpr (G1) {
+    // gate = ns 0,1 ; up = ns 2,3 (same h columns): global scales first
     float gsg = 1.0f, gsu = 1.0f;
     if (P.gscale) { gsg = P.gscale[2 * g]; gsu = P.gscale[2 * g + 1]; }
 #pragma unroll
@@ -215,39 +252,56 @@ __device__ __forceinline__ void tile_epilogue(const GemmParams& P, const Tile& t
           acc[ms][j][r] *= gsg;
           acc[ms][j + 2][r] *= gsu;
         }
-    if (P.z && g < P.lora_groups) {
-      // delta[row][n] = s * sum_q z[row][q] * B[g][n][q]; z staged as [q][BM]
-      float* sz = (float*)smem;
-      const int R = P.lora_rank;
-      for (int i = tid; i < R * BM; i += kThreads) {
-        int q = i / BM, tr = i - q * BM;
-        int rr = row0 + (tr < m ? tr : 0);
-        sz[q * BM + tr] = P.z[(long)rr * R + q];
-      }
-      __syncthreads();
-      const uint16_t* Bg = P.lora_B + (long)g * 2 * P.I * R;
-      for (int q = 0; q < R; ++q) {
-        float bgv[2], buv[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          int c = wn * 32 + j * 16 + lr;
-          bgv[j] = P.lora_scale * bf16_bits_to_f32(Bg[(long)(t.n_lo + c) * R + q]);
-          buv[j] = P.lora_scale * bf16_bits_to_f32(Bg[(long)(t.n_hi + c) * R + q]);
-        }
-#pragma unroll
-        for (int ms = 0; ms < MS; ++ms) {
-          f32x4 zq = *(const f32x4*)(sz + q * BM + rbase + ms * 16 + 4 * lg);
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              acc[ms][j][r] = fmaf(zq[r], bgv[j], acc[ms][j][r]);
-              acc[ms][j + 2][r] = fmaf(zq[r], buv[j], acc[ms][j + 2][r]);
-            }
-        }
-      }
-      __syncthreads();
+  }
+  if (P.z && g < P.lora_groups) {
+    // delta[row][n] = s * sum_q z[row][q] * B[g][n][q]; z staged as [q][BM]
+    float* sz = (float*)smem;
+    const int R = P.lora_rank;
+    for (int i = tid; i < R * BM; i += kThreads) {
+      int q = i / BM, tr = i - q * BM;
+      int rr = row0 + (tr < m ? tr : 0);
+      sz[q * BM + tr] = P.z[(long)rr * R + q];
     }
+    __syncthreads();
+    const uint16_t* Bg = P.lora_B + (long)g * P.N * R;
+    const int nhi = hi_ok ? t.n_hi : t.n_lo;      // an absent hi half is never stored
+    for (int q = 0; q < R; ++q) {
+      float bgv[2], buv[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        int c = wn * 32 + j * 16 + lr;
+        bgv[j] = P.lora_scale * bf16_bits_to_f32(Bg[(long)(t.n_lo + c) * R + q]);
+        buv[j] = P.lora_scale * bf16_bits_to_f32(Bg[(long)(nhi + c) * R + q]);
+      }
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms) {
+        f32x4 zq = *(const f32x4*)(sz + q * BM + rbase + ms * 16 + 4 * lg);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            acc[ms][j][r] = fmaf(zq[r], bgv[j], acc[ms][j][r]);
+            acc[ms][j + 2][r] = fmaf(zq[r], buv[j], acc[ms][j + 2][r]);
+          }
+      }
+    }
+    __syncthreads();
+  }
+  if constexpr (!G1) {
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+      for (int ns = 0; ns < 4; ++ns) {
+        int col = (ns < 2 ? t.n_lo : t.n_hi) + wn * 32 + (ns & 1) * 16 + lr;
+        bool colok = (ns < 2) || hi_ok;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          int tr = rbase + ms * 16 + 4 * lg + r;
+          if (tr < m && colok) P.y[(long)(row0 + tr) * P.N + col] = acc[ms][ns][r];
+        }
+      }
+    return;
+  } else {
     float hv[MS][2][4];
     const float L = P.limit, al = P.alpha, be = P.beta;
 #pragma unroll

@@ -103,6 +103,7 @@ __device__ __forceinline__ void fp8_epilogue(const GemmParams& P, const Tile& t,
   const int g = t.g, row0 = t.row0, m = t.m;
   if constexpr (!G1) {
     const bool hi_ok = t.n_hi != t.n_lo;
+    if (P.z && g < P.lora_groups) lora_delta_tile<BM>(P, t, acc, smem, hi_ok);   // down LoRA
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) {
       const int tr = 16 * ms + lr;
@@ -122,35 +123,7 @@ __device__ __forceinline__ void fp8_epilogue(const GemmParams& P, const Tile& t,
         acc[ms][0][r] *= gsg;
         acc[ms][1][r] *= gsu;
       }
-    if (P.z && g < P.lora_groups) {
-      // delta[row][n] = s * sum_q z[row][q] * B[g][n][q], z staged as [q][BM]
-      float* sz = (float*)smem;
-      const int R = P.lora_rank;
-      for (int i = tid; i < R * BM; i += kThreads) {
-        const int q = i / BM, tr = i - q * BM;
-        sz[q * BM + tr] = P.z[(long)(row0 + (tr < m ? tr : 0)) * R + q];
-      }
-      __syncthreads();
-      const uint16_t* Bg = P.lora_B + (long)g * 2 * P.I * R;
-      for (int q = 0; q < R; ++q) {
-        float bgv[4], buv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          bgv[r] = P.lora_scale * bf16_bits_to_f32(Bg[(long)(t.n_lo + c0 + r) * R + q]);
-          buv[r] = P.lora_scale * bf16_bits_to_f32(Bg[(long)(t.n_hi + c0 + r) * R + q]);
-        }
-#pragma unroll
-        for (int ms = 0; ms < MS; ++ms) {
-          const float zq = sz[q * BM + 16 * ms + lr];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            acc[ms][0][r] = fmaf(zq, bgv[r], acc[ms][0][r]);
-            acc[ms][1][r] = fmaf(zq, buv[r], acc[ms][1][r]);
-          }
-        }
-      }
-      __syncthreads();
-    }
+    if (P.z && g < P.lora_groups) lora_delta_tile<BM>(P, t, acc, smem, true);
     float hv[MS][4];
     const float L = P.limit, al = P.alpha, be = P.beta;
 #pragma unroll
@@ -162,6 +135,16 @@ __device__ __forceinline__ void fp8_epilogue(const GemmParams& P, const Tile& t,
         const float sg = __builtin_amdgcn_rcpf(1.0f + expf(-al * gg));
         hv[ms][r] = gg * sg * (uu + be);
       }
+    if (P.h_lora) {   // the down-LoRA input: h before the re-quantisation, bf16
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms) {
+        const int tr = 16 * ms + lr;
+        if (tr < m)
+          *(uint2*)(P.h_lora + (long)(row0 + tr) * P.I + t.nt * 128 + c0) =
+              (uint2){f32_to_bf16_bits(hv[ms][0]) | (f32_to_bf16_bits(hv[ms][1]) << 16),
+                      f32_to_bf16_bits(hv[ms][2]) | (f32_to_bf16_bits(hv[ms][3]) << 16)};
+      }
+    }
     // e4m3 re-quantisation per row and 128 columns: s = amax / 448, codes
     // round-to-nearest-even of h * (1 / s). Row amax: the lane's 4 columns,
     // the 4 lanes of the row (lane / 16), then the 8 waves through LDS.
@@ -452,6 +435,9 @@ __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, ui
     // acc[ms][ns][r]: row 16 ms + lr, column (ns ? hi : lo) + 16 wave + 4 lg + r
     const int c0 = 16 * wave + 4 * lg;
     const bool hi_ok = G1 || tl.n_hi != tl.n_lo;
+    // GEMM2's down-LoRA delta goes into the tile's first partial slot once
+    if (!G1 && slot == 0 && P.z && tl.g < P.lora_groups)
+      lora_delta_tile<BM>(P, tl, acc, smem, hi_ok);
     float* base = P.part + ((long)slot * P.p_rows + row0) * P.N;
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) {
@@ -629,6 +615,9 @@ __global__ __launch_bounds__(kThreads) void gemm1_sk_epilogue_kernel(GemmParams 
       const int v = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
       *(uint16_t*)(P.h + (long)r * I + c) = (uint16_t)v;
       if (lane == 0) P.hs[(long)r * NT + nt] = sc;
+      if (P.h_lora)
+        *(uint32_t*)(P.h_lora + (long)r * I + c) =
+            f32_to_bf16_bits(hv[0]) | (f32_to_bf16_bits(hv[1]) << 16);
     } else {
       *(uint32_t*)((uint16_t*)P.h + (long)r * I + c) =
           f32_to_bf16_bits(hv[0]) | (f32_to_bf16_bits(hv[1]) << 16);

@@ -95,6 +95,7 @@ __device__ __forceinline__ void int4_epilogue(const GemmParams& P, const Tile& t
   const int g = t.g, row0 = t.row0, m = t.m;
   if constexpr (!G1) {
     const bool hi_ok = t.n_hi != t.n_lo;
+    if (P.z && g < P.lora_groups) lora_delta_tile<BM>(P, t, acc, smem, hi_ok);   // down LoRA
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) {
       const int tr = 16 * ms + lr;
@@ -115,35 +116,7 @@ __device__ __forceinline__ void int4_epilogue(const GemmParams& P, const Tile& t
           acc[ms][1][r] *= gsu;
         }
     }
-    if (P.z && g < P.lora_groups) {
-      // delta[row][n] = s * sum_q z[row][q] * B[g][n][q], z staged as [q][BM]
-      float* sz = (float*)smem;
-      const int R = P.lora_rank;
-      for (int i = tid; i < R * BM; i += kThreads) {
-        const int q = i / BM, tr = i - q * BM;
-        sz[q * BM + tr] = P.z[(long)(row0 + (tr < m ? tr : 0)) * R + q];
-      }
-      __syncthreads();
-      const uint16_t* Bg = P.lora_B + (long)g * 2 * P.I * R;
-      for (int q = 0; q < R; ++q) {
-        float bgv[4], buv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          bgv[r] = P.lora_scale * bf16_bits_to_f32(Bg[(long)(t.n_lo + c0 + r) * R + q]);
-          buv[r] = P.lora_scale * bf16_bits_to_f32(Bg[(long)(t.n_hi + c0 + r) * R + q]);
-        }
-#pragma unroll
-        for (int ms = 0; ms < MS; ++ms) {
-          const float zq = sz[q * BM + 16 * ms + lr];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            acc[ms][0][r] = fmaf(zq, bgv[r], acc[ms][0][r]);
-            acc[ms][1][r] = fmaf(zq, buv[r], acc[ms][1][r]);
-          }
-        }
-      }
-      __syncthreads();
-    }
+    if (P.z && g < P.lora_groups) lora_delta_tile<BM>(P, t, acc, smem, true);
     const float L = P.limit, al = P.alpha, be = P.beta;
     uint16_t* h = (uint16_t*)P.h;
 #pragma unroll
@@ -334,6 +307,9 @@ __device__ __forceinline__ void int4_tile(const GemmParams& P, const Tile& tl, u
   if constexpr (PART) {
     const int c0 = 16 * wave + 4 * lg;
     const bool hi_ok = G1 || tl.n_hi != tl.n_lo;
+    // GEMM2's down-LoRA delta goes into the tile's first partial slot once
+    if (!G1 && slot == 0 && P.z && tl.g < P.lora_groups)
+      lora_delta_tile<BM>(P, tl, acc, smem, hi_ok);
     float* base = P.part + ((long)slot * P.p_rows + row0) * P.N;
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) {

@@ -51,7 +51,9 @@ hipError_t launch_quant_act(const void* x, long T, int H, void* xq, float* xs,
                             hipStream_t s);
 
 // z[r][q] = sum_h x[t(r)][h] * A[g(r)][q][h] for every sorted row of a
-// local group (fp32)
+// local group (fp32); t(r) = sorted_pair[r] / top_k, or r itself when
+// sorted_pair is NULL (x then holds one row per sorted row, e.g. the
+// down-LoRA input, and H is its length I)
 hipError_t launch_lora_z(const void* x_bf16, const void* A, int rank, long T,
                          int H, int top_k, int n_lora_groups, long p_cap,
                          const int* offsets, const int* sorted_pair, float* z,
@@ -94,6 +96,7 @@ struct Gemm1Args {
   float* hs;
   float* part;           // split-K partials (when splitk_use) or NULL
   void* x16;             // INT4: f16 activations (T * H * 2 bytes) or NULL
+  void* h_lora;          // FP8: bf16 SwiGLU output before the requant, or NULL
 };
 hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t s);
 
@@ -108,6 +111,11 @@ struct Gemm2Args {
   const int* offsets;
   float* y;              // [p_cap][H] fp32, or the split-K partials
   int* sk_grid;          // out: split-K kernel grid (0 = plain kernel)
+  // down-projection LoRA (nullable z): y += scale * z[row] . B[g][n]
+  const float* z;        // [p_cap][rank]
+  const void* lora_B;    // bf16 [G_lora][H][rank]
+  int lora_rank, lora_groups;
+  float lora_scale;
 };
 hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t s);
 

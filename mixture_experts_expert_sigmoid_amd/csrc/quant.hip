@@ -130,7 +130,9 @@ __global__ __launch_bounds__(256) void lora_z_kernel(
   const int wave = threadIdx.x >> 6, lane = lane_id(), lr = lane & 15, lg = lane >> 4;
   const int hq = H >> 2;                         // this wave's quarter of H
   const long rl = r0 + min(lr, m - 1);           // this lane's operand row
-  const uint16_t* xr = x + (long)(sorted_pair[rl] / top_k) * H + wave * hq + 8 * lg;
+  // operand row: the token of the pair (gathered x), or the sorted row itself
+  const long src = sorted_pair ? (long)(sorted_pair[rl] / top_k) : rl;
+  const uint16_t* xr = x + src * H + wave * hq + 8 * lg;
   const uint16_t* Ag = A + (long)g * rank * H + wave * hq + 8 * lg;
   f32x4 acc[NQ];
 #pragma unroll

@@ -504,13 +504,14 @@ def expert_ffn(spec, arr, e, xhat_rows, x_bf16_rows, detail=False):
     err_h = ACC_REL * (dg * mag[:, :I] + du * mag[:, I:]) + EVAL_REL * np.abs(h)
     alt = rounding_alternatives(h, err_h, spec.fmt)
     y_allow = alt @ np.abs(w2).T
+    alt_l = None
     if down:   # boundary decisions of the bf16 down-LoRA input
         alt_l = rounding_alternatives(h, err_h, "bf16")
         A2 = np.abs(bf16_decode(arr["lora_A2"][e]))
         B2 = np.abs(bf16_decode(arr["lora_B2"][e]))
         y_allow = y_allow + abs(spec.lora_scale) * ((alt_l @ A2.T) @ B2.T)
     return y, dict(h=h, hhat=hhat, alt=alt, y_allow=y_allow,
-                   n_boundary=int(np.count_nonzero(alt)))
+                   n_boundary=int(np.count_nonzero(alt)), alt_lora=alt_l)
 
 
 def gemm1_input(spec, x_bits):

@@ -29,7 +29,8 @@ def module_for(spec: LayerSpec, layer: Layer, **over) -> M.MoeModule:
         route_scale=spec.route_scale, global_scale=spec.global_scale,
         shared_w=spec.shared_w, alpha=spec.alpha, beta=spec.beta,
         limit=spec.limit, lora_A=_dev(layer.lora_A), lora_B=_dev(layer.lora_B),
-        lora_scale=spec.lora_scale)
+        lora_scale=spec.lora_scale, lora_A2=_dev(layer.lora_A2),
+        lora_B2=_dev(layer.lora_B2))
     kw.update(over)
     return M.MoeModule(**kw)
 

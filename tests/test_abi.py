@@ -100,9 +100,9 @@ def test_gemm_validation():
     L = M.lib()
     act = M.act_params(1.0, 0.0, math.inf)
     w = _w(N=2 * 128, K=256)
-    g1 = lambda w_, act_, H=256, I=128, lora=None: L.moe_grouped_gemm1_act(
+    g1 = lambda w_, act_, H=256, I=128, lora=None, hl=None: L.moe_grouped_gemm1_act(
         ctypes.byref(w_), 1, 1, None, 4, H, I, 2, 8, 1, 1, ctypes.byref(act_),
-        lora, 1, 1, ctypes.c_void_p(1), 1 << 20, None)
+        lora, 1, 1, hl, ctypes.c_void_p(1), 1 << 20, None)
     assert g1(_w(N=256, K=250), act, H=250) == -2        # H % 128
     assert g1(_w(N=256, K=256), act, H=256, I=100) == -2   # I % 128
     assert g1(_w(N=512, K=256), act) == -2               # N != 2I
@@ -114,20 +114,29 @@ def test_gemm_validation():
     assert g1(w, M.act_params(1.0, math.nan, 7.0)) == -5
     lo = M.MoeLora(64, 4, 1.0, 1, 1)
     assert g1(w, act, lora=ctypes.pointer(lo)) == -2      # rank > 32
+    # the bf16 down-LoRA input is an FP8-only output of GEMM1
+    assert g1(_w(fmt=M.MOE_W_BF16, N=256, K=256), act, hl=ctypes.c_void_p(256)) == -5
     w2 = _w(N=256, K=128)
-    out = L.moe_grouped_gemm2_combine(ctypes.byref(w2), 1, 1, 4, 256, 128, 2, 0, 8,
-                                      1, 1, 1, 1.0, 1, None, 0, None)
-    assert out == -6                                     # workspace
-    assert L.moe_gemm2_workspace_size(ctypes.byref(w2), 100) >= 100 * 256 * 4
-    assert L.moe_gemm2_workspace_size(None, 100) == 0
+    g2 = lambda hl=None, ld=None, ws=None, nb=0: L.moe_grouped_gemm2_combine(
+        ctypes.byref(w2), 1, 1, hl, ld, 4, 256, 128, 2, 0, 8, 1, 1, 1, 1.0, 1, ws, nb,
+        None)
+    assert g2() == -6                                    # workspace
+    ld = M.MoeLora(16, 4, 1.0, 1, 1)
+    assert g2(ld=ctypes.pointer(ld), ws=ctypes.c_void_p(256), nb=1 << 30) == -1  # no h_lora
+    assert g2(ld=ctypes.pointer(M.MoeLora(40, 4, 1.0, 1, 1)), hl=ctypes.c_void_p(256),
+              ws=ctypes.c_void_p(256), nb=1 << 30) == -2  # rank > 32
+    assert L.moe_gemm2_workspace_size(ctypes.byref(w2), 100, None) >= 100 * 256 * 4
+    assert (L.moe_gemm2_workspace_size(ctypes.byref(w2), 100, ctypes.pointer(ld)) -
+            L.moe_gemm2_workspace_size(ctypes.byref(w2), 100, None)) >= 100 * 16 * 4
+    assert L.moe_gemm2_workspace_size(None, 100, None) == 0
     # FP8 at decode sizes (few tiles for the CUs): room for the split-K
     # partial sums; at large p_cap plain rows only
     w13f = _w(fmt=M.MOE_W_FP8_B128, G=289, N=4096, K=6144)      # 9 x 16 tiles
     assert L.moe_gemm1_workspace_size(ctypes.byref(w13f), 9, None) >= 4 * 9 * 4096 * 4
     assert L.moe_gemm1_workspace_size(ctypes.byref(w13f), 36864, None) == 0
     w2f = _w(fmt=M.MOE_W_FP8_B128, G=128, N=3072, K=1536)       # 4 x 12 tiles
-    assert L.moe_gemm2_workspace_size(ctypes.byref(w2f), 4) >= 4 * 4 * 3072 * 4
-    assert L.moe_gemm2_workspace_size(ctypes.byref(w2f), 16384) == 16384 * 3072 * 4
+    assert L.moe_gemm2_workspace_size(ctypes.byref(w2f), 4, None) >= 4 * 4 * 3072 * 4
+    assert L.moe_gemm2_workspace_size(ctypes.byref(w2f), 16384, None) == 16384 * 3072 * 4
     w13b = _w(fmt=M.MOE_W_BF16, G=289, N=4096, K=6144)
     assert L.moe_gemm1_workspace_size(ctypes.byref(w13b), 9, None) == 0   # BF16: none
     assert L.moe_gemm1_workspace_size(None, 9, None) == 0

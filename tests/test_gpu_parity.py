@@ -234,12 +234,19 @@ def _stepwise(spec, mod, batch, T):
         hs = None
     ws1 = torch.empty(max(M.moe_gemm1_workspace_size(mod.w13, pc, mod.lora), 1),
                       dtype=torch.uint8, device="cuda")
+    # the down-LoRA input: FP8 layers write it beside the codes, the others
+    # read h itself
+    h_lora = None
+    if mod.lora_down is not None:
+        h_lora = torch.zeros(pc, I, dtype=torch.bfloat16, device="cuda") if fp8 else h
     M.moe_grouped_gemm1_act(mod.w13, xin, xs, x, T, H, I, k, pc, offsets, sp, mod.act,
-                            mod.lora, h, hs, ws1)
+                            mod.lora, h, hs, ws1, h_lora=h_lora if fp8 else None)
     out = torch.empty(T, H, device="cuda")
-    ws2 = torch.empty(M.moe_gemm2_workspace_size(mod.w2, pc), dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty(M.moe_gemm2_workspace_size(mod.w2, pc, mod.lora_down),
+                      dtype=torch.uint8, device="cuda")
     M.moe_grouped_gemm2_combine(mod.w2, h, hs, T, H, I, k, spec.shared, pc, offsets, pr,
-                                w, spec.shared_w, out, ws2)
+                                w, spec.shared_w, out, ws2, h_lora=h_lora,
+                                lora_down=mod.lora_down)
     torch.cuda.synchronize()
     assert M.moe_read_device_error(err) == 0
     if fp8:
@@ -248,7 +255,9 @@ def _stepwise(spec, mod, batch, T):
     else:
         hval = h.float().cpu().numpy().astype(np.float64)
     return dict(out=out, offsets=offsets.cpu().numpy(), sp=sp.cpu().numpy(),
-                hval=hval, hs=None if hs is None else hs.cpu().numpy())
+                hval=hval, hs=None if hs is None else hs.cpu().numpy(),
+                h_lora=None if h_lora is None or not fp8
+                else h_lora.float().cpu().numpy().astype(np.float64))
 
 
 @pytest.mark.parametrize("name", ["tiny_bf16", "fp8_clamp_small", "fp8_oai_small",
@@ -282,6 +291,12 @@ def test_gemm1_h_codes(name):
                  f"alt={det['alt'][i, j]!r}")
         n_bnd += det["n_boundary"]
         n_tot += diff.size
+        if r["h_lora"] is not None and det["alt_lora"] is not None:
+            # the FP8 layer's bf16 down-LoRA input: the bf16 rounding of the
+            # exact h, either neighbour at a boundary
+            dl = np.abs(r["h_lora"][rows] - O.down_lora_input(det["h"]))
+            bad_l = dl > det["alt_lora"] * (1 + 1e-5)
+            n_bad += int(np.count_nonzero(bad_l))
     _log(f"  h elements={n_tot} boundary={n_bnd} outside-admissible={n_bad}")
     assert n_bad == 0
 
