@@ -94,8 +94,9 @@ def dense_weight(fmt, q, s, N, K, gsc=None):
     return W
 
 
-def layer(spec, arr, x_bits, logits):
-    """out[t][h] for every token, float64 Python lists."""
+def layer(spec, arr, x_bits, logits, adapter_ids=None):
+    """out[t][h] for every token, float64 Python lists. adapter_ids [T]
+    (a batch of adapters): each token's LoRA adapter, -1 for none."""
     T = len(x_bits)
     H, I, k = spec.H, spec.I, spec.top_k
     f32 = lambda v: float(torch.tensor(v, dtype=torch.float32))
@@ -129,9 +130,12 @@ def layer(spec, arr, x_bits, logits):
                           None if arr["w2_s"] is None else arr["w2_s"][e], H, I)
         for t in range(T):
             gu = [sum(xin[t][kk] * W13[n][kk] for kk in range(H)) for n in range(2 * I)]
-            if spec.lora_rank and e < spec.n_local:
-                A = arr["lora_A"][e]
-                B = arr["lora_B"][e]
+            a = 0 if adapter_ids is None else int(adapter_ids[t])
+            pick = lambda name: arr[name][e] if spec.n_adapters == 1 else arr[name][a][e]
+            has_lora = spec.lora_rank and e < spec.n_local and 0 <= a < spec.n_adapters
+            if has_lora:
+                A = pick("lora_A")
+                B = pick("lora_B")
                 r = spec.lora_rank
                 z = [sum(x[t][kk] * bf16_bits_value(int(A[q][kk])) for kk in range(H))
                      for q in range(r)]
@@ -144,10 +148,10 @@ def layer(spec, arr, x_bits, logits):
                 u = max(min(gu[I + n], L), -L)
                 h.append(g * _sig(alpha * g) * (u + beta))
             dn = None
-            if spec.lora_rank and spec.lora_down and e < spec.n_local:
+            if has_lora and spec.lora_down:
                 # down LoRA on the true-units SwiGLU output, bf16-rounded
-                A2 = arr["lora_A2"][e]
-                B2 = arr["lora_B2"][e]
+                A2 = pick("lora_A2")
+                B2 = pick("lora_B2")
                 hl = [bf16_nearest(v) for v in h]
                 z2 = [sum(hl[n] * bf16_bits_value(int(A2[q][n])) for n in range(I))
                       for q in range(spec.lora_rank)]

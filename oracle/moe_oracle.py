@@ -375,13 +375,39 @@ def w13_dequant(spec, arr, e):
     return w
 
 
-def lora_delta(spec, arr, e, x_bf16_rows):
+def lora_mat(spec, arr, name, a, e):
+    """Adapter a's matrix of group e: arrays are [G, ...] for one adapter and
+    [n_adapters, G, ...] for a batch of adapters."""
+    return arr[name][e] if spec.n_adapters == 1 else arr[name][a][e]
+
+
+def _per_adapter(spec, rows, adapters, fn):
+    """fn(a, row_selection) for every adapter a >= 0 that some row uses;
+    rows whose adapter is -1 (or out of range) get no delta (zero rows)."""
+    m = rows.shape[0]
+    ad = np.zeros(m, np.int64) if adapters is None else np.asarray(adapters, np.int64)
+    out = None
+    for a in np.unique(ad):
+        if a < 0 or a >= spec.n_adapters:
+            continue
+        sel = ad == a
+        d = fn(int(a), sel)
+        if out is None:
+            out = np.zeros((m, d.shape[1]))
+        out[sel] = d
+    return out
+
+
+def lora_delta(spec, arr, e, x_bf16_rows, adapters=None):
     """Rank-r delta on [gate | up] in true units: z = x A_e^T (kept in full
-    precision), delta = lora_scale * z B_e^T, shape [m, 2I]."""
-    A = bf16_decode(arr["lora_A"][e])              # [r, H]
-    B = bf16_decode(arr["lora_B"][e])              # [2I, r]
-    z = x_bf16_rows @ A.T
-    return float(np.float32(spec.lora_scale)) * (z @ B.T)
+    precision), delta = lora_scale * z B_e^T, shape [m, 2I]; with a batch of
+    adapters each row uses its token's adapter (none: zero)."""
+    def one(a, sel):
+        A = bf16_decode(lora_mat(spec, arr, "lora_A", a, e))    # [r, H]
+        B = bf16_decode(lora_mat(spec, arr, "lora_B", a, e))    # [2I, r]
+        return float(np.float32(spec.lora_scale)) * ((x_bf16_rows[sel] @ A.T) @ B.T)
+    d = _per_adapter(spec, x_bf16_rows, adapters, one)
+    return np.zeros((x_bf16_rows.shape[0], 2 * spec.I)) if d is None else d
 
 
 def down_lora_input(h):
@@ -391,14 +417,17 @@ def down_lora_input(h):
     return bf16_round(h)
 
 
-def down_lora_delta(spec, arr, e, h_lora_rows):
+def down_lora_delta(spec, arr, e, h_lora_rows, adapters=None):
     """Rank-r delta on the down projection: z2 = h_lora A2_e^T (full
     precision), delta = lora_scale * z2 B2_e^T, shape [m, H]; added to the
-    expert's output row before the routing-weighted combine."""
-    A2 = bf16_decode(arr["lora_A2"][e])            # [r, I]
-    B2 = bf16_decode(arr["lora_B2"][e])            # [H, r]
-    z2 = h_lora_rows @ A2.T
-    return float(np.float32(spec.lora_scale)) * (z2 @ B2.T)
+    expert's output row before the routing-weighted combine. Per-row
+    adapters as in lora_delta."""
+    def one(a, sel):
+        A2 = bf16_decode(lora_mat(spec, arr, "lora_A2", a, e))  # [r, I]
+        B2 = bf16_decode(lora_mat(spec, arr, "lora_B2", a, e))  # [H, r]
+        return float(np.float32(spec.lora_scale)) * ((h_lora_rows[sel] @ A2.T) @ B2.T)
+    d = _per_adapter(spec, h_lora_rows, adapters, one)
+    return np.zeros((h_lora_rows.shape[0], spec.H)) if d is None else d
 
 
 # ----------------------------------------------------------------------------
@@ -468,10 +497,11 @@ def rounding_alternatives(h, err_h, fmt, group=128):
     return np.where(dist <= e, ulp + 2.0 * e, 0.0)
 
 
-def expert_ffn(spec, arr, e, xhat_rows, x_bf16_rows, detail=False):
+def expert_ffn(spec, arr, e, xhat_rows, x_bf16_rows, detail=False, adapters=None):
     """y = round_h(swiglu(g, u)) W2_e^T for the rows of one group.
     xhat_rows are the GEMM1 input values (fp8-dequantised for FP8 layers,
-    the bf16 values otherwise); x_bf16_rows feed the LoRA input.
+    the bf16 values otherwise); x_bf16_rows feed the LoRA input; adapters
+    (per row, with a batch of adapters) select each row's adapter.
     detail=True also returns the bound on y from boundary rounding decisions
     of h (see rounding_alternatives) and the intermediates."""
     I = spec.I
@@ -480,7 +510,7 @@ def expert_ffn(spec, arr, e, xhat_rows, x_bf16_rows, detail=False):
     g, u = gu[:, :I].copy(), gu[:, I:].copy()
     lora = spec.lora_rank and e < spec.n_local
     if lora:
-        d = lora_delta(spec, arr, e, x_bf16_rows)
+        d = lora_delta(spec, arr, e, x_bf16_rows, adapters)
         g += d[:, :I]
         u += d[:, I:]
     f32 = lambda v: float(np.float32(v))
@@ -492,14 +522,18 @@ def expert_ffn(spec, arr, e, xhat_rows, x_bf16_rows, detail=False):
     y = hhat @ w2.T                                # [m, H]
     down = lora and spec.lora_down
     if down:
-        y = y + down_lora_delta(spec, arr, e, down_lora_input(h))
+        y = y + down_lora_delta(spec, arr, e, down_lora_input(h), adapters)
     if not detail:
         return y
     mag = np.abs(xhat_rows) @ np.abs(w13).T
     if lora:
-        A = np.abs(bf16_decode(arr["lora_A"][e]))
-        B = np.abs(bf16_decode(arr["lora_B"][e]))
-        mag = mag + abs(spec.lora_scale) * ((np.abs(x_bf16_rows) @ A.T) @ B.T)
+        def mag_one(a, sel):
+            A = np.abs(bf16_decode(lora_mat(spec, arr, "lora_A", a, e)))
+            B = np.abs(bf16_decode(lora_mat(spec, arr, "lora_B", a, e)))
+            return abs(spec.lora_scale) * ((np.abs(x_bf16_rows[sel]) @ A.T) @ B.T)
+        mm = _per_adapter(spec, x_bf16_rows, adapters, mag_one)
+        if mm is not None:
+            mag = mag + mm
     dg, du = swiglu_slopes(g, u, al, be, L)
     err_h = ACC_REL * (dg * mag[:, :I] + du * mag[:, I:]) + EVAL_REL * np.abs(h)
     alt = rounding_alternatives(h, err_h, spec.fmt)
@@ -507,9 +541,14 @@ def expert_ffn(spec, arr, e, xhat_rows, x_bf16_rows, detail=False):
     alt_l = None
     if down:   # boundary decisions of the bf16 down-LoRA input
         alt_l = rounding_alternatives(h, err_h, "bf16")
-        A2 = np.abs(bf16_decode(arr["lora_A2"][e]))
-        B2 = np.abs(bf16_decode(arr["lora_B2"][e]))
-        y_allow = y_allow + abs(spec.lora_scale) * ((alt_l @ A2.T) @ B2.T)
+
+        def allow_one(a, sel):
+            A2 = np.abs(bf16_decode(lora_mat(spec, arr, "lora_A2", a, e)))
+            B2 = np.abs(bf16_decode(lora_mat(spec, arr, "lora_B2", a, e)))
+            return abs(spec.lora_scale) * ((alt_l[sel] @ A2.T) @ B2.T)
+        ya = _per_adapter(spec, alt_l, adapters, allow_one)
+        if ya is not None:
+            y_allow = y_allow + ya
     return y, dict(h=h, hhat=hhat, alt=alt, y_allow=y_allow,
                    n_boundary=int(np.count_nonzero(alt)), alt_lora=alt_l)
 
@@ -525,7 +564,7 @@ def gemm1_input(spec, x_bits):
 
 
 def moe_layer(spec, arr, x_bits, logits, tokens=None, routing=None,
-              with_allowance=False):
+              with_allowance=False, adapter_ids=None):
     """Output rows out[t, :] (float64) for the tokens asked for (all by
     default): route, rebase, per-expert FFN, then for each token
     sum_j w[t, j] y[t, j] over its local slots in ascending j, plus
@@ -533,7 +572,9 @@ def moe_layer(spec, arr, x_bits, logits, tokens=None, routing=None,
     arrays (a dict of full arrays, or lazy accessors).
     with_allowance=True also returns, per output element, the largest change
     that boundary rounding decisions of h (either neighbour admissible) can
-    make: sum_j |w[t, j]| * |alt_h| |W2|^T, and the count of such elements."""
+    make: sum_j |w[t, j]| * |alt_h| |W2|^T, and the count of such elements.
+    adapter_ids [T] (a batch of adapters): each token's LoRA adapter, -1 for
+    none."""
     T = x_bits.shape[0]
     if routing is None:
         routing = route(logits, spec.n_routed, spec.n_sink, spec.top_k,
@@ -553,13 +594,15 @@ def moe_layer(spec, arr, x_bits, logits, tokens=None, routing=None,
     n_boundary = 0
     for e in sorted(pairs):
         rows = [i for i, _ in pairs[e]]
+        ad = None if adapter_ids is None else np.asarray(adapter_ids)[tokens[rows]]
         if with_allowance:
-            y, det = expert_ffn(spec, arr, e, xhat[rows], xb[rows], detail=True)
+            y, det = expert_ffn(spec, arr, e, xhat[rows], xb[rows], detail=True,
+                                adapters=ad)
             n_boundary += det["n_boundary"]
             for (i, j), arow in zip(pairs[e], det["y_allow"]):
                 allow[(i, j)] = arow
         else:
-            y = expert_ffn(spec, arr, e, xhat[rows], xb[rows])
+            y = expert_ffn(spec, arr, e, xhat[rows], xb[rows], adapters=ad)
         for (i, j), yrow in zip(pairs[e], y):
             contrib[(i, j)] = yrow
     out = np.zeros((len(tokens), spec.H))

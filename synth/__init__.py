@@ -59,6 +59,7 @@ class LayerSpec:
     lora_rank: int = 0
     lora_scale: float = 1.0
     lora_down: bool = False  # the same adapter also carries a down-projection LoRA
+    n_adapters: int = 1      # a batch of adapters: per-token ids in [-1, n_adapters)
     gscale: bool = False     # per-expert (gate, up) global scales
     logits: str = "normal"   # normal | skewed | router | mix258
     w13_std: Optional[float] = None
@@ -145,6 +146,7 @@ class Batch:
     T: int
     x: torch.Tensor        # [T, H] bf16
     logits: torch.Tensor   # [T, n_routed + n_sink] f32
+    adapter_ids: Optional[torch.Tensor] = None   # [T] int32 (a batch of adapters)
 
 
 def _rand_weights(spec: LayerSpec, N: int, K: int, std: float, gen, device,
@@ -186,15 +188,18 @@ def make_layer(spec: LayerSpec, device="cpu") -> Layer:
         c, d = _rand_weights(spec, H, I, std2, g, device)
         q13.append(a); s13.append(b); q2.append(c); s2.append(d)
     st = lambda xs: None if xs[0] is None else torch.stack(xs).contiguous()
+    # a batch of adapters stacks them first: [n_adapters, G, ...]
+    na = spec.n_adapters
+    lead = (G,) if na == 1 else (na, G)
     lora_A = lora_B = None
     if spec.lora_rank:
         r = spec.lora_rank
         g = _gen(device, spec.cfg_id, 7002)
-        lora_A = (torch.randn(G, r, H, generator=g, device=device)
+        lora_A = (torch.randn(*lead, r, H, generator=g, device=device)
                   / math.sqrt(H)).to(torch.bfloat16)
         # RMS(x.A^T) ~ 1 and RMS(g) ~ 4 (std13 * sqrt(H)); B std 0.5 gives
         # RMS(delta) ~ sqrt(r) * 0.5 = 2 ~ 0.5 * RMS(g).
-        lora_B = (torch.randn(G, 2 * I, r, generator=g, device=device)
+        lora_B = (torch.randn(*lead, 2 * I, r, generator=g, device=device)
                   * 0.5).to(torch.bfloat16)
     w_router = None
     if spec.logits == "router":
@@ -207,9 +212,9 @@ def make_layer(spec: LayerSpec, device="cpu") -> Layer:
         g = _gen(device, spec.cfg_id, 7006)
         # RMS(h A2^T) ~ RMS(h) ~ RMS(y); B2 std 0.5 / sqrt(r) gives a delta
         # of about half the base down-projection output
-        lora_A2 = (torch.randn(G, r, I, generator=g, device=device)
+        lora_A2 = (torch.randn(*lead, r, I, generator=g, device=device)
                    / math.sqrt(I)).to(torch.bfloat16)
-        lora_B2 = (torch.randn(G, H, r, generator=g, device=device)
+        lora_B2 = (torch.randn(*lead, H, r, generator=g, device=device)
                    * (0.5 / math.sqrt(r))).to(torch.bfloat16)
     return Layer(spec, st(q13), st(s13), st(q2), st(s2), gs, lora_A, lora_B,
                  w_router, lora_A2, lora_B2)
@@ -264,7 +269,13 @@ def make_batch(spec: LayerSpec, layer: Optional[Layer], T: int,
         lg = _logits_mix258(spec, T, g, device)
     else:
         lg = torch.randn(T, N + S, generator=g, device=device)
-    return Batch(T, x.contiguous(), lg.float().contiguous())
+    ad = None
+    if spec.lora_rank and spec.n_adapters > 1:
+        # each token picks one of the adapters or none (-1), uniformly
+        ga = _gen(device, spec.cfg_id, T, 13 + seed_extra)
+        ad = (torch.randint(0, spec.n_adapters + 1, (T,), generator=ga, device=device)
+              - 1).to(torch.int32).contiguous()
+    return Batch(T, x.contiguous(), lg.float().contiguous(), ad)
 
 
 @dataclasses.dataclass
@@ -313,4 +324,6 @@ def to_numpy_batch(batch: Batch) -> dict:
         "x_bits": batch.x.detach().cpu().contiguous().view(torch.int16)
                   .numpy().view(np.uint16),
         "logits": batch.logits.detach().cpu().numpy(),
+        "adapter_ids": (None if batch.adapter_ids is None
+                        else batch.adapter_ids.detach().cpu().numpy()),
     }

@@ -62,10 +62,10 @@ def _oracle_and_brute(spec, T, mutate=None, monkeypatch=None):
     batch = make_batch(spec, layer, T)
     arr = to_numpy_layer(layer)
     nb = to_numpy_batch(batch)
-    ref = np.array(brute.layer(spec, arr, nb["x_bits"], nb["logits"]))
+    ref = np.array(brute.layer(spec, arr, nb["x_bits"], nb["logits"], nb["adapter_ids"]))
     if mutate is not None:
         mutate(monkeypatch)
-    ours = O.moe_layer(spec, arr, nb["x_bits"], nb["logits"])
+    ours = O.moe_layer(spec, arr, nb["x_bits"], nb["logits"], adapter_ids=nb["adapter_ids"])
     if monkeypatch is not None:
         monkeypatch.undo()
     return ours, ref
@@ -176,12 +176,12 @@ def _mut_down_input_gate_units(mp):
     """The pre-fix units: the up half (and so h and the down-LoRA input)
     left off by gate/up."""
     real = O.down_lora_delta
-    mp.setattr(O, "down_lora_delta", lambda spec, arr, e, hl: real(
-        spec, arr, e, hl * (float(arr["gs"][e][0]) / float(arr["gs"][e][1]))))
+    mp.setattr(O, "down_lora_delta", lambda spec, arr, e, hl, adapters=None: real(
+        spec, arr, e, hl * (float(arr["gs"][e][0]) / float(arr["gs"][e][1])), adapters))
 
 
 def _mut_down_dropped(mp):
-    mp.setattr(O, "down_lora_delta", lambda spec, arr, e, hl: 0.0)
+    mp.setattr(O, "down_lora_delta", lambda spec, arr, e, hl, adapters=None: 0.0)
 
 
 @pytest.mark.parametrize("mut", [_mut_down_input_after_requant, _mut_down_input_gate_units,
@@ -222,8 +222,8 @@ def test_lora_old_units_bug_is_caught(monkeypatch):
     spec, layer, arr, nb = _lora_setup()
     real = O.lora_delta
 
-    def buggy(spec_, arr_, e, xrows):
-        d = real(spec_, arr_, e, xrows)
+    def buggy(spec_, arr_, e, xrows, adapters=None):
+        d = real(spec_, arr_, e, xrows, adapters)
         gs = arr_["gs"][e].astype(np.float64)
         d[:, spec_.I:] *= gs[1] / gs[0]
         return d
@@ -277,3 +277,35 @@ def test_allowance_is_zero_or_small_and_value_unchanged():
     assert np.all(allow >= 0)
     # boundary decisions are rare for an fp32-accurate kernel
     assert nbnd <= 0.01 * 5 * 3 * spec.I
+
+
+# ------------------------------------------------------ a batch of adapters
+
+def test_adapter_batch_matches_brute_force_and_single_adapter_runs():
+    """Eight adapters, tokens picking one or none: the oracle equals the
+    brute force (in test_oracle_layer_matches_brute_force too); tokens of
+    adapter a give exactly the one-adapter layer built from adapter a's
+    matrices; tokens with no adapter give the base layer."""
+    spec = TINY["ep_lora_multi"]
+    layer = make_layer(spec)
+    batch = make_batch(spec, layer, 12)
+    arr, nb = to_numpy_layer(layer), to_numpy_batch(batch)
+    ad = nb["adapter_ids"]
+    assert (ad == -1).any() and len(set(ad.tolist())) >= 4
+    out = O.moe_layer(spec, arr, nb["x_bits"], nb["logits"], adapter_ids=ad)
+    one = spec.scaled(n_adapters=1)
+    base = O.moe_layer(one.scaled(lora_rank=0), arr, nb["x_bits"], nb["logits"])
+    for a in sorted(set(ad.tolist())):
+        sel = ad == a
+        if a < 0:
+            np.testing.assert_array_equal(out[sel], base[sel])
+            continue
+        arr_a = dict(arr, **{k: arr[k][a] for k in ("lora_A", "lora_B", "lora_A2", "lora_B2")})
+        ref = O.moe_layer(one, arr_a, nb["x_bits"], nb["logits"])
+        np.testing.assert_array_equal(out[sel], ref[sel])
+    # a wrong adapter for one token is seen
+    bad = ad.copy()
+    i = int(np.nonzero(ad >= 0)[0][0])
+    bad[i] = (ad[i] + 1) % spec.n_adapters
+    out_bad = O.moe_layer(spec, arr, nb["x_bits"], nb["logits"], adapter_ids=bad)
+    assert np.max(np.abs(out_bad[i] - out[i])) > 1e-6 * np.abs(out).max()

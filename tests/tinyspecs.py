@@ -19,3 +19,6 @@ TINY = {
                          offset=2, lora_rank=4, gscale=True, logits="mix258",
                          route_scale=1.5, lora_down=True),
 }
+# eight adapters in one batch (tokens pick one or none)
+TINY["ep_lora_multi"] = TINY["ep_lora"].scaled(name="tiny_ep_lora_multi_t", cfg_id=106,
+                                               n_adapters=8)
