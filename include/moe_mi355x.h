@@ -100,7 +100,13 @@ typedef struct {
  * re-quantisation); z2 = h A2_e^T (fp32), y += scale * z2 B2_e^T, added to
  * the expert's output row before the routing-weighted combine.  A2: bf16
  * [n_groups][rank][I], B2: bf16 [n_groups][H][rank].
- * The shared expert (group E_loc) carries no LoRA. */
+ * The shared expert (group E_loc) carries no LoRA.
+ * A batch of adapters (n_adapters > 1; the page's harness serves eight
+ * rank-16 adapters at once): A and B gain a leading adapter dimension,
+ * [n_adapters][n_groups][...], and adapter_ids (device int32 [T], per call)
+ * gives each token's adapter; a token whose id is outside [0, n_adapters)
+ * gets no delta. n_adapters 0 or 1: one adapter for every token,
+ * adapter_ids unused. */
 typedef struct {
   int rank;             /* 1..32 */
   int n_groups;         /* adapters for groups 0..n_groups-1 (the local
@@ -108,6 +114,8 @@ typedef struct {
   float scale;
   const void *A;
   const void *B;
+  int n_adapters;       /* 0..1024 */
+  const int *adapter_ids;
 } moe_lora;
 
 /* ---------------------------------------------------------------- route -- */
@@ -249,15 +257,18 @@ size_t moe_gemm1_workspace_size(const moe_weights *w13, long p_cap,
  * for FP8 / INT4 weights at decode sizes their split-K partial sums
  * (4 * p_cap * H floats, reduced by the combine in a fixed order; the
  * down-LoRA delta enters the first partial of each tile), then the
- * down-LoRA z2 rows (p_cap * rank floats). Errors: NULL for a lora_down
- * without h_lora. Returns 0 for a NULL w2. */
+ * down-LoRA z2 rows (p_cap * rank floats, plus p_cap ints with a batch of
+ * adapters). sorted_pair (moe_permute's) is needed with lora_down only (it
+ * maps rows to tokens for the adapter ids). Errors: NULL for a lora_down
+ * without h_lora or sorted_pair. Returns 0 for a NULL w2. */
 int moe_grouped_gemm2_combine(const moe_weights *w2, const void *h,
                               const float *hs, const void *h_lora,
                               const moe_lora *lora_down, long T, int H, int I,
                               int top_k, int shared_expert, long p_cap,
-                              const int *offsets, const int *pair_row,
-                              const float *topk_w, float shared_w, float *out,
-                              void *ws, size_t ws_bytes, void *stream);
+                              const int *offsets, const int *sorted_pair,
+                              const int *pair_row, const float *topk_w,
+                              float shared_w, float *out, void *ws,
+                              size_t ws_bytes, void *stream);
 size_t moe_gemm2_workspace_size(const moe_weights *w2, long p_cap,
                                 const moe_lora *lora_down);
 

@@ -46,7 +46,8 @@ class MoeWeights(ctypes.Structure):
 
 class MoeLora(ctypes.Structure):
     _fields_ = [("rank", c_int), ("n_groups", c_int), ("scale", c_float),
-                ("A", c_void_p), ("B", c_void_p)]
+                ("A", c_void_p), ("B", c_void_p), ("n_adapters", c_int),
+                ("adapter_ids", c_void_p)]
 
 
 class MoeLayer(ctypes.Structure):
@@ -87,8 +88,8 @@ _SIGS = {
                                           c_void_p, POINTER(MoeLora),
                                           c_long, c_int, c_int, c_int, c_int,
                                           c_long, c_void_p, c_void_p, c_void_p,
-                                          c_float, c_void_p, c_void_p, c_size_t,
-                                          c_void_p]),
+                                          c_void_p, c_float, c_void_p, c_void_p,
+                                          c_size_t, c_void_p]),
     "moe_gemm2_workspace_size": (c_size_t, [POINTER(MoeWeights), c_long,
                                             POINTER(MoeLora)]),
     "moe_forward": (c_int, [POINTER(MoeLayer), c_void_p, c_void_p, c_long, c_long,
@@ -153,10 +154,15 @@ def act_params(alpha=1.0, beta=0.0, limit=math.inf) -> MoeActParams:
     return MoeActParams(alpha, beta, limit)
 
 
-def lora_desc(A: torch.Tensor, B: torch.Tensor, scale=1.0) -> MoeLora:
-    G, r, _ = A.shape
-    d = MoeLora(r, G, scale, A.data_ptr(), B.data_ptr())
-    d._keep = (A, B)
+def lora_desc(A: torch.Tensor, B: torch.Tensor, scale=1.0,
+              adapter_ids: Optional[torch.Tensor] = None) -> MoeLora:
+    """A [G][r][K] (one adapter) or [n_adapters][G][r][K] (a batch, with
+    per-token adapter_ids int32 [T] set here or per call)."""
+    na = 1 if A.dim() == 3 else A.shape[0]
+    G, r = A.shape[-3], A.shape[-2]
+    d = MoeLora(r, G, scale, A.data_ptr(), B.data_ptr(), na,
+                None if adapter_ids is None else adapter_ids.data_ptr())
+    d._keep = (A, B, adapter_ids)
     return d
 
 
@@ -250,11 +256,11 @@ def moe_gemm2_workspace_size(w2: MoeWeights, p_cap,
 def moe_grouped_gemm2_combine(w2: MoeWeights, h, hs, T, H, I, top_k,
                               shared_expert, p_cap, offsets, pair_row, topk_w,
                               shared_w, out, ws, stream=None, h_lora=None,
-                              lora_down: Optional[MoeLora] = None):
+                              lora_down: Optional[MoeLora] = None, sorted_pair=None):
     _check(lib().moe_grouped_gemm2_combine(
         ctypes.byref(w2), _p(h), _p(hs), _p(h_lora), _lp(lora_down), T, H, I,
-        top_k, shared_expert, p_cap, _p(offsets), _p(pair_row), _p(topk_w),
-        shared_w, _p(out), _p(ws), ws.numel() * ws.element_size(),
+        top_k, shared_expert, p_cap, _p(offsets), _p(sorted_pair), _p(pair_row),
+        _p(topk_w), shared_w, _p(out), _p(ws), ws.numel() * ws.element_size(),
         _stream(stream)), "moe_grouped_gemm2_combine")
 
 
@@ -325,8 +331,17 @@ class MoeModule:
                     if self.n_sink else None),
             err_word=torch.zeros(1, dtype=torch.int32, device=dev))
 
-    def forward(self, x_bf16, logits, outs=None, stream=None):
+    def set_adapters(self, adapter_ids: Optional[torch.Tensor]):
+        """Per-token adapter ids (int32 [T], -1 none) for a batch of adapters."""
+        for d in (self.lora, self.lora_down):
+            if d is not None and d.n_adapters > 1:
+                d.adapter_ids = None if adapter_ids is None else adapter_ids.data_ptr()
+                d._keep = d._keep[:2] + (adapter_ids,)
+
+    def forward(self, x_bf16, logits, outs=None, stream=None, adapter_ids=None):
         T = x_bf16.shape[0]
+        if adapter_ids is not None:
+            self.set_adapters(adapter_ids)
         o = outs if outs is not None else self.alloc_outputs(T)
         moe_forward(self.desc, x_bf16, logits, o["out"], o["topk_ids"], o["topk_w"],
                     o["sink_w"], o["err_word"], self.workspace(T), stream)

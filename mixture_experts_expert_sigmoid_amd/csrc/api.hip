@@ -26,6 +26,7 @@ int hip_fail(hipError_t e, const char* where) {
 }
 
 inline size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
+constexpr int kMaxAdapters = 1024;
 inline bool finite(float v) { return isfinite(v); }
 
 int check_weights(const moe_weights* w, int N, int K) {
@@ -51,8 +52,12 @@ int check_lora(const moe_lora* l, int G) {
   if (l->rank < 1 || l->rank > 32) return MOE_ERR_SHAPE;
   if (l->n_groups < 0 || l->n_groups > G) return MOE_ERR_SHAPE;
   if (!finite(l->scale)) return MOE_ERR_PARAM;
+  if (l->n_adapters < 0 || l->n_adapters > kMaxAdapters) return MOE_ERR_SHAPE;
+  if (l->n_adapters > 1 && !l->adapter_ids) return MOE_ERR_NULL;
   return MOE_OK;
 }
+
+bool batched(const moe_lora* l) { return l && l->n_adapters > 1; }
 
 long pcap_of(long T, int k, int shared) { return T * (long)k + (shared ? T : 0); }
 
@@ -190,8 +195,13 @@ int moe_quantize_act_fp8(const void* x_bf16, long T, int H, void* xq,
 namespace {
 // GEMM1 workspace: LoRA z rows, then (split-K) the fp32 partial sums, then
 // (INT4) the f16 activations, T <= p_cap rows of K
+// LoRA z rows, and with a batch of adapters each row's adapter
 size_t g1_z_bytes(long p_cap, const moe_lora* lora) {
-  return lora ? al((size_t)p_cap * lora->rank * 4) : 0;
+  if (!lora) return 0;
+  return al((size_t)p_cap * lora->rank * 4) + (batched(lora) ? al((size_t)p_cap * 4) : 0);
+}
+int* zad_of(float* z, long p_cap, const moe_lora* lora) {
+  return batched(lora) ? (int*)((char*)z + al((size_t)p_cap * lora->rank * 4)) : nullptr;
 }
 size_t g1_part_bytes(const moe_weights* w13, long p_cap) {
   if (!moe::splitk_use(w13->fmt, p_cap, w13->n_groups, w13->N / 256, w13->K / 128)) return 0;
@@ -263,6 +273,8 @@ static moe::Gemm1Args gemm1_args(const moe_weights* w13, const void* x,
   a.lora_rank = lora ? lora->rank : 0;
   a.lora_groups = lora ? lora->n_groups : 0;
   a.lora_scale = lora ? lora->scale : 0.0f;
+  a.n_adapters = lora ? lora->n_adapters : 0;
+  a.zad = lora ? zad_of(const_cast<float*>(z), p_cap, lora) : nullptr;
   a.h = h;
   a.hs = hs;
   a.part = part;
@@ -293,7 +305,9 @@ int moe_grouped_gemm1_act(const moe_weights* w13, const void* x,
   hipError_t e = hipSuccess;
   if (lora)
     e = moe::launch_lora_z(x_bf16, lora->A, lora->rank, T, H, top_k,
-                           lora->n_groups, p_cap, offsets, sorted_pair, z, s);
+                           lora->n_groups, p_cap, offsets, sorted_pair, true,
+                           lora->n_adapters, lora->adapter_ids, z,
+                           zad_of(z, p_cap, lora), s);
   if (e == hipSuccess)
     e = moe::launch_gemm1(gemm1_args(w13, x, xs, T, H, I, top_k, p_cap, offsets,
                                      sorted_pair, act, lora, z, h, hs, part, x16,
@@ -328,14 +342,15 @@ int moe_grouped_gemm2_combine(const moe_weights* w2, const void* h,
                               const float* hs, const void* h_lora,
                               const moe_lora* lora_down, long T, int H, int I,
                               int top_k, int shared_expert, long p_cap,
-                              const int* offsets, const int* pair_row,
-                              const float* topk_w, float shared_w, float* out,
-                              void* ws, size_t ws_bytes, void* stream) {
+                              const int* offsets, const int* sorted_pair,
+                              const int* pair_row, const float* topk_w,
+                              float shared_w, float* out, void* ws,
+                              size_t ws_bytes, void* stream) {
   int st = gemm2_checks(w2, h, hs, T, H, I, top_k, shared_expert, p_cap,
                         offsets, pair_row, topk_w, shared_w, out);
   if (st) return st;
   if ((st = check_lora(lora_down, w2->n_groups))) return st;
-  if (lora_down && p_cap > 0 && !h_lora) return MOE_ERR_NULL;
+  if (lora_down && p_cap > 0 && (!h_lora || !sorted_pair)) return MOE_ERR_NULL;
   size_t need = moe_gemm2_workspace_size(w2, p_cap, lora_down);
   if (need && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
@@ -344,7 +359,9 @@ int moe_grouped_gemm2_combine(const moe_weights* w2, const void* h,
   hipError_t e = hipSuccess;
   if (lora_down)
     e = moe::launch_lora_z(h_lora, lora_down->A, lora_down->rank, T, I, top_k,
-                           lora_down->n_groups, p_cap, offsets, nullptr, z2, s);
+                           lora_down->n_groups, p_cap, offsets, sorted_pair, false,
+                           lora_down->n_adapters, lora_down->adapter_ids, z2,
+                           zad_of(z2, p_cap, lora_down), s);
   if (e != hipSuccess) return hip_fail(e, "moe_grouped_gemm2_combine/lora_z");
   moe::Gemm2Args a{};
   a.fmt = w2->fmt;
@@ -366,6 +383,8 @@ int moe_grouped_gemm2_combine(const moe_weights* w2, const void* h,
     a.lora_rank = lora_down->rank;
     a.lora_groups = lora_down->n_groups;
     a.lora_scale = lora_down->scale;
+    a.n_adapters = lora_down->n_adapters;
+    a.zad = zad_of(z2, p_cap, lora_down);
   }
   e = moe::launch_gemm2(a, s);
   if (e == hipSuccess)
@@ -397,12 +416,12 @@ FwdLayout layout(const moe_layer* L, long T) {
   // FP8 activation codes, or (INT4) the f16 activations
   o.xq = take(fp8 ? (size_t)T * L->H : g1_x16_bytes(&L->w13, T));
   o.xs = take(fp8 ? (size_t)T * (L->H / 128) * 4 : 0);
-  o.z = take(L->lora ? (size_t)pc * L->lora->rank * 4 : 0);
+  o.z = take(g1_z_bytes(pc, L->lora));
   o.h = take((size_t)pc * L->I * (fp8 ? 1 : 2));
   o.hs = take(fp8 ? (size_t)pc * (L->I / 128) * 4 : 0);
   // down LoRA: its bf16 input (FP8 layers; BF16 / INT4 read h) and z rows
   o.h_lora = take(fp8 && L->lora_down ? (size_t)pc * L->I * 2 : 0);
-  o.z2 = take(L->lora_down ? (size_t)pc * L->lora_down->rank * 4 : 0);
+  o.z2 = take(g1_z_bytes(pc, L->lora_down));
   // y rows (or their stream-K partials); GEMM1's partials, consumed before
   // GEMM2 starts, share the region
   o.y = take(std::max(g2_bytes(&L->w2, pc), g1_part_bytes(&L->w13, pc)));
@@ -490,7 +509,8 @@ int moe_forward(const moe_layer* L, const void* x_bf16, const float* logits,
   if (L->lora) {
     e = moe::launch_lora_z(x_bf16, L->lora->A, L->lora->rank, T, L->H,
                            L->top_k, L->lora->n_groups, pc, offsets,
-                           sorted_pair, z, s);
+                           sorted_pair, true, L->lora->n_adapters,
+                           L->lora->adapter_ids, z, zad_of(z, pc, L->lora), s);
     if (e != hipSuccess) return hip_fail(e, "moe_forward/lora_z");
   }
   float* g1_part = g1_part_bytes(&L->w13, pc) ? y : nullptr;
@@ -502,8 +522,10 @@ int moe_forward(const moe_layer* L, const void* x_bf16, const float* logits,
   if (e != hipSuccess) return hip_fail(e, "moe_forward/gemm1");
   if (L->lora_down) {
     e = moe::launch_lora_z(h_lora, L->lora_down->A, L->lora_down->rank, T, L->I,
-                           L->top_k, L->lora_down->n_groups, pc, offsets, nullptr,
-                           z2, s);
+                           L->top_k, L->lora_down->n_groups, pc, offsets,
+                           sorted_pair, false, L->lora_down->n_adapters,
+                           L->lora_down->adapter_ids, z2,
+                           zad_of(z2, pc, L->lora_down), s);
     if (e != hipSuccess) return hip_fail(e, "moe_forward/lora_z_down");
   }
   moe::Gemm2Args a{};
@@ -526,6 +548,8 @@ int moe_forward(const moe_layer* L, const void* x_bf16, const float* logits,
     a.lora_rank = L->lora_down->rank;
     a.lora_groups = L->lora_down->n_groups;
     a.lora_scale = L->lora_down->scale;
+    a.n_adapters = L->lora_down->n_adapters;
+    a.zad = zad_of(z2, pc, L->lora_down);
   }
   e = moe::launch_gemm2(a, s);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/gemm2");

@@ -283,6 +283,8 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t s) {
   P.lora_rank = a.lora_rank;
   P.lora_groups = a.lora_groups;
   P.lora_scale = a.lora_scale;
+  P.n_adapters = a.n_adapters;
+  P.zad = a.zad;
   P.h = (uint8_t*)a.h;
   P.hs = a.hs;
   P.h_lora = (uint16_t*)a.h_lora;
@@ -327,6 +329,8 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t s) {
   P.lora_rank = a.lora_rank;
   P.lora_groups = a.z ? a.lora_groups : 0;
   P.lora_scale = a.lora_scale;
+  P.n_adapters = a.n_adapters;
+  P.zad = a.zad;
   long hint = a.G > 0 ? a.p_cap / a.G : a.p_cap;
   *a.sk_grid = 0;
   const int NT = (a.H + 255) / 256;

@@ -51,6 +51,10 @@ struct GemmParams {
   const uint16_t* lora_B;
   int lora_rank, lora_groups;
   float lora_scale;
+  // a batch of adapters: B is [n_adapters][lora_groups][N][rank] and row r
+  // uses adapter zad[r] (-1: none, its z row is zero)
+  int n_adapters;
+  const int* zad;
   uint8_t* h;                // GEMM1 out: e4m3 [p_cap][I] or bf16 [p_cap][I]
   float* hs;
   uint16_t* h_lora;          // GEMM1 out (FP8 layers), nullable: bf16 [p_cap][I]
@@ -202,22 +206,42 @@ __device__ __forceinline__ void lora_delta_tile(const GemmParams& P, const Tile&
     sz[q * BM + tr] = P.z[(long)(row0 + (tr < m ? tr : 0)) * R + q];
   }
   __syncthreads();
-  const uint16_t* Bg = P.lora_B + (long)g * P.N * R;
   const int nhi = hi_ok ? t.n_hi : t.n_lo;
-  for (int q = 0; q < R; ++q) {
-    float bl[4], bh[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      bl[r] = P.lora_scale * bf16_bits_to_f32(Bg[(long)(t.n_lo + c0 + r) * R + q]);
-      bh[r] = P.lora_scale * bf16_bits_to_f32(Bg[(long)(nhi + c0 + r) * R + q]);
-    }
-#pragma unroll
-    for (int ms = 0; ms < MS; ++ms) {
-      const float zq = sz[q * BM + 16 * ms + lr];
+  if (P.n_adapters <= 1) {
+    const uint16_t* Bg = P.lora_B + (long)g * P.N * R;
+    for (int q = 0; q < R; ++q) {
+      float bl[4], bh[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        acc[ms][0][r] = fmaf(zq, bl[r], acc[ms][0][r]);
-        acc[ms][1][r] = fmaf(zq, bh[r], acc[ms][1][r]);
+        bl[r] = P.lora_scale * bf16_bits_to_f32(Bg[(long)(t.n_lo + c0 + r) * R + q]);
+        bh[r] = P.lora_scale * bf16_bits_to_f32(Bg[(long)(nhi + c0 + r) * R + q]);
+      }
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms) {
+        const float zq = sz[q * BM + 16 * ms + lr];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          acc[ms][0][r] = fmaf(zq, bl[r], acc[ms][0][r]);
+          acc[ms][1][r] = fmaf(zq, bh[r], acc[ms][1][r]);
+        }
+      }
+    }
+  } else {
+    // a batch of adapters: each row's B (rows without one have z = 0)
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+      const int tr = 16 * ms + lr;
+      const int a = max(P.zad[row0 + (tr < m ? tr : 0)], 0);
+      const uint16_t* Bg = P.lora_B + ((long)a * P.lora_groups + g) * P.N * R;
+      for (int q = 0; q < R; ++q) {
+        const float zq = sz[q * BM + tr];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          acc[ms][0][r] = fmaf(zq, P.lora_scale * bf16_bits_to_f32(
+                                       Bg[(long)(t.n_lo + c0 + r) * R + q]), acc[ms][0][r]);
+          acc[ms][1][r] = fmaf(zq, P.lora_scale * bf16_bits_to_f32(
+                                       Bg[(long)(nhi + c0 + r) * R + q]), acc[ms][1][r]);
+        }
       }
     }
   }
@@ -263,27 +287,50 @@ __device__ __forceinline__ void tile_epilogue(const GemmParams& P, const Tile& t
       sz[q * BM + tr] = P.z[(long)rr * R + q];
     }
     __syncthreads();
-    const uint16_t* Bg = P.lora_B + (long)g * P.N * R;
     const int nhi = hi_ok ? t.n_hi : t.n_lo;      // an absent hi half is never stored
-    for (int q = 0; q < R; ++q) {
-      float bgv[2], buv[2];
+    if (P.n_adapters <= 1) {
+      const uint16_t* Bg = P.lora_B + (long)g * P.N * R;
+      for (int q = 0; q < R; ++q) {
+        float bgv[2], buv[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        int c = wn * 32 + j * 16 + lr;
-        bgv[j] = P.lora_scale * bf16_bits_to_f32(Bg[(long)(t.n_lo + c) * R + q]);
-        buv[j] = P.lora_scale * bf16_bits_to_f32(Bg[(long)(nhi + c) * R + q]);
+        for (int j = 0; j < 2; ++j) {
+          int c = wn * 32 + j * 16 + lr;
+          bgv[j] = P.lora_scale * bf16_bits_to_f32(Bg[(long)(t.n_lo + c) * R + q]);
+          buv[j] = P.lora_scale * bf16_bits_to_f32(Bg[(long)(nhi + c) * R + q]);
+        }
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) {
+          f32x4 zq = *(const f32x4*)(sz + q * BM + rbase + ms * 16 + 4 * lg);
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              acc[ms][j][r] = fmaf(zq[r], bgv[j], acc[ms][j][r]);
+              acc[ms][j + 2][r] = fmaf(zq[r], buv[j], acc[ms][j + 2][r]);
+            }
+        }
       }
+    } else {
+      // a batch of adapters: each row's B (rows without one have z = 0)
 #pragma unroll
-      for (int ms = 0; ms < MS; ++ms) {
-        f32x4 zq = *(const f32x4*)(sz + q * BM + rbase + ms * 16 + 4 * lg);
+      for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int r = 0; r < 4; ++r) {
+          const int tr = rbase + ms * 16 + 4 * lg + r;
+          const int a = max(P.zad[row0 + (tr < m ? tr : 0)], 0);
+          const uint16_t* Bg = P.lora_B + ((long)a * P.lora_groups + g) * P.N * R;
+          for (int q = 0; q < R; ++q) {
+            const float zq = sz[q * BM + tr];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            acc[ms][j][r] = fmaf(zq[r], bgv[j], acc[ms][j][r]);
-            acc[ms][j + 2][r] = fmaf(zq[r], buv[j], acc[ms][j + 2][r]);
+            for (int j = 0; j < 2; ++j) {
+              int c = wn * 32 + j * 16 + lr;
+              acc[ms][j][r] = fmaf(zq, P.lora_scale * bf16_bits_to_f32(
+                                           Bg[(long)(t.n_lo + c) * R + q]), acc[ms][j][r]);
+              acc[ms][j + 2][r] = fmaf(zq, P.lora_scale * bf16_bits_to_f32(
+                                               Bg[(long)(nhi + c) * R + q]), acc[ms][j + 2][r]);
+            }
           }
-      }
+        }
     }
     __syncthreads();
   }

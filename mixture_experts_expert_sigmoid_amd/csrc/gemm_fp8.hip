@@ -569,9 +569,11 @@ __global__ __launch_bounds__(kThreads) void gemm1_sk_epilogue_kernel(GemmParams 
     }
     if (P.z && g < P.lora_groups) {
       // ranks in steps of 8 whose loads are all issued before the FMAs
-      // (ascending q, as in the fused epilogue)
+      // (ascending q, as in the fused epilogue); a batch of adapters takes
+      // the row's adapter's B (a row without one has z = 0)
       const int R = P.lora_rank;
-      const uint16_t* Bg = P.lora_B + (long)g * 2 * I * R;
+      const int ad = P.n_adapters > 1 ? max(P.zad[r], 0) : 0;
+      const uint16_t* Bg = P.lora_B + ((long)ad * P.lora_groups + g) * 2 * I * R;
       const float* zr = P.z + (long)r * R;
       for (int q0 = 0; q0 < R; q0 += 8) {
         float zq[8], bv[2][2][8];

@@ -50,14 +50,17 @@ hipError_t launch_permute(const int* ids, long T, int k, int E_global, int off,
 hipError_t launch_quant_act(const void* x, long T, int H, void* xq, float* xs,
                             hipStream_t s);
 
-// z[r][q] = sum_h x[t(r)][h] * A[g(r)][q][h] for every sorted row of a
-// local group (fp32); t(r) = sorted_pair[r] / top_k, or r itself when
-// sorted_pair is NULL (x then holds one row per sorted row, e.g. the
-// down-LoRA input, and H is its length I)
+// z[r][q] = sum_h x[row][h] * A[a(r)][g(r)][q][h] for every sorted row r of
+// a local group (fp32). row = t(r) = sorted_pair[r] / top_k when gather,
+// else r itself (x then holds one row per sorted row, e.g. the down-LoRA
+// input, and H is its length I). a(r) = adapter_ids[t(r)] with a batch of
+// adapters (n_adapters > 1; none: z = 0), else 0; zad[r] (nullable) gets
+// a(r), -1 for none.
 hipError_t launch_lora_z(const void* x_bf16, const void* A, int rank, long T,
                          int H, int top_k, int n_lora_groups, long p_cap,
-                         const int* offsets, const int* sorted_pair, float* z,
-                         hipStream_t s);
+                         const int* offsets, const int* sorted_pair, bool gather,
+                         int n_adapters, const int* adapter_ids, float* z,
+                         int* zad, hipStream_t s);
 
 // Split-K (stream-K) for the FP8 and INT4 grouped GEMMs at decode sizes:
 // used when at most kSkMaxTiles tiles of 32 rows can exist (tiles <=
@@ -89,9 +92,11 @@ struct Gemm1Args {
   const int* sorted_pair;
   float alpha, beta, limit;
   const float* z;        // LoRA z rows [p_cap][rank] or NULL
-  const void* lora_B;    // bf16 [E_loc][2I][rank]
+  const void* lora_B;    // bf16 [n_adapters][lora_groups][2I][rank]
   int lora_rank, lora_groups;
   float lora_scale;
+  int n_adapters;        // > 1: a batch of adapters, row adapters in zad
+  const int* zad;        // [p_cap] (a batch of adapters) or NULL
   void* h;
   float* hs;
   float* part;           // split-K partials (when splitk_use) or NULL
@@ -111,11 +116,13 @@ struct Gemm2Args {
   const int* offsets;
   float* y;              // [p_cap][H] fp32, or the split-K partials
   int* sk_grid;          // out: split-K kernel grid (0 = plain kernel)
-  // down-projection LoRA (nullable z): y += scale * z[row] . B[g][n]
+  // down-projection LoRA (nullable z): y += scale * z[row] . B[a][g][n]
   const float* z;        // [p_cap][rank]
-  const void* lora_B;    // bf16 [G_lora][H][rank]
+  const void* lora_B;    // bf16 [n_adapters][G_lora][H][rank]
   int lora_rank, lora_groups;
   float lora_scale;
+  int n_adapters;
+  const int* zad;
 };
 hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t s);
 

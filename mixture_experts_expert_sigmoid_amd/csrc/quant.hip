@@ -108,12 +108,19 @@ __device__ __forceinline__ void lora_tile_prefix(const int* offsets, int G, int*
 // products, fp32 accumulation), A_g read once per tile instead of once per
 // row. Wave w covers the w-th quarter of H; the four partials are added in
 // wave order through LDS.
+// A batch of adapters (n_adapters > 1): row r belongs to token
+// t = sorted_pair[r] / top_k and uses adapter adapter_ids[t] (none if
+// outside [0, n_adapters)); A is [n_adapters][n_lora_groups][rank][H]. The
+// tile runs its K loop once per adapter that one of its rows uses and keeps
+// each row's own result; rows without an adapter get z = 0, and zad[r]
+// records every row's adapter (-1: none) for the epilogues.
 template <int NQ>    // 16-column blocks covering the rank
 __global__ __launch_bounds__(256) void lora_z_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ A, int rank,
     long T, int H, int top_k, int n_lora_groups,
     const int* __restrict__ offsets, const int* __restrict__ sorted_pair,
-    float* __restrict__ z) {
+    bool gather, int n_adapters, const int* __restrict__ adapter_ids,
+    float* __restrict__ z, int* __restrict__ zad) {
   __shared__ f32x4 red[4][NQ][64];
   __shared__ int s_cum[1025];
   __shared__ int s_wsum[4];
@@ -130,58 +137,87 @@ __global__ __launch_bounds__(256) void lora_z_kernel(
   const int wave = threadIdx.x >> 6, lane = lane_id(), lr = lane & 15, lg = lane >> 4;
   const int hq = H >> 2;                         // this wave's quarter of H
   const long rl = r0 + min(lr, m - 1);           // this lane's operand row
+  const long tok = sorted_pair[rl] / top_k;
   // operand row: the token of the pair (gathered x), or the sorted row itself
-  const long src = sorted_pair ? (long)(sorted_pair[rl] / top_k) : rl;
-  const uint16_t* xr = x + src * H + wave * hq + 8 * lg;
-  const uint16_t* Ag = A + (long)g * rank * H + wave * hq + 8 * lg;
-  f32x4 acc[NQ];
+  const uint16_t* xr = x + (gather ? tok : rl) * H + wave * hq + 8 * lg;
+  const bool batch = n_adapters > 1;
+  int ad = 0;                                    // this lane's row's adapter
+  if (batch) {
+    ad = adapter_ids[tok];
+    if (ad < 0 || ad >= n_adapters) ad = -1;
+  }
+  if (zad && wave == 0 && lg == 0 && lr < m) zad[r0 + lr] = ad;
+  for (int a = batch ? 0 : -1; a < (batch ? n_adapters : 0); ++a) {
+    // the adapter's rows in this tile (lanes 0..15 hold rows 0..15 in every
+    // wave, so the test is uniform over the workgroup)
+    const int aa = batch ? a : 0;
+    if (batch && !(__ballot(lr < m && ad == a) & 0xFFFFull)) continue;
+    const uint16_t* Ag = A + ((long)aa * n_lora_groups + g) * rank * H + wave * hq + 8 * lg;
+    f32x4 acc[NQ];
 #pragma unroll
-  for (int n = 0; n < NQ; ++n) acc[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  // 8 K steps per round: all their loads are issued before the MFMAs
-  for (int h0 = 0; h0 < hq; h0 += 256) {
-    i32x4 xv[8], av[NQ][8];
+    for (int n = 0; n < NQ; ++n) acc[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    // 8 K steps per round: all their loads are issued before the MFMAs
+    for (int h0 = 0; h0 < hq; h0 += 256) {
+      i32x4 xv[8], av[NQ][8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int h = min(h0 + 32 * j, hq - 32);   // hq % 32 == 0
-      xv[j] = *(const i32x4*)(xr + h);
+      for (int j = 0; j < 8; ++j) {
+        const int h = min(h0 + 32 * j, hq - 32);   // hq % 32 == 0
+        xv[j] = *(const i32x4*)(xr + h);
 #pragma unroll
-      for (int n = 0; n < NQ; ++n) {
-        const int q = 16 * n + lr;
-        av[n][j] = (i32x4){0, 0, 0, 0};
-        if (q < rank) av[n][j] = *(const i32x4*)(Ag + (long)q * H + h);
+        for (int n = 0; n < NQ; ++n) {
+          const int q = 16 * n + lr;
+          av[n][j] = (i32x4){0, 0, 0, 0};
+          if (q < rank) av[n][j] = *(const i32x4*)(Ag + (long)q * H + h);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (h0 + 32 * j >= hq) break;
+#pragma unroll
+        for (int n = 0; n < NQ; ++n)
+          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[j]),
+                                                          __builtin_bit_cast(bf16x8, av[n][j]),
+                                                          acc[n], 0, 0, 0);
       }
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (h0 + 32 * j >= hq) break;
+    for (int n = 0; n < NQ; ++n) red[wave][n][lane] = acc[n];
+    __syncthreads();
+    if (wave == 0) {
+      // acc[n][r]: row 4 (lane / 16) + r, rank 16 n + lane % 16; row
+      // adapters come from the lane holding that row (lane % 16 == row)
 #pragma unroll
-      for (int n = 0; n < NQ; ++n)
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[j]),
-                                                        __builtin_bit_cast(bf16x8, av[n][j]),
-                                                        acc[n], 0, 0, 0);
+      for (int n = 0; n < NQ; ++n) {
+        const f32x4 v = ((red[0][n][lane] + red[1][n][lane]) + red[2][n][lane]) + red[3][n][lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tr = 4 * lg + r;
+          const int q = 16 * n + lr;
+          const int rad = __shfl(ad, tr, 64);
+          if (tr < m && q < rank && (!batch || rad == a)) z[(r0 + tr) * rank + q] = v[r];
+        }
+      }
     }
+    __syncthreads();                             // red is reused by the next adapter
   }
+  if (batch && wave == 0) {                      // rows with no adapter: z = 0
 #pragma unroll
-  for (int n = 0; n < NQ; ++n) red[wave][n][lane] = acc[n];
-  __syncthreads();
-  if (wave == 0) {
-#pragma unroll
-    for (int n = 0; n < NQ; ++n) {
-      const f32x4 v = ((red[0][n][lane] + red[1][n][lane]) + red[2][n][lane]) + red[3][n][lane];
+    for (int n = 0; n < NQ; ++n)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tr = 4 * lg + r;
         const int q = 16 * n + lr;
-        if (tr < m && q < rank) z[(r0 + tr) * rank + q] = v[r];
+        const int rad = __shfl(ad, tr, 64);
+        if (tr < m && q < rank && rad < 0) z[(r0 + tr) * rank + q] = 0.0f;
       }
-    }
   }
 }
 
 hipError_t launch_lora_z(const void* x_bf16, const void* A, int rank, long T,
                          int H, int top_k, int n_lora_groups, long p_cap,
-                         const int* offsets, const int* sorted_pair, float* z,
-                         hipStream_t s) {
+                         const int* offsets, const int* sorted_pair, bool gather,
+                         int n_adapters, const int* adapter_ids, float* z,
+                         int* zad, hipStream_t s) {
   if (p_cap == 0 || n_lora_groups == 0) return hipSuccess;
   // tiles <= one per non-empty expert plus one per 16 rows
   const long tiles = std::min<long>(p_cap, n_lora_groups + p_cap / 16);
@@ -189,7 +225,8 @@ hipError_t launch_lora_z(const void* x_bf16, const void* A, int rank, long T,
 #define LZ(NQ)                                                                \
   hipLaunchKernelGGL(lora_z_kernel<NQ>, grid, block, 0, s,                    \
                      (const uint16_t*)x_bf16, (const uint16_t*)A, rank, T, H, \
-                     top_k, n_lora_groups, offsets, sorted_pair, z)
+                     top_k, n_lora_groups, offsets, sorted_pair, gather,      \
+                     n_adapters, adapter_ids, z, zad)
   if (rank <= 16) LZ(1);
   else LZ(2);
 #undef LZ

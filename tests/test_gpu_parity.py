@@ -152,6 +152,21 @@ SMALL = {
     # INT4 at the C4 shape with 16 experts, T = 2: 16 pairs, split-K on GEMM1
     "int4_sk": (CONFIGS["int4_g32_64"].scaled(
         name="int4_sk", n_routed=16, cfg_id=28), 2),
+    # a batch of eight adapters (tokens pick one or none) with both LoRAs:
+    # FP8 plain and split-K, INT4 plain and decode, BF16
+    "ep_lora_multi": (CONFIGS["ep_lora_258"].scaled(
+        name="ep_lora_multi", H=256, I=256, cfg_id=31, n_adapters=8), 300),
+    "ep_lora_multi_sk": (CONFIGS["ep_lora_258"].scaled(
+        name="ep_lora_multi_sk", H=2048, I=2048, n_routed=64, offset=16, cfg_id=32,
+        n_adapters=8), 4),
+    "int4_lora_multi": (CONFIGS["int4_g32_64"].scaled(
+        name="int4_lora_multi", H=512, I=256, n_routed=16, cfg_id=33, lora_rank=16,
+        lora_down=True, n_adapters=4), 100),
+    "int4_lora_multi_dec": (CONFIGS["int4_g32_64"].scaled(
+        name="int4_lora_multi_dec", n_routed=16, cfg_id=34, lora_rank=16,
+        lora_down=True, n_adapters=4), 3),
+    "bf16_lora_multi": (CONFIGS["tiny_bf16"].scaled(
+        name="bf16_lora_multi", cfg_id=35, lora_rank=8, lora_down=True, n_adapters=4), 16),
 }
 
 _cache = {}
@@ -173,7 +188,8 @@ def check_layer(spec, out_gpu, arr, nb, tokens=None, routing=None):
     sit on a rounding boundary within the kernel's fp32 error, for which
     either neighbouring code is a correct result."""
     ref, allow, nbnd = O.moe_layer(spec, arr, nb["x_bits"], nb["logits"], tokens=tokens,
-                                   routing=routing, with_allowance=True)
+                                   routing=routing, with_allowance=True,
+                                   adapter_ids=nb.get("adapter_ids"))
     tol, cmin = tolerance(spec.fmt)
     got = np.asarray(out_gpu, np.float64)
     rms = float(np.sqrt(np.mean(ref ** 2)))
@@ -192,7 +208,7 @@ def test_forward_parity_small(name):
     spec, T, layer, batch, arr, nb = _setup(name)
     _log("forward", name, "T", T, spec.fmt, "H", spec.H, "I", spec.I)
     mod = module_for(spec, layer)
-    o = mod.forward(batch.x.cuda(), batch.logits.cuda())
+    o = mod.forward(batch.x.cuda(), batch.logits.cuda(), adapter_ids=_ad(batch))
     torch.cuda.synchronize()
     assert M.moe_read_device_error(o["err_word"]) == 0
     rid, rw, rsw = O.route(nb["logits"], spec.n_routed, spec.n_sink, spec.top_k,
@@ -202,10 +218,15 @@ def test_forward_parity_small(name):
     check_layer(spec, o["out"].cpu().numpy(), arr, nb)
 
 
+def _ad(batch):
+    return None if batch.adapter_ids is None else batch.adapter_ids.cuda()
+
+
 def _stepwise(spec, mod, batch, T):
     """route -> permute -> quant -> gemm1 -> gemm2+combine through the
     individual C-ABI calls; returns every intermediate on the host."""
     x, lg = batch.x.cuda(), batch.logits.cuda()
+    mod.set_adapters(_ad(batch))
     k, N, S, H, I = spec.top_k, spec.n_routed, spec.n_sink, spec.H, spec.I
     G = spec.n_groups
     fp8 = spec.fmt == "fp8"
@@ -246,7 +267,7 @@ def _stepwise(spec, mod, batch, T):
                       dtype=torch.uint8, device="cuda")
     M.moe_grouped_gemm2_combine(mod.w2, h, hs, T, H, I, k, spec.shared, pc, offsets, pr,
                                 w, spec.shared_w, out, ws2, h_lora=h_lora,
-                                lora_down=mod.lora_down)
+                                lora_down=mod.lora_down, sorted_pair=sp)
     torch.cuda.synchronize()
     assert M.moe_read_device_error(err) == 0
     if fp8:
@@ -262,7 +283,9 @@ def _stepwise(spec, mod, batch, T):
 
 @pytest.mark.parametrize("name", ["tiny_bf16", "fp8_clamp_small", "fp8_oai_small",
                                   "int4_small", "ep_lora_small", "fp8_oai_sk",
-                                  "ep_lora_sk", "int4_sk"])
+                                  "ep_lora_sk", "int4_sk", "ep_lora_multi",
+                                  "ep_lora_multi_sk", "int4_lora_multi_dec",
+                                  "bf16_lora_multi"])
 def test_gemm1_h_codes(name):
     """GEMM1 output h (codes and scales) against the oracle: equal wherever
     the exact h is not within the kernel's error of a rounding boundary;
@@ -279,7 +302,8 @@ def test_gemm1_h_codes(name):
         if len(rows) == 0:
             continue
         toks = np.array([p // k if p < T * k else p - T * k for p in r["sp"][rows]])
-        _, det = O.expert_ffn(spec, arr, g, xhat[toks], xb[toks], detail=True)
+        ad = None if nb["adapter_ids"] is None else nb["adapter_ids"][toks]
+        _, det = O.expert_ffn(spec, arr, g, xhat[toks], xb[toks], detail=True, adapters=ad)
         diff = np.abs(r["hval"][rows] - det["hhat"])
         # scales agree to fp32 accuracy of the group amax
         slack = 1e-5 * np.abs(det["hhat"]) + det["alt"] * (1 + 1e-5)
@@ -301,7 +325,8 @@ def test_gemm1_h_codes(name):
     assert n_bad == 0
 
 
-@pytest.mark.parametrize("name", ["ep_lora_small", "fp8_oai_sk", "ep_lora_sk", "int4_sk"])
+@pytest.mark.parametrize("name", ["ep_lora_small", "fp8_oai_sk", "ep_lora_sk", "int4_sk",
+                                  "ep_lora_multi_sk", "int4_lora_multi_dec"])
 def test_stepwise_entry_points_match_forward_and_oracle(name):
     """route -> permute -> quant -> gemm1 -> gemm2+combine through the
     individual C-ABI calls gives moe_forward's output bit for bit (also on
@@ -309,7 +334,8 @@ def test_stepwise_entry_points_match_forward_and_oracle(name):
     spec, T, layer, batch, arr, nb = _setup(name)
     _log("stepwise", spec.name, T)
     mod = module_for(spec, layer)
-    ref_out = mod.forward(batch.x.cuda(), batch.logits.cuda())["out"].clone()
+    ref_out = mod.forward(batch.x.cuda(), batch.logits.cuda(),
+                          adapter_ids=_ad(batch))["out"].clone()
     r = _stepwise(spec, mod, batch, T)
     assert torch.equal(r["out"], ref_out)
     check_layer(spec, r["out"].cpu().numpy(), arr, nb)
@@ -333,6 +359,36 @@ def test_lora_zero_B_and_power_of_two_resplit_on_gpu():
     moved = module_for(spec, layer, w13_s=s.cuda(), gscale=gs.cuda()).forward(x, lg)["out"]
     torch.cuda.synchronize()
     assert torch.equal(moved, full)
+
+
+def test_down_lora_zero_B2_and_adapter_batch_on_gpu():
+    """Zero down-B gives the layer without the down LoRA bit for bit; a batch
+    of adapters where every token takes adapter a gives the one-adapter layer
+    built from adapter a's matrices bit for bit (same sums in the same order),
+    and tokens without an adapter give the layer without LoRA."""
+    spec, T, layer, batch, arr, nb = _setup("ep_lora_small")
+    _log("down-lora / adapter-batch invariants", spec.name, T)
+    x, lg = batch.x.cuda(), batch.logits.cuda()
+    no_down = module_for(spec, layer, lora_A2=None, lora_B2=None).forward(x, lg)["out"].clone()
+    zb2 = module_for(spec, layer, lora_B2=torch.zeros_like(layer.lora_B2).cuda()) \
+        .forward(x, lg)["out"].clone()
+    assert torch.equal(no_down, zb2)
+    spec, T, layer, batch, arr, nb = _setup("ep_lora_multi")
+    x, lg = batch.x.cuda(), batch.logits.cuda()
+    multi = module_for(spec, layer)
+    for a in (3, -1):
+        ids = torch.full((T,), a, dtype=torch.int32, device="cuda")
+        got = multi.forward(x, lg, adapter_ids=ids)["out"].clone()
+        if a >= 0:
+            one = module_for(spec.scaled(n_adapters=1), layer,
+                             lora_A=layer.lora_A[a].cuda(), lora_B=layer.lora_B[a].cuda(),
+                             lora_A2=layer.lora_A2[a].cuda(), lora_B2=layer.lora_B2[a].cuda())
+        else:
+            one = module_for(spec.scaled(n_adapters=1), layer, lora_A=None, lora_B=None,
+                             lora_A2=None, lora_B2=None)
+        ref = one.forward(x, lg)["out"]
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), a
 
 
 def test_zero_tokens_and_no_local_pairs():
