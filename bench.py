@@ -367,11 +367,17 @@ def config_table(args, stream, flush):
     from tests.gpu_helpers import module_for
     print("# config              T    ms/step  flushed-med  flushed-min    tokens/s"
           "    TFLOP/s  weight GB/s", file=sys.stderr)
-    for name, spec in CONFIGS.items():
+    # the EP + LoRA layer also with a batch of eight rank-16 adapters
+    # (tokens pick one or none), the page's multi-adapter serving case
+    table = dict(CONFIGS)
+    table["ep_lora_258_x8"] = CONFIGS["ep_lora_258"].scaled(
+        name="ep_lora_258_x8", cfg_id=15, n_adapters=8)
+    for name, spec in table.items():
         layer = make_layer(spec, device="cuda")
         mod = module_for(spec, layer)
         for T in spec.Ts:
             batch = make_batch(spec, layer, T, device="cuda")
+            mod.set_adapters(batch.adapter_ids)
             outs = mod.alloc_outputs(T)
             mod.workspace(T)
             # warm up for >= 50 ms of wall time: a GPU left idle while the

@@ -106,7 +106,7 @@ typedef struct {
  * [n_adapters][n_groups][...], and adapter_ids (device int32 [T], per call)
  * gives each token's adapter; a token whose id is outside [0, n_adapters)
  * gets no delta. n_adapters 0 or 1: one adapter for every token,
- * adapter_ids unused. */
+ * adapter_ids unused. A and B must be 16-byte aligned (MOE_ERR_PARAM). */
 typedef struct {
   int rank;             /* 1..32 */
   int n_groups;         /* adapters for groups 0..n_groups-1 (the local

@@ -54,6 +54,7 @@ int check_lora(const moe_lora* l, int G) {
   if (!finite(l->scale)) return MOE_ERR_PARAM;
   if (l->n_adapters < 0 || l->n_adapters > kMaxAdapters) return MOE_ERR_SHAPE;
   if (l->n_adapters > 1 && !l->adapter_ids) return MOE_ERR_NULL;
+  if ((((uintptr_t)l->A) | ((uintptr_t)l->B)) & 15) return MOE_ERR_PARAM;   // 16-byte loads
   return MOE_OK;
 }
 

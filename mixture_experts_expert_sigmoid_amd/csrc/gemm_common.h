@@ -207,25 +207,56 @@ __device__ __forceinline__ void lora_delta_tile(const GemmParams& P, const Tile&
   }
   __syncthreads();
   const int nhi = hi_ok ? t.n_hi : t.n_lo;
-  if (P.n_adapters <= 1) {
-    const uint16_t* Bg = P.lora_B + (long)g * P.N * R;
-    for (int q = 0; q < R; ++q) {
-      float bl[4], bh[4];
+  // B[n][q] rows hold the R ranks contiguously, so with R % 8 == 0 a lane
+  // reads ranks q0..q0+7 of one of its columns as one 16-byte load; the 8
+  // loads of a chunk (4 columns x 2 halves) are issued before the FMAs
+  const bool vec = (R & 7) == 0;
+  auto chunk = [&](const uint16_t* Bg, int q0, int ms_lo, int ms_hi) {
+    // ranks q0..q0+7 of the lane's 4 columns per half, kept packed (bf16
+    // pairs) and widened at use
+    i32x4 vl[4], vh[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        bl[r] = P.lora_scale * bf16_bits_to_f32(Bg[(long)(t.n_lo + c0 + r) * R + q]);
-        bh[r] = P.lora_scale * bf16_bits_to_f32(Bg[(long)(nhi + c0 + r) * R + q]);
-      }
+    for (int r = 0; r < 4; ++r) {
+      if (vec) {
+        vl[r] = *(const i32x4*)(Bg + (long)(t.n_lo + c0 + r) * R + q0);
+        vh[r] = *(const i32x4*)(Bg + (long)(nhi + c0 + r) * R + q0);
+      } else {
+        uint32_t u[8], w[8];
 #pragma unroll
-      for (int ms = 0; ms < MS; ++ms) {
-        const float zq = sz[q * BM + 16 * ms + lr];
+        for (int i = 0; i < 8; ++i) {
+          const int q = min(q0 + i, R - 1);
+          u[i] = Bg[(long)(t.n_lo + c0 + r) * R + q];
+          w[i] = Bg[(long)(nhi + c0 + r) * R + q];
+        }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          acc[ms][0][r] = fmaf(zq, bl[r], acc[ms][0][r]);
-          acc[ms][1][r] = fmaf(zq, bh[r], acc[ms][1][r]);
+        for (int i = 0; i < 4; ++i) {
+          vl[r][i] = (int)(u[2 * i] | (u[2 * i + 1] << 16));
+          vh[r][i] = (int)(w[2 * i] | (w[2 * i + 1] << 16));
         }
       }
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (q0 + i >= R) break;
+      const int q = q0 + i;
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms) {
+        if (ms < ms_lo || ms >= ms_hi) continue;
+        const float zq = sz[q * BM + 16 * ms + lr];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t pl = (uint32_t)vl[r][i >> 1], ph = (uint32_t)vh[r][i >> 1];
+          const float bl = __uint_as_float((i & 1) ? (pl & 0xFFFF0000u) : (pl << 16));
+          const float bh = __uint_as_float((i & 1) ? (ph & 0xFFFF0000u) : (ph << 16));
+          acc[ms][0][r] = fmaf(zq, P.lora_scale * bl, acc[ms][0][r]);
+          acc[ms][1][r] = fmaf(zq, P.lora_scale * bh, acc[ms][1][r]);
+        }
+      }
+    }
+  };
+  if (P.n_adapters <= 1) {
+    const uint16_t* Bg = P.lora_B + (long)g * P.N * R;
+    for (int q0 = 0; q0 < R; q0 += 8) chunk(Bg, q0, 0, MS);
   } else {
     // a batch of adapters: each row's B (rows without one have z = 0)
 #pragma unroll
@@ -233,16 +264,7 @@ __device__ __forceinline__ void lora_delta_tile(const GemmParams& P, const Tile&
       const int tr = 16 * ms + lr;
       const int a = max(P.zad[row0 + (tr < m ? tr : 0)], 0);
       const uint16_t* Bg = P.lora_B + ((long)a * P.lora_groups + g) * P.N * R;
-      for (int q = 0; q < R; ++q) {
-        const float zq = sz[q * BM + tr];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          acc[ms][0][r] = fmaf(zq, P.lora_scale * bf16_bits_to_f32(
-                                       Bg[(long)(t.n_lo + c0 + r) * R + q]), acc[ms][0][r]);
-          acc[ms][1][r] = fmaf(zq, P.lora_scale * bf16_bits_to_f32(
-                                       Bg[(long)(nhi + c0 + r) * R + q]), acc[ms][1][r]);
-        }
-      }
+      for (int q0 = 0; q0 < R; q0 += 8) chunk(Bg, q0, ms, ms + 1);
     }
   }
   __syncthreads();

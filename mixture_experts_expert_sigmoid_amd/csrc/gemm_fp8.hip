@@ -93,7 +93,7 @@ __device__ __forceinline__ bf16x8 e4m3x8_bf16(uint32_t w0, uint32_t w1) {
 // Accumulator layout (weights are the MFMA's first operand): acc[ms][ns][r]
 // is activation row 16 ms + (lane % 16) and weight column
 // (ns ? hi : lo) + 16 wave + 4 (lane / 16) + r.
-template <int BM, bool G1>
+template <int BM, bool G1, bool LORA>
 __device__ __forceinline__ void fp8_epilogue(const GemmParams& P, const Tile& t,
                                              f32x4 (&acc)[BM / 16][2], uint8_t* smem) {
   constexpr int MS = BM / 16;
@@ -103,7 +103,8 @@ __device__ __forceinline__ void fp8_epilogue(const GemmParams& P, const Tile& t,
   const int g = t.g, row0 = t.row0, m = t.m;
   if constexpr (!G1) {
     const bool hi_ok = t.n_hi != t.n_lo;
-    if (P.z && g < P.lora_groups) lora_delta_tile<BM>(P, t, acc, smem, hi_ok);   // down LoRA
+    if constexpr (LORA)
+      if (P.z && g < P.lora_groups) lora_delta_tile<BM>(P, t, acc, smem, hi_ok);   // down LoRA
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) {
       const int tr = 16 * ms + lr;
@@ -123,7 +124,8 @@ __device__ __forceinline__ void fp8_epilogue(const GemmParams& P, const Tile& t,
         acc[ms][0][r] *= gsg;
         acc[ms][1][r] *= gsu;
       }
-    if (P.z && g < P.lora_groups) lora_delta_tile<BM>(P, t, acc, smem, true);
+    if constexpr (LORA)
+      if (P.z && g < P.lora_groups) lora_delta_tile<BM>(P, t, acc, smem, true);
     float hv[MS][4];
     const float L = P.limit, al = P.alpha, be = P.beta;
 #pragma unroll
@@ -135,7 +137,7 @@ __device__ __forceinline__ void fp8_epilogue(const GemmParams& P, const Tile& t,
         const float sg = __builtin_amdgcn_rcpf(1.0f + expf(-al * gg));
         hv[ms][r] = gg * sg * (uu + be);
       }
-    if (P.h_lora) {   // the down-LoRA input: h before the re-quantisation, bf16
+    if (LORA && P.h_lora) {   // the down-LoRA input: h before the re-quantisation, bf16
 #pragma unroll
       for (int ms = 0; ms < MS; ++ms) {
         const int tr = 16 * ms + lr;
@@ -199,7 +201,7 @@ __device__ __forceinline__ void fp8_epilogue(const GemmParams& P, const Tile& t,
 // it pays where registers allow (kernels whose largest row class is 64 or
 // less) and spills in the 128-row class. PART: the block-scaled fp32 sums
 // go to partial slot `slot` instead of the epilogue (stream-K).
-template <int BM, bool G1, bool DEEP, bool PART = false>
+template <int BM, bool G1, bool DEEP, bool PART, bool LORA>
 __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, uint8_t* smem,
                                          int k0, int k1, int slot = 0) {
   // GEMM2 runs on the FP8 MFMA: its fp32 output feeds only the weighted
@@ -436,8 +438,9 @@ __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, ui
     const int c0 = 16 * wave + 4 * lg;
     const bool hi_ok = G1 || tl.n_hi != tl.n_lo;
     // GEMM2's down-LoRA delta goes into the tile's first partial slot once
-    if (!G1 && slot == 0 && P.z && tl.g < P.lora_groups)
-      lora_delta_tile<BM>(P, tl, acc, smem, hi_ok);
+    if constexpr (!G1 && LORA)
+      if (slot == 0 && P.z && tl.g < P.lora_groups)
+        lora_delta_tile<BM>(P, tl, acc, smem, hi_ok);
     float* base = P.part + ((long)slot * P.p_rows + row0) * P.N;
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) {
@@ -448,7 +451,7 @@ __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, ui
       }
     }
   } else {
-    fp8_epilogue<BM, G1>(P, tl, acc, smem);
+    fp8_epilogue<BM, G1, LORA>(P, tl, acc, smem);
     __syncthreads();       // LDS is reused by the next tile
   }
 }
@@ -460,7 +463,7 @@ __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, ui
 // The tiles (TBM-row scheduling, s_cum its prefix) walked by persistent
 // workgroups: XCD x (= blockIdx % 8) owns logical tiles [x*chunk,
 // (x+1)*chunk), so the N-tiles of one expert share an L2.
-template <int TBM, bool G1>
+template <int TBM, bool G1, bool LORA>
 __device__ __forceinline__ void plain_tiles(const GemmParams& P, uint8_t* smem,
                                             const int* s_cum) {
   const int NT = G1 ? (P.I >> 7) : ((P.N + 255) >> 8);
@@ -478,28 +481,33 @@ __device__ __forceinline__ void plain_tiles(const GemmParams& P, uint8_t* smem,
     tl.n_lo = __builtin_amdgcn_readfirstlane(tl.n_lo);
     tl.n_hi = __builtin_amdgcn_readfirstlane(tl.n_hi);
     if constexpr (TBM >= 128) {
-      if (tl.m > 64) { fp8_tile<128, G1, false>(P, tl, smem, 0, NS); continue; }
+      if (tl.m > 64) { fp8_tile<128, G1, false, false, LORA>(P, tl, smem, 0, NS); continue; }
     }
     if constexpr (TBM >= 64) {
-      if (tl.m > 32) { fp8_tile<64, G1, G1 && TBM <= 64>(P, tl, smem, 0, NS); continue; }
+      if (tl.m > 32) {
+        fp8_tile<64, G1, G1 && TBM <= 64, false, LORA>(P, tl, smem, 0, NS);
+        continue;
+      }
     }
-    fp8_tile<32, G1, G1 && TBM <= 64>(P, tl, smem, 0, NS);
+    fp8_tile<32, G1, G1 && TBM <= 64, false, LORA>(P, tl, smem, 0, NS);
   }
 }
 
-template <int TBM, bool G1>
+// LORA: the kernel carries the LoRA delta (and the bf16 down-LoRA input of
+// GEMM1); layers without LoRA run the instantiation without that code.
+template <int TBM, bool G1, bool LORA>
 __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // 2 stages
   __shared__ int s_cum[kMaxGroups + 1];
   __shared__ int s_wsum[8];
   tile_prefix<TBM>(P.offsets, P.G, s_cum, s_wsum);
-  plain_tiles<TBM, G1>(P, smem, s_cum);
+  plain_tiles<TBM, G1, LORA>(P, smem, s_cum);
 }
 
 // Split-K (stream-K) kernel over 32-row tiles (see gemm_common.h):
 // workgroup b runs the K-block segments of its unit range and leaves fp32
 // partial sums in slot b - (first workgroup of the tile).
-template <bool G1>
+template <bool G1, bool LORA>
 __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_sk_kernel(GemmParams P) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_cum[kMaxGroups + 1];
@@ -525,7 +533,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_sk_kernel(GemmParams P)
     tl.n_lo = __builtin_amdgcn_readfirstlane(tl.n_lo);
     tl.n_hi = __builtin_amdgcn_readfirstlane(tl.n_hi);
     const int slot = b - sk_owner((long)t * NS, U, W);
-    fp8_tile<kSkBM, G1, G1, true>(P, tl, smem, k0, k1, slot);
+    fp8_tile<kSkBM, G1, G1, true, LORA>(P, tl, smem, k0, k1, slot);
     u += k1 - k0;
   }
 }
@@ -627,18 +635,18 @@ __global__ __launch_bounds__(kThreads) void gemm1_sk_epilogue_kernel(GemmParams 
   }
 }
 
-template <int TBM, bool G1>
+template <int TBM, bool G1, bool LORA>
 static hipError_t run_fp8(const GemmParams& P, long p_cap, int NT, hipStream_t s) {
   constexpr int shm = F8Geo<TBM, !G1>::LDS;
   static int per_cu = 0;   // resident workgroups per CU, per instantiation
   if (per_cu == 0) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&moe_gemm_fp8_kernel<TBM, G1>),
+        reinterpret_cast<const void*>(&moe_gemm_fp8_kernel<TBM, G1, LORA>),
         hipFuncAttributeMaxDynamicSharedMemorySize, shm);
     if (e != hipSuccess) return e;
     int nb = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &nb, reinterpret_cast<const void*>(&moe_gemm_fp8_kernel<TBM, G1>), kThreads, shm);
+        &nb, reinterpret_cast<const void*>(&moe_gemm_fp8_kernel<TBM, G1, LORA>), kThreads, shm);
     if (e != hipSuccess) return e;
     per_cu = nb > 0 ? nb : 1;
   }
@@ -646,30 +654,30 @@ static hipError_t run_fp8(const GemmParams& P, long p_cap, int NT, hipStream_t s
   long nwg = std::min<long>(max_tiles, (long)num_cus() * per_cu);
   nwg = (nwg + 7) & ~7L;
   if (nwg == 0) return hipSuccess;
-  moe_gemm_fp8_kernel<TBM, G1><<<dim3((unsigned)nwg), dim3(kThreads), shm, s>>>(P);
+  moe_gemm_fp8_kernel<TBM, G1, LORA><<<dim3((unsigned)nwg), dim3(kThreads), shm, s>>>(P);
   return hipGetLastError();
 }
 
-template <bool G1>
+template <bool G1, bool LORA>
 static hipError_t run_fp8_sk(const GemmParams& P, long p_cap, int NT, hipStream_t s,
                              int* sk_grid) {
   constexpr int shm = F8Geo<kSkBM, !G1>::LDS;
   static int per_cu = 0;
   if (per_cu == 0) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&moe_gemm_fp8_sk_kernel<G1>),
+        reinterpret_cast<const void*>(&moe_gemm_fp8_sk_kernel<G1, LORA>),
         hipFuncAttributeMaxDynamicSharedMemorySize, shm);
     if (e != hipSuccess) return e;
     int nb = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &nb, reinterpret_cast<const void*>(&moe_gemm_fp8_sk_kernel<G1>), kThreads, shm);
+        &nb, reinterpret_cast<const void*>(&moe_gemm_fp8_sk_kernel<G1, LORA>), kThreads, shm);
     if (e != hipSuccess) return e;
     per_cu = nb > 0 ? nb : 1;
   }
   const int grid = num_cus() * per_cu;
   *sk_grid = grid;
   if (p_cap == 0) return hipSuccess;
-  moe_gemm_fp8_sk_kernel<G1><<<dim3((unsigned)grid), dim3(kThreads), shm, s>>>(P);
+  moe_gemm_fp8_sk_kernel<G1, LORA><<<dim3((unsigned)grid), dim3(kThreads), shm, s>>>(P);
   return hipGetLastError();
 }
 
@@ -684,21 +692,28 @@ hipError_t launch_gemm1_sk_epilogue(const GemmParams& P, int sk_grid, bool fp8h,
   return hipGetLastError();
 }
 
-template <bool G1>
+template <bool G1, bool LORA>
 static hipError_t run_fp8_tbm(const GemmParams& P, long p_cap, int NT, hipStream_t s) {
   // the largest row class worth scheduling: rows per group on average
   const long hint = P.G > 0 ? p_cap / P.G : p_cap;
-  if (hint <= 32) return run_fp8<32, G1>(P, p_cap, NT, s);
-  if (hint <= 64) return run_fp8<64, G1>(P, p_cap, NT, s);
-  return run_fp8<128, G1>(P, p_cap, NT, s);
+  if (hint <= 32) return run_fp8<32, G1, LORA>(P, p_cap, NT, s);
+  if (hint <= 64) return run_fp8<64, G1, LORA>(P, p_cap, NT, s);
+  return run_fp8<128, G1, LORA>(P, p_cap, NT, s);
+}
+
+template <bool LORA>
+static hipError_t launch_fp8(const GemmParams& P, bool g1, long p_cap, int NT, hipStream_t s,
+                             int* sk_grid) {
+  if (P.part)
+    return g1 ? run_fp8_sk<true, LORA>(P, p_cap, NT, s, sk_grid)
+              : run_fp8_sk<false, LORA>(P, p_cap, NT, s, sk_grid);
+  return g1 ? run_fp8_tbm<true, LORA>(P, p_cap, NT, s) : run_fp8_tbm<false, LORA>(P, p_cap, NT, s);
 }
 
 hipError_t launch_gemm_fp8(const GemmParams& P, bool g1, long p_cap, int NT, hipStream_t s,
                            int* sk_grid) {
-  if (P.part)
-    return g1 ? run_fp8_sk<true>(P, p_cap, NT, s, sk_grid)
-              : run_fp8_sk<false>(P, p_cap, NT, s, sk_grid);
-  return g1 ? run_fp8_tbm<true>(P, p_cap, NT, s) : run_fp8_tbm<false>(P, p_cap, NT, s);
+  return (P.z || P.h_lora) ? launch_fp8<true>(P, g1, p_cap, NT, s, sk_grid)
+                           : launch_fp8<false>(P, g1, p_cap, NT, s, sk_grid);
 }
 
 }  // namespace moe

@@ -85,7 +85,7 @@ __device__ __forceinline__ f16x8 bf16x8_f16p(i32x4 v) {
 
 // Accumulator layout: acc[ms][ns][r] is activation row 16 ms + (lane % 16)
 // and weight column (ns ? hi : lo) + 16 wave + 4 (lane / 16) + r.
-template <int BM, bool G1>
+template <int BM, bool G1, bool LORA>
 __device__ __forceinline__ void int4_epilogue(const GemmParams& P, const Tile& t,
                                               f32x4 (&acc)[BM / 16][2], uint8_t* smem) {
   constexpr int MS = BM / 16;
@@ -95,7 +95,8 @@ __device__ __forceinline__ void int4_epilogue(const GemmParams& P, const Tile& t
   const int g = t.g, row0 = t.row0, m = t.m;
   if constexpr (!G1) {
     const bool hi_ok = t.n_hi != t.n_lo;
-    if (P.z && g < P.lora_groups) lora_delta_tile<BM>(P, t, acc, smem, hi_ok);   // down LoRA
+    if constexpr (LORA)
+      if (P.z && g < P.lora_groups) lora_delta_tile<BM>(P, t, acc, smem, hi_ok);   // down LoRA
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) {
       const int tr = 16 * ms + lr;
@@ -116,7 +117,8 @@ __device__ __forceinline__ void int4_epilogue(const GemmParams& P, const Tile& t
           acc[ms][1][r] *= gsu;
         }
     }
-    if (P.z && g < P.lora_groups) lora_delta_tile<BM>(P, t, acc, smem, true);
+    if constexpr (LORA)
+      if (P.z && g < P.lora_groups) lora_delta_tile<BM>(P, t, acc, smem, true);
     const float L = P.limit, al = P.alpha, be = P.beta;
     uint16_t* h = (uint16_t*)P.h;
 #pragma unroll
@@ -139,7 +141,7 @@ __device__ __forceinline__ void int4_epilogue(const GemmParams& P, const Tile& t
 
 // One tile of BM rows over K blocks [k0, k1) (see the FP8 kernel for the
 // pipeline); PART: fp32 sums to partial slot `slot` (split-K).
-template <int BM, bool G1, bool PART = false>
+template <int BM, bool G1, bool PART, bool LORA>
 __device__ __forceinline__ void int4_tile(const GemmParams& P, const Tile& tl, uint8_t* smem,
                                           int k0, int k1, int slot = 0) {
   using Gm = I4Geo<BM>;
@@ -308,8 +310,9 @@ __device__ __forceinline__ void int4_tile(const GemmParams& P, const Tile& tl, u
     const int c0 = 16 * wave + 4 * lg;
     const bool hi_ok = G1 || tl.n_hi != tl.n_lo;
     // GEMM2's down-LoRA delta goes into the tile's first partial slot once
-    if (!G1 && slot == 0 && P.z && tl.g < P.lora_groups)
-      lora_delta_tile<BM>(P, tl, acc, smem, hi_ok);
+    if constexpr (!G1 && LORA)
+      if (slot == 0 && P.z && tl.g < P.lora_groups)
+        lora_delta_tile<BM>(P, tl, acc, smem, hi_ok);
     float* base = P.part + ((long)slot * P.p_rows + row0) * P.N;
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) {
@@ -320,12 +323,12 @@ __device__ __forceinline__ void int4_tile(const GemmParams& P, const Tile& tl, u
       }
     }
   } else {
-    int4_epilogue<BM, G1>(P, tl, acc, smem);
+    int4_epilogue<BM, G1, LORA>(P, tl, acc, smem);
     __syncthreads();       // LDS is reused by the next tile
   }
 }
 
-template <int TBM, bool G1>
+template <int TBM, bool G1, bool LORA>
 __device__ __forceinline__ void int4_plain_tiles(const GemmParams& P, uint8_t* smem,
                                                  const int* s_cum) {
   const int NT = G1 ? (P.I >> 7) : ((P.N + 255) >> 8);
@@ -343,26 +346,26 @@ __device__ __forceinline__ void int4_plain_tiles(const GemmParams& P, uint8_t* s
     tl.n_lo = __builtin_amdgcn_readfirstlane(tl.n_lo);
     tl.n_hi = __builtin_amdgcn_readfirstlane(tl.n_hi);
     if constexpr (TBM >= 128) {
-      if (tl.m > 64) { int4_tile<128, G1>(P, tl, smem, 0, NS); continue; }
+      if (tl.m > 64) { int4_tile<128, G1, false, LORA>(P, tl, smem, 0, NS); continue; }
     }
     if constexpr (TBM >= 64) {
-      if (tl.m > 32) { int4_tile<64, G1>(P, tl, smem, 0, NS); continue; }
+      if (tl.m > 32) { int4_tile<64, G1, false, LORA>(P, tl, smem, 0, NS); continue; }
     }
-    int4_tile<32, G1>(P, tl, smem, 0, NS);
+    int4_tile<32, G1, false, LORA>(P, tl, smem, 0, NS);
   }
 }
 
-template <int TBM, bool G1>
+template <int TBM, bool G1, bool LORA>
 __global__ __launch_bounds__(kThreads) void moe_gemm_int4_kernel(GemmParams P) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_cum[kMaxGroups + 1];
   __shared__ int s_wsum[8];
   tile_prefix<TBM>(P.offsets, P.G, s_cum, s_wsum);
-  int4_plain_tiles<TBM, G1>(P, smem, s_cum);
+  int4_plain_tiles<TBM, G1, LORA>(P, smem, s_cum);
 }
 
 // Split-K (stream-K) variant, schedule as in the FP8 kernel
-template <bool G1>
+template <bool G1, bool LORA>
 __global__ __launch_bounds__(kThreads) void moe_gemm_int4_sk_kernel(GemmParams P) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_cum[kMaxGroups + 1];
@@ -388,7 +391,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_int4_sk_kernel(GemmParams P
     tl.n_lo = __builtin_amdgcn_readfirstlane(tl.n_lo);
     tl.n_hi = __builtin_amdgcn_readfirstlane(tl.n_hi);
     const int slot = b - sk_owner((long)t * NS, U, W);
-    int4_tile<kSkBM, G1, true>(P, tl, smem, k0, k1, slot);
+    int4_tile<kSkBM, G1, true, LORA>(P, tl, smem, k0, k1, slot);
     u += k1 - k0;
   }
 }
@@ -410,18 +413,18 @@ hipError_t launch_act_f16p(const void* x, long T, int H, void* out, hipStream_t 
   return hipGetLastError();
 }
 
-template <int TBM, bool G1>
+template <int TBM, bool G1, bool LORA>
 static hipError_t run_int4(const GemmParams& P, long p_cap, int NT, hipStream_t s) {
   constexpr int shm = I4Geo<TBM>::LDS;
   static int per_cu = 0;
   if (per_cu == 0) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&moe_gemm_int4_kernel<TBM, G1>),
+        reinterpret_cast<const void*>(&moe_gemm_int4_kernel<TBM, G1, LORA>),
         hipFuncAttributeMaxDynamicSharedMemorySize, shm);
     if (e != hipSuccess) return e;
     int nb = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &nb, reinterpret_cast<const void*>(&moe_gemm_int4_kernel<TBM, G1>), kThreads, shm);
+        &nb, reinterpret_cast<const void*>(&moe_gemm_int4_kernel<TBM, G1, LORA>), kThreads, shm);
     if (e != hipSuccess) return e;
     per_cu = nb > 0 ? nb : 1;
   }
@@ -429,45 +432,55 @@ static hipError_t run_int4(const GemmParams& P, long p_cap, int NT, hipStream_t 
   long nwg = std::min<long>(max_tiles, (long)num_cus() * per_cu);
   nwg = (nwg + 7) & ~7L;
   if (nwg == 0) return hipSuccess;
-  moe_gemm_int4_kernel<TBM, G1><<<dim3((unsigned)nwg), dim3(kThreads), shm, s>>>(P);
+  moe_gemm_int4_kernel<TBM, G1, LORA><<<dim3((unsigned)nwg), dim3(kThreads), shm, s>>>(P);
   return hipGetLastError();
 }
 
-template <bool G1>
+template <bool G1, bool LORA>
 static hipError_t run_int4_sk(const GemmParams& P, long p_cap, hipStream_t s, int* sk_grid) {
   constexpr int shm = I4Geo<kSkBM>::LDS;
   static int per_cu = 0;
   if (per_cu == 0) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&moe_gemm_int4_sk_kernel<G1>),
+        reinterpret_cast<const void*>(&moe_gemm_int4_sk_kernel<G1, LORA>),
         hipFuncAttributeMaxDynamicSharedMemorySize, shm);
     if (e != hipSuccess) return e;
     int nb = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &nb, reinterpret_cast<const void*>(&moe_gemm_int4_sk_kernel<G1>), kThreads, shm);
+        &nb, reinterpret_cast<const void*>(&moe_gemm_int4_sk_kernel<G1, LORA>), kThreads, shm);
     if (e != hipSuccess) return e;
     per_cu = nb > 0 ? nb : 1;
   }
   const int grid = num_cus() * per_cu;
   *sk_grid = grid;
   if (p_cap == 0) return hipSuccess;
-  moe_gemm_int4_sk_kernel<G1><<<dim3((unsigned)grid), dim3(kThreads), shm, s>>>(P);
+  moe_gemm_int4_sk_kernel<G1, LORA><<<dim3((unsigned)grid), dim3(kThreads), shm, s>>>(P);
   return hipGetLastError();
 }
 
-template <bool G1>
+template <bool G1, bool LORA>
 static hipError_t run_int4_tbm(const GemmParams& P, long p_cap, int NT, hipStream_t s) {
   const long hint = P.G > 0 ? p_cap / P.G : p_cap;
-  if (hint <= 32) return run_int4<32, G1>(P, p_cap, NT, s);
-  if (hint <= 64) return run_int4<64, G1>(P, p_cap, NT, s);
-  return run_int4<128, G1>(P, p_cap, NT, s);
+  if (hint <= 32) return run_int4<32, G1, LORA>(P, p_cap, NT, s);
+  if (hint <= 64) return run_int4<64, G1, LORA>(P, p_cap, NT, s);
+  return run_int4<128, G1, LORA>(P, p_cap, NT, s);
 }
 
+template <bool LORA>
+static hipError_t launch_int4(const GemmParams& P, bool g1, long p_cap, int NT, hipStream_t s,
+                              int* sk_grid) {
+  if (P.part)
+    return g1 ? run_int4_sk<true, LORA>(P, p_cap, s, sk_grid)
+              : run_int4_sk<false, LORA>(P, p_cap, s, sk_grid);
+  return g1 ? run_int4_tbm<true, LORA>(P, p_cap, NT, s)
+            : run_int4_tbm<false, LORA>(P, p_cap, NT, s);
+}
+
+// layers with a LoRA run the instantiations that carry the delta
 hipError_t launch_gemm_int4(const GemmParams& P, bool g1, long p_cap, int NT, hipStream_t s,
                             int* sk_grid) {
-  if (P.part)
-    return g1 ? run_int4_sk<true>(P, p_cap, s, sk_grid) : run_int4_sk<false>(P, p_cap, s, sk_grid);
-  return g1 ? run_int4_tbm<true>(P, p_cap, NT, s) : run_int4_tbm<false>(P, p_cap, NT, s);
+  return P.z ? launch_int4<true>(P, g1, p_cap, NT, s, sk_grid)
+             : launch_int4<false>(P, g1, p_cap, NT, s, sk_grid);
 }
 
 }  // namespace moe

@@ -112,7 +112,7 @@ def test_gemm_validation():
     assert g1(w, M.act_params(1.0, 0.0, math.nan)) == -5
     assert g1(w, M.act_params(math.inf, 0.0, 7.0)) == -5
     assert g1(w, M.act_params(1.0, math.nan, 7.0)) == -5
-    lo = M.MoeLora(64, 4, 1.0, 1, 1, 1, None)
+    lo = M.MoeLora(64, 4, 1.0, 256, 256, 1, None)
     assert g1(w, act, lora=ctypes.pointer(lo)) == -2      # rank > 32
     # the bf16 down-LoRA input is an FP8-only output of GEMM1
     assert g1(_w(fmt=M.MOE_W_BF16, N=256, K=256), act, hl=ctypes.c_void_p(256)) == -5
@@ -121,15 +121,17 @@ def test_gemm_validation():
         ctypes.byref(w2), 1, 1, hl, ld, 4, 256, 128, 2, 0, 8, 1, sp, 1, 1, 1.0, 1, ws, nb,
         None)
     assert g2() == -6                                    # workspace
-    ld = M.MoeLora(16, 4, 1.0, 1, 1, 1, None)
+    ld = M.MoeLora(16, 4, 1.0, 256, 256, 1, None)
     big = dict(ws=ctypes.c_void_p(256), nb=1 << 30)
     assert g2(ld=ctypes.pointer(ld), **big) == -1         # no h_lora
     assert g2(ld=ctypes.pointer(ld), hl=ctypes.c_void_p(256), sp=None, **big) == -1
-    assert g2(ld=ctypes.pointer(M.MoeLora(40, 4, 1.0, 1, 1, 1, None)),
+    assert g2(ld=ctypes.pointer(M.MoeLora(40, 4, 1.0, 256, 256, 1, None)),
               hl=ctypes.c_void_p(256), **big) == -2       # rank > 32
     # a batch of adapters needs the per-token ids
-    assert g2(ld=ctypes.pointer(M.MoeLora(16, 4, 1.0, 1, 1, 8, None)),
+    assert g2(ld=ctypes.pointer(M.MoeLora(16, 4, 1.0, 256, 256, 8, None)),
               hl=ctypes.c_void_p(256), **big) == -1
+    assert g2(ld=ctypes.pointer(M.MoeLora(16, 4, 1.0, 256, 264, 1, None)),
+              hl=ctypes.c_void_p(256), **big) == -5     # B not 16-byte aligned
     assert L.moe_gemm2_workspace_size(ctypes.byref(w2), 100, None) >= 100 * 256 * 4
     assert (L.moe_gemm2_workspace_size(ctypes.byref(w2), 100, ctypes.pointer(ld)) -
             L.moe_gemm2_workspace_size(ctypes.byref(w2), 100, None)) >= 100 * 16 * 4
