@@ -4,6 +4,7 @@ TEST INFRASTRUCTURE, independent of moe_oracle.py (it imports nothing from
 it): pure-Python scalar loops over every expert, with its own number-format
 handling:
   * e4m3 values come from torch's float8_e4m3fn decoding (a library table),
+    e2m1 values from the list of its eight magnitudes, e8m0 as ldexp,
     and rounding to e4m3 is a nearest-value search over that table (ties to
     the even code, saturation at 448);
   * bfloat16 rounding is Python's round-half-even on the scaled value;
@@ -26,6 +27,10 @@ _E4M3_ALL = torch.arange(256, dtype=torch.int32).to(torch.uint8) \
     .view(torch.float8_e4m3fn).double().tolist()
 _E4M3 = [(c, v) for c, v in enumerate(_E4M3_ALL)
          if not math.isnan(v) and c < 0x80]
+
+
+# the eight e2m1 magnitudes, codes 0..7
+_E2M1 = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
 
 
 def _e4m3_table():
@@ -84,10 +89,18 @@ def dense_weight(fmt, q, s, N, K, gsc=None):
                 v = bf16_bits_value(int(q[n][kk]))
             elif fmt == "fp8":
                 v = e4m3_value(int(q[n][kk])) * float(s[n // 128][kk // 128])
-            else:
+            elif fmt == "int4":
                 byte = int(q[n][kk // 2])
                 nib = byte & 0xF if kk % 2 == 0 else byte >> 4
                 v = (nib - 8) * bf16_bits_value(int(s[n][kk // 32]))
+            else:                      # nvfp4 | mxfp4: e2m1 from its value list
+                byte = int(q[n][kk // 2])
+                nib = byte & 0xF if kk % 2 == 0 else byte >> 4
+                v = _E2M1[nib & 7] * (-1.0 if nib & 8 else 1.0)
+                if fmt == "nvfp4":
+                    v *= e4m3_value(int(s[n][kk // 16]))
+                else:
+                    v *= math.ldexp(1.0, int(s[n][kk // 32]) - 127)
             if gsc is not None:
                 v *= gsc[n]
             W[n][kk] = v
@@ -126,8 +139,11 @@ def layer(spec, arr, x_bits, logits, adapter_ids=None):
             gsc = [g0] * I + [g1] * I
         W13 = dense_weight(spec.fmt, arr["w13_q"][e],
                            None if arr["w13_s"] is None else arr["w13_s"][e], 2 * I, H, gsc)
+        gsc2 = None
+        if arr.get("gs2") is not None:
+            gsc2 = [float(arr["gs2"][e])] * H
         W2 = dense_weight(spec.fmt, arr["w2_q"][e],
-                          None if arr["w2_s"] is None else arr["w2_s"][e], H, I)
+                          None if arr["w2_s"] is None else arr["w2_s"][e], H, I, gsc2)
         for t in range(T):
             gu = [sum(xin[t][kk] * W13[n][kk] for kk in range(H)) for n in range(2 * I)]
             a = 0 if adapter_ids is None else int(adapter_ids[t])

@@ -33,7 +33,15 @@ title and section):
                 sglang PR #39920, "Modifications"; rounding read as
                 round-to-nearest-even with saturation at +-448.
   dequant    -- FP8 q * block scale; INT4 (nibble - 8) * scale[n, k/32],
-                low nibble = even k: batchgen PR #239, commit text.
+                low nibble = even k: batchgen PR #239, commit text. NVFP4
+                expert weights with distinct per-half global scales (the
+                format the MoE-LoRA AOT release notes serve, "Changes since
+                1b699bf"): e2m1 codes times an e4m3 scale per 16 K times
+                the fp32 global scale (W13: gate, up; W2: one per expert);
+                MXFP4: e2m1 codes times a power-of-two e8m0 scale per 32 K.
+                The pages name these formats without defining them; the
+                element and scale encodings are the public ones, written
+                here from their bit fields.
   swiglu     -- g' = min(g, L), u' = clamp(u, -L, L),
                 h = g' * sigmoid(alpha g') * (u' + beta); defaults alpha = 1,
                 beta = 0, no clamp: sglang PR #39920 "Modifications" and
@@ -330,6 +338,49 @@ def dequant_int4_g32(packed, scale_bits):
     return nib * np.repeat(bf16_decode(scale_bits), 32, axis=1)
 
 
+def e2m1_decode(codes) -> np.ndarray:
+    """4-bit e2m1 element code -> value: bit 3 sign, bits 2..1 exponent e
+    (bias 1), bit 0 mantissa m; sign * 2^(e-1) * (1 + m/2) for e >= 1 and
+    sign * m/2 for e == 0 (no infinities or NaN). The eight magnitudes are
+    0, 0.5, 1, 1.5, 2, 3, 4, 6."""
+    c = np.asarray(codes, dtype=np.int64) & 0xF
+    sign = np.where(c & 0x8, -1.0, 1.0)
+    e = (c >> 1) & 0x3
+    m = (c & 0x1).astype(np.float64)
+    val = np.where(e == 0, m / 2.0,
+                   np.ldexp(1.0 + m / 2.0, (e - 1).astype(np.int32)))
+    return sign * val
+
+
+def _nibbles(packed):
+    """[N][K/2] bytes -> [N][K] 4-bit codes; byte j holds k = 2j in its low
+    nibble and k = 2j + 1 in its high nibble."""
+    b = np.asarray(packed, dtype=np.uint8).astype(np.int64)
+    N, Kh = b.shape
+    nib = np.empty((N, 2 * Kh), dtype=np.int64)
+    nib[:, 0::2] = b & 0xF
+    nib[:, 1::2] = b >> 4
+    return nib
+
+
+def dequant_nvfp4(packed, scale_codes):
+    """NVFP4: w[n, k] = e2m1(code[n, k]) * e4m3(scale[n, k // 16]); the
+    per-tensor fp32 global scale (here per expert, per half of W13) is
+    applied by the caller."""
+    return e2m1_decode(_nibbles(packed)) * np.repeat(e4m3_decode(scale_codes), 16, axis=1)
+
+
+def e8m0_decode(codes) -> np.ndarray:
+    """e8m0 scale code -> 2^(e - 127); 0xFF is NaN."""
+    e = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    return np.where(e == 0xFF, np.nan, np.ldexp(1.0, (e - 127).astype(np.int32)))
+
+
+def dequant_mxfp4(packed, scale_codes):
+    """MXFP4: w[n, k] = e2m1(code[n, k]) * 2^(scale[n, k // 32] - 127)."""
+    return e2m1_decode(_nibbles(packed)) * np.repeat(e8m0_decode(scale_codes), 32, axis=1)
+
+
 def dequant(fmt, q, s):
     if fmt == "bf16":
         return bf16_decode(q)
@@ -337,6 +388,10 @@ def dequant(fmt, q, s):
         return dequant_fp8_block(q, s)
     if fmt == "int4":
         return dequant_int4_g32(q, s)
+    if fmt == "nvfp4":
+        return dequant_nvfp4(q, s)
+    if fmt == "mxfp4":
+        return dequant_mxfp4(q, s)
     raise ValueError(fmt)
 
 
@@ -372,6 +427,16 @@ def w13_dequant(spec, arr, e):
         gs = np.asarray(arr["gs"][e], dtype=np.float32).astype(np.float64)
         w[:I] *= gs[0]
         w[I:] *= gs[1]
+    return w
+
+
+def w2_dequant(spec, arr, e):
+    """Dequantised down weight of group e, times its global scale when
+    present (FP4 layers: one fp32 per expert)."""
+    w = dequant(spec.fmt, arr["w2_q"][e],
+                None if arr["w2_s"] is None else arr["w2_s"][e])
+    if arr.get("gs2") is not None:
+        w *= float(np.float32(arr["gs2"][e]))
     return w
 
 
@@ -517,8 +582,7 @@ def expert_ffn(spec, arr, e, xhat_rows, x_bf16_rows, detail=False, adapters=None
     al, be, L = f32(spec.alpha), f32(spec.beta), f32(spec.limit)
     h = swiglu(g, u, al, be, L)
     hhat = requant_fp8(h) if spec.fmt == "fp8" else bf16_round(h)
-    w2 = dequant(spec.fmt, arr["w2_q"][e],
-                 None if arr["w2_s"] is None else arr["w2_s"][e])
+    w2 = w2_dequant(spec, arr, e)
     y = hhat @ w2.T                                # [m, H]
     down = lora and spec.lora_down
     if down:

@@ -2,7 +2,8 @@
 
 This module only DRAWS inputs: random activations, router logits and expert
 weights stored in the formats the path consumes (bf16, fp8-e4m3 with fp32
-128x128 block scales, packed int4 with bf16 group-32 scales). It holds none of
+128x128 block scales, packed int4 with bf16 group-32 scales, packed e2m1
+with e4m3 block-16 or e8m0 block-32 scales). It holds none of
 the path's arithmetic: no routing, no permutation, no activation quantisation,
 no GEMM, no SwiGLU, no combine. Weight quantisation to e4m3 uses torch's own
 float8_e4m3fn conversion, as an offline quantiser would.
@@ -17,6 +18,9 @@ Workload shapes follow the MoE layers named on the pages:
     PR #445, "Summary".
   * INT4 group-32 weights, w_packed [N, K/2] u8 with low nibble = even K and
     scale [N, K/32] bf16 -- batchgen PR #239, commit text.
+  * NVFP4 expert weights with distinct per-half global scales -- the
+    MoE-LoRA release notes, "Changes since 1b699bf" (and MXFP4 at the INT4
+    layer's shape).
   * Inkling [T, 258] gate rows (256 routed + 2 shared-sink columns) with ties,
     all-negative rows and a dominating sink -- sglang PR #36385, "Correctness".
   * distinct gate/up global scales with up/gate ratio 0.52-1.22 and a rank-16
@@ -35,6 +39,9 @@ import torch
 FMT_BF16 = "bf16"
 FMT_FP8 = "fp8"
 FMT_INT4 = "int4"
+FMT_NVFP4 = "nvfp4"
+FMT_MXFP4 = "mxfp4"
+FP4_FORMATS = (FMT_NVFP4, FMT_MXFP4)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -102,6 +109,20 @@ CONFIGS = {
         gscale=True, logits="mix258", Ts=(1, 37, 512, 8192)),
 }
 
+# The same expert-parallel LoRA layer in the weight format the MoE-LoRA
+# release serves (NVFP4 with distinct gate/up global scales), and the INT4
+# layer's shape with MXFP4 weights.
+FP4_CONFIGS = {
+    "nvfp4_lora_258": LayerSpec(
+        name="nvfp4_lora_258", cfg_id=6, fmt=FMT_NVFP4, H=2048, I=1024,
+        n_routed=256, n_sink=2, top_k=8, E_loc=32, offset=96, lora_rank=16,
+        lora_down=True,
+        gscale=True, logits="mix258", Ts=(1, 37, 512, 8192)),
+    "mxfp4_g32_64": LayerSpec(
+        name="mxfp4_g32_64", cfg_id=7, fmt=FMT_MXFP4, H=2048, I=768,
+        n_routed=64, top_k=8, Ts=(1, 64, 2048)),
+}
+
 
 def _seed(*parts: int) -> int:
     ss = np.random.SeedSequence([int(p) & 0xFFFFFFFF for p in parts])
@@ -130,7 +151,8 @@ def _fp8_block_quant(w: torch.Tensor):
 class Layer:
     spec: LayerSpec
     w13_q: torch.Tensor           # [G, 2I, H] (bf16 | e4m3fn) or [G, 2I, H/2] u8
-    w13_s: Optional[torch.Tensor]  # fp8: [G, 2I/128, H/128] f32; int4: [G, 2I, H/32] bf16
+    w13_s: Optional[torch.Tensor]  # fp8: [G, 2I/128, H/128] f32; int4: [G, 2I, H/32] bf16;
+                                   # nvfp4: [G, 2I, H/16] e4m3fn; mxfp4: [G, 2I, H/32] u8
     w2_q: torch.Tensor            # [G, H, I] or [G, H, I/2] u8
     w2_s: Optional[torch.Tensor]
     gs: Optional[torch.Tensor]    # [G, 2] f32 (gate, up) or None
@@ -139,6 +161,7 @@ class Layer:
     w_router: Optional[torch.Tensor]  # [H, E] f64 (router GEMM input recipe)
     lora_A2: Optional[torch.Tensor] = None  # [G, r, I] bf16 (down LoRA)
     lora_B2: Optional[torch.Tensor] = None  # [G, H, r] bf16
+    gs2: Optional[torch.Tensor] = None      # [G] f32 W2 global scales (NVFP4)
 
 
 @dataclasses.dataclass
@@ -150,7 +173,8 @@ class Batch:
 
 
 def _rand_weights(spec: LayerSpec, N: int, K: int, std: float, gen, device,
-                  half_scale: Optional[torch.Tensor] = None):
+                  half_scale: Optional[torch.Tensor] = None,
+                  fp4_scale_codes: tuple = (0x08, 0x18)):
     """One expert's [N, K] matrix in the spec's storage format."""
     if spec.fmt == FMT_BF16:
         w = torch.randn(N, K, generator=gen, device=device) * std
@@ -166,6 +190,21 @@ def _rand_weights(spec: LayerSpec, N: int, K: int, std: float, gen, device,
                           dtype=torch.int32).to(torch.uint8)
         s = (torch.rand(N, K // 32, generator=gen, device=device) * 0.015
              + 0.005).to(torch.bfloat16)
+        return q, s
+    if spec.fmt in FP4_FORMATS:
+        # uniform e2m1 codes (RMS 2.93); the scale codes set the magnitude
+        q = torch.randint(0, 256, (N, K // 2), generator=gen, device=device,
+                          dtype=torch.int32).to(torch.uint8)
+        if spec.fmt == FMT_NVFP4:
+            # e4m3 codes lo..hi-1 (W13: 2^-6 .. 0.117; W2: from 2^-7, so
+            # subnormal scale codes 4..7 occur)
+            lo, hi = fp4_scale_codes
+            s = torch.randint(lo, hi, (N, K // 16), generator=gen, device=device,
+                              dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+        else:
+            # e8m0 exponents 119..123: 2^-8 .. 2^-4
+            s = torch.randint(119, 124, (N, K // 32), generator=gen, device=device,
+                              dtype=torch.int32).to(torch.uint8)
         return q, s
     raise ValueError(spec.fmt)
 
@@ -185,7 +224,7 @@ def make_layer(spec: LayerSpec, device="cpu") -> Layer:
         g = _gen(device, spec.cfg_id, 1000 + e)
         a, b = _rand_weights(spec, 2 * I, H, std13, g, device,
                              None if gs is None else gs[e])
-        c, d = _rand_weights(spec, H, I, std2, g, device)
+        c, d = _rand_weights(spec, H, I, std2, g, device, fp4_scale_codes=(0x04, 0x14))
         q13.append(a); s13.append(b); q2.append(c); s2.append(d)
     st = lambda xs: None if xs[0] is None else torch.stack(xs).contiguous()
     # a batch of adapters stacks them first: [n_adapters, G, ...]
@@ -216,8 +255,12 @@ def make_layer(spec: LayerSpec, device="cpu") -> Layer:
                    / math.sqrt(I)).to(torch.bfloat16)
         lora_B2 = (torch.randn(*lead, H, r, generator=g, device=device)
                    * (0.5 / math.sqrt(r))).to(torch.bfloat16)
+    gs2 = None
+    if spec.fmt == FMT_NVFP4:
+        g = _gen(device, spec.cfg_id, 7007)
+        gs2 = (torch.rand(G, generator=g, device=device) + 0.5).float().contiguous()
     return Layer(spec, st(q13), st(s13), st(q2), st(s2), gs, lora_A, lora_B,
-                 w_router, lora_A2, lora_B2)
+                 w_router, lora_A2, lora_B2, gs2)
 
 
 def _logits_mix258(spec: LayerSpec, T: int, g, device) -> torch.Tensor:
@@ -316,7 +359,7 @@ def to_numpy_layer(layer: Layer, experts=None) -> dict:
         return t.numpy()
     return {k: cp(getattr(layer, k)) for k in
             ("w13_q", "w13_s", "w2_q", "w2_s", "gs", "lora_A", "lora_B",
-             "lora_A2", "lora_B2")}
+             "lora_A2", "lora_B2", "gs2")}
 
 
 def to_numpy_batch(batch: Batch) -> dict:

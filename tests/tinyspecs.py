@@ -22,3 +22,11 @@ TINY = {
 # eight adapters in one batch (tokens pick one or none)
 TINY["ep_lora_multi"] = TINY["ep_lora"].scaled(name="tiny_ep_lora_multi_t", cfg_id=106,
                                                n_adapters=8)
+# NVFP4 weights with per-half W13 and per-expert W2 global scales, LoRA on
+# both projections; MXFP4 with a shared expert
+TINY["nvfp4_lora"] = LayerSpec(name="tiny_nvfp4_lora_t", cfg_id=107, fmt="nvfp4",
+                               H=128, I=128, n_routed=8, n_sink=2, top_k=3, E_loc=3,
+                               offset=2, lora_rank=4, gscale=True, logits="mix258",
+                               route_scale=1.5, lora_down=True)
+TINY["mxfp4_shared"] = LayerSpec(name="tiny_mxfp4_t", cfg_id=108, fmt="mxfp4", H=128,
+                                 I=128, n_routed=4, top_k=2, shared=1, limit=7.0)
