@@ -168,11 +168,11 @@ def main():
     import torch
 
     import mixture_experts_expert_sigmoid_amd as M
-    from synth import CONFIGS, make_batch, make_layer
+    from synth import CONFIGS, FP4_CONFIGS, make_batch, make_layer
     from tests.gpu_helpers import module_for
 
     assert torch.cuda.is_available(), "bench needs a GPU"
-    spec = CONFIGS[args.profile_config if args.profile else WORKLOAD]
+    spec = {**CONFIGS, **FP4_CONFIGS}[args.profile_config if args.profile else WORKLOAD]
     t0 = time.time()
     layer = make_layer(spec, device="cuda")
     torch.cuda.synchronize()
@@ -363,7 +363,7 @@ def config_table(args, stream, flush):
     touched-weight GB/s and useful TFLOP/s (stderr): back to back, and the
     median with the MALL flushed before every step (the rates use that)."""
     import torch
-    from synth import CONFIGS, make_batch, make_layer
+    from synth import CONFIGS, FP4_CONFIGS, make_batch, make_layer
     from tests.gpu_helpers import module_for
     print("# config              T    ms/step  flushed-med  flushed-min    tokens/s"
           "    TFLOP/s  weight GB/s", file=sys.stderr)
@@ -372,6 +372,9 @@ def config_table(args, stream, flush):
     table = dict(CONFIGS)
     table["ep_lora_258_x8"] = CONFIGS["ep_lora_258"].scaled(
         name="ep_lora_258_x8", cfg_id=15, n_adapters=8)
+    # the EP + LoRA layer in NVFP4 (the page's own weight format) and the
+    # INT4 layer's shape in MXFP4
+    table.update(FP4_CONFIGS)
     for name, spec in table.items():
         layer = make_layer(spec, device="cuda")
         mod = module_for(spec, layer)

@@ -12,7 +12,8 @@
  *   [INT4-PR]  "sm100: Fused INT4 grouped + SiLU Triton kernel"
  *              (batchgen PR #239)
  *   [LORA-AOT] "FlashInfer 0.6.18 SM100a+SM103a MoE-LoRA AOT -- SwiGLU LoRA
- *              up-delta units, EP scale lookups" (release notes)
+ *              up-delta units, EP scale lookups" (release notes); it serves
+ *              NVFP4 expert weights with distinct gate/up global scales
  *
  * Conventions for every entry point:
  *   - Every array argument is DEVICE memory owned by the caller (plain
@@ -58,9 +59,19 @@ typedef enum {
   MOE_W_FP8_B128 = 1,  /* OCP e4m3fn [G][N][K]; scale fp32 [G][N/128][K/128]
                           (w = q * scale, 128x128 blocks) [CLAMP-PR
                           "Modifications": blockwise 128x128 FP8] */
-  MOE_W_INT4_G32 = 2   /* u8 [G][N][K/2] (byte j of a row: low nibble k=2j,
+  MOE_W_INT4_G32 = 2,  /* u8 [G][N][K/2] (byte j of a row: low nibble k=2j,
                           high nibble k=2j+1); scale bf16 [G][N][K/32];
                           w = (nibble - 8) * scale [INT4-PR commit text] */
+  MOE_W_NVFP4 = 3,     /* e2m1 codes packed like INT4, u8 [G][N][K/2];
+                          scale e4m3fn u8 [G][N][K/16]; w = e2m1(code) *
+                          e4m3(scale) * gscale [LORA-AOT "Changes since
+                          1b699bf": per-half NVFP4 global scales]. e2m1:
+                          sign bit 3, magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6.
+                          NaN scale codes (0x7F, 0xFF) are not supported. */
+  MOE_W_MXFP4 = 4      /* e2m1 codes as NVFP4; scale e8m0 u8 [G][N][K/32];
+                          w = e2m1(code) * 2^(scale - 127). Exact for scale
+                          exponents 104..128 (2^-23 .. 2); others are
+                          clamped to 99..128, giving wrong values. */
 } moe_wfmt;
 
 /* err_word bits */
@@ -84,11 +95,16 @@ typedef struct {
                            W2 N = H, K = I */
   const void *q;        /* codes, layout per moe_wfmt */
   const void *scale;    /* scales, layout per moe_wfmt (NULL for BF16) */
-  const float *gscale;  /* W13 only, nullable: fp32 [G][2] = (gate, up)
+  const float *gscale;  /* nullable. W13: fp32 [G][2] = (gate, up)
                            per-expert global scales multiplying the dequantised
                            gate rows 0..I-1 and up rows I..2I-1; the "true
-                           units" of [LORA-AOT "Changes since 1b699bf"] */
+                           units" of [LORA-AOT "Changes since 1b699bf"].
+                           W2: NVFP4 / MXFP4 only (else MOE_ERR_FORMAT),
+                           fp32 [G], one per expert. */
 } moe_weights;
+/* Alignment (MOE_ERR_PARAM): 4-bit codes 16 bytes; INT4 and NVFP4 scales
+ * 2 bytes. Activations of 4-bit layers enter the matrix cores as f16:
+ * exact for |x| in [2^-14, 65504] (and h alike). */
 
 /* Rank-r LoRA of the local experts [LORA-AOT "Changes since 1b699bf"].
  * On the fused gate/up projection ("lora"): z = x A_e^T (fp32),
@@ -214,22 +230,22 @@ int moe_quantize_act_fp8(const void *x_bf16, long T, int H, void *xq,
  *   FP8 weights: x = xq e4m3fn [T][H] with xs fp32 [T][H/128]; h is
  *     re-quantised like moe_quantize_act_fp8 per row and 128 columns:
  *     h e4m3fn [P_cap][I], hs fp32 [P_cap][I/128].
- *   BF16 / INT4 weights: x bf16 [T][H] (xs NULL); h bf16 [P_cap][I]
- *     (round-to-nearest-even), hs NULL.
+ *   BF16 / 4-bit (INT4, NVFP4, MXFP4) weights: x bf16 [T][H] (xs NULL);
+ *     h bf16 [P_cap][I] (round-to-nearest-even), hs NULL.
  * x_bf16 bf16 [T][H] is the LoRA input (NULL without LoRA).
  * h_lora (FP8 weights only, else it must be NULL: MOE_ERR_PARAM), nullable:
  * bf16 [P_cap][I], the SwiGLU output before the re-quantisation (round to
- * nearest even), i.e. the down-LoRA input; BF16 / INT4 layers pass h itself
+ * nearest even), i.e. the down-LoRA input; BF16 / 4-bit layers pass h itself
  * to moe_grouped_gemm2_combine instead.
  * offsets / sorted_pair come from moe_permute for the same (T, top_k);
  * w13->n_groups = G, w13->N = 2I, w13->K = H. p_cap = rows allocated in h.
  * Limits: H % 128 == 0 and I % 128 == 0. Workspace:
  * moe_gemm1_workspace_size(w13, p_cap, lora) bytes: the LoRA z rows; for
- * FP8 / INT4 weights at decode sizes (few enough tiles of 32 rows x 128 h
+ * FP8 / 4-bit weights at decode sizes (few enough tiles of 32 rows x 128 h
  * columns that one tile per workgroup would leave CUs idle) the fp32
  * partial sums of a split-K schedule (4 * p_cap * 2I floats), which spreads
  * the K blocks of those tiles over all CUs and reduces them in a fixed
- * order; for INT4 weights the f16 copy of the activations (p_cap * H * 2
+ * order; for 4-bit weights the f16 copy of the activations (p_cap * H * 2
  * bytes, T <= p_cap). Returns 0 for a NULL w13 or N not a multiple of 256. */
 int moe_grouped_gemm1_act(const moe_weights *w13, const void *x,
                           const float *xs, const void *x_bf16, long T, int H,
@@ -243,10 +259,11 @@ size_t moe_gemm1_workspace_size(const moe_weights *w13, long p_cap,
 
 /* ---------------------------------------- grouped GEMM2 + weighted combine -- */
 /* y[r] = h[r] W2_g^T (fp32; FP8 per 128-K block partial sums times
- * hs[r][kb] * scale[g][nb][kb]) for every sorted row, plus with lora_down
+ * hs[r][kb] * scale[g][nb][kb]; FP4 times w2->gscale[g] when given) for
+ * every sorted row, plus with lora_down
  * the down-LoRA delta scale * (h_lora[r] A2_g^T) B2_g^T for groups
  * g < lora_down->n_groups (h_lora bf16 [P_cap][I]: GEMM1's h_lora output
- * for FP8 weights, h itself for BF16 / INT4), then
+ * for FP8 weights, h itself for BF16 / 4-bit weights), then
  *   out[t][:] = sum_{j < top_k, pair_row[t*top_k+j] >= 0} topk_w[t][j] *
  *               y[pair_row[t*top_k+j]]   (ascending j, fp32)
  *             + shared_w * y[pair_row[T*top_k + t]]   (if shared_expert)
@@ -254,7 +271,7 @@ size_t moe_gemm1_workspace_size(const moe_weights *w13, long p_cap,
  * Every out element is written (0 for a token with no local pair).
  * w2->N = H, w2->K = I. out fp32 [T][H]. Workspace:
  * moe_gemm2_workspace_size(w2, p_cap, lora_down) bytes: the fp32 y rows, or
- * for FP8 / INT4 weights at decode sizes their split-K partial sums
+ * for FP8 / 4-bit weights at decode sizes their split-K partial sums
  * (4 * p_cap * H floats, reduced by the combine in a fixed order; the
  * down-LoRA delta enters the first partial of each tile), then the
  * down-LoRA z2 rows (p_cap * rank floats, plus p_cap ints with a batch of

@@ -22,7 +22,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "moe_mi355x.h")
 
-MOE_W_BF16, MOE_W_FP8_B128, MOE_W_INT4_G32 = 0, 1, 2
+MOE_W_BF16, MOE_W_FP8_B128, MOE_W_INT4_G32, MOE_W_NVFP4, MOE_W_MXFP4 = 0, 1, 2, 3, 4
+_PACKED4 = (MOE_W_INT4_G32, MOE_W_NVFP4, MOE_W_MXFP4)
 MOE_DEVERR_GLOBAL_ID_OOB = 0x1
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE",
           -3: "MOE_ERR_FORMAT", -4: "MOE_ERR_LOCAL_RANGE", -5: "MOE_ERR_PARAM",
@@ -140,9 +141,10 @@ def _check(status: int, where: str):
 
 def weights(fmt: int, q: torch.Tensor, scale: Optional[torch.Tensor] = None,
             gscale: Optional[torch.Tensor] = None) -> MoeWeights:
-    """Descriptor of a stacked [G][N][K] weight (INT4: q is [G][N][K/2])."""
+    """Descriptor of a stacked [G][N][K] weight (4-bit formats: q is
+    [G][N][K/2]). gscale: W13 [G][2] (gate, up), W2 [G] (FP4 formats)."""
     G, N, Kq = q.shape
-    K = 2 * Kq if fmt == MOE_W_INT4_G32 else Kq
+    K = 2 * Kq if fmt in _PACKED4 else Kq
     w = MoeWeights(fmt, G, N, K, q.data_ptr(),
                    None if scale is None else scale.data_ptr(),
                    None if gscale is None else gscale.data_ptr())
@@ -295,7 +297,8 @@ class MoeModule:
     the outputs and a workspace with torch and calls moe_forward."""
 
     def __init__(self, *, fmt, H, I, num_experts_global, top_k, w13_q, w2_q,
-                 w13_s=None, w2_s=None, gscale=None, num_local_experts=None,
+                 w13_s=None, w2_s=None, gscale=None, gscale2=None,
+                 num_local_experts=None,
                  local_expert_offset=0, shared_expert=0, n_sink=0,
                  route_scale=1.0, global_scale=1.0, shared_w=1.0, alpha=1.0,
                  beta=0.0, limit=math.inf, lora_A=None, lora_B=None,
@@ -304,7 +307,7 @@ class MoeModule:
         self.shared_expert = shared_expert
         E_loc = num_experts_global if num_local_experts is None else num_local_experts
         self.w13 = weights(fmt, w13_q, w13_s, gscale)
-        self.w2 = weights(fmt, w2_q, w2_s)
+        self.w2 = weights(fmt, w2_q, w2_s, gscale2)
         self.act = act_params(alpha, beta, limit)
         self.lora = lora_desc(lora_A, lora_B, lora_scale) if lora_A is not None else None
         self.lora_down = (lora_desc(lora_A2, lora_B2, lora_scale)

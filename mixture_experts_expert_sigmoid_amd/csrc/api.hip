@@ -29,13 +29,24 @@ inline size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
 constexpr int kMaxAdapters = 1024;
 inline bool finite(float v) { return isfinite(v); }
 
-int check_weights(const moe_weights* w, int N, int K) {
+// 4-bit formats: packed codes, the 4-bit kernel family, bf16 h
+bool is4(int fmt) {
+  return fmt == MOE_W_INT4_G32 || fmt == MOE_W_NVFP4 || fmt == MOE_W_MXFP4;
+}
+bool is_fp4(int fmt) { return fmt == MOE_W_NVFP4 || fmt == MOE_W_MXFP4; }
+
+// w2: the down weight, whose global scales ([G]) only FP4 formats take
+int check_weights(const moe_weights* w, int N, int K, bool w2 = false) {
   if (!w || !w->q) return MOE_ERR_NULL;
-  if (w->fmt != MOE_W_BF16 && w->fmt != MOE_W_FP8_B128 && w->fmt != MOE_W_INT4_G32)
-    return MOE_ERR_FORMAT;
+  if (w->fmt < MOE_W_BF16 || w->fmt > MOE_W_MXFP4) return MOE_ERR_FORMAT;
   if (w->fmt != MOE_W_BF16 && !w->scale) return MOE_ERR_NULL;
+  if (w2 && w->gscale && !is_fp4(w->fmt)) return MOE_ERR_FORMAT;
   if (w->N != N || w->K != K) return MOE_ERR_SHAPE;
   if (w->n_groups < 1 || w->n_groups > 1024) return MOE_ERR_SHAPE;
+  // 16-byte code loads; 2-byte scale words (INT4 bf16, NVFP4 e4m3 pairs)
+  if (is4(w->fmt) && ((uintptr_t)w->q & 15)) return MOE_ERR_PARAM;
+  if ((w->fmt == MOE_W_INT4_G32 || w->fmt == MOE_W_NVFP4) && ((uintptr_t)w->scale & 1))
+    return MOE_ERR_PARAM;
   return MOE_OK;
 }
 
@@ -195,7 +206,7 @@ int moe_quantize_act_fp8(const void* x_bf16, long T, int H, void* xq,
 
 namespace {
 // GEMM1 workspace: LoRA z rows, then (split-K) the fp32 partial sums, then
-// (INT4) the f16 activations, T <= p_cap rows of K
+// (4-bit formats) the f16 activations, T <= p_cap rows of K
 // LoRA z rows, and with a batch of adapters each row's adapter
 size_t g1_z_bytes(long p_cap, const moe_lora* lora) {
   if (!lora) return 0;
@@ -209,7 +220,7 @@ size_t g1_part_bytes(const moe_weights* w13, long p_cap) {
   return moe::splitk_bytes(p_cap, w13->N);
 }
 size_t g1_x16_bytes(const moe_weights* w13, long rows) {
-  return w13->fmt == MOE_W_INT4_G32 ? al((size_t)rows * w13->K * 2) : 0;
+  return is4(w13->fmt) ? al((size_t)rows * w13->K * 2) : 0;
 }
 // GEMM2 workspace: fp32 y rows, or (split-K) their partial sums
 size_t g2_bytes(const moe_weights* w2, long p_cap) {
@@ -293,12 +304,12 @@ int moe_grouped_gemm1_act(const moe_weights* w13, const void* x,
   int st = gemm1_checks(w13, x, xs, x_bf16, T, H, I, top_k, p_cap, offsets,
                         sorted_pair, act, lora, h, hs);
   if (st) return st;
-  // BF16 / INT4 layers write h in bf16 already: it is the down-LoRA input
+  // BF16 / 4-bit layers write h in bf16 already: it is the down-LoRA input
   if (h_lora && w13->fmt != MOE_W_FP8_B128) return MOE_ERR_PARAM;
   size_t need = moe_gemm1_workspace_size(w13, p_cap, lora);
   if (need && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
-  if (w13->fmt == MOE_W_INT4_G32 && T > p_cap) return MOE_ERR_SHAPE;
+  if (is4(w13->fmt) && T > p_cap) return MOE_ERR_SHAPE;
   float* z = (float*)ws;
   float* part = g1_part_bytes(w13, p_cap)
                     ? (float*)((char*)ws + g1_z_bytes(p_cap, lora)) : nullptr;
@@ -330,7 +341,7 @@ static int gemm2_checks(const moe_weights* w2, const void* h, const float* hs,
   if (H < 128 || I < 128 || H % 128 || I % 128) return MOE_ERR_SHAPE;
   if (shared != 0 && shared != 1) return MOE_ERR_PARAM;
   if (!finite(shared_w)) return MOE_ERR_PARAM;
-  int st = check_weights(w2, H, I);
+  int st = check_weights(w2, H, I, true);
   if (st) return st;
   if (!offsets) return MOE_ERR_NULL;
   if (p_cap > 0 && (!h || (w2->fmt == MOE_W_FP8_B128 && !hs))) return MOE_ERR_NULL;
@@ -368,6 +379,7 @@ int moe_grouped_gemm2_combine(const moe_weights* w2, const void* h,
   a.fmt = w2->fmt;
   a.wq = w2->q;
   a.ws = w2->scale;
+  a.gscale = w2->gscale;
   a.h = h;
   a.hs = hs;
   a.H = H;
@@ -414,13 +426,13 @@ FwdLayout layout(const moe_layer* L, long T) {
   o.pair_row = take((size_t)pc * 4);
   o.perm_bytes = moe::permute_ws_bytes(T, L->top_k, G);
   o.perm_ws = take(o.perm_bytes);
-  // FP8 activation codes, or (INT4) the f16 activations
+  // FP8 activation codes, or (4-bit formats) the f16 activations
   o.xq = take(fp8 ? (size_t)T * L->H : g1_x16_bytes(&L->w13, T));
   o.xs = take(fp8 ? (size_t)T * (L->H / 128) * 4 : 0);
   o.z = take(g1_z_bytes(pc, L->lora));
   o.h = take((size_t)pc * L->I * (fp8 ? 1 : 2));
   o.hs = take(fp8 ? (size_t)pc * (L->I / 128) * 4 : 0);
-  // down LoRA: its bf16 input (FP8 layers; BF16 / INT4 read h) and z rows
+  // down LoRA: its bf16 input (FP8 layers; BF16 / 4-bit layers read h) and z rows
   o.h_lora = take(fp8 && L->lora_down ? (size_t)pc * L->I * 2 : 0);
   o.z2 = take(g1_z_bytes(pc, L->lora_down));
   // y rows (or their stream-K partials); GEMM1's partials, consumed before
@@ -439,7 +451,7 @@ int layer_checks(const moe_layer* L) {
   if (st) return st;
   int G = L->num_local_experts + L->shared_expert;
   if ((st = check_weights(&L->w13, 2 * L->I, L->H))) return st;
-  if ((st = check_weights(&L->w2, L->H, L->I))) return st;
+  if ((st = check_weights(&L->w2, L->H, L->I, true))) return st;
   if (L->w13.n_groups != G || L->w2.n_groups != G) return MOE_ERR_SHAPE;
   if (L->w13.fmt != L->w2.fmt) return MOE_ERR_FORMAT;
   if ((st = check_act(&L->act))) return st;
@@ -533,6 +545,7 @@ int moe_forward(const moe_layer* L, const void* x_bf16, const float* logits,
   a.fmt = L->w2.fmt;
   a.wq = L->w2.q;
   a.ws = L->w2.scale;
+  a.gscale = L->w2.gscale;
   a.h = h;
   a.hs = fp8 ? hs : nullptr;
   a.H = L->H;

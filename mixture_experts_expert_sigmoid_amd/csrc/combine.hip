@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
   *(f32x4*)(out + t * H + 4 * c4) = acc;
 }
 
-// The same combine over the partial sums of the FP8 / INT4 GEMM2's split-K
+// The same combine over the partial sums of the FP8 / 4-bit GEMM2's split-K
 // kernel (slots [kSkSlots][p_rows][H]): each y element is first summed over
 // the slots of its tile in slot order. The tile schedule is rebuilt exactly as
 // the GEMM built it (32-row tiles, 256-column tiles, I / 128 K blocks). One

@@ -2,8 +2,8 @@
 // [gate | up] weight with the parameterized-SwiGLU epilogue (plus optional
 // per-half global scales and LoRA delta), and GEMM2 (down) writing fp32 rows
 // for the weighted combine. Blockwise-FP8 layers use the kernels of
-// gemm_fp8.hip, group-32 INT4 layers those of gemm_int4.hip; this file also
-// holds the host dispatch for all three formats.
+// gemm_fp8.hip, 4-bit layers (INT4, NVFP4, MXFP4) those of gemm_w4.h; this
+// file also holds the host dispatch for every format.
 //
 // Epilogue: g' = min(g, L), u' = clamp(u, -L, L), h = g' sigmoid(alpha g')
 // (u' + beta) ("[Moe] Fix flashinfer_trtllm silently dropping swiglu_limit
@@ -289,17 +289,17 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t s) {
   P.hs = a.hs;
   P.h_lora = (uint16_t*)a.h_lora;
   long hint = a.G > 0 ? a.p_cap / a.G : a.p_cap;
-  if (a.fmt == FMT_FP8 || a.fmt == FMT_INT4) {
+  if (a.fmt != FMT_BF16) {
     const bool fp8 = a.fmt == FMT_FP8;
     hipError_t e = hipSuccess;
-    if (!fp8) {                    // f16 activations in the INT4 kernel's K order
+    if (!fp8) {                    // f16 activations in the 4-bit kernel's K order
       e = launch_act_f16p(a.x, a.T, a.H, a.x16, s);
       if (e != hipSuccess) return e;
       P.a = (const uint8_t*)a.x16;
     }
     auto run = [&](int* grid) {
       return fp8 ? launch_gemm_fp8(P, true, a.p_cap, a.I / 128, s, grid)
-                 : launch_gemm_int4(P, true, a.p_cap, a.I / 128, s, grid);
+                 : launch_gemm_w4(a.fmt, P, true, a.p_cap, a.I / 128, s, grid);
     };
     if (!a.part) return run(nullptr);
     P.part = a.part;
@@ -323,6 +323,7 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t s) {
   P.G = a.G;
   P.offsets = a.offsets;
   P.I = a.I;
+  P.gscale = a.gscale;
   P.y = a.y;
   P.z = a.z;
   P.lora_B = (const uint16_t*)a.lora_B;
@@ -334,7 +335,7 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t s) {
   long hint = a.G > 0 ? a.p_cap / a.G : a.p_cap;
   *a.sk_grid = 0;
   const int NT = (a.H + 255) / 256;
-  if (a.fmt == FMT_FP8 || a.fmt == FMT_INT4) {
+  if (a.fmt != FMT_BF16) {
     const bool fp8 = a.fmt == FMT_FP8;
     int* grid = nullptr;
     if (splitk_use(a.fmt, a.p_cap, a.G, NT, a.I / 128)) {
@@ -343,13 +344,13 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t s) {
       grid = a.sk_grid;
     }
     return fp8 ? launch_gemm_fp8(P, false, a.p_cap, NT, s, grid)
-               : launch_gemm_int4(P, false, a.p_cap, NT, s, grid);
+               : launch_gemm_w4(a.fmt, P, false, a.p_cap, NT, s, grid);
   }
   return dispatch<false>(P, a.p_cap, NT, hint, s);
 }
 
 bool splitk_use(int fmt, long p_cap, int G, int NT, int NS) {
-  if ((fmt != FMT_FP8 && fmt != FMT_INT4) || p_cap <= 0) return false;
+  if (fmt == FMT_BF16 || p_cap <= 0) return false;
   const long tiles = std::min<long>(p_cap, G + p_cap / kSkBM) * NT;
   if (tiles > kSkMaxTiles) return false;
   const long waves = (tiles + kSkCUs - 1) / kSkCUs;

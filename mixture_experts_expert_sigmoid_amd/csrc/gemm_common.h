@@ -1,6 +1,6 @@
 // Shared pieces of the grouped expert GEMM kernels: parameters, the
 // device-side tile and split-K schedules, and the BF16 epilogue (the FP8 and
-// INT4 kernels have their own).
+// 4-bit kernels have their own).
 //
 // Epilogue semantics: g' = min(g, L), u' = clamp(u, -L, L),
 // h = g' sigmoid(alpha g') (u' + beta) ("[Moe] Fix flashinfer_trtllm silently
@@ -19,7 +19,7 @@
 
 namespace moe {
 
-enum { FMT_BF16 = 0, FMT_FP8 = 1, FMT_INT4 = 2 };
+enum { FMT_BF16 = 0, FMT_FP8 = 1, FMT_INT4 = 2, FMT_NVFP4 = 3, FMT_MXFP4 = 4 };
 
 constexpr int kThreads = 512;
 constexpr int kMaxGroups = 1024;
@@ -37,11 +37,13 @@ struct GemmParams {
   int top_k;
   // B side
   const uint8_t* w;          // [G][N][K] codes (bytes; INT4 packed)
-  const void* wsc;           // FP8 fp32 [G][N/128][K/128]; INT4 bf16 [G][N][K/32]
+  const void* wsc;           // FP8 fp32 [G][N/128][K/128]; INT4 bf16 [G][N][K/32];
+                             // NVFP4 e4m3 [G][N][K/16]; MXFP4 e8m0 [G][N][K/32]
   int N, K, G;
   const int* offsets;
   int I;
-  // GEMM1 epilogue
+  // global scales: GEMM1 [G][2] (gate, up) in the epilogue; GEMM2 (FP4
+  // formats) [G] after the K loop
   const float* gscale;
   float alpha, beta, limit;
   // LoRA delta of this GEMM (GEMM1: on [gate | up]; GEMM2: on the down
@@ -419,10 +421,16 @@ hipError_t launch_gemm_fp8(const GemmParams& P, bool g1, long p_cap, int NT, hip
 // fp8h: e4m3 h + scales (FP8 layers), else bf16 h (INT4 layers)
 hipError_t launch_gemm1_sk_epilogue(const GemmParams& P, int sk_grid, bool fp8h, hipStream_t s);
 
-// Group-32 INT4 grouped GEMM (gemm_int4.hip), same conventions; GEMM1
-// reads f16 activations prepared by launch_act_f16p.
+// 4-bit grouped GEMMs (gemm_w4.h: INT4, NVFP4, MXFP4), same conventions;
+// GEMM1 reads f16 activations prepared by launch_act_f16p.
+hipError_t launch_gemm_w4(int fmt, const GemmParams& P, bool g1, long p_cap, int NT,
+                          hipStream_t s, int* sk_grid = nullptr);
 hipError_t launch_gemm_int4(const GemmParams& P, bool g1, long p_cap, int NT, hipStream_t s,
-                            int* sk_grid = nullptr);
+                            int* sk_grid);
+hipError_t launch_gemm_nvfp4(const GemmParams& P, bool g1, long p_cap, int NT, hipStream_t s,
+                             int* sk_grid);
+hipError_t launch_gemm_mxfp4(const GemmParams& P, bool g1, long p_cap, int NT, hipStream_t s,
+                             int* sk_grid);
 hipError_t launch_act_f16p(const void* x, long T, int H, void* out, hipStream_t s);
 
 }  // namespace moe

@@ -1,400 +1,9 @@
-// Grouped GEMM for group-32 INT4 experts: GEMM1 over [gate | up] with the
-// parameterized SwiGLU epilogue writing bf16 h, and GEMM2 (down) writing
-// fp32 rows for the weighted combine.
-//
-// Format ("sm100: Fused INT4 grouped + SiLU Triton kernel", batchgen PR
-// #239, commit text): w[n][k] = (nibble - 8) * scale[n][k / 32], byte j of a
-// row holding k = 2j in its low nibble and k = 2j + 1 in its high nibble;
-// bf16 activations, fp32 accumulation.
-//
-// Arithmetic: each nibble is expanded in registers to the exact f16 value
-// (nibble - 8) * scale: an AND-OR with 0x6400 places a nibble n in the
-// mantissa of 1024 + n (or 1024 + 16 n for the second nibble of a byte),
-// one f16 subtraction leaves n - 8 (or 16 (n - 8)) exactly, and one f16
-// multiplication by the scale (or scale / 16) is exact because n - 8 has at
-// most 3 significant bits and a bf16 scale 8: the product fits f16's 11 for
-// scales in [2^-10, 2^15]. The products with f16 activations are formed on
-// v_mfma_f32_16x16x32_f16 and accumulated in fp32 across the whole K; no
-// per-block scaling step is needed (the scale is inside the operand).
-//
-// K order: the expansion of one dword (k0..k7 of a 32-K group) yields the
-// f16 values in the order k0, k4, k1, k5, k2, k6, k3, k7; the activations
-// are laid out with the same permutation of each 8 (by the f16 conversion
-// pass for GEMM1, while staging for GEMM2), so the dot products are
-// unchanged.
-//
-// Work split as in the FP8 kernel: 8 waves own BM rows of one expert and
-// 256 weight rows in two halves (GEMM1: 128 gate + the matching 128 up
-// rows; GEMM2: 256 output columns); wave w computes all BM rows of columns
-// 16w..16w+15 of both halves, weights go HBM -> registers (two 128-K blocks
-// in flight, 16 bytes per row and lane per block) and are expanded there;
-// the f16 activation block is staged in LDS (double buffered).
-#include "gemm_common.h"
+// Group-32 INT4 instantiation of the 4-bit grouped GEMM (gemm_w4.h), the
+// f16 activation pass its GEMM1 reads, and the format dispatch of the
+// 4-bit kernels (INT4 here, NVFP4 and MXFP4 in their own files).
+#include "gemm_w4.h"
 
 namespace moe {
-
-template <int BM>
-struct I4Geo {
-  static constexpr int MS = BM / 16;              // 16-row subtiles
-  static constexpr int A_BYTES = BM * 256;        // one K block, f16
-  static constexpr int A_CH = BM * 16;            // 16-byte chunks
-  static constexpr int A_PT = (A_CH + kThreads - 1) / kThreads;
-  static constexpr int STAGE = A_BYTES;
-  static constexpr int LDS = 2 * STAGE;
-};
-
-// f16 A rows are 256 bytes; chunk c of row r is stored at c ^ (r & 0b1011),
-// conflict-free for the fragment reads and the row-wise stores (the FP8
-// kernel's bf16 layout)
-__device__ __forceinline__ int i4_swz(int row, int c) { return c ^ (row & 11); }
-
-__device__ __forceinline__ f16x2 h2_bits(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
-
-// (a & m) | c in one v_and_or_b32 (m uniform: one scalar operand per VOP3)
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
-  return r;
-}
-
-// one dword of nibbles (k0..k7, low nibble first) -> the 8 exact f16 values
-// (n - 8) * s in the order k0, k4, k1, k5, k2, k6, k3, k7; s2 = (s, s),
-// s16 = (s / 16, s / 16)
-__device__ __forceinline__ f16x8 int4x8_f16(uint32_t w, f16x2 s2, f16x2 s16) {
-  const uint32_t w8 = w >> 8;
-  const f16x2 b1032 = h2_bits(0x64086408u), b1152 = h2_bits(0x64806480u);   // 1032, 1152
-  const f16x2 a = (h2_bits(and_or(w, 0x000F000Fu, 0x64006400u)) - b1032) * s2;
-  const f16x2 b = (h2_bits(and_or(w, 0x00F000F0u, 0x64006400u)) - b1152) * s16;
-  const f16x2 c = (h2_bits(and_or(w8, 0x000F000Fu, 0x64006400u)) - b1032) * s2;
-  const f16x2 d = (h2_bits(and_or(w8, 0x00F000F0u, 0x64006400u)) - b1152) * s16;
-  return (f16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
-// 8 bf16 (k0..k7) -> 8 f16 in the order k0, k4, k1, k5, k2, k6, k3, k7
-__device__ __forceinline__ f16x8 bf16x8_f16p(i32x4 v) {
-  float f[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t u = (uint32_t)v[i];
-    f[2 * i] = __uint_as_float(u << 16);
-    f[2 * i + 1] = __uint_as_float(u & 0xFFFF0000u);
-  }
-  return (f16x8){(_Float16)f[0], (_Float16)f[4], (_Float16)f[1], (_Float16)f[5],
-                 (_Float16)f[2], (_Float16)f[6], (_Float16)f[3], (_Float16)f[7]};
-}
-
-// Accumulator layout: acc[ms][ns][r] is activation row 16 ms + (lane % 16)
-// and weight column (ns ? hi : lo) + 16 wave + 4 (lane / 16) + r.
-template <int BM, bool G1, bool LORA>
-__device__ __forceinline__ void int4_epilogue(const GemmParams& P, const Tile& t,
-                                              f32x4 (&acc)[BM / 16][2], uint8_t* smem) {
-  constexpr int MS = BM / 16;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, lg = lane >> 4;
-  const int c0 = 16 * wave + 4 * lg;
-  const int g = t.g, row0 = t.row0, m = t.m;
-  if constexpr (!G1) {
-    const bool hi_ok = t.n_hi != t.n_lo;
-    if constexpr (LORA)
-      if (P.z && g < P.lora_groups) lora_delta_tile<BM>(P, t, acc, smem, hi_ok);   // down LoRA
-#pragma unroll
-    for (int ms = 0; ms < MS; ++ms) {
-      const int tr = 16 * ms + lr;
-      if (tr < m) {
-        float* yr = P.y + (long)(row0 + tr) * P.N;
-        *(f32x4*)(yr + t.n_lo + c0) = acc[ms][0];
-        if (hi_ok) *(f32x4*)(yr + t.n_hi + c0) = acc[ms][1];
-      }
-    }
-  } else {
-    if (P.gscale) {
-      const float gsg = P.gscale[2 * g], gsu = P.gscale[2 * g + 1];
-#pragma unroll
-      for (int ms = 0; ms < MS; ++ms)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          acc[ms][0][r] *= gsg;
-          acc[ms][1][r] *= gsu;
-        }
-    }
-    if constexpr (LORA)
-      if (P.z && g < P.lora_groups) lora_delta_tile<BM>(P, t, acc, smem, true);
-    const float L = P.limit, al = P.alpha, be = P.beta;
-    uint16_t* h = (uint16_t*)P.h;
-#pragma unroll
-    for (int ms = 0; ms < MS; ++ms) {
-      const int tr = 16 * ms + lr;
-      uint32_t hb[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float gg = fminf(acc[ms][0][r], L);
-        const float uu = fminf(fmaxf(acc[ms][1][r], -L), L);
-        const float sg = __builtin_amdgcn_rcpf(1.0f + expf(-al * gg));
-        hb[r] = f32_to_bf16_bits(gg * sg * (uu + be));
-      }
-      if (tr < m)         // 4 consecutive h columns
-        *(uint2*)(h + (long)(row0 + tr) * P.I + t.nt * 128 + c0) =
-            (uint2){hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
-    }
-  }
-}
-
-// One tile of BM rows over K blocks [k0, k1) (see the FP8 kernel for the
-// pipeline); PART: fp32 sums to partial slot `slot` (split-K).
-template <int BM, bool G1, bool PART, bool LORA>
-__device__ __forceinline__ void int4_tile(const GemmParams& P, const Tile& tl, uint8_t* smem,
-                                          int k0, int k1, int slot = 0) {
-  using Gm = I4Geo<BM>;
-  constexpr int MS = Gm::MS;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, lg = lane >> 4;
-  const int K = P.K;
-  const int g = tl.g, row0 = tl.row0, m = tl.m;
-
-  // ---- sources at K block 0 ----------------------------------------------
-  // A: 256 bytes (128 f16 or bf16) per row and block, 16 chunks of 16
-  const uint8_t* ap[Gm::A_PT];
-  int a_st[Gm::A_PT];
-#pragma unroll
-  for (int i = 0; i < Gm::A_PT; ++i) {
-    const int cc = min(tid + i * kThreads, Gm::A_CH - 1);
-    const int row = cc >> 4, ch = cc & 15;
-    ap[i] = P.a + a_source_row<G1>(P, row0 + (row < m ? row : 0)) * P.a_ld + ch * 16;
-    a_st[i] = row * 256 + 16 * i4_swz(row, ch);
-  }
-  // weights: K / 2 bytes per row, 64 per block; this lane's 16 bytes hold
-  // K 32 lg .. 32 lg + 31 of the block, whose scale is group 4 s + lg
-  const long wrow = K >> 1;
-  const uint8_t* wg = P.w + (long)g * P.N * wrow;
-  const long nl = tl.n_lo + 16 * wave + lr, nh = tl.n_hi + 16 * wave + lr;
-  const uint8_t* bp0 = wg + nl * wrow + 16 * lg;
-  const uint8_t* bp1 = wg + nh * wrow + 16 * lg;
-  const uint16_t* sc = (const uint16_t*)P.wsc + (long)g * P.N * (K >> 5);
-  const uint16_t* sp0 = sc + nl * (K >> 5) + lg;
-  const uint16_t* sp1 = sc + nh * (K >> 5) + lg;
-
-  i32x4 ra[Gm::A_PT];
-  auto gload_a = [&](int s) {            // past the last block: re-read it
-    const long adv = (long)min(s, k1 - 1) * 256;
-#pragma unroll
-    for (int i = 0; i < Gm::A_PT; ++i) ra[i] = *(const i32x4*)(ap[i] + adv);
-  };
-  auto store_a = [&](int buf) {
-    uint8_t* st = smem + buf * Gm::STAGE;
-#pragma unroll
-    for (int i = 0; i < Gm::A_PT; ++i) {
-      if (Gm::A_CH % kThreads == 0 || tid + i * kThreads < Gm::A_CH) {
-        if constexpr (G1)                // already f16 in the K order above
-          *(i32x4*)(st + a_st[i]) = ra[i];
-        else                             // h: bf16 -> f16, reordered
-          *(f16x8*)(st + a_st[i]) = bf16x8_f16p(ra[i]);
-      }
-    }
-  };
-  struct WB {
-    i32x4 q[2];                          // lo, hi rows
-    uint32_t s[2];                       // their bf16 group scales
-  };
-  auto gload_b = [&](WB& b, int s) {   // past the last block: re-read it
-    const int sb = min(s, k1 - 1);
-    b.q[0] = *(const i32x4*)(bp0 + (long)sb * 64);
-    b.q[1] = *(const i32x4*)(bp1 + (long)sb * 64);
-    b.s[0] = sp0[4 * sb];
-    b.s[1] = sp1[4 * sb];
-  };
-
-  f32x4 acc[MS][2];
-#pragma unroll
-  for (int i = 0; i < MS; ++i) {
-    acc[i][0] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    acc[i][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  }
-
-  // The weight expansion is pipelined: each block is done in two K halves
-  // (32-deep steps j = 0, 1, then j = 2, 3); the MFMAs of the first half run
-  // while the second half's weights are expanded, and those of the second
-  // half while the next block's first half is expanded, the conversions
-  // spread over the subtiles between the MFMAs.
-  f16x8 bwA[2][2], bwB[2][2];            // [ns][j] of the first / second half
-  auto scale_regs = [&](const WB& b, f16x2 (&s2)[2], f16x2 (&s16)[2]) {
-#pragma unroll
-    for (int ns = 0; ns < 2; ++ns) {
-      const _Float16 sh = (_Float16)bf16_bits_to_f32(b.s[ns]);
-      s2[ns] = (f16x2){sh, sh};
-      s16[ns] = s2[ns] * (f16x2){(_Float16)0.0625f, (_Float16)0.0625f};
-    }
-  };
-  auto block = [&](int s, int buf, WB& rc, WB& rn) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) asm volatile("" : "+v"(rc.q[i]), "+v"(rn.q[i]));
-    f16x2 s2[2], s16[2], s2n[2], s16n[2];
-    scale_regs(rc, s2, s16);
-    scale_regs(rn, s2n, s16n);
-    gload_a(s + 1);
-    const uint8_t* sa = smem + buf * Gm::STAGE;
-    // A fragment of step t = (half h, subtile ms): chunks 4 lg + 2 h, + 1
-    auto lds_h = [&](int t, f16x8 (&af)[2]) {
-      const int h = t / MS, row = 16 * (t % MS) + lr;
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-        af[jj] = *(const f16x8*)(sa + row * 256 + 16 * i4_swz(row, 4 * lg + 2 * h + jj));
-    };
-    f16x8 fr[2][2];
-    lds_h(0, fr[0]);
-#pragma unroll
-    for (int t = 0; t < 2 * MS; ++t) {
-      const int h = t / MS, ms = t % MS;
-      if (t + 1 < 2 * MS) lds_h(t + 1, fr[(t + 1) & 1]);
-      if (t == MS) gload_b(rc, s + 2);   // this block's raw weights are expanded
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        acc[ms][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(h ? bwB[0][jj] : bwA[0][jj],
-                                                           fr[t & 1][jj], acc[ms][0], 0, 0, 0);
-        acc[ms][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(h ? bwB[1][jj] : bwA[1][jj],
-                                                           fr[t & 1][jj], acc[ms][1], 0, 0, 0);
-      }
-      // expansion items (ns, jj) of this step: item i goes to subtile i*MS/4
-      int nitem = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (i * MS / 4 == ms) {
-          const int ns = i >> 1, jj = i & 1;
-          if (h == 0)
-            bwB[ns][jj] = int4x8_f16((uint32_t)rc.q[ns][2 + jj], s2[ns], s16[ns]);
-          else
-            bwA[ns][jj] = int4x8_f16((uint32_t)rn.q[ns][jj], s2n[ns], s16n[ns]);
-          ++nitem;
-        }
-      }
-      if (t + 1 < 2 * MS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // MFMA
-        if (q < 3) {                                                          // VALU
-          if (nitem == 1) __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-          if (nitem == 2) __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    store_a(buf ^ 1);
-  };
-
-  WB rb0, rb1;
-  gload_b(rb0, k0);
-  gload_b(rb1, k0 + 1);
-  gload_a(k0);
-  store_a(0);
-  {                                      // first half of block k0
-    f16x2 s2[2], s16[2];
-    scale_regs(rb0, s2, s16);
-#pragma unroll
-    for (int ns = 0; ns < 2; ++ns)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-        bwA[ns][jj] = int4x8_f16((uint32_t)rb0.q[ns][jj], s2[ns], s16[ns]);
-  }
-  __syncthreads();
-  int s = k0;
-  for (; s + 2 <= k1; s += 2) {
-    block(s, 0, rb0, rb1);
-    __syncthreads();
-    block(s + 1, 1, rb1, rb0);
-    __syncthreads();
-  }
-  if (s < k1) {
-    block(s, 0, rb0, rb1);
-    __syncthreads();
-  }
-  if constexpr (PART) {
-    const int c0 = 16 * wave + 4 * lg;
-    const bool hi_ok = G1 || tl.n_hi != tl.n_lo;
-    // GEMM2's down-LoRA delta goes into the tile's first partial slot once
-    if constexpr (!G1 && LORA)
-      if (slot == 0 && P.z && tl.g < P.lora_groups)
-        lora_delta_tile<BM>(P, tl, acc, smem, hi_ok);
-    float* base = P.part + ((long)slot * P.p_rows + row0) * P.N;
-#pragma unroll
-    for (int ms = 0; ms < MS; ++ms) {
-      const int tr = 16 * ms + lr;
-      if (tr < m) {
-        *(f32x4*)(base + (long)tr * P.N + tl.n_lo + c0) = acc[ms][0];
-        if (hi_ok) *(f32x4*)(base + (long)tr * P.N + tl.n_hi + c0) = acc[ms][1];
-      }
-    }
-  } else {
-    int4_epilogue<BM, G1, LORA>(P, tl, acc, smem);
-    __syncthreads();       // LDS is reused by the next tile
-  }
-}
-
-template <int TBM, bool G1, bool LORA>
-__device__ __forceinline__ void int4_plain_tiles(const GemmParams& P, uint8_t* smem,
-                                                 const int* s_cum) {
-  const int NT = G1 ? (P.I >> 7) : ((P.N + 255) >> 8);
-  const int NS = P.K >> 7;
-  const int total = s_cum[P.G] * NT;
-  const int xcd = blockIdx.x & 7, nper = gridDim.x >> 3, slot = blockIdx.x >> 3;
-  const int chunk = (total + 7) >> 3;
-  const int t_end = min(total, (xcd + 1) * chunk);
-  for (int lt = xcd * chunk + slot; lt < t_end; lt += nper) {
-    Tile tl = decode_tile<TBM, G1>(P, lt, NT, s_cum);
-    tl.g = __builtin_amdgcn_readfirstlane(tl.g);
-    tl.row0 = __builtin_amdgcn_readfirstlane(tl.row0);
-    tl.m = __builtin_amdgcn_readfirstlane(tl.m);
-    tl.nt = __builtin_amdgcn_readfirstlane(tl.nt);
-    tl.n_lo = __builtin_amdgcn_readfirstlane(tl.n_lo);
-    tl.n_hi = __builtin_amdgcn_readfirstlane(tl.n_hi);
-    if constexpr (TBM >= 128) {
-      if (tl.m > 64) { int4_tile<128, G1, false, LORA>(P, tl, smem, 0, NS); continue; }
-    }
-    if constexpr (TBM >= 64) {
-      if (tl.m > 32) { int4_tile<64, G1, false, LORA>(P, tl, smem, 0, NS); continue; }
-    }
-    int4_tile<32, G1, false, LORA>(P, tl, smem, 0, NS);
-  }
-}
-
-template <int TBM, bool G1, bool LORA>
-__global__ __launch_bounds__(kThreads) void moe_gemm_int4_kernel(GemmParams P) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ int s_cum[kMaxGroups + 1];
-  __shared__ int s_wsum[8];
-  tile_prefix<TBM>(P.offsets, P.G, s_cum, s_wsum);
-  int4_plain_tiles<TBM, G1, LORA>(P, smem, s_cum);
-}
-
-// Split-K (stream-K) variant, schedule as in the FP8 kernel
-template <bool G1, bool LORA>
-__global__ __launch_bounds__(kThreads) void moe_gemm_int4_sk_kernel(GemmParams P) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ int s_cum[kMaxGroups + 1];
-  __shared__ int s_wsum[8];
-  const int G = P.G;
-  const int NT = G1 ? (P.I >> 7) : ((P.N + 255) >> 8);
-  const int NS = P.K >> 7;
-  tile_prefix<kSkBM>(P.offsets, G, s_cum, s_wsum);
-  const long U = (long)s_cum[G] * NT * NS;
-  const int W = sk_workgroups((long)s_cum[G] * NT, NS, gridDim.x);
-  const int b = blockIdx.x;
-  if (b >= W) return;
-  const long u1 = (long)(b + 1) * U / W;
-  for (long u = (long)b * U / W; u < u1;) {
-    const int t = (int)(u / NS);
-    const int k0 = (int)(u - (long)t * NS);
-    const int k1 = (int)std::min<long>(NS, k0 + (u1 - u));
-    Tile tl = decode_tile<kSkBM, G1>(P, t, NT, s_cum);
-    tl.g = __builtin_amdgcn_readfirstlane(tl.g);
-    tl.row0 = __builtin_amdgcn_readfirstlane(tl.row0);
-    tl.m = __builtin_amdgcn_readfirstlane(tl.m);
-    tl.nt = __builtin_amdgcn_readfirstlane(tl.nt);
-    tl.n_lo = __builtin_amdgcn_readfirstlane(tl.n_lo);
-    tl.n_hi = __builtin_amdgcn_readfirstlane(tl.n_hi);
-    const int slot = b - sk_owner((long)t * NS, U, W);
-    int4_tile<kSkBM, G1, true, LORA>(P, tl, smem, k0, k1, slot);
-    u += k1 - k0;
-  }
-}
 
 // x bf16 [T][H] -> f16 [T][H] with each 8 columns in the order k0, k4, k1,
 // k5, k2, k6, k3, k7 (the GEMM1 activation operand); one thread per 8
@@ -413,74 +22,19 @@ hipError_t launch_act_f16p(const void* x, long T, int H, void* out, hipStream_t 
   return hipGetLastError();
 }
 
-template <int TBM, bool G1, bool LORA>
-static hipError_t run_int4(const GemmParams& P, long p_cap, int NT, hipStream_t s) {
-  constexpr int shm = I4Geo<TBM>::LDS;
-  static int per_cu = 0;
-  if (per_cu == 0) {
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&moe_gemm_int4_kernel<TBM, G1, LORA>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, shm);
-    if (e != hipSuccess) return e;
-    int nb = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &nb, reinterpret_cast<const void*>(&moe_gemm_int4_kernel<TBM, G1, LORA>), kThreads, shm);
-    if (e != hipSuccess) return e;
-    per_cu = nb > 0 ? nb : 1;
-  }
-  long max_tiles = ((p_cap + TBM - 1) / TBM + P.G) * (long)NT;
-  long nwg = std::min<long>(max_tiles, (long)num_cus() * per_cu);
-  nwg = (nwg + 7) & ~7L;
-  if (nwg == 0) return hipSuccess;
-  moe_gemm_int4_kernel<TBM, G1, LORA><<<dim3((unsigned)nwg), dim3(kThreads), shm, s>>>(P);
-  return hipGetLastError();
-}
-
-template <bool G1, bool LORA>
-static hipError_t run_int4_sk(const GemmParams& P, long p_cap, hipStream_t s, int* sk_grid) {
-  constexpr int shm = I4Geo<kSkBM>::LDS;
-  static int per_cu = 0;
-  if (per_cu == 0) {
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&moe_gemm_int4_sk_kernel<G1, LORA>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, shm);
-    if (e != hipSuccess) return e;
-    int nb = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &nb, reinterpret_cast<const void*>(&moe_gemm_int4_sk_kernel<G1, LORA>), kThreads, shm);
-    if (e != hipSuccess) return e;
-    per_cu = nb > 0 ? nb : 1;
-  }
-  const int grid = num_cus() * per_cu;
-  *sk_grid = grid;
-  if (p_cap == 0) return hipSuccess;
-  moe_gemm_int4_sk_kernel<G1, LORA><<<dim3((unsigned)grid), dim3(kThreads), shm, s>>>(P);
-  return hipGetLastError();
-}
-
-template <bool G1, bool LORA>
-static hipError_t run_int4_tbm(const GemmParams& P, long p_cap, int NT, hipStream_t s) {
-  const long hint = P.G > 0 ? p_cap / P.G : p_cap;
-  if (hint <= 32) return run_int4<32, G1, LORA>(P, p_cap, NT, s);
-  if (hint <= 64) return run_int4<64, G1, LORA>(P, p_cap, NT, s);
-  return run_int4<128, G1, LORA>(P, p_cap, NT, s);
-}
-
-template <bool LORA>
-static hipError_t launch_int4(const GemmParams& P, bool g1, long p_cap, int NT, hipStream_t s,
-                              int* sk_grid) {
-  if (P.part)
-    return g1 ? run_int4_sk<true, LORA>(P, p_cap, s, sk_grid)
-              : run_int4_sk<false, LORA>(P, p_cap, s, sk_grid);
-  return g1 ? run_int4_tbm<true, LORA>(P, p_cap, NT, s)
-            : run_int4_tbm<false, LORA>(P, p_cap, NT, s);
-}
-
-// layers with a LoRA run the instantiations that carry the delta
 hipError_t launch_gemm_int4(const GemmParams& P, bool g1, long p_cap, int NT, hipStream_t s,
                             int* sk_grid) {
-  return P.z ? launch_int4<true>(P, g1, p_cap, NT, s, sk_grid)
-             : launch_int4<false>(P, g1, p_cap, NT, s, sk_grid);
+  return launch_w4_fmt<FMT_INT4>(P, g1, p_cap, NT, s, sk_grid);
+}
+
+hipError_t launch_gemm_w4(int fmt, const GemmParams& P, bool g1, long p_cap, int NT,
+                          hipStream_t s, int* sk_grid) {
+  switch (fmt) {
+    case FMT_INT4: return launch_gemm_int4(P, g1, p_cap, NT, s, sk_grid);
+    case FMT_NVFP4: return launch_gemm_nvfp4(P, g1, p_cap, NT, s, sk_grid);
+    case FMT_MXFP4: return launch_gemm_mxfp4(P, g1, p_cap, NT, s, sk_grid);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace moe

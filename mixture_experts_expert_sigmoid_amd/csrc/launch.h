@@ -62,7 +62,7 @@ hipError_t launch_lora_z(const void* x_bf16, const void* A, int rank, long T,
                          int n_adapters, const int* adapter_ids, float* z,
                          int* zad, hipStream_t s);
 
-// Split-K (stream-K) for the FP8 and INT4 grouped GEMMs at decode sizes:
+// Split-K (stream-K) for the FP8 and 4-bit grouped GEMMs at decode sizes:
 // used when at most kSkMaxTiles tiles of 32 rows can exist (tiles <=
 // min(p_cap, G + p_cap / 32) * NT, NS K blocks each) and one tile per
 // workgroup, in waves over an MI355X's kSkCUs CUs, would leave idle slots
@@ -100,7 +100,7 @@ struct Gemm1Args {
   void* h;
   float* hs;
   float* part;           // split-K partials (when splitk_use) or NULL
-  void* x16;             // INT4: f16 activations (T * H * 2 bytes) or NULL
+  void* x16;             // 4-bit formats: f16 activations (T * H * 2 bytes) or NULL
   void* h_lora;          // FP8: bf16 SwiGLU output before the requant, or NULL
 };
 hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t s);
@@ -109,6 +109,7 @@ struct Gemm2Args {
   int fmt;
   const void* wq;
   const void* ws;
+  const float* gscale;   // FP4 formats: [G] per-expert global scales, or NULL
   const void* h;
   const float* hs;
   int H, I, G;
@@ -126,7 +127,7 @@ struct Gemm2Args {
 };
 hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t s);
 
-// sk_grid > 0: y holds the partial sums of the FP8 / INT4 GEMM2's split-K
+// sk_grid > 0: y holds the partial sums of the FP8 / 4-bit GEMM2's split-K
 // kernel over G groups, reduced here per element in slot order
 hipError_t launch_combine(const float* y, long T, int H, int top_k, int shared,
                           const int* pair_row, const float* topk_w,

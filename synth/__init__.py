@@ -174,7 +174,7 @@ class Batch:
 
 def _rand_weights(spec: LayerSpec, N: int, K: int, std: float, gen, device,
                   half_scale: Optional[torch.Tensor] = None,
-                  fp4_scale_codes: tuple = (0x08, 0x18)):
+                  fp4_scale_codes: tuple = (0x30, 0x68)):
     """One expert's [N, K] matrix in the spec's storage format."""
     if spec.fmt == FMT_BF16:
         w = torch.randn(N, K, generator=gen, device=device) * std
@@ -196,8 +196,9 @@ def _rand_weights(spec: LayerSpec, N: int, K: int, std: float, gen, device,
         q = torch.randint(0, 256, (N, K // 2), generator=gen, device=device,
                           dtype=torch.int32).to(torch.uint8)
         if spec.fmt == FMT_NVFP4:
-            # e4m3 codes lo..hi-1 (W13: 2^-6 .. 0.117; W2: from 2^-7, so
-            # subnormal scale codes 4..7 occur)
+            # e4m3 codes lo..hi-1 (W13: 0.5 .. 120, W2: 0.25 .. 60); the
+            # global scales bring the weights to their usual size, as an
+            # NVFP4 quantiser's amax / (6 * 448) does
             lo, hi = fp4_scale_codes
             s = torch.randint(lo, hi, (N, K // 16), generator=gen, device=device,
                               dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
@@ -218,13 +219,16 @@ def make_layer(spec: LayerSpec, device="cpu") -> Layer:
         g = _gen(device, spec.cfg_id, 7001)
         gate = torch.rand(G, generator=g, device=device) * 1.5 + 0.5
         ratio = torch.rand(G, generator=g, device=device) * 0.70 + 0.52
-        gs = torch.stack([gate, gate * ratio], dim=1).float().contiguous()
+        gs = torch.stack([gate, gate * ratio], dim=1).float()
+        if spec.fmt == FMT_NVFP4:
+            gs = gs * 2.0 ** -9      # NVFP4 block scales are in the tens
+        gs = gs.contiguous()
     q13, s13, q2, s2 = [], [], [], []
     for e in range(G):
         g = _gen(device, spec.cfg_id, 1000 + e)
         a, b = _rand_weights(spec, 2 * I, H, std13, g, device,
                              None if gs is None else gs[e])
-        c, d = _rand_weights(spec, H, I, std2, g, device, fp4_scale_codes=(0x04, 0x14))
+        c, d = _rand_weights(spec, H, I, std2, g, device, fp4_scale_codes=(0x28, 0x60))
         q13.append(a); s13.append(b); q2.append(c); s2.append(d)
     st = lambda xs: None if xs[0] is None else torch.stack(xs).contiguous()
     # a batch of adapters stacks them first: [n_adapters, G, ...]
@@ -258,7 +262,8 @@ def make_layer(spec: LayerSpec, device="cpu") -> Layer:
     gs2 = None
     if spec.fmt == FMT_NVFP4:
         g = _gen(device, spec.cfg_id, 7007)
-        gs2 = (torch.rand(G, generator=g, device=device) + 0.5).float().contiguous()
+        gs2 = ((torch.rand(G, generator=g, device=device) + 0.5)
+               * 2.0 ** -10).float().contiguous()
     return Layer(spec, st(q13), st(s13), st(q2), st(s2), gs, lora_A, lora_B,
                  w_router, lora_A2, lora_B2, gs2)
 

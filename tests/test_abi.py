@@ -107,6 +107,12 @@ def test_gemm_validation():
     assert g1(_w(N=256, K=256), act, H=256, I=100) == -2   # I % 128
     assert g1(_w(N=512, K=256), act) == -2               # N != 2I
     assert g1(M.MoeWeights(7, 4, 256, 256, 1, 1, None), act) == -3
+    assert g1(M.MoeWeights(-1, 4, 256, 256, 1, 1, None), act) == -3
+    # 4-bit codes are read 16 bytes at a time, NVFP4 scales as 2-byte pairs
+    for f in (M.MOE_W_INT4_G32, M.MOE_W_NVFP4, M.MOE_W_MXFP4):
+        assert g1(M.MoeWeights(f, 4, 256, 256, 264, 256, None), act) == -5
+    assert g1(M.MoeWeights(M.MOE_W_NVFP4, 4, 256, 256, 256, 257, None), act) == -5
+    assert g1(M.MoeWeights(M.MOE_W_NVFP4, 4, 256, 256, 256, None, None), act) == -1
     assert g1(M.MoeWeights(1, 4, 256, 256, 1, None, None), act) == -1   # fp8 needs scales
     assert g1(w, M.act_params(1.0, 0.0, 0.0)) == -5       # limit must be > 0
     assert g1(w, M.act_params(1.0, 0.0, math.nan)) == -5
@@ -132,6 +138,11 @@ def test_gemm_validation():
               hl=ctypes.c_void_p(256), **big) == -1
     assert g2(ld=ctypes.pointer(M.MoeLora(16, 4, 1.0, 256, 264, 1, None)),
               hl=ctypes.c_void_p(256), **big) == -5     # B not 16-byte aligned
+    # W2 global scales are an FP4-format input
+    w2g = M.MoeWeights(M.MOE_W_FP8_B128, 4, 256, 128, 1, 1, 256)
+    assert L.moe_grouped_gemm2_combine(ctypes.byref(w2g), 1, 1, None, None, 4, 256, 128, 2,
+                                       0, 8, 1, 1, 1, 1, 1.0, 1, ctypes.c_void_p(256),
+                                       1 << 30, None) == -3
     assert L.moe_gemm2_workspace_size(ctypes.byref(w2), 100, None) >= 100 * 256 * 4
     assert (L.moe_gemm2_workspace_size(ctypes.byref(w2), 100, ctypes.pointer(ld)) -
             L.moe_gemm2_workspace_size(ctypes.byref(w2), 100, None)) >= 100 * 16 * 4

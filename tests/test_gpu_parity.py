@@ -13,7 +13,8 @@ import torch
 
 import mixture_experts_expert_sigmoid_amd as M
 from oracle import moe_oracle as O
-from synth import CONFIGS, make_batch, make_layer, to_numpy_batch, to_numpy_layer
+from synth import (CONFIGS, FP4_CONFIGS, make_batch, make_layer, to_numpy_batch,
+                   to_numpy_layer)
 from tests.gpu_helpers import compare, module_for, tolerance
 
 pytestmark = [pytest.mark.gpu,
@@ -167,6 +168,21 @@ SMALL = {
         lora_down=True, n_adapters=4), 3),
     "bf16_lora_multi": (CONFIGS["tiny_bf16"].scaled(
         name="bf16_lora_multi", cfg_id=35, lora_rank=8, lora_down=True, n_adapters=4), 16),
+    # NVFP4 (per-half W13 and per-expert W2 global scales, both LoRAs) on
+    # 128-row tiles, 32-row tiles, the split-K schedule and a batch of
+    # adapters; MXFP4 with a shared expert and the clamp, plain and split-K
+    "nvfp4_lora_small": (FP4_CONFIGS["nvfp4_lora_258"].scaled(
+        name="nvfp4_lora_small", H=256, I=256, cfg_id=41), 300),
+    "nvfp4_lora_mid": (FP4_CONFIGS["nvfp4_lora_258"].scaled(
+        name="nvfp4_lora_mid", H=384, I=256, cfg_id=41), 37),
+    "nvfp4_lora_sk": (FP4_CONFIGS["nvfp4_lora_258"].scaled(
+        name="nvfp4_lora_sk", H=2048, I=2048, n_routed=64, offset=16, cfg_id=42), 1),
+    "nvfp4_multi": (FP4_CONFIGS["nvfp4_lora_258"].scaled(
+        name="nvfp4_multi", H=256, I=256, cfg_id=43, n_adapters=8), 300),
+    "mxfp4_small": (FP4_CONFIGS["mxfp4_g32_64"].scaled(
+        name="mxfp4_small", H=512, I=256, n_routed=16, shared=1, limit=7.0, cfg_id=44), 100),
+    "mxfp4_sk": (FP4_CONFIGS["mxfp4_g32_64"].scaled(
+        name="mxfp4_sk", n_routed=16, cfg_id=45), 2),
 }
 
 _cache = {}
@@ -251,7 +267,7 @@ def _stepwise(spec, mod, batch, T):
         hs = torch.empty(pc, I // 128, device="cuda")
     else:
         xin, xs = x, None
-        h = torch.empty(pc, I, dtype=torch.bfloat16, device="cuda")
+        h = torch.zeros(pc, I, dtype=torch.bfloat16, device="cuda")   # rows of other ranks stay 0
         hs = None
     ws1 = torch.empty(max(M.moe_gemm1_workspace_size(mod.w13, pc, mod.lora), 1),
                       dtype=torch.uint8, device="cuda")
@@ -285,7 +301,8 @@ def _stepwise(spec, mod, batch, T):
                                   "int4_small", "ep_lora_small", "fp8_oai_sk",
                                   "ep_lora_sk", "int4_sk", "ep_lora_multi",
                                   "ep_lora_multi_sk", "int4_lora_multi_dec",
-                                  "bf16_lora_multi"])
+                                  "bf16_lora_multi", "nvfp4_lora_small", "nvfp4_lora_sk",
+                                  "nvfp4_multi", "mxfp4_small", "mxfp4_sk"])
 def test_gemm1_h_codes(name):
     """GEMM1 output h (codes and scales) against the oracle: equal wherever
     the exact h is not within the kernel's error of a rounding boundary;
@@ -326,7 +343,8 @@ def test_gemm1_h_codes(name):
 
 
 @pytest.mark.parametrize("name", ["ep_lora_small", "fp8_oai_sk", "ep_lora_sk", "int4_sk",
-                                  "ep_lora_multi_sk", "int4_lora_multi_dec"])
+                                  "ep_lora_multi_sk", "int4_lora_multi_dec",
+                                  "nvfp4_lora_sk", "nvfp4_multi", "mxfp4_sk"])
 def test_stepwise_entry_points_match_forward_and_oracle(name):
     """route -> permute -> quant -> gemm1 -> gemm2+combine through the
     individual C-ABI calls gives moe_forward's output bit for bit (also on
@@ -409,3 +427,34 @@ def test_zero_tokens_and_no_local_pairs():
     assert torch.all(o["out"] == 0)
     ids = o["topk_ids"].cpu()
     assert torch.all((ids < 96) | (ids >= 128))
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_fp4_small_block_scales_on_gpu(fmt):
+    """Block scales at the small end of each format (NVFP4: e4m3 subnormal
+    codes 1..7, MXFP4: exponents 104..112), so that many expanded weights
+    are f16 subnormals; W13 global scales (2^4, 2^16) bring g and u back
+    to their usual size. Checks that the f16 products and the matrix cores
+    keep those subnormals exactly."""
+    base = SMALL["nvfp4_lora_small" if fmt == "nvfp4" else "mxfp4_small"][0]
+    spec = base.scaled(name=f"{fmt}_tiny_scales", cfg_id=46, lora_rank=0, lora_down=False,
+                       gscale=True)
+    T = 64
+    layer = make_layer(spec)
+    g = torch.Generator().manual_seed(46)
+    sh = layer.w13_s.shape
+    if fmt == "nvfp4":
+        codes = torch.randint(1, 8, sh, generator=g, dtype=torch.int32).to(torch.uint8)
+        layer.w13_s = codes.view(torch.float8_e4m3fn)
+        gsv = 2.0 ** 4
+    else:
+        layer.w13_s = torch.randint(104, 113, sh, generator=g, dtype=torch.int32).to(torch.uint8)
+        gsv = 2.0 ** 16
+    layer.gs = torch.full((spec.n_groups, 2), gsv, dtype=torch.float32)
+    batch = make_batch(spec, layer, T)
+    arr, nb = to_numpy_layer(layer), to_numpy_batch(batch)
+    _log("fp4-small-scales", fmt, T)
+    mod = module_for(spec, layer)
+    o = mod.forward(batch.x.cuda(), batch.logits.cuda())
+    torch.cuda.synchronize()
+    check_layer(spec, o["out"].cpu().numpy(), arr, nb)
