@@ -418,7 +418,8 @@ int num_cus();
 // consumer (launch_gemm1_sk_epilogue, or the combine) reduces them.
 hipError_t launch_gemm_fp8(const GemmParams& P, bool g1, long p_cap, int NT, hipStream_t s,
                            int* sk_grid = nullptr);
-// fp8h: e4m3 h + scales (FP8 layers), else bf16 h (INT4 layers)
+// GEMM1 epilogue after split-K (sk_epilogue.hip); fp8h: e4m3 h + scales
+// (FP8 layers), else bf16 h (4-bit layers)
 hipError_t launch_gemm1_sk_epilogue(const GemmParams& P, int sk_grid, bool fp8h, hipStream_t s);
 
 // 4-bit grouped GEMMs (gemm_w4.h: INT4, NVFP4, MXFP4), same conventions;

@@ -6,7 +6,7 @@ times (MoeModule.forward -> moe_forward with a workspace sized for T):
 - the device error word stays clear;
 - output rows of sampled tokens against the oracle, element by element,
   with the boundary-rounding allowance: max|err| <= tol * RMS and cosine
-  >= 0.9999 (tol 1e-2 FP8/INT4, 5e-3 BF16); sampled tokens are the first,
+  >= 0.9999 (tol 1e-2 FP8/4-bit, 5e-3 BF16); sampled tokens are the first,
   the last and evenly spaced ones in between;
 - a token with no slot on this GPU's experts (expert-parallel share, no
   shared expert) gets an exactly zero row.
@@ -16,7 +16,7 @@ import pytest
 import torch
 
 from oracle import moe_oracle as O
-from synth import CONFIGS, make_batch, make_layer, to_numpy_batch
+from synth import CONFIGS, FP4_CONFIGS, make_batch, make_layer, to_numpy_batch
 from tests.gpu_helpers import LazyExperts, compare, module_for, tolerance
 
 pytestmark = [pytest.mark.gpu,
@@ -26,7 +26,9 @@ pytestmark = [pytest.mark.gpu,
 FULL = [("fp8_clamp_288", 4096, 3), ("fp8_clamp_288", 64, 2), ("fp8_clamp_288", 1, 1),
         ("fp8_oai_128_skew", 4096, 6), ("fp8_oai_128_skew", 1, 1),
         ("int4_g32_64", 2048, 6), ("int4_g32_64", 64, 4),
-        ("ep_lora_258", 8192, 8), ("ep_lora_258", 37, 4), ("ep_lora_258", 1, 1)]
+        ("ep_lora_258", 8192, 8), ("ep_lora_258", 37, 4), ("ep_lora_258", 1, 1),
+        ("nvfp4_lora_258", 8192, 8), ("nvfp4_lora_258", 37, 4), ("nvfp4_lora_258", 1, 1),
+        ("mxfp4_g32_64", 2048, 6), ("mxfp4_g32_64", 1, 1)]
 
 _layers = {}
 
@@ -34,7 +36,7 @@ _layers = {}
 def _layer(name):
     if name not in _layers:
         _layers.clear()                 # one full-size layer resident at a time
-        spec = CONFIGS[name]
+        spec = {**CONFIGS, **FP4_CONFIGS}[name]
         layer = make_layer(spec, device="cuda")
         _layers[name] = (spec, layer, module_for(spec, layer))
     return _layers[name]
