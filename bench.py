@@ -192,8 +192,10 @@ def main():
         for _ in range(args.warmup + args.steps):
             mod.forward(batch.x, batch.logits, outs)
         torch.cuda.synchronize()
+        alg = algorithmic(spec, outs["topk_ids"].cpu().numpy(), Tp)
         print(f"# profile run done: copy 3 x 1 GiB, {spec.name} forward T={Tp} x "
-              f"{args.warmup + args.steps}", flush=True)
+              f"{args.warmup + args.steps}; pairs {alg['P']}, experts touched "
+              f"{alg['touched']}", flush=True)
         return
 
     flush = MallFlush()
