@@ -66,7 +66,14 @@ struct GemmParams {
   // split-K (decode sizes): fp32 partial sums [kSkSlots][p_rows][N]
   float* part;
   long p_rows;
+  int lds_bytes;             // the launch's dynamic LDS (the LoRA epilogue's room)
 };
+
+// Dynamic LDS of the FP8 / 4-bit instantiations with LoRA code: room for a
+// tile's z rows and the B blocks of 8 rank-16 adapters at once (see
+// lora_delta_tile); those kernels run one workgroup per CU either way.
+constexpr int kLoraLds = 80 * 1024;
+constexpr int kLoraSlots = 16;           // most adapters staged per round
 
 
 // ---------------------------------------------------------------------------
@@ -185,13 +192,40 @@ __device__ __forceinline__ long a_source_row(const GemmParams& P, int r) {
   return (p < npr) ? (long)(p / P.top_k) : (long)(p - npr);
 }
 
-// LoRA delta on a tile of the FP8 / INT4 kernels, whose weights are the
+// LoRA delta on a tile of the FP8 / 4-bit kernels, whose weights are the
 // MFMA's first operand: acc[ms][ns][r] is row 16 ms + lane % 16 of the tile
 // and column (ns ? n_hi : n_lo) + 16 wave + 4 (lane / 16) + r.
-//   acc += lora_scale * sum_q z[row][q] * B[g][column][q]  (q ascending)
-// z is staged through LDS as [q][BM]. The hi half is read only when hi_ok
-// (otherwise the lo columns are read again and the hi values never stored).
-// Every thread of the workgroup calls it (two barriers).
+//   acc += sum_q (lora_scale * z[row][q]) * B[a(row)][g][column][q]
+// on the matrix cores: v_mfma_f32_16x16x16bf16_1k with the B rows as the
+// first operand (lane: column 16 wave + lane % 16, ranks 4 (lane / 16) ..
+// + 3) and z' = lora_scale * z as the second. z' is fp32; it enters as the
+// exact sum of three bf16 terms (z1 = bf16(z'), z2 = bf16(z' - z1),
+// z3 = z' - z1 - z2), so every product is exact and only the fp32
+// accumulation rounds. Ranks are padded with zeros to 16 (or 32).
+// The tile's distinct adapters (one when there is no batch of adapters)
+// are listed in ascending order; their B blocks ([lo 128 | hi 128 columns]
+// [ranks] bf16) are staged in LDS after the z' rows, as many per round as
+// fit, and for each adapter the rows that use it take its product (the
+// others multiply zeros, which leaves their accumulators unchanged). So a
+// row's result depends only on its own adapter: a batch in which every
+// token uses adapter a gives the one-adapter result bit for bit. Rows
+// without an adapter (z = 0) are skipped. The hi half is read only when
+// hi_ok (otherwise the lo columns are staged twice and the hi values never
+// stored). Every thread of the workgroup calls it (barriers inside).
+typedef short lora_s4 __attribute__((ext_vector_type(4)));
+
+// three bf16 terms whose sum is the fp32 pair (x, y) exactly (normal range),
+// packed two per dword: t[0] = (x1 | y1 << 16), t[1] = (x2 ...), t[2] = ...
+__device__ __forceinline__ void split3_bf16(float x, float y, uint32_t (&t)[3]) {
+  const uint32_t x1 = f32_to_bf16_bits(x), y1 = f32_to_bf16_bits(y);
+  const float rx = x - __uint_as_float(x1 << 16), ry = y - __uint_as_float(y1 << 16);
+  const uint32_t x2 = f32_to_bf16_bits(rx), y2 = f32_to_bf16_bits(ry);
+  const float sx = rx - __uint_as_float(x2 << 16), sy = ry - __uint_as_float(y2 << 16);
+  t[0] = x1 | (y1 << 16);
+  t[1] = x2 | (y2 << 16);
+  t[2] = f32_to_bf16_bits(sx) | (f32_to_bf16_bits(sy) << 16);
+}
+
 template <int BM>
 __device__ __forceinline__ void lora_delta_tile(const GemmParams& P, const Tile& t,
                                                 f32x4 (&acc)[BM / 16][2], uint8_t* smem,
@@ -199,77 +233,132 @@ __device__ __forceinline__ void lora_delta_tile(const GemmParams& P, const Tile&
   constexpr int MS = BM / 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int c0 = 16 * wave + 4 * lg;
   const int g = t.g, row0 = t.row0, m = t.m;
-  float* sz = (float*)smem;
   const int R = P.lora_rank;
-  for (int i = tid; i < R * BM; i += kThreads) {
-    const int q = i / BM, tr = i - q * BM;
-    sz[q * BM + tr] = P.z[(long)(row0 + (tr < m ? tr : 0)) * R + q];
+  const int Rp = R <= 16 ? 16 : 32;                  // padded ranks
+  const bool batch = P.n_adapters > 1;
+  const int nhi = hi_ok ? t.n_hi : t.n_lo;
+  // LDS: z' [BM][Rp] fp32 | row -> list index [BM] | adapter list [BM] |
+  // list length | B slots, each [lo | hi][128][Rp] bf16 + a 16-byte pad
+  // that puts the same column of different slots in different banks
+  float* sz = (float*)smem;
+  int* s_idx = (int*)(sz + BM * Rp);
+  int* s_list = s_idx + BM;
+  int* s_n = s_list + BM;
+  uint8_t* sb = (uint8_t*)(s_n + 4);
+  const int blk = 128 * Rp * 2;                      // bytes of one 128-column block
+  const int ss = 2 * blk + 16;
+  // LoRA launches give kLoraLds bytes: at least 3 slots at 32 ranks and
+  // BM = 128 (the floor of 1 only keeps the round loop finite)
+  const int slots = max(1, min(kLoraSlots, (P.lds_bytes - (int)(sb - smem)) / ss));
+  for (int i = tid; i < BM * Rp; i += kThreads) {
+    const int tr = i / Rp, q = i - tr * Rp;
+    sz[i] = (q < R && tr < m) ? P.lora_scale * P.z[(long)(row0 + tr) * R + q] : 0.0f;
+  }
+  if (wave == 0) {
+    // distinct adapters of the tile's rows, ascending (one wave minimum each)
+    constexpr int RPL = (BM + 63) / 64;              // rows per lane
+    int ad[RPL], ix[RPL];
+#pragma unroll
+    for (int j = 0; j < RPL; ++j) {
+      const int tr = lane + 64 * j;
+      ad[j] = tr < m ? (batch ? P.zad[row0 + tr] : 0) : -1;
+      ix[j] = -1;
+    }
+    int n = 0;
+    while (true) {
+      int cand = 0x7FFFFFFF;
+#pragma unroll
+      for (int j = 0; j < RPL; ++j)
+        if (ad[j] >= 0 && ix[j] < 0) cand = min(cand, ad[j]);
+      cand = wave_min_i32(cand);
+      if (cand == 0x7FFFFFFF) break;
+#pragma unroll
+      for (int j = 0; j < RPL; ++j)
+        if (ad[j] == cand) ix[j] = n;
+      if (lane == 0) s_list[n] = cand;
+      ++n;
+    }
+#pragma unroll
+    for (int j = 0; j < RPL; ++j) {
+      const int tr = lane + 64 * j;
+      if (tr < BM) s_idx[tr] = ix[j];
+    }
+    if (lane == 0) s_n[0] = n;
   }
   __syncthreads();
-  const int nhi = hi_ok ? t.n_hi : t.n_lo;
-  // B[n][q] rows hold the R ranks contiguously, so with R % 8 == 0 a lane
-  // reads ranks q0..q0+7 of one of its columns as one 16-byte load; the 8
-  // loads of a chunk (4 columns x 2 halves) are issued before the FMAs
-  const bool vec = (R & 7) == 0;
-  auto chunk = [&](const uint16_t* Bg, int q0, int ms_lo, int ms_hi) {
-    // ranks q0..q0+7 of the lane's 4 columns per half, kept packed (bf16
-    // pairs) and widened at use
-    i32x4 vl[4], vh[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (vec) {
-        vl[r] = *(const i32x4*)(Bg + (long)(t.n_lo + c0 + r) * R + q0);
-        vh[r] = *(const i32x4*)(Bg + (long)(nhi + c0 + r) * R + q0);
-      } else {
-        uint32_t u[8], w[8];
+  const int n = s_n[0];
+  for (int base = 0; base < n; base += slots) {
+    const int cnt = min(slots, n - base);
+    // stage the B blocks of adapters base .. base + cnt - 1
+    if (R == Rp) {
+      // 16-byte chunks in rounds of 8 per thread, each round's loads
+      // issued before its LDS stores
+      const int per = 2 * blk / 16;                  // chunks per slot
+      const int total = cnt * per;
+      for (int c0 = 0; c0 < total; c0 += 8 * kThreads) {
+        i32x4 v[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const int q = min(q0 + i, R - 1);
-          u[i] = Bg[(long)(t.n_lo + c0 + r) * R + q];
-          w[i] = Bg[(long)(nhi + c0 + r) * R + q];
+          const int c = min(c0 + tid + i * kThreads, total - 1);
+          const int j = c / per, rem = c - j * per;
+          const int half = rem >= per / 2, off = rem - half * (per / 2);
+          const uint16_t* src = P.lora_B +
+              ((long)s_list[base + j] * P.lora_groups + g) * P.N * R + (long)(half ? nhi : t.n_lo) * R;
+          v[i] = *(const i32x4*)((const uint8_t*)src + 16 * off);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          vl[r][i] = (int)(u[2 * i] | (u[2 * i + 1] << 16));
-          vh[r][i] = (int)(w[2 * i] | (w[2 * i + 1] << 16));
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (q0 + i >= R) break;
-      const int q = q0 + i;
-#pragma unroll
-      for (int ms = 0; ms < MS; ++ms) {
-        if (ms < ms_lo || ms >= ms_hi) continue;
-        const float zq = sz[q * BM + 16 * ms + lr];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint32_t pl = (uint32_t)vl[r][i >> 1], ph = (uint32_t)vh[r][i >> 1];
-          const float bl = __uint_as_float((i & 1) ? (pl & 0xFFFF0000u) : (pl << 16));
-          const float bh = __uint_as_float((i & 1) ? (ph & 0xFFFF0000u) : (ph << 16));
-          acc[ms][0][r] = fmaf(zq, P.lora_scale * bl, acc[ms][0][r]);
-          acc[ms][1][r] = fmaf(zq, P.lora_scale * bh, acc[ms][1][r]);
+        for (int i = 0; i < 8; ++i) {
+          const int c = c0 + tid + i * kThreads;
+          if (c < total) {
+            const int j = c / per, rem = c - j * per;
+            const int half = rem >= per / 2, off = rem - half * (per / 2);
+            *(i32x4*)(sb + j * ss + half * blk + 16 * off) = v[i];
+          }
         }
       }
+    } else {                                         // ranks padded with zeros
+      const int per = 2 * 128 * Rp;                  // elements per slot
+      for (int c = tid; c < cnt * per; c += kThreads) {
+        const int j = c / per, rem = c - j * per;
+        const int col = rem / Rp, q = rem - col * Rp;
+        const int half = col >= 128, cc = col - 128 * half;
+        uint16_t v = 0;
+        if (q < R)
+          v = P.lora_B[((long)s_list[base + j] * P.lora_groups + g) * P.N * R +
+                       (long)((half ? nhi : t.n_lo) + cc) * R + q];
+        *(uint16_t*)(sb + j * ss + half * blk + (cc * Rp + q) * 2) = v;
+      }
     }
-  };
-  if (P.n_adapters <= 1) {
-    const uint16_t* Bg = P.lora_B + (long)g * P.N * R;
-    for (int q0 = 0; q0 < R; q0 += 8) chunk(Bg, q0, 0, MS);
-  } else {
-    // a batch of adapters: each row's B (rows without one have z = 0)
+    __syncthreads();
+    const int colb = (16 * wave + lr) * Rp * 2;      // the lane's B column
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) {
-      const int tr = 16 * ms + lr;
-      const int a = max(P.zad[row0 + (tr < m ? tr : 0)], 0);
-      const uint16_t* Bg = P.lora_B + ((long)a * P.lora_groups + g) * P.N * R;
-      for (int q0 = 0; q0 < R; q0 += 8) chunk(Bg, q0, ms, ms + 1);
+      const int row = 16 * ms + lr;
+      const int k = s_idx[row] - base;               // the row's slot this round
+      for (int ks = 0; ks < Rp; ks += 16) {
+        const f32x4 zv = *(const f32x4*)(sz + row * Rp + ks + 4 * lg);
+        uint32_t za[3], zb[3];
+        split3_bf16(zv[0], zv[1], za);
+        split3_bf16(zv[2], zv[3], zb);
+        for (int j = 0; j < cnt; ++j) {
+          if (!__ballot(k == j)) continue;           // no row of this subtile uses it
+          const uint8_t* bj = sb + j * ss + colb + (ks + 4 * lg) * 2;
+          const lora_s4 blo = *(const lora_s4*)bj;
+          const lora_s4 bhi = *(const lora_s4*)(bj + blk);
+          const bool take = k == j;
+#pragma unroll
+          for (int u = 0; u < 3; ++u) {
+            const uint2 zz = take ? make_uint2(za[u], zb[u]) : make_uint2(0u, 0u);
+            const lora_s4 zo = __builtin_bit_cast(lora_s4, zz);
+            acc[ms][0] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(blo, zo, acc[ms][0], 0, 0, 0);
+            acc[ms][1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bhi, zo, acc[ms][1], 0, 0, 0);
+          }
+        }
+      }
     }
+    __syncthreads();
   }
-  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------

@@ -540,7 +540,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_sk_kernel(GemmParams P)
 
 template <int TBM, bool G1, bool LORA>
 static hipError_t run_fp8(const GemmParams& P, long p_cap, int NT, hipStream_t s) {
-  constexpr int shm = F8Geo<TBM, !G1>::LDS;
+  constexpr int shm = LORA ? std::max(F8Geo<TBM, !G1>::LDS, kLoraLds) : F8Geo<TBM, !G1>::LDS;
   static int per_cu = 0;   // resident workgroups per CU, per instantiation
   if (per_cu == 0) {
     hipError_t e = hipFuncSetAttribute(
@@ -557,14 +557,16 @@ static hipError_t run_fp8(const GemmParams& P, long p_cap, int NT, hipStream_t s
   long nwg = std::min<long>(max_tiles, (long)num_cus() * per_cu);
   nwg = (nwg + 7) & ~7L;
   if (nwg == 0) return hipSuccess;
-  moe_gemm_fp8_kernel<TBM, G1, LORA><<<dim3((unsigned)nwg), dim3(kThreads), shm, s>>>(P);
+  GemmParams Q = P;
+  Q.lds_bytes = shm;
+  moe_gemm_fp8_kernel<TBM, G1, LORA><<<dim3((unsigned)nwg), dim3(kThreads), shm, s>>>(Q);
   return hipGetLastError();
 }
 
 template <bool G1, bool LORA>
 static hipError_t run_fp8_sk(const GemmParams& P, long p_cap, int NT, hipStream_t s,
                              int* sk_grid) {
-  constexpr int shm = F8Geo<kSkBM, !G1>::LDS;
+  constexpr int shm = LORA ? std::max(F8Geo<kSkBM, !G1>::LDS, kLoraLds) : F8Geo<kSkBM, !G1>::LDS;
   static int per_cu = 0;
   if (per_cu == 0) {
     hipError_t e = hipFuncSetAttribute(
@@ -580,7 +582,9 @@ static hipError_t run_fp8_sk(const GemmParams& P, long p_cap, int NT, hipStream_
   const int grid = num_cus() * per_cu;
   *sk_grid = grid;
   if (p_cap == 0) return hipSuccess;
-  moe_gemm_fp8_sk_kernel<G1, LORA><<<dim3((unsigned)grid), dim3(kThreads), shm, s>>>(P);
+  GemmParams Q = P;
+  Q.lds_bytes = shm;
+  moe_gemm_fp8_sk_kernel<G1, LORA><<<dim3((unsigned)grid), dim3(kThreads), shm, s>>>(Q);
   return hipGetLastError();
 }
 

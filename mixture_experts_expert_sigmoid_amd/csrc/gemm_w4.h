@@ -495,7 +495,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_w4_sk_kernel(GemmParams P) 
 
 template <int WF, int TBM, bool G1, bool LORA>
 static hipError_t run_w4(const GemmParams& P, long p_cap, int NT, hipStream_t s) {
-  constexpr int shm = I4Geo<TBM>::LDS;
+  constexpr int shm = LORA ? std::max(I4Geo<TBM>::LDS, kLoraLds) : I4Geo<TBM>::LDS;
   static int per_cu = 0;
   if (per_cu == 0) {
     hipError_t e = hipFuncSetAttribute(
@@ -512,13 +512,15 @@ static hipError_t run_w4(const GemmParams& P, long p_cap, int NT, hipStream_t s)
   long nwg = std::min<long>(max_tiles, (long)num_cus() * per_cu);
   nwg = (nwg + 7) & ~7L;
   if (nwg == 0) return hipSuccess;
-  moe_gemm_w4_kernel<WF, TBM, G1, LORA><<<dim3((unsigned)nwg), dim3(kThreads), shm, s>>>(P);
+  GemmParams Q = P;
+  Q.lds_bytes = shm;
+  moe_gemm_w4_kernel<WF, TBM, G1, LORA><<<dim3((unsigned)nwg), dim3(kThreads), shm, s>>>(Q);
   return hipGetLastError();
 }
 
 template <int WF, bool G1, bool LORA>
 static hipError_t run_w4_sk(const GemmParams& P, long p_cap, hipStream_t s, int* sk_grid) {
-  constexpr int shm = I4Geo<kSkBM>::LDS;
+  constexpr int shm = LORA ? std::max(I4Geo<kSkBM>::LDS, kLoraLds) : I4Geo<kSkBM>::LDS;
   static int per_cu = 0;
   if (per_cu == 0) {
     hipError_t e = hipFuncSetAttribute(
@@ -534,7 +536,9 @@ static hipError_t run_w4_sk(const GemmParams& P, long p_cap, hipStream_t s, int*
   const int grid = num_cus() * per_cu;
   *sk_grid = grid;
   if (p_cap == 0) return hipSuccess;
-  moe_gemm_w4_sk_kernel<WF, G1, LORA><<<dim3((unsigned)grid), dim3(kThreads), shm, s>>>(P);
+  GemmParams Q = P;
+  Q.lds_bytes = shm;
+  moe_gemm_w4_sk_kernel<WF, G1, LORA><<<dim3((unsigned)grid), dim3(kThreads), shm, s>>>(Q);
   return hipGetLastError();
 }
 

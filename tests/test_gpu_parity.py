@@ -183,6 +183,19 @@ SMALL = {
         name="mxfp4_small", H=512, I=256, n_routed=16, shared=1, limit=7.0, cfg_id=44), 100),
     "mxfp4_sk": (FP4_CONFIGS["mxfp4_g32_64"].scaled(
         name="mxfp4_sk", n_routed=16, cfg_id=45), 2),
+    # adapter batches on 128-row tiles (all 16 experts local, ~150 rows
+    # each): the tile's adapters' B blocks staged in LDS; with 40 adapters a
+    # tile meets more than fit and reads B from memory; rank 32 halves the
+    # slots
+    "ep_lora_multi_big": (CONFIGS["ep_lora_258"].scaled(
+        name="ep_lora_multi_big", H=256, I=256, n_routed=16, n_sink=0, E_loc=None,
+        offset=0, cfg_id=47, n_adapters=8), 300),
+    "nvfp4_multi_many": (FP4_CONFIGS["nvfp4_lora_258"].scaled(
+        name="nvfp4_multi_many", H=256, I=256, n_routed=16, n_sink=0, E_loc=None,
+        offset=0, cfg_id=48, n_adapters=40), 300),
+    "int4_lora32_multi": (CONFIGS["int4_g32_64"].scaled(
+        name="int4_lora32_multi", H=512, I=256, n_routed=16, cfg_id=49, lora_rank=32,
+        lora_down=True, n_adapters=8), 300),
 }
 
 _cache = {}
@@ -302,7 +315,9 @@ def _stepwise(spec, mod, batch, T):
                                   "ep_lora_sk", "int4_sk", "ep_lora_multi",
                                   "ep_lora_multi_sk", "int4_lora_multi_dec",
                                   "bf16_lora_multi", "nvfp4_lora_small", "nvfp4_lora_sk",
-                                  "nvfp4_multi", "mxfp4_small", "mxfp4_sk"])
+                                  "nvfp4_multi", "mxfp4_small", "mxfp4_sk",
+                                  "ep_lora_multi_big", "nvfp4_multi_many",
+                                  "int4_lora32_multi"])
 def test_gemm1_h_codes(name):
     """GEMM1 output h (codes and scales) against the oracle: equal wherever
     the exact h is not within the kernel's error of a rounding boundary;
