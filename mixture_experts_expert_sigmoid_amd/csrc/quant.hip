@@ -102,25 +102,62 @@ __device__ __forceinline__ void lora_tile_prefix(const int* offsets, int G, int*
   __syncthreads();
 }
 
+// token of pair p: p / top_k for the routed pairs p < T top_k, p - T top_k
+// for the shared expert's rows
+__device__ __forceinline__ long pair_token(long p, long T, int top_k) {
+  const long npr = T * top_k;
+  return p < npr ? p / top_k : p - npr;
+}
+
+// The K loop of one 16-row block: acc[n] = x rows . A rows 16 n .. 16 n + 15
+// over this wave's quarter of H on v_mfma_f32_16x16x32_bf16 (x the first
+// operand), 8 K steps per round with all their loads issued before the
+// MFMAs. xr / Ag: the lane's row and rank-row pointers at the quarter's
+// start + 8 (lane / 16).
+template <int NQ>
+__device__ __forceinline__ void lora_z_rows(const uint16_t* xr, const uint16_t* Ag, int rank,
+                                            int H, f32x4 (&acc)[NQ]) {
+  const int lr = lane_id() & 15;
+  const int hq = H >> 2;
+#pragma unroll
+  for (int n = 0; n < NQ; ++n) acc[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int h0 = 0; h0 < hq; h0 += 256) {
+    i32x4 xv[8], av[NQ][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int h = min(h0 + 32 * j, hq - 32);   // hq % 32 == 0
+      xv[j] = *(const i32x4*)(xr + h);
+#pragma unroll
+      for (int n = 0; n < NQ; ++n) {
+        const int q = 16 * n + lr;
+        av[n][j] = (i32x4){0, 0, 0, 0};
+        if (q < rank) av[n][j] = *(const i32x4*)(Ag + (long)q * H + h);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (h0 + 32 * j >= hq) break;
+#pragma unroll
+      for (int n = 0; n < NQ; ++n)
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[j]),
+                                                        __builtin_bit_cast(bf16x8, av[n][j]),
+                                                        acc[n], 0, 0, 0);
+    }
+  }
+}
+
 // One workgroup (4 waves) per 16-row tile of one expert's sorted rows (tile
 // t of expert g covers rows offsets[g] + 16 (t - s_cum[g]) ..):
 // z[16 rows][16 ranks] = X A_g^T on v_mfma_f32_16x16x32_bf16 (bf16
 // products, fp32 accumulation), A_g read once per tile instead of once per
 // row. Wave w covers the w-th quarter of H; the four partials are added in
-// wave order through LDS.
-// A batch of adapters (n_adapters > 1): row r belongs to token
-// t = sorted_pair[r] / top_k and uses adapter adapter_ids[t] (none if
-// outside [0, n_adapters)); A is [n_adapters][n_lora_groups][rank][H]. The
-// tile runs its K loop once per adapter that one of its rows uses and keeps
-// each row's own result; rows without an adapter get z = 0, and zad[r]
-// records every row's adapter (-1: none) for the epilogues.
+// wave order through LDS. (One adapter for every row.)
 template <int NQ>    // 16-column blocks covering the rank
 __global__ __launch_bounds__(256) void lora_z_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ A, int rank,
     long T, int H, int top_k, int n_lora_groups,
     const int* __restrict__ offsets, const int* __restrict__ sorted_pair,
-    bool gather, int n_adapters, const int* __restrict__ adapter_ids,
-    float* __restrict__ z, int* __restrict__ zad) {
+    bool gather, float* __restrict__ z) {
   __shared__ f32x4 red[4][NQ][64];
   __shared__ int s_cum[1025];
   __shared__ int s_wsum[4];
@@ -137,79 +174,106 @@ __global__ __launch_bounds__(256) void lora_z_kernel(
   const int wave = threadIdx.x >> 6, lane = lane_id(), lr = lane & 15, lg = lane >> 4;
   const int hq = H >> 2;                         // this wave's quarter of H
   const long rl = r0 + min(lr, m - 1);           // this lane's operand row
-  const long tok = sorted_pair[rl] / top_k;
   // operand row: the token of the pair (gathered x), or the sorted row itself
-  const uint16_t* xr = x + (gather ? tok : rl) * H + wave * hq + 8 * lg;
-  const bool batch = n_adapters > 1;
-  int ad = 0;                                    // this lane's row's adapter
-  if (batch) {
-    ad = adapter_ids[tok];
-    if (ad < 0 || ad >= n_adapters) ad = -1;
-  }
-  if (zad && wave == 0 && lg == 0 && lr < m) zad[r0 + lr] = ad;
-  for (int a = batch ? 0 : -1; a < (batch ? n_adapters : 0); ++a) {
-    // the adapter's rows in this tile (lanes 0..15 hold rows 0..15 in every
-    // wave, so the test is uniform over the workgroup)
-    const int aa = batch ? a : 0;
-    if (batch && !(__ballot(lr < m && ad == a) & 0xFFFFull)) continue;
-    const uint16_t* Ag = A + ((long)aa * n_lora_groups + g) * rank * H + wave * hq + 8 * lg;
-    f32x4 acc[NQ];
+  const uint16_t* xr = x + (gather ? pair_token(sorted_pair[rl], T, top_k) : rl) * H +
+                       wave * hq + 8 * lg;
+  const uint16_t* Ag = A + (long)g * rank * H + wave * hq + 8 * lg;
+  f32x4 acc[NQ];
+  lora_z_rows<NQ>(xr, Ag, rank, H, acc);
 #pragma unroll
-    for (int n = 0; n < NQ; ++n) acc[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    // 8 K steps per round: all their loads are issued before the MFMAs
-    for (int h0 = 0; h0 < hq; h0 += 256) {
-      i32x4 xv[8], av[NQ][8];
+  for (int n = 0; n < NQ; ++n) red[wave][n][lane] = acc[n];
+  __syncthreads();
+  if (wave == 0) {
+    // acc[n][r]: row 4 (lane / 16) + r, rank 16 n + lane % 16
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int h = min(h0 + 32 * j, hq - 32);   // hq % 32 == 0
-        xv[j] = *(const i32x4*)(xr + h);
-#pragma unroll
-        for (int n = 0; n < NQ; ++n) {
-          const int q = 16 * n + lr;
-          av[n][j] = (i32x4){0, 0, 0, 0};
-          if (q < rank) av[n][j] = *(const i32x4*)(Ag + (long)q * H + h);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (h0 + 32 * j >= hq) break;
-#pragma unroll
-        for (int n = 0; n < NQ; ++n)
-          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[j]),
-                                                          __builtin_bit_cast(bf16x8, av[n][j]),
-                                                          acc[n], 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int n = 0; n < NQ; ++n) red[wave][n][lane] = acc[n];
-    __syncthreads();
-    if (wave == 0) {
-      // acc[n][r]: row 4 (lane / 16) + r, rank 16 n + lane % 16; row
-      // adapters come from the lane holding that row (lane % 16 == row)
-#pragma unroll
-      for (int n = 0; n < NQ; ++n) {
-        const f32x4 v = ((red[0][n][lane] + red[1][n][lane]) + red[2][n][lane]) + red[3][n][lane];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tr = 4 * lg + r;
-          const int q = 16 * n + lr;
-          const int rad = __shfl(ad, tr, 64);
-          if (tr < m && q < rank && (!batch || rad == a)) z[(r0 + tr) * rank + q] = v[r];
-        }
-      }
-    }
-    __syncthreads();                             // red is reused by the next adapter
-  }
-  if (batch && wave == 0) {                      // rows with no adapter: z = 0
-#pragma unroll
-    for (int n = 0; n < NQ; ++n)
+    for (int n = 0; n < NQ; ++n) {
+      const f32x4 v = ((red[0][n][lane] + red[1][n][lane]) + red[2][n][lane]) + red[3][n][lane];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tr = 4 * lg + r;
         const int q = 16 * n + lr;
-        const int rad = __shfl(ad, tr, 64);
-        if (tr < m && q < rank && rad < 0) z[(r0 + tr) * rank + q] = 0.0f;
+        if (tr < m && q < rank) z[(r0 + tr) * rank + q] = v[r];
       }
+    }
+  }
+}
+
+// A batch of adapters, grouped by adapter: one work item per (local group g,
+// adapter a) pair, a = -1 standing for the rows without an adapter (z = 0).
+// The item walks g's sorted rows in windows of 256, compacts those of
+// adapter a into LDS (ballot prefix) and runs the K loop above on 16 of
+// them at a time, so each adapter's A is read once per 16 of its rows
+// instead of once per 16-row tile that meets it. zad[r] gets a (-1: none).
+template <int NQ>
+__global__ __launch_bounds__(256) void lora_z_batch_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ A, int rank,
+    long T, int H, int top_k, int n_lora_groups, const int* __restrict__ offsets,
+    const int* __restrict__ sorted_pair, bool gather, int n_adapters,
+    const int* __restrict__ adapter_ids, float* __restrict__ z, int* __restrict__ zad) {
+  __shared__ f32x4 red[4][NQ][64];
+  __shared__ int s_rows[256];
+  __shared__ int s_cnt[4];
+  const int wave = threadIdx.x >> 6, lane = lane_id(), lr = lane & 15, lg = lane >> 4;
+  const int hq = H >> 2;                         // each wave's quarter of H
+  const int items = n_lora_groups * (n_adapters + 1);
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int g = it / (n_adapters + 1), a = it - g * (n_adapters + 1) - 1;
+    const int rb = offsets[g], re = offsets[g + 1];
+    for (int w0 = rb; w0 < re; w0 += 256) {
+      const int r = w0 + (int)threadIdx.x;
+      bool take = false;
+      if (r < re) {
+        int ad = adapter_ids[pair_token(sorted_pair[r], T, top_k)];
+        if (ad < 0 || ad >= n_adapters) ad = -1;
+        take = ad == a;
+      }
+      const unsigned long long bal = __ballot(take);
+      if (lane == 0) s_cnt[wave] = __popcll(bal);
+      __syncthreads();
+      int before = 0, cnt = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        before += w < wave ? s_cnt[w] : 0;
+        cnt += s_cnt[w];
+      }
+      if (take) s_rows[before + __popcll(bal & ((1ull << lane) - 1ull))] = r;
+      __syncthreads();
+      if (a < 0) {                               // rows without an adapter
+        for (int i = threadIdx.x; i < cnt * rank; i += 256)
+          z[(long)s_rows[i / rank] * rank + i % rank] = 0.0f;
+        if (zad)
+          for (int i = threadIdx.x; i < cnt; i += 256) zad[s_rows[i]] = -1;
+      } else {
+        const uint16_t* Ag = A + ((long)a * n_lora_groups + g) * rank * H + wave * hq + 8 * lg;
+        for (int c0 = 0; c0 < cnt; c0 += 16) {
+          const int m = min(16, cnt - c0);
+          const int rl = s_rows[c0 + min(lr, m - 1)];
+          const uint16_t* xr = x + (gather ? pair_token(sorted_pair[rl], T, top_k) : (long)rl) * H +
+                               wave * hq + 8 * lg;
+          f32x4 acc[NQ];
+          lora_z_rows<NQ>(xr, Ag, rank, H, acc);
+#pragma unroll
+          for (int n = 0; n < NQ; ++n) red[wave][n][lane] = acc[n];
+          __syncthreads();
+          if (wave == 0) {
+            // acc[n][r]: row 4 (lane / 16) + r of the 16, rank 16 n + lane % 16
+#pragma unroll
+            for (int n = 0; n < NQ; ++n) {
+              const f32x4 v = ((red[0][n][lane] + red[1][n][lane]) + red[2][n][lane]) + red[3][n][lane];
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) {
+                const int tr = 4 * lg + rr;
+                const int q = 16 * n + lr;
+                if (tr < m && q < rank) z[(long)s_rows[c0 + tr] * rank + q] = v[rr];
+              }
+            }
+            if (zad && lane < m) zad[s_rows[c0 + lane]] = a;
+          }
+          __syncthreads();                       // red is reused by the next 16 rows
+        }
+      }
+      __syncthreads();                           // s_rows / s_cnt are reused
+    }
   }
 }
 
@@ -219,14 +283,26 @@ hipError_t launch_lora_z(const void* x_bf16, const void* A, int rank, long T,
                          int n_adapters, const int* adapter_ids, float* z,
                          int* zad, hipStream_t s) {
   if (p_cap == 0 || n_lora_groups == 0) return hipSuccess;
+  if (n_adapters > 1) {
+    const long items = (long)n_lora_groups * (n_adapters + 1);
+    dim3 grid((unsigned)std::min<long>(items, 2048)), block(256);
+    if (rank <= 16)
+      hipLaunchKernelGGL(lora_z_batch_kernel<1>, grid, block, 0, s, (const uint16_t*)x_bf16,
+                         (const uint16_t*)A, rank, T, H, top_k, n_lora_groups, offsets,
+                         sorted_pair, gather, n_adapters, adapter_ids, z, zad);
+    else
+      hipLaunchKernelGGL(lora_z_batch_kernel<2>, grid, block, 0, s, (const uint16_t*)x_bf16,
+                         (const uint16_t*)A, rank, T, H, top_k, n_lora_groups, offsets,
+                         sorted_pair, gather, n_adapters, adapter_ids, z, zad);
+    return hipGetLastError();
+  }
   // tiles <= one per non-empty expert plus one per 16 rows
   const long tiles = std::min<long>(p_cap, n_lora_groups + p_cap / 16);
   dim3 grid((unsigned)tiles), block(256);
 #define LZ(NQ)                                                                \
   hipLaunchKernelGGL(lora_z_kernel<NQ>, grid, block, 0, s,                    \
                      (const uint16_t*)x_bf16, (const uint16_t*)A, rank, T, H, \
-                     top_k, n_lora_groups, offsets, sorted_pair, gather,      \
-                     n_adapters, adapter_ids, z, zad)
+                     top_k, n_lora_groups, offsets, sorted_pair, gather, z)
   if (rank <= 16) LZ(1);
   else LZ(2);
 #undef LZ
