@@ -505,19 +505,51 @@ int moe_forward(const moe_layer* L, const void* x_bf16, const float* logits,
   void* h_lora = fp8 ? (void*)(base + o.h_lora) : h;
   float* z2 = (float*)(base + o.z2);
 
-  hipError_t e = moe::launch_route(logits, T, ld_logits, L->num_experts_global,
-                                   L->n_sink, L->top_k, nullptr,
-                                   L->route_scale * L->global_scale, topk_ids,
-                                   topk_w, sink_w, nullptr, s);
-  if (e != hipSuccess) return hip_fail(e, "moe_forward/route");
-  e = moe::launch_permute(topk_ids, T, L->top_k, L->num_experts_global,
-                          L->local_expert_offset, L->num_local_experts,
-                          L->shared_expert, offsets, sorted_pair, pair_row,
-                          err_word, base + o.perm_ws, s);
-  if (e != hipSuccess) return hip_fail(e, "moe_forward/permute");
-  if (fp8) {
-    e = moe::launch_quant_act(x_bf16, T, L->H, xq, xs, s);
-    if (e != hipSuccess) return hip_fail(e, "moe_forward/quant");
+  const bool four = is4(L->w13.fmt);
+  bool x16_ready = false;
+  hipError_t e = hipSuccess;
+  if (moe::front_small_fits(T, L->top_k, G, L->H)) {
+    // decode sizes: route + activation pass + permute in one launch
+    moe::FrontArgs fa{};
+    fa.logits = logits;
+    fa.T = T;
+    fa.ld = ld_logits;
+    fa.n_routed = L->num_experts_global;
+    fa.n_sink = L->n_sink;
+    fa.k = L->top_k;
+    fa.scale = L->route_scale * L->global_scale;
+    fa.ids = topk_ids;
+    fa.w = topk_w;
+    fa.sw = sink_w;
+    fa.x = x_bf16;
+    fa.H = L->H;
+    fa.xq = xq;
+    fa.xs = xs;
+    fa.off = L->local_expert_offset;
+    fa.E_loc = L->num_local_experts;
+    fa.G = G;
+    fa.shared = L->shared_expert;
+    fa.offsets = offsets;
+    fa.sorted_pair = sorted_pair;
+    fa.pair_row = pair_row;
+    fa.err_word = err_word;
+    e = moe::launch_front_small(fa, fp8 ? 1 : (four ? 2 : 0), s);
+    if (e != hipSuccess) return hip_fail(e, "moe_forward/front");
+    x16_ready = four;
+  } else {
+    e = moe::launch_route(logits, T, ld_logits, L->num_experts_global, L->n_sink,
+                          L->top_k, nullptr, L->route_scale * L->global_scale,
+                          topk_ids, topk_w, sink_w, nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_forward/route");
+    e = moe::launch_permute(topk_ids, T, L->top_k, L->num_experts_global,
+                            L->local_expert_offset, L->num_local_experts,
+                            L->shared_expert, offsets, sorted_pair, pair_row,
+                            err_word, base + o.perm_ws, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_forward/permute");
+    if (fp8) {
+      e = moe::launch_quant_act(x_bf16, T, L->H, xq, xs, s);
+      if (e != hipSuccess) return hip_fail(e, "moe_forward/quant");
+    }
   }
   if (L->lora) {
     e = moe::launch_lora_z(x_bf16, L->lora->A, L->lora->rank, T, L->H,
@@ -527,11 +559,13 @@ int moe_forward(const moe_layer* L, const void* x_bf16, const float* logits,
     if (e != hipSuccess) return hip_fail(e, "moe_forward/lora_z");
   }
   float* g1_part = g1_part_bytes(&L->w13, pc) ? y : nullptr;
-  e = moe::launch_gemm1(gemm1_args(&L->w13, fp8 ? xq : x_bf16, fp8 ? xs : nullptr,
-                                   T, L->H, L->I, L->top_k, pc, offsets,
-                                   sorted_pair, &L->act, L->lora, z, h,
-                                   fp8 ? hs : nullptr, g1_part, xq,
-                                   fp8 && L->lora_down ? h_lora : nullptr), s);
+  moe::Gemm1Args ga = gemm1_args(&L->w13, fp8 ? xq : x_bf16, fp8 ? xs : nullptr,
+                                 T, L->H, L->I, L->top_k, pc, offsets,
+                                 sorted_pair, &L->act, L->lora, z, h,
+                                 fp8 ? hs : nullptr, g1_part, xq,
+                                 fp8 && L->lora_down ? h_lora : nullptr);
+  ga.x16_ready = x16_ready;
+  e = moe::launch_gemm1(ga, s);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/gemm1");
   if (L->lora_down) {
     e = moe::launch_lora_z(h_lora, L->lora_down->A, L->lora_down->rank, T, L->I,

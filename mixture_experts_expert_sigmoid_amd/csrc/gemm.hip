@@ -293,7 +293,7 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t s) {
     const bool fp8 = a.fmt == FMT_FP8;
     hipError_t e = hipSuccess;
     if (!fp8) {                    // f16 activations in the 4-bit kernel's K order
-      e = launch_act_f16p(a.x, a.T, a.H, a.x16, s);
+      if (!a.x16_ready) e = launch_act_f16p(a.x, a.T, a.H, a.x16, s);
       if (e != hipSuccess) return e;
       P.a = (const uint8_t*)a.x16;
     }

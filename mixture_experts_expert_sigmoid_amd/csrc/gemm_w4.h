@@ -47,6 +47,7 @@
 // in flight, 16 bytes per row and lane per block) and are expanded there;
 // the f16 activation block is staged in LDS (double buffered).
 #pragma once
+#include "act16_dev.h"
 #include "gemm_common.h"
 
 namespace moe {
@@ -154,19 +155,6 @@ struct W4 {
     else return fp4x8_f16(w, second ? y : x);
   }
 };
-
-// 8 bf16 (k0..k7) -> 8 f16 in the order k0, k4, k1, k5, k2, k6, k3, k7
-__device__ __forceinline__ f16x8 bf16x8_f16p(i32x4 v) {
-  float f[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t u = (uint32_t)v[i];
-    f[2 * i] = __uint_as_float(u << 16);
-    f[2 * i + 1] = __uint_as_float(u & 0xFFFF0000u);
-  }
-  return (f16x8){(_Float16)f[0], (_Float16)f[4], (_Float16)f[1], (_Float16)f[5],
-                 (_Float16)f[2], (_Float16)f[6], (_Float16)f[3], (_Float16)f[7]};
-}
 
 // Accumulator layout: acc[ms][ns][r] is activation row 16 ms + (lane % 16)
 // and weight column (ns ? hi : lo) + 16 wave + 4 (lane / 16) + r.

@@ -50,6 +50,32 @@ hipError_t launch_permute(const int* ids, long T, int k, int E_global, int off,
 hipError_t launch_quant_act(const void* x, long T, int H, void* xq, float* xs,
                             hipStream_t s);
 
+// Decode front end (front.hip): route (no bias, no packed output) + the
+// activation pass + permute in one workgroup when T * k <= kPermBlock, 17 G
+// ints fit 64 KB of LDS and T * ceil(H / 512) <= 64 (front_small_fits);
+// hipErrorNotSupported otherwise. mode 1: FP8 quantisation into xq / xs; 2: the f16 copy of x
+// into xq (4-bit formats); 0: none.
+struct FrontArgs {
+  const float* logits;
+  long T, ld;
+  int n_routed, n_sink, k;
+  float scale;
+  int* ids;
+  float* w;
+  float* sw;
+  const void* x;         // bf16 [T][H]
+  int H;
+  void* xq;
+  float* xs;
+  int off, E_loc, G, shared;
+  int* offsets;
+  int* sorted_pair;
+  int* pair_row;
+  int* err_word;
+};
+bool front_small_fits(long T, int k, int G, int H);
+hipError_t launch_front_small(const FrontArgs& a, int mode, hipStream_t s);
+
 // z[r][q] = sum_h x[row][h] * A[a(r)][g(r)][q][h] for every sorted row r of
 // a local group (fp32). row = t(r) = sorted_pair[r] / top_k when gather,
 // else r itself (x then holds one row per sorted row, e.g. the down-LoRA
@@ -101,6 +127,7 @@ struct Gemm1Args {
   float* hs;
   float* part;           // split-K partials (when splitk_use) or NULL
   void* x16;             // 4-bit formats: f16 activations (T * H * 2 bytes) or NULL
+  bool x16_ready;        // x16 already holds them (the decode front end wrote it)
   void* h_lora;          // FP8: bf16 SwiGLU output before the requant, or NULL
 };
 hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t s);

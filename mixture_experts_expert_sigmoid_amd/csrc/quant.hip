@@ -12,53 +12,18 @@
 // z is kept in fp32 and consumed by the GEMM1 epilogue.
 #include <algorithm>
 
-#include "common.h"
 #include "launch.h"
+#include "quant_dev.h"
 
 namespace moe {
 
-// One wave per (row, 512-column chunk): lane l converts the 8 columns
-// chunk*512 + 8l .. +7 with one 16-byte load; the 16 lanes of a DPP row
-// (lane / 16) hold one 128-column group, so the group amax is a row
-// reduction in registers. The quotient x / s is a correctly rounded fp32
-// division; it is clamped to +-448 and rounded to nearest-even e4m3fn by
-// v_cvt_pk_fp8_f32 (identical to RNE with saturation for clamped inputs).
 __global__ __launch_bounds__(256) void quant_act_kernel(
     const uint16_t* __restrict__ x, long T, int H, uint8_t* __restrict__ xq,
     float* __restrict__ xs) {
   const int nc = (H + 511) >> 9;
   const long wi = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (wi >= T * nc) return;
-  const int lane = lane_id();
-  const long row = wi / nc;
-  const int col = (int)(wi - row * nc) * 512 + 8 * lane;
-  const bool on = col < H;              // whole 16-lane rows (H % 128 == 0)
-  float f[8];
-  i32x4 v = {0, 0, 0, 0};
-  if (on) v = *(const i32x4*)(x + row * H + col);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = bf16_bits_to_f32((uint32_t)v[i] & 0xFFFFu);
-    f[2 * i + 1] = bf16_bits_to_f32((uint32_t)v[i] >> 16);
-  }
-  float a = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[i]));
-  a = max16(a);
-  const float sc = a > 0.0f ? a / 448.0f : 1.0f;
-  uint32_t w[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    float q[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) q[i] = __builtin_amdgcn_fmed3f(f[4 * h + i] / sc, -448.0f, 448.0f);
-    int c = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
-    w[h] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], c, true);
-  }
-  if (on) {
-    *(uint2*)(xq + row * H + col) = make_uint2(w[0], w[1]);
-    if ((lane & 15) == 0) xs[row * (H >> 7) + (col >> 7)] = sc;
-  }
+  quant_act_unit(x, wi, H, xq, xs);
 }
 
 hipError_t launch_quant_act(const void* x, long T, int H, void* xq, float* xs,
