@@ -15,6 +15,8 @@ at T = 4096 (10.9 GB of touched weights per step, far beyond the 256 MB
 MALL); the sweep and --configs also time every step alone after a 512 MB
 copy that evicts the MALL, and their rates use that median, so repeated
 small-T weights count as HBM traffic only when they come from HBM.
+"decode_graph" compares host-issued T = 1 steps with replays of the same
+step captured in a HIP graph.
 
 roofline: the dominant kernel is the FP8 GEMM1 (moe_gemm_fp8_kernel<128,
 true>). "achieved" is its algorithmic bytes (touched W13 codes + scales, the
@@ -309,8 +311,49 @@ def main():
         "per_call_ms": {k_: round(v, 4) for k_, v in per_call.items()},
         "sweep": sweep,
         "gate_route": gate_route_table(args.steps, stream) if not args.no_sweep else None,
+        "decode_graph": (decode_graph(mod, results[1]["batch"], results[1]["outs"])
+                         if 1 in results else None),
     }
     print(json.dumps(line))
+
+
+def decode_graph(mod, batch, outs, n=50):
+    """A decode step (T = 1) issued by the host: wall time per step of n
+    moe_forward calls from Python (each ~10 kernel launches through the C
+    ABI) against n replays of the same forward captured once in a HIP graph
+    (torch.cuda.graph), both ending in one synchronisation. The MALL is not
+    flushed (the 340 MB of this step's weights partly stay in it), so the
+    replay time is the launch-bound floor of a serving loop, not an HBM
+    figure."""
+    import torch
+    x, lg = batch.x, batch.logits
+    for _ in range(5):
+        mod.forward(x, lg, outs)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        mod.forward(x, lg, outs)
+    torch.cuda.synchronize()
+    eager = (time.perf_counter() - t0) / n
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mod.forward(x, lg, outs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        mod.forward(x, lg, outs)
+    for _ in range(5):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        g.replay()
+    torch.cuda.synchronize()
+    replay = (time.perf_counter() - t0) / n
+    return {"T": 1, "eager_ms_per_step": round(eager * 1e3, 4),
+            "graph_replay_ms_per_step": round(replay * 1e3, 4), "steps": n}
 
 
 GATE_CFG = "ep_lora_258"

@@ -473,3 +473,27 @@ def test_fp4_small_block_scales_on_gpu(fmt):
     o = mod.forward(batch.x.cuda(), batch.logits.cuda())
     torch.cuda.synchronize()
     check_layer(spec, o["out"].cpu().numpy(), arr, nb)
+
+
+def test_mxfp4_exponents_outside_the_exact_window_are_clamped():
+    """The header documents MXFP4 block exponents outside 104..128 as
+    clamped to 99..128: a layer with some exponents 90 and 131 gives the
+    oracle's result for the same layer with those set to 99 and 128."""
+    spec = SMALL["mxfp4_small"][0].scaled(name="mxfp4_clamp", cfg_id=50)
+    T = 40
+    layer = make_layer(spec)
+    g = torch.Generator().manual_seed(50)
+    s13 = layer.w13_s.clone()
+    pick = torch.rand(s13.shape, generator=g)
+    s13[pick < 0.01] = 90
+    s13[pick > 0.99] = 131
+    layer.w13_s = s13
+    batch = make_batch(spec, layer, T)
+    nb = to_numpy_batch(batch)
+    arr = to_numpy_layer(layer)
+    arr["w13_s"] = np.clip(arr["w13_s"], 99, 128).astype(np.uint8)
+    _log("mxfp4-clamp", T, "exponents 90 / 131:", int((pick < 0.01).sum()), int((pick > 0.99).sum()))
+    mod = module_for(spec, layer)
+    o = mod.forward(batch.x.cuda(), batch.logits.cuda())
+    torch.cuda.synchronize()
+    check_layer(spec, o["out"].cpu().numpy(), arr, nb)
