@@ -288,6 +288,12 @@ def main():
                       "pct_fp8_mfma_peak": round(100 * a["flops"] / s / 1e12 / FP8_PEAK_TFLOPS, 2),
                       "weight_gbs": round(a["weight_bytes"] / s / 1e9, 1),
                       "pct_hbm_peak": round(100 * a["weight_bytes"] / s / 1e9 / HBM_PEAK_GBS, 2),
+                      # the attainable roofline min(peak, AI * BW) as a time:
+                      # max(flops / FP8 peak, touched weight bytes / 8 TB/s)
+                      "roofline_bound": ("hbm" if a["weight_bytes"] / (HBM_PEAK_GBS * 1e9) >=
+                                         a["flops"] / (FP8_PEAK_TFLOPS * 1e12) else "mfma"),
+                      "pct_attainable": round(100 * max(a["weight_bytes"] / (HBM_PEAK_GBS * 1e9),
+                                                        a["flops"] / (FP8_PEAK_TFLOPS * 1e12)) / s, 2),
                       "pairs": a["P"], "experts_touched": a["touched"]})
 
     cpu = None
