@@ -503,8 +503,18 @@ def cpu_baseline(spec, layer, batch, T, n_experts=20):
     t_ffn = time.time() - t1
     P = int(offsets[-1])
     t_layer = t_fixed + t_ffn * P / max(done, 1)
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(T / t_layer, 2), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model,
+            "gflops": round(6.0 * P * spec.H * spec.I / t_layer / 1e9, 2),
             "sample": f"fp64 oracle: route+permute+quant of all {T} tokens "
                       f"({t_fixed:.1f}s) + expert FFN of {n_experts} of {spec.n_groups} "
                       f"groups ({done} of {P} pairs, {t_ffn:.1f}s), layer time "
