@@ -156,11 +156,11 @@ class Layer:
     w2_q: torch.Tensor            # [G, H, I] or [G, H, I/2] u8
     w2_s: Optional[torch.Tensor]
     gs: Optional[torch.Tensor]    # [G, 2] f32 (gate, up) or None
-    lora_A: Optional[torch.Tensor]  # [G, r, H] bf16
-    lora_B: Optional[torch.Tensor]  # [G, 2I, r] bf16
+    lora_A: Optional[torch.Tensor]  # [n_local, r, H] bf16 (routed experts only)
+    lora_B: Optional[torch.Tensor]  # [n_local, 2I, r] bf16
     w_router: Optional[torch.Tensor]  # [H, E] f64 (router GEMM input recipe)
-    lora_A2: Optional[torch.Tensor] = None  # [G, r, I] bf16 (down LoRA)
-    lora_B2: Optional[torch.Tensor] = None  # [G, H, r] bf16
+    lora_A2: Optional[torch.Tensor] = None  # [n_local, r, I] bf16 (down LoRA)
+    lora_B2: Optional[torch.Tensor] = None  # [n_local, H, r] bf16
     gs2: Optional[torch.Tensor] = None      # [G] f32 W2 global scales (NVFP4)
 
 
@@ -231,9 +231,10 @@ def make_layer(spec: LayerSpec, device="cpu") -> Layer:
         c, d = _rand_weights(spec, H, I, std2, g, device, fp4_scale_codes=(0x28, 0x60))
         q13.append(a); s13.append(b); q2.append(c); s2.append(d)
     st = lambda xs: None if xs[0] is None else torch.stack(xs).contiguous()
-    # a batch of adapters stacks them first: [n_adapters, G, ...]
+    # LoRA covers the local routed experts (the shared expert carries none);
+    # a batch of adapters stacks them first: [n_adapters, n_local, ...]
     na = spec.n_adapters
-    lead = (G,) if na == 1 else (na, G)
+    lead = (spec.n_local,) if na == 1 else (na, spec.n_local)
     lora_A = lora_B = None
     if spec.lora_rank:
         r = spec.lora_rank

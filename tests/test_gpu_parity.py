@@ -196,6 +196,11 @@ SMALL = {
     "int4_lora32_multi": (CONFIGS["int4_g32_64"].scaled(
         name="int4_lora32_multi", H=512, I=256, n_routed=16, cfg_id=49, lora_rank=32,
         lora_down=True, n_adapters=8), 300),
+    # the smallest FP4 layer (H = I = 128, one 128-K block) with a shared
+    # expert (W2 global scale included, no LoRA on it) and a rank-4 LoRA
+    "nvfp4_min_shared": (FP4_CONFIGS["nvfp4_lora_258"].scaled(
+        name="nvfp4_min_shared", H=128, I=128, n_routed=8, n_sink=0, E_loc=None, offset=0,
+        shared=1, lora_rank=4, cfg_id=51), 20),
 }
 
 _cache = {}
