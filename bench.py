@@ -414,14 +414,15 @@ def config_table(args, stream, flush):
     touched-weight GB/s and useful TFLOP/s (stderr): back to back, and the
     median with the MALL flushed before every step (the rates use that)."""
     import torch
-    from synth import CONFIGS, FP4_CONFIGS, make_batch, make_layer
+    from synth import CONFIGS, EXT_CONFIGS, FP4_CONFIGS, make_batch, make_layer
     from tests.gpu_helpers import module_for
     print("# config              T    ms/step  flushed-med  flushed-min    tokens/s"
           "    TFLOP/s  weight GB/s", file=sys.stderr)
     # the EP + LoRA layer also with a batch of eight rank-16 adapters
     # (tokens pick one or none), the page's multi-adapter serving case
     table = dict(CONFIGS)
-    table["ep_lora_258_x8"] = CONFIGS["ep_lora_258"].scaled(
+    table.update(EXT_CONFIGS)
+    table["ep_lora_258_x8"] = EXT_CONFIGS["ep_lora_258_down"].scaled(
         name="ep_lora_258_x8", cfg_id=15, n_adapters=8)
     # the EP + LoRA layer in NVFP4 (the page's own weight format) and the
     # INT4 layer's shape in MXFP4

@@ -66,6 +66,7 @@ print no layer outputs); each step is pinned separately by the tests.
 from __future__ import annotations
 
 import math
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -76,7 +77,7 @@ E4M3_MAX = 448.0
 # number formats (OCP e4m3fn, bfloat16), written from their definitions
 # ----------------------------------------------------------------------------
 
-def e4m3_decode(codes) -> np.ndarray:
+def _e4m3_from_fields(codes) -> np.ndarray:
     """OCP e4m3fn code -> value: sign * 2^(e-7) * (1 + m/8) for e >= 1,
     sign * 2^-6 * m/8 for e == 0; 0x7F / 0xFF are NaN (no infinities)."""
     c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
@@ -87,6 +88,16 @@ def e4m3_decode(codes) -> np.ndarray:
                    np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int32)))
     val = np.where((e == 15) & ((c & 7) == 7), np.nan, val)
     return sign * val
+
+
+# the formula above evaluated once per code; decoding is a lookup in it
+_E4M3_VALUES = _e4m3_from_fields(np.arange(256))
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """OCP e4m3fn code -> value (float64), looked up in the 256 values of the
+    bit-field formula."""
+    return _E4M3_VALUES[np.asarray(codes, dtype=np.uint8)]
 
 
 def e4m3_round(v) -> np.ndarray:
@@ -323,8 +334,9 @@ def requant_fp8(h, group=128):
 def dequant_fp8_block(q, bs):
     """w[n, k] = e4m3(q[n, k]) * bs[n // 128, k // 128]."""
     w = e4m3_decode(q)
-    return w * np.repeat(np.repeat(np.asarray(bs, np.float64), 128, axis=0),
-                         128, axis=1)
+    N, K = w.shape
+    b = np.asarray(bs, np.float64)
+    return (w.reshape(N // 128, 128, K // 128, 128) * b[:, None, :, None]).reshape(N, K)
 
 
 def dequant_int4_g32(packed, scale_bits):
@@ -628,7 +640,7 @@ def gemm1_input(spec, x_bits):
 
 
 def moe_layer(spec, arr, x_bits, logits, tokens=None, routing=None,
-              with_allowance=False, adapter_ids=None):
+              with_allowance=False, adapter_ids=None, workers=1):
     """Output rows out[t, :] (float64) for the tokens asked for (all by
     default): route, rebase, per-expert FFN, then for each token
     sum_j w[t, j] y[t, j] over its local slots in ascending j, plus
@@ -638,7 +650,9 @@ def moe_layer(spec, arr, x_bits, logits, tokens=None, routing=None,
     that boundary rounding decisions of h (either neighbour admissible) can
     make: sum_j |w[t, j]| * |alt_h| |W2|^T, and the count of such elements.
     adapter_ids [T] (a batch of adapters): each token's LoRA adapter, -1 for
-    none."""
+    none. workers > 1 runs the independent per-expert FFNs on that many
+    threads (numpy releases the interpreter lock in its array work); each
+    expert's arithmetic and the combine order are unchanged."""
     T = x_bits.shape[0]
     if routing is None:
         routing = route(logits, spec.n_routed, spec.n_sink, spec.top_k,
@@ -656,17 +670,27 @@ def moe_layer(spec, arr, x_bits, logits, tokens=None, routing=None,
     xhat, xb = gemm1_input(spec, x_bits[tokens])
     contrib, allow = {}, {}
     n_boundary = 0
-    for e in sorted(pairs):
+
+    def one_expert(e):
         rows = [i for i, _ in pairs[e]]
         ad = None if adapter_ids is None else np.asarray(adapter_ids)[tokens[rows]]
         if with_allowance:
             y, det = expert_ffn(spec, arr, e, xhat[rows], xb[rows], detail=True,
                                 adapters=ad)
-            n_boundary += det["n_boundary"]
-            for (i, j), arow in zip(pairs[e], det["y_allow"]):
+            return y, det["y_allow"], det["n_boundary"]
+        return expert_ffn(spec, arr, e, xhat[rows], xb[rows], adapters=ad), None, 0
+
+    groups = sorted(pairs)
+    if workers > 1 and len(groups) > 1:
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            results = list(ex.map(one_expert, groups))
+    else:
+        results = [one_expert(e) for e in groups]
+    for e, (y, y_allow, nb) in zip(groups, results):
+        n_boundary += nb
+        if with_allowance:
+            for (i, j), arow in zip(pairs[e], y_allow):
                 allow[(i, j)] = arow
-        else:
-            y = expert_ffn(spec, arr, e, xhat[rows], xb[rows], adapters=ad)
         for (i, j), yrow in zip(pairs[e], y):
             contrib[(i, j)] = yrow
     out = np.zeros((len(tokens), spec.H))

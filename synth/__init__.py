@@ -105,8 +105,16 @@ CONFIGS = {
     "ep_lora_258": LayerSpec(
         name="ep_lora_258", cfg_id=5, fmt=FMT_FP8, H=2048, I=1024,
         n_routed=256, n_sink=2, top_k=8, E_loc=32, offset=96, lora_rank=16,
-        lora_down=True,
         gscale=True, logits="mix258", Ts=(1, 37, 512, 8192)),
+}
+
+# The expert-parallel LoRA layer with the same adapter also on the down
+# projection (its input is the SwiGLU output in true units: the MoE-LoRA
+# release notes, "Changes since 1b699bf"). Same seeds as ep_lora_258, so the
+# base weights and the up LoRA are identical.
+EXT_CONFIGS = {
+    "ep_lora_258_down": CONFIGS["ep_lora_258"].scaled(
+        name="ep_lora_258_down", lora_down=True),
 }
 
 # The same expert-parallel LoRA layer in the weight format the MoE-LoRA

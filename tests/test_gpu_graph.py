@@ -20,7 +20,7 @@ CASES = [
     # decode: one-launch front end, split-K GEMM1 + its epilogue kernel
     ("fp8_clamp_288", dict(H=2048, I=1024, n_routed=64, cfg_id=61), 1),
     # EP share with both LoRAs and a batch of adapters, plain kernels
-    ("ep_lora_258", dict(H=512, I=512, cfg_id=62, n_adapters=8), 37),
+    ("ep_lora_258", dict(H=512, I=512, cfg_id=62, n_adapters=8, lora_down=True), 37),
     # NVFP4 decode
     ("nvfp4_lora_258", dict(H=2048, I=1024, cfg_id=63), 2),
 ]

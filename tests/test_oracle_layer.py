@@ -110,9 +110,49 @@ def _mut_no_requant(mp):
     mp.setattr(O, "requant_fp8", lambda h, group=128: h)
 
 
+def _row_amax_quant(v):
+    """e4m3 quantisation with one scale per row (amax over the whole row)
+    instead of one per 128 columns: the planted grouping mistake."""
+    v = np.asarray(v, np.float64)
+    amax = np.abs(v).max(axis=1).astype(np.float32) if v.shape[0] else \
+        np.zeros(0, np.float32)
+    s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    return s
+
+
+def _mut_requant_per_row(mp):
+    def per_row(h, group=128):
+        s = _row_amax_quant(h).astype(np.float64)
+        return O.e4m3_decode(O.e4m3_round(h / s[:, None])) * s[:, None]
+    mp.setattr(O, "requant_fp8", per_row)
+
+
+def _mut_quant_act_per_row(mp):
+    def per_row(x_f32, group=128):
+        x = np.asarray(x_f32, np.float32)
+        s = _row_amax_quant(x)
+        q = O.e4m3_round((x / s[:, None]).astype(np.float32).astype(np.float64))
+        return q, np.repeat(s[:, None], x.shape[1] // group, axis=1)
+    mp.setattr(O, "quant_act_fp8", per_row)
+
+
+def _mut_w13_block_scale_rows_only(mp):
+    """Weight block scales indexed by the row block only (the first K
+    block's scale used for every K): a dropped index."""
+    real = O.dequant_fp8_block
+
+    def first_k_block(q, bs):
+        b = np.asarray(bs)
+        return real(q, np.repeat(b[:, :1], b.shape[1], axis=1))
+    mp.setattr(O, "dequant_fp8_block", first_k_block)
+
+
 @pytest.mark.parametrize("mut,name", [
     (_mut_swap_gate_up, "fp8_clamp_shared"), (_mut_drop_clamp, "fp8_clamp_shared"),
-    (_mut_drop_clamp, "fp8_oai"), (_mut_no_requant, "fp8_oai")])
+    (_mut_drop_clamp, "fp8_oai"), (_mut_no_requant, "fp8_oai"),
+    (_mut_requant_per_row, "fp8_2grp_shared"), (_mut_requant_per_row, "ep_lora_2grp"),
+    (_mut_quant_act_per_row, "fp8_2grp_shared"),
+    (_mut_w13_block_scale_rows_only, "fp8_2grp_shared")])
 def test_planted_mistakes_are_caught_by_brute_force(mut, name, monkeypatch):
     spec = TINY[name]
     ours, ref = _oracle_and_brute(spec, 5, mut, monkeypatch)
@@ -253,6 +293,43 @@ def test_rounding_alternatives_fp8_marks_only_boundary_elements():
     # a wider error band catches 1.03 too (distance to 1.0625 is 0.0325)
     alt = O.rounding_alternatives(h, np.full_like(h, 0.04), "fp8")
     assert alt[0, 2] >= 0.125
+
+
+def test_rounding_alternatives_fp8_scale_per_128_columns():
+    """Two rows, two 128-column groups each, with group amax 448, 300, 100
+    and 420 (scales in ratios that are not powers of two): the same e4m3
+    midpoints placed in every group, in that group's units, are found only
+    when each group uses its own scale, and the admissible step scales with
+    that group's s."""
+    h = np.zeros((2, 256))
+    amax = [[448.0, 300.0], [100.0, 420.0]]
+    scale = lambda a: float(np.float32(np.float32(a) / np.float32(448.0)))
+    for r in range(2):
+        for gi in range(2):
+            s = scale(amax[r][gi])
+            c = 128 * gi
+            h[r, c] = amax[r][gi]
+            h[r, c + 1] = 1.0625 * s       # midpoint of 1 and 1.125 (times s)
+            h[r, c + 2] = 248.0 * s        # midpoint of 240 and 256
+            h[r, c + 3] = 1.03 * s         # inside: 1 is nearest
+    alt = O.rounding_alternatives(h, np.full_like(h, 1e-12), "fp8")
+    for r in range(2):
+        for gi in range(2):
+            s = scale(amax[r][gi])
+            c = 128 * gi
+            np.testing.assert_allclose([alt[r, c + 1], alt[r, c + 2]],
+                                       [0.125 * s, 16.0 * s], rtol=1e-4)
+            assert alt[r, c] == 0 and alt[r, c + 3] == 0
+    # the re-quantisation itself: every group's amax element becomes 448 s of
+    # that group and the midpoints go to the even neighbour in its units
+    hq = O.requant_fp8(h)
+    for r in range(2):
+        for gi in range(2):
+            s = scale(amax[r][gi])
+            c = 128 * gi
+            assert hq[r, c] == 448.0 * s
+            assert hq[r, c + 1] == 1.0 * s and hq[r, c + 2] == 256.0 * s
+            assert hq[r, c + 3] == 1.0 * s
 
 
 def test_rounding_alternatives_bf16():

@@ -30,3 +30,15 @@ TINY["nvfp4_lora"] = LayerSpec(name="tiny_nvfp4_lora_t", cfg_id=107, fmt="nvfp4"
                                route_scale=1.5, lora_down=True)
 TINY["mxfp4_shared"] = LayerSpec(name="tiny_mxfp4_t", cfg_id=108, fmt="mxfp4", H=128,
                                  I=128, n_routed=4, top_k=2, shared=1, limit=7.0)
+# FP8 layers with H = I = 256: each GEMM spans two 128-deep K blocks and two
+# 128-row weight-scale blocks, and h spans two 128-column requant groups, so
+# the blockwise grouping of the activation scales, the weight scales and the
+# h re-quantisation is exercised (one group per row cannot tell per-group
+# from per-row scaling)
+TINY["fp8_2grp_shared"] = LayerSpec(name="tiny_fp8_2grp_t", cfg_id=109, fmt="fp8",
+                                    H=256, I=256, n_routed=4, top_k=2, shared=1,
+                                    limit=10.0)
+TINY["ep_lora_2grp"] = LayerSpec(name="tiny_ep_lora_2grp_t", cfg_id=110, fmt="fp8",
+                                 H=256, I=256, n_routed=8, n_sink=2, top_k=3, E_loc=3,
+                                 offset=2, lora_rank=4, gscale=True, logits="mix258",
+                                 alpha=1.702, beta=1.0, limit=7.0, lora_down=True)
