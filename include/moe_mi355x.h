@@ -67,15 +67,26 @@ typedef enum {
                           e4m3(scale) * gscale [LORA-AOT "Changes since
                           1b699bf": per-half NVFP4 global scales]. e2m1:
                           sign bit 3, magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6.
-                          NaN scale codes (0x7F, 0xFF) are not supported. */
+                          NaN scale codes (0x7F, 0xFF) set
+                          MOE_DEVERR_W4_SCALE. */
   MOE_W_MXFP4 = 4      /* e2m1 codes as NVFP4; scale e8m0 u8 [G][N][K/32];
                           w = e2m1(code) * 2^(scale - 127). Exact for scale
-                          exponents 104..128 (2^-23 .. 2); others are
-                          clamped to 99..128, giving wrong values. */
+                          exponents 104..128 (2^-23 .. 2); a call that meets
+                          another exponent sets MOE_DEVERR_W4_SCALE (its
+                          outputs are then not valid). */
 } moe_wfmt;
 
 /* err_word bits */
 #define MOE_DEVERR_GLOBAL_ID_OOB 0x1 /* a routing id < 0 or >= num_experts_global */
+#define MOE_DEVERR_F16_RANGE 0x2     /* 4-bit layer: a bf16 activation x or h with
+                                        |v| > 65504 (or not finite), beyond the f16
+                                        operands of its matrix cores; the outputs
+                                        of that call are not valid */
+#define MOE_DEVERR_W4_SCALE 0x4      /* 4-bit layer: a weight scale outside the
+                                        range the kernels expand exactly: INT4 a
+                                        nonzero |scale| outside [2^-13, 2^13),
+                                        NVFP4 a NaN e4m3 code, MXFP4 an exponent
+                                        outside 104..128; outputs not valid */
 
 /* Parameterized SwiGLU [CLAMP-PR "Modifications"; OAI-PR "Summary",
  * "Compatibility"]:
@@ -104,7 +115,9 @@ typedef struct {
 } moe_weights;
 /* Alignment (MOE_ERR_PARAM): 4-bit codes 16 bytes; INT4 and NVFP4 scales
  * 2 bytes. Activations of 4-bit layers enter the matrix cores as f16:
- * exact for |x| in [2^-14, 65504] (and h alike). */
+ * exact for |x| in [2^-14, 65504] (and h alike); larger magnitudes set
+ * MOE_DEVERR_F16_RANGE, smaller ones lose low bits (an absolute error below
+ * 2^-25 per element). */
 
 /* Rank-r LoRA of the local experts [LORA-AOT "Changes since 1b699bf"].
  * On the fused gate/up projection ("lora"): z = x A_e^T (fp32),
@@ -222,6 +235,10 @@ int moe_quantize_act_fp8(const void *x_bf16, long T, int H, void *xq,
                          float *xs, void *stream);
 
 /* ------------------------------------------------ grouped GEMM1 + SwiGLU -- */
+/* err_word of the GEMM entry points: device int32, ORed with the
+ * MOE_DEVERR_F16_RANGE / MOE_DEVERR_W4_SCALE bits a 4-bit layer meets
+ * (required for 4-bit weights: MOE_ERR_NULL without it; nullable, and
+ * never written, for BF16 and FP8 weights). */
 /* For each group g and each of its sorted rows r (token t of pair
  * sorted_pair[r]):  [g | u] = x_t W13_g^T  (fp32 accumulation;
  * FP8: per 128-K block partial sums times xs[t][kb] * scale[g][nb][kb]),
@@ -252,8 +269,8 @@ int moe_grouped_gemm1_act(const moe_weights *w13, const void *x,
                           int I, int top_k, long p_cap, const int *offsets,
                           const int *sorted_pair, const moe_act_params *act,
                           const moe_lora *lora, void *h, float *hs,
-                          void *h_lora, void *ws, size_t ws_bytes,
-                          void *stream);
+                          void *h_lora, int *err_word, void *ws,
+                          size_t ws_bytes, void *stream);
 size_t moe_gemm1_workspace_size(const moe_weights *w13, long p_cap,
                                 const moe_lora *lora);
 
@@ -269,7 +286,8 @@ size_t moe_gemm1_workspace_size(const moe_weights *w13, long p_cap,
  *             + shared_w * y[pair_row[T*top_k + t]]   (if shared_expert)
  * [INT4-PR: slot-specific routing-weight reduction, fp32 accumulation].
  * Every out element is written (0 for a token with no local pair).
- * w2->N = H, w2->K = I. out fp32 [T][H]. Workspace:
+ * w2->N = H, w2->K = I. out fp32 [T][H]. Limits: 1 <= top_k <= 64
+ * (MOE_ERR_SHAPE). err_word as for moe_grouped_gemm1_act. Workspace:
  * moe_gemm2_workspace_size(w2, p_cap, lora_down) bytes: the fp32 y rows, or
  * for FP8 / 4-bit weights at decode sizes their split-K partial sums
  * (4 * p_cap * H floats, reduced by the combine in a fixed order; the
@@ -284,8 +302,8 @@ int moe_grouped_gemm2_combine(const moe_weights *w2, const void *h,
                               int top_k, int shared_expert, long p_cap,
                               const int *offsets, const int *sorted_pair,
                               const int *pair_row, const float *topk_w,
-                              float shared_w, float *out, void *ws,
-                              size_t ws_bytes, void *stream);
+                              float shared_w, float *out, int *err_word,
+                              void *ws, size_t ws_bytes, void *stream);
 size_t moe_gemm2_workspace_size(const moe_weights *w2, long p_cap,
                                 const moe_lora *lora_down);
 
@@ -311,7 +329,7 @@ typedef struct {
  * moe_grouped_gemm2_combine. x_bf16 bf16 [T][H]; logits fp32 [T][ld_logits]
  * with ld_logits >= num_experts_global + n_sink. Outputs out fp32 [T][H],
  * topk_ids/topk_w [T][top_k], sink_w [T][n_sink] (NULL iff n_sink == 0),
- * err_word as in moe_permute. Workspace: moe_workspace_size(layer, T_max)
+ * err_word as in moe_permute and the GEMM entry points. Workspace: moe_workspace_size(layer, T_max)
  * bytes, T <= T_max. Errors: those of the steps, checked before any launch. */
 int moe_forward(const moe_layer *layer, const void *x_bf16,
                 const float *logits, long T, long ld_logits, float *out,

@@ -25,6 +25,8 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "moe_mi355x.h")
 MOE_W_BF16, MOE_W_FP8_B128, MOE_W_INT4_G32, MOE_W_NVFP4, MOE_W_MXFP4 = 0, 1, 2, 3, 4
 _PACKED4 = (MOE_W_INT4_G32, MOE_W_NVFP4, MOE_W_MXFP4)
 MOE_DEVERR_GLOBAL_ID_OOB = 0x1
+MOE_DEVERR_F16_RANGE = 0x2
+MOE_DEVERR_W4_SCALE = 0x4
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE",
           -3: "MOE_ERR_FORMAT", -4: "MOE_ERR_LOCAL_RANGE", -5: "MOE_ERR_PARAM",
           -6: "MOE_ERR_WORKSPACE", -8: "MOE_ERR_HIP"}
@@ -83,14 +85,14 @@ _SIGS = {
                                       c_long, c_void_p, c_void_p,
                                       POINTER(MoeActParams), POINTER(MoeLora),
                                       c_void_p, c_void_p, c_void_p, c_void_p,
-                                      c_size_t, c_void_p]),
+                                      c_void_p, c_size_t, c_void_p]),
     "moe_gemm1_workspace_size": (c_size_t, [POINTER(MoeWeights), c_long, POINTER(MoeLora)]),
     "moe_grouped_gemm2_combine": (c_int, [POINTER(MoeWeights), c_void_p, c_void_p,
                                           c_void_p, POINTER(MoeLora),
                                           c_long, c_int, c_int, c_int, c_int,
                                           c_long, c_void_p, c_void_p, c_void_p,
                                           c_void_p, c_float, c_void_p, c_void_p,
-                                          c_size_t, c_void_p]),
+                                          c_void_p, c_size_t, c_void_p]),
     "moe_gemm2_workspace_size": (c_size_t, [POINTER(MoeWeights), c_long,
                                             POINTER(MoeLora)]),
     "moe_forward": (c_int, [POINTER(MoeLayer), c_void_p, c_void_p, c_long, c_long,
@@ -242,11 +244,12 @@ def _lp(lora):
 def moe_grouped_gemm1_act(w13: MoeWeights, x, xs, x_bf16, T, H, I, top_k, p_cap,
                           offsets, sorted_pair, act: MoeActParams,
                           lora: Optional[MoeLora], h, hs, ws, stream=None,
-                          h_lora=None):
+                          h_lora=None, err_word=None):
     _check(lib().moe_grouped_gemm1_act(
         ctypes.byref(w13), _p(x), _p(xs), _p(x_bf16), T, H, I, top_k, p_cap,
         _p(offsets), _p(sorted_pair), ctypes.byref(act), _lp(lora), _p(h), _p(hs),
-        _p(h_lora), _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+        _p(h_lora), _p(err_word), _p(ws),
+        0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream)), "moe_grouped_gemm1_act")
 
 
@@ -258,12 +261,13 @@ def moe_gemm2_workspace_size(w2: MoeWeights, p_cap,
 def moe_grouped_gemm2_combine(w2: MoeWeights, h, hs, T, H, I, top_k,
                               shared_expert, p_cap, offsets, pair_row, topk_w,
                               shared_w, out, ws, stream=None, h_lora=None,
-                              lora_down: Optional[MoeLora] = None, sorted_pair=None):
+                              lora_down: Optional[MoeLora] = None, sorted_pair=None,
+                              err_word=None):
     _check(lib().moe_grouped_gemm2_combine(
         ctypes.byref(w2), _p(h), _p(hs), _p(h_lora), _lp(lora_down), T, H, I,
         top_k, shared_expert, p_cap, _p(offsets), _p(sorted_pair), _p(pair_row),
-        _p(topk_w), shared_w, _p(out), _p(ws), ws.numel() * ws.element_size(),
-        _stream(stream)), "moe_grouped_gemm2_combine")
+        _p(topk_w), shared_w, _p(out), _p(err_word), _p(ws),
+        ws.numel() * ws.element_size(), _stream(stream)), "moe_grouped_gemm2_combine")
 
 
 def moe_workspace_size(layer: MoeLayer, T_max) -> int:

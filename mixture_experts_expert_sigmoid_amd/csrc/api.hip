@@ -14,6 +14,8 @@
 #include "moe_mi355x.h"
 
 static_assert(MOE_DEVERR_GLOBAL_ID_OOB == MOE_DEVERR_BIT_OOB, "err bit");
+static_assert(MOE_DEVERR_F16_RANGE == MOE_DEVERR_BIT_F16_RANGE, "err bit");
+static_assert(MOE_DEVERR_W4_SCALE == MOE_DEVERR_BIT_W4_SCALE, "err bit");
 
 namespace {
 
@@ -261,7 +263,8 @@ static moe::Gemm1Args gemm1_args(const moe_weights* w13, const void* x,
                                  const int* sorted_pair,
                                  const moe_act_params* act,
                                  const moe_lora* lora, const float* z, void* h,
-                                 float* hs, float* part, void* x16, void* h_lora) {
+                                 float* hs, float* part, void* x16, void* h_lora,
+                                 int* err_word) {
   moe::Gemm1Args a{};
   a.fmt = w13->fmt;
   a.wq = w13->q;
@@ -292,6 +295,7 @@ static moe::Gemm1Args gemm1_args(const moe_weights* w13, const void* x,
   a.part = part;
   a.x16 = x16;
   a.h_lora = h_lora;
+  a.err = err_word;
   return a;
 }
 
@@ -300,10 +304,12 @@ int moe_grouped_gemm1_act(const moe_weights* w13, const void* x,
                           int I, int top_k, long p_cap, const int* offsets,
                           const int* sorted_pair, const moe_act_params* act,
                           const moe_lora* lora, void* h, float* hs, void* h_lora,
-                          void* ws, size_t ws_bytes, void* stream) {
+                          int* err_word, void* ws, size_t ws_bytes, void* stream) {
   int st = gemm1_checks(w13, x, xs, x_bf16, T, H, I, top_k, p_cap, offsets,
                         sorted_pair, act, lora, h, hs);
   if (st) return st;
+  // 4-bit layers report activation and scale range problems there
+  if (is4(w13->fmt) && p_cap > 0 && !err_word) return MOE_ERR_NULL;
   // BF16 / 4-bit layers write h in bf16 already: it is the down-LoRA input
   if (h_lora && w13->fmt != MOE_W_FP8_B128) return MOE_ERR_PARAM;
   size_t need = moe_gemm1_workspace_size(w13, p_cap, lora);
@@ -323,7 +329,7 @@ int moe_grouped_gemm1_act(const moe_weights* w13, const void* x,
   if (e == hipSuccess)
     e = moe::launch_gemm1(gemm1_args(w13, x, xs, T, H, I, top_k, p_cap, offsets,
                                      sorted_pair, act, lora, z, h, hs, part, x16,
-                                     h_lora), s);
+                                     h_lora, err_word), s);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_grouped_gemm1_act");
 }
 
@@ -337,7 +343,8 @@ static int gemm2_checks(const moe_weights* w2, const void* h, const float* hs,
                         long T, int H, int I, int top_k, int shared,
                         long p_cap, const int* offsets, const int* pair_row,
                         const float* topk_w, float shared_w, const float* out) {
-  if (T < 0 || p_cap < 0 || top_k < 1) return MOE_ERR_SHAPE;
+  // top_k <= 64: the split-K combine keeps a token's top_k + 1 pairs in LDS
+  if (T < 0 || p_cap < 0 || top_k < 1 || top_k > 64) return MOE_ERR_SHAPE;
   if (H < 128 || I < 128 || H % 128 || I % 128) return MOE_ERR_SHAPE;
   if (shared != 0 && shared != 1) return MOE_ERR_PARAM;
   if (!finite(shared_w)) return MOE_ERR_PARAM;
@@ -356,11 +363,12 @@ int moe_grouped_gemm2_combine(const moe_weights* w2, const void* h,
                               int top_k, int shared_expert, long p_cap,
                               const int* offsets, const int* sorted_pair,
                               const int* pair_row, const float* topk_w,
-                              float shared_w, float* out, void* ws,
+                              float shared_w, float* out, int* err_word, void* ws,
                               size_t ws_bytes, void* stream) {
   int st = gemm2_checks(w2, h, hs, T, H, I, top_k, shared_expert, p_cap,
                         offsets, pair_row, topk_w, shared_w, out);
   if (st) return st;
+  if (is4(w2->fmt) && p_cap > 0 && !err_word) return MOE_ERR_NULL;
   if ((st = check_lora(lora_down, w2->n_groups))) return st;
   if (lora_down && p_cap > 0 && (!h_lora || !sorted_pair)) return MOE_ERR_NULL;
   size_t need = moe_gemm2_workspace_size(w2, p_cap, lora_down);
@@ -399,6 +407,7 @@ int moe_grouped_gemm2_combine(const moe_weights* w2, const void* h,
     a.n_adapters = lora_down->n_adapters;
     a.zad = zad_of(z2, p_cap, lora_down);
   }
+  a.err = err_word;
   e = moe::launch_gemm2(a, s);
   if (e == hipSuccess)
     e = moe::launch_combine(y, T, H, top_k, shared_expert, pair_row, topk_w,
@@ -563,7 +572,7 @@ int moe_forward(const moe_layer* L, const void* x_bf16, const float* logits,
                                  T, L->H, L->I, L->top_k, pc, offsets,
                                  sorted_pair, &L->act, L->lora, z, h,
                                  fp8 ? hs : nullptr, g1_part, xq,
-                                 fp8 && L->lora_down ? h_lora : nullptr);
+                                 fp8 && L->lora_down ? h_lora : nullptr, err_word);
   ga.x16_ready = x16_ready;
   e = moe::launch_gemm1(ga, s);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/gemm1");
@@ -599,6 +608,7 @@ int moe_forward(const moe_layer* L, const void* x_bf16, const float* logits,
     a.n_adapters = L->lora_down->n_adapters;
     a.zad = zad_of(z2, pc, L->lora_down);
   }
+  a.err = err_word;
   e = moe::launch_gemm2(a, s);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/gemm2");
   e = moe::launch_combine(y, T, L->H, L->top_k, L->shared_expert, pair_row,

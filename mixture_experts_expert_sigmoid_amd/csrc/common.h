@@ -4,9 +4,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-// err_word bit for a routing id outside [0, num_experts_global); equal to
-// MOE_DEVERR_GLOBAL_ID_OOB of the public header.
+// err_word bits, equal to the public header's MOE_DEVERR_*: a routing id
+// outside [0, num_experts_global); a 4-bit layer's bf16 activation (x or h)
+// beyond the f16 range of its matrix-core operands; a 4-bit weight scale
+// outside the range whose products expand exactly to f16.
 #define MOE_DEVERR_BIT_OOB 0x1
+#define MOE_DEVERR_BIT_F16_RANGE 0x2
+#define MOE_DEVERR_BIT_W4_SCALE 0x4
 
 namespace moe {
 

@@ -26,8 +26,13 @@ __global__ __launch_bounds__(1024) void front_small_kernel(FrontArgs a) {
       quant_act_unit((const uint16_t*)a.x, wi, a.H, (uint8_t*)a.xq, a.xs);
   } else if constexpr (MODE == 2) {
     const long n8 = a.T * (long)a.H / 8;
-    for (long i = threadIdx.x; i < n8; i += 1024)
-      *(f16x8*)((uint16_t*)a.xq + 8 * i) = bf16x8_f16p(*(const i32x4*)((const uint16_t*)a.x + 8 * i));
+    bool over = false;
+    for (long i = threadIdx.x; i < n8; i += 1024) {
+      const i32x4 v = *(const i32x4*)((const uint16_t*)a.x + 8 * i);
+      *(f16x8*)((uint16_t*)a.xq + 8 * i) = bf16x8_f16p(v);
+      over |= bf16x8_f16_overflow(v);
+    }
+    if (over) atomicOr(a.err_word, MOE_DEVERR_BIT_F16_RANGE);
   }
   __syncthreads();                               // the ids are complete
   permute_small_body(a.ids, a.T * (long)a.k, a.T, a.n_routed, a.off, a.E_loc, a.G, a.shared,

@@ -288,12 +288,13 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t s) {
   P.h = (uint8_t*)a.h;
   P.hs = a.hs;
   P.h_lora = (uint16_t*)a.h_lora;
+  P.err = a.err;
   long hint = a.G > 0 ? a.p_cap / a.G : a.p_cap;
   if (a.fmt != FMT_BF16) {
     const bool fp8 = a.fmt == FMT_FP8;
     hipError_t e = hipSuccess;
     if (!fp8) {                    // f16 activations in the 4-bit kernel's K order
-      if (!a.x16_ready) e = launch_act_f16p(a.x, a.T, a.H, a.x16, s);
+      if (!a.x16_ready) e = launch_act_f16p(a.x, a.T, a.H, a.x16, a.err, s);
       if (e != hipSuccess) return e;
       P.a = (const uint8_t*)a.x16;
     }
@@ -332,6 +333,7 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t s) {
   P.lora_scale = a.lora_scale;
   P.n_adapters = a.n_adapters;
   P.zad = a.zad;
+  P.err = a.err;
   long hint = a.G > 0 ? a.p_cap / a.G : a.p_cap;
   *a.sk_grid = 0;
   const int NT = (a.H + 255) / 256;

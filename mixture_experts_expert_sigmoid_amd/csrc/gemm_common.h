@@ -67,6 +67,7 @@ struct GemmParams {
   float* part;
   long p_rows;
   int lds_bytes;             // the launch's dynamic LDS (the LoRA epilogue's room)
+  int* err;                  // nullable: 4-bit range problems (MOE_DEVERR_BIT_*)
 };
 
 // Dynamic LDS of the FP8 / 4-bit instantiations with LoRA code: room for a
@@ -521,6 +522,7 @@ hipError_t launch_gemm_nvfp4(const GemmParams& P, bool g1, long p_cap, int NT, h
                              int* sk_grid);
 hipError_t launch_gemm_mxfp4(const GemmParams& P, bool g1, long p_cap, int NT, hipStream_t s,
                              int* sk_grid);
-hipError_t launch_act_f16p(const void* x, long T, int H, void* out, hipStream_t s);
+// err (nullable): MOE_DEVERR_BIT_F16_RANGE is ORed in for a value beyond f16
+hipError_t launch_act_f16p(const void* x, long T, int H, void* out, int* err, hipStream_t s);
 
 }  // namespace moe

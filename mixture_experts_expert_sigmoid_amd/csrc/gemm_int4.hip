@@ -8,17 +8,19 @@ namespace moe {
 // x bf16 [T][H] -> f16 [T][H] with each 8 columns in the order k0, k4, k1,
 // k5, k2, k6, k3, k7 (the GEMM1 activation operand); one thread per 8
 __global__ __launch_bounds__(256) void act_f16p_kernel(const uint16_t* __restrict__ x, long n8,
-                                                       uint16_t* __restrict__ out) {
+                                                       uint16_t* __restrict__ out, int* err) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= n8) return;
-  *(f16x8*)(out + 8 * i) = bf16x8_f16p(*(const i32x4*)(x + 8 * i));
+  const i32x4 v = *(const i32x4*)(x + 8 * i);
+  *(f16x8*)(out + 8 * i) = bf16x8_f16p(v);
+  if (err && bf16x8_f16_overflow(v)) atomicOr(err, MOE_DEVERR_BIT_F16_RANGE);
 }
 
-hipError_t launch_act_f16p(const void* x, long T, int H, void* out, hipStream_t s) {
+hipError_t launch_act_f16p(const void* x, long T, int H, void* out, int* err, hipStream_t s) {
   const long n8 = T * (long)H / 8;
   if (n8 == 0) return hipSuccess;
   act_f16p_kernel<<<dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s>>>(
-      (const uint16_t*)x, n8, (uint16_t*)out);
+      (const uint16_t*)x, n8, (uint16_t*)out, err);
   return hipGetLastError();
 }
 

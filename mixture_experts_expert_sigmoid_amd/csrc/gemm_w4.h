@@ -23,7 +23,8 @@
 //   subtraction leaves n - 8 (or 16 (n - 8)) exactly, and one f16
 //   multiplication by the scale (or scale / 16) is exact because n - 8 has
 //   at most 3 significant bits and a bf16 scale 8: the product fits f16's
-//   11 for scales in [2^-10, 2^15].
+//   11 for |scale| in [2^-13, 2^13) (scale / 16 stays on f16's 2^-24 grid,
+//   8 |scale| below its 65504).
 //   FP4: the three magnitude bits of a code go to f16 bits 11..9 and its
 //   sign to bit 15, which is exactly e2m1 * 2^-14 (the e2m1 subnormal 0.5
 //   lands on the f16 subnormal 2^-15); one f16 multiplication by the block
@@ -33,6 +34,10 @@
 //   on a grid of 2^-24 or coarser (MXFP4: for exponents 104..128). The
 //   NVFP4 accumulator is multiplied by 2^7 (and W2's by its global scale)
 //   after the K loop; W13's global scales are applied in the epilogue.
+//   Scales outside those ranges (INT4 and MXFP4 as stated, NVFP4's NaN
+//   codes) and bf16 activations beyond f16's 65504 are checked as they are
+//   used and reported in the error word; the kernels then still run (with
+//   MXFP4 exponents clamped to 99..128), but those outputs are not valid.
 //
 // K order: the expansion of one dword (k0..k7 of a 32-K group) yields the
 // f16 values in the order k0, k4, k1, k5, k2, k6, k3, k7; the activations
@@ -150,6 +155,19 @@ struct W4 {
       y = x;
     }
   }
+  // a scale word whose products would not expand exactly to f16: INT4 a
+  // bf16 |s| outside [2^-13, 2^13) other than zero, NVFP4 a NaN e4m3 code,
+  // MXFP4 an exponent outside 104..128
+  __device__ static bool scale_bad(uint32_t sw) {
+    if constexpr (WF == FMT_INT4) {
+      const uint32_t a = sw & 0x7FFFu;
+      return a != 0u && (a < 0x3900u || a >= 0x4600u);
+    } else if constexpr (WF == FMT_NVFP4) {
+      return (sw & 0x7Fu) == 0x7Fu || (sw & 0x7F00u) == 0x7F00u;
+    } else {
+      return sw - 104u > 24u;
+    }
+  }
   __device__ static f16x8 expand(uint32_t w, f16x2 x, f16x2 y, bool second) {
     if constexpr (WF == FMT_INT4) return int4x8_f16(w, x, y);
     else return fp4x8_f16(w, second ? y : x);
@@ -247,6 +265,8 @@ __device__ __forceinline__ void w4_tile(const GemmParams& P, const Tile& tl, uin
   const uint8_t* sp1 = F::lane_ptr(P, g, nh, lg);
 
   i32x4 ra[Gm::A_PT];
+  // range problems met by the wave (ballot masks, uniform): scales, h
+  uint64_t bad_s = 0, bad_h = 0;
   auto gload_a = [&](int s) {            // past the last block: re-read it
     const long adv = (long)min(s, k1 - 1) * 256;
 #pragma unroll
@@ -259,8 +279,10 @@ __device__ __forceinline__ void w4_tile(const GemmParams& P, const Tile& tl, uin
       if (Gm::A_CH % kThreads == 0 || tid + i * kThreads < Gm::A_CH) {
         if constexpr (G1)                // already f16 in the K order above
           *(i32x4*)(st + a_st[i]) = ra[i];
-        else                             // h: bf16 -> f16, reordered
+        else {                           // h: bf16 -> f16, reordered
           *(f16x8*)(st + a_st[i]) = bf16x8_f16p(ra[i]);
+          bad_h |= __builtin_amdgcn_ballot_w64(bf16x8_f16_overflow(ra[i]));
+        }
       }
     }
   };
@@ -290,6 +312,7 @@ __device__ __forceinline__ void w4_tile(const GemmParams& P, const Tile& tl, uin
   // spread over the subtiles between the MFMAs.
   f16x8 bwA[2][2], bwB[2][2];            // [ns][j] of the first / second half
   auto scale_regs = [&](const WB& b, f16x2 (&sx)[2], f16x2 (&sy)[2]) {
+    bad_s |= __builtin_amdgcn_ballot_w64(F::scale_bad(b.s[0]) || F::scale_bad(b.s[1]));
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns) F::regs(b.s[ns], sx[ns], sy[ns]);
   };
@@ -375,6 +398,8 @@ __device__ __forceinline__ void w4_tile(const GemmParams& P, const Tile& tl, uin
     block(s, 0, rb0, rb1);
     __syncthreads();
   }
+  if ((bad_s | bad_h) && P.err && lane == 0)
+    atomicOr(P.err, (bad_s ? MOE_DEVERR_BIT_W4_SCALE : 0) | (bad_h ? MOE_DEVERR_BIT_F16_RANGE : 0));
   if constexpr (WF != FMT_INT4) {
     // NVFP4's 2^7 and, for W2, the expert's global scale (before the LoRA
     // delta, which is in true units)

@@ -129,6 +129,7 @@ struct Gemm1Args {
   void* x16;             // 4-bit formats: f16 activations (T * H * 2 bytes) or NULL
   bool x16_ready;        // x16 already holds them (the decode front end wrote it)
   void* h_lora;          // FP8: bf16 SwiGLU output before the requant, or NULL
+  int* err;              // nullable: 4-bit range problems (f16 activations, scales)
 };
 hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t s);
 
@@ -151,6 +152,7 @@ struct Gemm2Args {
   float lora_scale;
   int n_adapters;
   const int* zad;
+  int* err;              // nullable: 4-bit range problems (f16 h, scales)
 };
 hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t s);
 

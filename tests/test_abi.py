@@ -100,9 +100,9 @@ def test_gemm_validation():
     L = M.lib()
     act = M.act_params(1.0, 0.0, math.inf)
     w = _w(N=2 * 128, K=256)
-    g1 = lambda w_, act_, H=256, I=128, lora=None, hl=None: L.moe_grouped_gemm1_act(
+    g1 = lambda w_, act_, H=256, I=128, lora=None, hl=None, err=1: L.moe_grouped_gemm1_act(
         ctypes.byref(w_), 1, 1, None, 4, H, I, 2, 8, 1, 1, ctypes.byref(act_),
-        lora, 1, 1, hl, ctypes.c_void_p(1), 1 << 20, None)
+        lora, 1, 1, hl, err, ctypes.c_void_p(1), 1 << 20, None)
     assert g1(_w(N=256, K=250), act, H=250) == -2        # H % 128
     assert g1(_w(N=256, K=256), act, H=256, I=100) == -2   # I % 128
     assert g1(_w(N=512, K=256), act) == -2               # N != 2I
@@ -114,6 +114,9 @@ def test_gemm_validation():
     assert g1(M.MoeWeights(M.MOE_W_NVFP4, 4, 256, 256, 256, 257, None), act) == -5
     assert g1(M.MoeWeights(M.MOE_W_NVFP4, 4, 256, 256, 256, None, None), act) == -1
     assert g1(M.MoeWeights(1, 4, 256, 256, 1, None, None), act) == -1   # fp8 needs scales
+    # 4-bit layers report range problems through the error word: required
+    for f in (M.MOE_W_INT4_G32, M.MOE_W_NVFP4, M.MOE_W_MXFP4):
+        assert g1(M.MoeWeights(f, 4, 256, 256, 256, 256, None), act, err=None) == -1
     assert g1(w, M.act_params(1.0, 0.0, 0.0)) == -5       # limit must be > 0
     assert g1(w, M.act_params(1.0, 0.0, math.nan)) == -5
     assert g1(w, M.act_params(math.inf, 0.0, 7.0)) == -5
@@ -123,10 +126,14 @@ def test_gemm_validation():
     # the bf16 down-LoRA input is an FP8-only output of GEMM1
     assert g1(_w(fmt=M.MOE_W_BF16, N=256, K=256), act, hl=ctypes.c_void_p(256)) == -5
     w2 = _w(N=256, K=128)
-    g2 = lambda hl=None, ld=None, ws=None, nb=0, sp=1: L.moe_grouped_gemm2_combine(
-        ctypes.byref(w2), 1, 1, hl, ld, 4, 256, 128, 2, 0, 8, 1, sp, 1, 1, 1.0, 1, ws, nb,
-        None)
+    g2 = lambda hl=None, ld=None, ws=None, nb=0, sp=1, k=2, w_=w2, err=1: \
+        L.moe_grouped_gemm2_combine(ctypes.byref(w_), 1, 1, hl, ld, 4, 256, 128, k, 0,
+                                    4 * k, 1, sp, 1, 1, 1.0, 1, err, ws, nb, None)
     assert g2() == -6                                    # workspace
+    # top_k <= 64: the split-K combine holds a token's pairs in LDS
+    assert g2(k=65) == -2 and g2(k=64) == -6 and g2(k=0) == -2
+    w2i = M.MoeWeights(M.MOE_W_INT4_G32, 4, 256, 128, 256, 256, None)
+    assert g2(w_=w2i, err=None) == -1                     # 4-bit: error word required
     ld = M.MoeLora(16, 4, 1.0, 256, 256, 1, None)
     big = dict(ws=ctypes.c_void_p(256), nb=1 << 30)
     assert g2(ld=ctypes.pointer(ld), **big) == -1         # no h_lora
@@ -141,7 +148,7 @@ def test_gemm_validation():
     # W2 global scales are an FP4-format input
     w2g = M.MoeWeights(M.MOE_W_FP8_B128, 4, 256, 128, 1, 1, 256)
     assert L.moe_grouped_gemm2_combine(ctypes.byref(w2g), 1, 1, None, None, 4, 256, 128, 2,
-                                       0, 8, 1, 1, 1, 1, 1.0, 1, ctypes.c_void_p(256),
+                                       0, 8, 1, 1, 1, 1, 1.0, 1, None, ctypes.c_void_p(256),
                                        1 << 30, None) == -3
     assert L.moe_gemm2_workspace_size(ctypes.byref(w2), 100, None) >= 100 * 256 * 4
     assert (L.moe_gemm2_workspace_size(ctypes.byref(w2), 100, ctypes.pointer(ld)) -

@@ -303,13 +303,14 @@ def _stepwise(spec, mod, batch, T):
     if mod.lora_down is not None:
         h_lora = torch.zeros(pc, I, dtype=torch.bfloat16, device="cuda") if fp8 else h
     M.moe_grouped_gemm1_act(mod.w13, xin, xs, x, T, H, I, k, pc, offsets, sp, mod.act,
-                            mod.lora, h, hs, ws1, h_lora=h_lora if fp8 else None)
+                            mod.lora, h, hs, ws1, h_lora=h_lora if fp8 else None,
+                            err_word=err)
     out = torch.empty(T, H, device="cuda")
     ws2 = torch.empty(M.moe_gemm2_workspace_size(mod.w2, pc, mod.lora_down),
                       dtype=torch.uint8, device="cuda")
     M.moe_grouped_gemm2_combine(mod.w2, h, hs, T, H, I, k, spec.shared, pc, offsets, pr,
                                 w, spec.shared_w, out, ws2, h_lora=h_lora,
-                                lora_down=mod.lora_down, sorted_pair=sp)
+                                lora_down=mod.lora_down, sorted_pair=sp, err_word=err)
     torch.cuda.synchronize()
     assert M.moe_read_device_error(err) == 0
     if fp8:
@@ -490,10 +491,11 @@ def test_fp4_small_block_scales_on_gpu(fmt):
     check_layer(spec, o["out"].cpu().numpy(), arr, nb)
 
 
-def test_mxfp4_exponents_outside_the_exact_window_are_clamped():
-    """The header documents MXFP4 block exponents outside 104..128 as
-    clamped to 99..128: a layer with some exponents 90 and 131 gives the
-    oracle's result for the same layer with those set to 99 and 128."""
+def test_mxfp4_exponents_outside_the_exact_window_are_flagged():
+    """MXFP4 block exponents outside the exactly expanded 104..128 set
+    MOE_DEVERR_W4_SCALE (and nothing else); the kernels clamp them to
+    99..128, so a layer with some exponents 90 and 131 gives the oracle's
+    result for the same layer with those set to 99 and 128."""
     spec = SMALL["mxfp4_small"][0].scaled(name="mxfp4_clamp", cfg_id=50)
     T = 40
     layer = make_layer(spec)
@@ -511,4 +513,63 @@ def test_mxfp4_exponents_outside_the_exact_window_are_clamped():
     mod = module_for(spec, layer)
     o = mod.forward(batch.x.cuda(), batch.logits.cuda())
     torch.cuda.synchronize()
+    assert M.moe_read_device_error(o["err_word"]) == M.MOE_DEVERR_W4_SCALE
     check_layer(spec, o["out"].cpu().numpy(), arr, nb)
+
+
+@pytest.mark.parametrize("case", ["int4_scale_big", "int4_scale_tiny", "nvfp4_nan_scale",
+                                  "x_beyond_f16", "h_beyond_f16", "in_range"])
+def test_4bit_range_problems_set_error_bits(case):
+    """In-range data that the 4-bit kernels cannot expand exactly sets its
+    error bit: an INT4 scale of 2^13 or 2^-14, an NVFP4 NaN scale code, an
+    activation beyond f16 (1e5, finite in bf16) and an h beyond f16 (huge
+    gate and up values). Edge values just inside the ranges set nothing: a
+    W2 scale of 8160 and a W13 scale of -2^-13 in every expert, and x =
+    65280 in a column whose W13 weights are zero (so h stays ordinary)."""
+    _log("4bit-range", case)
+    fmt = "nvfp4" if case == "nvfp4_nan_scale" else "int4"
+    spec = (SMALL["nvfp4_lora_small"][0] if fmt == "nvfp4" else SMALL["int4_small"][0]) \
+        .scaled(name=f"range_{case}", cfg_id=52, lora_rank=0, lora_down=False)
+    layer = make_layer(spec)
+    batch = make_batch(spec, layer, 24)
+    x = batch.x.clone()
+    want = 0
+    if case == "int4_scale_big":          # every expert, so a routed one meets it
+        s = layer.w2_s.clone()
+        s[:, 3, 1] = 8192.0
+        layer.w2_s = s
+        want = M.MOE_DEVERR_W4_SCALE
+    elif case == "int4_scale_tiny":
+        s = layer.w13_s.clone()
+        s[:, 7, 2] = 2.0 ** -14
+        layer.w13_s = s
+        want = M.MOE_DEVERR_W4_SCALE
+    elif case == "nvfp4_nan_scale":
+        s = layer.w13_s.clone().view(torch.uint8)
+        s[:, 5, 3] = 0xFF
+        layer.w13_s = s.view(torch.float8_e4m3fn)
+        want = M.MOE_DEVERR_W4_SCALE
+    elif case == "x_beyond_f16":
+        x[3, 17] = 1e5
+        want = M.MOE_DEVERR_F16_RANGE
+    elif case == "h_beyond_f16":
+        # every W13 scale of every expert 8160: |g|, |u| in the thousands,
+        # so h = silu(g) u reaches far beyond 65504 while the weights expand
+        # exactly; x stays N(0, 1)
+        layer.w13_s = torch.full_like(layer.w13_s, 8160.0)
+        want = M.MOE_DEVERR_F16_RANGE
+    else:
+        s2 = layer.w2_s.clone()
+        s2[:, 0, 0] = 8160.0
+        layer.w2_s = s2
+        s = layer.w13_s.clone()
+        s[:, 1, 0] = -(2.0 ** -13)
+        layer.w13_s = s
+        q = layer.w13_q.clone()
+        q[:, :, 0] = (q[:, :, 0] & 0xF0) | 0x08      # k = 0: nibble 8, weight 0
+        layer.w13_q = q
+        x[0, 0] = 65280.0
+    mod = module_for(spec, layer)
+    o = mod.forward(x.cuda(), batch.logits.cuda())
+    torch.cuda.synchronize()
+    assert M.moe_read_device_error(o["err_word"]) == want
