@@ -51,7 +51,9 @@ typedef enum {
   MOE_ERR_LOCAL_RANGE = -4, /* missing/invalid local expert range */
   MOE_ERR_PARAM = -5,       /* non-finite or out-of-range scalar parameter */
   MOE_ERR_WORKSPACE = -6,   /* workspace NULL or too small */
-  MOE_ERR_HIP = -8          /* a HIP launch or runtime call failed */
+  MOE_ERR_HIP = -8,         /* a HIP launch or runtime call failed */
+  MOE_ERR_SCRATCH = -9      /* the call needs more than the static scratch of
+                               moe_forward_no_workspace holds */
 } moe_status;
 
 typedef enum {
@@ -336,6 +338,29 @@ int moe_forward(const moe_layer *layer, const void *x_bf16,
                 int *topk_ids, float *topk_w, float *sink_w, int *err_word,
                 void *ws, size_t ws_bytes, void *stream);
 size_t moe_workspace_size(const moe_layer *layer, long T_max);
+
+/* moe_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and the same kernels, with the workspace taken from
+ * a static device array of MOE_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on, from module load until the process ends. Arguments
+ * as for moe_forward without ws / ws_bytes; the caller still passes (and
+ * owns) every input and output. The device is the current one; its
+ * array's address is looked up on the first call there. A layer and T whose
+ * moe_workspace_size exceeds MOE_SCRATCH_BYTES return MOE_ERR_SCRATCH
+ * (moe_scratch_error() says how much was needed) and launch nothing; 32 MiB
+ * holds every layer here at T <= 64. Calls on one GPU share its array:
+ * calls that overlap on one GPU (two streams, two threads) race and must be
+ * ordered by the caller. Nothing in the array has to start at zero (each
+ * call writes every workspace byte before reading it). */
+#define MOE_SCRATCH_BYTES (32u << 20)
+int moe_forward_no_workspace(const moe_layer *layer, const void *x_bf16,
+                             const float *logits, long T, long ld_logits,
+                             float *out, int *topk_ids, float *topk_w,
+                             float *sink_w, int *err_word, void *stream);
+/* Message of the calling thread's last moe_forward_no_workspace refusal
+ * ("" if none). */
+const char *moe_scratch_error(void);
 
 /* --------------------------------------------------------------- misc -- */
 /* Synchronises `stream`, then copies *err_word (device) to *host_bits. */

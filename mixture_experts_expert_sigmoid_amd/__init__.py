@@ -29,7 +29,8 @@ MOE_DEVERR_F16_RANGE = 0x2
 MOE_DEVERR_W4_SCALE = 0x4
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE",
           -3: "MOE_ERR_FORMAT", -4: "MOE_ERR_LOCAL_RANGE", -5: "MOE_ERR_PARAM",
-          -6: "MOE_ERR_WORKSPACE", -8: "MOE_ERR_HIP"}
+          -6: "MOE_ERR_WORKSPACE", -8: "MOE_ERR_HIP", -9: "MOE_ERR_SCRATCH"}
+MOE_SCRATCH_BYTES = 32 << 20
 
 
 class MoeError(RuntimeError):
@@ -99,6 +100,10 @@ _SIGS = {
                             c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                             c_void_p, c_size_t, c_void_p]),
     "moe_workspace_size": (c_size_t, [POINTER(MoeLayer), c_long]),
+    "moe_forward_no_workspace": (c_int, [POINTER(MoeLayer), c_void_p, c_void_p, c_long,
+                                         c_long, c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_void_p, c_void_p]),
+    "moe_scratch_error": (ctypes.c_char_p, []),
     "moe_read_device_error": (c_int, [c_void_p, POINTER(c_int), c_void_p]),
     "moe_status_string": (ctypes.c_char_p, [c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
@@ -285,6 +290,19 @@ def moe_forward(layer: MoeLayer, x_bf16, logits, out, topk_ids, topk_w, sink_w,
                              _p(sink_w), _p(err_word), _p(ws),
                              ws.numel() * ws.element_size(), _stream(stream)),
            "moe_forward")
+
+
+def moe_forward_no_workspace(layer: MoeLayer, x_bf16, logits, out, topk_ids, topk_w,
+                             sink_w, err_word, stream=None):
+    """moe_forward with the library's static device scratch as workspace."""
+    T = x_bf16.shape[0]
+    L = lib()
+    st = L.moe_forward_no_workspace(ctypes.byref(layer), _p(x_bf16), _p(logits), T,
+                                    logits.stride(0), _p(out), _p(topk_ids), _p(topk_w),
+                                    _p(sink_w), _p(err_word), _stream(stream))
+    if st == -9:
+        raise MoeError(st, "moe_forward_no_workspace", L.moe_scratch_error().decode())
+    _check(st, "moe_forward_no_workspace")
 
 
 def moe_read_device_error(err_word, stream=None) -> int:

@@ -89,6 +89,7 @@ const char* moe_status_string(int s) {
     case MOE_ERR_PARAM: return "non-finite or out-of-range parameter";
     case MOE_ERR_WORKSPACE: return "workspace NULL or too small";
     case MOE_ERR_HIP: return "HIP launch or runtime failure";
+    case MOE_ERR_SCRATCH: return "the call needs more than the static scratch holds";
     default: return "unknown status";
   }
 }
