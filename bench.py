@@ -12,7 +12,7 @@ synthetic and resident in HBM before timing. A step is one moe_forward: route
 -> permute -> activation quant -> grouped GEMM1 + SwiGLU -> grouped GEMM2 +
 combine. Prints one JSON line. "value" is the back-to-back time of K steps
 at T = 4096 (10.9 GB of touched weights per step, far beyond the 256 MB
-MALL); the sweep and --configs also time every step alone after a 512 MB
+MALL); the sweep and "configs" also time every step alone after a 512 MB
 copy that evicts the MALL, and their rates use that median, so repeated
 small-T weights count as HBM traffic only when they come from HBM.
 "decode_graph" compares host-issued T = 1 steps with replays of the same
@@ -68,10 +68,9 @@ def parse():
     ap.add_argument("--profile-tokens", type=int, default=T_MAIN)
     ap.add_argument("--profile-config", default=WORKLOAD,
                     help="seeded configuration the --profile run uses")
-    ap.add_argument("--configs", action="store_true",
-                    help="also time moe_forward on every seeded configuration at its "
-                         "token counts and print a table to stderr (not part of the "
-                         "JSON line)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration array (every seeded layer at each "
+                         "of its token counts)")
     return ap.parse_args()
 
 
@@ -300,8 +299,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(spec, layer, r["batch"], T_MAIN)
 
-    if args.configs:
-        config_table(args, stream, flush)
+    configs = None if args.no_configs else config_table(args, stream, flush)
 
     main_ms = results[T_MAIN]["ms"]
     line = {
@@ -319,6 +317,7 @@ def main():
         "gate_route": gate_route_table(args.steps, stream) if not args.no_sweep else None,
         "decode_graph": (decode_graph(mod, results[1]["batch"], results[1]["outs"])
                          if 1 in results else None),
+        "configs": configs,
     }
     print(json.dumps(line))
 
@@ -409,27 +408,48 @@ def gate_route_table(steps, stream):
     return out
 
 
+def _weight_bytes(layer):
+    """Bytes of one group's W13 and W2 (codes + scales)."""
+    b13 = layer.w13_q[0].numel() * layer.w13_q.element_size()
+    b2 = layer.w2_q[0].numel() * layer.w2_q.element_size()
+    if layer.w13_s is not None:
+        b13 += layer.w13_s[0].numel() * layer.w13_s.element_size()
+        b2 += layer.w2_s[0].numel() * layer.w2_s.element_size()
+    return b13, b2
+
+
+def _peak_tflops(fmt):
+    return FP8_PEAK_TFLOPS if fmt == "fp8" else BF16_PEAK_TFLOPS
+
+
 def config_table(args, stream, flush):
-    """moe_forward time per seeded configuration and token count, with the
-    touched-weight GB/s and useful TFLOP/s (stderr): back to back, and the
-    median with the MALL flushed before every step (the rates use that)."""
+    """moe_forward on every seeded configuration at each of its token
+    counts: back to back and MALL-flushed (median), tokens/s, useful TFLOP/s
+    (6 P H I) against the format's MFMA peak (FP8 layers the FP8 peak, the
+    others bf16), touched-weight GB/s against 8 TB/s, the attainable-roofline
+    percentage, and the two GEMM entry points timed alone (MALL flushed)
+    with their algorithmic bytes: GEMM1 = touched W13 + x + h written,
+    GEMM2 + combine = touched W2 + h read + out written. Also printed as a
+    table on stderr."""
     import torch
     from synth import CONFIGS, EXT_CONFIGS, FP4_CONFIGS, make_batch, make_layer
-    from tests.gpu_helpers import module_for
+    from tests.gpu_helpers import StepCalls, module_for
     print("# config              T    ms/step  flushed-med  flushed-min    tokens/s"
-          "    TFLOP/s  weight GB/s", file=sys.stderr)
-    # the EP + LoRA layer also with a batch of eight rank-16 adapters
-    # (tokens pick one or none), the page's multi-adapter serving case
+          "    TFLOP/s  weight GB/s  gemm1 ms  gemm2+comb ms", file=sys.stderr)
+    # C5 with the down LoRA too, and with a batch of eight rank-16 adapters
+    # (tokens pick one or none), the page's multi-adapter serving case; the
+    # C5 layer in NVFP4 (the page's own weight format) and the INT4 layer's
+    # shape in MXFP4
     table = dict(CONFIGS)
     table.update(EXT_CONFIGS)
     table["ep_lora_258_x8"] = EXT_CONFIGS["ep_lora_258_down"].scaled(
         name="ep_lora_258_x8", cfg_id=15, n_adapters=8)
-    # the EP + LoRA layer in NVFP4 (the page's own weight format) and the
-    # INT4 layer's shape in MXFP4
     table.update(FP4_CONFIGS)
+    entries = []
     for name, spec in table.items():
         layer = make_layer(spec, device="cuda")
         mod = module_for(spec, layer)
+        b13, b2 = _weight_bytes(layer)
         for T in spec.Ts:
             batch = make_batch(spec, layer, T, device="cuda")
             mod.set_adapters(batch.adapter_ids)
@@ -459,20 +479,53 @@ def config_table(args, stream, flush):
             local = (e_loc >= 0) & (e_loc < spec.n_local)
             touched = len(set(e_loc[local].tolist())) + (spec.shared if T > 0 else 0)
             P = int(local.sum()) + (T if spec.shared else 0)
-            bytes_w = layer.w13_q[0].numel() * layer.w13_q.element_size() + \
-                layer.w2_q[0].numel() * layer.w2_q.element_size()
-            if layer.w13_s is not None:
-                bytes_w += layer.w13_s[0].numel() * layer.w13_s.element_size() + \
-                    layer.w2_s[0].numel() * layer.w2_s.element_size()
             fl = 6.0 * P * spec.H * spec.I
+            wbytes = touched * (b13 + b2)
+            peak = _peak_tflops(spec.fmt)
+            s_ = fmed * 1e-3
+            # the two GEMM entry points alone, MALL flushed before each call
+            st = StepCalls(spec, mod, batch.x, batch.logits, batch.adapter_ids)
+            st.run()
+            g1_med, _ = time_flushed(st.gemm1, args.steps, stream, flush)
+            g2_med, _ = time_flushed(st.gemm2, args.steps, stream, flush)
+            fp8 = spec.fmt == "fp8"
+            xb = T * spec.H * ((1 + 4 / 128) if fp8 else 2)
+            hb = P * spec.I * ((1 + 4 / 128) if fp8 else 2)
+            g1_bytes = touched * b13 + xb + hb
+            g2_bytes = touched * b2 + hb + T * spec.H * 4
+
+            def rate(ms_, byts, flops):
+                gbs = byts / (ms_ * 1e-3) / 1e9
+                tfl = flops / (ms_ * 1e-3) / 1e12
+                return {"ms": round(ms_, 4), "gbs": round(gbs, 1),
+                        "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                        "tflops": round(tfl, 2), "frac_mfma": round(tfl / peak, 4)}
+            ent = {"config": name, "T": T, "fmt": spec.fmt,
+                   "ms_per_step": round(ms, 4), "ms_flushed_median": round(fmed, 4),
+                   "ms_flushed_min": round(fmin, 4), "tokens_per_s": round(T / s_, 1),
+                   "tflops": round(fl / s_ / 1e12, 2),
+                   "pct_mfma_peak": round(100 * fl / s_ / 1e12 / peak, 2),
+                   "weight_gbs": round(wbytes / s_ / 1e9, 1),
+                   "pct_hbm_peak": round(100 * wbytes / s_ / 1e9 / HBM_PEAK_GBS, 2),
+                   "roofline_bound": ("hbm" if wbytes / (HBM_PEAK_GBS * 1e9) >=
+                                      fl / (peak * 1e12) else "mfma"),
+                   "pct_attainable": round(100 * max(wbytes / (HBM_PEAK_GBS * 1e9),
+                                                     fl / (peak * 1e12)) / s_, 2),
+                   "pairs": P, "experts_touched": touched,
+                   "gemm1": rate(g1_med, g1_bytes, 4.0 * P * spec.H * spec.I),
+                   "gemm2_combine": rate(g2_med, g2_bytes, 2.0 * P * spec.H * spec.I)}
+            entries.append(ent)
             print(f"# {name:18s} {T:5d} {ms:10.4f} {fmed:12.4f} {fmin:12.4f} "
                   f"{T / fmed * 1e3:11.1f} {fl / fmed / 1e9:10.2f} "
-                  f"{touched * bytes_w / fmed / 1e6:12.1f}", file=sys.stderr, flush=True)
+                  f"{wbytes / fmed / 1e6:12.1f} {g1_med:9.4f} {g2_med:14.4f}",
+                  file=sys.stderr, flush=True)
+            del st
         del layer, mod
         torch.cuda.empty_cache()
+    return entries
 
 
-def cpu_baseline(spec, layer, batch, T, n_experts=20):
+def cpu_baseline(spec, layer, batch, T, n_experts=80):
     """The fp64 oracle as it stands on the host cores, on a bounded sample:
     routing, permutation and activation quantisation of all T tokens plus
     the expert FFNs of the first `n_experts` routed experts (all their

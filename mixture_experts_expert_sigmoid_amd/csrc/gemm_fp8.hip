@@ -53,6 +53,15 @@ namespace moe {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// Activation blocks live in a ring of kF8Stages LDS stages: block i of a
+// tile is staged during block i - 2 and read in block i, and the workgroup
+// meets at a barrier after every second block. Between barriers the waves
+// drift apart (the two waves of a SIMD share its matrix core, and the one
+// with the lower issue priority falls behind); the ring keeps the stage a
+// fast wave writes two blocks ahead distinct from the two a slow wave may
+// still read.
+constexpr int kF8Stages = 4;
+
 // F8: the activation block stays e4m3 (128-byte rows) for the FP8 MFMA;
 // otherwise it is expanded to bf16 (256-byte rows)
 template <int BM, bool F8>
@@ -63,7 +72,7 @@ struct F8Geo {
   static constexpr int A_PT = (A_CH + kThreads - 1) / kThreads;
   static constexpr int X_BYTES = BM * 4;                   // row scales, [16][MS]
   static constexpr int STAGE = A_BYTES + X_BYTES;
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int LDS = kF8Stages * STAGE;
 };
 
 // bf16 A rows are 256 bytes = 16 chunks of 16; chunk c of row r is stored
@@ -244,6 +253,9 @@ __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, ui
 #pragma unroll
     for (int i = 0; i < Gm::A_PT; ++i) ra[i] = *(const i32x4*)(ap[i] + adv);
     if (tid < BM) rxs = xsp[sc];
+  };
+  auto gload_ws = [&](int s) {
+    const int sc = min(s, k1 - 1);
     wl_n = wsl[sc];
     wh_n = wsh[sc];
   };
@@ -336,7 +348,8 @@ __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, ui
     // block s's weight scales arrived with its activations; reading them
     // here would expose a global-load latency per block on small tiles
     const float wl = wl_n, wh = wh_n;
-    gload_a(s + 1);
+    gload_ws(s + 1);
+    gload_a(s + 2);
     gload_b(rb, s + 2);
     // this lane's activation scales for rows lr + 16 ms
     float xs[MS];
@@ -413,24 +426,31 @@ __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, ui
       __builtin_amdgcn_sched_barrier(0);
     }
     scale_into(MS - 1, pp[(MS - 1) & 1][0], pp[(MS - 1) & 1][1]);
-    store_a(buf ^ 1);
+    store_a((buf + 2) & (kF8Stages - 1));   // block s + 2
   };
 
   i32x4 rb0[4], rb1[4];
   gload_b(rb0, k0);
   gload_b(rb1, k0 + 1);
+  gload_ws(k0);
   gload_a(k0);
   store_a(0);
+  gload_a(k0 + 1);
+  store_a(1);
   __syncthreads();
+  // block i = s - k0 reads stage i % 4 (staged in block i - 2) and stages
+  // block i + 2 into stage (i + 2) % 4, which held block i - 2; both were
+  // completed by every wave before the barrier that closed the pair
+  // i - 2, i - 1 (or the prologue's)
   int s = k0;
   for (; s + 2 <= k1; s += 2) {
-    block(s, 0, rb0);
-    __syncthreads();
-    block(s + 1, 1, rb1);
+    const int i = s - k0;
+    block(s, i & 3, rb0);
+    block(s + 1, (i + 1) & 3, rb1);
     __syncthreads();
   }
   if (s < k1) {            // odd block count
-    block(s, 0, rb0);
+    block(s, (s - k0) & 3, rb0);
     __syncthreads();
   }
   if constexpr (PART) {

@@ -9,7 +9,11 @@ Bars:
   * gate logits: |kernel - exact| <= 2^-24 (H / 32 + 40) sum_h |x_h w_h|
     + 2^-24 |exact| (fp32 accumulation over H / 32 MFMA steps and up to 32
     split partials, each adding at most one rounding of the running sum);
-  * ids bit-exact on every row whose oracle ranking is robust (each slot's
+  * moe_route on given logits (with or without a selection bias): ids
+    bit-exact on every row -- the kernel's key is the same fp32 value as the
+    oracle's (sigmoid evaluated in fp64, rounded once, plus the bias);
+  * behind the router GEMM, whose logits carry its accumulation error: ids
+    bit-exact on every row whose oracle ranking is robust (each slot's
     winner beats every remaining candidate by more than twice the key
     uncertainty); rows with a near-tie below that gap must still hold a
     valid selection (each pick within the uncertainty of the best remaining
@@ -22,9 +26,9 @@ Bars:
   * packed: p >> 16 equals the ids bit for bit, p & 0xFFFF equals torch's
     bfloat16 rounding of the kernel's own fp32 weight, and lies within one
     bf16 step of the oracle's weight.
-Key uncertainty per column: without a bias the logit bound above; with a
-bias sigmoid'(x) times it plus 2^-21 for the fp32 sigmoid and the bias
-addition.
+Key uncertainty per column behind the GEMM: without a bias the logit bound
+above; with a bias sigmoid'(x) times it plus 2^-23 (one rounding of the key
+at its magnitude).
 """
 import numpy as np
 import pytest
@@ -156,7 +160,7 @@ def test_gate_route_parity(name, T, bias, std):
     else:
         keys = O.selection_keys(olg[:, :N], bnp).astype(np.float64)
         sg = O.sigmoid(exact[:, :N])
-        delta = sg * (1.0 - sg) * tol[:, :N] + 2.0 ** -21
+        delta = sg * (1.0 - sg) * tol[:, :N] + 2.0 ** -23
     gids = ids.cpu().numpy()
     exact_rows = _check_selection(gids, keys, delta, oids, N)
     _check_weights(gids, w.cpu().numpy(), sw.cpu().numpy() if S else np.zeros((T, 0)),
@@ -218,14 +222,17 @@ def test_gate_route_empty_and_no_workspace_for_large_T():
 
 # ---------------------------------------------- moe_route: bias and packed
 
-@pytest.mark.parametrize("name,T", [("ep_lora_258", 1), ("ep_lora_258", 37),
-                                    ("ep_lora_258", 8192), ("fp8_clamp_288", 4096),
-                                    ("int4_g32_64", 64)])
-def test_route_bias_and_packed(name, T):
-    _log("route bias", name, T)
+@pytest.mark.parametrize("name,T,lscale", [
+    ("ep_lora_258", 1, 1.0), ("ep_lora_258", 37, 1.0), ("ep_lora_258", 8192, 1.0),
+    ("fp8_clamp_288", 4096, 1.0), ("int4_g32_64", 64, 1.0),
+    # logits times 12 / 6: many keys in sigmoid's saturated and flushed
+    # ranges, where fp32 sigmoid ties distinct logits
+    ("ep_lora_258", 512, 12.0), ("fp8_clamp_288", 4096, 6.0)])
+def test_route_bias_and_packed(name, T, lscale):
+    _log("route bias", name, T, lscale)
     spec = CONFIGS[name]
     N, S, k = spec.n_routed, spec.n_sink, spec.top_k
-    lg = make_batch(spec, None, T).logits
+    lg = make_batch(spec, None, T).logits * lscale
     bias = make_gate(spec).bias
     ids = torch.empty(T, k, dtype=torch.int32, device="cuda")
     w = torch.empty(T, k, device="cuda")
@@ -235,9 +242,10 @@ def test_route_bias_and_packed(name, T):
                 packed=packed)
     torch.cuda.synchronize()
     oids, ow, osw = O.route(lg.numpy(), N, S, k, 2.6, 4.0, sel_bias=bias.numpy())
-    keys = O.selection_keys(lg.numpy()[:, :N], bias.numpy()).astype(np.float64)
-    delta = np.full((T, N), 2.0 ** -21)
     gids = ids.cpu().numpy()
-    exact_rows = _check_selection(gids, keys, delta, oids, N)
+    # the same fp32 keys on both sides: every row's ids bit for bit
+    nd = int(np.any(gids != oids, axis=1).sum())
+    print(f"  differing rows {nd} of {T}", flush=True)
+    assert np.array_equal(gids, oids)
     _check_weights(gids, w.cpu().numpy(), sw.cpu().numpy() if S else np.zeros((T, 0)),
-                   packed.cpu().numpy(), oids, ow, osw, 10.4, exact_rows, 2e-5)
+                   packed.cpu().numpy(), oids, ow, osw, 10.4, np.ones(T, bool), 2e-5)

@@ -15,7 +15,7 @@ import mixture_experts_expert_sigmoid_amd as M
 from oracle import moe_oracle as O
 from synth import (CONFIGS, FP4_CONFIGS, make_batch, make_layer, to_numpy_batch,
                    to_numpy_layer)
-from tests.gpu_helpers import compare, module_for, tolerance
+from tests.gpu_helpers import StepCalls, compare, module_for, tolerance
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="no GPU")]
@@ -267,61 +267,19 @@ def _ad(batch):
 def _stepwise(spec, mod, batch, T):
     """route -> permute -> quant -> gemm1 -> gemm2+combine through the
     individual C-ABI calls; returns every intermediate on the host."""
-    x, lg = batch.x.cuda(), batch.logits.cuda()
-    mod.set_adapters(_ad(batch))
-    k, N, S, H, I = spec.top_k, spec.n_routed, spec.n_sink, spec.H, spec.I
-    G = spec.n_groups
-    fp8 = spec.fmt == "fp8"
-    dev32 = dict(device="cuda", dtype=torch.int32)
-    ids = torch.empty(T, k, **dev32)
-    w = torch.empty(T, k, device="cuda")
-    sw = torch.empty(T, S, device="cuda") if S else None
-    M.moe_route(lg, N, S, k, spec.route_scale, spec.global_scale, ids, w, sw)
-    pc = T * k + (T if spec.shared else 0)
-    offsets = torch.empty(G + 1, **dev32)
-    sp = torch.empty(pc, **dev32)
-    pr = torch.empty(pc, **dev32)
-    err = torch.zeros(1, **dev32)
-    ws = torch.empty(M.moe_permute_workspace_size(T, k, G), dtype=torch.uint8, device="cuda")
-    M.moe_permute(ids, k, N, spec.offset, spec.n_local, spec.shared, offsets, sp, pr,
-                  err, ws)
-    if fp8:
-        xin = torch.empty(T, H, dtype=torch.uint8, device="cuda")
-        xs = torch.empty(T, H // 128, device="cuda")
-        M.moe_quantize_act_fp8(x, xin, xs)
-        h = torch.empty(pc, I, dtype=torch.uint8, device="cuda")
-        hs = torch.empty(pc, I // 128, device="cuda")
-    else:
-        xin, xs = x, None
-        h = torch.zeros(pc, I, dtype=torch.bfloat16, device="cuda")   # rows of other ranks stay 0
-        hs = None
-    ws1 = torch.empty(max(M.moe_gemm1_workspace_size(mod.w13, pc, mod.lora), 1),
-                      dtype=torch.uint8, device="cuda")
-    # the down-LoRA input: FP8 layers write it beside the codes, the others
-    # read h itself
-    h_lora = None
-    if mod.lora_down is not None:
-        h_lora = torch.zeros(pc, I, dtype=torch.bfloat16, device="cuda") if fp8 else h
-    M.moe_grouped_gemm1_act(mod.w13, xin, xs, x, T, H, I, k, pc, offsets, sp, mod.act,
-                            mod.lora, h, hs, ws1, h_lora=h_lora if fp8 else None,
-                            err_word=err)
-    out = torch.empty(T, H, device="cuda")
-    ws2 = torch.empty(M.moe_gemm2_workspace_size(mod.w2, pc, mod.lora_down),
-                      dtype=torch.uint8, device="cuda")
-    M.moe_grouped_gemm2_combine(mod.w2, h, hs, T, H, I, k, spec.shared, pc, offsets, pr,
-                                w, spec.shared_w, out, ws2, h_lora=h_lora,
-                                lora_down=mod.lora_down, sorted_pair=sp, err_word=err)
+    st = StepCalls(spec, mod, batch.x.cuda(), batch.logits.cuda(), _ad(batch))
+    st.run()
     torch.cuda.synchronize()
-    assert M.moe_read_device_error(err) == 0
-    if fp8:
-        hval = O.e4m3_decode(h.cpu().numpy()) * np.repeat(
-            hs.cpu().numpy().astype(np.float64), 128, axis=1)
+    assert M.moe_read_device_error(st.err) == 0
+    if st.fp8:
+        hval = O.e4m3_decode(st.h.cpu().numpy()) * np.repeat(
+            st.hs.cpu().numpy().astype(np.float64), 128, axis=1)
     else:
-        hval = h.float().cpu().numpy().astype(np.float64)
-    return dict(out=out, offsets=offsets.cpu().numpy(), sp=sp.cpu().numpy(),
-                hval=hval, hs=None if hs is None else hs.cpu().numpy(),
-                h_lora=None if h_lora is None or not fp8
-                else h_lora.float().cpu().numpy().astype(np.float64))
+        hval = st.h.float().cpu().numpy().astype(np.float64)
+    return dict(out=st.out, offsets=st.offsets.cpu().numpy(), sp=st.sp.cpu().numpy(),
+                hval=hval, hs=None if st.hs is None else st.hs.cpu().numpy(),
+                h_lora=None if st.h_lora is None or not st.fp8
+                else st.h_lora.float().cpu().numpy().astype(np.float64))
 
 
 @pytest.mark.parametrize("name", ["tiny_bf16", "fp8_clamp_small", "fp8_oai_small",
