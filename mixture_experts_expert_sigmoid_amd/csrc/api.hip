@@ -219,7 +219,8 @@ int* zad_of(float* z, long p_cap, const moe_lora* lora) {
   return batched(lora) ? (int*)((char*)z + al((size_t)p_cap * lora->rank * 4)) : nullptr;
 }
 size_t g1_part_bytes(const moe_weights* w13, long p_cap) {
-  if (!moe::splitk_use(w13->fmt, p_cap, w13->n_groups, w13->N / 256, w13->K / 128)) return 0;
+  if (!moe::splitk_use(w13->fmt, p_cap, w13->n_groups, w13->N / 256, w13->K / 128, true))
+    return 0;
   return moe::splitk_bytes(p_cap, w13->N);
 }
 size_t g1_x16_bytes(const moe_weights* w13, long rows) {
@@ -227,7 +228,7 @@ size_t g1_x16_bytes(const moe_weights* w13, long rows) {
 }
 // GEMM2 workspace: fp32 y rows, or (split-K) their partial sums
 size_t g2_bytes(const moe_weights* w2, long p_cap) {
-  if (moe::splitk_use(w2->fmt, p_cap, w2->n_groups, (w2->N + 255) / 256, w2->K / 128))
+  if (moe::splitk_use(w2->fmt, p_cap, w2->n_groups, (w2->N + 255) / 256, w2->K / 128, false))
     return moe::splitk_bytes(p_cap, w2->N);
   return al((size_t)p_cap * w2->N * 4);
 }
@@ -397,8 +398,9 @@ int moe_grouped_gemm2_combine(const moe_weights* w2, const void* h,
   a.p_cap = p_cap;
   a.offsets = offsets;
   a.y = y;
-  int sk_grid = 0;
+  int sk_grid = 0, sk_mode = 0;
   a.sk_grid = &sk_grid;
+  a.sk_mode = &sk_mode;
   if (lora_down) {
     a.z = z2;
     a.lora_B = lora_down->B;
@@ -412,7 +414,7 @@ int moe_grouped_gemm2_combine(const moe_weights* w2, const void* h,
   e = moe::launch_gemm2(a, s);
   if (e == hipSuccess)
     e = moe::launch_combine(y, T, H, top_k, shared_expert, pair_row, topk_w,
-                            shared_w, out, s, sk_grid, p_cap, I, a.G, offsets);
+                            shared_w, out, s, sk_grid, p_cap, I, a.G, offsets, sk_mode);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_grouped_gemm2_combine");
 }
 
@@ -598,8 +600,9 @@ int moe_forward(const moe_layer* L, const void* x_bf16, const float* logits,
   a.p_cap = pc;
   a.offsets = offsets;
   a.y = y;
-  int sk_grid = 0;
+  int sk_grid = 0, sk_mode = 0;
   a.sk_grid = &sk_grid;
+  a.sk_mode = &sk_mode;
   if (L->lora_down) {
     a.z = z2;
     a.lora_B = L->lora_down->B;
@@ -613,7 +616,7 @@ int moe_forward(const moe_layer* L, const void* x_bf16, const float* logits,
   e = moe::launch_gemm2(a, s);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/gemm2");
   e = moe::launch_combine(y, T, L->H, L->top_k, L->shared_expert, pair_row,
-                          topk_w, L->shared_w, out, s, sk_grid, pc, L->I, G, offsets);
+                          topk_w, L->shared_w, out, s, sk_grid, pc, L->I, G, offsets, sk_mode);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/combine");
   return MOE_OK;
 }

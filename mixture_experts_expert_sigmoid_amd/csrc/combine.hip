@@ -49,7 +49,7 @@ __global__ __launch_bounds__(512) void combine_sk_kernel(
     const float* __restrict__ part, long T, int H, int top_k, int shared,
     const int* __restrict__ pair_row, const float* __restrict__ topk_w,
     float shared_w, float* __restrict__ out, int grid, long p_rows, int I, int G,
-    const int* __restrict__ offsets) {
+    const int* __restrict__ offsets, int mode) {
   __shared__ int s_cum[kMaxGroups + 1];
   __shared__ int s_off[kMaxGroups + 1];
   __shared__ int s_wsum[8];
@@ -60,6 +60,9 @@ __global__ __launch_bounds__(512) void combine_sk_kernel(
   for (int i = threadIdx.x; i <= G; i += 512) s_off[i] = offsets[i];
   const long U = (long)s_cum[G] * NT * NS;
   const int W = sk_workgroups((long)s_cum[G] * NT, NS, grid);
+  // SK_DEVICE: the GEMM kernels chose split-K or plain rows by the same rule
+  // on the same tile count; plain rows are slot 0 of the partial layout
+  const bool split = mode != SK_DEVICE || sk_rule((long)s_cum[G] * NT, NS);
   const int chunks = (H + kCsCols - 1) / kCsCols;
   const long t = blockIdx.x / chunks;
   const int col0 = (int)(blockIdx.x - t * chunks) * kCsCols;
@@ -85,7 +88,7 @@ __global__ __launch_bounds__(512) void combine_sk_kernel(
   for (int j = 0; j < np; ++j) {               // ascending slot, shared last
     const int r = s_row[j];
     if (r < 0) continue;
-    const int nsl = sk_nslots(((long)s_mt[j] * NT + nt) * NS, NS, U, W);
+    const int nsl = split ? sk_nslots(((long)s_mt[j] * NT + nt) * NS, NS, U, W) : 1;
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
     for (int sl = 0; sl < nsl; ++sl) {
       const f32x4 p = *(const f32x4*)(part + ((long)sl * p_rows + r) * H + col);
@@ -102,14 +105,14 @@ __global__ __launch_bounds__(512) void combine_sk_kernel(
 hipError_t launch_combine(const float* y, long T, int H, int top_k, int shared,
                           const int* pair_row, const float* topk_w,
                           float shared_w, float* out, hipStream_t s, int sk_grid,
-                          long p_cap, int I, int G, const int* offsets) {
+                          long p_cap, int I, int G, const int* offsets, int sk_mode) {
   long n = T * (long)(H / 4);
   if (n == 0) return hipSuccess;
   if (sk_grid > 0) {
     const long nwg = T * ((H + kCsCols - 1) / kCsCols);
     hipLaunchKernelGGL(combine_sk_kernel, dim3((unsigned)nwg), dim3(512), 0, s, y, T, H,
                        top_k, shared, pair_row, topk_w, shared_w, out, sk_grid, p_cap,
-                       I, G, offsets);
+                       I, G, offsets, sk_mode);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)),

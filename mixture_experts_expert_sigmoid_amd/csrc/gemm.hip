@@ -302,7 +302,13 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t s) {
       return fp8 ? launch_gemm_fp8(P, true, a.p_cap, a.I / 128, s, grid)
                  : launch_gemm_w4(a.fmt, P, true, a.p_cap, a.I / 128, s, grid);
     };
-    if (!a.part) return run(nullptr);
+    const int mode = a.part ? splitk_mode(a.fmt, a.p_cap, a.G, a.I / 128, a.H / 128, true)
+                            : SK_PLAIN;
+    P.sk_mode = mode;
+    if (mode != SK_SPLIT) {        // the plain kernel (it returns at once if an
+      e = run(nullptr);            // SK_DEVICE launch picks split-K)
+      if (e != hipSuccess || mode == SK_PLAIN) return e;
+    }
     P.part = a.part;
     P.p_rows = a.p_cap;
     int grid = 0;
@@ -336,27 +342,33 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t s) {
   P.err = a.err;
   long hint = a.G > 0 ? a.p_cap / a.G : a.p_cap;
   *a.sk_grid = 0;
+  *a.sk_mode = SK_PLAIN;
   const int NT = (a.H + 255) / 256;
   if (a.fmt != FMT_BF16) {
     const bool fp8 = a.fmt == FMT_FP8;
-    int* grid = nullptr;
-    if (splitk_use(a.fmt, a.p_cap, a.G, NT, a.I / 128)) {
-      P.part = a.y;                // the partial-sum slots
-      P.p_rows = a.p_cap;
-      grid = a.sk_grid;
+    auto run = [&](int* grid) {
+      return fp8 ? launch_gemm_fp8(P, false, a.p_cap, NT, s, grid)
+                 : launch_gemm_w4(a.fmt, P, false, a.p_cap, NT, s, grid);
+    };
+    const int mode = splitk_mode(a.fmt, a.p_cap, a.G, NT, a.I / 128, false);
+    P.sk_mode = mode;
+    *a.sk_mode = mode;
+    if (mode != SK_SPLIT) {
+      hipError_t e = run(nullptr);
+      if (e != hipSuccess || mode == SK_PLAIN) return e;
     }
-    return fp8 ? launch_gemm_fp8(P, false, a.p_cap, NT, s, grid)
-               : launch_gemm_w4(a.fmt, P, false, a.p_cap, NT, s, grid);
+    P.part = a.y;                  // the partial-sum slots (slot 0 = plain rows)
+    P.p_rows = a.p_cap;
+    return run(a.sk_grid);
   }
   return dispatch<false>(P, a.p_cap, NT, hint, s);
 }
 
-bool splitk_use(int fmt, long p_cap, int G, int NT, int NS) {
-  if (fmt == FMT_BF16 || p_cap <= 0) return false;
+int splitk_mode(int fmt, long p_cap, int G, int NT, int NS, bool g1) {
+  if (fmt == FMT_BF16 || p_cap <= 0) return SK_PLAIN;
   const long tiles = std::min<long>(p_cap, G + p_cap / kSkBM) * NT;
-  if (tiles > kSkMaxTiles) return false;
-  const long waves = (tiles + kSkCUs - 1) / kSkCUs;
-  return (waves * kSkCUs - tiles) * NS >= 8 * kSkCUs;
+  if (sk_rule(tiles, NS)) return SK_SPLIT;
+  return g1 && tiles <= kSkDeviceMaxTiles && p_cap <= 16L * G ? SK_DEVICE : SK_PLAIN;
 }
 
 }  // namespace moe

@@ -68,6 +68,7 @@ struct GemmParams {
   long p_rows;
   int lds_bytes;             // the launch's dynamic LDS (the LoRA epilogue's room)
   int* err;                  // nullable: 4-bit range problems (MOE_DEVERR_BIT_*)
+  int sk_mode;               // SK_DEVICE: decide plain / split-K on the device
 };
 
 // Dynamic LDS of the FP8 / 4-bit instantiations with LoRA code: room for a
@@ -130,6 +131,31 @@ struct Tile {
 // timing. Producer and consumers evaluate this from the same (tiles, NS,
 // grid).
 // ---------------------------------------------------------------------------
+// the split-K rule on a tile count (tiles of kSkBM rows times NT): the
+// host applies it to its shape-only bound, the kernels of an SK_DEVICE
+// launch to the real count
+__host__ __device__ inline bool sk_rule(long tiles, int NS) {
+  if (tiles <= 0 || tiles > kSkMaxTiles) return false;
+  const long waves = (tiles + kSkCUs - 1) / kSkCUs;
+  return (waves * kSkCUs - tiles) * NS >= 8 * kSkCUs;
+}
+
+// sum over the G groups of ceil(rows / kSkBM), for the whole workgroup
+// (blockDim.x threads, a multiple of 64; s_red holds 16 ints)
+__device__ __forceinline__ long tiles32(const int* offsets, int G, int* s_red) {
+  int v = 0;
+  for (int g = threadIdx.x; g < G; g += blockDim.x)
+    v += (offsets[g + 1] - offsets[g] + kSkBM - 1) / kSkBM;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  long tot = 0;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) tot += s_red[i];
+  __syncthreads();
+  return tot;
+}
+
 __device__ __forceinline__ int sk_workgroups(long tiles, int NS, int grid) {
   if (tiles <= grid && tiles * 5 >= 4L * grid) return (int)tiles;
   const int lmin = (NS + kSkSlots - 2) / (kSkSlots - 1);

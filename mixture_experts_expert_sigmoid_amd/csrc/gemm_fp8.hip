@@ -520,6 +520,11 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // 2 stages
   __shared__ int s_cum[kMaxGroups + 1];
   __shared__ int s_wsum[8];
+  // SK_DEVICE launch: return if the split-K kernel takes this GEMM
+  if (P.sk_mode == SK_DEVICE &&
+      sk_rule(tiles32(P.offsets, P.G, s_cum) * (G1 ? (P.I >> 7) : ((P.N + 255) >> 8)),
+              P.K >> 7))
+    return;
   tile_prefix<TBM>(P.offsets, P.G, s_cum, s_wsum);
   plain_tiles<TBM, G1, LORA>(P, smem, s_cum);
 }
@@ -536,6 +541,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_sk_kernel(GemmParams P)
   const int NT = G1 ? (P.I >> 7) : ((P.N + 255) >> 8);
   const int NS = P.K >> 7;
   tile_prefix<kSkBM>(P.offsets, G, s_cum, s_wsum);
+  if (P.sk_mode == SK_DEVICE && !sk_rule((long)s_cum[G] * NT, NS)) return;
   const long U = (long)s_cum[G] * NT * NS;
   const int W = sk_workgroups((long)s_cum[G] * NT, NS, gridDim.x);
   const int b = blockIdx.x;

@@ -57,6 +57,10 @@
 
 namespace moe {
 
+// Activation blocks in a ring of four LDS stages, staged two blocks ahead,
+// with a barrier after every second block (as in the FP8 kernel)
+constexpr int kW4Stages = 4;
+
 template <int BM>
 struct I4Geo {
   static constexpr int MS = BM / 16;              // 16-row subtiles
@@ -64,7 +68,7 @@ struct I4Geo {
   static constexpr int A_CH = BM * 16;            // 16-byte chunks
   static constexpr int A_PT = (A_CH + kThreads - 1) / kThreads;
   static constexpr int STAGE = A_BYTES;
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int LDS = kW4Stages * STAGE;
 };
 
 // f16 A rows are 256 bytes; chunk c of row r is stored at c ^ (r & 0b1011),
@@ -322,7 +326,7 @@ __device__ __forceinline__ void w4_tile(const GemmParams& P, const Tile& tl, uin
     f16x2 s2[2], s16[2], s2n[2], s16n[2];
     scale_regs(rc, s2, s16);
     scale_regs(rn, s2n, s16n);
-    gload_a(s + 1);
+    gload_a(s + 2);
     const uint8_t* sa = smem + buf * Gm::STAGE;
     // A fragment of step t = (half h, subtile ms): chunks 4 lg + 2 h, + 1
     auto lds_h = [&](int t, f16x8 (&af)[2]) {
@@ -369,7 +373,7 @@ __device__ __forceinline__ void w4_tile(const GemmParams& P, const Tile& tl, uin
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    store_a(buf ^ 1);
+    store_a((buf + 2) & (kW4Stages - 1));   // block s + 2
   };
 
   WB rb0, rb1;
@@ -377,6 +381,8 @@ __device__ __forceinline__ void w4_tile(const GemmParams& P, const Tile& tl, uin
   gload_b(rb1, k0 + 1);
   gload_a(k0);
   store_a(0);
+  gload_a(k0 + 1);
+  store_a(1);
   {                                      // first half of block k0
     f16x2 s2[2], s16[2];
     scale_regs(rb0, s2, s16);
@@ -387,15 +393,18 @@ __device__ __forceinline__ void w4_tile(const GemmParams& P, const Tile& tl, uin
         bwA[ns][jj] = F::expand((uint32_t)rb0.q[ns][jj], s2[ns], s16[ns], false);
   }
   __syncthreads();
+  // block i = s - k0 reads stage i % 4 (staged in block i - 2) and stages
+  // block i + 2 into the stage of block i - 2; the barrier after each pair
+  // orders both (see the FP8 kernel)
   int s = k0;
   for (; s + 2 <= k1; s += 2) {
-    block(s, 0, rb0, rb1);
-    __syncthreads();
-    block(s + 1, 1, rb1, rb0);
+    const int i = s - k0;
+    block(s, i & 3, rb0, rb1);
+    block(s + 1, (i + 1) & 3, rb1, rb0);
     __syncthreads();
   }
   if (s < k1) {
-    block(s, 0, rb0, rb1);
+    block(s, (s - k0) & 3, rb0, rb1);
     __syncthreads();
   }
   if ((bad_s | bad_h) && P.err && lane == 0)
@@ -470,6 +479,11 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_w4_kernel(GemmParams P) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_cum[kMaxGroups + 1];
   __shared__ int s_wsum[8];
+  // SK_DEVICE launch: return if the split-K kernel takes this GEMM
+  if (P.sk_mode == SK_DEVICE &&
+      sk_rule(tiles32(P.offsets, P.G, s_cum) * (G1 ? (P.I >> 7) : ((P.N + 255) >> 8)),
+              P.K >> 7))
+    return;
   tile_prefix<TBM>(P.offsets, P.G, s_cum, s_wsum);
   w4_plain_tiles<WF, TBM, G1, LORA>(P, smem, s_cum);
 }
@@ -484,6 +498,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_w4_sk_kernel(GemmParams P) 
   const int NT = G1 ? (P.I >> 7) : ((P.N + 255) >> 8);
   const int NS = P.K >> 7;
   tile_prefix<kSkBM>(P.offsets, G, s_cum, s_wsum);
+  if (P.sk_mode == SK_DEVICE && !sk_rule((long)s_cum[G] * NT, NS)) return;
   const long U = (long)s_cum[G] * NT * NS;
   const int W = sk_workgroups((long)s_cum[G] * NT, NS, gridDim.x);
   const int b = blockIdx.x;

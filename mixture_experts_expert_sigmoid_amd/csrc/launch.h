@@ -94,11 +94,25 @@ hipError_t launch_lora_z(const void* x_bf16, const void* A, int rank, long T,
 // workgroup, in waves over an MI355X's kSkCUs CUs, would leave idle slots
 // worth at least 8 K blocks per CU. A shape-only rule, so workspace sizes
 // need no device; the partial sums need kSkSlots * p_cap * N fp32.
+// For GEMM1, when that bound is too loose to decide because few rows per
+// expert are possible (p_cap <= 16 G: skewed routing can leave far fewer
+// tiles than the bound), the plain and the split-K kernels are both
+// launched and each applies the same rule to the real tile count it reads
+// from the expert offsets, returning at once when the other one is chosen
+// (SK_DEVICE); the reduction kernel decides the same way. Each unused
+// launch costs a few microseconds, so GEMM2 (shorter K, smaller gains)
+// keeps the shape-only rule.
 constexpr long kSkMaxTiles = 1024;
 constexpr long kSkCUs = 256;
 constexpr int kSkSlots = 4;          // partial-sum slots per tile
 constexpr int kSkBM = 32;            // tile rows under the split-K kernels
-bool splitk_use(int fmt, long p_cap, int G, int NT, int NS);
+constexpr long kSkDeviceMaxTiles = 2048;   // bound on tiles for SK_DEVICE
+enum { SK_PLAIN = 0, SK_SPLIT = 1, SK_DEVICE = 2 };
+// g1: GEMM1 (SK_DEVICE allowed)
+int splitk_mode(int fmt, long p_cap, int G, int NT, int NS, bool g1);
+inline bool splitk_use(int fmt, long p_cap, int G, int NT, int NS, bool g1) {
+  return splitk_mode(fmt, p_cap, G, NT, NS, g1) != SK_PLAIN;
+}
 // bytes of a split-K workspace (the partial-sum slots)
 inline size_t splitk_bytes(long p_cap, int N) {
   return ((size_t)kSkSlots * p_cap * N * 4 + 255) & ~(size_t)255;
@@ -145,6 +159,7 @@ struct Gemm2Args {
   const int* offsets;
   float* y;              // [p_cap][H] fp32, or the split-K partials
   int* sk_grid;          // out: split-K kernel grid (0 = plain kernel)
+  int* sk_mode;          // out: SK_PLAIN, SK_SPLIT or SK_DEVICE
   // down-projection LoRA (nullable z): y += scale * z[row] . B[a][g][n]
   const float* z;        // [p_cap][rank]
   const void* lora_B;    // bf16 [n_adapters][G_lora][H][rank]
@@ -157,11 +172,13 @@ struct Gemm2Args {
 hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t s);
 
 // sk_grid > 0: y holds the partial sums of the FP8 / 4-bit GEMM2's split-K
-// kernel over G groups, reduced here per element in slot order
+// kernel over G groups, reduced here per element in slot order (sk_mode
+// SK_SPLIT), or -- SK_DEVICE -- either those or plain rows, as the device
+// rule decides on the real tile count
 hipError_t launch_combine(const float* y, long T, int H, int top_k, int shared,
                           const int* pair_row, const float* topk_w,
                           float shared_w, float* out, hipStream_t s,
                           int sk_grid = 0, long p_cap = 0, int I = 0, int G = 0,
-                          const int* offsets = nullptr);
+                          const int* offsets = nullptr, int sk_mode = 0);
 
 }  // namespace moe

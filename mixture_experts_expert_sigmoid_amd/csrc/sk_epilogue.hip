@@ -25,6 +25,8 @@ __global__ __launch_bounds__(kThreads) void gemm1_sk_epilogue_kernel(GemmParams 
   tile_prefix<kSkBM>(P.offsets, G, s_cum, s_wsum);
   for (int i = threadIdx.x; i <= G; i += kThreads) s_off[i] = P.offsets[i];
   __syncthreads();
+  // SK_DEVICE: the plain kernel ran the fused epilogue instead
+  if (P.sk_mode == SK_DEVICE && !sk_rule((long)s_cum[G] * NT, NS)) return;
   const long U = (long)s_cum[G] * NT * NS;
   const int W = sk_workgroups((long)s_cum[G] * NT, NS, grid);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
