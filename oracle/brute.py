@@ -8,6 +8,9 @@ handling:
     and rounding to e4m3 is a nearest-value search over that table (ties to
     the even code, saturation at 448);
   * bfloat16 rounding is Python's round-half-even on the scaled value;
+  * MXFP8 activations (the W4A8 MXFP4 layers) scan for the smallest power
+    of two that keeps a 32-column group within 448 and round each element
+    by that same table search;
   * routing sorts the routed columns by (-logit, index) and forms the
     weights as sigmoid(x_i) / sum_j sigmoid(x_j) (the plain form the
     log-sigmoid renormalisation is algebraically equal to, sglang PR #36385,
@@ -54,6 +57,25 @@ def e4m3_nearest(v):
     return math.copysign(best[2], v)
 
 
+def mxfp8_exponent(amax):
+    """The smallest e >= -127 with amax <= 448 * 2^e, by scanning upwards."""
+    e = -127
+    while amax > 448.0 * 2.0 ** e:
+        e += 1
+    return e
+
+
+def mxfp8_row(row):
+    """MXFP8 values of one activation row: per 32 columns the exponent above
+    and the nearest e4m3 value of each element divided by 2^e, times 2^e."""
+    out = []
+    for c0 in range(0, len(row), 32):
+        grp = row[c0:c0 + 32]
+        e = mxfp8_exponent(max(abs(v) for v in grp))
+        out.extend(e4m3_nearest(v / 2.0 ** e) * 2.0 ** e for v in grp)
+    return out
+
+
 def bf16_nearest(v):
     if v == 0:
         return 0.0
@@ -93,7 +115,7 @@ def dense_weight(fmt, q, s, N, K, gsc=None):
                 byte = int(q[n][kk // 2])
                 nib = byte & 0xF if kk % 2 == 0 else byte >> 4
                 v = (nib - 8) * bf16_bits_value(int(s[n][kk // 32]))
-            else:                      # nvfp4 | mxfp4: e2m1 from its value list
+            else:                      # nvfp4 | mxfp4(_a8): e2m1 from its value list
                 byte = int(q[n][kk // 2])
                 nib = byte & 0xF if kk % 2 == 0 else byte >> 4
                 v = _E2M1[nib & 7] * (-1.0 if nib & 8 else 1.0)
@@ -117,7 +139,9 @@ def layer(spec, arr, x_bits, logits, adapter_ids=None):
     x = [[bf16_bits_value(int(b)) for b in row] for row in x_bits]
     xin = []
     for t in range(T):
-        if spec.fmt == "fp8":
+        if spec.fmt == "mxfp4_a8":
+            xin.append(mxfp8_row(x[t]))
+        elif spec.fmt == "fp8":
             row = []
             for c0 in range(0, H, 128):
                 grp = [float(torch.tensor(v, dtype=torch.float32)) for v in x[t][c0:c0 + 128]]

@@ -39,6 +39,12 @@ title and section):
                 1b699bf"): e2m1 codes times an e4m3 scale per 16 K times
                 the fp32 global scale (W13: gate, up; W2: one per expert);
                 MXFP4: e2m1 codes times a power-of-two e8m0 scale per 32 K.
+  quant_mx   -- the W4A8 variant of the MXFP4 layers: activations enter
+                GEMM1 as MXFP8 (e4m3 codes with a power-of-two e8m0 scale
+                per 32 columns, the smallest that keeps the group's amax
+                within 448), the form the block-scaled matrix instructions
+                take; a design choice of this library (the pages fix no
+                activation format for 4-bit weights), h stays bf16.
                 The pages name these formats without defining them; the
                 element and scale encodings are the public ones, written
                 here from their bit fields.
@@ -312,6 +318,27 @@ def quant_act_fp8(x_f32, group=128):
     return q, s
 
 
+def quant_act_mxfp8(x_f32, group=32):
+    """MXFP8 activations (the GEMM1 input of the MXFP4 W4A8 layers): per row
+    and 32 columns, amax = max |x| (fp32), e = the smallest integer with
+    amax <= 448 * 2^e, held as the e8m0 code e + 127 (e is raised to -127
+    when smaller, e.g. for an all-zero group), and codes = e4m3 RNE of the
+    exact quotient x / 2^e (never above 448, so never saturated). Returns
+    (codes uint8 [T, H], e8m0 codes uint8 [T, H/32])."""
+    x = np.asarray(x_f32, dtype=np.float32).astype(np.float64)
+    T, H = x.shape
+    xg = x.reshape(T, H // group, group)
+    amax = np.abs(xg).max(axis=2) if T else np.zeros((0, H // group))
+    # candidate from the logarithm, then corrected against the exact bound
+    e = np.ceil(np.log2(np.where(amax > 0, amax, 1.0) / E4M3_MAX)).astype(np.int64)
+    for _ in range(2):
+        e = np.where(amax > E4M3_MAX * np.ldexp(1.0, e.astype(np.int32)), e + 1, e)
+        e = np.where(amax <= E4M3_MAX * np.ldexp(1.0, (e - 1).astype(np.int32)), e - 1, e)
+    e = np.where(amax > 0, np.maximum(e, -127), -127)
+    q = e4m3_round(xg / np.ldexp(1.0, e.astype(np.int32))[:, :, None]).reshape(T, H)
+    return q, (e + 127).astype(np.uint8)
+
+
 def requant_fp8(h, group=128):
     """The FP8 path's intermediate rounding of h [P, I] (float64): per row and
     128-column group, amax taken to fp32, s = fp32(amax / 448) (1 if zero),
@@ -402,7 +429,7 @@ def dequant(fmt, q, s):
         return dequant_int4_g32(q, s)
     if fmt == "nvfp4":
         return dequant_nvfp4(q, s)
-    if fmt == "mxfp4":
+    if fmt in ("mxfp4", "mxfp4_a8"):
         return dequant_mxfp4(q, s)
     raise ValueError(fmt)
 
@@ -519,6 +546,16 @@ def down_lora_delta(spec, arr, e, h_lora_rows, adapters=None):
 # not change the oracle's own value):
 ACC_REL = 2e-6     # |fp32 sum - exact| <= ACC_REL * sum |terms| (g, u, delta)
 EVAL_REL = 2e-6    # relative error of the fp32 SwiGLU evaluation and of s
+# GEMM1 of the MXFP4 W4A8 layers runs on a block-scaled matrix instruction
+# whose 128-deep sums are not fp32-accurate: a kernel reaches g and u only
+# to within ACC_REL_MX * sum |terms| (measured on gfx950: at most 2.0e-5 of
+# the block's sum of |products|, 2e-6 over 16 chained blocks)
+ACC_REL_MX = 3e-5
+
+
+def acc_rel(fmt):
+    """The kernel-side accumulation bound of a layer format."""
+    return ACC_REL_MX if fmt == "mxfp4_a8" else ACC_REL
 
 
 def swiglu_slopes(g, u, alpha=1.0, beta=0.0, limit=math.inf):
@@ -611,7 +648,7 @@ def expert_ffn(spec, arr, e, xhat_rows, x_bf16_rows, detail=False, adapters=None
         if mm is not None:
             mag = mag + mm
     dg, du = swiglu_slopes(g, u, al, be, L)
-    err_h = ACC_REL * (dg * mag[:, :I] + du * mag[:, I:]) + EVAL_REL * np.abs(h)
+    err_h = acc_rel(spec.fmt) * (dg * mag[:, :I] + du * mag[:, I:]) + EVAL_REL * np.abs(h)
     alt = rounding_alternatives(h, err_h, spec.fmt)
     y_allow = alt @ np.abs(w2).T
     alt_l = None
@@ -631,11 +668,15 @@ def expert_ffn(spec, arr, e, xhat_rows, x_bf16_rows, detail=False, adapters=None
 
 def gemm1_input(spec, x_bits):
     """Values that enter GEMM1: the bf16 x, or for FP8 layers the dequantised
-    per-token per-128-column e4m3 codes."""
+    per-token per-128-column e4m3 codes, or for MXFP4 W4A8 layers the
+    dequantised MXFP8 codes (e4m3 times 2^(e - 127) per 32 columns)."""
     x = bf16_decode(x_bits)
     if spec.fmt == "fp8":
         q, s = quant_act_fp8(x.astype(np.float32))
         return e4m3_decode(q) * np.repeat(s.astype(np.float64), 128, axis=1), x
+    if spec.fmt == "mxfp4_a8":
+        q, e = quant_act_mxfp8(x.astype(np.float32))
+        return e4m3_decode(q) * np.repeat(e8m0_decode(e), 32, axis=1), x
     return x, x
 
 

@@ -41,7 +41,10 @@ FMT_FP8 = "fp8"
 FMT_INT4 = "int4"
 FMT_NVFP4 = "nvfp4"
 FMT_MXFP4 = "mxfp4"
-FP4_FORMATS = (FMT_NVFP4, FMT_MXFP4)
+# MXFP4 weights with MXFP8 activations into GEMM1 (block-scaled matrix
+# instructions); the weights are stored exactly as for FMT_MXFP4
+FMT_MXFP4_A8 = "mxfp4_a8"
+FP4_FORMATS = (FMT_NVFP4, FMT_MXFP4, FMT_MXFP4_A8)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -130,6 +133,10 @@ FP4_CONFIGS = {
         name="mxfp4_g32_64", cfg_id=7, fmt=FMT_MXFP4, H=2048, I=768,
         n_routed=64, top_k=8, Ts=(1, 64, 2048)),
 }
+# The same MXFP4 layer (same seeds: identical weights and inputs) with its
+# activations entering GEMM1 as MXFP8, on the block-scaled matrix cores
+FP4_CONFIGS["mxfp4a8_g32_64"] = FP4_CONFIGS["mxfp4_g32_64"].scaled(
+    name="mxfp4a8_g32_64", fmt=FMT_MXFP4_A8)
 
 
 def _seed(*parts: int) -> int:

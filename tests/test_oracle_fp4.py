@@ -94,7 +94,7 @@ def _setup(name, T=5):
     return spec, to_numpy_layer(layer), to_numpy_batch(batch)
 
 
-@pytest.mark.parametrize("name", ["nvfp4_lora", "mxfp4_shared"])
+@pytest.mark.parametrize("name", ["nvfp4_lora", "mxfp4_shared", "mxfp4a8_oai"])
 def test_fp4_layer_matches_brute_force(name):
     spec, arr, nb = _setup(name)
     ref = np.array(brute.layer(spec, arr, nb["x_bits"], nb["logits"]))
@@ -131,3 +131,121 @@ def test_nvfp4_true_units_invariant_to_a_power_of_two_resplit():
     gs[:, 1] *= np.float32(0.5)
     a["w13_s"], a["gs"] = s, gs
     assert np.array_equal(O.moe_layer(spec, a, nb["x_bits"], nb["logits"]), ref)
+
+
+# ---------------------------------------------------------------- MXFP8 pins
+# The W4A8 MXFP4 layers quantise the GEMM1 activations to MXFP8: per row and
+# 32 columns an e8m0 power of two 2^e, the smallest that keeps the group's
+# amax within 448 (e4m3's largest value), and e4m3 codes of x / 2^e.
+
+def _mx(rows):
+    q, e = O.quant_act_mxfp8(np.asarray(rows, np.float32))
+    return q, e.astype(np.int64)
+
+
+def test_mxfp8_exponent_closed_forms():
+    rows = np.zeros((6, 32), np.float32)
+    rows[0, 3] = 448.0                      # amax = 448 * 2^0: e = 0
+    rows[1, 0] = -448.0 * 2.0 ** -20        # e = -20, sign kept
+    rows[2, 7] = 450.0                      # next bf16 above 448: e = 1
+    rows[3, 1] = 500.0                      # floor(log2) - 8 would give 0 and clip
+    rows[4, 0] = 3.0e38                     # 448 * 2^119 = 2.98e38 < 3e38: e = 120
+    # row 5 all zero: e8m0 code 0, every code 0
+    q, e = _mx(rows)
+    assert e[:, 0].tolist() == [127, 107, 128, 128, 247, 0]
+    assert q[0, 3] == 0x7E and q[1, 0] == 0xFE          # +-448
+    assert O.e4m3_decode(q[2, 7]) == 224.0              # 225 rounds to even 224
+    assert O.e4m3_decode(q[3, 1]) == 256.0              # 250 -> 256 (step 16 below 256)
+    assert not q[5].any()
+    # amax exactly 448 * 2^e is kept; a hair above moves e up by one
+    for k in (-30, -1, 0, 7, 40):
+        a = np.float32(448.0 * 2.0 ** k)
+        up = np.nextafter(a, np.float32(np.inf))
+        _, e2 = _mx([[a] + [0.0] * 31, [up] + [0.0] * 31])
+        assert e2[:, 0].tolist() == [127 + k, 128 + k]
+
+
+def test_mxfp8_ties_go_to_the_even_code():
+    # amax 448 (e = 0); 1.0625 lies midway between 1.0 (0x38) and 1.125
+    # (0x39), 1.1875 between 1.125 and 1.25 (0x3A), 232 between 224 (0x76)
+    # and 240 (0x77)
+    row = np.zeros((1, 32), np.float32)
+    row[0, :4] = [448.0, 1.0625, 1.1875, 232.0]
+    q, e = _mx(row)
+    assert e[0, 0] == 127
+    assert q[0, :4].tolist() == [0x7E, 0x38, 0x3A, 0x76]
+
+
+def test_mxfp8_groups_are_32_wide():
+    # 1.0 everywhere, amax 448 in columns 0..31 only: the first group keeps
+    # e = 0 (1.0 exact), the second has amax 1 (e = -8: 1.0 -> 256)
+    row = np.ones((1, 64), np.float32)
+    row[0, 31] = 448.0
+    q, e = _mx(row)
+    assert e[0].tolist() == [127, 119]
+    v = O.e4m3_decode(q[0]) * np.repeat(O.e8m0_decode(e[0].astype(np.uint8)), 32)
+    assert np.array_equal(v, row[0].astype(np.float64))
+
+
+def _mx_against_brute():
+    """Random bf16 rows whose magnitude changes from one 32-column group to
+    the next (and zero, tiny and huge groups): the oracle's MXFP8 values
+    and exponents against the brute-force scan-and-search."""
+    rng = np.random.default_rng(11)
+    T, H = 12, 256
+    mag = np.ldexp(1.0, rng.integers(-40, 40, (T, H // 32)).repeat(32, axis=1))
+    x = rng.standard_normal((T, H)) * mag * (rng.random((T, H)) < 0.9)
+    x[3, :32] = 0.0
+    x[4, 32:64] = 1e-39
+    x[5, 64:96] *= 1e30
+    xb = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    q, e = _mx(xb)
+    ours = O.e4m3_decode(q) * np.repeat(O.e8m0_decode(e.astype(np.uint8)), 32, axis=1)
+    ref = np.array([brute.mxfp8_row([float(v) for v in row]) for row in xb])
+    exps = np.array([[brute.mxfp8_exponent(float(np.abs(xb[t, 32 * b:32 * b + 32]).max()))
+                      for b in range(H // 32)] for t in range(T)])
+    return np.array_equal(ours, ref) and np.array_equal(e - 127, exps)
+
+
+def test_mxfp8_matches_brute_force():
+    assert _mx_against_brute()
+
+
+def _mut_mx_group_64(mp):
+    real = O.quant_act_mxfp8
+
+    def g64(x_f32, group=32):
+        q, e = real(x_f32, 64)
+        return q, np.repeat(e, 2, axis=1)
+    mp.setattr(O, "quant_act_mxfp8", g64)
+
+
+def _mut_mx_truncate(mp):
+    """Codes truncated toward zero instead of rounded to nearest."""
+    real = O.quant_act_mxfp8
+
+    def trunc(x_f32, group=32):
+        q, e = real(x_f32, group)
+        x = np.asarray(x_f32, np.float32).astype(np.float64)
+        v = x / np.repeat(O.e8m0_decode(e), group, axis=1)
+        qv = O.e4m3_decode(q)
+        down = np.abs(qv) > np.abs(v)               # rounded away from zero
+        q = np.where(down & ((q & 0x7F) > 0), q - 1, q).astype(np.uint8)
+        return q, e
+    mp.setattr(O, "quant_act_mxfp8", trunc)
+
+
+@pytest.mark.parametrize("mut", [_mut_mx_group_64, _mut_mx_truncate])
+def test_planted_mxfp8_mistakes_are_caught(mut, monkeypatch):
+    mut(monkeypatch)
+    assert not _mx_against_brute()
+
+
+def test_w4a8_layer_differs_from_w4a16_by_the_activation_rounding():
+    """Same weights and inputs: the MXFP8 activation rounding moves the
+    output (so it is applied), by about e4m3's relative precision."""
+    spec, arr, nb = _setup("mxfp4a8_oai")
+    a8 = O.moe_layer(spec, arr, nb["x_bits"], nb["logits"])
+    a16 = O.moe_layer(spec.scaled(fmt="mxfp4"), arr, nb["x_bits"], nb["logits"])
+    rel = np.sqrt(np.mean((a8 - a16) ** 2) / np.mean(a16 ** 2))
+    assert 1e-3 < rel < 0.1

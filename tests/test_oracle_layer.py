@@ -147,12 +147,29 @@ def _mut_w13_block_scale_rows_only(mp):
     mp.setattr(O, "dequant_fp8_block", first_k_block)
 
 
+def _mut_mx_floor_exponent(mp):
+    """MXFP8 exponent from floor(log2 amax) - 8 (the largest element may then
+    exceed 448 and is saturated) instead of the smallest e that keeps the
+    group within 448."""
+    def floor_exp(x_f32, group=32):
+        x = np.asarray(x_f32, np.float32).astype(np.float64)
+        T, H = x.shape
+        xg = x.reshape(T, H // group, group)
+        amax = np.abs(xg).max(axis=2)
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8, -127)
+        e = np.maximum(e, -127).astype(np.int64)
+        q = O.e4m3_round(xg / np.ldexp(1.0, e.astype(np.int32))[:, :, None]).reshape(T, H)
+        return q, (e + 127).astype(np.uint8)
+    mp.setattr(O, "quant_act_mxfp8", floor_exp)
+
+
 @pytest.mark.parametrize("mut,name", [
     (_mut_swap_gate_up, "fp8_clamp_shared"), (_mut_drop_clamp, "fp8_clamp_shared"),
     (_mut_drop_clamp, "fp8_oai"), (_mut_no_requant, "fp8_oai"),
     (_mut_requant_per_row, "fp8_2grp_shared"), (_mut_requant_per_row, "ep_lora_2grp"),
     (_mut_quant_act_per_row, "fp8_2grp_shared"),
-    (_mut_w13_block_scale_rows_only, "fp8_2grp_shared")])
+    (_mut_w13_block_scale_rows_only, "fp8_2grp_shared"),
+    (_mut_mx_floor_exponent, "mxfp4a8_oai")])
 def test_planted_mistakes_are_caught_by_brute_force(mut, name, monkeypatch):
     spec = TINY[name]
     ours, ref = _oracle_and_brute(spec, 5, mut, monkeypatch)

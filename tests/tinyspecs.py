@@ -42,3 +42,8 @@ TINY["ep_lora_2grp"] = LayerSpec(name="tiny_ep_lora_2grp_t", cfg_id=110, fmt="fp
                                  H=256, I=256, n_routed=8, n_sink=2, top_k=3, E_loc=3,
                                  offset=2, lora_rank=4, gscale=True, logits="mix258",
                                  alpha=1.702, beta=1.0, limit=7.0, lora_down=True)
+# MXFP4 weights with MXFP8 activations into GEMM1, H = 256 (eight 32-column
+# activation groups per row, two 128-deep K blocks), OAI SwiGLU
+TINY["mxfp4a8_oai"] = LayerSpec(name="tiny_mxfp4a8_t", cfg_id=111, fmt="mxfp4_a8", H=256,
+                                I=128, n_routed=4, top_k=2, shared=1, alpha=1.702,
+                                beta=1.0, limit=7.0)
