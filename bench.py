@@ -418,8 +418,19 @@ def _weight_bytes(layer):
     return b13, b2
 
 
-def _peak_tflops(fmt):
-    return FP8_PEAK_TFLOPS if fmt == "fp8" else BF16_PEAK_TFLOPS
+def _peak_tflops(fmt, gemm=0):
+    """The dense MFMA peak a GEMM of the format runs against: FP8 layers and
+    the W4A8 GEMM1 (fp4 x fp8 on the block-scaled instructions) the FP8
+    rate, the others bf16 / f16; gemm 0 = the whole layer, where the W4A8
+    layer takes the rate of its GEMMs' flop mix (2/3 at FP8, 1/3 at f16)."""
+    if fmt == "fp8":
+        return FP8_PEAK_TFLOPS
+    if fmt == "mxfp4_a8":
+        if gemm == 1:
+            return FP8_PEAK_TFLOPS
+        if gemm == 0:
+            return 1.0 / (2.0 / 3.0 / FP8_PEAK_TFLOPS + 1.0 / 3.0 / BF16_PEAK_TFLOPS)
+    return BF16_PEAK_TFLOPS
 
 
 def config_table(args, stream, flush):
@@ -489,17 +500,18 @@ def config_table(args, stream, flush):
             g1_med, _ = time_flushed(st.gemm1, args.steps, stream, flush)
             g2_med, _ = time_flushed(st.gemm2, args.steps, stream, flush)
             fp8 = spec.fmt == "fp8"
-            xb = T * spec.H * ((1 + 4 / 128) if fp8 else 2)
+            xb = T * spec.H * ((1 + 4 / 128) if fp8 else (1 + 1 / 32)
+                               if spec.fmt == "mxfp4_a8" else 2)
             hb = P * spec.I * ((1 + 4 / 128) if fp8 else 2)
             g1_bytes = touched * b13 + xb + hb
             g2_bytes = touched * b2 + hb + T * spec.H * 4
 
-            def rate(ms_, byts, flops):
+            def rate(ms_, byts, flops, pk):
                 gbs = byts / (ms_ * 1e-3) / 1e9
                 tfl = flops / (ms_ * 1e-3) / 1e12
                 return {"ms": round(ms_, 4), "gbs": round(gbs, 1),
                         "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
-                        "tflops": round(tfl, 2), "frac_mfma": round(tfl / peak, 4)}
+                        "tflops": round(tfl, 2), "frac_mfma": round(tfl / pk, 4)}
             ent = {"config": name, "T": T, "fmt": spec.fmt,
                    "ms_per_step": round(ms, 4), "ms_flushed_median": round(fmed, 4),
                    "ms_flushed_min": round(fmin, 4), "tokens_per_s": round(T / s_, 1),
@@ -512,8 +524,10 @@ def config_table(args, stream, flush):
                    "pct_attainable": round(100 * max(wbytes / (HBM_PEAK_GBS * 1e9),
                                                      fl / (peak * 1e12)) / s_, 2),
                    "pairs": P, "experts_touched": touched,
-                   "gemm1": rate(g1_med, g1_bytes, 4.0 * P * spec.H * spec.I),
-                   "gemm2_combine": rate(g2_med, g2_bytes, 2.0 * P * spec.H * spec.I)}
+                   "gemm1": rate(g1_med, g1_bytes, 4.0 * P * spec.H * spec.I,
+                                 _peak_tflops(spec.fmt, 1)),
+                   "gemm2_combine": rate(g2_med, g2_bytes, 2.0 * P * spec.H * spec.I,
+                                         _peak_tflops(spec.fmt, 2))}
             entries.append(ent)
             print(f"# {name:18s} {T:5d} {ms:10.4f} {fmed:12.4f} {fmin:12.4f} "
                   f"{T / fmed * 1e3:11.1f} {fl / fmed / 1e9:10.2f} "

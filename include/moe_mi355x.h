@@ -71,11 +71,21 @@ typedef enum {
                           sign bit 3, magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6.
                           NaN scale codes (0x7F, 0xFF) set
                           MOE_DEVERR_W4_SCALE. */
-  MOE_W_MXFP4 = 4      /* e2m1 codes as NVFP4; scale e8m0 u8 [G][N][K/32];
+  MOE_W_MXFP4 = 4,     /* e2m1 codes as NVFP4; scale e8m0 u8 [G][N][K/32];
                           w = e2m1(code) * 2^(scale - 127). Exact for scale
                           exponents 104..128 (2^-23 .. 2); a call that meets
                           another exponent sets MOE_DEVERR_W4_SCALE (its
                           outputs are then not valid). */
+  MOE_W_MXFP4_A8 = 5   /* W4A8: the weights exactly as MOE_W_MXFP4, but the
+                          activations enter GEMM1 as MXFP8 (see
+                          moe_quantize_act_mxfp8) and GEMM1 runs on the
+                          block-scaled matrix instructions, which take the
+                          whole e8m0 range (code 0xFF, NaN, sets
+                          MOE_DEVERR_W4_SCALE). Its 128-deep sums are
+                          accurate to about 2e-5 of their sum of |products|
+                          (not fp32-accurate); h is bf16 and GEMM2 is the
+                          MOE_W_MXFP4 one. A choice of this library: the
+                          pages fix no activation format for 4-bit weights. */
 } moe_wfmt;
 
 /* err_word bits */
@@ -236,6 +246,15 @@ size_t moe_permute_workspace_size(long T, int top_k, int n_groups);
 int moe_quantize_act_fp8(const void *x_bf16, long T, int H, void *xq,
                          float *xs, void *stream);
 
+/* MXFP8 activations, the GEMM1 input of MOE_W_MXFP4_A8 layers: per token and
+ * per 32 columns, amax in fp32, e = the smallest integer with
+ * amax <= 448 * 2^e (raised to -127 when smaller, e.g. an all-zero group),
+ * xe = e + 127 (e8m0), xq = e4m3fn(round-to-nearest-even(x / 2^e)) (never
+ * beyond 448, so never saturated). x bf16 [T][H] -> xq e4m3fn [T][H] +
+ * xe u8 [T][H/32]. H % 128 == 0. */
+int moe_quantize_act_mxfp8(const void *x_bf16, long T, int H, void *xq,
+                           void *xe, void *stream);
+
 /* ------------------------------------------------ grouped GEMM1 + SwiGLU -- */
 /* err_word of the GEMM entry points: device int32, ORed with the
  * MOE_DEVERR_F16_RANGE / MOE_DEVERR_W4_SCALE bits a 4-bit layer meets
@@ -249,7 +268,9 @@ int moe_quantize_act_fp8(const void *x_bf16, long T, int H, void *xq,
  *   FP8 weights: x = xq e4m3fn [T][H] with xs fp32 [T][H/128]; h is
  *     re-quantised like moe_quantize_act_fp8 per row and 128 columns:
  *     h e4m3fn [P_cap][I], hs fp32 [P_cap][I/128].
- *   BF16 / 4-bit (INT4, NVFP4, MXFP4) weights: x bf16 [T][H] (xs NULL);
+ *   MXFP4_A8 weights: x = xq e4m3fn [T][H] with xs = xe u8 [T][H/32]
+ *     (moe_quantize_act_mxfp8); h bf16 as below, hs NULL.
+ *   BF16 / other 4-bit (INT4, NVFP4, MXFP4) weights: x bf16 [T][H] (xs NULL);
  *     h bf16 [P_cap][I] (round-to-nearest-even), hs NULL.
  * x_bf16 bf16 [T][H] is the LoRA input (NULL without LoRA).
  * h_lora (FP8 weights only, else it must be NULL: MOE_ERR_PARAM), nullable:
@@ -264,10 +285,10 @@ int moe_quantize_act_fp8(const void *x_bf16, long T, int H, void *xq,
  * columns that one tile per workgroup would leave CUs idle) the fp32
  * partial sums of a split-K schedule (4 * p_cap * 2I floats), which spreads
  * the K blocks of those tiles over all CUs and reduces them in a fixed
- * order; for 4-bit weights the f16 copy of the activations (p_cap * H * 2
- * bytes, T <= p_cap). Returns 0 for a NULL w13 or N not a multiple of 256. */
+ * order; for 4-bit weights other than MXFP4_A8 the f16 copy of the
+ * activations (p_cap * H * 2 bytes, T <= p_cap). Returns 0 for a NULL w13 or N not a multiple of 256. */
 int moe_grouped_gemm1_act(const moe_weights *w13, const void *x,
-                          const float *xs, const void *x_bf16, long T, int H,
+                          const void *xs, const void *x_bf16, long T, int H,
                           int I, int top_k, long p_cap, const int *offsets,
                           const int *sorted_pair, const moe_act_params *act,
                           const moe_lora *lora, void *h, float *hs,
@@ -327,7 +348,8 @@ typedef struct {
 } moe_layer;
 
 /* One call of the whole path on `stream`: moe_route -> moe_permute ->
- * (FP8) moe_quantize_act_fp8 -> moe_grouped_gemm1_act ->
+ * (FP8) moe_quantize_act_fp8 | (MXFP4_A8) moe_quantize_act_mxfp8 ->
+ * moe_grouped_gemm1_act ->
  * moe_grouped_gemm2_combine. x_bf16 bf16 [T][H]; logits fp32 [T][ld_logits]
  * with ld_logits >= num_experts_global + n_sink. Outputs out fp32 [T][H],
  * topk_ids/topk_w [T][top_k], sink_w [T][n_sink] (NULL iff n_sink == 0),

@@ -4,6 +4,7 @@ on MI355X (gfx950).
 Argument marshalling only. Every step of the path runs in the library's HIP
 kernels; torch supplies device memory (tensors) and the current stream. The
 functions carry the C names (moe_route, moe_permute, moe_quantize_act_fp8,
+moe_quantize_act_mxfp8,
 moe_grouped_gemm1_act, moe_grouped_gemm2_combine, moe_forward, ...), take
 torch tensors for the arrays, and raise MoeError on a negative status.
 There is no fallback: without the built library every call raises.
@@ -23,7 +24,8 @@ LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "moe_mi355x.h")
 
 MOE_W_BF16, MOE_W_FP8_B128, MOE_W_INT4_G32, MOE_W_NVFP4, MOE_W_MXFP4 = 0, 1, 2, 3, 4
-_PACKED4 = (MOE_W_INT4_G32, MOE_W_NVFP4, MOE_W_MXFP4)
+MOE_W_MXFP4_A8 = 5
+_PACKED4 = (MOE_W_INT4_G32, MOE_W_NVFP4, MOE_W_MXFP4, MOE_W_MXFP4_A8)
 MOE_DEVERR_GLOBAL_ID_OOB = 0x1
 MOE_DEVERR_F16_RANGE = 0x2
 MOE_DEVERR_W4_SCALE = 0x4
@@ -81,6 +83,8 @@ _SIGS = {
     "moe_permute_workspace_size": (c_size_t, [c_long, c_int, c_int]),
     "moe_quantize_act_fp8": (c_int, [c_void_p, c_long, c_int, c_void_p, c_void_p,
                                      c_void_p]),
+    "moe_quantize_act_mxfp8": (c_int, [c_void_p, c_long, c_int, c_void_p, c_void_p,
+                                       c_void_p]),
     "moe_grouped_gemm1_act": (c_int, [POINTER(MoeWeights), c_void_p, c_void_p,
                                       c_void_p, c_long, c_int, c_int, c_int,
                                       c_long, c_void_p, c_void_p,
@@ -235,6 +239,12 @@ def moe_quantize_act_fp8(x_bf16, xq, xs, stream=None):
     T, H = x_bf16.shape
     _check(lib().moe_quantize_act_fp8(_p(x_bf16), T, H, _p(xq), _p(xs),
                                       _stream(stream)), "moe_quantize_act_fp8")
+
+
+def moe_quantize_act_mxfp8(x_bf16, xq, xe, stream=None):
+    T, H = x_bf16.shape
+    _check(lib().moe_quantize_act_mxfp8(_p(x_bf16), T, H, _p(xq), _p(xe),
+                                        _stream(stream)), "moe_quantize_act_mxfp8")
 
 
 def moe_gemm1_workspace_size(w13: MoeWeights, p_cap, lora: Optional[MoeLora] = None) -> int:

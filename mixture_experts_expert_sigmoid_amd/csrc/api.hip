@@ -33,14 +33,19 @@ inline bool finite(float v) { return isfinite(v); }
 
 // 4-bit formats: packed codes, the 4-bit kernel family, bf16 h
 bool is4(int fmt) {
-  return fmt == MOE_W_INT4_G32 || fmt == MOE_W_NVFP4 || fmt == MOE_W_MXFP4;
+  return fmt == MOE_W_INT4_G32 || fmt == MOE_W_NVFP4 || fmt == MOE_W_MXFP4 ||
+         fmt == MOE_W_MXFP4_A8;
 }
-bool is_fp4(int fmt) { return fmt == MOE_W_NVFP4 || fmt == MOE_W_MXFP4; }
+bool is_fp4(int fmt) {
+  return fmt == MOE_W_NVFP4 || fmt == MOE_W_MXFP4 || fmt == MOE_W_MXFP4_A8;
+}
+// GEMM1 takes quantised activation codes with scales (FP8, MXFP8)
+bool quant_act(int fmt) { return fmt == MOE_W_FP8_B128 || fmt == MOE_W_MXFP4_A8; }
 
 // w2: the down weight, whose global scales ([G]) only FP4 formats take
 int check_weights(const moe_weights* w, int N, int K, bool w2 = false) {
   if (!w || !w->q) return MOE_ERR_NULL;
-  if (w->fmt < MOE_W_BF16 || w->fmt > MOE_W_MXFP4) return MOE_ERR_FORMAT;
+  if (w->fmt < MOE_W_BF16 || w->fmt > MOE_W_MXFP4_A8) return MOE_ERR_FORMAT;
   if (w->fmt != MOE_W_BF16 && !w->scale) return MOE_ERR_NULL;
   if (w2 && w->gscale && !is_fp4(w->fmt)) return MOE_ERR_FORMAT;
   if (w->N != N || w->K != K) return MOE_ERR_SHAPE;
@@ -205,6 +210,14 @@ int moe_quantize_act_fp8(const void* x_bf16, long T, int H, void* xq,
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_quantize_act_fp8");
 }
 
+int moe_quantize_act_mxfp8(const void* x_bf16, long T, int H, void* xq, void* xe,
+                           void* stream) {
+  if (T < 0 || H < 128 || H % 128) return MOE_ERR_SHAPE;
+  if (T > 0 && (!x_bf16 || !xq || !xe)) return MOE_ERR_NULL;
+  hipError_t e = moe::launch_quant_act_mx(x_bf16, T, H, xq, xe, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_quantize_act_mxfp8");
+}
+
 }  // extern "C"
 
 namespace {
@@ -224,7 +237,7 @@ size_t g1_part_bytes(const moe_weights* w13, long p_cap) {
   return moe::splitk_bytes(p_cap, w13->N);
 }
 size_t g1_x16_bytes(const moe_weights* w13, long rows) {
-  return is4(w13->fmt) ? al((size_t)rows * w13->K * 2) : 0;
+  return is4(w13->fmt) && w13->fmt != MOE_W_MXFP4_A8 ? al((size_t)rows * w13->K * 2) : 0;
 }
 // GEMM2 workspace: fp32 y rows, or (split-K) their partial sums
 size_t g2_bytes(const moe_weights* w2, long p_cap) {
@@ -242,7 +255,7 @@ size_t moe_gemm1_workspace_size(const moe_weights* w13, long p_cap,
   return g1_z_bytes(p_cap, lora) + g1_part_bytes(w13, p_cap) + g1_x16_bytes(w13, p_cap);
 }
 
-static int gemm1_checks(const moe_weights* w13, const void* x, const float* xs,
+static int gemm1_checks(const moe_weights* w13, const void* x, const void* xs,
                         const void* x_bf16, long T, int H, int I, int top_k,
                         long p_cap, const int* offsets, const int* sorted_pair,
                         const moe_act_params* act, const moe_lora* lora,
@@ -255,12 +268,13 @@ static int gemm1_checks(const moe_weights* w13, const void* x, const float* xs,
   if ((st = check_lora(lora, w13->n_groups))) return st;
   if (!offsets || (p_cap > 0 && (!x || !sorted_pair || !h))) return MOE_ERR_NULL;
   if (w13->fmt == MOE_W_FP8_B128 && p_cap > 0 && (!xs || !hs)) return MOE_ERR_NULL;
+  if (w13->fmt == MOE_W_MXFP4_A8 && p_cap > 0 && !xs) return MOE_ERR_NULL;
   if (lora && p_cap > 0 && !x_bf16) return MOE_ERR_NULL;
   return MOE_OK;
 }
 
 static moe::Gemm1Args gemm1_args(const moe_weights* w13, const void* x,
-                                 const float* xs, long T, int H, int I,
+                                 const void* xs, long T, int H, int I,
                                  int top_k, long p_cap, const int* offsets,
                                  const int* sorted_pair,
                                  const moe_act_params* act,
@@ -302,7 +316,7 @@ static moe::Gemm1Args gemm1_args(const moe_weights* w13, const void* x,
 }
 
 int moe_grouped_gemm1_act(const moe_weights* w13, const void* x,
-                          const float* xs, const void* x_bf16, long T, int H,
+                          const void* xs, const void* x_bf16, long T, int H,
                           int I, int top_k, long p_cap, const int* offsets,
                           const int* sorted_pair, const moe_act_params* act,
                           const moe_lora* lora, void* h, float* hs, void* h_lora,
@@ -431,6 +445,7 @@ FwdLayout layout(const moe_layer* L, long T) {
   int G = L->num_local_experts + L->shared_expert;
   long pc = pcap_of(T, L->top_k, L->shared_expert);
   bool fp8 = L->w13.fmt == MOE_W_FP8_B128;
+  bool mx = L->w13.fmt == MOE_W_MXFP4_A8;
   size_t cur = 0;
   auto take = [&](size_t bytes) { size_t at = cur; cur += al(bytes); return at; };
   o.offsets = take((size_t)(G + 1) * 4);
@@ -438,9 +453,9 @@ FwdLayout layout(const moe_layer* L, long T) {
   o.pair_row = take((size_t)pc * 4);
   o.perm_bytes = moe::permute_ws_bytes(T, L->top_k, G);
   o.perm_ws = take(o.perm_bytes);
-  // FP8 activation codes, or (4-bit formats) the f16 activations
-  o.xq = take(fp8 ? (size_t)T * L->H : g1_x16_bytes(&L->w13, T));
-  o.xs = take(fp8 ? (size_t)T * (L->H / 128) * 4 : 0);
+  // FP8 / MXFP8 activation codes, or (other 4-bit formats) the f16 activations
+  o.xq = take(fp8 || mx ? (size_t)T * L->H : g1_x16_bytes(&L->w13, T));
+  o.xs = take(fp8 ? (size_t)T * (L->H / 128) * 4 : mx ? (size_t)T * (L->H / 32) : 0);
   o.z = take(g1_z_bytes(pc, L->lora));
   o.h = take((size_t)pc * L->I * (fp8 ? 1 : 2));
   o.hs = take(fp8 ? (size_t)pc * (L->I / 128) * 4 : 0);
@@ -518,6 +533,7 @@ int moe_forward(const moe_layer* L, const void* x_bf16, const float* logits,
   float* z2 = (float*)(base + o.z2);
 
   const bool four = is4(L->w13.fmt);
+  const bool mx = L->w13.fmt == MOE_W_MXFP4_A8;
   bool x16_ready = false;
   hipError_t e = hipSuccess;
   if (moe::front_small_fits(T, L->top_k, G, L->H)) {
@@ -545,9 +561,9 @@ int moe_forward(const moe_layer* L, const void* x_bf16, const float* logits,
     fa.sorted_pair = sorted_pair;
     fa.pair_row = pair_row;
     fa.err_word = err_word;
-    e = moe::launch_front_small(fa, fp8 ? 1 : (four ? 2 : 0), s);
+    e = moe::launch_front_small(fa, fp8 ? 1 : mx ? 3 : (four ? 2 : 0), s);
     if (e != hipSuccess) return hip_fail(e, "moe_forward/front");
-    x16_ready = four;
+    x16_ready = four && !mx;
   } else {
     e = moe::launch_route(logits, T, ld_logits, L->num_experts_global, L->n_sink,
                           L->top_k, nullptr, L->route_scale * L->global_scale,
@@ -561,6 +577,9 @@ int moe_forward(const moe_layer* L, const void* x_bf16, const float* logits,
     if (fp8) {
       e = moe::launch_quant_act(x_bf16, T, L->H, xq, xs, s);
       if (e != hipSuccess) return hip_fail(e, "moe_forward/quant");
+    } else if (mx) {
+      e = moe::launch_quant_act_mx(x_bf16, T, L->H, xq, xs, s);
+      if (e != hipSuccess) return hip_fail(e, "moe_forward/quant");
     }
   }
   if (L->lora) {
@@ -571,7 +590,8 @@ int moe_forward(const moe_layer* L, const void* x_bf16, const float* logits,
     if (e != hipSuccess) return hip_fail(e, "moe_forward/lora_z");
   }
   float* g1_part = g1_part_bytes(&L->w13, pc) ? y : nullptr;
-  moe::Gemm1Args ga = gemm1_args(&L->w13, fp8 ? xq : x_bf16, fp8 ? xs : nullptr,
+  moe::Gemm1Args ga = gemm1_args(&L->w13, fp8 || mx ? xq : x_bf16,
+                                 fp8 || mx ? (const void*)xs : nullptr,
                                  T, L->H, L->I, L->top_k, pc, offsets,
                                  sorted_pair, &L->act, L->lora, z, h,
                                  fp8 ? hs : nullptr, g1_part, xq,

@@ -13,7 +13,7 @@
 
 namespace moe {
 
-template <int NV, int MODE>   // MODE 0: no activation pass, 1: FP8, 2: f16 copy
+template <int NV, int MODE>   // MODE 0: no activation pass, 1: FP8, 2: f16 copy, 3: MXFP8
 __global__ __launch_bounds__(1024) void front_small_kernel(FrontArgs a) {
   extern __shared__ int sm[];                    // the permutation's 17 G ints
   const int wave = threadIdx.x >> 6;
@@ -23,7 +23,11 @@ __global__ __launch_bounds__(1024) void front_small_kernel(FrontArgs a) {
   if constexpr (MODE == 1) {
     const long n = a.T * ((a.H + 511) >> 9);
     for (long wi = wave; wi < n; wi += 16)
-      quant_act_unit((const uint16_t*)a.x, wi, a.H, (uint8_t*)a.xq, a.xs);
+      quant_act_unit((const uint16_t*)a.x, wi, a.H, (uint8_t*)a.xq, (float*)a.xs);
+  } else if constexpr (MODE == 3) {
+    const long n = a.T * ((a.H + 511) >> 9);
+    for (long wi = wave; wi < n; wi += 16)
+      quant_mx_unit((const uint16_t*)a.x, wi, a.H, (uint8_t*)a.xq, (uint8_t*)a.xs);
   } else if constexpr (MODE == 2) {
     const long n8 = a.T * (long)a.H / 8;
     bool over = false;
@@ -53,11 +57,12 @@ hipError_t launch_front_small(const FrontArgs& a, int mode, hipStream_t s) {
   const int nv = (a.n_routed + 63) / 64;
 #define FS(NV, MODE) \
   hipLaunchKernelGGL((front_small_kernel<NV, MODE>), dim3(1), dim3(kPermBlock), shm, s, a)
-#define FSM(NV)                  \
-  do {                           \
-    if (mode == 1) FS(NV, 1);    \
+#define FSM(NV)                    \
+  do {                             \
+    if (mode == 1) FS(NV, 1);      \
     else if (mode == 2) FS(NV, 2); \
-    else FS(NV, 0);              \
+    else if (mode == 3) FS(NV, 3); \
+    else FS(NV, 0);                \
   } while (0)
   if (nv <= 1) FSM(1);
   else if (nv <= 2) FSM(2);

@@ -264,8 +264,9 @@ static hipError_t dispatch(const GemmParams& P, long p_cap, int NT, long rows_hi
 hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t s) {
   GemmParams P{};
   P.a = (const uint8_t*)a.x;
-  P.as = a.xs;
-  P.a_ld = (long)a.H * (a.fmt == FMT_FP8 ? 1 : 2);   // bytes per activation row
+  P.as = (const float*)a.xs;
+  const bool mx = a.fmt == FMT_MXFP4_A8;
+  P.a_ld = (long)a.H * (a.fmt == FMT_FP8 || mx ? 1 : 2);   // bytes per activation row
   P.sorted_pair = a.sorted_pair;
   P.T = a.T;
   P.top_k = a.top_k;
@@ -293,14 +294,15 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t s) {
   if (a.fmt != FMT_BF16) {
     const bool fp8 = a.fmt == FMT_FP8;
     hipError_t e = hipSuccess;
-    if (!fp8) {                    // f16 activations in the 4-bit kernel's K order
+    if (!fp8 && !mx) {             // f16 activations in the 4-bit kernel's K order
       if (!a.x16_ready) e = launch_act_f16p(a.x, a.T, a.H, a.x16, a.err, s);
       if (e != hipSuccess) return e;
       P.a = (const uint8_t*)a.x16;
     }
     auto run = [&](int* grid) {
       return fp8 ? launch_gemm_fp8(P, true, a.p_cap, a.I / 128, s, grid)
-                 : launch_gemm_w4(a.fmt, P, true, a.p_cap, a.I / 128, s, grid);
+             : mx ? launch_gemm1_mx(P, a.p_cap, a.I / 128, s, grid)
+                  : launch_gemm_w4(a.fmt, P, true, a.p_cap, a.I / 128, s, grid);
     };
     const int mode = a.part ? splitk_mode(a.fmt, a.p_cap, a.G, a.I / 128, a.H / 128, true)
                             : SK_PLAIN;

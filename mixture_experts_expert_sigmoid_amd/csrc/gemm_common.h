@@ -19,7 +19,9 @@
 
 namespace moe {
 
-enum { FMT_BF16 = 0, FMT_FP8 = 1, FMT_INT4 = 2, FMT_NVFP4 = 3, FMT_MXFP4 = 4 };
+// FMT_MXFP4_A8: MXFP4 weights with MXFP8 activations into GEMM1 (gemm_mx.hip);
+// its GEMM2 is the MXFP4 kernel
+enum { FMT_BF16 = 0, FMT_FP8 = 1, FMT_INT4 = 2, FMT_NVFP4 = 3, FMT_MXFP4 = 4, FMT_MXFP4_A8 = 5 };
 
 constexpr int kThreads = 512;
 constexpr int kMaxGroups = 1024;
@@ -30,7 +32,8 @@ __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >>
 struct GemmParams {
   // A side
   const uint8_t* a;          // x (GEMM1: gathered by token) or h (GEMM2)
-  const float* as;           // FP8 per-row scales [rows][K/128]
+  const float* as;           // FP8 per-row scales [rows][K/128]; MXFP4 W4A8: the
+                             // e8m0 codes [rows][K/32] (bytes, read as such)
   long a_ld;                 // bytes per A row
   const int* sorted_pair;    // GEMM1: sorted row -> pair id
   long T;
@@ -548,6 +551,10 @@ hipError_t launch_gemm_nvfp4(const GemmParams& P, bool g1, long p_cap, int NT, h
                              int* sk_grid);
 hipError_t launch_gemm_mxfp4(const GemmParams& P, bool g1, long p_cap, int NT, hipStream_t s,
                              int* sk_grid);
+// GEMM1 of the MXFP4 W4A8 layers on the block-scaled matrix cores
+// (gemm_mx.hip): A = MXFP8 codes, P.as their e8m0 codes; bf16 h
+hipError_t launch_gemm1_mx(const GemmParams& P, long p_cap, int NT, hipStream_t s,
+                           int* sk_grid);
 // err (nullable): MOE_DEVERR_BIT_F16_RANGE is ORed in for a value beyond f16
 hipError_t launch_act_f16p(const void* x, long T, int H, void* out, int* err, hipStream_t s);
 

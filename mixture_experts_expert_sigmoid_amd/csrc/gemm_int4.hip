@@ -34,7 +34,9 @@ hipError_t launch_gemm_w4(int fmt, const GemmParams& P, bool g1, long p_cap, int
   switch (fmt) {
     case FMT_INT4: return launch_gemm_int4(P, g1, p_cap, NT, s, sk_grid);
     case FMT_NVFP4: return launch_gemm_nvfp4(P, g1, p_cap, NT, s, sk_grid);
-    case FMT_MXFP4: return launch_gemm_mxfp4(P, g1, p_cap, NT, s, sk_grid);
+    case FMT_MXFP4:
+    case FMT_MXFP4_A8:             // GEMM2 (bf16 h); its GEMM1 is gemm_mx.hip's
+      return launch_gemm_mxfp4(P, g1, p_cap, NT, s, sk_grid);
     default: return hipErrorInvalidValue;
   }
 }

@@ -49,12 +49,16 @@ hipError_t launch_permute(const int* ids, long T, int k, int E_global, int off,
 
 hipError_t launch_quant_act(const void* x, long T, int H, void* xq, float* xs,
                             hipStream_t s);
+// MXFP8: x bf16 [T][H] -> e4m3 codes [T][H] + e8m0 codes [T][H/32]
+hipError_t launch_quant_act_mx(const void* x, long T, int H, void* xq, void* xe,
+                               hipStream_t s);
 
 // Decode front end (front.hip): route (no bias, no packed output) + the
 // activation pass + permute in one workgroup when T * k <= kPermBlock, 17 G
 // ints fit 64 KB of LDS and T * ceil(H / 512) <= 64 (front_small_fits);
 // hipErrorNotSupported otherwise. mode 1: FP8 quantisation into xq / xs; 2: the f16 copy of x
-// into xq (4-bit formats); 0: none.
+// into xq (4-bit formats); 3: MXFP8 quantisation into xq / xs (e8m0 bytes; the
+// MXFP4 W4A8 format); 0: none.
 struct FrontArgs {
   const float* logits;
   long T, ld;
@@ -66,7 +70,7 @@ struct FrontArgs {
   const void* x;         // bf16 [T][H]
   int H;
   void* xq;
-  float* xs;
+  void* xs;              // fp32 [T][H/128] (mode 1) or e8m0 [T][H/32] (mode 3)
   int off, E_loc, G, shared;
   int* offsets;
   int* sorted_pair;
@@ -124,7 +128,7 @@ struct Gemm1Args {
   const void* ws;
   const float* gscale;
   const void* x;
-  const float* xs;
+  const void* xs;        // FP8: fp32 [T][H/128]; MXFP4 W4A8: e8m0 [T][H/32]
   long T;
   int H, I, top_k, G;
   long p_cap;

@@ -1,4 +1,5 @@
-// Per-token, per-128-column e4m3fn activation quantisation, and the LoRA
+// Per-token, per-128-column e4m3fn activation quantisation (and the MXFP8
+// variant of the MXFP4 W4A8 layers, quant_dev.h), and the LoRA
 // down-projection z = x A^T of the rows of each local expert.
 //
 // Quantisation: the activation side of blockwise 128x128 FP8 ("[Moe] Fix
@@ -32,6 +33,24 @@ hipError_t launch_quant_act(const void* x, long T, int H, void* xq, float* xs,
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(quant_act_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256),
                      0, s, (const uint16_t*)x, T, H, (uint8_t*)xq, xs);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void quant_act_mx_kernel(
+    const uint16_t* __restrict__ x, long T, int H, uint8_t* __restrict__ xq,
+    uint8_t* __restrict__ xe) {
+  const int nc = (H + 511) >> 9;
+  const long wi = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wi >= T * nc) return;
+  quant_mx_unit(x, wi, H, xq, xe);
+}
+
+hipError_t launch_quant_act_mx(const void* x, long T, int H, void* xq, void* xe,
+                               hipStream_t s) {
+  long n = T * (long)((H + 511) / 512);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(quant_act_mx_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256),
+                     0, s, (const uint16_t*)x, T, H, (uint8_t*)xq, (uint8_t*)xe);
   return hipGetLastError();
 }
 

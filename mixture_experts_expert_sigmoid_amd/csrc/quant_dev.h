@@ -53,4 +53,52 @@ __device__ __forceinline__ void quant_act_unit(const uint16_t* __restrict__ x, l
   }
 }
 
+// MXFP8 activations for the GEMM1 of the MXFP4 W4A8 layers: per row and 32
+// columns, amax (fp32, exact for bf16 inputs), e = the smallest integer
+// with amax <= 448 * 2^e (raised to -127, e.g. for an all-zero group),
+// stored as the e8m0 code e + 127, and codes = e4m3 RNE of x * 2^-e (an
+// exact product of magnitude <= 448, so the conversion never saturates).
+// With amax = m * 2^E (1 <= m < 2, biased exponent field B = E + 127):
+// 448 = 1.75 * 2^8, so e = E - 8 when m <= 1.75 and E - 7 otherwise, i.e.
+// e = B - 135 + (mantissa field > 0x600000). Same units as quant_act_unit:
+// one wave per (row, 512 columns); the 4 lanes of a DPP quad hold one
+// 32-column group.
+__device__ __forceinline__ void quant_mx_unit(const uint16_t* __restrict__ x, long wi, int H,
+                                              uint8_t* __restrict__ xq,
+                                              uint8_t* __restrict__ xe) {
+  const int nc = (H + 511) >> 9;
+  const int lane = lane_id();
+  const long row = wi / nc;
+  const int col = (int)(wi - row * nc) * 512 + 8 * lane;
+  const bool on = col < H;              // whole quads (H % 32 == 0)
+  float f[8];
+  i32x4 v = {0, 0, 0, 0};
+  if (on) v = *(const i32x4*)(x + row * H + col);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_bits_to_f32((uint32_t)v[i] & 0xFFFFu);
+    f[2 * i + 1] = bf16_bits_to_f32((uint32_t)v[i] >> 16);
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[i]));
+  a = fmaxf(a, __builtin_bit_cast(float, dpp_u32<0xB1>(__builtin_bit_cast(uint32_t, a))));
+  a = fmaxf(a, __builtin_bit_cast(float, dpp_u32<0x4E>(__builtin_bit_cast(uint32_t, a))));
+  const uint32_t ab = __builtin_bit_cast(uint32_t, a);
+  int e = (int)(ab >> 23) - 135 + ((ab & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  e = max(e, -127);
+  const float inv = __builtin_bit_cast(float, (uint32_t)(127 - e) << 23);   // 2^-e
+  uint32_t w[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    int c = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * h] * inv, f[4 * h + 1] * inv, 0, false);
+    w[h] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f[4 * h + 2] * inv, f[4 * h + 3] * inv,
+                                                     c, true);
+  }
+  if (on) {
+    *(uint2*)(xq + row * H + col) = make_uint2(w[0], w[1]);
+    if ((lane & 3) == 0) xe[row * (H >> 5) + (col >> 5)] = (uint8_t)(e + 127);
+  }
+}
+
 }  // namespace moe

@@ -601,14 +601,14 @@ def rounding_alternatives(h, err_h, fmt, group=128):
         step = np.maximum(np.where(near_lo, qv - lo, 0.0), np.where(near_hi, hi - qv, 0.0))
         alt = np.where(near_lo | near_hi, step + 2.0 * ev, 0.0)
         return (alt * s[:, :, None]).reshape(P, I)
-    # bf16 grid: spacing 2^(e-7) for |h| in [2^e, 2^(e+1))
-    a = np.abs(h)
-    _, ex = np.frexp(np.where(a == 0, 1.0, a))
-    ulp = np.ldexp(1.0, (ex - 8).astype(np.int32))
-    r = bf16_round(a)
-    dist = ulp / 2 - np.abs(a - r)
-    e = np.asarray(err_h) + a * EVAL_REL
-    return np.where(dist <= e, ulp + 2.0 * e, 0.0)
+    # bf16: rounding is monotone, so the roundings of the values within e of
+    # h lie between those of h - e and h + e; the largest step from the
+    # oracle's own rounding is at one of the two ends (zero when no rounding
+    # boundary lies in the band, whatever the grid spacing there: near 0 and
+    # below a power of two it is finer than at h)
+    e = np.asarray(err_h) + np.abs(h) * EVAL_REL
+    r = bf16_round(h)
+    return np.maximum(np.abs(bf16_round(h + e) - r), np.abs(bf16_round(h - e) - r))
 
 
 def expert_ffn(spec, arr, e, xhat_rows, x_bf16_rows, detail=False, adapters=None):

@@ -96,6 +96,16 @@ def test_permute_validation_local_range():
     assert L.moe_permute_workspace_size(4096, 8, 289) > 4096 * 8 * 4
 
 
+def test_quantize_validation():
+    L = M.lib()
+    for f in (L.moe_quantize_act_fp8, L.moe_quantize_act_mxfp8):
+        assert f(1, 4, 100, 1, 1, None) == -2      # H % 128
+        assert f(1, -1, 128, 1, 1, None) == -2
+        assert f(None, 4, 128, 1, 1, None) == -1
+        assert f(1, 4, 128, 1, None, None) == -1
+        assert f(None, 0, 128, None, None, None) == 0   # T = 0: nothing to do
+
+
 def test_gemm_validation():
     L = M.lib()
     act = M.act_params(1.0, 0.0, math.inf)
@@ -107,16 +117,27 @@ def test_gemm_validation():
     assert g1(_w(N=256, K=256), act, H=256, I=100) == -2   # I % 128
     assert g1(_w(N=512, K=256), act) == -2               # N != 2I
     assert g1(M.MoeWeights(7, 4, 256, 256, 1, 1, None), act) == -3
+    assert g1(M.MoeWeights(6, 4, 256, 256, 1, 1, None), act) == -3
     assert g1(M.MoeWeights(-1, 4, 256, 256, 1, 1, None), act) == -3
     # 4-bit codes are read 16 bytes at a time, NVFP4 scales as 2-byte pairs
-    for f in (M.MOE_W_INT4_G32, M.MOE_W_NVFP4, M.MOE_W_MXFP4):
+    for f in (M.MOE_W_INT4_G32, M.MOE_W_NVFP4, M.MOE_W_MXFP4, M.MOE_W_MXFP4_A8):
         assert g1(M.MoeWeights(f, 4, 256, 256, 264, 256, None), act) == -5
     assert g1(M.MoeWeights(M.MOE_W_NVFP4, 4, 256, 256, 256, 257, None), act) == -5
     assert g1(M.MoeWeights(M.MOE_W_NVFP4, 4, 256, 256, 256, None, None), act) == -1
     assert g1(M.MoeWeights(1, 4, 256, 256, 1, None, None), act) == -1   # fp8 needs scales
     # 4-bit layers report range problems through the error word: required
-    for f in (M.MOE_W_INT4_G32, M.MOE_W_NVFP4, M.MOE_W_MXFP4):
+    for f in (M.MOE_W_INT4_G32, M.MOE_W_NVFP4, M.MOE_W_MXFP4, M.MOE_W_MXFP4_A8):
         assert g1(M.MoeWeights(f, 4, 256, 256, 256, 256, None), act, err=None) == -1
+    # MXFP4 W4A8: GEMM1 takes the MXFP8 codes' e8m0 exponents in xs
+    mxw = M.MoeWeights(M.MOE_W_MXFP4_A8, 4, 256, 256, 256, 256, None)
+    assert L.moe_grouped_gemm1_act(ctypes.byref(mxw), 1, None, None, 4, 256, 128, 2, 8, 1, 1,
+                                   ctypes.byref(act), None, 1, None, None, 1,
+                                   ctypes.c_void_p(1), 1 << 20, None) == -1
+    # and needs no f16 copy of the activations in its workspace
+    big13 = M.MoeWeights(M.MOE_W_MXFP4_A8, 64, 1536, 2048, 256, 256, None)
+    big13i = M.MoeWeights(M.MOE_W_MXFP4, 64, 1536, 2048, 256, 256, None)
+    assert L.moe_gemm1_workspace_size(ctypes.byref(big13), 16384, None) == 0
+    assert L.moe_gemm1_workspace_size(ctypes.byref(big13i), 16384, None) >= 16384 * 2048 * 2
     assert g1(w, M.act_params(1.0, 0.0, 0.0)) == -5       # limit must be > 0
     assert g1(w, M.act_params(1.0, 0.0, math.nan)) == -5
     assert g1(w, M.act_params(math.inf, 0.0, 7.0)) == -5

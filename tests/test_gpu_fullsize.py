@@ -32,7 +32,8 @@ FULL = [("fp8_clamp_288", 4096), ("fp8_clamp_288", 64), ("fp8_clamp_288", 1),
         ("ep_lora_258", 1),
         ("ep_lora_258_down", 8192), ("ep_lora_258_down", 37),
         ("nvfp4_lora_258", 8192), ("nvfp4_lora_258", 37), ("nvfp4_lora_258", 1),
-        ("mxfp4_g32_64", 2048), ("mxfp4_g32_64", 1)]
+        ("mxfp4_g32_64", 2048), ("mxfp4_g32_64", 1),
+        ("mxfp4a8_g32_64", 2048), ("mxfp4a8_g32_64", 64), ("mxfp4a8_g32_64", 1)]
 N_ROWS = 64           # compared output rows per case (all of them when T <= 64)
 ORACLE_THREADS = 8    # per-expert FFNs of the oracle run side by side
 

@@ -125,6 +125,28 @@ def test_quant_act_bit_exact(T, H):
     assert np.array_equal(xq.cpu().numpy(), rq)
 
 
+@pytest.mark.parametrize("T,H", [(1, 128), (37, 2048), (512, 6144)])
+def test_quant_act_mxfp8_bit_exact(T, H):
+    """MXFP8 codes and e8m0 exponents of the W4A8 layers' activations,
+    bit for bit, on rows whose magnitude changes every 32 columns (and zero,
+    tiny and huge groups)."""
+    _log("quant-mx", T, H)
+    g = torch.Generator().manual_seed(7 * T + H)
+    mag = torch.exp2(torch.randint(-30, 30, (T, H // 32), generator=g).float())
+    x = torch.randn(T, H, generator=g) * mag.repeat_interleave(32, dim=1)
+    if T > 3:
+        x[1, :32] = 0.0
+        x[2, 32:64] *= 1e-30
+        x[3, 5] = 3e38
+    xb = x.to(torch.bfloat16)
+    xq = torch.empty(T, H, dtype=torch.uint8, device="cuda")
+    xe = torch.empty(T, H // 32, dtype=torch.uint8, device="cuda")
+    M.moe_quantize_act_mxfp8(xb.cuda(), xq, xe)
+    rq, re = O.quant_act_mxfp8(xb.float().numpy())
+    assert np.array_equal(xe.cpu().numpy(), re)
+    assert np.array_equal(xq.cpu().numpy(), rq)
+
+
 # ------------------------------------------------------------ whole layer
 
 SMALL = {
@@ -190,6 +212,19 @@ SMALL = {
         name="mxfp4_small", H=512, I=256, n_routed=16, shared=1, limit=7.0, cfg_id=44), 100),
     "mxfp4_sk": (FP4_CONFIGS["mxfp4_g32_64"].scaled(
         name="mxfp4_sk", n_routed=16, cfg_id=45), 2),
+    # MXFP4 weights with MXFP8 activations into GEMM1 on the block-scaled
+    # matrix cores: 128-, 64- and 32-row tiles with a shared expert and the
+    # clamp; OAI SwiGLU with an odd K-block count (H = 384); per-half W13
+    # global scales with a LoRA on both projections; the decode split-K
+    "mxfp4a8_small": (FP4_CONFIGS["mxfp4a8_g32_64"].scaled(
+        name="mxfp4a8_small", H=512, I=256, n_routed=16, shared=1, limit=7.0, cfg_id=44), 300),
+    "mxfp4a8_oai": (FP4_CONFIGS["mxfp4a8_g32_64"].scaled(
+        name="mxfp4a8_oai", H=384, I=256, n_routed=16, alpha=1.702, beta=1.0, limit=7.0,
+        cfg_id=53), 200),
+    "mxfp4a8_lora": (FP4_CONFIGS["nvfp4_lora_258"].scaled(
+        name="mxfp4a8_lora", fmt="mxfp4_a8", H=256, I=256, cfg_id=54), 300),
+    "mxfp4a8_sk": (FP4_CONFIGS["mxfp4a8_g32_64"].scaled(
+        name="mxfp4a8_sk", n_routed=16, cfg_id=45), 2),
     # adapter batches on 128-row tiles (all 16 experts local, ~150 rows
     # each): the tile's adapters' B blocks staged in LDS; with 40 adapters a
     # tile meets more than fit and reads B from memory; rank 32 halves the
@@ -290,7 +325,8 @@ def _stepwise(spec, mod, batch, T):
                                   "bf16_lora_multi", "nvfp4_lora_small", "nvfp4_lora_sk",
                                   "nvfp4_multi", "mxfp4_small", "mxfp4_sk",
                                   "ep_lora_multi_big", "nvfp4_multi_many",
-                                  "int4_lora32_multi"])
+                                  "int4_lora32_multi", "mxfp4a8_small", "mxfp4a8_oai",
+                                  "mxfp4a8_lora", "mxfp4a8_sk"])
 def test_gemm1_h_codes(name):
     """GEMM1 output h (codes and scales) against the oracle: equal wherever
     the exact h is not within the kernel's error of a rounding boundary;
@@ -333,7 +369,8 @@ def test_gemm1_h_codes(name):
 @pytest.mark.parametrize("name", ["ep_lora_small", "fp8_oai_sk", "ep_lora_sk",
                                   "ep_lora_up_sk", "int4_sk",
                                   "ep_lora_multi_sk", "int4_lora_multi_dec",
-                                  "nvfp4_lora_sk", "nvfp4_multi", "mxfp4_sk"])
+                                  "nvfp4_lora_sk", "nvfp4_multi", "mxfp4_sk",
+                                  "mxfp4a8_small", "mxfp4a8_lora", "mxfp4a8_sk"])
 def test_stepwise_entry_points_match_forward_and_oracle(name):
     """route -> permute -> quant -> gemm1 -> gemm2+combine through the
     individual C-ABI calls gives moe_forward's output bit for bit (also on
@@ -476,7 +513,8 @@ def test_mxfp4_exponents_outside_the_exact_window_are_flagged():
 
 
 @pytest.mark.parametrize("case", ["int4_scale_big", "int4_scale_tiny", "nvfp4_nan_scale",
-                                  "x_beyond_f16", "h_beyond_f16", "in_range"])
+                                  "mxfp4a8_nan_scale", "x_beyond_f16", "h_beyond_f16",
+                                  "in_range"])
 def test_4bit_range_problems_set_error_bits(case):
     """In-range data that the 4-bit kernels cannot expand exactly sets its
     error bit: an INT4 scale of 2^13 or 2^-14, an NVFP4 NaN scale code, an
@@ -485,8 +523,8 @@ def test_4bit_range_problems_set_error_bits(case):
     W2 scale of 8160 and a W13 scale of -2^-13 in every expert, and x =
     65280 in a column whose W13 weights are zero (so h stays ordinary)."""
     _log("4bit-range", case)
-    fmt = "nvfp4" if case == "nvfp4_nan_scale" else "int4"
-    spec = (SMALL["nvfp4_lora_small"][0] if fmt == "nvfp4" else SMALL["int4_small"][0]) \
+    base = {"nvfp4_nan_scale": "nvfp4_lora_small", "mxfp4a8_nan_scale": "mxfp4a8_small"}
+    spec = SMALL[base.get(case, "int4_small")][0] \
         .scaled(name=f"range_{case}", cfg_id=52, lora_rank=0, lora_down=False)
     layer = make_layer(spec)
     batch = make_batch(spec, layer, 24)
@@ -506,6 +544,11 @@ def test_4bit_range_problems_set_error_bits(case):
         s = layer.w13_s.clone().view(torch.uint8)
         s[:, 5, 3] = 0xFF
         layer.w13_s = s.view(torch.float8_e4m3fn)
+        want = M.MOE_DEVERR_W4_SCALE
+    elif case == "mxfp4a8_nan_scale":    # e8m0 0xFF (NaN) in the block-scaled GEMM1
+        s = layer.w13_s.clone()
+        s[:, 5, 3] = 0xFF
+        layer.w13_s = s
         want = M.MOE_DEVERR_W4_SCALE
     elif case == "x_beyond_f16":
         x[3, 17] = 1e5

@@ -354,9 +354,43 @@ def test_rounding_alternatives_bf16():
     alt = O.rounding_alternatives(h, np.full_like(h, 1e-12), "bf16")
     np.testing.assert_allclose(alt[0, 0], 2.0 ** -7, rtol=1e-3)
     assert alt[0, 1] == 0 and alt[0, 2] == 0
-    # an error band wider than the grid: every rounding inside it is allowed
-    alt = O.rounding_alternatives(np.array([[5.6e-7]]), np.array([[1e-6]]), "bf16")
-    assert alt[0, 0] >= 2e-6
+
+
+_BF16_CODES = np.array([c for c in range(1 << 16) if (c & 0x7F80) != 0x7F80])
+_BF16_VALS = O.bf16_decode(_BF16_CODES.astype(np.uint16))
+
+
+def _bf16_brute(v, near):
+    """Nearest bf16 value by search over the finite bit patterns' values
+    within `near` of the samples (ties to the even pattern): independent of
+    bf16_round."""
+    v = np.asarray(v, np.float64)
+    keep = (_BF16_VALS >= v.min() - near) & (_BF16_VALS <= v.max() + near)
+    vals, codes = _BF16_VALS[keep], _BF16_CODES[keep]
+    d = np.abs(vals[None, :] - v[:, None])
+    best = d.min(axis=1, keepdims=True)
+    cand = np.where(d == best, codes[None, :], 1 << 20)
+    even = np.where((cand & 1) == 0, cand, 1 << 20).min(axis=1)
+    pick = np.where(even < (1 << 20), even, cand.min(axis=1))
+    return O.bf16_decode(pick.astype(np.uint16))
+
+
+@pytest.mark.parametrize("h,err", [
+    (5.6e-7, 1e-6),            # a band wider than the grid
+    (0.0, 5e-6), (-0.0, 5e-6), # around zero the grid is far finer than at 1
+    (0.5, 2.0 ** -11),         # just below a power of two the spacing halves
+    (0.5 - 2.0 ** -10, 2.0 ** -12), (-2.0, 2.0 ** -8), (1.0 + 2.0 ** -9, 1e-9),
+    (3.0, 1e-3), (1e-39, 1e-40)])
+def test_rounding_alternatives_bf16_cover_every_rounding_in_the_band(h, err):
+    """The bound equals the largest |bf16(v) - bf16(h)| over v in
+    [h - err, h + err], found by sampling the band densely and rounding each
+    sample by exhaustive search."""
+    alt = O.rounding_alternatives(np.array([[h]]), np.array([[err]]), "bf16")[0, 0]
+    e = err + abs(h) * O.EVAL_REL
+    v = h + np.linspace(-e, e, 4001)
+    near = 2 * e + abs(h) / 64 + 1e-37          # more than one grid step
+    dev = np.abs(_bf16_brute(v, near) - _bf16_brute(np.array([h]), near)[0]).max()
+    assert dev <= alt <= dev * (1 + 1e-9) + 1e-300
 
 
 def test_allowance_is_zero_or_small_and_value_unchanged():
