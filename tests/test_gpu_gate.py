@@ -114,6 +114,7 @@ GATE_CASES = [
     # (config, T, bias, logit_std): split path below 96 tiles of 32 tokens,
     # one fused launch from 3072 tokens; ragged tails; every column count
     ("ep_lora_258", 1, True, 1.0), ("ep_lora_258", 3, False, 1.0),
+    ("ep_lora_258", 2, False, 4.0), ("fp8_oai_128_skew", 2, True, 1.0),
     ("ep_lora_258", 37, True, 1.0), ("ep_lora_258", 512, True, 1.0),
     ("ep_lora_258", 3109, True, 1.0), ("ep_lora_258", 8192, True, 1.0),
     ("ep_lora_258", 4096, False, 4.0), ("ep_lora_258", 700, True, 12.0),
@@ -207,6 +208,69 @@ def test_gate_route_ties_go_to_the_lower_column():
             for lo, hi in ((10, 200), (17, 18), (5, 99)):
                 if hi in row:
                     assert lo in row and row.index(lo) < row.index(hi)
+
+
+def test_gate_route_decode_workspace_reuse_and_replay():
+    """At decode sizes the split partial sums live in the workspace, which
+    needs no initialisation: a workspace full of 0xFF bytes, further calls
+    on the same workspace (with another call on another workspace in
+    between) and replays of a captured HIP graph, with eager work on the
+    same workspace between them, all give the first call's outputs bit for
+    bit."""
+    spec = CONFIGS["ep_lora_258"]
+    N, S, k, H = spec.n_routed, spec.n_sink, spec.top_k, spec.H
+    gate = make_gate(spec)
+    wg, b = gate.wg.cuda(), gate.bias.cuda()
+    dev = dict(device="cuda")
+    for T in (1, 2):
+        _log("gate_route workspace reuse", T)
+        x = make_tokens(spec, T).cuda()
+        x2 = make_tokens(spec, T, seed_extra=3).cuda()
+        nb = M.moe_gate_route_workspace_size(T, H, N, S)
+        ws = torch.full((nb,), 0xFF, dtype=torch.uint8, **dev)
+        ws2 = torch.full((nb,), 0x00, dtype=torch.uint8, **dev)
+        outs = dict(ids=torch.empty(T, k, dtype=torch.int32, **dev),
+                    w=torch.empty(T, k, **dev), sw=torch.empty(T, S, **dev),
+                    lg=torch.empty(T, N + S, **dev),
+                    packed=torch.empty(T, k, dtype=torch.int32, **dev))
+
+        def call(xx, o, w_s):
+            M.moe_gate_route(xx, wg, N, S, k, 2.6, 4.0, o["ids"], o["w"], o["sw"],
+                             sel_bias=b, logits=o["lg"], packed=o["packed"], ws=w_s)
+
+        def scrub():
+            for v in outs.values():
+                v.fill_(-7)
+
+        call(x, outs, ws)
+        torch.cuda.synchronize()
+        ref = {n: v.clone() for n, v in outs.items()}
+        other = {n: torch.empty_like(v) for n, v in outs.items()}
+        for rep in range(3):
+            scrub()
+            call(x2, other, ws2)
+            call(x, outs, ws)
+            torch.cuda.synchronize()
+            for n, v in ref.items():
+                assert torch.equal(outs[n], v), (T, rep, n)
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            call(x, outs, ws)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            call(x, outs, ws)
+        torch.cuda.synchronize()
+        for rep in range(5):
+            scrub()
+            g.replay()
+            torch.cuda.synchronize()
+            for n, v in ref.items():
+                assert torch.equal(outs[n], v), (T, "replay", rep, n)
+            call(x2, other, ws)          # eager work on the same workspace
+            torch.cuda.synchronize()
 
 
 def test_gate_route_empty_and_no_workspace_for_large_T():
