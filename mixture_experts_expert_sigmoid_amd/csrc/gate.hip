@@ -24,13 +24,16 @@
 // tokens the K range is split over workgroups that write fp32 partial sums,
 // and a second kernel adds them in split order and runs the same epilogue.
 //
-// Epilogue: one 16-lane group per token row (one DPP row: max, min and sum
-// over the group take four steps). Lane l of a group holds columns l,
-// l + 16, ...; each of the k passes takes the group maximum of the lanes'
-// best untaken keys, then the lowest column holding it, so equal keys go to
-// the lower column; the owner lane marks it taken and publishes the raw
-// logit. Then lane j < k holds slot j, lanes k .. k + S - 1 the sinks, and
-// the renormalisation is a group max and a group sum.
+// Epilogue: with a selection bias the ranking keys sigmoid(logit) + bias
+// (fp64-evaluated sigmoid, see sigmoid_key) are computed first by the whole
+// workgroup into LDS, one key per thread and pass; then one 16-lane group
+// per token row (one DPP row: max, min and sum over the group take four
+// steps). Lane l of a group holds columns l, l + 16, ...; each of the k
+// passes takes the group maximum of the lanes' best untaken keys, then the
+// lowest column holding it, so equal keys go to the lower column; the owner
+// lane marks it taken and publishes the raw logit. Then lane j < k holds
+// slot j, lanes k .. k + S - 1 the sinks, and the renormalisation is a group
+// max and a group sum.
 #include <algorithm>
 
 #include "common.h"
@@ -140,21 +143,30 @@ __device__ __forceinline__ void gate_gemm(const GateP& P, f32x4 (&acc)[NQ][2],
 }
 
 // ------------------------------------------------------------ epilogue --
+// Ranking keys of rows 0 .. rows - 1 (logits in LDS at L, pitch LP) into
+// LDS at Kd (same pitch), computed by the whole workgroup: sigmoid(logit) +
+// bias[c] over the routed columns. Only with a selection bias (without one
+// the key is the raw logit and the rows are ranked in place).
+__device__ __forceinline__ void gate_keys(const GateP& P, const float* L, float* Kd, int LP,
+                                          int rows) {
+  for (int r = 0; r < rows; ++r)
+    for (int c = threadIdx.x; c < P.n_routed; c += kGThreads)
+      Kd[r * LP + c] = sigmoid_key(L[r * LP + c]) + P.bias[c];
+}
+
 // One token row per 16-lane group. L points at the row's fp32 logits in LDS
-// (columns 0 .. NC - 1 valid). NV >= ceil(n_routed / 16). Taken and
-// non-candidate columns hold key -inf; the winner's raw logit is read back
-// from L.
+// (columns 0 .. NC - 1 valid), Kr at its ranking keys (gate_keys; L itself
+// without a bias). NV >= ceil(n_routed / 16). Taken and non-candidate
+// columns hold key -inf; the winner's raw logit is read back from L.
 template <int NV>
-__device__ __forceinline__ void route_row16(const GateP& P, const float* L, long row,
-                                            bool row_ok) {
+__device__ __forceinline__ void route_row16(const GateP& P, const float* L, const float* Kr,
+                                            long row, bool row_ok) {
   const int lr = threadIdx.x & 15;
   float key[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int c = lr + 16 * i;
-    const bool cand = c < P.n_routed;
-    const float raw = cand ? L[c] : 0.0f;
-    key[i] = !cand ? -INFINITY : P.bias ? sigmoid_key(raw) + P.bias[c] : raw;
+    key[i] = c < P.n_routed ? Kr[c] : -INFINITY;
   }
   float my_x = 0.0f;
   int my_c = 0;
@@ -189,6 +201,7 @@ __device__ __forceinline__ void route_row16(const GateP& P, const float* L, long
 
 // ------------------------------------------------------------- kernels --
 // S == 1: GEMM over the whole K, logits to LDS, epilogue for the 32 rows.
+// LDS: the logits [kGBM][LP], then (with a bias) their keys [kGBM][LP].
 template <int NQ>
 __global__ __launch_bounds__(kGThreads) void gate_fused_kernel(GateP P) {
   extern __shared__ __attribute__((aligned(16))) float sl[];
@@ -206,18 +219,23 @@ __global__ __launch_bounds__(kGThreads) void gate_fused_kernel(GateP P) {
       *(f32x4*)(sl + (16 * ts + lr) * LP + 16 * (4 * j + wave) + 4 * lg) = acc[j][ts];
   }
   __syncthreads();
+  const int rows = (int)min((long)kGBM, P.T - t0);
   if (P.logits) {
-    const int rows = (int)min((long)kGBM, P.T - t0);
     for (int i = threadIdx.x; i < rows * P.NC; i += kGThreads) {
       const int r = i / P.NC, c = i - r * P.NC;
       P.logits[(t0 + r) * P.NC + c] = sl[r * LP + c];
     }
   }
+  float* sk = P.bias ? sl + kGBM * LP : sl;
+  if (P.bias) {
+    gate_keys(P, sl, sk, LP, rows);
+    __syncthreads();
+  }
   const int grp = threadIdx.x >> 4;                // 0..15
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const int r = 16 * half + grp;
-    route_row16<4 * NQ>(P, sl + r * LP, t0 + r, t0 + r < P.T);
+    route_row16<4 * NQ>(P, sl + r * LP, sk + r * LP, t0 + r, t0 + r < P.T);
   }
 }
 
@@ -247,6 +265,7 @@ __global__ __launch_bounds__(kGThreads) void gate_part_kernel(GateP P) {
 // S > 1: add the partial sums in split order for kGRows rows, then the
 // epilogue. Each thread owns one 4-column chunk of one row at a time and
 // issues the loads of all its splits before adding them in split order.
+// LDS: the logits [kGRows][LP], then (with a bias) their keys.
 template <int NQ>
 __global__ __launch_bounds__(kGThreads) void gate_reduce_route_kernel(GateP P) {
   extern __shared__ __attribute__((aligned(16))) float sl[];
@@ -273,9 +292,14 @@ __global__ __launch_bounds__(kGThreads) void gate_reduce_route_kernel(GateP P) {
     }
   }
   __syncthreads();
+  float* sk = P.bias ? sl + kGRows * LP : sl;
+  if (P.bias) {
+    gate_keys(P, sl, sk, LP, rows);
+    __syncthreads();
+  }
   const int grp = threadIdx.x >> 4;
   if (grp < kGRows)                                 // whole 16-lane groups
-    route_row16<4 * NQ>(P, sl + grp * LP, t0 + grp, grp < rows);
+    route_row16<4 * NQ>(P, sl + grp * LP, sk + grp * LP, t0 + grp, grp < rows);
 }
 
 int splits_for(long T, int H) {
@@ -292,13 +316,14 @@ template <int NQ>
 hipError_t run_gate(GateP& P, hipStream_t s) {
   const unsigned tiles = (unsigned)((P.T + kGBM - 1) / kGBM);
   const int LP = 16 * P.NS + 4;
+  const int nb = P.bias ? 2 : 1;                 // logits (+ keys)
   if (P.S == 1) {
-    const size_t shm = (size_t)kGBM * LP * 4;   // <= 32 * 516 * 4 bytes
+    const size_t shm = (size_t)nb * kGBM * LP * 4;   // <= 2 * 32 * 516 * 4 bytes
     static bool attr = false;
     if (!attr) {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gate_fused_kernel<NQ>),
                                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         kGBM * (16 * 4 * NQ + 4) * 4);
+                                         2 * kGBM * (16 * 4 * NQ + 4) * 4);
       if (e != hipSuccess) return e;
       attr = true;
     }
@@ -310,7 +335,7 @@ hipError_t run_gate(GateP& P, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned rb = (unsigned)((P.T + kGRows - 1) / kGRows);
-  const size_t shm = (size_t)kGRows * LP * 4;
+  const size_t shm = (size_t)nb * kGRows * LP * 4;
   hipLaunchKernelGGL(gate_reduce_route_kernel<NQ>, dim3(rb), dim3(kGThreads), shm, s, P);
   return hipGetLastError();
 }
