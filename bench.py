@@ -369,9 +369,12 @@ def gate_route_table(steps, stream):
     """moe_gate_route (router GEMM fused with the gate epilogue: selection
     bias, raw-logit carry, two sinks, packed output) on the 258-column gate
     of the ep_lora_258 layer (H = 2048). Per-call time (HIP events on the
-    launching stream), algorithmic bytes (x once, the router weight once,
-    ids / weights / packed / sink weights written) as GB/s and % of 8 TB/s,
-    and 2 T C H flop as % of the bf16 MFMA peak."""
+    launching stream around each call, so host submission counts when the
+    GPU outruns it), the GPU time per call from replays of a captured HIP
+    graph of 20 calls (us_per_call_graph), algorithmic bytes (x once, the
+    router weight once, ids / weights / packed / sink weights written) as
+    GB/s and % of 8 TB/s, and 2 T C H flop as % of the bf16 MFMA peak; the
+    rates use the per-call time."""
     import torch
     import mixture_experts_expert_sigmoid_amd as M
     from synth import CONFIGS, make_gate, make_tokens
@@ -393,18 +396,36 @@ def gate_route_table(steps, stream):
         for _ in range(5):
             f()
         ms = time_calls(f, steps, stream)
+        reps = 20
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                f()
+        g.replay()
+        torch.cuda.synchronize()
+        cur = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(cur)
+        for _ in range(5):
+            g.replay()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        us_graph = e0.elapsed_time(e1) / (5 * reps) * 1e3
+        del g
         byts = T * H * 2 + (N + S) * H * 2 + T * (k * 12 + S * 4)
         flops = 2.0 * T * (N + S) * H
         gbs = byts / (ms * 1e-3) / 1e9
         tfl = flops / (ms * 1e-3) / 1e12
         out.append({"T": T, "us_per_call": round(ms * 1e3, 2),
+                    "us_per_call_graph": round(us_graph, 2),
                     "tokens_per_s": round(T / (ms * 1e-3), 1),
                     "path": "fused" if nb == 0 else "split-K + epilogue kernel",
                     "algorithmic_bytes": byts, "gbs": round(gbs, 1),
                     "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
                     "tflops": round(tfl, 2),
                     "pct_bf16_mfma_peak": round(100 * tfl / BF16_PEAK_TFLOPS, 2)})
-        print(f"# gate_route T={T}: {ms * 1e3:.2f} us/call", file=sys.stderr, flush=True)
+        print(f"# gate_route T={T}: {ms * 1e3:.2f} us/call, {us_graph:.2f} us/call "
+              f"from graph replays", file=sys.stderr, flush=True)
     return out
 
 
