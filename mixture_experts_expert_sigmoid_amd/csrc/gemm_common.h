@@ -91,11 +91,12 @@ template <int BM>
 __device__ __forceinline__ void tile_prefix(const int* offsets, int G, int* s_cum,
                                             int* s_wsum) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int c0 = 0, c1 = 0;
-  const int g0 = 2 * tid, g1 = 2 * tid + 1;
-  if (g0 < G) c0 = (offsets[g0 + 1] - offsets[g0] + BM - 1) / BM;
-  if (g1 < G) c1 = (offsets[g1 + 1] - offsets[g1] + BM - 1) / BM;
-  int v = c0 + c1, incl = v;
+  const int q = (kMaxGroups + (int)blockDim.x - 1) / (int)blockDim.x;   // groups per thread
+  auto tiles_of = [&](int g) { return (offsets[g + 1] - offsets[g] + BM - 1) / BM; };
+  int v = 0;
+  for (int i = 0; i < q; ++i)
+    if (tid * q + i < G) v += tiles_of(tid * q + i);
+  int incl = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     int t = __shfl_up(incl, o, 64);
@@ -103,14 +104,16 @@ __device__ __forceinline__ void tile_prefix(const int* offsets, int G, int* s_cu
   }
   if (lane == 63) s_wsum[wave] = incl;
   __syncthreads();
-  int base = 0;
-  for (int i = 0; i < wave; ++i) base += s_wsum[i];
-  int excl = base + incl - v;
-  if (g0 < G) s_cum[g0] = excl;
-  if (g1 < G) s_cum[g1] = excl + c0;
+  int run = incl - v;
+  for (int i = 0; i < wave; ++i) run += s_wsum[i];
+  for (int i = 0; i < q; ++i)
+    if (tid * q + i < G) {
+      s_cum[tid * q + i] = run;
+      run += tiles_of(tid * q + i);
+    }
   if (tid == 0) {
     int tot = 0;
-    for (int i = 0; i < 8; ++i) tot += s_wsum[i];
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) tot += s_wsum[i];
     s_cum[G] = tot;
   }
   __syncthreads();
@@ -190,7 +193,7 @@ __device__ __forceinline__ int group_of_row(const int* s_off, int G, int r) {
 // GEMM2: lo/hi = output columns nt*256.. and nt*256+128.. (hi = lo if ragged).
 template <int BM, bool G1>
 __device__ __forceinline__ Tile decode_tile(const GemmParams& P, int lt, int NT,
-                                            const int* s_cum) {
+                                            const int* s_cum, int w2 = 256) {
   Tile t;
   const int mt = lt / NT;
   t.nt = lt - mt * NT;
@@ -206,8 +209,8 @@ __device__ __forceinline__ Tile decode_tile(const GemmParams& P, int lt, int NT,
     t.n_lo = t.nt * 128;
     t.n_hi = P.I + t.nt * 128;
   } else {
-    t.n_lo = t.nt * 256;
-    t.n_hi = (t.n_lo + 128 < P.N) ? t.n_lo + 128 : t.n_lo;
+    t.n_lo = t.nt * w2;
+    t.n_hi = (t.n_lo + w2 / 2 < P.N) ? t.n_lo + w2 / 2 : t.n_lo;
   }
   return t;
 }

@@ -64,12 +64,12 @@ constexpr int kF8Stages = 4;
 
 // F8: the activation block stays e4m3 (128-byte rows) for the FP8 MFMA;
 // otherwise it is expanded to bf16 (256-byte rows)
-template <int BM, bool F8>
+template <int BM, bool F8, int NTH = kThreads>
 struct F8Geo {
   static constexpr int MS = BM / 16;                       // 16-row subtiles
   static constexpr int A_BYTES = BM * (F8 ? 128 : 256);    // one K block
   static constexpr int A_CH = BM * 8;                      // 16-byte code chunks
-  static constexpr int A_PT = (A_CH + kThreads - 1) / kThreads;
+  static constexpr int A_PT = (A_CH + NTH - 1) / NTH;
   static constexpr int X_BYTES = BM * 4;                   // row scales, [16][MS]
   static constexpr int STAGE = A_BYTES + X_BYTES;
   static constexpr int LDS = kF8Stages * STAGE;
@@ -210,15 +210,16 @@ __device__ __forceinline__ void fp8_epilogue(const GemmParams& P, const Tile& t,
 // it pays where registers allow (kernels whose largest row class is 64 or
 // less) and spills in the 128-row class. PART: the block-scaled fp32 sums
 // go to partial slot `slot` instead of the epilogue (stream-K).
-template <int BM, bool G1, bool DEEP, bool PART, bool LORA>
+template <int BM, bool G1, bool DEEP, bool PART, bool LORA, int NTH = kThreads>
 __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, uint8_t* smem,
                                          int k0, int k1, int slot = 0) {
+  static_assert(NTH == kThreads || (!G1 && !LORA && !PART), "4-wave tiles: plain GEMM2 only");
   // GEMM2 runs on the FP8 MFMA: its fp32 output feeds only the weighted
   // combine, where the FP8 MFMA's reduced-precision accumulation stays far
   // inside the output tolerance; GEMM1 keeps the exact bf16 path because its
   // output is re-quantised to e4m3.
   constexpr bool F8 = !G1;
-  using Gm = F8Geo<BM, F8>;
+  using Gm = F8Geo<BM, F8, NTH>;
   constexpr int MS = Gm::MS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -231,7 +232,7 @@ __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, ui
   int a_st[Gm::A_PT];
 #pragma unroll
   for (int i = 0; i < Gm::A_PT; ++i) {
-    const int cc = min(tid + i * kThreads, Gm::A_CH - 1);
+    const int cc = min(tid + i * NTH, Gm::A_CH - 1);
     const int row = cc >> 3, ch = cc & 7;
     ap[i] = P.a + a_source_row<G1>(P, row0 + (row < m ? row : 0)) * P.a_ld + ch * 16;
     a_st[i] = F8 ? row * 128 + 16 * (ch ^ swz8(row)) : row * 256;
@@ -265,8 +266,8 @@ __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, ui
     uint8_t* st = smem + buf * Gm::STAGE;
 #pragma unroll
     for (int i = 0; i < Gm::A_PT; ++i) {
-      if (Gm::A_CH % kThreads == 0 || tid + i * kThreads < Gm::A_CH) {
-        const int cc = tid + i * kThreads, row = cc >> 3, ch = cc & 7;
+      if (Gm::A_CH % NTH == 0 || tid + i * NTH < Gm::A_CH) {
+        const int cc = tid + i * NTH, row = cc >> 3, ch = cc & 7;
         const i32x4 v = ra[i];
         if constexpr (F8) {
           *(i32x4*)(st + a_st[i]) = v;
@@ -483,17 +484,18 @@ __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, ui
 // The tiles (TBM-row scheduling, s_cum its prefix) walked by persistent
 // workgroups: XCD x (= blockIdx % 8) owns logical tiles [x*chunk,
 // (x+1)*chunk), so the N-tiles of one expert share an L2.
-template <int TBM, bool G1, bool LORA>
+template <int TBM, bool G1, bool LORA, int NTH>
 __device__ __forceinline__ void plain_tiles(const GemmParams& P, uint8_t* smem,
                                             const int* s_cum) {
-  const int NT = G1 ? (P.I >> 7) : ((P.N + 255) >> 8);
+  constexpr int W2 = NTH / 2;                // GEMM2 tile columns: 16 per wave and half
+  const int NT = G1 ? (P.I >> 7) : ((P.N + W2 - 1) / W2);
   const int NS = P.K >> 7;
   const int total = s_cum[P.G] * NT;
   const int xcd = blockIdx.x & 7, nper = gridDim.x >> 3, slot = blockIdx.x >> 3;
   const int chunk = (total + 7) >> 3;
   const int t_end = min(total, (xcd + 1) * chunk);
   for (int lt = xcd * chunk + slot; lt < t_end; lt += nper) {
-    Tile tl = decode_tile<TBM, G1>(P, lt, NT, s_cum);
+    Tile tl = decode_tile<TBM, G1>(P, lt, NT, s_cum, W2);
     tl.g = __builtin_amdgcn_readfirstlane(tl.g);
     tl.row0 = __builtin_amdgcn_readfirstlane(tl.row0);
     tl.m = __builtin_amdgcn_readfirstlane(tl.m);
@@ -501,22 +503,30 @@ __device__ __forceinline__ void plain_tiles(const GemmParams& P, uint8_t* smem,
     tl.n_lo = __builtin_amdgcn_readfirstlane(tl.n_lo);
     tl.n_hi = __builtin_amdgcn_readfirstlane(tl.n_hi);
     if constexpr (TBM >= 128) {
-      if (tl.m > 64) { fp8_tile<128, G1, false, false, LORA>(P, tl, smem, 0, NS); continue; }
-    }
-    if constexpr (TBM >= 64) {
-      if (tl.m > 32) {
-        fp8_tile<64, G1, G1 && TBM <= 64, false, LORA>(P, tl, smem, 0, NS);
+      if (tl.m > 64) {
+        fp8_tile<128, G1, false, false, LORA, NTH>(P, tl, smem, 0, NS);
         continue;
       }
     }
-    fp8_tile<32, G1, G1 && TBM <= 64, false, LORA>(P, tl, smem, 0, NS);
+    if constexpr (TBM >= 64) {
+      if (tl.m > 32) {
+        fp8_tile<64, G1, G1 && TBM <= 64, false, LORA, NTH>(P, tl, smem, 0, NS);
+        continue;
+      }
+    }
+    fp8_tile<32, G1, G1 && TBM <= 64, false, LORA, NTH>(P, tl, smem, 0, NS);
   }
 }
 
 // LORA: the kernel carries the LoRA delta (and the bf16 down-LoRA input of
 // GEMM1); layers without LoRA run the instantiation without that code.
-template <int TBM, bool G1, bool LORA>
-__global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
+// NTH: 512 threads (8 waves), or 256 (4 waves, 128-column GEMM2 tiles) for
+// the plain GEMM2 without LoRA at decode sizes (32-row tiles): twice the
+// tiles, so that a few experts' tiles still spread over the whole GPU, with
+// more workgroups per CU and independent barriers. (With 128-row tiles the
+// 256-column tiles are faster: half the activation reads.)
+template <int TBM, bool G1, bool LORA, int NTH>
+__global__ __launch_bounds__(NTH) void moe_gemm_fp8_kernel(GemmParams P) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // 2 stages
   __shared__ int s_cum[kMaxGroups + 1];
   __shared__ int s_wsum[8];
@@ -526,7 +536,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_kernel(GemmParams P) {
               P.K >> 7))
     return;
   tile_prefix<TBM>(P.offsets, P.G, s_cum, s_wsum);
-  plain_tiles<TBM, G1, LORA>(P, smem, s_cum);
+  plain_tiles<TBM, G1, LORA, NTH>(P, smem, s_cum);
 }
 
 // Split-K (stream-K) kernel over 32-row tiles (see gemm_common.h):
@@ -566,16 +576,18 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_sk_kernel(GemmParams P)
 
 template <int TBM, bool G1, bool LORA>
 static hipError_t run_fp8(const GemmParams& P, long p_cap, int NT, hipStream_t s) {
-  constexpr int shm = LORA ? std::max(F8Geo<TBM, !G1>::LDS, kLoraLds) : F8Geo<TBM, !G1>::LDS;
+  constexpr int NTH = (!G1 && !LORA && TBM <= 32) ? 256 : kThreads;
+  if (NTH != kThreads) NT = (P.N + NTH / 2 - 1) / (NTH / 2);
+  constexpr int shm = LORA ? std::max(F8Geo<TBM, !G1>::LDS, kLoraLds) : F8Geo<TBM, !G1, NTH>::LDS;
   static int per_cu = 0;   // resident workgroups per CU, per instantiation
   if (per_cu == 0) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&moe_gemm_fp8_kernel<TBM, G1, LORA>),
+        reinterpret_cast<const void*>(&moe_gemm_fp8_kernel<TBM, G1, LORA, NTH>),
         hipFuncAttributeMaxDynamicSharedMemorySize, shm);
     if (e != hipSuccess) return e;
     int nb = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &nb, reinterpret_cast<const void*>(&moe_gemm_fp8_kernel<TBM, G1, LORA>), kThreads, shm);
+        &nb, reinterpret_cast<const void*>(&moe_gemm_fp8_kernel<TBM, G1, LORA, NTH>), NTH, shm);
     if (e != hipSuccess) return e;
     per_cu = nb > 0 ? nb : 1;
   }
@@ -585,7 +597,7 @@ static hipError_t run_fp8(const GemmParams& P, long p_cap, int NT, hipStream_t s
   if (nwg == 0) return hipSuccess;
   GemmParams Q = P;
   Q.lds_bytes = shm;
-  moe_gemm_fp8_kernel<TBM, G1, LORA><<<dim3((unsigned)nwg), dim3(kThreads), shm, s>>>(Q);
+  moe_gemm_fp8_kernel<TBM, G1, LORA, NTH><<<dim3((unsigned)nwg), dim3(NTH), shm, s>>>(Q);
   return hipGetLastError();
 }
 
