@@ -157,6 +157,11 @@ SMALL = {
         name="fp8_clamp_dec", H=512, I=384, n_routed=24, cfg_id=22), 5),
     "fp8_oai_small": (CONFIGS["fp8_oai_128_skew"].scaled(
         name="fp8_oai_small", H=384, I=256, n_routed=16, cfg_id=23), 200),
+    # 600 routed experts + the shared one at T = 50: a decode-sized launch
+    # (32-row class, the 4-wave 128-column GEMM2 tiles) whose tile prefix
+    # covers more groups than the workgroup has threads
+    "fp8_many_groups": (CONFIGS["fp8_clamp_288"].scaled(
+        name="fp8_many_groups", H=256, I=256, n_routed=600, cfg_id=55), 50),
     "int4_small": (CONFIGS["int4_g32_64"].scaled(
         name="int4_small", H=512, I=256, n_routed=16, cfg_id=24), 100),
     "int4_decode": (CONFIGS["int4_g32_64"].scaled(
