@@ -85,8 +85,10 @@ constexpr int kLoraSlots = 16;           // most adapters staged per round
 // device-side tile schedule: M-tiles of BM rows per group, NT column tiles
 // ---------------------------------------------------------------------------
 
-// Fills s_cum[0..G] with the exclusive prefix of ceil(rows_g / BM) (needs
-// all 512 threads; G <= 1024).
+// Fills s_cum[0..G] with the exclusive prefix of ceil(rows_g / BM), called
+// by the whole workgroup (a multiple of 64 threads; s_wsum holds one int per
+// wave); G <= kMaxGroups, each thread taking kMaxGroups / blockDim.x
+// consecutive groups.
 template <int BM>
 __device__ __forceinline__ void tile_prefix(const int* offsets, int G, int* s_cum,
                                             int* s_wsum) {
@@ -190,7 +192,8 @@ __device__ __forceinline__ int group_of_row(const int* s_off, int G, int r) {
 
 // Logical tile lt -> group, first sorted row, valid rows, column halves.
 // GEMM1: lo = gate rows nt*128.., hi = up rows I + nt*128..;
-// GEMM2: lo/hi = output columns nt*256.. and nt*256+128.. (hi = lo if ragged).
+// GEMM2: lo/hi = output columns nt*w2.. and nt*w2 + w2/2.. (hi = lo if
+// ragged); w2 = 256 for 8-wave workgroups, 128 for 4-wave ones.
 template <int BM, bool G1>
 __device__ __forceinline__ Tile decode_tile(const GemmParams& P, int lt, int NT,
                                             const int* s_cum, int w2 = 256) {

@@ -28,19 +28,20 @@
 // 256 weight rows in two halves ("lo", "hi"). GEMM1: lo = gate rows
 // nt*128.., hi = the matching up rows I + nt*128.., so one tile yields 128
 // complete h columns, the FP8 re-quantisation group; GEMM2: lo/hi = output
-// columns nt*256.. and nt*256 + 128... Wave w computes all BM rows of
-// columns 16w..16w+15 of both halves: gate and up of one h element meet in
-// one lane, and every weight byte is used by exactly one wave, so weights
-// stream from HBM straight into registers (two K blocks in flight) and
-// never pass through LDS (GEMM1 expands them there once per block). The
-// activation block is staged in LDS (double buffered, one barrier per K
-// block) together with its rows' activation scales -- expanded to bf16 once
-// per workgroup for GEMM1, as raw codes for GEMM2 -- and read by all 8
-// waves. The weights are the MFMA's first operand, so a lane's partials
-// belong to one activation row and four consecutive weight columns: the
-// block scale of a partial is one product xs[row] * ws[half] per lane and
-// subtile, and the epilogue writes whole dwords of codes (GEMM1) or 16-byte
-// fp32 runs (GEMM2).
+// columns nt*256.. and nt*256 + 128.. (the decode-sized GEMM2 without LoRA
+// runs 4-wave workgroups of half that width, see moe_gemm_fp8_kernel).
+// Wave w computes all BM rows of columns 16w..16w+15 of both halves: gate
+// and up of one h element meet in one lane, and every weight byte is used
+// by exactly one wave, so weights stream from HBM straight into registers
+// (two K blocks in flight) and never pass through LDS (GEMM1 expands them
+// there once per block). The activation block is staged in LDS (a ring of
+// four stages, below) together with its rows' activation scales --
+// expanded to bf16 once per workgroup for GEMM1, as raw codes for GEMM2 --
+// and read by every wave. The weights are the MFMA's first operand, so a
+// lane's partials belong to one activation row and four consecutive weight
+// columns: the block scale of a partial is one product xs[row] * ws[half]
+// per lane and subtile, and the epilogue writes whole dwords of codes
+// (GEMM1) or 16-byte fp32 runs (GEMM2).
 //
 // K order inside a block: lane (r = l % 16, q = l / 16) feeds the MFMA with
 // elements 32q .. 32q + 31 of its row (bf16: 8 of them per 32-deep MFMA,
