@@ -50,7 +50,7 @@
 // rows; GEMM2: 256 output columns); wave w computes all BM rows of columns
 // 16w..16w+15 of both halves, weights go HBM -> registers (two 128-K blocks
 // in flight, 16 bytes per row and lane per block) and are expanded there;
-// the f16 activation block is staged in LDS (double buffered).
+// the f16 activation block is staged in LDS (a ring of four stages).
 #pragma once
 #include "act16_dev.h"
 #include "gemm_common.h"
