@@ -15,10 +15,13 @@
 //      popcount of lower lanes = stable rank); per-wave counts go to LDS and
 //      an exclusive prefix over the 16 waves gives each pair its rank inside
 //      the block and each block its per-group count.
-//   2. scan (one block): per group, exclusive prefix of the block counts;
-//      exclusive prefix over groups -> offsets; bases made absolute.
-//   3. scatter: sorted row = base[block][group] + rank; the always-on shared
-//      group takes pairs T*k + t at rows offsets[E_loc] + t.
+//   2. scan (one block): per group, exclusive prefix of the block counts
+//      (each group's thread reads its column of counts 32 blocks at a time,
+//      all loads in flight, and writes the prefixes back); exclusive prefix
+//      over groups -> offsets.
+//   3. scatter: sorted row = offsets[group] + prefix[block][group] + rank;
+//      the always-on shared group takes pairs T*k + t at rows
+//      offsets[E_loc] + t.
 #include "permute_dev.h"
 
 namespace moe {
@@ -79,14 +82,14 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(
   // per-group totals and exclusive per-block prefixes
   int total = 0;
   if (tid < E_loc) {
-    // 16 block counts in flight at a time (a dependent walk would pay one
+    // 32 block counts in flight at a time (a dependent walk would pay one
     // memory latency per block)
-    for (long b0 = 0; b0 < nblk; b0 += 16) {
-      int c[16];
+    for (long b0 = 0; b0 < nblk; b0 += 32) {
+      int c[32];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) c[i] = b0 + i < nblk ? blockcnt[(b0 + i) * G + tid] : 0;
+      for (int i = 0; i < 32; ++i) c[i] = b0 + i < nblk ? blockcnt[(b0 + i) * G + tid] : 0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
+      for (int i = 0; i < 32; ++i)
         if (b0 + i < nblk) {
           blockcnt[(b0 + i) * G + tid] = total;
           total += c[i];
@@ -109,8 +112,6 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(
   int excl = wbase + incl - total;
   if (tid < G) offsets[tid] = excl;
   if (tid == G - 1) offsets[G] = excl + total;
-  if (tid < E_loc)
-    for (long b = 0; b < nblk; ++b) blockcnt[b * G + tid] += excl;
 }
 
 __global__ __launch_bounds__(256) void permute_scatter_kernel(
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
     bool oob = false;
     int g = local_group(ids[p], E_global, off, E_loc, &oob);
     if (g >= 0) {
-      int pos = blockcnt[(p / kPermBlock) * G + g] + rank[p];
+      int pos = offsets[g] + blockcnt[(p / kPermBlock) * G + g] + rank[p];
       sorted_pair[pos] = (int)p;
       pair_row[p] = pos;
     } else {

@@ -291,10 +291,14 @@ def test_gate_route_empty_and_no_workspace_for_large_T():
     ("fp8_clamp_288", 4096, 1.0), ("int4_g32_64", 64, 1.0),
     # logits times 12 / 6: many keys in sigmoid's saturated and flushed
     # ranges, where fp32 sigmoid ties distinct logits
-    ("ep_lora_258", 512, 12.0), ("fp8_clamp_288", 4096, 6.0)])
+    ("ep_lora_258", 512, 12.0), ("fp8_clamp_288", 4096, 6.0),
+    # more reported slots per row (k + n_sink = 18) and more routed experts
+    ("k16_sink2", 300, 1.0), ("routed_600", 300, 6.0)])
 def test_route_bias_and_packed(name, T, lscale):
     _log("route bias", name, T, lscale)
-    spec = CONFIGS[name]
+    spec = {"k16_sink2": CONFIGS["ep_lora_258"].scaled(name="k16_sink2", top_k=16),
+            "routed_600": CONFIGS["fp8_clamp_288"].scaled(name="routed_600", n_routed=600),
+            }.get(name) or CONFIGS[name]
     N, S, k = spec.n_routed, spec.n_sink, spec.top_k
     lg = make_batch(spec, None, T).logits * lscale
     bias = make_gate(spec).bias

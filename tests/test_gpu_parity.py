@@ -29,13 +29,22 @@ def _log(*a):
 
 ROUTE_CASES = [("ep_lora_258", 1), ("ep_lora_258", 37), ("ep_lora_258", 512),
                ("ep_lora_258", 8192), ("fp8_clamp_288", 64), ("fp8_oai_128_skew", 4096),
-               ("int4_g32_64", 2048)]
+               ("int4_g32_64", 2048), ("k14_sink2", 300), ("routed_512", 300),
+               ("routed_600", 300), ("k16_sink2", 300)]
+# Beyond the five workloads: 512 and 600 routed experts (8 and 16 columns
+# per lane) and 16 or 18 reported slots per row.
+ROUTE_SPECS = {
+    "k14_sink2": CONFIGS["ep_lora_258"].scaled(name="k14_sink2", top_k=14),
+    "routed_512": CONFIGS["fp8_clamp_288"].scaled(name="routed_512", n_routed=512),
+    "routed_600": CONFIGS["fp8_clamp_288"].scaled(name="routed_600", n_routed=600),
+    "k16_sink2": CONFIGS["ep_lora_258"].scaled(name="k16_sink2", top_k=16),
+}
 
 
 @pytest.mark.parametrize("name,T", ROUTE_CASES)
 def test_route_parity(name, T):
     _log("route", name, T)
-    spec = CONFIGS[name]
+    spec = ROUTE_SPECS.get(name) or CONFIGS[name]
     lg = make_batch(spec, None, T).logits
     N, S, k = spec.n_routed, spec.n_sink, spec.top_k
     # padded rows exercise the row stride
