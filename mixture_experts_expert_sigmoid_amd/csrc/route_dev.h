@@ -34,6 +34,10 @@ __device__ __forceinline__ void route_row(
   const int lane = lane_id();
   const float* x = logits + row * ld;
 
+  // the sink logits are loaded with the row, not after the passes
+  const bool sink = lane >= k && lane < k + n_sink;
+  const float sink_x = sink ? x[n_routed + (lane - k)] : 0.0f;
+
   float v[NV], key[NV];
   uint32_t taken = 0;
 #pragma unroll
@@ -68,7 +72,7 @@ __device__ __forceinline__ void route_row(
     if (lane == j) { my_x = xw; my_c = bc; }
   }
   const bool active = lane < k + n_sink;
-  if (lane >= k && active) my_x = x[n_routed + (lane - k)];
+  if (sink) my_x = sink_x;
 
   // lp = logsigmoid(x) = min(x, 0) - log1p(exp(-|x|));
   // exp(lp - logsumexp(lp)) evaluated as e / sum(e) with e = exp(lp - max lp):
