@@ -38,15 +38,23 @@ __device__ __forceinline__ void route_row(
   const bool sink = lane >= k && lane < k + n_sink;
   const float sink_x = sink ? x[n_routed + (lane - k)] : 0.0f;
 
-  float v[NV], key[NV];
+  // All of the row's loads are issued before any of them is used: a
+  // lane past the last routed column re-reads that column (n_routed >= 1),
+  // so the loads need no branch, and no wait sits between two of them.
+  float v[NV], key[NV], b[NV];
   uint32_t taken = 0;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    int c = lane + 64 * i;
-    v[i] = (c < n_routed) ? x[c] : 0.0f;
-    if (c >= n_routed) taken |= 1u << i;   // not a candidate
+    const int c = min(lane + 64 * i, n_routed - 1);
+    v[i] = x[c];
+    b[i] = bias ? bias[c] : 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + 64 * i;
+    if (c >= n_routed) { taken |= 1u << i; v[i] = 0.0f; }   // not a candidate
     // with a selection bias the key is fp32 sigmoid(x) + bias
-    key[i] = bias ? sigmoid_key(v[i]) + bias[c < n_routed ? c : 0] : v[i];
+    key[i] = bias ? sigmoid_key(v[i]) + b[i] : v[i];
   }
 
   float my_x = -INFINITY;   // raw logit of the slot / sink this lane reports
