@@ -45,6 +45,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
 // the GEMM built it (32-row tiles, 256-column tiles, I / 128 K blocks). One
 // workgroup per (token, 2048 columns); its token's pairs are looked up once.
 constexpr int kCsCols = 2048;
+constexpr int kCsPairs = 4;
 __global__ __launch_bounds__(512) void combine_sk_kernel(
     const float* __restrict__ part, long T, int H, int top_k, int shared,
     const int* __restrict__ pair_row, const float* __restrict__ topk_w,
@@ -85,19 +86,36 @@ __global__ __launch_bounds__(512) void combine_sk_kernel(
   if (col >= H) return;
   const int nt = col >> 8;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < np; ++j) {               // ascending slot, shared last
-    const int r = s_row[j];
-    if (r < 0) continue;
-    const int nsl = split ? sk_nslots(((long)s_mt[j] * NT + nt) * NS, NS, U, W) : 1;
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    for (int sl = 0; sl < nsl; ++sl) {
-      const f32x4 p = *(const f32x4*)(part + ((long)sl * p_rows + r) * H + col);
+  // pairs kCsPairs at a time (ascending slot, shared last): the partial
+  // slots of all of them are loaded first, then summed per pair in slot
+  // order and accumulated in pair order
+  for (int j0 = 0; j0 < np; j0 += kCsPairs) {
+    int nsl[kCsPairs];
+    f32x4 p[kCsPairs][kSkSlots];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] += p[q];
+    for (int u = 0; u < kCsPairs; ++u) {
+      const int j = j0 + u;
+      const int r = j < np ? s_row[j] : -1;
+      nsl[u] = r < 0 ? 0
+                     : split ? sk_nslots(((long)s_mt[j] * NT + nt) * NS, NS, U, W) : 1;
+#pragma unroll
+      for (int sl = 0; sl < kSkSlots; ++sl)
+        if (sl < nsl[u]) p[u][sl] = *(const f32x4*)(part + ((long)sl * p_rows + r) * H + col);
     }
-    const float wj = s_w[j];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[q] = fmaf(wj, v[q], acc[q]);
+    for (int u = 0; u < kCsPairs; ++u) {
+      if (nsl[u] == 0) continue;
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int sl = 0; sl < kSkSlots; ++sl)
+        if (sl < nsl[u]) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] += p[u][sl][q];
+        }
+      const float wj = s_w[j0 + u];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = fmaf(wj, v[q], acc[q]);
+    }
   }
   *(f32x4*)(out + t * H + col) = acc;
 }

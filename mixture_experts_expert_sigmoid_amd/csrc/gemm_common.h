@@ -86,32 +86,41 @@ constexpr int kLoraSlots = 16;           // most adapters staged per round
 // ---------------------------------------------------------------------------
 
 // Fills s_cum[0..G] with the exclusive prefix of ceil(rows_g / BM), called
-// by the whole workgroup (a multiple of 64 threads; s_wsum holds one int per
-// wave); G <= kMaxGroups, each thread taking kMaxGroups / blockDim.x
-// consecutive groups.
+// by the whole workgroup (a multiple of 64 threads, at least 256; s_wsum
+// holds one int per wave); G <= kMaxGroups, each thread taking
+// kMaxGroups / blockDim.x consecutive groups.
 template <int BM>
 __device__ __forceinline__ void tile_prefix(const int* offsets, int G, int* s_cum,
                                             int* s_wsum) {
+  constexpr int QMAX = kMaxGroups / 256;     // workgroups of at least 256 threads
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = (kMaxGroups + (int)blockDim.x - 1) / (int)blockDim.x;   // groups per thread
-  auto tiles_of = [&](int g) { return (offsets[g + 1] - offsets[g] + BM - 1) / BM; };
+  // the thread's q + 1 offsets, all loads issued before the first use
+  // (indices past G re-read offsets[G])
+  int o[QMAX + 1], tl[QMAX];
+#pragma unroll
+  for (int i = 0; i <= QMAX; ++i) o[i] = i <= q ? offsets[min(tid * q + i, G)] : 0;
   int v = 0;
-  for (int i = 0; i < q; ++i)
-    if (tid * q + i < G) v += tiles_of(tid * q + i);
+#pragma unroll
+  for (int i = 0; i < QMAX; ++i) {
+    tl[i] = (i < q && tid * q + i < G) ? (o[i + 1] - o[i] + BM - 1) / BM : 0;
+    v += tl[i];
+  }
   int incl = v;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
+  for (int d = 1; d < 64; d <<= 1) {
+    int t = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += t;
   }
   if (lane == 63) s_wsum[wave] = incl;
   __syncthreads();
   int run = incl - v;
   for (int i = 0; i < wave; ++i) run += s_wsum[i];
-  for (int i = 0; i < q; ++i)
-    if (tid * q + i < G) {
+#pragma unroll
+  for (int i = 0; i < QMAX; ++i)
+    if (i < q && tid * q + i < G) {
       s_cum[tid * q + i] = run;
-      run += tiles_of(tid * q + i);
+      run += tl[i];
     }
   if (tid == 0) {
     int tot = 0;

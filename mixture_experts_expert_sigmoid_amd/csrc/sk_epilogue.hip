@@ -38,12 +38,22 @@ __global__ __launch_bounds__(kThreads) void gemm1_sk_epilogue_kernel(GemmParams 
     const int nsl = sk_nslots(((long)mt * NT + nt) * NS, NS, U, W);
     const int c = nt * 128 + 2 * lane;
     float a[2][2] = {{0.f, 0.f}, {0.f, 0.f}};       // [gate | up][column]
-    for (int sl = 0; sl < nsl; ++sl) {
-      const float* pr = P.part + ((long)sl * P.p_rows + r) * P.N;
-      const f32x2 vg = *(const f32x2*)(pr + c), vu = *(const f32x2*)(pr + I + c);
-      a[0][0] += vg[0]; a[0][1] += vg[1];
-      a[1][0] += vu[0]; a[1][1] += vu[1];
-    }
+    // the tile's slots (at most kSkSlots): every load issued, then the
+    // additions in slot order
+    f32x2 vg[kSkSlots], vu[kSkSlots];
+#pragma unroll
+    for (int sl = 0; sl < kSkSlots; ++sl)
+      if (sl < nsl) {
+        const float* pr = P.part + ((long)sl * P.p_rows + r) * P.N;
+        vg[sl] = *(const f32x2*)(pr + c);
+        vu[sl] = *(const f32x2*)(pr + I + c);
+      }
+#pragma unroll
+    for (int sl = 0; sl < kSkSlots; ++sl)
+      if (sl < nsl) {
+        a[0][0] += vg[sl][0]; a[0][1] += vg[sl][1];
+        a[1][0] += vu[sl][0]; a[1][1] += vu[sl][1];
+      }
     if (P.gscale) {
       const float gsg = P.gscale[2 * g], gsu = P.gscale[2 * g + 1];
       a[0][0] *= gsg; a[0][1] *= gsg;
