@@ -303,7 +303,11 @@ size_t moe_gemm1_workspace_size(const moe_weights *w13, long p_cap,
  * every sorted row, plus with lora_down
  * the down-LoRA delta scale * (h_lora[r] A2_g^T) B2_g^T for groups
  * g < lora_down->n_groups (h_lora bf16 [P_cap][I]: GEMM1's h_lora output
- * for FP8 weights, h itself for BF16 / 4-bit weights), then
+ * for FP8 weights, h itself for BF16 / 4-bit weights). For FP8 and 4-bit
+ * weights the rows y pass to the combine as fp16 with one power-of-two
+ * scale per row and 16 columns (relative rounding error at most 2^-11 on
+ * every value above 2^-29 of its run's largest); BF16 layers keep fp32
+ * rows. Then
  *   out[t][:] = sum_{j < top_k, pair_row[t*top_k+j] >= 0} topk_w[t][j] *
  *               y[pair_row[t*top_k+j]]   (ascending j, fp32)
  *             + shared_w * y[pair_row[T*top_k + t]]   (if shared_expert)
@@ -311,7 +315,8 @@ size_t moe_gemm1_workspace_size(const moe_weights *w13, long p_cap,
  * Every out element is written (0 for a token with no local pair).
  * w2->N = H, w2->K = I. out fp32 [T][H]. Limits: 1 <= top_k <= 64
  * (MOE_ERR_SHAPE). err_word as for moe_grouped_gemm1_act. Workspace:
- * moe_gemm2_workspace_size(w2, p_cap, lora_down) bytes: the fp32 y rows, or
+ * moe_gemm2_workspace_size(w2, p_cap, lora_down) bytes: the y rows (and
+ * their scale exponents), or
  * for FP8 / 4-bit weights at decode sizes their split-K partial sums
  * (4 * p_cap * H floats, reduced by the combine in a fixed order; the
  * down-LoRA delta enters the first partial of each tile), then the

@@ -428,7 +428,8 @@ int moe_grouped_gemm2_combine(const moe_weights* w2, const void* h,
   e = moe::launch_gemm2(a, s);
   if (e == hipSuccess)
     e = moe::launch_combine(y, T, H, top_k, shared_expert, pair_row, topk_w,
-                            shared_w, out, s, sk_grid, p_cap, I, a.G, offsets, sk_mode);
+                            shared_w, out, s, sk_grid, p_cap, I, a.G, offsets, sk_mode,
+                            w2->fmt != MOE_W_BF16);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_grouped_gemm2_combine");
 }
 
@@ -636,7 +637,8 @@ int moe_forward(const moe_layer* L, const void* x_bf16, const float* logits,
   e = moe::launch_gemm2(a, s);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/gemm2");
   e = moe::launch_combine(y, T, L->H, L->top_k, L->shared_expert, pair_row,
-                          topk_w, L->shared_w, out, s, sk_grid, pc, L->I, G, offsets, sk_mode);
+                          topk_w, L->shared_w, out, s, sk_grid, pc, L->I, G, offsets, sk_mode,
+                          L->w2.fmt != MOE_W_BF16);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/combine");
   return MOE_OK;
 }

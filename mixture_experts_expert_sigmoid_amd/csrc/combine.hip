@@ -39,6 +39,60 @@ __global__ __launch_bounds__(256) void combine_kernel(
   *(f32x4*)(out + t * H + 4 * c4) = acc;
 }
 
+// The same combine over GEMM2's fp16 rows (FP8 and 4-bit layers): y16
+// [p_rows][H] fp16 and ye [p_rows][H / 16], value = y16 * 2^ye (exact in
+// fp32), then the same fp32 multiply-adds in the same order. Each thread owns
+// 8 consecutive columns, one scale exponent.
+__global__ __launch_bounds__(256) void combine16_kernel(
+    const uint16_t* __restrict__ y16, const int8_t* __restrict__ ye, long T, int H,
+    int top_k, int shared, const int* __restrict__ pair_row,
+    const float* __restrict__ topk_w, float shared_w, float* __restrict__ out) {
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  const int cpr = H >> 3;                       // 8-column runs per row
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= T * cpr) return;
+  const long t = i / cpr;
+  const int c8 = (int)(i - t * cpr);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  // kPairs pairs at a time (ascending slot, the shared pair last): their
+  // rows and weights are loaded together, then their y runs, then they are
+  // accumulated in pair order
+  constexpr int kPairs = 4;
+  const int np = top_k + shared;
+  for (int j0 = 0; j0 < np; j0 += kPairs) {
+    int r[kPairs];
+    float w[kPairs];
+#pragma unroll
+    for (int u = 0; u < kPairs; ++u) {
+      const int j = min(j0 + u, np - 1);
+      const long jr = j < top_k ? t * top_k + j : T * top_k + t;
+      r[u] = pair_row[jr];
+      const float wl = topk_w[t * top_k + min(j, top_k - 1)];
+      w[u] = j < top_k ? wl : shared_w;
+    }
+    f16x8 v[kPairs];
+    int e[kPairs];
+    // a pair without a local row reads row 0 instead (the launch has
+    // p_rows >= 1; the value is not used), so no load waits on a branch
+#pragma unroll
+    for (int u = 0; u < kPairs; ++u) {
+      const long rr = max(r[u], 0);
+      v[u] = *(const f16x8*)(y16 + rr * H + 8 * c8);
+      e[u] = ye[rr * (H >> 4) + (c8 >> 1)];
+    }
+#pragma unroll
+    for (int u = 0; u < kPairs; ++u)
+      if (j0 + u < np && r[u] >= 0) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          acc[q] = fmaf(w[u], __builtin_amdgcn_ldexpf((float)v[u][q], e[u]), acc[q]);
+      }
+  }
+  float* o = out + t * H + 8 * c8;
+  *(f32x4*)o = (f32x4){acc[0], acc[1], acc[2], acc[3]};
+  *(f32x4*)(o + 4) = (f32x4){acc[4], acc[5], acc[6], acc[7]};
+}
+
 // The same combine over the partial sums of the FP8 / 4-bit GEMM2's split-K
 // kernel (slots [kSkSlots][p_rows][H]): each y element is first summed over
 // the slots of its tile in slot order. The tile schedule is rebuilt exactly as
@@ -123,9 +177,18 @@ __global__ __launch_bounds__(512) void combine_sk_kernel(
 hipError_t launch_combine(const float* y, long T, int H, int top_k, int shared,
                           const int* pair_row, const float* topk_w,
                           float shared_w, float* out, hipStream_t s, int sk_grid,
-                          long p_cap, int I, int G, const int* offsets, int sk_mode) {
+                          long p_cap, int I, int G, const int* offsets, int sk_mode,
+                          bool y16) {
   long n = T * (long)(H / 4);
   if (n == 0) return hipSuccess;
+  if (sk_grid == 0 && y16 && p_cap > 0) {   // (p_cap == 0: no rows, out = 0 below)
+    const uint16_t* yh = (const uint16_t*)y;
+    const int8_t* ye = (const int8_t*)(yh + p_cap * H);
+    const long n8 = T * (long)(H / 8);
+    hipLaunchKernelGGL(combine16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s,
+                       yh, ye, T, H, top_k, shared, pair_row, topk_w, shared_w, out);
+    return hipGetLastError();
+  }
   if (sk_grid > 0) {
     const long nwg = T * ((H + kCsCols - 1) / kCsCols);
     hipLaunchKernelGGL(combine_sk_kernel, dim3((unsigned)nwg), dim3(512), 0, s, y, T, H,

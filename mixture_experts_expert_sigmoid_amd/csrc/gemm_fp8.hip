@@ -118,11 +118,8 @@ __device__ __forceinline__ void fp8_epilogue(const GemmParams& P, const Tile& t,
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) {
       const int tr = 16 * ms + lr;
-      if (tr < m) {
-        float* yr = P.y + (long)(row0 + tr) * P.N;
-        *(f32x4*)(yr + t.n_lo + c0) = acc[ms][0];
-        if (hi_ok) *(f32x4*)(yr + t.n_hi + c0) = acc[ms][1];
-      }
+      store_y16(P, row0 + tr, t.n_lo + c0, acc[ms][0], tr < m);
+      if (hi_ok) store_y16(P, row0 + tr, t.n_hi + c0, acc[ms][1], tr < m);
     }
   } else {
     float gsg = 1.0f, gsu = 1.0f;
