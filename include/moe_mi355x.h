@@ -304,10 +304,11 @@ size_t moe_gemm1_workspace_size(const moe_weights *w13, long p_cap,
  * the down-LoRA delta scale * (h_lora[r] A2_g^T) B2_g^T for groups
  * g < lora_down->n_groups (h_lora bf16 [P_cap][I]: GEMM1's h_lora output
  * for FP8 weights, h itself for BF16 / 4-bit weights). For FP8 and 4-bit
- * weights the rows y pass to the combine as fp16 with one power-of-two
- * scale per row and 16 columns (relative rounding error at most 2^-11 on
- * every value above 2^-29 of its run's largest); BF16 layers keep fp32
- * rows. Then
+ * weights the rows y pass to the combine in block floating point: one
+ * power-of-two scale per row and 16 columns and an int16 multiple of it per
+ * value, rounded to nearest (error at most 2^-15 of the run's largest
+ * magnitude; a value that is not finite becomes NaN); BF16 layers keep
+ * fp32 rows. Then
  *   out[t][:] = sum_{j < top_k, pair_row[t*top_k+j] >= 0} topk_w[t][j] *
  *               y[pair_row[t*top_k+j]]   (ascending j, fp32)
  *             + shared_w * y[pair_row[T*top_k + t]]   (if shared_expert)

@@ -39,15 +39,16 @@ __global__ __launch_bounds__(256) void combine_kernel(
   *(f32x4*)(out + t * H + 4 * c4) = acc;
 }
 
-// The same combine over GEMM2's fp16 rows (FP8 and 4-bit layers): y16
-// [p_rows][H] fp16 and ye [p_rows][H / 16], value = y16 * 2^ye (exact in
-// fp32), then the same fp32 multiply-adds in the same order. Each thread owns
-// 8 consecutive columns, one scale exponent.
+// The same combine over GEMM2's block-floating-point rows (FP8 and 4-bit
+// layers): y16 [p_rows][H] int16 and ye [p_rows][H / 16], value = y16 *
+// 2^ye (exact in fp32; -32768 stands for a value that was not finite and
+// reads as NaN), then the same fp32 multiply-adds in the same order. Each
+// thread owns 8 consecutive columns, one scale exponent.
 __global__ __launch_bounds__(256) void combine16_kernel(
     const uint16_t* __restrict__ y16, const int8_t* __restrict__ ye, long T, int H,
     int top_k, int shared, const int* __restrict__ pair_row,
     const float* __restrict__ topk_w, float shared_w, float* __restrict__ out) {
-  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
   const int cpr = H >> 3;                       // 8-column runs per row
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= T * cpr) return;
@@ -70,22 +71,25 @@ __global__ __launch_bounds__(256) void combine16_kernel(
       const float wl = topk_w[t * top_k + min(j, top_k - 1)];
       w[u] = j < top_k ? wl : shared_w;
     }
-    f16x8 v[kPairs];
+    i16x8 v[kPairs];
     int e[kPairs];
     // a pair without a local row reads row 0 instead (the launch has
     // p_rows >= 1; the value is not used), so no load waits on a branch
 #pragma unroll
     for (int u = 0; u < kPairs; ++u) {
       const long rr = max(r[u], 0);
-      v[u] = *(const f16x8*)(y16 + rr * H + 8 * c8);
+      v[u] = *(const i16x8*)(y16 + rr * H + 8 * c8);
       e[u] = ye[rr * (H >> 4) + (c8 >> 1)];
     }
 #pragma unroll
     for (int u = 0; u < kPairs; ++u)
       if (j0 + u < np && r[u] >= 0) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-          acc[q] = fmaf(w[u], __builtin_amdgcn_ldexpf((float)v[u][q], e[u]), acc[q]);
+        for (int q = 0; q < 8; ++q) {
+          const float yv = v[u][q] == -32768 ? __builtin_nanf("")
+                                             : __builtin_amdgcn_ldexpf((float)v[u][q], e[u]);
+          acc[q] = fmaf(w[u], yv, acc[q]);
+        }
       }
   }
   float* o = out + t * H + 8 * c8;

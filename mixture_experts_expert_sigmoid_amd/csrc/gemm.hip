@@ -356,7 +356,7 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t s) {
     P.sk_mode = mode;
     *a.sk_mode = mode;
     if (mode != SK_SPLIT) {
-      P.y16 = (uint16_t*)a.y;      // fp16 rows, then their scale exponents
+      P.y16 = (uint16_t*)a.y;      // int16 rows, then their scale exponents
       P.ye = (int8_t*)((char*)a.y + (size_t)a.p_cap * a.H * 2);
       hipError_t e = run(nullptr);
       if (e != hipSuccess || mode == SK_PLAIN) return e;

@@ -65,7 +65,7 @@ struct GemmParams {
   uint16_t* h_lora;          // GEMM1 out (FP8 layers), nullable: bf16 [p_cap][I]
                              // SwiGLU output before the re-quantisation
   // GEMM2 out: fp32 rows [p_cap][N] (BF16 layers), or for the FP8 and 4-bit
-  // kernels fp16 rows y16 [p_cap][N] with one power-of-two scale exponent
+  // kernels int16 rows y16 [p_cap][N] with one power-of-two scale exponent
   // per row and 16 columns, ye [p_cap][N / 16] (see store_y16)
   float* y;
   uint16_t* y16;
@@ -275,26 +275,38 @@ __device__ __forceinline__ void split3_bf16(float x, float y, uint32_t (&t)[3]) 
   t[2] = f32_to_bf16_bits(sx) | (f32_to_bf16_bits(sy) << 16);
 }
 
-// GEMM2's rows for the weighted combine, stored in half the bytes of fp32:
-// each run of 16 columns of a row (the 4 lanes r, r + 16, r + 32, r + 48
-// hold 4 consecutive columns each) shares one power-of-two scale 2^e, e
-// chosen from the run's largest magnitude m in [2^(E-1), 2^E) as E - 15 (at
-// least -128), so the values enter fp16 at most 2^15 in magnitude and are
-// rounded to nearest even: a relative error of at most 2^-11 for every
-// value above m * 2^-29. The combine multiplies each back by 2^e exactly.
-// Called by all 64 lanes of the wave (the run maximum is a lane exchange);
-// ok: this lane's row is valid.
+// GEMM2's rows for the weighted combine in half the bytes of fp32, as block
+// floating point: each run of 16 columns of a row (the 4 lanes r, r + 16,
+// r + 32, r + 48 hold 4 consecutive columns each) shares one power-of-two
+// scale 2^e and every value is an int16 multiple of it. With m the run's
+// largest finite magnitude, m in [2^(E-1), 2^E), e = E - 15 (at least -128),
+// so q = round-to-nearest-even(v / 2^e) lies in [-32767, 32767] (|v| <= m <
+// 2^(e+15); a value that rounds to 2^15 is clamped, one unit) and the error
+// of every value is at most 2^e / 2 <= 2^-15 m (2^e when clamped). A value
+// that is not finite is stored as -32768 and read back as NaN. The combine
+// multiplies q by 2^e exactly. Called by all 64 lanes of the wave (the run
+// maximum is a lane exchange); ok: this lane's row is valid.
 __device__ __forceinline__ void store_y16(const GemmParams& P, long row, int col,
                                           const f32x4& v, bool ok) {
-  float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+  float m = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float a = fabsf(v[r]);
+    m = fmaxf(m, a <= 3.402823466e38f ? a : 0.0f);
+  }
   m = max_across_rows(m);
   const int e = max(__builtin_amdgcn_frexp_expf(m) - 15, -128);
   if (ok) {
-    _Float16 q[4];
+    int q[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) q[r] = (_Float16)__builtin_amdgcn_ldexpf(v[r], -e);
-    uint2 w;
-    __builtin_memcpy(&w, q, 8);
+    for (int r = 0; r < 4; ++r) {
+      const float t = __builtin_rintf(__builtin_amdgcn_ldexpf(v[r], -e));
+      q[r] = fabsf(v[r]) <= 3.402823466e38f
+                 ? (int)__builtin_amdgcn_fmed3f(t, -32767.0f, 32767.0f)
+                 : -32768;
+    }
+    const uint2 w = {(uint32_t)(q[0] & 0xFFFF) | ((uint32_t)q[1] << 16),
+                     (uint32_t)(q[2] & 0xFFFF) | ((uint32_t)q[3] << 16)};
     *(uint2*)(P.y16 + row * P.N + col) = w;
     if ((threadIdx.x & 48) == 0) P.ye[row * (P.N >> 4) + (col >> 4)] = (int8_t)e;
   }

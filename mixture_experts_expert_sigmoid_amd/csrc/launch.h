@@ -161,7 +161,7 @@ struct Gemm2Args {
   int H, I, G;
   long p_cap;
   const int* offsets;
-  float* y;              // [p_cap][H] fp32 (BF16), fp16 rows + their scale
+  float* y;              // [p_cap][H] fp32 (BF16), int16 rows + their scale
                          // exponents (FP8, 4-bit), or the split-K partials
   int* sk_grid;          // out: split-K kernel grid (0 = plain kernel)
   int* sk_mode;          // out: SK_PLAIN, SK_SPLIT or SK_DEVICE
@@ -180,7 +180,7 @@ hipError_t launch_gemm2(const Gemm2Args& a, hipStream_t s);
 // kernel over G groups, reduced here per element in slot order (sk_mode
 // SK_SPLIT), or -- SK_DEVICE -- either those or plain rows, as the device
 // rule decides on the real tile count. sk_grid == 0: y holds GEMM2's rows,
-// fp32 [p_cap][H] (y16 = false) or fp16 [p_cap][H] followed by the int8
+// fp32 [p_cap][H] (y16 = false) or int16 [p_cap][H] followed by the int8
 // scale exponents [p_cap][H / 16] (y16 = true, see store_y16)
 hipError_t launch_combine(const float* y, long T, int H, int top_k, int shared,
                           const int* pair_row, const float* topk_w,

@@ -500,6 +500,38 @@ def test_fp4_small_block_scales_on_gpu(fmt):
     check_layer(spec, o["out"].cpu().numpy(), arr, nb)
 
 
+@pytest.mark.parametrize("name,log2f", [("fp8_clamp_small", 100), ("fp8_clamp_small", -90),
+                                         ("fp8_clamp_decode", 100), ("nvfp4_lora_small", 96),
+                                         ("nvfp4_lora_small", -100)])
+def test_gemm2_rows_far_from_unit_scale(name, log2f):
+    """GEMM2's rows reach the combine as fp16 with a power-of-two scale per
+    row and 16 columns. W2 scaled by 2^log2f (FP8: the block scales, NVFP4:
+    the per-expert W2 global scales) puts y and the output far outside
+    fp16's own range (about 1e30 and 1e-26 here); the output must still meet
+    the bar against the oracle, which scales exactly."""
+    spec, T = SMALL[name]
+    if spec.fmt != "fp8":     # no LoRA: its delta would not scale with W2
+        spec = spec.scaled(name=name + "_nolora", lora_rank=0, lora_down=False)
+    layer = make_layer(spec)
+    batch = make_batch(spec, layer, T)
+    nb = to_numpy_batch(batch)
+    f = 2.0 ** log2f
+    if spec.fmt == "fp8":
+        layer.w2_s = (layer.w2_s.double() * f).float()
+    else:
+        layer.gs2 = (layer.gs2.double() * f).float()
+    arr = to_numpy_layer(layer)
+    _log("gemm2-row-scale", name, T, log2f)
+    mod = module_for(spec, layer)
+    o = mod.forward(batch.x.cuda(), batch.logits.cuda(), adapter_ids=_ad(batch))
+    torch.cuda.synchronize()
+    assert M.moe_read_device_error(o["err_word"]) == 0
+    out = o["out"].cpu().numpy()
+    assert np.isfinite(out).all()
+    ref = check_layer(spec, out, arr, nb)
+    assert np.sqrt(np.mean(ref ** 2)) > 0
+
+
 def test_mxfp4_exponents_outside_the_exact_window_are_flagged():
     """MXFP4 block exponents outside the exactly expanded 104..128 set
     MOE_DEVERR_W4_SCALE (and nothing else); the kernels clamp them to
