@@ -354,11 +354,17 @@ __device__ __forceinline__ void fp8_tile(const GemmParams& P, const Tile& tl, ui
     float xs[MS];
     {
       const float* sx = (const float*)(sa + Gm::A_BYTES) + lr * MS;
-      if constexpr (MS >= 4) {
+      if constexpr (MS % 4 == 0) {
 #pragma unroll
         for (int i = 0; i < MS; i += 4) {
           const f32x4 v = *(const f32x4*)(sx + i);
           xs[i] = v[0]; xs[i + 1] = v[1]; xs[i + 2] = v[2]; xs[i + 3] = v[3];
+        }
+      } else if constexpr (MS % 2 == 0) {   // rows of MS floats: 8-byte aligned
+#pragma unroll
+        for (int i = 0; i < MS; i += 2) {
+          const float2 v = *(const float2*)(sx + i);
+          xs[i] = v.x; xs[i + 1] = v.y;
         }
       } else {
 #pragma unroll
@@ -500,6 +506,12 @@ __device__ __forceinline__ void plain_tiles(const GemmParams& P, uint8_t* smem,
     tl.nt = __builtin_amdgcn_readfirstlane(tl.nt);
     tl.n_lo = __builtin_amdgcn_readfirstlane(tl.n_lo);
     tl.n_hi = __builtin_amdgcn_readfirstlane(tl.n_hi);
+    if constexpr (TBM >= 160) {
+      if (tl.m > 128) {
+        fp8_tile<160, G1, false, false, LORA, NTH>(P, tl, smem, 0, NS);
+        continue;
+      }
+    }
     if constexpr (TBM >= 128) {
       if (tl.m > 64) {
         fp8_tile<128, G1, false, false, LORA, NTH>(P, tl, smem, 0, NS);
@@ -630,6 +642,11 @@ static hipError_t run_fp8_tbm(const GemmParams& P, long p_cap, int NT, hipStream
   const long hint = P.G > 0 ? p_cap / P.G : p_cap;
   if (hint <= 32) return run_fp8<32, G1, LORA>(P, p_cap, NT, s);
   if (hint <= 64) return run_fp8<64, G1, LORA>(P, p_cap, NT, s);
+  // GEMM2 without LoRA also has a 160-row class: a group of 129..160 rows
+  // (common when groups average ~115 rows) streams its weights once instead
+  // of twice, and a large group needs a fifth fewer M-tiles. GEMM1's bf16
+  // activation ring has no room for it.
+  if constexpr (!G1 && !LORA) return run_fp8<160, G1, LORA>(P, p_cap, NT, s);
   return run_fp8<128, G1, LORA>(P, p_cap, NT, s);
 }
 
