@@ -537,8 +537,10 @@ int moe_forward(const moe_layer* L, const void* x_bf16, const float* logits,
   const bool mx = L->w13.fmt == MOE_W_MXFP4_A8;
   bool x16_ready = false;
   hipError_t e = hipSuccess;
-  if (moe::front_small_fits(T, L->top_k, G, L->H)) {
-    // decode sizes: route + activation pass + permute in one launch
+  const bool small = moe::front_small_fits(T, L->top_k, G, L->H);
+  {
+    // decode sizes: route + activation pass + permute in one launch; larger
+    // batches: route + activation pass in one launch, then the permutation
     moe::FrontArgs fa{};
     fa.logits = logits;
     fa.T = T;
@@ -562,26 +564,17 @@ int moe_forward(const moe_layer* L, const void* x_bf16, const float* logits,
     fa.sorted_pair = sorted_pair;
     fa.pair_row = pair_row;
     fa.err_word = err_word;
-    e = moe::launch_front_small(fa, fp8 ? 1 : mx ? 3 : (four ? 2 : 0), s);
+    const int mode = fp8 ? 1 : mx ? 3 : (four ? 2 : 0);
+    e = small ? moe::launch_front_small(fa, mode, s) : moe::launch_front_large(fa, mode, s);
     if (e != hipSuccess) return hip_fail(e, "moe_forward/front");
     x16_ready = four && !mx;
-  } else {
-    e = moe::launch_route(logits, T, ld_logits, L->num_experts_global, L->n_sink,
-                          L->top_k, nullptr, L->route_scale * L->global_scale,
-                          topk_ids, topk_w, sink_w, nullptr, s);
-    if (e != hipSuccess) return hip_fail(e, "moe_forward/route");
+  }
+  if (!small) {
     e = moe::launch_permute(topk_ids, T, L->top_k, L->num_experts_global,
                             L->local_expert_offset, L->num_local_experts,
                             L->shared_expert, offsets, sorted_pair, pair_row,
                             err_word, base + o.perm_ws, s);
     if (e != hipSuccess) return hip_fail(e, "moe_forward/permute");
-    if (fp8) {
-      e = moe::launch_quant_act(x_bf16, T, L->H, xq, xs, s);
-      if (e != hipSuccess) return hip_fail(e, "moe_forward/quant");
-    } else if (mx) {
-      e = moe::launch_quant_act_mx(x_bf16, T, L->H, xq, xs, s);
-      if (e != hipSuccess) return hip_fail(e, "moe_forward/quant");
-    }
   }
   if (L->lora) {
     e = moe::launch_lora_z(x_bf16, L->lora->A, L->lora->rank, T, L->H,

@@ -74,4 +74,71 @@ hipError_t launch_front_small(const FrontArgs& a, int mode, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Larger batches: the router epilogue and the activation pass are
+// independent, so one launch runs both. Workgroups come in groups of 1 + q:
+// the first of group g routes token rows 4g .. 4g + 3 (a wave per row, as
+// route_kernel), the other q run activation workgroups g q .. g q + q - 1:
+// four 512-column units each (as quant_act_kernel / quant_act_mx_kernel) or
+// 256 runs of 8 columns of the f16 copy (as act_f16p_kernel). Interleaved
+// this way the long, latency-bound routing waves share the CUs with the
+// short, bandwidth-bound activation waves instead of filling every wave
+// slot first. The device code is the separate kernels', so every output is
+// bit-identical to theirs.
+template <int NV, int MODE>
+__global__ __launch_bounds__(256) void front_large_kernel(FrontArgs a, long q, long nb_act) {
+  const int wave = threadIdx.x >> 6;
+  const long grp = (long)blockIdx.x / (q + 1), pos = (long)blockIdx.x - grp * (q + 1);
+  if (pos == 0) {
+    const long row = grp * 4 + wave;                   // wave-uniform
+    if (row < a.T)
+      route_row<NV>(a.logits, row, a.ld, a.n_routed, a.n_sink, a.k, nullptr, a.scale, a.ids,
+                    a.w, a.sw, nullptr);
+    return;
+  }
+  const long b = grp * q + pos - 1;
+  if (b >= nb_act) return;
+  if constexpr (MODE == 1 || MODE == 3) {
+    const long wi = b * 4 + wave;                      // wave-uniform
+    if (wi >= a.T * ((a.H + 511) >> 9)) return;
+    if constexpr (MODE == 1)
+      quant_act_unit((const uint16_t*)a.x, wi, a.H, (uint8_t*)a.xq, (float*)a.xs);
+    else
+      quant_mx_unit((const uint16_t*)a.x, wi, a.H, (uint8_t*)a.xq, (uint8_t*)a.xs);
+  } else if constexpr (MODE == 2) {
+    const long i = b * 256 + threadIdx.x;
+    if (i >= a.T * (long)a.H / 8) return;
+    const i32x4 v = *(const i32x4*)((const uint16_t*)a.x + 8 * i);
+    *(f16x8*)((uint16_t*)a.xq + 8 * i) = bf16x8_f16p(v);
+    if (a.err_word && bf16x8_f16_overflow(v)) atomicOr(a.err_word, MOE_DEVERR_BIT_F16_RANGE);
+  }
+}
+
+hipError_t launch_front_large(const FrontArgs& a, int mode, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  const long nb_route = (a.T + 3) / 4;
+  long nb_act = 0;
+  if (mode == 1 || mode == 3) nb_act = (a.T * ((a.H + 511) / 512) + 3) / 4;
+  else if (mode == 2) nb_act = (a.T * (long)a.H / 8 + 255) / 256;
+  const long q = (nb_act + nb_route - 1) / nb_route;   // activation workgroups per route one
+  const dim3 grid((unsigned)(nb_route * (q + 1))), block(256);
+  const int nv = (a.n_routed + 63) / 64;
+#define FL(NV, MODE) \
+  hipLaunchKernelGGL((front_large_kernel<NV, MODE>), grid, block, 0, s, a, q, nb_act)
+#define FLM(NV)                    \
+  do {                             \
+    if (mode == 1) FL(NV, 1);      \
+    else if (mode == 2) FL(NV, 2); \
+    else if (mode == 3) FL(NV, 3); \
+    else FL(NV, 0);                \
+  } while (0)
+  if (nv <= 1) FLM(1);
+  else if (nv <= 2) FLM(2);
+  else if (nv <= 4) FLM(4);
+  else if (nv <= 8) FLM(8);
+  else FLM(16);
+#undef FLM
+#undef FL
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -79,6 +79,10 @@ struct FrontArgs {
 };
 bool front_small_fits(long T, int k, int G, int H);
 hipError_t launch_front_small(const FrontArgs& a, int mode, hipStream_t s);
+// the router epilogue and the activation pass (mode as for the small front
+// end) in one launch of independent workgroups, for any T; the permutation
+// follows separately
+hipError_t launch_front_large(const FrontArgs& a, int mode, hipStream_t s);
 
 // z[r][q] = sum_h x[row][h] * A[a(r)][g(r)][q][h] for every sorted row r of
 // a local group (fp32). row = t(r) = sorted_pair[r] / top_k when gather,
