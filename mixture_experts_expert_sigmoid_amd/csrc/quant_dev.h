@@ -10,6 +10,23 @@
 
 namespace moe {
 
+// The unit index is the same for every lane of the wave: make it a scalar so
+// that row = wi / nc is scalar arithmetic (32-bit whenever wi fits, as it
+// does for any realistic batch) instead of a 64-bit division per lane.
+__device__ __forceinline__ void unit_row_col(long wi, int nc, long& row, int& chunk) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)wi);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(wi >> 32));
+  if (hi == 0) {
+    const uint32_t r = lo / (uint32_t)nc;
+    row = r;
+    chunk = (int)(lo - r * (uint32_t)nc);
+  } else {
+    const long w = ((long)hi << 32) | lo;
+    row = w / nc;
+    chunk = (int)(w - row * nc);
+  }
+}
+
 // One wave per (row, 512-column chunk): lane l converts the 8 columns
 // chunk*512 + 8l .. +7 with one 16-byte load; the 16 lanes of a DPP row
 // (lane / 16) hold one 128-column group, so the group amax is a row
@@ -22,8 +39,10 @@ __device__ __forceinline__ void quant_act_unit(const uint16_t* __restrict__ x, l
                                                float* __restrict__ xs) {
   const int nc = (H + 511) >> 9;
   const int lane = lane_id();
-  const long row = wi / nc;
-  const int col = (int)(wi - row * nc) * 512 + 8 * lane;
+  long row;
+  int chunk;
+  unit_row_col(wi, nc, row, chunk);
+  const int col = chunk * 512 + 8 * lane;
   const bool on = col < H;              // whole 16-lane rows (H % 128 == 0)
   float f[8];
   i32x4 v = {0, 0, 0, 0};
@@ -38,12 +57,33 @@ __device__ __forceinline__ void quant_act_unit(const uint16_t* __restrict__ x, l
   for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[i]));
   a = max16(a);
   const float sc = a > 0.0f ? a / 448.0f : 1.0f;
+  // x / sc: with r = 1 / sc correctly rounded, q0 = x r, the residual
+  // x - q0 sc (exact by FMA) and one correction q0 + (x - q0 sc) r give the
+  // correctly rounded quotient whenever it is normal, and the same e4m3 code
+  // always, for every bf16 x = 0 or |x| >= 2^-64 and sc >= 2^-64: checked
+  // exhaustively over all bf16 amax / x pairs on the host. Other lanes
+  // divide. Three operations per value instead of the division's ten.
+  bool fast = sc >= 0x1p-64f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) fast = fast && (f[i] == 0.0f || fabsf(f[i]) >= 0x1p-64f);
+  float qv[8];
+  if (fast) {
+    const float r = 1.0f / sc;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float q0 = __fmul_rn(f[i], r);
+      qv[i] = __builtin_fmaf(__builtin_fmaf(-q0, sc, f[i]), r, q0);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qv[i] = f[i] / sc;
+  }
   uint32_t w[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     float q[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) q[i] = __builtin_amdgcn_fmed3f(f[4 * h + i] / sc, -448.0f, 448.0f);
+    for (int i = 0; i < 4; ++i) q[i] = __builtin_amdgcn_fmed3f(qv[4 * h + i], -448.0f, 448.0f);
     int c = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
     w[h] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], c, true);
   }
@@ -68,8 +108,10 @@ __device__ __forceinline__ void quant_mx_unit(const uint16_t* __restrict__ x, lo
                                               uint8_t* __restrict__ xe) {
   const int nc = (H + 511) >> 9;
   const int lane = lane_id();
-  const long row = wi / nc;
-  const int col = (int)(wi - row * nc) * 512 + 8 * lane;
+  long row;
+  int chunk;
+  unit_row_col(wi, nc, row, chunk);
+  const int col = chunk * 512 + 8 * lane;
   const bool on = col < H;              // whole quads (H % 32 == 0)
   float f[8];
   i32x4 v = {0, 0, 0, 0};
