@@ -75,28 +75,26 @@ hipError_t launch_front_small(const FrontArgs& a, int mode, hipStream_t s) {
 }
 
 // Larger batches: the router epilogue and the activation pass are
-// independent, so one launch runs both. Workgroups come in groups of 1 + q:
-// the first of group g routes token rows 4g .. 4g + 3 (a wave per row, as
-// route_kernel), the other q run activation workgroups g q .. g q + q - 1:
-// four 512-column units each (as quant_act_kernel / quant_act_mx_kernel) or
-// 256 runs of 8 columns of the f16 copy (as act_f16p_kernel). Interleaved
-// this way the long, latency-bound routing waves share the CUs with the
-// short, bandwidth-bound activation waves instead of filling every wave
-// slot first. The device code is the separate kernels', so every output is
-// bit-identical to theirs.
+// independent, so one launch runs both. The first nb_route workgroups route
+// four token rows each (a wave per row, as route_kernel) and are dispatched
+// first; the others run the activation pass, four 512-column units each (as
+// quant_act_kernel / quant_act_mx_kernel) or 256 runs of 8 columns of the
+// f16 copy (as act_f16p_kernel), filling the wave slots the routing leaves
+// and taking over as its waves finish. (Interleaving the two kinds of
+// workgroups through the grid measured slower at C2 T = 4096: the last
+// routing waves then start near the end and lengthen its tail.) The device
+// code is the separate kernels', so every output is bit-identical to theirs.
 template <int NV, int MODE>
-__global__ __launch_bounds__(256) void front_large_kernel(FrontArgs a, long q, long nb_act) {
+__global__ __launch_bounds__(256) void front_large_kernel(FrontArgs a, long nb_route) {
   const int wave = threadIdx.x >> 6;
-  const long grp = (long)blockIdx.x / (q + 1), pos = (long)blockIdx.x - grp * (q + 1);
-  if (pos == 0) {
-    const long row = grp * 4 + wave;                   // wave-uniform
+  if ((long)blockIdx.x < nb_route) {
+    const long row = (long)blockIdx.x * 4 + wave;      // wave-uniform
     if (row < a.T)
       route_row<NV>(a.logits, row, a.ld, a.n_routed, a.n_sink, a.k, nullptr, a.scale, a.ids,
                     a.w, a.sw, nullptr);
     return;
   }
-  const long b = grp * q + pos - 1;
-  if (b >= nb_act) return;
+  const long b = (long)blockIdx.x - nb_route;
   if constexpr (MODE == 1 || MODE == 3) {
     const long wi = b * 4 + wave;                      // wave-uniform
     if (wi >= a.T * ((a.H + 511) >> 9)) return;
@@ -119,11 +117,10 @@ hipError_t launch_front_large(const FrontArgs& a, int mode, hipStream_t s) {
   long nb_act = 0;
   if (mode == 1 || mode == 3) nb_act = (a.T * ((a.H + 511) / 512) + 3) / 4;
   else if (mode == 2) nb_act = (a.T * (long)a.H / 8 + 255) / 256;
-  const long q = (nb_act + nb_route - 1) / nb_route;   // activation workgroups per route one
-  const dim3 grid((unsigned)(nb_route * (q + 1))), block(256);
+  const dim3 grid((unsigned)(nb_route + nb_act)), block(256);
   const int nv = (a.n_routed + 63) / 64;
 #define FL(NV, MODE) \
-  hipLaunchKernelGGL((front_large_kernel<NV, MODE>), grid, block, 0, s, a, q, nb_act)
+  hipLaunchKernelGGL((front_large_kernel<NV, MODE>), grid, block, 0, s, a, nb_route)
 #define FLM(NV)                    \
   do {                             \
     if (mode == 1) FL(NV, 1);      \
