@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void combine16_kernel(
   const int cpr = H >> 3;                       // 8-column runs per row
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= T * cpr) return;
-  const long t = i / cpr;
+  long t = i / cpr;
   const int c8 = (int)(i - t * cpr);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   // kPairs pairs at a time (ascending slot, the shared pair last): their
@@ -60,6 +60,48 @@ __global__ __launch_bounds__(256) void combine16_kernel(
   // accumulated in pair order
   constexpr int kPairs = 4;
   const int np = top_k + shared;
+  if ((cpr & 63) == 0 && T * top_k + T < (1L << 31)) {
+    // a wave never straddles two tokens: the token, its pair rows and
+    // weights are wave-uniform (scalar loads); the y loads stay branch-free
+    // (a pair with no local row reads row 0, its value unused). Loading only
+    // the local pairs' rows (a branch per pair) helped the expert-parallel
+    // share at T = 8192 but cost 1.5-2 us per call at decode sizes.
+    t = (long)__builtin_amdgcn_readfirstlane((int)t);
+    for (int j0 = 0; j0 < np; j0 += kPairs) {
+      int r[kPairs];
+      float w[kPairs];
+#pragma unroll
+      for (int u = 0; u < kPairs; ++u) {
+        const int j = min(j0 + u, np - 1);
+        const int jr = (int)(j < top_k ? t * top_k + j : T * top_k + t);
+        r[u] = j0 + u < np ? pair_row[jr] : -1;
+        const float wl = topk_w[t * top_k + min(j, top_k - 1)];
+        w[u] = j < top_k ? wl : shared_w;
+      }
+      i16x8 v[kPairs];
+      int e[kPairs];
+#pragma unroll
+      for (int u = 0; u < kPairs; ++u) {
+        const long rr = max(r[u], 0);
+        v[u] = *(const i16x8*)(y16 + rr * H + 8 * c8);
+        e[u] = ye[rr * (H >> 4) + (c8 >> 1)];
+      }
+#pragma unroll
+      for (int u = 0; u < kPairs; ++u)
+        if (r[u] >= 0) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const float yv = v[u][q] == -32768 ? __builtin_nanf("")
+                                               : __builtin_amdgcn_ldexpf((float)v[u][q], e[u]);
+            acc[q] = fmaf(w[u], yv, acc[q]);
+          }
+        }
+    }
+    float* o = out + t * H + 8 * c8;
+    *(f32x4*)o = (f32x4){acc[0], acc[1], acc[2], acc[3]};
+    *(f32x4*)(o + 4) = (f32x4){acc[4], acc[5], acc[6], acc[7]};
+    return;
+  }
   for (int j0 = 0; j0 < np; j0 += kPairs) {
     int r[kPairs];
     float w[kPairs];
