@@ -239,7 +239,9 @@ size_t g1_part_bytes(const moe_weights* w13, long p_cap) {
 size_t g1_x16_bytes(const moe_weights* w13, long rows) {
   return is4(w13->fmt) && w13->fmt != MOE_W_MXFP4_A8 ? al((size_t)rows * w13->K * 2) : 0;
 }
-// GEMM2 workspace: fp32 y rows, or (split-K) their partial sums
+// GEMM2 workspace: the y rows (fp32 for BF16 layers; int16 + one scale
+// exponent per 16 columns otherwise, at most the fp32 size), or (split-K)
+// their partial sums
 size_t g2_bytes(const moe_weights* w2, long p_cap) {
   if (moe::splitk_use(w2->fmt, p_cap, w2->n_groups, (w2->N + 255) / 256, w2->K / 128, false))
     return moe::splitk_bytes(p_cap, w2->N);
