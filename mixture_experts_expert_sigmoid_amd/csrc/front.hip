@@ -17,7 +17,10 @@ template <int NV, int MODE>   // MODE 0: no activation pass, 1: FP8, 2: f16 copy
 __global__ __launch_bounds__(1024) void front_small_kernel(FrontArgs a) {
   extern __shared__ int sm[];                    // the permutation's 17 G ints
   const int wave = threadIdx.x >> 6;
-  for (long row = wave; row < a.T; row += 16)
+  // rows from the last wave down, activation units from the first wave up,
+  // so that at T = 1 the routing wave and the activation waves run side by
+  // side instead of one wave doing both in turn
+  for (long row = 15 - wave; row < a.T; row += 16)
     route_row<NV>(a.logits, row, a.ld, a.n_routed, a.n_sink, a.k, nullptr, a.scale, a.ids,
                   a.w, a.sw, nullptr);
   if constexpr (MODE == 1) {
