@@ -307,8 +307,13 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t s) {
     const int mode = a.part ? splitk_mode(a.fmt, a.p_cap, a.G, a.I / 128, a.H / 128, true)
                             : SK_PLAIN;
     P.sk_mode = mode;
-    if (mode != SK_SPLIT) {        // the plain kernel (it returns at once if an
-      e = run(nullptr);            // SK_DEVICE launch picks split-K)
+    // SK_DEVICE: the FP8 split-K kernel alone decides on the device and runs
+    // whole tiles itself when split-K does not pay; for the 4-bit formats
+    // the plain kernel is launched too (it returns at once if the split-K
+    // kernel takes the GEMM): carrying the whole-tile code would cost their
+    // split-K kernels occupancy
+    if (mode == SK_PLAIN || (mode == SK_DEVICE && !fp8)) {
+      e = run(nullptr);
       if (e != hipSuccess || mode == SK_PLAIN) return e;
     }
     P.part = a.part;

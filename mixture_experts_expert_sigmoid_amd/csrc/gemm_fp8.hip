@@ -540,11 +540,6 @@ __global__ __launch_bounds__(NTH) void moe_gemm_fp8_kernel(GemmParams P) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // 2 stages
   __shared__ int s_cum[kMaxGroups + 1];
   __shared__ int s_wsum[8];
-  // SK_DEVICE launch: return if the split-K kernel takes this GEMM
-  if (P.sk_mode == SK_DEVICE &&
-      sk_rule(tiles32(P.offsets, P.G, s_cum) * (G1 ? (P.I >> 7) : ((P.N + 255) >> 8)),
-              P.K >> 7))
-    return;
   tile_prefix<TBM>(P.offsets, P.G, s_cum, s_wsum);
   plain_tiles<TBM, G1, LORA, NTH>(P, smem, s_cum);
 }
@@ -561,7 +556,13 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_fp8_sk_kernel(GemmParams P)
   const int NT = G1 ? (P.I >> 7) : ((P.N + 255) >> 8);
   const int NS = P.K >> 7;
   tile_prefix<kSkBM>(P.offsets, G, s_cum, s_wsum);
-  if (P.sk_mode == SK_DEVICE && !sk_rule((long)s_cum[G] * NT, NS)) return;
+  // SK_DEVICE: the rule on the real tile count picked whole tiles; run them
+  // here as the plain kernel would (its 32-row class: the host sends only
+  // batches of at most 16 rows per group this way), so no second launch
+  if (P.sk_mode == SK_DEVICE && !sk_rule((long)s_cum[G] * NT, NS)) {
+    plain_tiles<kSkBM, G1, LORA, kThreads>(P, smem, s_cum);
+    return;
+  }
   const long U = (long)s_cum[G] * NT * NS;
   const int W = sk_workgroups((long)s_cum[G] * NT, NS, gridDim.x);
   const int b = blockIdx.x;
@@ -627,7 +628,9 @@ static hipError_t run_fp8_sk(const GemmParams& P, long p_cap, int NT, hipStream_
     if (e != hipSuccess) return e;
     per_cu = nb > 0 ? nb : 1;
   }
-  const int grid = num_cus() * per_cu;
+  // a multiple of 8: the whole-tile walk of an SK_DEVICE launch splits
+  // the grid over the 8 XCDs
+  const int grid = std::max(8, (num_cus() * per_cu) & ~7);
   *sk_grid = grid;
   if (p_cap == 0) return hipSuccess;
   GemmParams Q = P;
