@@ -307,12 +307,13 @@ hipError_t launch_gemm1(const Gemm1Args& a, hipStream_t s) {
     const int mode = a.part ? splitk_mode(a.fmt, a.p_cap, a.G, a.I / 128, a.H / 128, true)
                             : SK_PLAIN;
     P.sk_mode = mode;
-    // SK_DEVICE: the FP8 split-K kernel alone decides on the device and runs
-    // whole tiles itself when split-K does not pay; for the 4-bit formats
-    // the plain kernel is launched too (it returns at once if the split-K
-    // kernel takes the GEMM): carrying the whole-tile code would cost their
-    // split-K kernels occupancy
-    if (mode == SK_PLAIN || (mode == SK_DEVICE && !fp8)) {
+    // SK_DEVICE: the split-K kernel alone decides on the device and runs
+    // whole tiles itself when split-K does not pay, except for NVFP4 and a
+    // W4A8 layer with LoRA, whose split-K kernels would lose occupancy to
+    // the whole-tile code: there the plain kernel is launched too and
+    // returns at once if the split-K kernel takes the GEMM
+    const bool whole = fp8 || (mx ? !P.z : a.fmt != FMT_NVFP4);
+    if (mode == SK_PLAIN || (mode == SK_DEVICE && !whole)) {
       e = run(nullptr);
       if (e != hipSuccess || mode == SK_PLAIN) return e;
     }

@@ -225,16 +225,12 @@ __device__ __forceinline__ void mx_tile(const GemmParams& P, const Tile& tl, uin
   }
 }
 
+// Whole tiles walked by persistent workgroups: XCD x (= blockIdx % 8) owns
+// logical tiles [x*chunk, (x+1)*chunk)
 template <int TBM, bool LORA>
-__global__ __launch_bounds__(kThreads) void moe_gemm_mx_kernel(GemmParams P) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ int s_cum[kMaxGroups + 1];
-  __shared__ int s_wsum[8];
+__device__ __forceinline__ void mx_plain_tiles(const GemmParams& P, uint8_t* smem,
+                                               const int* s_cum) {
   const int NT = P.I >> 7, NS = P.K >> 7;
-  // SK_DEVICE launch: return if the split-K kernel takes this GEMM
-  if (P.sk_mode == SK_DEVICE && sk_rule(tiles32(P.offsets, P.G, s_cum) * NT, NS)) return;
-  tile_prefix<TBM>(P.offsets, P.G, s_cum, s_wsum);
-  // XCD x (= blockIdx % 8) owns logical tiles [x*chunk, (x+1)*chunk)
   const int total = s_cum[P.G] * NT;
   const int xcd = blockIdx.x & 7, nper = gridDim.x >> 3, slot = blockIdx.x >> 3;
   const int chunk = (total + 7) >> 3;
@@ -257,6 +253,19 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_mx_kernel(GemmParams P) {
   }
 }
 
+template <int TBM, bool LORA>
+__global__ __launch_bounds__(kThreads) void moe_gemm_mx_kernel(GemmParams P) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int s_cum[kMaxGroups + 1];
+  __shared__ int s_wsum[8];
+  const int NT = P.I >> 7, NS = P.K >> 7;
+  // SK_DEVICE launch (with LoRA only): return if the split-K kernel takes
+  // this GEMM
+  if (P.sk_mode == SK_DEVICE && sk_rule(tiles32(P.offsets, P.G, s_cum) * NT, NS)) return;
+  tile_prefix<TBM>(P.offsets, P.G, s_cum, s_wsum);
+  mx_plain_tiles<TBM, LORA>(P, smem, s_cum);
+}
+
 // Split-K (stream-K) variant for decode sizes, schedule as in the FP8 kernel
 template <bool LORA>
 __global__ __launch_bounds__(kThreads) void moe_gemm_mx_sk_kernel(GemmParams P) {
@@ -266,7 +275,14 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_mx_sk_kernel(GemmParams P) 
   const int G = P.G;
   const int NT = P.I >> 7, NS = P.K >> 7;
   tile_prefix<kSkBM>(P.offsets, G, s_cum, s_wsum);
-  if (P.sk_mode == SK_DEVICE && !sk_rule((long)s_cum[G] * NT, NS)) return;
+  if (P.sk_mode == SK_DEVICE && !sk_rule((long)s_cum[G] * NT, NS)) {
+    // whole tiles here, as the plain kernel's 32-row class would run them
+    // (without LoRA: with it the extra registers would cost the split-K
+    // kernel its second workgroup per CU, and the plain kernel is launched
+    // beside it)
+    if constexpr (!LORA) mx_plain_tiles<kSkBM, LORA>(P, smem, s_cum);
+    return;
+  }
   const long U = (long)s_cum[G] * NT * NS;
   const int W = sk_workgroups((long)s_cum[G] * NT, NS, gridDim.x);
   const int b = blockIdx.x;
@@ -329,7 +345,9 @@ static hipError_t run_mx_sk(const GemmParams& P, long p_cap, hipStream_t s, int*
     if (e != hipSuccess) return e;
     per_cu = nb > 0 ? nb : 1;
   }
-  const int grid = num_cus() * per_cu;
+  // a multiple of 8: the whole-tile walk of an SK_DEVICE launch splits
+  // the grid over the 8 XCDs
+  const int grid = std::max(8, (num_cus() * per_cu) & ~7);
   *sk_grid = grid;
   if (p_cap == 0) return hipSuccess;
   GemmParams Q = P;

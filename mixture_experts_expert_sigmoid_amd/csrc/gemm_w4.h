@@ -495,7 +495,14 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_w4_sk_kernel(GemmParams P) 
   const int NT = G1 ? (P.I >> 7) : ((P.N + 255) >> 8);
   const int NS = P.K >> 7;
   tile_prefix<kSkBM>(P.offsets, G, s_cum, s_wsum);
-  if (P.sk_mode == SK_DEVICE && !sk_rule((long)s_cum[G] * NT, NS)) return;
+  if (P.sk_mode == SK_DEVICE && !sk_rule((long)s_cum[G] * NT, NS)) {
+    // whole tiles here, as the plain kernel's 32-row class would run them
+    // (GEMM1 of INT4 and MXFP4; NVFP4's split-K kernel would lose its
+    // second workgroup per CU to the extra registers, so its plain kernel
+    // is launched beside it and takes this case)
+    if constexpr (G1 && WF != FMT_NVFP4) w4_plain_tiles<WF, kSkBM, G1, LORA>(P, smem, s_cum);
+    return;
+  }
   const long U = (long)s_cum[G] * NT * NS;
   const int W = sk_workgroups((long)s_cum[G] * NT, NS, gridDim.x);
   const int b = blockIdx.x;
@@ -558,7 +565,9 @@ static hipError_t run_w4_sk(const GemmParams& P, long p_cap, hipStream_t s, int*
     if (e != hipSuccess) return e;
     per_cu = nb > 0 ? nb : 1;
   }
-  const int grid = num_cus() * per_cu;
+  // a multiple of 8: the whole-tile walk of an SK_DEVICE launch splits
+  // the grid over the 8 XCDs
+  const int grid = std::max(8, (num_cus() * per_cu) & ~7);
   *sk_grid = grid;
   if (p_cap == 0) return hipSuccess;
   GemmParams Q = P;

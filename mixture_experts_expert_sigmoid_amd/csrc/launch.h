@@ -105,12 +105,12 @@ hipError_t launch_lora_z(const void* x_bf16, const void* A, int rank, long T,
 // For GEMM1, when that bound is too loose to decide because few rows per
 // expert are possible (p_cap <= 16 G: skewed routing can leave far fewer
 // tiles than the bound), the split-K kernel applies the same rule to the
-// real tile count it reads from the expert offsets (SK_DEVICE): the FP8 one
-// then runs whole tiles itself with the plain kernel's 32-row code when
-// split-K does not pay; for the 4-bit formats the plain kernel is launched
-// as well and returns at once when split-K is chosen (and the split-K kernel
-// when it is not). The reduction kernel decides the same way. GEMM2
-// (shorter K, smaller gains) keeps the shape-only rule.
+// real tile count it reads from the expert offsets (SK_DEVICE) and runs
+// whole tiles itself with the plain kernel's 32-row code when split-K does
+// not pay; for NVFP4 and W4A8 with LoRA the plain kernel is launched as well
+// and returns at once when split-K is chosen (and the split-K kernel when it
+// is not). The reduction kernel decides the same way. GEMM2 (shorter K,
+// smaller gains) keeps the shape-only rule.
 constexpr long kSkMaxTiles = 1024;
 constexpr long kSkCUs = 256;
 constexpr int kSkSlots = 4;          // partial-sum slots per tile
