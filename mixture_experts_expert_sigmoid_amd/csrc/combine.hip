@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void combine16_kernel(
   // kPairs pairs at a time (ascending slot, the shared pair last): their
   // rows and weights are loaded together, then their y runs, then they are
   // accumulated in pair order
-  constexpr int kPairs = 4;
+  constexpr int kPairs = 8;
   const int np = top_k + shared;
   if ((cpr & 63) == 0 && T * top_k + T < (1L << 31)) {
     // a wave never straddles two tokens: the token, its pair rows and
