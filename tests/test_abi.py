@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(M.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    # the spec entry points are all there
+    # the four steps of the path and the one-shot layer call are all declared
     for n in ("moe_route", "moe_permute", "moe_grouped_gemm1_act",
               "moe_grouped_gemm2_combine", "moe_forward"):
         assert n in names
